@@ -1,0 +1,151 @@
+"""Seeded synthetic inputs shared by the tests, the smoke check and bench.py.
+
+This module holds random draws and dtype narrowing only -- none of the
+quantization arithmetic.  Every generator uses numpy's PCG64
+``default_rng(seed)``, draws in the order written, produces values in
+float32 and narrows them to bf16 / fp16 / fp8-e4m3fn with torch's
+round-to-nearest-even casts.  Tensors are returned on the CPU.
+
+The full-size workloads are the ones the benchmark and the large parity
+tests use (rows x columns):
+
+* ``dq_sym_f16_64x256``             symmetric INT8, fp16 x, no smooth
+* ``dq_sym_smooth_bf16_8192x7168``  symmetric INT8, bf16 x with 0.1 % outliers
+                                    +-U(20, 60), fp32 smooth U(0.5, 2)
+* ``dq_moe_asym_{int8,int4}_bf16_32768x4096``  asymmetric, 64 experts, fp32
+                                    smooth [64, 4096], multinomial row counts
+* ``ada_ln_quant_bf16_4x4096x3072`` AdaLayerNorm + smooth + INT8
+* ``aq_{per_tensor,per_channel,per_token,per_group}_int8_16384x8192`` and
+  ``aq_per_group_fp8e4m3_16384x8192``  AntiQuantize to bf16
+"""
+from __future__ import annotations
+
+from typing import Dict, Optional
+
+import numpy as np
+import torch
+
+_TORCH = {"bfloat16": torch.bfloat16, "float16": torch.float16}
+
+
+def _narrow(a: np.ndarray, dtype: str) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(_TORCH[dtype])
+
+
+def dq_inputs(rows: int, n: int, seed: int, *, dtype: str = "bfloat16",
+              smooth: Optional[str] = None, experts: int = 0,
+              outlier_frac: float = 0.0) -> Dict[str, object]:
+    """Inputs of one DynamicQuant call.
+
+    Draw order: x ~ N(0, 1) [rows, n]; if outlier_frac > 0: positions
+    (without replacement), signs (+-1 equiprobable), magnitudes U(20, 60);
+    smooth ~ U(0.5, 2.0) of shape [n] ('vector') or [experts, n]
+    ('experts'); then the per-expert row counts ~ multinomial(rows, uniform
+    over experts), whose running sum is the int32 group index.
+    """
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((rows, n), dtype=np.float32)
+    if outlier_frac > 0.0 and rows * n > 0:
+        k = int(round(rows * n * outlier_frac))
+        pos = rng.choice(rows * n, size=k, replace=False)
+        sign = rng.integers(0, 2, size=k).astype(np.float32) * 2.0 - 1.0
+        mag = rng.uniform(20.0, 60.0, size=k).astype(np.float32)
+        x.reshape(-1)[pos] = sign * mag
+    out: Dict[str, object] = {"x": _narrow(x, dtype), "smooth": None, "group_index": None}
+    if smooth == "vector":
+        out["smooth"] = torch.from_numpy(rng.uniform(0.5, 2.0, n).astype(np.float32))
+    elif smooth == "experts":
+        out["smooth"] = torch.from_numpy(rng.uniform(0.5, 2.0, (experts, n)).astype(np.float32))
+        counts = rng.multinomial(rows, [1.0 / experts] * experts)
+        out["group_index"] = torch.from_numpy(np.cumsum(counts).astype(np.int32))
+    return out
+
+
+def ada_inputs(B: int, S: int, H: int, seed: int, *, dtype: str = "bfloat16",
+               affine: bool = True, smooth: bool = True) -> Dict[str, object]:
+    """Inputs of one AdaLayerNormQuant call.
+
+    Draw order: x ~ N(0, 1) [B, S, H]; scale, shift ~ N(0, 0.1) [B, 1, H];
+    weight ~ N(1, 0.05) [H]; bias ~ N(0, 0.05) [H]; smooth ~ U(0.5, 2.0) [H]
+    (fp32).  eps = 1e-5.
+    """
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((B, S, H), dtype=np.float32)
+    sc = rng.normal(0.0, 0.1, (B, 1, H)).astype(np.float32)
+    sh = rng.normal(0.0, 0.1, (B, 1, H)).astype(np.float32)
+    w = rng.normal(1.0, 0.05, H).astype(np.float32)
+    b = rng.normal(0.0, 0.05, H).astype(np.float32)
+    sm = rng.uniform(0.5, 2.0, H).astype(np.float32)
+    return {
+        "x": _narrow(x, dtype), "scale": _narrow(sc, dtype), "shift": _narrow(sh, dtype),
+        "weight": _narrow(w, dtype) if affine else None,
+        "bias": _narrow(b, dtype) if affine else None,
+        "smooth": torch.from_numpy(sm) if smooth else None,
+        "eps": 1e-5,
+    }
+
+
+def aq_param_shape(policy: str, m: int, n: int, kdim: int = 1, group_size: int = 128):
+    if policy == "per_tensor":
+        return (1,)
+    if policy == "per_channel":
+        return (1, n)
+    if policy == "per_token":
+        return (m, 1)
+    if kdim == 1:
+        return (m, -(-n // group_size))
+    return (-(-m // group_size), n)
+
+
+def aq_inputs(m: int, n: int, policy: str, seed: int, *, src: str = "int8", kdim: int = 1,
+              group_size: int = 128, offset: bool = True) -> Dict[str, object]:
+    """Inputs of one AntiQuantize call.
+
+    Draw order: src (int8 uniform over [-128, 127], or fp8-e4m3fn from
+    N(0, 4) clipped to +-448 then rounded to nearest even); scale ~ U(0.001,
+    0.05) and offset ~ U(-8, 8), both fp32, in the policy's shape.
+    """
+    rng = np.random.default_rng(seed)
+    if src == "int8":
+        s = torch.from_numpy(rng.integers(-128, 128, (m, n)).astype(np.int8))
+    else:
+        v = np.clip(rng.normal(0.0, 4.0, (m, n)).astype(np.float32), -448.0, 448.0)
+        s = torch.from_numpy(v).to(torch.float8_e4m3fn)
+    shape = aq_param_shape(policy, m, n, kdim, group_size)
+    scale = torch.from_numpy(rng.uniform(0.001, 0.05, shape).astype(np.float32))
+    off = torch.from_numpy(rng.uniform(-8.0, 8.0, shape).astype(np.float32)) if offset else None
+    return {"src": s, "scale": scale, "offset": off, "policy": policy, "kdim": kdim,
+            "group_size": group_size if policy == "per_group" else 0}
+
+
+# Full-size workloads: name -> (op, builder).
+WORKLOADS = {
+    "dq_sym_f16_64x256": (
+        "dynamic_quant",
+        lambda: dict(dq_inputs(64, 256, 1, dtype="float16"), symmetric=True, out="int8")),
+    "dq_sym_smooth_bf16_8192x7168": (
+        "dynamic_quant",
+        lambda: dict(dq_inputs(8192, 7168, 2, smooth="vector", outlier_frac=0.001),
+                     symmetric=True, out="int8")),
+    "dq_moe_asym_int8_bf16_32768x4096": (
+        "dynamic_quant",
+        lambda: dict(dq_inputs(32768, 4096, 3, smooth="experts", experts=64),
+                     symmetric=False, out="int8")),
+    "dq_moe_asym_int4_bf16_32768x4096": (
+        "dynamic_quant",
+        lambda: dict(dq_inputs(32768, 4096, 3, smooth="experts", experts=64),
+                     symmetric=False, out="int4")),
+    "ada_ln_quant_bf16_4x4096x3072": (
+        "ada_layernorm_quant", lambda: ada_inputs(4, 4096, 3072, 4)),
+    "aq_per_tensor_int8_16384x8192": (
+        "antiquantize", lambda: aq_inputs(16384, 8192, "per_tensor", 5)),
+    "aq_per_channel_int8_16384x8192": (
+        "antiquantize", lambda: aq_inputs(16384, 8192, "per_channel", 5)),
+    "aq_per_token_int8_16384x8192": (
+        "antiquantize", lambda: aq_inputs(16384, 8192, "per_token", 5)),
+    "aq_per_group_int8_16384x8192": (
+        "antiquantize", lambda: aq_inputs(16384, 8192, "per_group", 5, group_size=128)),
+    "aq_per_group_fp8e4m3_16384x8192": (
+        "antiquantize",
+        lambda: aq_inputs(16384, 8192, "per_group", 6, src="float8_e4m3fn", group_size=128)),
+}

@@ -1,0 +1,239 @@
+"""CPU oracle for per-token dynamic quantization, AdaLayerNorm-quant and
+AntiQuantize -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, the smoke check in ``__graft_entry__`` and the CPU-baseline
+leg of ``bench.py`` may import this package.  The product path (the HIP
+library and its binding) never calls it, and shares no code with it.
+
+The arithmetic lives in ``dquant_oracle.c`` (plain, single-threaded C with
+one IEEE binary32 rounding per step); this module only marshals numpy / CPU
+torch arrays into it through ctypes.  Each function cites, in the C file,
+the passage of the pages it follows:
+
+* ``dynamic_quant``           -- aclnnDynamicQuantV2, Formula.
+* ``ada_layernorm_modulate``  -- aclnnAdaLayerNormQuant, Formula steps 1-3.
+* ``ada_layernorm_quant``     -- aclnnAdaLayerNormQuant, Formula steps 1-5.
+* ``antiquantize``            -- AntiQuantize, 功能说明 / 表1-表3.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Tuple
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(HERE, "dquant_oracle.c")
+LIBRARY = os.path.join(HERE, "liboracle.so")
+
+# The oracle's own type codes (see the enum in dquant_oracle.c).
+F32, F16, BF16, I8, I4, I32, F8E4M3 = 0, 1, 2, 3, 4, 5, 6
+_OUT_CODES = {"int8": I8, "int4": I4, "int32": I32}
+_FLOAT_CODES = {"float32": F32, "float16": F16, "bfloat16": BF16}
+POLICIES = {"per_tensor": 0, "per_channel": 1, "per_token": 2, "per_group": 3}
+
+CFLAGS = ["-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
+          "-Wall", "-Wextra"]
+
+
+def build(source: str = SOURCE, output: str = LIBRARY) -> str:
+    """Compile the oracle with the host C compiler (no GPU code involved)."""
+    cmd = ["gcc", *CFLAGS, "-o", output, source, "-lm"]
+    subprocess.run(cmd, check=True)
+    return output
+
+
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_int = ctypes.c_int
+_dbl = ctypes.c_double
+
+
+def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
+    lib.oracle_dynamic_quant.argtypes = [_vp, _int, _i64, _i64, _vp, _vp, _i64, _int, _int,
+                                         _vp, _vp, _vp]
+    lib.oracle_dynamic_quant.restype = None
+    lib.oracle_ada_layernorm_modulate.argtypes = [_vp, _int, _i64, _i64, _i64,
+                                                  _vp, _int, _vp, _int, _vp, _int, _vp, _int,
+                                                  _vp, _int, _dbl, _vp]
+    lib.oracle_ada_layernorm_modulate.restype = None
+    lib.oracle_ada_layernorm_quant.argtypes = [_vp, _int, _i64, _i64, _i64,
+                                               _vp, _int, _vp, _int, _vp, _int, _vp, _int,
+                                               _vp, _int, _dbl, _vp, _vp, _vp]
+    lib.oracle_ada_layernorm_quant.restype = None
+    lib.oracle_antiquantize.argtypes = [_vp, _int, _i64, _i64, _vp, _int, _vp, _int,
+                                        _int, _int, _i64, _int, _vp]
+    lib.oracle_antiquantize.restype = None
+    lib.orc_convert_to_f32.argtypes = [_vp, _int, _i64, _vp]
+    lib.orc_convert_to_f32.restype = None
+    lib.orc_convert_from_f32.argtypes = [_vp, _i64, _int, _vp]
+    lib.orc_convert_from_f32.restype = None
+    return lib
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _buffer(t) -> Tuple[Optional[np.ndarray], int]:
+    """Contiguous host buffer and the oracle type code of an array.
+
+    Accepts numpy arrays and CPU torch tensors; 16-bit floats travel as raw
+    bit patterns, since numpy has no bfloat16.
+    """
+    if t is None:
+        return None, F32
+    try:
+        import torch
+    except ImportError:  # pragma: no cover - torch is always present here
+        torch = None
+    if torch is not None and isinstance(t, torch.Tensor):
+        t = t.detach().contiguous().cpu()
+        if t.dtype == torch.bfloat16:
+            return t.view(torch.int16).numpy().view(np.uint16), BF16
+        if t.dtype == torch.float16:
+            return t.view(torch.int16).numpy().view(np.uint16), F16
+        if t.dtype == torch.float8_e4m3fn:
+            return t.view(torch.uint8).numpy(), F8E4M3
+        t = t.numpy()
+    a = np.ascontiguousarray(t)
+    if a.dtype == np.float32:
+        return a, F32
+    if a.dtype == np.float16:
+        return a.view(np.uint16), F16
+    if a.dtype == np.int8:
+        return a, I8
+    if a.dtype == np.int32:
+        return a, I32
+    raise TypeError(f"oracle: unsupported array dtype {a.dtype}")
+
+
+class Oracle:
+    """ctypes front end of one compiled oracle library."""
+
+    def __init__(self, path: str = LIBRARY):
+        self.path = path
+        self.lib = _bind(ctypes.CDLL(path))
+
+    # -- element conversions (pinned against library routines in the tests) --
+    def to_f32(self, t) -> np.ndarray:
+        a, code = _buffer(t)
+        out = np.empty(a.size, dtype=np.float32)
+        self.lib.orc_convert_to_f32(_ptr(a), code, a.size, _ptr(out))
+        return out.reshape(a.shape)
+
+    def from_f32(self, a: np.ndarray, dtype: str) -> np.ndarray:
+        """Round fp32 values to 'bfloat16' or 'float16'; returns raw uint16 bits."""
+        a = np.ascontiguousarray(a, dtype=np.float32)
+        out = np.empty(a.size, dtype=np.uint16)
+        self.lib.orc_convert_from_f32(_ptr(a), a.size, _FLOAT_CODES[dtype], _ptr(out))
+        return out.reshape(a.shape)
+
+    def e4m3_to_f32(self, codes: np.ndarray) -> np.ndarray:
+        a = np.ascontiguousarray(codes, dtype=np.uint8)
+        out = np.empty(a.size, dtype=np.float32)
+        self.lib.orc_convert_to_f32(_ptr(a), F8E4M3, a.size, _ptr(out))
+        return out.reshape(a.shape)
+
+    # -- aclnnDynamicQuantV2 --------------------------------------------------
+    def dynamic_quant(self, x, smooth=None, group_index=None, symmetric=True, out="int8"):
+        """Return (y, scale, offset); offset is None when symmetric.
+
+        x: [..., N] fp16/bf16 (torch CPU tensor or float16 numpy array).
+        y: int8 [..., N] for 'int8'; uint8 [..., N/2] for 'int4' (two codes
+        per byte); uint32 [..., N/8] for 'int32'.
+        """
+        xa, xcode = _buffer(x)
+        shape = xa.shape
+        n = int(shape[-1])
+        rows = int(np.prod(shape[:-1], dtype=np.int64)) if len(shape) > 1 else 1
+        s = None if smooth is None else np.ascontiguousarray(smooth, dtype=np.float32)
+        gi = None if group_index is None else np.ascontiguousarray(group_index, dtype=np.int32)
+        n_exp = 0 if gi is None else gi.size
+        code = _OUT_CODES[out]
+        if out == "int8":
+            y = np.empty(shape, dtype=np.int8)
+        elif out == "int4":
+            y = np.empty(shape[:-1] + (n // 2,), dtype=np.uint8)
+        else:
+            y = np.empty(shape[:-1] + (n // 8,), dtype=np.uint32)
+        scale = np.empty(shape[:-1], dtype=np.float32)
+        offset = None if symmetric else np.empty(shape[:-1], dtype=np.float32)
+        self.lib.oracle_dynamic_quant(_ptr(xa), xcode, rows, n, _ptr(s), _ptr(gi), n_exp,
+                                      1 if symmetric else 0, code, _ptr(y), _ptr(scale),
+                                      _ptr(offset))
+        return y, scale, offset
+
+    # -- aclnnAdaLayerNormQuant -----------------------------------------------
+    def _ada_args(self, x, scale, shift, weight, bias, smooth):
+        xa, xc = _buffer(x)
+        if xa.ndim != 3:
+            raise ValueError("oracle: AdaLayerNorm x must be [B, S, H]")
+        B, S, H = (int(d) for d in xa.shape)
+        sc, scc = _buffer(scale)
+        sh, shc = _buffer(shift)
+        w, wc = _buffer(weight)
+        b, bc = _buffer(bias)
+        sm, smc = _buffer(smooth)
+        keep = (xa, sc, sh, w, b, sm)
+        args = [_ptr(xa), xc, B, S, H, _ptr(sc), scc, _ptr(sh), shc, _ptr(w), wc, _ptr(b), bc,
+                _ptr(sm), smc]
+        return (B, S, H), args, keep
+
+    def ada_layernorm_modulate(self, x, scale, shift, weight=None, bias=None, smooth=None,
+                               eps=1e-5) -> np.ndarray:
+        (B, S, H), args, keep = self._ada_args(x, scale, shift, weight, bias, smooth)
+        y = np.empty((B, S, H), dtype=np.float64)
+        self.lib.oracle_ada_layernorm_modulate(*args, float(eps), _ptr(y))
+        del keep
+        return y
+
+    def ada_layernorm_quant(self, x, scale, shift, weight=None, bias=None, smooth=None,
+                            eps=1e-5, want_y=False):
+        """Return (out int8 [B,S,H], quant_scale fp32 [B,S]) (+ y fp64 if want_y)."""
+        (B, S, H), args, keep = self._ada_args(x, scale, shift, weight, bias, smooth)
+        out = np.empty((B, S, H), dtype=np.int8)
+        qs = np.empty((B, S), dtype=np.float32)
+        y = np.empty((B, S, H), dtype=np.float64) if want_y else None
+        self.lib.oracle_ada_layernorm_quant(*args, float(eps), _ptr(out), _ptr(qs), _ptr(y))
+        del keep
+        return (out, qs, y) if want_y else (out, qs)
+
+    # -- AntiQuantize ---------------------------------------------------------
+    def antiquantize(self, src, scale, offset=None, policy="per_tensor", kdim=1,
+                     group_size=0, dst="bfloat16") -> np.ndarray:
+        """Return dst [m, n]: raw uint16 bits for bf16/fp16, float32 for 'float32'.
+
+        src: int8 [m, n] numpy/torch, or torch float8_e4m3fn, or
+        ('float8_e4m3fn', uint8 codes ndarray).
+        """
+        if isinstance(src, tuple):
+            sa, scode = np.ascontiguousarray(src[1], dtype=np.uint8), F8E4M3
+        else:
+            sa, scode = _buffer(src)
+        if sa.ndim != 2:
+            raise ValueError("oracle: AntiQuantize src must be 2-D")
+        m, n = (int(d) for d in sa.shape)
+        sc, scc = _buffer(scale)
+        of, ofc = _buffer(offset)
+        dcode = {"bfloat16": BF16, "float16": F16, "float32": F32}[dst]
+        out = np.empty((m, n), dtype=np.float32 if dcode == F32 else np.uint16)
+        self.lib.oracle_antiquantize(_ptr(sa), scode, m, n, _ptr(sc), scc, _ptr(of), ofc,
+                                     POLICIES[policy], int(kdim), int(group_size), dcode,
+                                     _ptr(out))
+        return out
+
+
+_default: Optional[Oracle] = None
+
+
+def load() -> Oracle:
+    """The oracle built in-tree; compiled on first use if it is not there."""
+    global _default
+    if _default is None:
+        if not os.path.exists(LIBRARY):
+            build()
+        _default = Oracle(LIBRARY)
+    return _default

@@ -1,0 +1,537 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each ``pin_*`` function takes an ``oracle.Oracle`` and raises AssertionError
+when the oracle disagrees with a value fixed by the pages, by hand-worked
+arithmetic, by a closed form, by an invariant the formulas imply, or by a
+library routine that a special case reduces to.  ``test_oracle_pins.py``
+runs them on the real oracle; ``test_oracle_mutants.py`` runs them on copies
+of the oracle with planted mistakes and expects each copy to fail one.
+
+No expected value here is computed by the oracle itself or by the HIP
+library.
+"""
+from __future__ import annotations
+
+import os
+
+import numpy as np
+import torch
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+f32 = np.float32
+
+
+def _bf16(values):
+    return torch.tensor(values, dtype=torch.float32).to(torch.bfloat16)
+
+
+def _f16(values):
+    return torch.tensor(values, dtype=torch.float32).to(torch.float16)
+
+
+def _bits_to_bf16_f32(bits: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).float().numpy()
+
+
+def _bits_to_f16_f32(bits: np.ndarray) -> np.ndarray:
+    return bits.view(np.float16).astype(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# aclnnDynamicQuantV2 -- hand-worked rows (Formula)
+# ---------------------------------------------------------------------------
+
+def pin_dq_sym_unit_scale_ties(orc):
+    """Symmetric INT8, scale exactly 1: row max |x| = 127, so 127/127 = 1 and
+    every quotient is x itself; round-half-to-even decides the ties
+    (0.5 -> 0, 1.5 -> 2, 2.5 -> 2, -63.5 -> -64, -2.5 -> -2)."""
+    for mk in (_bf16, _f16):
+        x = mk([[127, -63.5, 0.5, 1.5, 2.5, -0.5, -2.5, 3.25]])
+        y, s, o = orc.dynamic_quant(x)
+        assert o is None
+        assert s.tolist() == [1.0]
+        assert y.tolist() == [[127, -64, 0, 2, 2, 0, -2, 3]]
+
+
+def pin_dq_sym_true_division(orc):
+    """x = [1, -2, 0.5, 4]: scale = RN(4/127) = 0x3D010204.  Dividing by that
+    binary32 value gives the quotients 31.75, -63.5, 15.875, 127 exactly
+    (checked by hand: 4/127 rounds down by less than half an ulp of the
+    quotient), so the codes are 32, -64, 16, 127."""
+    y, s, _ = orc.dynamic_quant(_f16([[1, -2, 0.5, 4]]))
+    assert s.view(np.uint32).tolist() == [0x3D010204]
+    assert y.tolist() == [[32, -64, 16, 127]]
+
+
+def pin_dq_sym_smooth_multiplies(orc):
+    """smoothScalesOptional multiplies x element-wise: x = [1, -2, 0.5, 4],
+    smooth = [2, 0.5, 4, 0.25] gives input = [2, -1, 2, 1] (exact), scale =
+    RN(2/127) (the pin above halved), quotients 127, -63.5, 127, 63.5 and
+    codes 127, -64, 127, 64."""
+    y, s, _ = orc.dynamic_quant(_bf16([[1, -2, 0.5, 4]]), smooth=np.array([2, 0.5, 4, 0.25], f32))
+    assert s.view(np.uint32).tolist() == [0x3C810204]
+    assert y.tolist() == [[127, -64, 127, 64]]
+
+
+def pin_dq_asym_int8_rne(orc):
+    """Asymmetric INT8 (scale_opt 255, offset_opt 127): x = [127.5, -127.5, 0,
+    1, 2, -1, 3] has max - min = 255, so scale = 1, offset = 127 - 127.5 =
+    -0.5 and the codes are round(x - 0.5) = [127, -128, -0.5->0, 0.5->0,
+    1.5->2, -1.5->-2, 2.5->2].  Half-away-from-zero would give -1, 1, 3."""
+    y, s, o = orc.dynamic_quant(_bf16([[127.5, -127.5, 0, 1, 2, -1, 3]]), symmetric=False)
+    assert s.tolist() == [1.0] and o.tolist() == [-0.5]
+    assert y.tolist() == [[127, -128, 0, 0, 2, -2, 2]]
+
+
+def pin_dq_asym_int4_nibbles(orc):
+    """Asymmetric INT4 (15, 7): x = [7.5, -7.5, 0, 1, 2, -1.5] -> scale 1,
+    offset -0.5, codes [7, -8, 0, 0, 2, -2]; two codes per byte, the first
+    in the low nibble: 0x87, 0x00, 0xE2."""
+    y, s, o = orc.dynamic_quant(_bf16([[7.5, -7.5, 0, 1, 2, -1.5]]), symmetric=False, out="int4")
+    assert s.tolist() == [1.0] and o.tolist() == [-0.5]
+    assert y.tolist() == [[0x87, 0x00, 0xE2]]
+
+
+def pin_dq_asym_int32_word(orc):
+    """INT32 packs eight codes per word, code i in bits [4i, 4i+3]: codes
+    [7, -8, 0, 0, 2, -2, 1, -1] give 0xF1E20087, whose little-endian bytes
+    equal the INT4 bytes of the same row."""
+    x = _bf16([[7.5, -7.5, 0, 1, 2, -1.5, 1.5, -0.5]])
+    y32, _, _ = orc.dynamic_quant(x, symmetric=False, out="int32")
+    y4, _, _ = orc.dynamic_quant(x, symmetric=False, out="int4")
+    assert y32.tolist() == [[0xF1E20087]]
+    assert y32.view(np.uint8).tolist() == y4.tolist() == [[0x87, 0x00, 0xE2, 0xF1]]
+
+
+def pin_dq_sym_int4_divisor(orc):
+    """Symmetric INT4: the divisor is 7 (the top of the INT4 code range).
+    x = [7, -3.5, 1, 0.5] -> scale 1, codes [7, -4, 1, 0] -> bytes 0xC7 0x01."""
+    y, s, _ = orc.dynamic_quant(_bf16([[7, -3.5, 1, 0.5]]), out="int4")
+    assert s.tolist() == [1.0]
+    assert y.tolist() == [[0xC7, 0x01]]
+
+
+def pin_dq_degenerate_rows(orc):
+    """IEEE propagation plus saturation: an all-zero row (symmetric) has
+    scale 0 and 0/0 = NaN quotients, which map to code 0.  A constant row
+    (asymmetric) has scale 0, offset -inf / +inf / NaN and codes 0."""
+    y, s, _ = orc.dynamic_quant(_bf16([[0, 0, 0, 0]]))
+    assert s.tolist() == [0.0] and y.tolist() == [[0, 0, 0, 0]]
+    x = _bf16([[3, 3, 3, 3], [-2, -2, -2, -2], [0, 0, 0, 0]])
+    y, s, o = orc.dynamic_quant(x, symmetric=False)
+    assert s.tolist() == [0.0, 0.0, 0.0]
+    assert o[0] == -np.inf and o[1] == np.inf and np.isnan(o[2])
+    assert not y.any()
+
+
+# ---------------------------------------------------------------------------
+# aclnnDynamicQuantV2 -- invariants on random rows
+# ---------------------------------------------------------------------------
+
+def _rand_bf16(rng, shape, scale=1.0):
+    return torch.from_numpy((rng.standard_normal(shape) * scale).astype(np.float32)).to(torch.bfloat16)
+
+
+def pin_dq_sym_absmax_and_error(orc):
+    """Symmetric INT8 on random rows: the absmax element maps to +-127 and
+    every element satisfies |in - code * scale| <= scale * (1/2 + 2^-16)
+    (half a step plus the binary32 roundings)."""
+    rng = np.random.default_rng(11)
+    x = _rand_bf16(rng, (64, 200))
+    sm = rng.uniform(0.5, 2.0, 200).astype(f32)
+    y, s, _ = orc.dynamic_quant(x, smooth=sm)
+    v = (x.float().numpy() * sm).astype(np.float64)
+    assert np.all(np.abs(y).max(axis=1) == 127)
+    am = np.abs(v).argmax(axis=1)
+    assert np.all(np.abs(y[np.arange(64), am]) == 127)
+    err = np.abs(v - y.astype(np.float64) * s[:, None].astype(np.float64))
+    assert np.all(err <= s[:, None] * (0.5 + 2.0 ** -16))
+
+
+def pin_dq_asym_extremes(orc):
+    """Asymmetric on random rows: row_max maps to offset_opt and row_min to
+    offset_opt - scale_opt (127 / -128 for INT8, 7 / -8 for INT4), and
+    |in - (code - offset) * scale| <= scale * (1/2 + 2^-14)."""
+    rng = np.random.default_rng(12)
+    x = _rand_bf16(rng, (64, 96), scale=3.0)
+    v = x.float().numpy().astype(np.float64)
+    for out, top, bot in (("int8", 127, -128), ("int4", 7, -8)):
+        y, s, o = orc.dynamic_quant(x, symmetric=False, out=out)
+        c = y.astype(np.int64) if out == "int8" else _unpack_int4(y)
+        r = np.arange(64)
+        assert np.all(c[r, v.argmax(axis=1)] == top)
+        assert np.all(c[r, v.argmin(axis=1)] == bot)
+        rec = (c - o[:, None].astype(np.float64)) * s[:, None].astype(np.float64)
+        assert np.all(np.abs(v - rec) <= s[:, None] * (0.5 + 2.0 ** -14))
+
+
+def _unpack_int4(y: np.ndarray) -> np.ndarray:
+    lo = (y & 0xF).astype(np.int64)
+    hi = (y >> 4).astype(np.int64)
+    lo = np.where(lo >= 8, lo - 16, lo)
+    hi = np.where(hi >= 8, hi - 16, hi)
+    out = np.empty(y.shape[:-1] + (2 * y.shape[-1],), dtype=np.int64)
+    out[..., 0::2] = lo
+    out[..., 1::2] = hi
+    return out
+
+
+def pin_dq_power_of_two_scaling(orc):
+    """Multiplying x (or the smooth scales) by 2^k leaves every code and the
+    offset unchanged and multiplies scale by exactly 2^k (no rounding is
+    introduced by a power of two away from under/overflow)."""
+    rng = np.random.default_rng(13)
+    x = _rand_bf16(rng, (16, 64))
+    sm = rng.uniform(0.5, 2.0, 64).astype(f32)
+    for sym in (True, False):
+        for out in ("int8", "int4"):
+            y0, s0, o0 = orc.dynamic_quant(x, smooth=sm, symmetric=sym, out=out)
+            y1, s1, o1 = orc.dynamic_quant((x.float() * 8).to(torch.bfloat16), smooth=sm,
+                                           symmetric=sym, out=out)
+            y2, s2, o2 = orc.dynamic_quant(x, smooth=sm / 4, symmetric=sym, out=out)
+            assert np.array_equal(y0, y1) and np.array_equal(y0, y2)
+            assert np.array_equal(s1, s0 * 8) and np.array_equal(s2, s0 / 4)
+            if not sym:
+                assert np.array_equal(o0, o1) and np.array_equal(o0, o2)
+
+
+def pin_dq_smooth_one_and_permutation(orc):
+    """smooth = 1 is the same as no smooth; permuting the columns of x and
+    of smooth together permutes the codes and keeps scale and offset."""
+    rng = np.random.default_rng(14)
+    x = _rand_bf16(rng, (8, 48))
+    sm = rng.uniform(0.5, 2.0, 48).astype(f32)
+    perm = rng.permutation(48)
+    for sym in (True, False):
+        a = orc.dynamic_quant(x, symmetric=sym)
+        b = orc.dynamic_quant(x, smooth=np.ones(48, f32), symmetric=sym)
+        assert all(np.array_equal(u, w) for u, w in zip(a, b) if u is not None)
+        c = orc.dynamic_quant(x, smooth=sm, symmetric=sym)
+        d = orc.dynamic_quant(x[:, perm].contiguous(), smooth=sm[perm], symmetric=sym)
+        assert np.array_equal(c[0][:, perm], d[0])
+        assert np.array_equal(c[1], d[1])
+        if not sym:
+            assert np.array_equal(c[2], d[2])
+
+
+def pin_dq_moe_reductions(orc):
+    """MoE: groupIndex holds cumulative per-expert row ends.  Every row must
+    equal the non-MoE result of that row with its own expert's smooth row,
+    with expert e owning rows [gi[e-1], gi[e]), empty experts skipped and
+    rows past gi[E-1] taken by the last expert; E = 1 with gi = [R] equals
+    the non-MoE smooth call."""
+    rng = np.random.default_rng(15)
+    R, N = 12, 32
+    x = _rand_bf16(rng, (R, N))
+    sm = rng.uniform(0.5, 2.0, (4, N)).astype(f32)
+    gi = np.array([3, 3, 7, 10], np.int32)  # expert 1 is empty; rows 10, 11 past the end
+    owner = [0, 0, 0, 2, 2, 2, 2, 3, 3, 3, 3, 3]
+    for sym in (True, False):
+        for out in ("int8", "int4"):
+            y, s, o = orc.dynamic_quant(x, smooth=sm, group_index=gi, symmetric=sym, out=out)
+            for r in range(R):
+                yr, sr, orr = orc.dynamic_quant(x[r:r + 1], smooth=sm[owner[r]],
+                                                symmetric=sym, out=out)
+                assert np.array_equal(y[r:r + 1], yr) and s[r] == sr[0]
+                if not sym:
+                    assert o[r] == orr[0]
+            one = orc.dynamic_quant(x, smooth=sm[2:3], group_index=np.array([R], np.int32),
+                                    symmetric=sym, out=out)
+            ref = orc.dynamic_quant(x, smooth=sm[2], symmetric=sym, out=out)
+            assert all(np.array_equal(u, w) for u, w in zip(one, ref) if u is not None)
+
+
+def pin_dq_leading_dims(orc):
+    """x of rank 3 is quantized per row of its last dimension: the result
+    equals the rank-2 call on the flattened rows."""
+    rng = np.random.default_rng(16)
+    x = _rand_bf16(rng, (3, 5, 16))
+    a = orc.dynamic_quant(x, symmetric=False)
+    b = orc.dynamic_quant(x.reshape(15, 16), symmetric=False)
+    assert np.array_equal(a[0].reshape(15, 16), b[0])
+    assert np.array_equal(a[1].reshape(15), b[1]) and np.array_equal(a[2].reshape(15), b[2])
+
+
+# ---------------------------------------------------------------------------
+# aclnnAdaLayerNormQuant
+# ---------------------------------------------------------------------------
+
+def _ada_params(rng, B, H, dtype=torch.bfloat16):
+    mk = lambda a: torch.from_numpy(a.astype(np.float32)).to(dtype)
+    return (mk(rng.normal(0, 0.1, (B, 1, H))), mk(rng.normal(0, 0.1, (B, 1, H))),
+            mk(rng.normal(1, 0.05, H)), mk(rng.normal(0, 0.05, H)))
+
+
+def pin_ada_layernorm_matches_torch(orc):
+    """With scale = shift = 0 and no smooth, y is LayerNorm(x) with weight and
+    bias, which torch.nn.functional.layer_norm computes in float64
+    (biased variance) to 1e-12."""
+    rng = np.random.default_rng(21)
+    B, S, H = 2, 3, 64
+    x = _rand_bf16(rng, (B, S, H))
+    _, _, w, b = _ada_params(rng, B, H)
+    zero = torch.zeros(B, 1, H, dtype=torch.bfloat16)
+    for eps in (1e-5, 0.5):
+        y = orc.ada_layernorm_modulate(x, zero, zero, w, b, None, eps)
+        ref = torch.nn.functional.layer_norm(x.double(), (H,), w.double(), b.double(), eps)
+        assert np.allclose(y, ref.numpy(), rtol=0, atol=1e-12)
+        y0 = orc.ada_layernorm_modulate(x, zero, zero, None, None, None, eps)
+        ref0 = torch.nn.functional.layer_norm(x.double(), (H,), None, None, eps)
+        assert np.allclose(y0, ref0.numpy(), rtol=0, atol=1e-12)
+
+
+def pin_ada_modulation_special_cases(orc):
+    """y = LN(x) * (1 + scale) + shift, then * smooth, with scale and shift
+    taken from the row's batch.  scale = 1 doubles LN; scale = -1 leaves
+    exactly shift * smooth; scale = 2^k - 1 per column (or per batch)
+    multiplies LN by 2^k; shift enters additively."""
+    rng = np.random.default_rng(22)
+    B, S, H = 2, 2, 32
+    x = _rand_bf16(rng, (B, S, H))
+    sc, sh, w, b = _ada_params(rng, B, H)
+    sm = rng.uniform(0.5, 2.0, H).astype(f32)
+    zero = torch.zeros(B, 1, H, dtype=torch.bfloat16)
+    ln = orc.ada_layernorm_modulate(x, zero, zero, w, b, None)
+    one = torch.ones(B, 1, H, dtype=torch.bfloat16)
+    assert np.array_equal(orc.ada_layernorm_modulate(x, one, zero, w, b, None), 2 * ln)
+    y = orc.ada_layernorm_modulate(x, -one, sh, w, b, sm)
+    exact = sh.double().numpy() * sm.astype(np.float64)
+    assert np.array_equal(y, np.broadcast_to(exact, y.shape))
+    k = rng.integers(-2, 3, H)
+    pw = torch.from_numpy((2.0 ** k - 1).astype(np.float32)).to(torch.bfloat16).expand(B, 1, H)
+    y = orc.ada_layernorm_modulate(x, pw.contiguous(), zero, w, b, None)
+    assert np.allclose(y, ln * 2.0 ** k, rtol=1e-15, atol=0)
+    per_batch = torch.tensor([0.0, 3.0], dtype=torch.bfloat16).reshape(B, 1, 1).expand(B, 1, H)
+    y = orc.ada_layernorm_modulate(x, per_batch.contiguous(), zero, w, b, None)
+    assert np.allclose(y, ln * np.array([1.0, 4.0]).reshape(B, 1, 1), rtol=1e-15, atol=0)
+    y = orc.ada_layernorm_modulate(x, zero, sh, w, b, None)
+    assert np.allclose(y - ln, np.broadcast_to(sh.double().numpy(), y.shape), rtol=0, atol=1e-15)
+    y = orc.ada_layernorm_modulate(x, zero, zero, w, b, sm)
+    assert np.allclose(y, ln * sm.astype(np.float64), rtol=1e-15, atol=0)
+
+
+def pin_ada_worked_row(orc):
+    """Row [1, 2, 3, 4], eps 1e-5, no affine or modulation: LN is
+    [-1.5, -0.5, 0.5, 1.5] / sqrt(1.25 + eps), so the codes are
+    round(127 * [-1, -1/3, 1/3, 1]) = [-127, -42, 42, 127]; a constant row
+    normalizes to 0, leaving y = bias * (1 + scale) + shift."""
+    x = _bf16([[[1, 2, 3, 4]]])
+    z = torch.zeros(1, 1, 4, dtype=torch.bfloat16)
+    out, qs = orc.ada_layernorm_quant(x, z, z, None, None, None, 1e-5)
+    assert out.tolist() == [[[-127, -42, 42, 127]]]
+    assert np.isclose(qs[0, 0], 1.5 / np.sqrt(1.25 + 1e-5) / 127, rtol=1e-6)
+    xc = _bf16([[[0.75] * 4]])
+    bias = _bf16([0.5, -1, 2, 0.25])
+    sc = _bf16([[[1, 0, -0.5, 3]]])
+    sh = _bf16([[[0.25, 0.5, -1, 0]]])
+    y = orc.ada_layernorm_modulate(xc, sc, sh, None, bias, None)
+    assert y.tolist() == [[[1.25, -0.5, 0.0, 1.0]]]
+
+
+def pin_ada_quant_matches_dq_sym(orc):
+    """Steps 4-5 are symmetric INT8 dynamic quantization of y.  With
+    scale = -1, y = shift * smooth exactly (a bf16 times an fp32 is exact in
+    float64), so codes and quantScale must equal DynamicQuant's symmetric
+    INT8 result for x = shift and the same smooth scales (hand-pinned
+    above), row by row."""
+    rng = np.random.default_rng(23)
+    B, S, H = 2, 3, 40
+    x = _rand_bf16(rng, (B, S, H))
+    _, sh, w, b = _ada_params(rng, B, H)
+    sm = rng.uniform(0.5, 2.0, H).astype(f32)
+    minus = -torch.ones(B, 1, H, dtype=torch.bfloat16)
+    out, qs = orc.ada_layernorm_quant(x, minus, sh, w, b, sm)
+    yd, sd, _ = orc.dynamic_quant(sh.reshape(B, H), smooth=sm)
+    for s in range(S):
+        assert np.array_equal(out[:, s, :], yd)
+        assert np.array_equal(qs[:, s], sd)
+
+
+def pin_ada_absmax_code(orc):
+    """Every row's absmax element quantizes to +-127 and all codes reproduce
+    y within half a step (plus binary32 rounding)."""
+    rng = np.random.default_rng(24)
+    B, S, H = 2, 8, 96
+    x = _rand_bf16(rng, (B, S, H))
+    sc, sh, w, b = _ada_params(rng, B, H)
+    sm = rng.uniform(0.5, 2.0, H).astype(f32)
+    out, qs, y = orc.ada_layernorm_quant(x, sc, sh, w, b, sm, want_y=True)
+    assert np.all(np.abs(out).max(axis=2) == 127)
+    err = np.abs(y - out.astype(np.float64) * qs[..., None].astype(np.float64))
+    assert np.all(err <= qs[..., None] * (0.5 + 2.0 ** -16))
+
+
+# ---------------------------------------------------------------------------
+# AntiQuantize
+# ---------------------------------------------------------------------------
+
+def _golden_identity_row():
+    with open(os.path.join(GOLDEN, "antiquantize_identity_example.txt")) as f:
+        rows = [ln.split() for ln in f if ln.strip() and not ln.startswith("#")]
+    return np.array([int(v) for v in rows[0]], dtype=np.int8)
+
+
+def pin_aq_page_identity_example(orc):
+    """The page's worked example: scale 1 and offset 0 (scalar for
+    PER_TENSOR, vectors otherwise) leave dst equal to src."""
+    row = _golden_identity_row()
+    m, n = 3, row.size
+    src = np.stack([row, row[::-1], -row]).astype(np.int8)
+    cases = {
+        "per_tensor": (np.ones(1, f32), np.zeros(1, f32), {}),
+        "per_channel": (np.ones((1, n), f32), np.zeros((1, n), f32), {}),
+        "per_token": (np.ones((m, 1), f32), np.zeros((m, 1), f32), {}),
+        "per_group": (np.ones((m, 1), f32), np.zeros((m, 1), f32), {"kdim": 1, "group_size": n}),
+    }
+    for pol, (s, o, kw) in cases.items():
+        for dst, widen in (("float16", _bits_to_f16_f32), ("bfloat16", _bits_to_bf16_f32)):
+            d = orc.antiquantize(src, s, o, policy=pol, dst=dst, **kw)
+            assert np.array_equal(widen(d), src.astype(np.float32)), (pol, dst)
+            d_half_params = orc.antiquantize(src, s.astype(np.float16), o.astype(np.float16),
+                                             policy=pol, dst=dst, **kw)
+            assert np.array_equal(d_half_params, d)
+
+
+def pin_aq_policy_reductions(orc):
+    """PER_GROUP with kDim=1 and groupSize >= n is PER_TOKEN; kDim=0 and
+    groupSize >= m is PER_CHANNEL; PER_CHANNEL / PER_TOKEN with constant
+    vectors are PER_TENSOR; a PER_GROUP column block (kDim=1) is PER_TOKEN on
+    that block with that group's column, including a short last group."""
+    rng = np.random.default_rng(31)
+    m, n, gs = 6, 80, 32  # three groups along n, the last one 16 wide
+    src = rng.integers(-128, 128, (m, n)).astype(np.int8)
+    s_tok = rng.uniform(0.001, 0.05, (m, 1)).astype(f32)
+    o_tok = rng.uniform(-8, 8, (m, 1)).astype(f32)
+    s_ch = rng.uniform(0.001, 0.05, (1, n)).astype(f32)
+    o_ch = rng.uniform(-8, 8, (1, n)).astype(f32)
+    tok = orc.antiquantize(src, s_tok, o_tok, "per_token")
+    assert np.array_equal(orc.antiquantize(src, s_tok, o_tok, "per_group", 1, n), tok)
+    assert np.array_equal(orc.antiquantize(src, s_tok, o_tok, "per_group", 1, 4 * n), tok)
+    ch = orc.antiquantize(src, s_ch, o_ch, "per_channel")
+    assert np.array_equal(orc.antiquantize(src, s_ch, o_ch, "per_group", 0, m), ch)
+    assert np.array_equal(orc.antiquantize(src, s_ch, o_ch, "per_group", 0, 64), ch)
+    t = orc.antiquantize(src, s_tok[:1, 0], o_tok[:1, 0], "per_tensor")
+    assert np.array_equal(orc.antiquantize(src, np.repeat(s_tok[:1], n, 1),
+                                           np.repeat(o_tok[:1], n, 1), "per_channel"), t)
+    assert np.array_equal(orc.antiquantize(src, np.repeat(s_tok[:1], m, 0),
+                                           np.repeat(o_tok[:1], m, 0), "per_token"), t)
+    G = -(-n // gs)
+    s_g = rng.uniform(0.001, 0.05, (m, G)).astype(f32)
+    o_g = rng.uniform(-8, 8, (m, G)).astype(f32)
+    g = orc.antiquantize(src, s_g, o_g, "per_group", 1, gs)
+    for k in range(G):
+        blk = slice(k * gs, min(n, (k + 1) * gs))
+        ref = orc.antiquantize(np.ascontiguousarray(src[:, blk]), s_g[:, k:k + 1].copy(),
+                               o_g[:, k:k + 1].copy(), "per_token")
+        assert np.array_equal(g[:, blk], ref), k
+    mg = 70  # kDim = 0: groups along m, the last one short
+    src0 = rng.integers(-128, 128, (mg, 16)).astype(np.int8)
+    G0 = -(-mg // gs)
+    s0 = rng.uniform(0.001, 0.05, (G0, 16)).astype(f32)
+    o0 = rng.uniform(-8, 8, (G0, 16)).astype(f32)
+    g0 = orc.antiquantize(src0, s0, o0, "per_group", 0, gs)
+    for k in range(G0):
+        blk = slice(k * gs, min(mg, (k + 1) * gs))
+        ref = orc.antiquantize(np.ascontiguousarray(src0[blk]), s0[k:k + 1].copy(),
+                               o0[k:k + 1].copy(), "per_channel")
+        assert np.array_equal(g0[blk], ref), k
+
+
+def pin_aq_power_of_two_closed_form(orc):
+    """With scale 2^k and an integer offset, (src + offset) * scale is exact
+    in binary32 and, for |src + offset| < 256, in bf16 and fp16 too; so dst
+    equals (src + offset) * 2^k, checked for every int8 code.  Without an
+    offset dst = src * 2^k."""
+    src = np.arange(-128, 128, dtype=np.int8).reshape(4, 64)
+    for k, off in ((0, 0), (-3, 5), (2, -7), (-10, 100)):
+        s = np.full(1, 2.0 ** k, f32)
+        o = np.full(1, off, f32)
+        want = (src.astype(np.float64) + off) * 2.0 ** k
+        if np.abs(src.astype(np.int64) + off).max() < 256:
+            for dst, widen in (("bfloat16", _bits_to_bf16_f32), ("float16", _bits_to_f16_f32)):
+                d = widen(orc.antiquantize(src, s, o, "per_tensor", dst=dst))
+                assert np.array_equal(d.astype(np.float64), want), (k, off, dst)
+        d32 = orc.antiquantize(src, s, o, "per_tensor", dst="float32")
+        assert np.array_equal(d32.astype(np.float64), want)
+        d32 = orc.antiquantize(src, s, None, "per_tensor", dst="float32")
+        assert np.array_equal(d32.astype(np.float64), src * 2.0 ** k)
+
+
+def pin_aq_fp8_source(orc):
+    """An fp8-e4m3fn source is decoded exactly: with scale 1 and offset 0
+    the fp32 result equals torch's float8_e4m3fn -> float32 decode for all
+    256 codes (NaN codes stay NaN)."""
+    codes = np.arange(256, dtype=np.uint8).reshape(8, 32)
+    d = orc.antiquantize(("float8_e4m3fn", codes), np.ones(1, f32), np.zeros(1, f32),
+                         "per_tensor", dst="float32")
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(d), nan)
+    assert np.array_equal(d[~nan], ref[~nan])
+
+
+def pin_roundtrip_dq_asym_aq_token(orc):
+    """Round trip: AntiQuantize PER_TOKEN of DynamicQuant's asymmetric INT8
+    output, with scale = scaleOut and offset = -offsetOut, reproduces x to
+    within half a quantization step plus the binary32 roundings of both ops
+    and the final bf16 rounding.  This ties the reading dst = (src +
+    offset) * scale to DynamicQuant's y = x / scale + offset."""
+    rng = np.random.default_rng(41)
+    x = _rand_bf16(rng, (32, 128), scale=2.0)
+    y, s, o = orc.dynamic_quant(x, symmetric=False)
+    d = orc.antiquantize(y, s[:, None].copy(), -o[:, None], "per_token", dst="bfloat16")
+    xr = _bits_to_bf16_f32(d).astype(np.float64)
+    xv = x.float().numpy().astype(np.float64)
+    ulp = np.abs(xr) * 2.0 ** -8
+    assert np.all(np.abs(xr - xv) <= s[:, None] * (0.5 + 2.0 ** -14) + ulp)
+
+
+# ---------------------------------------------------------------------------
+# Element conversions against library routines
+# ---------------------------------------------------------------------------
+
+def _interesting_f32(rng, n):
+    with np.errstate(over="ignore"):
+        a = rng.standard_normal(n).astype(f32) * np.exp2(rng.integers(-140, 128, n)).astype(f32)
+    bits = rng.integers(0, 2 ** 32, n, dtype=np.uint64).astype(np.uint32)
+    ties = (bits & np.uint32(0xFFFF0000)) | np.uint32(0x8000)
+    specials = np.array([0.0, -0.0, np.inf, -np.inf, 65504, 65519.99, 65520, 65536, 6.1e-5,
+                         5.96e-8, 2.98e-8, 2.99e-8, 3.4e38, 1e-45, 448, 0.5, 1.5, 2.5], f32)
+    return np.concatenate([a, bits.view(f32), ties.view(f32), specials])
+
+
+def pin_conversions_against_libraries(orc):
+    """bf16 rounding equals torch's float32 -> bfloat16 cast; fp16 rounding
+    equals numpy's float32 -> float16 cast; widening of both equals torch's;
+    the e4m3fn decode equals torch's float8_e4m3fn -> float32 for all 256
+    codes (0x7E = 448, 0x01 = 2^-9, 0x08 = 2^-6, 0x7F / 0xFF NaN)."""
+    rng = np.random.default_rng(51)
+    a = _interesting_f32(rng, 20000)
+    fin = ~np.isnan(a)
+    bf = orc.from_f32(a, "bfloat16")
+    ref_bf = torch.from_numpy(a.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(bf[fin], ref_bf[fin])
+    assert np.all(np.isnan(_bits_to_bf16_f32(bf[~fin])))
+    h = orc.from_f32(a, "float16")
+    with np.errstate(over="ignore"):
+        ref_h = a.astype(np.float16).view(np.uint16)
+    assert np.array_equal(h[fin], ref_h[fin])
+    bits16 = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    w_bf = orc.to_f32(torch.from_numpy(bits16.view(np.int16).copy()).view(torch.bfloat16))
+    ref = torch.from_numpy(bits16.view(np.int16).copy()).view(torch.bfloat16).float().numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(w_bf), nan) and np.array_equal(w_bf[~nan], ref[~nan])
+    w_h = orc.to_f32(bits16.view(np.float16))
+    ref = bits16.view(np.float16).astype(np.float32)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(w_h), nan) and np.array_equal(w_h[~nan], ref[~nan])
+    codes = np.arange(256, dtype=np.uint8)
+    e = orc.e4m3_to_f32(codes)
+    ref = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).float().numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(e), nan) and np.array_equal(e[~nan], ref[~nan])
+    assert e[0x7E] == 448 and e[0x01] == 2.0 ** -9 and e[0x08] == 2.0 ** -6
+    assert np.isnan(e[0x7F]) and np.isnan(e[0xFF])
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

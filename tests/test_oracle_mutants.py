@@ -1,0 +1,94 @@
+"""Planted mistakes in a copy of the oracle must each fail a pin.
+
+Every mutant is a plausible slip (a dropped term, a wrong sign, divisor,
+index or rounding rule) applied textually to a temporary copy of
+oracle/dquant_oracle.c, compiled with the oracle's own flags and run
+against the pins in oracle_pins.py.  The real oracle is never modified.
+"""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+import oracle
+import oracle_pins
+
+SRC = oracle.SOURCE
+
+MUTANTS = [
+    ("sym_divisor_scale_opt", "float sc = amax / offset_opt;", "float sc = amax / scale_opt;"),
+    ("asym_offset_sign", "float off = offset_opt - q_hi;", "float off = q_hi - offset_opt;"),
+    ("asym_offset_subtracted", "float t = q + off;", "float t = q - off;"),
+    ("asym_range_uses_max_only", "float range = hi - lo;", "float range = hi;"),
+    ("asym_qhi_from_min", "float q_hi = hi / sc;", "float q_hi = lo / sc;"),
+    ("round_half_away", "float r = nearbyintf(t);", "float r = roundf(t);"),
+    ("nan_to_low", "if (isnan(t))\n        return 0;", "if (isnan(t))\n        return lo;"),
+    ("int4_nibble_order",
+     "yr[k] = (uint8_t)((c[2 * k] & 0xF) | ((c[2 * k + 1] & 0xF) << 4));",
+     "yr[k] = (uint8_t)((c[2 * k + 1] & 0xF) | ((c[2 * k] & 0xF) << 4));"),
+    ("int32_word_order", "<< (4 * i);", "<< (4 * (7 - i));"),
+    ("expert_le", "if (r < (int64_t)gi[e])", "if (r <= (int64_t)gi[e])"),
+    ("expert_tail_first", "return n_experts - 1;\n}", "return 0;\n}"),
+    ("smooth_row_index", "s = smooth + e * n;", "s = smooth + e;"),
+    ("smooth_divides", "v[j] = s ? xv * s[j] : xv;", "v[j] = s ? xv / s[j] : xv;"),
+    ("absmax_no_abs", "float a = fabsf(v[j]);", "float a = v[j];"),
+    ("ada_unbiased_var", "double var = ss / (double)H;", "double var = ss / (double)(H - 1);"),
+    ("ada_no_eps", "double rstd = 1.0 / sqrt(var + eps);", "double rstd = 1.0 / sqrt(var);"),
+    ("ada_modulate_without_one", "double yv = ln * (1.0 + sc) + sh;", "double yv = ln * sc + sh;"),
+    ("ada_shift_dropped", "double yv = ln * (1.0 + sc) + sh;", "double yv = ln * (1.0 + sc);"),
+    ("ada_bias_times_weight", "double ln = (xv - mean) * rstd * w + bb;",
+     "double ln = ((xv - mean) * rstd + bb) * w;"),
+    ("ada_smooth_dropped", "yv = yv * (double)load_as_f32(smooth, smooth_dtype, j);", "yv = yv;"),
+    ("ada_batch_index", "double sc = (double)load_as_f32(scale, scale_dtype, b * H + j);",
+     "double sc = (double)load_as_f32(scale, scale_dtype, j);"),
+    ("ada_divisor_128", "float qs = amax / 127.0f;", "float qs = amax / 128.0f;"),
+    ("aq_offset_sign", "float u = v + o;", "float u = v - o;"),
+    ("aq_group_mod", "p = i * ((n + group_size - 1) / group_size) + j / group_size;",
+     "p = i * ((n + group_size - 1) / group_size) + j % group_size;"),
+    ("aq_group_floor_count", "p = i * ((n + group_size - 1) / group_size) + j / group_size;",
+     "p = i * (n / group_size) + j / group_size;"),
+    ("aq_kdim0_index", "p = (i / group_size) * n + j;", "p = (i % group_size) * n + j;"),
+    ("aq_channel_is_token", "else if (policy == ORC_PER_CHANNEL)\n                p = j;",
+     "else if (policy == ORC_PER_CHANNEL)\n                p = i;"),
+    ("bf16_ties_up", "if (lower > 0x8000u || (lower == 0x8000u && (upper & 1u)))",
+     "if (lower >= 0x8000u)"),
+    ("f16_subnormal_quantum", "double q = nearbyint(ldexp(a, 24));",
+     "double q = nearbyint(ldexp(a, 23));"),
+    ("f16_trunc", "double q = nearbyint(ldexp(a, 10 - E));", "double q = floor(ldexp(a, 10 - E));"),
+    ("e4m3_bias8", "v = ldexp((double)(8 + f), e - 10);", "v = ldexp((double)(8 + f), e - 11);"),
+    ("e4m3_no_subnormal", "v = ldexp((double)f, -9);", "v = 0.0;"),
+    ("bf16_widen_shift", "return bits_to_f32((uint32_t)h << 16);",
+     "return bits_to_f32((uint32_t)h << 15);"),
+]
+
+
+def _run_pins(orc):
+    failed = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(orc)
+        except Exception as e:  # noqa: BLE001 - any failure counts as caught
+            failed.append((pin.__name__, type(e).__name__))
+            break
+    return failed
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, name, old, new):
+    text = open(SRC, encoding="utf-8").read()
+    assert text.count(old) == 1, f"mutation anchor for {name} must occur exactly once"
+    mutant_src = tmp_path / "mutant.c"
+    mutant_src.write_text(text.replace(old, new), encoding="utf-8")
+    lib = tmp_path / "libmutant.so"
+    oracle.build(str(mutant_src), str(lib))
+    failed = _run_pins(oracle.Oracle(str(lib)))
+    assert failed, f"mutant {name} passed every pin"
+
+
+def test_unmutated_copy_passes(tmp_path):
+    src = tmp_path / "copy.c"
+    shutil.copy(SRC, src)
+    lib = tmp_path / "libcopy.so"
+    oracle.build(str(src), str(lib))
+    assert _run_pins(oracle.Oracle(str(lib))) == []
