@@ -1,0 +1,316 @@
+"""Benchmark of libdquant on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAME] [--no-extra]
+
+Headline (the JSON line's "value"): symmetric INT8 DynamicQuant with fp32
+smooth scales on bf16 x [8192, 7168] with 0.1 % outliers -- achieved HBM
+GB/s on the algorithmic bytes (x read once, smooth read once, codes and
+scales written once), plus rows/s.
+
+One step is one call of the op on one batch.  Inputs sit in HBM before the
+timed region; consecutive steps rotate over independent buffer sets whose
+total exceeds 1 GiB, so the 256 MB Infinity Cache cannot serve a step from
+the previous one.  Every launch in the timed region is bracketed by HIP
+events on the stream it runs on; "roofline.achieved" is the algorithmic
+bytes of one launch over the mean event-measured launch time.  The other
+workloads (MoE asymmetric INT8/INT4, AdaLayerNorm-quant, AntiQuantize in
+every policy, the tiny fp16 case) are measured the same way and reported
+under "workloads"; a plain device copy gives the achievable-bandwidth
+ceiling.  "cpu_baseline" is the single-threaded CPU oracle timed on the
+host over a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import int4_quantization_amd as dq  # noqa: E402
+from int4_quantization_amd import synth  # noqa: E402
+
+PEAK_GBPS = 8000.0           # MI355X HBM3E
+ROTATE_BYTES = 1 << 30       # buffer-set rotation footprint (> 4x the 256 MB MALL)
+HEADLINE = "dq_sym_smooth_bf16_8192x7168"
+METRIC = "achieved HBM GB/s (% of peak) + rows/s, per-token bf16→int8 dynamic quant"
+
+
+def nbytes(t) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+# ---------------------------------------------------------------------------
+# Workload preparation: device buffer sets and one launch per step.
+# ---------------------------------------------------------------------------
+
+class Work:
+    """One workload: `sets` independent device buffer sets, a launch function
+    running the op on set i, the algorithmic bytes and rows of one call."""
+
+    def __init__(self, name, op, host, dev):
+        self.name = name
+        self.op = op
+        self.host = host
+        if op == "dynamic_quant":
+            x = host["x"]
+            n = x.shape[-1]
+            rows = x.numel() // n
+            out = host["out"]
+            ybytes = {"int8": rows * n, "int4": rows * n // 2, "int32": rows * n // 2}[out]
+            self.alg_bytes = (nbytes(x) + nbytes(host["smooth"]) + nbytes(host["group_index"])
+                              + ybytes + rows * 4 * (1 if host["symmetric"] else 2))
+            self.rows = rows
+            per_set = nbytes(x) + ybytes
+        elif op == "ada_layernorm_quant":
+            x = host["x"]
+            B, S, H = x.shape
+            self.rows = B * S
+            self.alg_bytes = (nbytes(x) + sum(nbytes(host[k]) for k in
+                                              ("scale", "shift", "weight", "bias", "smooth"))
+                              + B * S * H + B * S * 4)
+            per_set = nbytes(x) + B * S * H
+        else:
+            src = host["src"]
+            m, n = src.shape
+            self.rows = m
+            dbytes = m * n * 2
+            self.alg_bytes = nbytes(src) + nbytes(host["scale"]) + nbytes(host["offset"]) + dbytes
+            per_set = nbytes(src) + dbytes
+        self.sets = int(max(1, min(16, -(-ROTATE_BYTES // max(per_set, 1)))))
+        if per_set * self.sets > 6 * (1 << 30):
+            self.sets = max(1, (6 << 30) // per_set)
+        self._alloc(dev)
+
+    def _alloc(self, dev):
+        h = self.host
+        self.bufs = []
+        if self.op == "dynamic_quant":
+            xd = h["x"].to(dev)
+            sm = None if h["smooth"] is None else h["smooth"].to(dev)
+            gi = None if h["group_index"] is None else h["group_index"].to(dev)
+            for i in range(self.sets):
+                x = xd if i == 0 else xd.clone()
+                lead = tuple(x.shape[:-1])
+                n = x.shape[-1]
+                out = h["out"]
+                y = (torch.empty(x.shape, dtype=torch.int8, device=dev) if out == "int8" else
+                     torch.empty(lead + (n // 2,), dtype=torch.uint8, device=dev))
+                sc = torch.empty(lead, dtype=torch.float32, device=dev)
+                of = None if h["symmetric"] else torch.empty(lead, dtype=torch.float32, device=dev)
+                self.bufs.append((x, sm, gi, y, sc, of))
+        elif self.op == "ada_layernorm_quant":
+            p = {k: (None if h[k] is None else h[k].to(dev))
+                 for k in ("x", "scale", "shift", "weight", "bias", "smooth")}
+            for i in range(self.sets):
+                x = p["x"] if i == 0 else p["x"].clone()
+                B, S, H = x.shape
+                out = torch.empty(x.shape, dtype=torch.int8, device=dev)
+                qs = torch.empty((B, S), dtype=torch.float32, device=dev)
+                self.bufs.append((x, p, out, qs))
+        else:
+            src0 = h["src"].to(dev)
+            sc = h["scale"].to(dev)
+            of = None if h["offset"] is None else h["offset"].to(dev)
+            for i in range(self.sets):
+                src = src0 if i == 0 else src0.clone()
+                dst = torch.empty(src.shape, dtype=torch.bfloat16, device=dev)
+                self.bufs.append((src, sc, of, dst))
+
+    def launch(self, i):
+        b = self.bufs[i % self.sets]
+        h = self.host
+        if self.op == "dynamic_quant":
+            x, sm, gi, y, sc, of = b
+            ws, ex = dq.dq_dynamic_quant_get_workspace_size(x, sm, gi, h["symmetric"], y, sc, of,
+                                                            h["out"])
+            dq.dq_dynamic_quant(None, ws, ex)
+        elif self.op == "ada_layernorm_quant":
+            x, p, out, qs = b
+            ws, ex = dq.dq_ada_layernorm_quant_get_workspace_size(
+                x, p["scale"], p["shift"], p["weight"], p["bias"], p["smooth"], h["eps"], out, qs)
+            dq.dq_ada_layernorm_quant(None, ws, ex)
+        else:
+            src, sc, of, dst = b
+            ws, ex = dq.dq_antiquantize_get_workspace_size(src, sc, of, h["policy"], h["kdim"],
+                                                           h["group_size"], dst)
+            dq.dq_antiquantize(None, ws, ex)
+
+    def free(self):
+        self.bufs = []
+
+
+def make_work(name, dev) -> Work:
+    op, builder = synth.WORKLOADS[name]
+    return Work(name, op, builder(), dev)
+
+
+def time_work(w: Work, steps: int, warmup: int):
+    """Warm up, then time exactly `steps` launches: wall time between two
+    synchronizations, and per-launch HIP events on the launch stream."""
+    for i in range(warmup):
+        w.launch(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        w.launch(warmup + i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    lat = np.array([a.elapsed_time(b) for a, b in ev]) * 1e-3  # seconds per launch
+    return wall, lat
+
+
+def summarize(w: Work, wall: float, lat: np.ndarray, steps: int) -> dict:
+    mean = float(lat.mean())
+    return {
+        "op": w.op,
+        "alg_bytes": int(w.alg_bytes),
+        "rows": int(w.rows),
+        "us_mean": mean * 1e6,
+        "us_p10": float(np.percentile(lat, 10)) * 1e6,
+        "us_p50": float(np.percentile(lat, 50)) * 1e6,
+        "us_p90": float(np.percentile(lat, 90)) * 1e6,
+        "gbps_kernel": w.alg_bytes / mean / 1e9,
+        "pct_peak_kernel": 100.0 * w.alg_bytes / mean / 1e9 / PEAK_GBPS,
+        "gbps_wall": w.alg_bytes * steps / wall / 1e9,
+        "rows_per_s": w.rows / mean,
+        "buffer_sets": w.sets,
+    }
+
+
+def copy_ceiling(dev, steps: int = 50) -> float:
+    """Plain device copy of 512 MiB (read + write = 1 GiB of traffic)."""
+    nb = 512 << 20
+    src = torch.empty(nb, dtype=torch.uint8, device=dev).random_(0, 255)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dq.dq_copy_probe(dst, src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        dq.dq_copy_probe(dst, src)
+    b.record()
+    torch.cuda.synchronize()
+    t = a.elapsed_time(b) * 1e-3 / steps
+    return 2 * nb / t / 1e9
+
+
+def cpu_baseline(name: str, max_rows: int) -> dict:
+    """Time the single-threaded CPU oracle on the first rows of a workload."""
+    import oracle
+    orc = oracle.load()
+    op, builder = synth.WORKLOADS[name]
+    h = builder()
+    if op != "dynamic_quant":
+        raise ValueError("cpu baseline is taken on the DynamicQuant headline")
+    x = h["x"]
+    rows = min(max_rows, x.shape[0])
+    xs = x[:rows].contiguous()
+    sm = None if h["smooth"] is None else h["smooth"].numpy()
+    t0 = time.perf_counter()
+    orc.dynamic_quant(xs, sm, None, h["symmetric"], h["out"])
+    dt = time.perf_counter() - t0
+    n = x.shape[1]
+    alg = rows * n * 2 + nbytes(h["smooth"]) + rows * n + rows * 4
+    return {"value": alg / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{rows} of {x.shape[0]} rows of {name} (single-threaded C oracle, "
+                      f"{dt:.2f} s)", "rows_per_s": rows / dt}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--only", default=None, help="time only this workload (profiling runs)")
+    ap.add_argument("--no-extra", action="store_true", help="headline workload only")
+    ap.add_argument("--cpu-rows", type=int, default=8192)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the ops are row-independent and need no collective; "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+
+    if args.only:
+        w = make_work(args.only, dev)
+        wall, lat = time_work(w, args.steps, args.warmup)
+        print(json.dumps({"workload": args.only, **summarize(w, wall, lat, args.steps)}), flush=True)
+        return
+
+    w = make_work(HEADLINE, dev)
+    wall, lat = time_work(w, args.steps, args.warmup)
+    head = summarize(w, wall, lat, args.steps)
+    w.free()
+    print(f"# {HEADLINE}: {head['gbps_kernel']:.0f} GB/s ({head['pct_peak_kernel']:.1f}% of peak), "
+          f"{head['us_mean']:.2f} us/launch", file=sys.stderr, flush=True)
+    ceiling = copy_ceiling(dev)
+    print(f"# copy ceiling {ceiling:.0f} GB/s", file=sys.stderr, flush=True)
+
+    extra = {}
+    if not args.no_extra:
+        for name in synth.WORKLOADS:
+            if name == HEADLINE:
+                continue
+            wk = make_work(name, dev)
+            wl, lt = time_work(wk, args.steps, args.warmup)
+            extra[name] = summarize(wk, wl, lt, args.steps)
+            wk.free()
+            torch.cuda.empty_cache()
+            print(f"# {name}: {extra[name]['gbps_kernel']:.0f} GB/s "
+                  f"({extra[name]['pct_peak_kernel']:.1f}%), {extra[name]['us_mean']:.2f} us",
+                  file=sys.stderr, flush=True)
+
+    cpu = cpu_baseline(HEADLINE, args.cpu_rows)
+    traffic = None
+    prof = os.path.join(ROOT, "profiles", "traffic.json")
+    if os.path.exists(prof):
+        with open(prof) as f:
+            traffic = json.load(f).get(HEADLINE)
+    line = {
+        "metric": METRIC,
+        "value": round(head["alg_bytes"] * args.steps / wall / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": HEADLINE, "rows": 8192, "n": 7168, "x": "bf16", "out": "int8",
+                   "symmetric": True, "smooth": "fp32 [7168]", "outliers": "0.1% +-U(20,60)"},
+        "pct_of_peak": round(100.0 * head["alg_bytes"] * args.steps / wall / 1e9 / PEAK_GBPS, 2),
+        "rows_per_s": head["rows"] * args.steps / wall,
+        "roofline": {"bound": "hbm", "achieved": round(head["gbps_kernel"], 2), "peak": PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(head["gbps_kernel"] / PEAK_GBPS, 4),
+                     "traffic": traffic, "kernel_us_mean": round(head["us_mean"], 3),
+                     "alg_bytes_per_launch": head["alg_bytes"]},
+        "cpu_baseline": cpu,
+        "copy_ceiling_gbps": round(ceiling, 1),
+        "headline_detail": head,
+        "workloads": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,232 @@
+/*
+ * dquant.h -- C ABI of libdquant: per-token dynamic quantization, its
+ * AdaLayerNorm fusion and AntiQuantize on AMD MI355X (gfx950).
+ *
+ * Calling convention (after the two-phase form of the aclnn host ops,
+ * "Each operator has two calls": a get-workspace-size call that returns
+ * the workspace size and an executor holding the computation, then the
+ * execute call):
+ *
+ *   1. dq_<op>_get_workspace_size(...) validates every argument on the
+ *      host, picks the kernel variant and launch geometry and returns an
+ *      executor plus the workspace size in bytes.  It makes no HIP call and
+ *      touches no device memory, so it is usable without a GPU.
+ *   2. dq_<op>(workspace, workspace_size, executor, stream) enqueues the
+ *      kernel(s) on `stream` and returns without synchronizing.
+ *
+ * Ownership
+ *   - The caller owns every tensor buffer, the workspace and the stream.
+ *     The library never allocates device memory and never synchronizes.
+ *   - Tensors are dense, row-major (last dimension contiguous) device
+ *     buffers described by dq_tensor; the library keeps only the pointers.
+ *   - An executor is host memory owned by the library.  The execute call
+ *     consumes it, whether it succeeds or fails; an executor that is never
+ *     executed must be released with dq_executor_destroy.
+ *
+ * Errors
+ *   Every call returns a dq_status.  On any status other than DQ_SUCCESS,
+ *   dq_get_last_error() returns a message for the calling thread and no
+ *   executor is returned.  Device faults and other asynchronous errors
+ *   surface at the caller's next synchronization on the stream.
+ *
+ * Determinism: every op is bit-deterministic from run to run (fixed
+ * reduction trees, no atomics).
+ */
+#ifndef DQUANT_H
+#define DQUANT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum dq_status {
+    DQ_SUCCESS = 0,
+    DQ_ERR_NULLPTR = 1,   /* a required pointer is NULL                       */
+    DQ_ERR_DTYPE = 2,     /* unsupported dtype or dtype combination           */
+    DQ_ERR_SHAPE = 3,     /* shapes disagree, or a dimension is out of range  */
+    DQ_ERR_ALIGN = 4,     /* a size or address breaks an alignment rule       */
+    DQ_ERR_PARAM = 5,     /* a scalar parameter is out of range               */
+    DQ_ERR_OVERLAP = 6,   /* an output overlaps an input that forbids it      */
+    DQ_ERR_WORKSPACE = 7, /* the workspace passed is smaller than required    */
+    DQ_ERR_RUNTIME = 8    /* the HIP runtime rejected a launch                */
+} dq_status;
+
+typedef enum dq_dtype {
+    DQ_F32 = 0,
+    DQ_F16 = 1,
+    DQ_BF16 = 2,
+    DQ_I8 = 3,
+    DQ_I4 = 4,     /* two 4-bit codes per byte, the even element in the low nibble */
+    DQ_I32 = 5,    /* int32; as a DynamicQuant output: eight 4-bit codes per word  */
+    DQ_F8E4M3 = 6  /* OCP fp8 E4M3FN (no infinities, max 448)                      */
+} dq_dtype;
+
+#define DQ_MAX_DIMS 8
+
+/* A dense row-major tensor in device memory.  dims[0..ndim-1] are element
+ * counts; for DQ_I4 they count 4-bit codes (the buffer holds half as many
+ * bytes along the last dimension). */
+typedef struct dq_tensor {
+    void* data;
+    dq_dtype dtype;
+    int32_t ndim;
+    int64_t dims[DQ_MAX_DIMS];
+} dq_tensor;
+
+typedef struct dq_executor dq_executor;
+
+/* AntiQuantize quantization policy (AntiQuantize, 表1 AntiQuantizePolicy). */
+typedef enum dq_antiquant_policy {
+    DQ_PER_TENSOR = 0,
+    DQ_PER_CHANNEL = 1,
+    DQ_PER_TOKEN = 2,
+    DQ_PER_GROUP = 3
+} dq_antiquant_policy;
+
+/* ------------------------------------------------------------------------
+ * DynamicQuant -- aclnnDynamicQuantV2, Description and Formula.
+ *
+ * Per row r of x (the last dimension is the row; leading dimensions are
+ * flattened into R rows of N elements):
+ *   in = x * smooth[e(r)]            (when smooth_scales is given)
+ *   symmetric:  scale = row_max(|in|) / D,  y = round(in / scale)
+ *   asymmetric: scale = (row_max(in) - row_min(in)) / scale_opt,
+ *               offset = offset_opt - row_max(in) / scale,
+ *               y = round(in / scale + offset)
+ * with (scale_opt, offset_opt) = (255, 127) for INT8 and (15, 7) for INT4
+ * and INT32 output, D = offset_opt, round = half to even, codes saturated
+ * to [-128, 127] or [-8, 7] (NaN -> 0).  Every step is one correctly
+ * rounded binary32 operation in the order printed, so results are
+ * bit-exact against a plain IEEE evaluation.
+ *
+ *   x             F16 or BF16, [..., N], N >= 1.  R = prod(leading dims)
+ *                 may be 0 (the execute call is then a no-op).
+ *   smooth_scales NULL, or F32 [N] (no group_index), or F32 [E, N] with
+ *                 group_index.
+ *   group_index   NULL, or I32 [E] (E >= 1) holding cumulative per-expert
+ *                 row ends: expert e owns rows [gi[e-1], gi[e]); the owner
+ *                 of row r is the first e with r < gi[e], and rows at or
+ *                 past gi[E-1] belong to expert E-1 ("In the MOE scenario,
+ *                 smoothScalesOptional for each expert is different and is
+ *                 distinguished by groupIndexOptional").  Requires
+ *                 smooth_scales.  Its device contents are not validated.
+ *   symmetric     nonzero: symmetric; 0: asymmetric.
+ *   y             output.  DQ_I8 [..., N]; DQ_I4 [..., N] with N even
+ *                 (N/2 bytes per row); DQ_I32 [..., N/8] with N % 8 == 0
+ *                 (code 8w+i in bits [4i, 4i+3] of word w, so the bytes
+ *                 equal the INT4 bytes).
+ *   scale         output, F32, shape x.shape[:-1].
+ *   offset        output, F32, shape x.shape[:-1]; required when
+ *                 asymmetric, must be NULL when symmetric.
+ *   workspace_size, executor: returned.  The workspace size is 0.
+ * Errors: DQ_ERR_NULLPTR (missing x/y/scale/offset, NULL data),
+ *   DQ_ERR_DTYPE, DQ_ERR_SHAPE (shape mismatch, N == 0, INT4 N odd, INT32
+ *   N % 8 != 0, group_index without smooth_scales), DQ_ERR_PARAM (offset
+ *   given for symmetric).
+ * ------------------------------------------------------------------------ */
+dq_status dq_dynamic_quant_get_workspace_size(const dq_tensor* x, const dq_tensor* smooth_scales,
+                                              const dq_tensor* group_index, int symmetric,
+                                              const dq_tensor* y, const dq_tensor* scale,
+                                              const dq_tensor* offset, size_t* workspace_size,
+                                              dq_executor** executor);
+dq_status dq_dynamic_quant(void* workspace, size_t workspace_size, dq_executor* executor,
+                           hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * AdaLayerNorm + DynamicQuant fusion -- aclnnAdaLayerNormQuant, Formula.
+ *
+ * For each row (b, s) of x [B, S, H]:
+ *   LN = (x - E(x)) / sqrt(Var(x) + epsilon) * weight + bias  (biased Var)
+ *   y  = LN * (1 + scale[b]) + shift[b];  y = y * smooth       (if given)
+ *   quant_scale = row_max(|y|) / 127;  out = round(y / quant_scale)
+ * Only symmetric INT8 quantization is fused (the page: "only DynamicQuant
+ * is supported").  Statistics and modulation run in fp32 on the device;
+ * the quantization step is the bit-exact symmetric step of DynamicQuant
+ * applied to the fp32 y.
+ *
+ *   x             F16 or BF16 [B, S, H], H >= 1; B * S may be 0.
+ *   scale, shift  same dtype as x, [B, 1, H] or [B, H].
+ *   weight, bias  NULL or same dtype as x, [H] (absent: weight 1, bias 0).
+ *   smooth_scales NULL or F32 [H].
+ *   epsilon       > 0 and finite (used as fp32).
+ *   out           I8 [B, S, H].   quant_scale: F32 [B, S].
+ *   workspace size: 0.
+ * Errors: DQ_ERR_NULLPTR, DQ_ERR_DTYPE, DQ_ERR_SHAPE, DQ_ERR_PARAM
+ *   (epsilon <= 0 or not finite).
+ * ------------------------------------------------------------------------ */
+dq_status dq_ada_layernorm_quant_get_workspace_size(const dq_tensor* x, const dq_tensor* scale,
+                                                    const dq_tensor* shift,
+                                                    const dq_tensor* weight,
+                                                    const dq_tensor* bias,
+                                                    const dq_tensor* smooth_scales,
+                                                    double epsilon, const dq_tensor* out,
+                                                    const dq_tensor* quant_scale,
+                                                    size_t* workspace_size,
+                                                    dq_executor** executor);
+dq_status dq_ada_layernorm_quant(void* workspace, size_t workspace_size, dq_executor* executor,
+                                 hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * AntiQuantize -- AntiQuantize (Ascend C API), 功能说明 / 表1-表3 / 约束说明.
+ *
+ * Element-wise dequantization of src [m, n] into dst [m, n]:
+ *   dst[i, j] = (src[i, j] + offset[p]) * scale[p]     (offset given)
+ *   dst[i, j] = src[i, j] * scale[p]                    (offset NULL,
+ *                                                        hasOffset = false)
+ * computed as two correctly rounded fp32 operations, then rounded once
+ * (nearest even) to dst's type.  The parameter p by policy:
+ *   DQ_PER_TENSOR   scale/offset [1]                         p = 0
+ *   DQ_PER_CHANNEL  [1, n] (or [n])                          p = j
+ *   DQ_PER_TOKEN    [m, 1] (or [m])                          p = i
+ *   DQ_PER_GROUP    k_dim = 1: [m, ceil(n/gs)]               p = (i, j / gs)
+ *                   k_dim = 0: [ceil(m/gs), n]               p = (i / gs, j)
+ * The page leaves the formula itself out; the sign convention of the
+ * offset is this library's reading (it is the value that undoes
+ * DynamicQuant's "+ offset" when passed negated).
+ *
+ *   src        I8 or F8E4M3, exactly 2-D (the page: at most two dims).
+ *   scale      F32, policy shape.   offset: NULL or F32, same shape.
+ *   k_dim      0 or 1, used by DQ_PER_GROUP only.
+ *   group_size DQ_PER_GROUP: > 0 and a multiple of 32 (表2); ignored
+ *              otherwise.
+ *   dst        BF16 or F16 [m, n].
+ *   n * sizeof(src) and n * sizeof(dst) must be multiples of 32 bytes and
+ *   src/dst 16-byte aligned (约束说明: 32-byte aligned rows); src and dst
+ *   must not overlap.  m may be 0.  Workspace size: 0.
+ * Errors: DQ_ERR_NULLPTR, DQ_ERR_DTYPE, DQ_ERR_SHAPE (ndim != 2, param
+ *   shape), DQ_ERR_ALIGN, DQ_ERR_PARAM (policy, k_dim, group_size),
+ *   DQ_ERR_OVERLAP.
+ * ------------------------------------------------------------------------ */
+dq_status dq_antiquantize_get_workspace_size(const dq_tensor* src, const dq_tensor* scale,
+                                             const dq_tensor* offset, dq_antiquant_policy policy,
+                                             int32_t k_dim, uint32_t group_size,
+                                             const dq_tensor* dst, size_t* workspace_size,
+                                             dq_executor** executor);
+dq_status dq_antiquantize(void* workspace, size_t workspace_size, dq_executor* executor,
+                          hipStream_t stream);
+
+/* Release an executor that was never passed to an execute call.  NULL is a
+ * no-op. */
+void dq_executor_destroy(dq_executor* executor);
+
+/* Message for the calling thread's last non-success status ("" if none).
+ * The pointer stays valid until the thread's next libdquant call. */
+const char* dq_get_last_error(void);
+
+/* Measurement utility (not a quantization op): enqueue a plain device copy
+ * of `bytes` bytes (a multiple of 16, both pointers 16-byte aligned, no
+ * overlap) on `stream`.  Its bandwidth is the achievable-ceiling reference
+ * for the memory-bound kernels above, and its HBM counters calibrate the
+ * profiler's FETCH_SIZE / WRITE_SIZE readings. */
+dq_status dq_copy_probe(void* dst, const void* src, size_t bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DQUANT_H */

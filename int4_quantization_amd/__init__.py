@@ -1,0 +1,25 @@
+"""libdquant for MI355X (gfx950): per-token dynamic quantization
+(DynamicQuantV2), its AdaLayerNorm fusion, and AntiQuantize.
+
+The compute runs in hand-written HIP kernels inside ``libdquant.so``, reached
+through the C ABI declared in ``include/dquant.h``.  This package is the thin
+ctypes binding over that library (``dquant``) plus the seeded synthetic
+input generators (``synth``).  There is no CPU fallback: calling an op
+without the built library raises.
+"""
+from .dquant import (  # noqa: F401
+    DquantError,
+    ada_layernorm_quant,
+    antiquantize,
+    dq_ada_layernorm_quant,
+    dq_ada_layernorm_quant_get_workspace_size,
+    dq_antiquantize,
+    dq_antiquantize_get_workspace_size,
+    dq_dynamic_quant,
+    dq_dynamic_quant_get_workspace_size,
+    dq_executor_destroy,
+    dq_get_last_error,
+    dynamic_quant,
+    library,
+    library_path,
+)

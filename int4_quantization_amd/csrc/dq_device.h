@@ -1,0 +1,165 @@
+// dq_device.h -- device helpers shared by the libdquant kernels (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace dq {
+
+constexpr int kWave = 64;
+constexpr int kBlock = 256;  // four waves
+
+// ---------------------------------------------------------------------------
+// XCD-aware block order.  The dispatcher hands workgroup `bid` to XCD
+// bid % 8; this bijection on [0, nb) gives each XCD one contiguous range of
+// logical blocks, so rows that share parameters (an expert's smooth row, a
+// batch's modulation vectors) stay in that XCD's L2.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int64_t xcd_block(int64_t bid, int64_t nb)
+{
+    const int64_t x = bid & 7, idx = bid >> 3;
+    const int64_t per = nb >> 3, rem = nb & 7;
+    return x * per + (x < rem ? x : rem) + idx;
+}
+
+// ---------------------------------------------------------------------------
+// Wave-wide reductions.  Lanes combine in a fixed butterfly: quad swaps and
+// row mirrors through DPP, the 16-lane swap through ds_swizzle, and the two
+// 32-lane halves through readlane.  Every lane ends with the same value and
+// the order never changes, so sums are deterministic.  All 64 lanes must be
+// active.
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v)
+{
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float swz_xor16(float v)
+{
+    // BitMode swizzle within 32 lanes: and_mask 0x1F, or 0, xor 0x10.
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
+}
+
+__device__ __forceinline__ float lane_f(float v, int lane)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+constexpr int kDppQuadXor1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+
+template <typename Op>
+__device__ __forceinline__ float wave_reduce(float v, Op op)
+{
+    v = op(v, dpp_f<kDppQuadXor1>(v));
+    v = op(v, dpp_f<kDppQuadXor2>(v));
+    v = op(v, dpp_f<kDppHalfMirror>(v));
+    v = op(v, dpp_f<kDppMirror>(v));
+    v = op(v, swz_xor16(v));
+    return op(lane_f(v, 0), lane_f(v, 32));
+}
+
+struct MaxOp {
+    __device__ float operator()(float a, float b) const { return __builtin_fmaxf(a, b); }
+};
+struct MinOp {
+    __device__ float operator()(float a, float b) const { return __builtin_fminf(a, b); }
+};
+struct AddOp {
+    __device__ float operator()(float a, float b) const { return a + b; }
+};
+
+__device__ __forceinline__ float wave_max(float v) { return wave_reduce(v, MaxOp{}); }
+__device__ __forceinline__ float wave_min(float v) { return wave_reduce(v, MinOp{}); }
+__device__ __forceinline__ float wave_sum(float v) { return wave_reduce(v, AddOp{}); }
+
+// ---------------------------------------------------------------------------
+// Element widening (exact).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
+__device__ __forceinline__ float f16_lo(uint32_t w)
+{
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w & 0xFFFFu)));
+}
+__device__ __forceinline__ float f16_hi(uint32_t w)
+{
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w >> 16)));
+}
+
+template <int XT>  // 0: fp16, 1: bf16
+__device__ __forceinline__ void widen8(const uint4 p, float (&v)[8])
+{
+    const uint32_t w[4] = {p.x, p.y, p.z, p.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if (XT == 1) {
+            v[2 * i] = bf16_lo(w[i]);
+            v[2 * i + 1] = bf16_hi(w[i]);
+        } else {
+            v[2 * i] = f16_lo(w[i]);
+            v[2 * i + 1] = f16_hi(w[i]);
+        }
+    }
+}
+
+template <int XT>
+__device__ __forceinline__ float widen1(const uint16_t h)
+{
+    if (XT == 1)
+        return __builtin_bit_cast(float, static_cast<uint32_t>(h) << 16);
+    return static_cast<float>(__builtin_bit_cast(_Float16, h));
+}
+
+// ---------------------------------------------------------------------------
+// Correctly rounded division by a per-row divisor.
+//
+// For d in [2^-60, 2^60] and r = RN(1/d) (itself a correctly rounded
+// division done once per row), q0 = RN(v*r) is within an ulp of v/d, the
+// residual fma(-d, q0, v) is exact, and one more fma gives RN(v/d)
+// (Markstein's correction step).  Quotients so small that the residual
+// could underflow (|v/d| < 2^-40) only ever meet the rounding to an integer
+// code, which maps them to 0 either way.  Rows whose divisor lies outside
+// the range take a true division per element instead.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float div_by_row(float v, float d, float r)
+{
+    const float q0 = v * r;
+    const float e = __builtin_fmaf(-d, q0, v);
+    return __builtin_fmaf(e, r, q0);
+}
+
+__device__ __forceinline__ bool row_divisor_in_range(float d)
+{
+    return d >= 0x1p-60f && d <= 0x1p60f;  // false for 0, NaN, inf
+}
+
+// Round-half-to-even to an integer code through the binary32 adder: for
+// |t| < 2^22, t + 1.5*2^23 rounds at the units place with ties to even, and
+// the low bits of the sum's encoding are the two's complement code.
+constexpr float kRoundMagic = 12582912.0f;  // 1.5 * 2^23
+
+__device__ __forceinline__ uint32_t code_bits(float t) { return __builtin_bit_cast(uint32_t, t + kRoundMagic); }
+
+// Pack the low bytes of four code words into one dword (byte i = code i).
+__device__ __forceinline__ uint32_t pack4_i8(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3)
+{
+    const uint32_t lo = __builtin_amdgcn_perm(c1, c0, 0x0C0C0400u);  // [c0, c1, 0, 0]
+    const uint32_t hi = __builtin_amdgcn_perm(c3, c2, 0x0C0C0400u);  // [c2, c3, 0, 0]
+    return lo | (hi << 16);
+}
+
+// Pack eight 4-bit codes into one dword, code i in bits [4i, 4i+3].
+__device__ __forceinline__ uint32_t pack8_i4(const uint32_t (&c)[8])
+{
+    const uint32_t even = pack4_i8(c[0], c[2], c[4], c[6]);  // byte k = code 2k
+    const uint32_t odd = pack4_i8(c[1], c[3], c[5], c[7]);   // byte k = code 2k+1
+    return (even & 0x0F0F0F0Fu) | ((odd << 4) & 0xF0F0F0F0u);
+}
+
+}  // namespace dq

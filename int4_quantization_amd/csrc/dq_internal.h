@@ -1,0 +1,93 @@
+// dq_internal.h -- plans shared between the host validation layer
+// (dquant_api.cpp) and the kernel launchers (*.hip).  Not installed.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include <hip/hip_runtime_api.h>
+
+#include "dquant.h"
+
+namespace dq {
+
+// Element codes used inside the kernels.
+enum XType : int { X_F16 = 0, X_BF16 = 1 };
+enum OutKind : int { OUT_I8 = 0, OUT_I4 = 1 };  // INT32 output shares the INT4 bytes
+
+// ---- DynamicQuant --------------------------------------------------------
+enum DqVariant : int {
+    DQ_VAR_VECTOR = 0,   // row held in VGPRs, 16-byte loads, TEAM waves per row
+    DQ_VAR_GENERIC = 1,  // one workgroup per row, element loads, two passes
+};
+
+struct DqPlan {
+    const void* x;
+    const float* smooth;       // nullptr: no smooth step
+    const int32_t* group_index;  // nullptr: one smooth row for all rows
+    int64_t n_experts;
+    int64_t rows;
+    int64_t n;
+    int x_type;    // XType
+    int out_kind;  // OutKind
+    bool symmetric;
+    void* y;
+    float* scale;
+    float* offset;
+    // launch choice
+    int variant;
+    int vpl;   // 16-byte vectors per lane (vector variant)
+    int team;  // waves per row (vector variant): 1 or 4
+};
+
+// ---- AdaLayerNorm-quant ----------------------------------------------------
+enum AdaVariant : int { ADA_VAR_VECTOR = 0, ADA_VAR_GENERIC = 1 };
+
+struct AdaPlan {
+    const void* x;
+    const void* scale;   // [B, H]
+    const void* shift;   // [B, H]
+    const void* weight;  // [H] or nullptr
+    const void* bias;    // [H] or nullptr
+    const float* smooth; // [H] or nullptr
+    int64_t B, S, H;
+    int x_type;  // XType; parameters share it
+    float eps;
+    int8_t* out;
+    float* quant_scale;
+    int variant;
+    int vpl;
+    int rows_per_block;
+};
+
+// ---- AntiQuantize ---------------------------------------------------------
+enum SrcKind : int { SRC_I8 = 0, SRC_F8E4M3 = 1 };
+enum DstKind : int { DST_BF16 = 0, DST_F16 = 1, DST_F32 = 2 };
+
+struct AqPlan {
+    const void* src;
+    const float* scale;
+    const float* offset;  // nullptr: hasOffset = false
+    int64_t m, n;
+    int policy;  // dq_antiquant_policy
+    int k_dim;
+    int64_t group_size;
+    int src_kind;
+    int dst_kind;
+    void* dst;
+    int rows_per_tile;
+};
+
+// Kernel launchers (defined in the .hip files).  They enqueue on `stream`
+// and return the launch status; they never synchronize.
+hipError_t launch_dynamic_quant(const DqPlan& p, hipStream_t stream);
+hipError_t launch_ada_layernorm_quant(const AdaPlan& p, hipStream_t stream);
+hipError_t launch_antiquantize(const AqPlan& p, hipStream_t stream);
+hipError_t launch_copy_probe(void* dst, const void* src, size_t bytes, hipStream_t stream);
+
+// Largest row (in elements) the register-resident DynamicQuant variant
+// holds: 16 vectors of 8 elements per lane, 64 lanes, TEAM waves.
+constexpr int64_t kDqVecMaxPerWave = 16 * 8 * 64;
+constexpr int64_t kDqVecMaxTeam4 = 4 * kDqVecMaxPerWave;
+
+}  // namespace dq

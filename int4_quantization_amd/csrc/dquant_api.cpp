@@ -1,0 +1,584 @@
+// dquant_api.cpp -- the C ABI of libdquant: argument validation, kernel
+// variant selection and executors (phase 1, host only, no HIP calls), and
+// the execute calls that enqueue the kernels (phase 2).
+//
+// The two-phase shape follows the aclnn host ops (aclnnDynamicQuantV2,
+// aclnnAdaLayerNormQuant: a get-workspace-size call that validates the
+// parameters and returns an executor, then the execute call).
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "dq_internal.h"
+
+enum ExecOp : int { OP_DYNAMIC_QUANT = 1, OP_ADA_LAYERNORM_QUANT = 2, OP_ANTIQUANTIZE = 3 };
+
+struct dq_executor {
+    int op;
+    dq::DqPlan dq;
+    dq::AdaPlan ada;
+    dq::AqPlan aq;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+dq_status fail(dq_status st, const char* fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+dq_status ok()
+{
+    g_last_error.clear();
+    return DQ_SUCCESS;
+}
+
+const char* dtype_name(dq_dtype d)
+{
+    switch (d) {
+    case DQ_F32: return "F32";
+    case DQ_F16: return "F16";
+    case DQ_BF16: return "BF16";
+    case DQ_I8: return "I8";
+    case DQ_I4: return "I4";
+    case DQ_I32: return "I32";
+    case DQ_F8E4M3: return "F8E4M3";
+    }
+    return "unknown";
+}
+
+// Checks ndim range and non-negative dims; returns the element count.
+bool shape_ok(const dq_tensor* t, int64_t* numel)
+{
+    if (t->ndim < 0 || t->ndim > DQ_MAX_DIMS)
+        return false;
+    int64_t n = 1;
+    for (int i = 0; i < t->ndim; ++i) {
+        if (t->dims[i] < 0)
+            return false;
+        n *= t->dims[i];
+    }
+    *numel = n;
+    return true;
+}
+
+// A tensor's data must be non-null whenever it holds elements.
+dq_status check_tensor(const dq_tensor* t, const char* name, int64_t* numel)
+{
+    if (!t)
+        return fail(DQ_ERR_NULLPTR, "%s is NULL", name);
+    int64_t n = 0;
+    if (!shape_ok(t, &n))
+        return fail(DQ_ERR_SHAPE, "%s: ndim %d or a dimension is out of range", name, t->ndim);
+    if (n > 0 && !t->data)
+        return fail(DQ_ERR_NULLPTR, "%s->data is NULL", name);
+    if (numel)
+        *numel = n;
+    return DQ_SUCCESS;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool same_dims(const dq_tensor* t, const int64_t* dims, int ndim)
+{
+    if (t->ndim != ndim)
+        return false;
+    for (int i = 0; i < ndim; ++i)
+        if (t->dims[i] != dims[i])
+            return false;
+    return true;
+}
+
+// Shape [d0] or [1, d0] / [d0, 1] style checks used by AntiQuantize.
+bool is_shape(const dq_tensor* t, std::initializer_list<int64_t> want)
+{
+    if (t->ndim != static_cast<int>(want.size()))
+        return false;
+    int i = 0;
+    for (int64_t w : want)
+        if (t->dims[i++] != w)
+            return false;
+    return true;
+}
+
+int64_t elem_bytes_x16(dq_dtype d)  // bytes per element times 2 (I4 is half a byte)
+{
+    switch (d) {
+    case DQ_F32: case DQ_I32: return 8;
+    case DQ_F16: case DQ_BF16: return 4;
+    case DQ_I8: case DQ_F8E4M3: return 2;
+    case DQ_I4: return 1;
+    }
+    return 0;
+}
+
+dq_executor* new_executor(int op)
+{
+    dq_executor* e = new (std::nothrow) dq_executor;
+    if (e) {
+        std::memset(e, 0, sizeof *e);
+        e->op = op;
+    }
+    return e;
+}
+
+int pick_vpl(int64_t per_lane, const int* choices, int count)
+{
+    for (int i = 0; i < count; ++i)
+        if (choices[i] >= per_lane)
+            return choices[i];
+    return -1;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dq_get_last_error(void) { return g_last_error.c_str(); }
+
+void dq_executor_destroy(dq_executor* executor) { delete executor; }
+
+// ---------------------------------------------------------------------------
+// DynamicQuant
+// ---------------------------------------------------------------------------
+dq_status dq_dynamic_quant_get_workspace_size(const dq_tensor* x, const dq_tensor* smooth_scales,
+                                              const dq_tensor* group_index, int symmetric,
+                                              const dq_tensor* y, const dq_tensor* scale,
+                                              const dq_tensor* offset, size_t* workspace_size,
+                                              dq_executor** executor)
+{
+    if (!workspace_size || !executor)
+        return fail(DQ_ERR_NULLPTR, "workspace_size and executor must not be NULL");
+    *executor = nullptr;
+    *workspace_size = 0;
+    dq_status st;
+    int64_t nx = 0, ny = 0, ns = 0;
+    if ((st = check_tensor(x, "x", &nx)) != DQ_SUCCESS) return st;
+    if ((st = check_tensor(y, "y", &ny)) != DQ_SUCCESS) return st;
+    if ((st = check_tensor(scale, "scale", &ns)) != DQ_SUCCESS) return st;
+
+    if (x->dtype != DQ_F16 && x->dtype != DQ_BF16)
+        return fail(DQ_ERR_DTYPE, "x must be F16 or BF16, got %s", dtype_name(x->dtype));
+    if (y->dtype != DQ_I8 && y->dtype != DQ_I4 && y->dtype != DQ_I32)
+        return fail(DQ_ERR_DTYPE, "y must be I8, I4 or I32, got %s", dtype_name(y->dtype));
+    if (scale->dtype != DQ_F32)
+        return fail(DQ_ERR_DTYPE, "scale must be F32, got %s", dtype_name(scale->dtype));
+    if (x->ndim < 1)
+        return fail(DQ_ERR_SHAPE, "x must have at least one dimension");
+    const int64_t n = x->dims[x->ndim - 1];
+    if (n < 1)
+        return fail(DQ_ERR_SHAPE, "the last dimension of x must be >= 1");
+    const int64_t rows = nx / n;
+
+    if (y->dtype == DQ_I8 || y->dtype == DQ_I4) {
+        if (!same_dims(y, x->dims, x->ndim))
+            return fail(DQ_ERR_SHAPE, "y must have the shape of x");
+        if (y->dtype == DQ_I4 && n % 2 != 0)
+            return fail(DQ_ERR_SHAPE, "INT4 output needs an even last dimension, got %lld",
+                        (long long)n);
+    } else {
+        if (n % 8 != 0)
+            return fail(DQ_ERR_SHAPE, "INT32 output needs the last dimension of x divisible by 8, got %lld",
+                        (long long)n);
+        int64_t want[DQ_MAX_DIMS];
+        std::memcpy(want, x->dims, sizeof want);
+        want[x->ndim - 1] = n / 8;
+        if (!same_dims(y, want, x->ndim))
+            return fail(DQ_ERR_SHAPE, "INT32 y must be x.shape[:-1] + [N/8]");
+    }
+    if (!same_dims(scale, x->dims, x->ndim - 1))
+        return fail(DQ_ERR_SHAPE, "scale must have shape x.shape[:-1]");
+
+    if (symmetric) {
+        if (offset)
+            return fail(DQ_ERR_PARAM, "offset must be NULL for symmetric quantization");
+    } else {
+        int64_t no = 0;
+        if (!offset)
+            return fail(DQ_ERR_NULLPTR, "asymmetric quantization needs an offset output");
+        if ((st = check_tensor(offset, "offset", &no)) != DQ_SUCCESS) return st;
+        if (offset->dtype != DQ_F32)
+            return fail(DQ_ERR_DTYPE, "offset must be F32, got %s", dtype_name(offset->dtype));
+        if (!same_dims(offset, x->dims, x->ndim - 1))
+            return fail(DQ_ERR_SHAPE, "offset must have shape x.shape[:-1]");
+    }
+
+    int64_t n_experts = 0;
+    if (group_index) {
+        int64_t ng = 0;
+        if (!smooth_scales)
+            return fail(DQ_ERR_SHAPE, "group_index needs smooth_scales [E, N]");
+        if ((st = check_tensor(group_index, "group_index", &ng)) != DQ_SUCCESS) return st;
+        if (group_index->dtype != DQ_I32)
+            return fail(DQ_ERR_DTYPE, "group_index must be I32, got %s", dtype_name(group_index->dtype));
+        if (group_index->ndim != 1 || group_index->dims[0] < 1)
+            return fail(DQ_ERR_SHAPE, "group_index must be [E] with E >= 1");
+        if (!group_index->data)
+            return fail(DQ_ERR_NULLPTR, "group_index->data is NULL");
+        n_experts = group_index->dims[0];
+    }
+    if (smooth_scales) {
+        int64_t nsm = 0;
+        if ((st = check_tensor(smooth_scales, "smooth_scales", &nsm)) != DQ_SUCCESS) return st;
+        if (smooth_scales->dtype != DQ_F32)
+            return fail(DQ_ERR_DTYPE, "smooth_scales must be F32, got %s",
+                        dtype_name(smooth_scales->dtype));
+        if (group_index) {
+            if (!is_shape(smooth_scales, {n_experts, n}))
+                return fail(DQ_ERR_SHAPE, "smooth_scales must be [E, N] = [%lld, %lld]",
+                            (long long)n_experts, (long long)n);
+        } else if (!is_shape(smooth_scales, {n})) {
+            return fail(DQ_ERR_SHAPE, "smooth_scales must be [N] = [%lld]", (long long)n);
+        }
+        if (!smooth_scales->data)
+            return fail(DQ_ERR_NULLPTR, "smooth_scales->data is NULL");
+    }
+
+    dq_executor* e = new_executor(OP_DYNAMIC_QUANT);
+    if (!e)
+        return fail(DQ_ERR_RUNTIME, "out of host memory");
+    dq::DqPlan& p = e->dq;
+    p.x = x->data;
+    p.smooth = smooth_scales ? static_cast<const float*>(smooth_scales->data) : nullptr;
+    p.group_index = group_index ? static_cast<const int32_t*>(group_index->data) : nullptr;
+    p.n_experts = n_experts;
+    p.rows = rows;
+    p.n = n;
+    p.x_type = x->dtype == DQ_F16 ? dq::X_F16 : dq::X_BF16;
+    p.out_kind = y->dtype == DQ_I8 ? dq::OUT_I8 : dq::OUT_I4;
+    p.symmetric = symmetric != 0;
+    p.y = y->data;
+    p.scale = static_cast<float*>(scale->data);
+    p.offset = symmetric ? nullptr : static_cast<float*>(offset->data);
+
+    // Register-resident variant: rows of whole 16-byte vectors, aligned
+    // buffers, and a row that fits 16 vectors per lane of one or four waves.
+    const bool vec_ok = n % 8 == 0 && aligned(p.x, 16) && (!p.smooth || aligned(p.smooth, 16)) &&
+                        aligned(p.y, p.out_kind == dq::OUT_I8 ? 8 : 4);
+    static const int kVpl[] = {1, 2, 4, 8, 12, 14, 16};
+    static const int kVplTeam[] = {8, 16};
+    p.variant = dq::DQ_VAR_GENERIC;
+    if (vec_ok) {
+        const int64_t nvec = n / 8;
+        int v = pick_vpl((nvec + 63) / 64, kVpl, 7);
+        if (v > 0) {
+            p.variant = dq::DQ_VAR_VECTOR;
+            p.vpl = v;
+            p.team = 1;
+        } else if ((v = pick_vpl((nvec + 255) / 256, kVplTeam, 2)) > 0) {
+            p.variant = dq::DQ_VAR_VECTOR;
+            p.vpl = v;
+            p.team = 4;
+        }
+    }
+    *executor = e;
+    return ok();
+}
+
+dq_status dq_dynamic_quant(void* workspace, size_t workspace_size, dq_executor* executor,
+                           hipStream_t stream)
+{
+    (void)workspace;
+    (void)workspace_size;  // no workspace is needed
+    if (!executor)
+        return fail(DQ_ERR_NULLPTR, "executor is NULL");
+    dq_executor* e = executor;
+    if (e->op != OP_DYNAMIC_QUANT) {
+        delete e;
+        return fail(DQ_ERR_PARAM, "executor was not made by dq_dynamic_quant_get_workspace_size");
+    }
+    dq::DqPlan p = e->dq;
+    delete e;
+    if (p.rows == 0)
+        return ok();
+    hipError_t err = dq::launch_dynamic_quant(p, stream);
+    if (err != hipSuccess)
+        return fail(DQ_ERR_RUNTIME, "dynamic_quant launch failed: %s", hipGetErrorString(err));
+    return ok();
+}
+
+// ---------------------------------------------------------------------------
+// AdaLayerNorm-quant
+// ---------------------------------------------------------------------------
+dq_status dq_ada_layernorm_quant_get_workspace_size(const dq_tensor* x, const dq_tensor* scale,
+                                                    const dq_tensor* shift,
+                                                    const dq_tensor* weight,
+                                                    const dq_tensor* bias,
+                                                    const dq_tensor* smooth_scales,
+                                                    double epsilon, const dq_tensor* out,
+                                                    const dq_tensor* quant_scale,
+                                                    size_t* workspace_size,
+                                                    dq_executor** executor)
+{
+    if (!workspace_size || !executor)
+        return fail(DQ_ERR_NULLPTR, "workspace_size and executor must not be NULL");
+    *executor = nullptr;
+    *workspace_size = 0;
+    dq_status st;
+    if ((st = check_tensor(x, "x", nullptr)) != DQ_SUCCESS) return st;
+    if ((st = check_tensor(scale, "scale", nullptr)) != DQ_SUCCESS) return st;
+    if ((st = check_tensor(shift, "shift", nullptr)) != DQ_SUCCESS) return st;
+    if ((st = check_tensor(out, "out", nullptr)) != DQ_SUCCESS) return st;
+    if ((st = check_tensor(quant_scale, "quant_scale", nullptr)) != DQ_SUCCESS) return st;
+    if (weight && (st = check_tensor(weight, "weight", nullptr)) != DQ_SUCCESS) return st;
+    if (bias && (st = check_tensor(bias, "bias", nullptr)) != DQ_SUCCESS) return st;
+    if (smooth_scales && (st = check_tensor(smooth_scales, "smooth_scales", nullptr)) != DQ_SUCCESS)
+        return st;
+
+    if (x->dtype != DQ_F16 && x->dtype != DQ_BF16)
+        return fail(DQ_ERR_DTYPE, "x must be F16 or BF16, got %s", dtype_name(x->dtype));
+    const dq_tensor* same[] = {scale, shift, weight, bias};
+    const char* names[] = {"scale", "shift", "weight", "bias"};
+    for (int i = 0; i < 4; ++i)
+        if (same[i] && same[i]->dtype != x->dtype)
+            return fail(DQ_ERR_DTYPE, "%s must have x's dtype %s, got %s", names[i],
+                        dtype_name(x->dtype), dtype_name(same[i]->dtype));
+    if (smooth_scales && smooth_scales->dtype != DQ_F32)
+        return fail(DQ_ERR_DTYPE, "smooth_scales must be F32, got %s", dtype_name(smooth_scales->dtype));
+    if (out->dtype != DQ_I8)
+        return fail(DQ_ERR_DTYPE, "out must be I8 (only symmetric INT8 is fused), got %s",
+                    dtype_name(out->dtype));
+    if (quant_scale->dtype != DQ_F32)
+        return fail(DQ_ERR_DTYPE, "quant_scale must be F32, got %s", dtype_name(quant_scale->dtype));
+
+    if (x->ndim != 3)
+        return fail(DQ_ERR_SHAPE, "x must be [B, S, H]");
+    const int64_t B = x->dims[0], S = x->dims[1], H = x->dims[2];
+    if (H < 1)
+        return fail(DQ_ERR_SHAPE, "H must be >= 1");
+    if (!(is_shape(scale, {B, 1, H}) || is_shape(scale, {B, H})))
+        return fail(DQ_ERR_SHAPE, "scale must be [B, 1, H] or [B, H]");
+    if (!(is_shape(shift, {B, 1, H}) || is_shape(shift, {B, H})))
+        return fail(DQ_ERR_SHAPE, "shift must be [B, 1, H] or [B, H]");
+    if (weight && !is_shape(weight, {H}))
+        return fail(DQ_ERR_SHAPE, "weight must be [H]");
+    if (bias && !is_shape(bias, {H}))
+        return fail(DQ_ERR_SHAPE, "bias must be [H]");
+    if (smooth_scales && !is_shape(smooth_scales, {H}))
+        return fail(DQ_ERR_SHAPE, "smooth_scales must be [H]");
+    if (!same_dims(out, x->dims, 3))
+        return fail(DQ_ERR_SHAPE, "out must have the shape of x");
+    if (!is_shape(quant_scale, {B, S}))
+        return fail(DQ_ERR_SHAPE, "quant_scale must be [B, S]");
+    if (!(epsilon > 0.0) || !std::isfinite(epsilon))
+        return fail(DQ_ERR_PARAM, "epsilon must be positive and finite");
+    if (H > 0 && B > 0 && (!scale->data || !shift->data))
+        return fail(DQ_ERR_NULLPTR, "scale/shift data is NULL");
+
+    dq_executor* e = new_executor(OP_ADA_LAYERNORM_QUANT);
+    if (!e)
+        return fail(DQ_ERR_RUNTIME, "out of host memory");
+    dq::AdaPlan& p = e->ada;
+    p.x = x->data;
+    p.scale = scale->data;
+    p.shift = shift->data;
+    p.weight = weight ? weight->data : nullptr;
+    p.bias = bias ? bias->data : nullptr;
+    p.smooth = smooth_scales ? static_cast<const float*>(smooth_scales->data) : nullptr;
+    p.B = B;
+    p.S = S;
+    p.H = H;
+    p.x_type = x->dtype == DQ_F16 ? dq::X_F16 : dq::X_BF16;
+    p.eps = static_cast<float>(epsilon);
+    p.out = static_cast<int8_t*>(out->data);
+    p.quant_scale = static_cast<float*>(quant_scale->data);
+
+    static const int kVpl[] = {1, 2, 4, 6, 8, 12, 16};
+    const bool vec_ok = H % 8 == 0 && aligned(p.x, 16) && aligned(p.out, 8);
+    int v = vec_ok ? pick_vpl((H / 8 + 63) / 64, kVpl, 7) : -1;
+    p.variant = v > 0 ? dq::ADA_VAR_VECTOR : dq::ADA_VAR_GENERIC;
+    p.vpl = v;
+    // Rows per workgroup: enough rows per block to amortize the per-batch
+    // parameter table, while keeping well over 4 blocks per CU.
+    const int64_t rows = B * S;
+    int rpb = 4;
+    while (rpb < 64 && rows / (rpb * 2) >= 1024)
+        rpb *= 2;
+    p.rows_per_block = rpb;
+    *executor = e;
+    return ok();
+}
+
+dq_status dq_ada_layernorm_quant(void* workspace, size_t workspace_size, dq_executor* executor,
+                                 hipStream_t stream)
+{
+    (void)workspace;
+    (void)workspace_size;
+    if (!executor)
+        return fail(DQ_ERR_NULLPTR, "executor is NULL");
+    dq_executor* e = executor;
+    if (e->op != OP_ADA_LAYERNORM_QUANT) {
+        delete e;
+        return fail(DQ_ERR_PARAM,
+                    "executor was not made by dq_ada_layernorm_quant_get_workspace_size");
+    }
+    dq::AdaPlan p = e->ada;
+    delete e;
+    if (p.B * p.S == 0)
+        return ok();
+    hipError_t err = dq::launch_ada_layernorm_quant(p, stream);
+    if (err != hipSuccess)
+        return fail(DQ_ERR_RUNTIME, "ada_layernorm_quant launch failed: %s", hipGetErrorString(err));
+    return ok();
+}
+
+// ---------------------------------------------------------------------------
+// AntiQuantize
+// ---------------------------------------------------------------------------
+dq_status dq_antiquantize_get_workspace_size(const dq_tensor* src, const dq_tensor* scale,
+                                             const dq_tensor* offset, dq_antiquant_policy policy,
+                                             int32_t k_dim, uint32_t group_size,
+                                             const dq_tensor* dst, size_t* workspace_size,
+                                             dq_executor** executor)
+{
+    if (!workspace_size || !executor)
+        return fail(DQ_ERR_NULLPTR, "workspace_size and executor must not be NULL");
+    *executor = nullptr;
+    *workspace_size = 0;
+    dq_status st;
+    int64_t nsrc = 0, ndst = 0;
+    if ((st = check_tensor(src, "src", &nsrc)) != DQ_SUCCESS) return st;
+    if ((st = check_tensor(scale, "scale", nullptr)) != DQ_SUCCESS) return st;
+    if ((st = check_tensor(dst, "dst", &ndst)) != DQ_SUCCESS) return st;
+    if (offset && (st = check_tensor(offset, "offset", nullptr)) != DQ_SUCCESS) return st;
+
+    if (src->dtype != DQ_I8 && src->dtype != DQ_F8E4M3)
+        return fail(DQ_ERR_DTYPE, "src must be I8 or F8E4M3, got %s", dtype_name(src->dtype));
+    if (dst->dtype != DQ_BF16 && dst->dtype != DQ_F16 && dst->dtype != DQ_F32)
+        return fail(DQ_ERR_DTYPE, "dst must be BF16, F16 or F32, got %s", dtype_name(dst->dtype));
+    if (scale->dtype != DQ_F32)
+        return fail(DQ_ERR_DTYPE, "scale must be F32, got %s", dtype_name(scale->dtype));
+    if (offset && offset->dtype != DQ_F32)
+        return fail(DQ_ERR_DTYPE, "offset must be F32, got %s", dtype_name(offset->dtype));
+    if (src->ndim != 2)
+        return fail(DQ_ERR_SHAPE, "src must be 2-D [m, n] (got %d dims)", src->ndim);
+    const int64_t m = src->dims[0], n = src->dims[1];
+    if (!same_dims(dst, src->dims, 2))
+        return fail(DQ_ERR_SHAPE, "dst must have the shape of src");
+    if (policy < DQ_PER_TENSOR || policy > DQ_PER_GROUP)
+        return fail(DQ_ERR_PARAM, "unknown policy %d", (int)policy);
+    if (policy == DQ_PER_GROUP) {
+        if (k_dim != 0 && k_dim != 1)
+            return fail(DQ_ERR_PARAM, "k_dim must be 0 or 1 for PER_GROUP, got %d", k_dim);
+        if (group_size == 0 || group_size % 32 != 0)
+            return fail(DQ_ERR_PARAM, "group_size must be > 0 and a multiple of 32, got %u",
+                        group_size);
+    }
+    bool shape_good = false;
+    const int64_t gs = group_size;
+    switch (policy) {
+    case DQ_PER_TENSOR:
+        shape_good = is_shape(scale, {1}) || scale->ndim == 0 || is_shape(scale, {1, 1});
+        break;
+    case DQ_PER_CHANNEL:
+        shape_good = is_shape(scale, {1, n}) || is_shape(scale, {n});
+        break;
+    case DQ_PER_TOKEN:
+        shape_good = is_shape(scale, {m, 1}) || is_shape(scale, {m});
+        break;
+    case DQ_PER_GROUP:
+        shape_good = k_dim == 1 ? is_shape(scale, {m, (n + gs - 1) / gs})
+                                : is_shape(scale, {(m + gs - 1) / gs, n});
+        break;
+    }
+    if (!shape_good)
+        return fail(DQ_ERR_SHAPE, "scale shape does not match the policy");
+    if (offset) {
+        if (offset->ndim != scale->ndim || !same_dims(offset, scale->dims, scale->ndim))
+            return fail(DQ_ERR_SHAPE, "offset must have the shape of scale");
+    }
+    // 32-byte rule on the contiguous (n) direction for src and dst.
+    if ((n * elem_bytes_x16(src->dtype) / 2) % 32 != 0 || (n * elem_bytes_x16(dst->dtype) / 2) % 32 != 0)
+        return fail(DQ_ERR_ALIGN, "n * sizeof(src) and n * sizeof(dst) must be multiples of 32 bytes (n = %lld)",
+                    (long long)n);
+    if (nsrc > 0) {
+        if (!aligned(src->data, 16) || !aligned(dst->data, 16))
+            return fail(DQ_ERR_ALIGN, "src and dst must be 16-byte aligned");
+        const bool vec_params = policy == DQ_PER_CHANNEL || (policy == DQ_PER_GROUP && k_dim == 0);
+        if (vec_params && (!aligned(scale->data, 16) || (offset && !aligned(offset->data, 16))))
+            return fail(DQ_ERR_ALIGN, "scale/offset must be 16-byte aligned for this policy");
+        const uintptr_t s0 = reinterpret_cast<uintptr_t>(src->data);
+        const uintptr_t s1 = s0 + static_cast<uintptr_t>(nsrc * elem_bytes_x16(src->dtype) / 2);
+        const uintptr_t d0 = reinterpret_cast<uintptr_t>(dst->data);
+        const uintptr_t d1 = d0 + static_cast<uintptr_t>(ndst * elem_bytes_x16(dst->dtype) / 2);
+        if (s0 < d1 && d0 < s1)
+            return fail(DQ_ERR_OVERLAP, "src and dst overlap");
+        if (!scale->data || (offset && !offset->data))
+            return fail(DQ_ERR_NULLPTR, "scale/offset data is NULL");
+    }
+
+    dq_executor* e = new_executor(OP_ANTIQUANTIZE);
+    if (!e)
+        return fail(DQ_ERR_RUNTIME, "out of host memory");
+    dq::AqPlan& p = e->aq;
+    p.src = src->data;
+    p.scale = static_cast<const float*>(scale->data);
+    p.offset = offset ? static_cast<const float*>(offset->data) : nullptr;
+    p.m = m;
+    p.n = n;
+    p.policy = policy;
+    p.k_dim = policy == DQ_PER_GROUP ? k_dim : 1;
+    p.group_size = policy == DQ_PER_GROUP ? gs : 0;
+    p.src_kind = src->dtype == DQ_I8 ? dq::SRC_I8 : dq::SRC_F8E4M3;
+    p.dst_kind = dst->dtype == DQ_BF16 ? dq::DST_BF16 : dst->dtype == DQ_F16 ? dq::DST_F16 : dq::DST_F32;
+    p.dst = dst->data;
+    p.rows_per_tile = 16;
+    *executor = e;
+    return ok();
+}
+
+dq_status dq_antiquantize(void* workspace, size_t workspace_size, dq_executor* executor,
+                          hipStream_t stream)
+{
+    (void)workspace;
+    (void)workspace_size;
+    if (!executor)
+        return fail(DQ_ERR_NULLPTR, "executor is NULL");
+    dq_executor* e = executor;
+    if (e->op != OP_ANTIQUANTIZE) {
+        delete e;
+        return fail(DQ_ERR_PARAM, "executor was not made by dq_antiquantize_get_workspace_size");
+    }
+    dq::AqPlan p = e->aq;
+    delete e;
+    if (p.m == 0)
+        return ok();
+    hipError_t err = dq::launch_antiquantize(p, stream);
+    if (err != hipSuccess)
+        return fail(DQ_ERR_RUNTIME, "antiquantize launch failed: %s", hipGetErrorString(err));
+    return ok();
+}
+
+// ---------------------------------------------------------------------------
+// Copy probe
+// ---------------------------------------------------------------------------
+dq_status dq_copy_probe(void* dst, const void* src, size_t bytes, hipStream_t stream)
+{
+    if (bytes == 0)
+        return ok();
+    if (!dst || !src)
+        return fail(DQ_ERR_NULLPTR, "dst/src is NULL");
+    if (bytes % 16 != 0 || !aligned(dst, 16) || !aligned(src, 16))
+        return fail(DQ_ERR_ALIGN, "copy probe needs 16-byte aligned pointers and size");
+    const uintptr_t s0 = reinterpret_cast<uintptr_t>(src), d0 = reinterpret_cast<uintptr_t>(dst);
+    if (s0 < d0 + bytes && d0 < s0 + bytes)
+        return fail(DQ_ERR_OVERLAP, "copy probe buffers overlap");
+    hipError_t err = dq::launch_copy_probe(dst, src, bytes, stream);
+    if (err != hipSuccess)
+        return fail(DQ_ERR_RUNTIME, "copy probe launch failed: %s", hipGetErrorString(err));
+    return ok();
+}
+
+}  // extern "C"

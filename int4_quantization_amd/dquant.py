@@ -1,0 +1,285 @@
+"""ctypes binding of libdquant (include/dquant.h).
+
+The functions named ``dq_*`` mirror the C entry points one for one and only
+marshal arguments: torch tensors become ``dq_tensor`` descriptors (data
+pointer, dtype code, dims), executors travel as opaque handles, the stream
+is the current HIP stream unless one is given.  The convenience wrappers
+``dynamic_quant``, ``ada_layernorm_quant`` and ``antiquantize`` allocate the
+outputs with torch (device memory only) and run both phases.
+
+Every computation happens in the HIP kernels of ``libdquant.so``; there is
+no fallback of any kind.  If the library has not been built, every call
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libdquant.so")
+
+# dq_status
+SUCCESS, ERR_NULLPTR, ERR_DTYPE, ERR_SHAPE, ERR_ALIGN, ERR_PARAM, ERR_OVERLAP, ERR_WORKSPACE, \
+    ERR_RUNTIME = range(9)
+STATUS_NAMES = ["DQ_SUCCESS", "DQ_ERR_NULLPTR", "DQ_ERR_DTYPE", "DQ_ERR_SHAPE", "DQ_ERR_ALIGN",
+                "DQ_ERR_PARAM", "DQ_ERR_OVERLAP", "DQ_ERR_WORKSPACE", "DQ_ERR_RUNTIME"]
+# dq_dtype
+F32, F16, BF16, I8, I4, I32, F8E4M3 = range(7)
+# dq_antiquant_policy
+POLICIES = {"per_tensor": 0, "per_channel": 1, "per_token": 2, "per_group": 3}
+
+MAX_DIMS = 8
+
+EXPORTS = [
+    "dq_dynamic_quant_get_workspace_size", "dq_dynamic_quant",
+    "dq_ada_layernorm_quant_get_workspace_size", "dq_ada_layernorm_quant",
+    "dq_antiquantize_get_workspace_size", "dq_antiquantize",
+    "dq_executor_destroy", "dq_get_last_error", "dq_copy_probe",
+]
+
+
+class DquantError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        self.status = status
+        name = STATUS_NAMES[status] if 0 <= status < len(STATUS_NAMES) else str(status)
+        super().__init__(f"{name}: {message}")
+
+
+class DqTensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int), ("ndim", ctypes.c_int32),
+                ("dims", ctypes.c_int64 * MAX_DIMS)]
+
+
+_P = ctypes.POINTER
+_vp = ctypes.c_void_p
+_lib: Optional[ctypes.CDLL] = None
+
+
+def library() -> ctypes.CDLL:
+    """Load libdquant.so (built in-tree).  Raises if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(library_path):
+            raise RuntimeError(f"{library_path} is not built; run __graft_entry__.build() "
+                               "(hipcc, gfx950) first -- there is no fallback path")
+        lib = ctypes.CDLL(library_path)
+        st = ctypes.c_int
+        lib.dq_dynamic_quant_get_workspace_size.argtypes = [
+            _P(DqTensor), _P(DqTensor), _P(DqTensor), ctypes.c_int, _P(DqTensor), _P(DqTensor),
+            _P(DqTensor), _P(ctypes.c_size_t), _P(_vp)]
+        lib.dq_dynamic_quant_get_workspace_size.restype = st
+        lib.dq_ada_layernorm_quant_get_workspace_size.argtypes = [
+            _P(DqTensor), _P(DqTensor), _P(DqTensor), _P(DqTensor), _P(DqTensor), _P(DqTensor),
+            ctypes.c_double, _P(DqTensor), _P(DqTensor), _P(ctypes.c_size_t), _P(_vp)]
+        lib.dq_ada_layernorm_quant_get_workspace_size.restype = st
+        lib.dq_antiquantize_get_workspace_size.argtypes = [
+            _P(DqTensor), _P(DqTensor), _P(DqTensor), ctypes.c_int, ctypes.c_int32, ctypes.c_uint32,
+            _P(DqTensor), _P(ctypes.c_size_t), _P(_vp)]
+        lib.dq_antiquantize_get_workspace_size.restype = st
+        for name in ("dq_dynamic_quant", "dq_ada_layernorm_quant", "dq_antiquantize"):
+            fn = getattr(lib, name)
+            fn.argtypes = [_vp, ctypes.c_size_t, _vp, _vp]
+            fn.restype = st
+        lib.dq_executor_destroy.argtypes = [_vp]
+        lib.dq_executor_destroy.restype = None
+        lib.dq_get_last_error.argtypes = []
+        lib.dq_get_last_error.restype = ctypes.c_char_p
+        lib.dq_copy_probe.argtypes = [_vp, _vp, ctypes.c_size_t, _vp]
+        lib.dq_copy_probe.restype = st
+        _lib = lib
+    return _lib
+
+
+def dq_get_last_error() -> str:
+    return library().dq_get_last_error().decode()
+
+
+def _check(status: int) -> None:
+    if status != SUCCESS:
+        raise DquantError(status, dq_get_last_error())
+
+
+_TORCH_CODES = {
+    torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16, torch.int8: I8,
+    torch.int32: I32, torch.float8_e4m3fn: F8E4M3,
+}
+
+
+def tensor_desc(t: Optional[torch.Tensor], dtype: Optional[int] = None,
+                dims: Optional[Sequence[int]] = None) -> Optional[DqTensor]:
+    """Descriptor of a dense row-major tensor (None stays None).
+
+    ``dtype`` / ``dims`` override the tensor's own; an INT4 output travels as
+    a uint8 tensor of packed bytes with dtype=I4 and its logical dims.
+    """
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("libdquant takes dense row-major tensors")
+    d = DqTensor()
+    d.data = t.data_ptr() if t.numel() > 0 else None
+    d.dtype = _TORCH_CODES[t.dtype] if dtype is None else dtype
+    shape = list(t.shape) if dims is None else list(dims)
+    if len(shape) > MAX_DIMS:
+        raise ValueError("at most 8 dimensions")
+    d.ndim = len(shape)
+    for i, s in enumerate(shape):
+        d.dims[i] = int(s)
+    return d
+
+
+def _ref(d: Optional[DqTensor]):
+    return None if d is None else ctypes.byref(d)
+
+
+def _stream_handle(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _y_desc(y: torch.Tensor, x_shape, out_dtype: Optional[str]):
+    if out_dtype is None:
+        out_dtype = {torch.int8: "int8", torch.int32: "int32", torch.uint8: "int4"}[y.dtype]
+    if out_dtype == "int4":
+        return tensor_desc(y, I4, list(x_shape))
+    if out_dtype == "int32":
+        return tensor_desc(y, I32)
+    return tensor_desc(y, I8)
+
+
+# -- phase 1 / phase 2 entry points, named as in dquant.h ---------------------
+
+def dq_dynamic_quant_get_workspace_size(x, smooth_scales, group_index, symmetric, y, scale, offset,
+                                        out_dtype: Optional[str] = None) -> Tuple[int, int]:
+    """Returns (workspace_size, executor handle).  ``y`` is int8 (INT8),
+    uint8 [..., N/2] (INT4) or int32 [..., N/8] (INT32)."""
+    lib = library()
+    descs = [tensor_desc(x), tensor_desc(smooth_scales), tensor_desc(group_index),
+             _y_desc(y, x.shape, out_dtype), tensor_desc(scale), tensor_desc(offset)]
+    ws = ctypes.c_size_t(0)
+    ex = _vp(None)
+    _check(lib.dq_dynamic_quant_get_workspace_size(
+        _ref(descs[0]), _ref(descs[1]), _ref(descs[2]), 1 if symmetric else 0, _ref(descs[3]),
+        _ref(descs[4]), _ref(descs[5]), ctypes.byref(ws), ctypes.byref(ex)))
+    return ws.value, ex.value
+
+
+def dq_dynamic_quant(workspace, workspace_size: int, executor: int, stream=None) -> None:
+    _check(library().dq_dynamic_quant(_ws_ptr(workspace), workspace_size, executor,
+                                      _stream_handle(stream)))
+
+
+def dq_ada_layernorm_quant_get_workspace_size(x, scale, shift, weight, bias, smooth_scales,
+                                              epsilon: float, out, quant_scale) -> Tuple[int, int]:
+    lib = library()
+    d = [tensor_desc(t) for t in (x, scale, shift, weight, bias, smooth_scales, out, quant_scale)]
+    ws = ctypes.c_size_t(0)
+    ex = _vp(None)
+    _check(lib.dq_ada_layernorm_quant_get_workspace_size(
+        _ref(d[0]), _ref(d[1]), _ref(d[2]), _ref(d[3]), _ref(d[4]), _ref(d[5]), float(epsilon),
+        _ref(d[6]), _ref(d[7]), ctypes.byref(ws), ctypes.byref(ex)))
+    return ws.value, ex.value
+
+
+def dq_ada_layernorm_quant(workspace, workspace_size: int, executor: int, stream=None) -> None:
+    _check(library().dq_ada_layernorm_quant(_ws_ptr(workspace), workspace_size, executor,
+                                            _stream_handle(stream)))
+
+
+def dq_antiquantize_get_workspace_size(src, scale, offset, policy, k_dim: int, group_size: int,
+                                       dst) -> Tuple[int, int]:
+    lib = library()
+    pol = POLICIES[policy] if isinstance(policy, str) else int(policy)
+    d = [tensor_desc(t) for t in (src, scale, offset, dst)]
+    ws = ctypes.c_size_t(0)
+    ex = _vp(None)
+    _check(lib.dq_antiquantize_get_workspace_size(
+        _ref(d[0]), _ref(d[1]), _ref(d[2]), pol, int(k_dim), int(group_size), _ref(d[3]),
+        ctypes.byref(ws), ctypes.byref(ex)))
+    return ws.value, ex.value
+
+
+def dq_antiquantize(workspace, workspace_size: int, executor: int, stream=None) -> None:
+    _check(library().dq_antiquantize(_ws_ptr(workspace), workspace_size, executor,
+                                     _stream_handle(stream)))
+
+
+def dq_executor_destroy(executor: int) -> None:
+    library().dq_executor_destroy(executor)
+
+
+def dq_copy_probe(dst: torch.Tensor, src: torch.Tensor, nbytes: Optional[int] = None,
+                  stream=None) -> None:
+    n = src.numel() * src.element_size() if nbytes is None else nbytes
+    _check(library().dq_copy_probe(dst.data_ptr(), src.data_ptr(), n, _stream_handle(stream)))
+
+
+def _ws_ptr(workspace) -> Optional[int]:
+    if workspace is None:
+        return None
+    if isinstance(workspace, int):
+        return workspace
+    return workspace.data_ptr()
+
+
+def _workspace(size: int, device) -> Optional[torch.Tensor]:
+    return torch.empty(size, dtype=torch.uint8, device=device) if size > 0 else None
+
+
+# -- convenience wrappers ------------------------------------------------------
+
+def dynamic_quant(x: torch.Tensor, smooth_scales: Optional[torch.Tensor] = None,
+                  group_index: Optional[torch.Tensor] = None, symmetric: bool = True,
+                  out_dtype: str = "int8", stream=None):
+    """Per-token dynamic quantization.  Returns (y, scale, offset); offset is
+    None when symmetric.  y: int8 [..., N] ('int8'), uint8 [..., N/2] packed
+    ('int4'), int32 [..., N/8] ('int32')."""
+    lead = tuple(x.shape[:-1])
+    n = x.shape[-1]
+    dev = x.device
+    if out_dtype == "int8":
+        y = torch.empty(x.shape, dtype=torch.int8, device=dev)
+    elif out_dtype == "int4":
+        y = torch.empty(lead + (n // 2,), dtype=torch.uint8, device=dev)
+    elif out_dtype == "int32":
+        y = torch.empty(lead + (n // 8,), dtype=torch.int32, device=dev)
+    else:
+        raise ValueError(f"unknown out_dtype {out_dtype}")
+    scale = torch.empty(lead, dtype=torch.float32, device=dev)
+    offset = None if symmetric else torch.empty(lead, dtype=torch.float32, device=dev)
+    ws, ex = dq_dynamic_quant_get_workspace_size(x, smooth_scales, group_index, symmetric, y, scale,
+                                                 offset, out_dtype)
+    dq_dynamic_quant(_workspace(ws, dev), ws, ex, stream)
+    return y, scale, offset
+
+
+def ada_layernorm_quant(x: torch.Tensor, scale: torch.Tensor, shift: torch.Tensor,
+                        weight: Optional[torch.Tensor] = None, bias: Optional[torch.Tensor] = None,
+                        smooth_scales: Optional[torch.Tensor] = None, epsilon: float = 1e-5,
+                        stream=None):
+    """AdaLayerNorm + symmetric INT8 quantization.  Returns (out int8
+    [B, S, H], quant_scale fp32 [B, S])."""
+    B, S, _ = x.shape
+    out = torch.empty(x.shape, dtype=torch.int8, device=x.device)
+    qs = torch.empty((B, S), dtype=torch.float32, device=x.device)
+    ws, ex = dq_ada_layernorm_quant_get_workspace_size(x, scale, shift, weight, bias, smooth_scales,
+                                                       epsilon, out, qs)
+    dq_ada_layernorm_quant(_workspace(ws, x.device), ws, ex, stream)
+    return out, qs
+
+
+def antiquantize(src: torch.Tensor, scale: torch.Tensor, offset: Optional[torch.Tensor] = None,
+                 policy="per_tensor", k_dim: int = 1, group_size: int = 0,
+                 dst_dtype: torch.dtype = torch.bfloat16, stream=None) -> torch.Tensor:
+    """Dequantize src [m, n] (int8 or float8_e4m3fn) into dst_dtype."""
+    dst = torch.empty(src.shape, dtype=dst_dtype, device=src.device)
+    ws, ex = dq_antiquantize_get_workspace_size(src, scale, offset, policy, k_dim, group_size, dst)
+    dq_antiquantize(_workspace(ws, src.device), ws, ex, stream)
+    return dst

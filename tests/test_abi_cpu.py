@@ -1,0 +1,281 @@
+"""The C ABI without a GPU: the library loads, exports every entry point the
+header declares, and phase 1 (validation, no HIP calls) returns the right
+status for every rule it enforces.  No kernel is launched here."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from int4_quantization_amd import dquant as D
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(D.library_path):
+        from int4_quantization_amd import build
+        build.build(verbose=False)
+    return D.library()
+
+
+def desc(dtype, dims, ptr=0x10000):
+    d = D.DqTensor()
+    d.data = ptr
+    d.dtype = dtype
+    d.ndim = len(dims)
+    for i, s in enumerate(dims):
+        d.dims[i] = s
+    return d
+
+
+def ref(d):
+    return None if d is None else ctypes.byref(d)
+
+
+def dq_ws(lib, x, sm, gi, sym, y, sc, off):
+    ws = ctypes.c_size_t(99)
+    ex = ctypes.c_void_p(None)
+    st = lib.dq_dynamic_quant_get_workspace_size(ref(x), ref(sm), ref(gi), sym, ref(y), ref(sc),
+                                                 ref(off), ctypes.byref(ws), ctypes.byref(ex))
+    if st == D.SUCCESS:
+        assert ex.value and ws.value == 0
+        lib.dq_executor_destroy(ex)
+    else:
+        assert ex.value is None
+        assert lib.dq_get_last_error().decode() != ""
+    return st
+
+
+def test_exports_match_header(lib):
+    header = open(os.path.join(ROOT, "include", "dquant.h")).read()
+    declared = set(re.findall(r"^\s*(?:dq_status|void|const char\*)\s+(dq_\w+)\s*\(", header, re.M))
+    assert declared == set(D.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_struct_layout_matches_header():
+    assert ctypes.sizeof(D.DqTensor) == 80
+    assert D.DqTensor.dims.offset == 16
+
+
+# ---- DynamicQuant ------------------------------------------------------------
+
+R, N = 6, 64
+
+
+def good_dq():
+    return dict(x=desc(D.BF16, [R, N]), sm=None, gi=None, sym=1, y=desc(D.I8, [R, N]),
+                sc=desc(D.F32, [R]), off=None)
+
+
+@pytest.mark.parametrize("change,status", [
+    ({}, D.SUCCESS),
+    ({"x": None}, D.ERR_NULLPTR),
+    ({"y": None}, D.ERR_NULLPTR),
+    ({"sc": None}, D.ERR_NULLPTR),
+    ({"x": desc(D.BF16, [R, N], ptr=0)}, D.ERR_NULLPTR),
+    ({"x": desc(D.F32, [R, N])}, D.ERR_DTYPE),
+    ({"y": desc(D.F16, [R, N])}, D.ERR_DTYPE),
+    ({"sc": desc(D.F16, [R])}, D.ERR_DTYPE),
+    ({"x": desc(D.BF16, [R, 0]), "y": desc(D.I8, [R, 0])}, D.ERR_SHAPE),
+    ({"y": desc(D.I8, [R, N + 1])}, D.ERR_SHAPE),
+    ({"sc": desc(D.F32, [R + 1])}, D.ERR_SHAPE),
+    ({"sc": desc(D.F32, [R, 1])}, D.ERR_SHAPE),
+    ({"x": desc(D.BF16, [R, 7]), "y": desc(D.I4, [R, 7])}, D.ERR_SHAPE),       # INT4: even N
+    ({"x": desc(D.BF16, [R, 12]), "y": desc(D.I32, [R, 1])}, D.ERR_SHAPE),     # INT32: N % 8
+    ({"y": desc(D.I32, [R, N])}, D.ERR_SHAPE),                                 # INT32: [.., N/8]
+    ({"y": desc(D.I32, [R, N // 8])}, D.SUCCESS),
+    ({"y": desc(D.I4, [R, N])}, D.SUCCESS),
+    ({"off": desc(D.F32, [R])}, D.ERR_PARAM),                                  # sym with offset
+    ({"sym": 0}, D.ERR_NULLPTR),                                               # asym needs offset
+    ({"sym": 0, "off": desc(D.F16, [R])}, D.ERR_DTYPE),
+    ({"sym": 0, "off": desc(D.F32, [R + 2])}, D.ERR_SHAPE),
+    ({"sym": 0, "off": desc(D.F32, [R])}, D.SUCCESS),
+    ({"sm": desc(D.F32, [N])}, D.SUCCESS),
+    ({"sm": desc(D.F16, [N])}, D.ERR_DTYPE),
+    ({"sm": desc(D.F32, [N + 8])}, D.ERR_SHAPE),
+    ({"gi": desc(D.I32, [4])}, D.ERR_SHAPE),                                   # gi needs smooth
+    ({"gi": desc(D.I32, [4]), "sm": desc(D.F32, [4, N])}, D.SUCCESS),
+    ({"gi": desc(D.I8, [4]), "sm": desc(D.F32, [4, N])}, D.ERR_DTYPE),
+    ({"gi": desc(D.I32, [4]), "sm": desc(D.F32, [3, N])}, D.ERR_SHAPE),
+    ({"gi": desc(D.I32, [0]), "sm": desc(D.F32, [0, N])}, D.ERR_SHAPE),
+    ({"gi": desc(D.I32, [4]), "sm": desc(D.F32, [N])}, D.ERR_SHAPE),
+    ({"x": desc(D.BF16, [0, N]), "y": desc(D.I8, [0, N]), "sc": desc(D.F32, [0])}, D.SUCCESS),
+    ({"x": desc(D.F16, [2, 3, N]), "y": desc(D.I8, [2, 3, N]), "sc": desc(D.F32, [2, 3])}, D.SUCCESS),
+    ({"x": desc(D.F16, [2, 3, N]), "y": desc(D.I8, [2, 3, N]), "sc": desc(D.F32, [6])}, D.ERR_SHAPE),
+])
+def test_dynamic_quant_validation(lib, change, status):
+    a = good_dq()
+    a.update(change)
+    assert dq_ws(lib, a["x"], a["sm"], a["gi"], a["sym"], a["y"], a["sc"], a["off"]) == status
+
+
+# ---- AdaLayerNorm-quant ------------------------------------------------------
+
+B, S, H = 2, 3, 64
+
+
+def good_ada():
+    return dict(x=desc(D.BF16, [B, S, H]), sc=desc(D.BF16, [B, 1, H]), sh=desc(D.BF16, [B, 1, H]),
+                w=desc(D.BF16, [H]), b=desc(D.BF16, [H]), sm=desc(D.F32, [H]), eps=1e-5,
+                out=desc(D.I8, [B, S, H]), qs=desc(D.F32, [B, S]))
+
+
+def ada_ws(lib, a):
+    ws = ctypes.c_size_t(99)
+    ex = ctypes.c_void_p(None)
+    st = lib.dq_ada_layernorm_quant_get_workspace_size(
+        ref(a["x"]), ref(a["sc"]), ref(a["sh"]), ref(a["w"]), ref(a["b"]), ref(a["sm"]), a["eps"],
+        ref(a["out"]), ref(a["qs"]), ctypes.byref(ws), ctypes.byref(ex))
+    if st == D.SUCCESS:
+        assert ex.value and ws.value == 0
+        lib.dq_executor_destroy(ex)
+    return st
+
+
+@pytest.mark.parametrize("change,status", [
+    ({}, D.SUCCESS),
+    ({"w": None, "b": None, "sm": None}, D.SUCCESS),
+    ({"sc": desc(D.BF16, [B, H]), "sh": desc(D.BF16, [B, H])}, D.SUCCESS),
+    ({"x": None}, D.ERR_NULLPTR),
+    ({"sc": None}, D.ERR_NULLPTR),
+    ({"out": None}, D.ERR_NULLPTR),
+    ({"x": desc(D.F32, [B, S, H])}, D.ERR_DTYPE),
+    ({"sc": desc(D.F16, [B, 1, H])}, D.ERR_DTYPE),
+    ({"w": desc(D.F32, [H])}, D.ERR_DTYPE),
+    ({"sm": desc(D.BF16, [H])}, D.ERR_DTYPE),
+    ({"out": desc(D.I4, [B, S, H])}, D.ERR_DTYPE),
+    ({"qs": desc(D.F16, [B, S])}, D.ERR_DTYPE),
+    ({"x": desc(D.BF16, [B * S, H])}, D.ERR_SHAPE),
+    ({"sc": desc(D.BF16, [B, 2, H])}, D.ERR_SHAPE),
+    ({"sh": desc(D.BF16, [B + 1, 1, H])}, D.ERR_SHAPE),
+    ({"w": desc(D.BF16, [H + 1])}, D.ERR_SHAPE),
+    ({"sm": desc(D.F32, [2 * H])}, D.ERR_SHAPE),
+    ({"out": desc(D.I8, [B, S, H + 8])}, D.ERR_SHAPE),
+    ({"qs": desc(D.F32, [B * S])}, D.ERR_SHAPE),
+    ({"x": desc(D.BF16, [B, S, 0]), "sc": desc(D.BF16, [B, 1, 0]), "sh": desc(D.BF16, [B, 1, 0]),
+      "w": None, "b": None, "sm": None, "out": desc(D.I8, [B, S, 0])}, D.ERR_SHAPE),
+    ({"eps": 0.0}, D.ERR_PARAM),
+    ({"eps": -1.0}, D.ERR_PARAM),
+    ({"eps": float("inf")}, D.ERR_PARAM),
+    ({"eps": float("nan")}, D.ERR_PARAM),
+])
+def test_ada_validation(lib, change, status):
+    a = good_ada()
+    a.update(change)
+    assert ada_ws(lib, a) == status
+
+
+# ---- AntiQuantize ------------------------------------------------------------
+
+M, NN = 40, 256
+
+
+def aq_ws(lib, src, sc, off, pol, kdim, gs, dst):
+    ws = ctypes.c_size_t(99)
+    ex = ctypes.c_void_p(None)
+    st = lib.dq_antiquantize_get_workspace_size(ref(src), ref(sc), ref(off), pol, kdim, gs, ref(dst),
+                                                ctypes.byref(ws), ctypes.byref(ex))
+    if st == D.SUCCESS:
+        assert ex.value and ws.value == 0
+        lib.dq_executor_destroy(ex)
+    return st
+
+
+SRC_PTR, DST_PTR = 0x100000, 0x800000
+
+
+@pytest.mark.parametrize("pol,kdim,gs,sshape,status", [
+    (0, -1, 0, [1], D.SUCCESS),
+    (0, 1, 0, [M], D.ERR_SHAPE),
+    (1, 1, 0, [1, NN], D.SUCCESS),
+    (1, 1, 0, [NN], D.SUCCESS),
+    (1, 1, 0, [M, 1], D.ERR_SHAPE),
+    (2, 1, 0, [M, 1], D.SUCCESS),
+    (2, 1, 0, [1, NN], D.ERR_SHAPE),
+    (3, 1, 128, [M, 2], D.SUCCESS),
+    (3, 1, 96, [M, 3], D.SUCCESS),          # ceil(256 / 96) = 3, short last group
+    (3, 1, 96, [M, 2], D.ERR_SHAPE),
+    (3, 0, 32, [2, NN], D.SUCCESS),         # ceil(40 / 32) = 2
+    (3, 0, 32, [M, 8], D.ERR_SHAPE),
+    (3, 1, 0, [M, 2], D.ERR_PARAM),         # groupSize must be > 0
+    (3, 1, 48, [M, 6], D.ERR_PARAM),        # and a multiple of 32
+    (3, 2, 32, [M, 8], D.ERR_PARAM),        # kDim is 0 or 1
+    (4, 1, 0, [1], D.ERR_PARAM),            # unknown policy
+])
+def test_antiquantize_policy_shapes(lib, pol, kdim, gs, sshape, status):
+    src = desc(D.I8, [M, NN], SRC_PTR)
+    dst = desc(D.BF16, [M, NN], DST_PTR)
+    sc = desc(D.F32, sshape, 0x20000)
+    off = desc(D.F32, sshape, 0x40000)
+    assert aq_ws(lib, src, sc, off, pol, kdim, gs, dst) == status
+    if status == D.SUCCESS:
+        assert aq_ws(lib, src, sc, None, pol, kdim, gs, dst) == D.SUCCESS
+
+
+@pytest.mark.parametrize("src,dst,off,status", [
+    (desc(D.I8, [M, NN], SRC_PTR), desc(D.F16, [M, NN], DST_PTR), None, D.SUCCESS),
+    (desc(D.F8E4M3, [M, NN], SRC_PTR), desc(D.BF16, [M, NN], DST_PTR), None, D.SUCCESS),
+    (desc(D.I8, [M, NN], SRC_PTR), desc(D.F32, [M, NN], DST_PTR), None, D.SUCCESS),
+    (desc(D.F16, [M, NN], SRC_PTR), desc(D.BF16, [M, NN], DST_PTR), None, D.ERR_DTYPE),
+    (desc(D.I8, [M, NN], SRC_PTR), desc(D.I8, [M, NN], DST_PTR), None, D.ERR_DTYPE),
+    (desc(D.I8, [M, NN], SRC_PTR), desc(D.BF16, [M, NN], DST_PTR), desc(D.F16, [1], 0x40000), D.ERR_DTYPE),
+    (desc(D.I8, [M, NN], SRC_PTR), desc(D.BF16, [M, NN], DST_PTR), desc(D.F32, [2], 0x40000), D.ERR_SHAPE),
+    (desc(D.I8, [2, M, NN], SRC_PTR), desc(D.BF16, [2, M, NN], DST_PTR), None, D.ERR_SHAPE),
+    (desc(D.I8, [M, NN], SRC_PTR), desc(D.BF16, [M, NN + 32], DST_PTR), None, D.ERR_SHAPE),
+    (desc(D.I8, [M, 48], SRC_PTR), desc(D.BF16, [M, 48], DST_PTR), None, D.ERR_ALIGN),   # 48 B rows
+    (desc(D.I8, [M, NN], SRC_PTR + 8), desc(D.BF16, [M, NN], DST_PTR), None, D.ERR_ALIGN),
+    (desc(D.I8, [M, NN], SRC_PTR), desc(D.BF16, [M, NN], SRC_PTR + 64), None, D.ERR_OVERLAP),
+    (desc(D.I8, [M, NN], SRC_PTR), desc(D.BF16, [M, NN], SRC_PTR - 2 * M * NN + 16), None, D.ERR_OVERLAP),
+    (desc(D.I8, [0, NN], SRC_PTR), desc(D.BF16, [0, NN], DST_PTR), None, D.SUCCESS),
+])
+def test_antiquantize_types_alignment_overlap(lib, src, dst, off, status):
+    sc = desc(D.F32, [1], 0x20000)
+    assert aq_ws(lib, src, sc, off, 0, -1, 0, dst) == status
+
+
+def test_antiquantize_channel_params_alignment(lib):
+    src = desc(D.I8, [M, NN], SRC_PTR)
+    dst = desc(D.BF16, [M, NN], DST_PTR)
+    assert aq_ws(lib, src, desc(D.F32, [1, NN], 0x20004), None, 1, 1, 0, dst) == D.ERR_ALIGN
+    assert aq_ws(lib, src, desc(D.F32, [M, 1], 0x20004), None, 2, 1, 0, dst) == D.SUCCESS
+
+
+# ---- execute-phase errors that never reach the device -------------------------
+
+def test_execute_null_executor(lib):
+    for fn in (lib.dq_dynamic_quant, lib.dq_ada_layernorm_quant, lib.dq_antiquantize):
+        assert fn(None, 0, None, None) == D.ERR_NULLPTR
+
+
+def test_execute_wrong_executor_kind(lib):
+    a = good_dq()
+    ws = ctypes.c_size_t(0)
+    ex = ctypes.c_void_p(None)
+    st = lib.dq_dynamic_quant_get_workspace_size(ref(a["x"]), None, None, 1, ref(a["y"]), ref(a["sc"]),
+                                                 None, ctypes.byref(ws), ctypes.byref(ex))
+    assert st == D.SUCCESS
+    # consumed (freed) even though it fails
+    assert lib.dq_antiquantize(None, 0, ex, None) == D.ERR_PARAM
+    assert "dq_antiquantize_get_workspace_size" in lib.dq_get_last_error().decode()
+
+
+def test_copy_probe_validation(lib):
+    assert lib.dq_copy_probe(0x1000, 0x2001, 64, None) == D.ERR_ALIGN
+    assert lib.dq_copy_probe(0x1000, 0x2000, 60, None) == D.ERR_ALIGN
+    assert lib.dq_copy_probe(0x1000, 0x1010, 64, None) == D.ERR_OVERLAP
+    assert lib.dq_copy_probe(None, 0x2000, 64, None) == D.ERR_NULLPTR
+    assert lib.dq_copy_probe(0x1000, 0x2000, 0, None) == D.SUCCESS
+
+
+def test_python_binding_raises_without_gpu_launch(lib):
+    x = torch.zeros(4, 7, dtype=torch.bfloat16)
+    with pytest.raises(D.DquantError) as e:
+        D.dq_dynamic_quant_get_workspace_size(x, None, None, True, torch.zeros(4, 3, dtype=torch.uint8),
+                                              torch.zeros(4), None, "int4")
+    assert e.value.status == D.ERR_SHAPE
+    assert "even" in str(e.value)

@@ -1,0 +1,63 @@
+"""AdaLayerNorm-quant on the GPU (through the C ABI) against the CPU oracle
+at the stated tolerance (quantScale within 1e-5 relative; codes within +-1,
+differing on at most 0.01 % of elements): register-resident rows of 1..16
+vectors per lane, the generic path (H not a multiple of 8, H > 8192),
+optional weight / bias / smooth, [B,1,H] and [B,H] modulation, fp16 / bf16,
+chunks of rows that straddle batches."""
+import numpy as np
+import pytest
+import torch
+
+from int4_quantization_amd import synth
+from parity import DEV, announce, check_ada_layernorm_quant
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+SHAPES = [(2, 37, 3072), (1, 5, 256), (3, 7, 1000), (2, 9, 64), (1, 4, 8192), (5, 3, 512),
+          (2, 3, 250), (1, 3, 10000), (2, 11, 6144)]
+
+
+@pytest.mark.parametrize("B,S,H", SHAPES, ids=[f"{b}x{s}x{h}" for b, s, h in SHAPES])
+@pytest.mark.parametrize("affine,smooth", [(True, True), (False, False), (True, False)],
+                         ids=["full", "bare", "nosmooth"])
+def test_ada_parity(orc, B, S, H, affine, smooth):
+    announce("ada_layernorm_quant", B, S, H, affine, smooth)
+    inp = synth.ada_inputs(B, S, H, B * 1000 + S * 10 + H, affine=affine, smooth=smooth)
+    check_ada_layernorm_quant(orc, inp)
+
+
+@pytest.mark.parametrize("dtype", ["float16", "bfloat16"])
+def test_ada_dtype_and_2d_modulation(orc, dtype):
+    announce("ada_layernorm_quant dtype", dtype)
+    inp = synth.ada_inputs(3, 20, 1024, 31, dtype=dtype)
+    check_ada_layernorm_quant(orc, inp)
+    inp["scale"] = inp["scale"].reshape(3, 1024).contiguous()
+    inp["shift"] = inp["shift"].reshape(3, 1024).contiguous()
+    check_ada_layernorm_quant(orc, inp)
+
+
+def test_ada_special_rows(orc):
+    """Constant rows (variance 0), scale = -1 (y = shift * smooth exactly) and
+    a large-offset row."""
+    announce("ada_layernorm_quant special rows")
+    inp = synth.ada_inputs(2, 6, 512, 41)
+    x = inp["x"].float()
+    x[0, 0] = 1.5
+    x[1, 2] = 0.0
+    x[1, 3] = x[1, 3] * 100 + 1000
+    inp["x"] = x.to(torch.bfloat16)
+    check_ada_layernorm_quant(orc, inp)
+    inp["scale"] = -torch.ones_like(inp["scale"])
+    check_ada_layernorm_quant(orc, inp)
+
+
+def test_ada_deterministic():
+    announce("ada_layernorm_quant determinism")
+    import int4_quantization_amd as dq
+    inp = synth.ada_inputs(2, 64, 3072, 51)
+    args = [inp[k].to(DEV) for k in ("x", "scale", "shift", "weight", "bias", "smooth")]
+    a = dq.ada_layernorm_quant(*args, epsilon=inp["eps"])
+    b = dq.ada_layernorm_quant(*args, epsilon=inp["eps"])
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1].view(torch.int32), b[1].view(torch.int32))
