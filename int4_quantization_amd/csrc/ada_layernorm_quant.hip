@@ -164,7 +164,7 @@ __global__ __launch_bounds__(kBlock) void ada_vec_kernel(AdaArgs a)
 #pragma unroll
             for (int i = 0; i < VPL; ++i) {
                 const int64_t k = static_cast<int64_t>(i) * kWave + lane;
-                raw[i] = k < nvec ? xr[k] : make_uint4(0, 0, 0, 0);
+                raw[i] = k < nvec ? ld_stream16(xr + k) : make_uint4(0, 0, 0, 0);
             }
             float v[VPL][8];
             float cnt = 0.0f, sum = 0.0f;
@@ -235,7 +235,7 @@ __global__ __launch_bounds__(kBlock) void ada_vec_kernel(AdaArgs a)
                         for (int j = 0; j < 8; ++j)
                             c[j] = q8<false>(v[i][j], qp);
                     }
-                    orow[k] = make_uint2(pack4_i8(c[0], c[1], c[2], c[3]), pack4_i8(c[4], c[5], c[6], c[7]));
+                    st_stream8(orow + k, make_uint2(pack4_i8(c[0], c[1], c[2], c[3]), pack4_i8(c[4], c[5], c[6], c[7])));
                 }
             }
         }

@@ -2,17 +2,22 @@
 // (AntiQuantize, 功能说明: PER_TENSOR / PER_CHANNEL / PER_TOKEN / PER_GROUP,
 // 表1 kDim, 表2 groupSize).
 //
-// A wave owns a tile of RB rows x 1024 columns: lane l holds the 16
-// contiguous elements [16c, 16c + 16) of column-vector c = strip*64 + l, so
-// each row of the tile is one 16-byte load per lane (1 KiB per wave,
-// coalesced) and 32 (bf16/fp16) or 64 (fp32) bytes of stores per lane.  All
-// RB loads are issued before any arithmetic so RB KiB per wave are in
-// flight.  Parameters that vary along n (PER_CHANNEL, PER_GROUP with
-// kDim = 0) are loaded once per tile into VGPRs -- a 16-element vector
-// never straddles a group because groupSize is a multiple of 32, and a
-// 16-row tile never straddles a kDim = 0 group for the same reason.
-// PER_TOKEN parameters are wave-uniform per row; PER_GROUP kDim = 1 needs
-// one parameter per lane per row.
+// Each wave owns one 1024-column strip and every G-th row of it (G = waves
+// per strip), so at any moment all waves work inside one band of rows that
+// sweeps down the matrix -- a compact DRAM footprint, which measured far
+// faster than giving each wave a contiguous block of rows.  A wave keeps
+// kPD of its rows in flight: before it converts row i it has already
+// requested the next kPD-1, and right after converting row i it requests
+// the one kPD steps ahead.  Lanes own E-element
+// chunks, E = 8 for bf16/fp16 output (16 bytes) and E = 4 for fp32: chunk c
+// of lane l covers columns strip*1024 + c*64*E + l*E, so every store
+// instruction of the wave writes 1 KiB of contiguous output and every load
+// instruction reads 64*E contiguous source bytes.  Source and destination
+// are streamed with non-temporal accesses.  Parameters that vary along n
+// are loaded once per wave (PER_CHANNEL) or once per group of rows
+// (PER_GROUP with kDim = 0); a chunk never straddles a group because
+// groupSize is a multiple of 32.  PER_TOKEN parameters are wave-uniform per
+// row; PER_GROUP with kDim = 1 needs one parameter per chunk per row.
 //
 // Arithmetic (the page omits the formula; the library's reading):
 //   dst = RN(RN(src + offset) * scale)   or   RN(src * scale)
@@ -25,7 +30,8 @@
 namespace dq {
 namespace {
 
-constexpr int kRB = 16;  // rows per wave tile
+constexpr int kPD = 2;               // rows of loads in flight per wave
+constexpr int64_t kTargetWaves = 16384;  // 256 CUs x 64 waves
 
 enum AqPolicyKind : int { PK_TENSOR = 0, PK_CHANNEL = 1, PK_TOKEN = 2, PK_GROUP_N = 3, PK_GROUP_M = 4 };
 
@@ -37,32 +43,36 @@ struct AqArgs {
     int64_t gs;        // group size (PER_GROUP)
     int64_t n_groups;  // ceil(n / gs) for kDim = 1
     void* dst;
-    int64_t strips;    // ceil(n / 1024)
-    int64_t tiles;     // strips * ceil(m / kRB)
+    int64_t strips;         // ceil(n / 1024)
+    int64_t row_step;       // G: waves per strip, the stride between a wave's rows
+    int64_t waves;          // strips * G
     int64_t nblocks;
 };
 
-// 16 source bytes -> 16 floats (exact).
+template <int DST>
+struct Chunk {
+    static constexpr int E = DST == DST_F32 ? 4 : 8;       // elements per chunk
+    static constexpr int NCH = 1024 / (kWave * E);         // chunks per lane per row
+    static constexpr int W = E / 4;                        // source dwords per chunk
+};
+
+// Four source bytes -> four floats (exact).
 template <int SRC>
-__device__ __forceinline__ void decode16(const uint4 raw, float (&v)[16])
+__device__ __forceinline__ void decode4(uint32_t w, float* v)
 {
-    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        if (SRC == SRC_I8) {
-            v[4 * i + 0] = static_cast<float>(static_cast<int8_t>(w[i] & 0xFFu));
-            v[4 * i + 1] = static_cast<float>(static_cast<int8_t>((w[i] >> 8) & 0xFFu));
-            v[4 * i + 2] = static_cast<float>(static_cast<int8_t>((w[i] >> 16) & 0xFFu));
-            v[4 * i + 3] = static_cast<float>(static_cast<int8_t>(w[i] >> 24));
-        } else {
-            // gfx950 converts OCP E4M3FN (NaN only at 0x7F / 0xFF, max 448).
-            const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w[i]), false);
-            const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w[i]), true);
-            v[4 * i + 0] = lo[0];
-            v[4 * i + 1] = lo[1];
-            v[4 * i + 2] = hi[0];
-            v[4 * i + 3] = hi[1];
-        }
+    if (SRC == SRC_I8) {
+        v[0] = static_cast<float>(static_cast<int8_t>(w & 0xFFu));
+        v[1] = static_cast<float>(static_cast<int8_t>((w >> 8) & 0xFFu));
+        v[2] = static_cast<float>(static_cast<int8_t>((w >> 16) & 0xFFu));
+        v[3] = static_cast<float>(static_cast<int8_t>(w >> 24));
+    } else {
+        // gfx950 converts OCP E4M3FN (NaN only at 0x7F / 0xFF, max 448).
+        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), false);
+        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), true);
+        v[0] = lo[0];
+        v[1] = lo[1];
+        v[2] = hi[0];
+        v[3] = hi[1];
     }
 }
 
@@ -86,31 +96,28 @@ __device__ __forceinline__ uint32_t pack_f16x2(float a, float b)
     return lo | (hi << 16);
 }
 
+// Store one chunk (16 bytes) of results.
 template <int DST>
-__device__ __forceinline__ void store16(void* dst_row, int64_t j0, const float (&t)[16])
+__device__ __forceinline__ void store_chunk(void* p, const float* t)
 {
     if (DST == DST_F32) {
-        float4* d = reinterpret_cast<float4*>(static_cast<float*>(dst_row) + j0);
-        d[0] = make_float4(t[0], t[1], t[2], t[3]);
-        d[1] = make_float4(t[4], t[5], t[6], t[7]);
-        d[2] = make_float4(t[8], t[9], t[10], t[11]);
-        d[3] = make_float4(t[12], t[13], t[14], t[15]);
+        st_stream16(p, make_uint4(__builtin_bit_cast(uint32_t, t[0]), __builtin_bit_cast(uint32_t, t[1]),
+                                  __builtin_bit_cast(uint32_t, t[2]), __builtin_bit_cast(uint32_t, t[3])));
+    } else if (DST == DST_BF16) {
+        st_stream16(p, make_uint4(pack_bf16x2(t[0], t[1]), pack_bf16x2(t[2], t[3]),
+                                  pack_bf16x2(t[4], t[5]), pack_bf16x2(t[6], t[7])));
     } else {
-        uint32_t p[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            p[i] = DST == DST_BF16 ? pack_bf16x2(t[2 * i], t[2 * i + 1]) : pack_f16x2(t[2 * i], t[2 * i + 1]);
-        uint4* d = reinterpret_cast<uint4*>(static_cast<uint16_t*>(dst_row) + j0);
-        d[0] = make_uint4(p[0], p[1], p[2], p[3]);
-        d[1] = make_uint4(p[4], p[5], p[6], p[7]);
+        st_stream16(p, make_uint4(pack_f16x2(t[0], t[1]), pack_f16x2(t[2], t[3]),
+                                  pack_f16x2(t[4], t[5]), pack_f16x2(t[6], t[7])));
     }
 }
 
-__device__ __forceinline__ void load16f(const float* p, float (&v)[16])
+template <int E>
+__device__ __forceinline__ void load_params(const float* p, float* v)
 {
     const float4* q = reinterpret_cast<const float4*>(p);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < E / 4; ++i) {
         const float4 f = q[i];
         v[4 * i + 0] = f.x;
         v[4 * i + 1] = f.y;
@@ -119,76 +126,137 @@ __device__ __forceinline__ void load16f(const float* p, float (&v)[16])
     }
 }
 
+template <int NCH, int W>
+__device__ __forceinline__ void load_row(uint32_t (&raw)[NCH][W], const uint8_t* row, const int64_t (&jc)[NCH],
+                                         const bool (&okc)[NCH])
+{
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        if (okc[c]) {
+            if (W == 2) {
+                const uint2 w2 = ld_stream8(row + jc[c]);
+                raw[c][0] = w2.x;
+                raw[c][W - 1] = w2.y;
+            } else {
+                raw[c][0] = ld_stream4(row + jc[c]);
+            }
+        }
+    }
+}
+
 template <int SRC, int DST, int PK, bool OFF>
 __global__ __launch_bounds__(kBlock) void aq_kernel(AqArgs a)
 {
+    using C = Chunk<DST>;
+    constexpr int E = C::E, NCH = C::NCH, W = C::W;
+    constexpr bool kPerElem = PK == PK_CHANNEL || PK == PK_GROUP_M;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
-    const int64_t tile = xcd_block(blockIdx.x, a.nblocks) * 4 + wave;
-    if (tile >= a.tiles)
+    const int64_t wid = xcd_block(blockIdx.x, a.nblocks) * 4 + wave;
+    if (wid >= a.waves)
         return;
-    const int64_t strip = tile % a.strips;
-    const int64_t i0 = (tile / a.strips) * kRB;
-    const int64_t j0 = (strip * kWave + lane) * 16;
-    if (j0 >= a.n)
-        return;  // right edge of the last strip; nothing below synchronizes
-    const int rows = static_cast<int>(a.m - i0 < kRB ? a.m - i0 : kRB);
-
-    // Issue all loads of the tile first.
-    const uint8_t* src = static_cast<const uint8_t*>(a.src);
-    uint4 raw[kRB];
+    const int64_t strip = wid % a.strips;
+    const int64_t G = a.row_step;
+    const int64_t r0 = wid / a.strips;
+    const int64_t r1 = a.m;
+    if (r0 >= r1)
+        return;
+    int64_t jc[NCH];
+    bool okc[NCH];
+    int64_t gcol[NCH];  // PER_GROUP kDim = 1: the chunk's group
 #pragma unroll
-    for (int r = 0; r < kRB; ++r)
-        if (r < rows)
-            raw[r] = *reinterpret_cast<const uint4*>(src + (i0 + r) * a.n + j0);
+    for (int c = 0; c < NCH; ++c) {
+        jc[c] = strip * 1024 + (c * kWave + lane) * E;
+        okc[c] = jc[c] < a.n;  // n is a multiple of 16, so a chunk is whole or absent
+        gcol[c] = PK == PK_GROUP_N ? jc[c] / a.gs : 0;
+    }
+    const uint8_t* src = static_cast<const uint8_t*>(a.src);
+    uint8_t* dst = static_cast<uint8_t*>(a.dst);
+    const int64_t out_elem = DST == DST_F32 ? 4 : 2;
 
-    // Parameters that stay fixed over the tile.
-    float sv[16], ov[16];
+    // Rows r0 .. r0 + kPD - 1 in flight before any arithmetic.
+    uint32_t raw[kPD][NCH][W];
+#pragma unroll
+    for (int k = 0; k < kPD; ++k)
+        if (r0 + k * G < r1)
+            load_row<NCH, W>(raw[k], src + (r0 + k * G) * a.n, jc, okc);
+
+    // Parameters fixed over many rows.
+    float sv[NCH][E], ov[NCH][E];
     float s_u = 0.0f, o_u = 0.0f;
+    int64_t g_lo = 0, g_hi = 0;  // PER_GROUP kDim = 0: rows of the group held in sv / ov
+    auto load_vec_params = [&](int64_t row_base) {
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            if (okc[c]) {
+                load_params<E>(a.scale + row_base + jc[c], sv[c]);
+                if (OFF)
+                    load_params<E>(a.offset + row_base + jc[c], ov[c]);
+            }
+        }
+    };
     if (PK == PK_TENSOR) {
         s_u = a.scale[0];
         if (OFF)
             o_u = a.offset[0];
-    } else if (PK == PK_CHANNEL || PK == PK_GROUP_M) {
-        const int64_t base = PK == PK_CHANNEL ? j0 : (i0 / a.gs) * a.n + j0;
-        load16f(a.scale + base, sv);
-        if (OFF)
-            load16f(a.offset + base, ov);
+    } else if (PK == PK_CHANNEL) {
+        load_vec_params(0);
+    } else if (PK == PK_GROUP_M) {
+        const int64_t g = r0 / a.gs;
+        load_vec_params(g * a.n);
+        g_lo = g * a.gs;
+        g_hi = g_lo + a.gs;
     }
 
-    const int64_t out_elem = DST == DST_F32 ? 4 : 2;
+    for (int64_t r = r0; r < r1; r += kPD * G) {
 #pragma unroll
-    for (int r = 0; r < kRB; ++r) {
-        if (r >= rows)
-            continue;  // predicated, keeps raw[] in registers
-        const int64_t i = i0 + r;
-        float v[16];
-        decode16<SRC>(raw[r], v);
-        float s1 = s_u, o1 = o_u;
-        if (PK == PK_TOKEN) {
-            s1 = a.scale[i];
-            if (OFF)
-                o1 = a.offset[i];
-        } else if (PK == PK_GROUP_N) {
-            const int64_t p = i * a.n_groups + j0 / a.gs;
-            s1 = a.scale[p];
-            if (OFF)
-                o1 = a.offset[p];
-        }
-        float t[16];
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const bool per_elem = PK == PK_CHANNEL || PK == PK_GROUP_M;
-            const float s = per_elem ? sv[e] : s1;
-            if (OFF) {
-                const float o = per_elem ? ov[e] : o1;
-                const float u = v[e] + o;
-                t[e] = u * s;
-            } else {
-                t[e] = v[e] * s;
+        for (int k = 0; k < kPD; ++k) {
+            const int64_t i = r + k * G;
+            if (i >= r1)
+                continue;
+            if (PK == PK_GROUP_M && (i < g_lo || i >= g_hi)) {
+                const int64_t g = i / a.gs;
+                load_vec_params(g * a.n);
+                g_lo = g * a.gs;
+                g_hi = g_lo + a.gs;
             }
+            float s1 = s_u, o1 = o_u;
+            if (PK == PK_TOKEN) {
+                s1 = a.scale[i];
+                if (OFF)
+                    o1 = a.offset[i];
+            }
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) {
+                if (!okc[c])
+                    continue;
+                if (PK == PK_GROUP_N) {
+                    const int64_t p = i * a.n_groups + gcol[c];
+                    s1 = a.scale[p];
+                    if (OFF)
+                        o1 = a.offset[p];
+                }
+                float v[E];
+#pragma unroll
+                for (int w = 0; w < W; ++w)
+                    decode4<SRC>(raw[k][c][w], v + 4 * w);
+                float t[E];
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const float s = kPerElem ? sv[c][e] : s1;
+                    if (OFF) {
+                        const float o = kPerElem ? ov[c][e] : o1;
+                        const float u = v[e] + o;
+                        t[e] = u * s;
+                    } else {
+                        t[e] = v[e] * s;
+                    }
+                }
+                store_chunk<DST>(dst + (i * a.n + jc[c]) * out_elem, t);
+            }
+            if (i + kPD * G < r1)
+                load_row<NCH, W>(raw[k], src + (i + kPD * G) * a.n, jc, okc);
         }
-        store16<DST>(static_cast<uint8_t*>(a.dst) + i * a.n * out_elem, j0, t);
     }
 }
 
@@ -245,8 +313,12 @@ hipError_t launch_antiquantize(const AqPlan& p, hipStream_t stream)
     a.n_groups = (p.n + a.gs - 1) / a.gs;
     a.dst = p.dst;
     a.strips = (p.n + 1023) / 1024;
-    a.tiles = a.strips * ((p.m + kRB - 1) / kRB);
-    a.nblocks = (a.tiles + 3) / 4;
+    int64_t G = (kTargetWaves + a.strips - 1) / a.strips;  // waves per strip
+    if (G > p.m)
+        G = p.m;
+    a.row_step = G;
+    a.waves = a.strips * G;
+    a.nblocks = (a.waves + 3) / 4;
     void* args[] = {&a};
     return hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3(static_cast<uint32_t>(a.nblocks)),
                            dim3(kBlock), args, 0, stream);

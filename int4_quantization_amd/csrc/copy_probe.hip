@@ -8,7 +8,7 @@
 namespace dq {
 namespace {
 
-constexpr int kUnroll = 4;
+constexpr int kUnroll = 1;
 
 __global__ __launch_bounds__(kBlock) void copy_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
                                                       int64_t n16, int64_t nblocks)
@@ -19,13 +19,13 @@ __global__ __launch_bounds__(kBlock) void copy_kernel(const uint4* __restrict__ 
     for (int u = 0; u < kUnroll; ++u) {
         const int64_t i = base + u * kBlock;
         if (i < n16)
-            v[u] = src[i];
+            v[u] = ld_stream16(src + i);
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
         const int64_t i = base + u * kBlock;
         if (i < n16)
-            dst[i] = v[u];
+            st_stream16(dst + i, v[u]);
     }
 }
 

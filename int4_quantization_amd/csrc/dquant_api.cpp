@@ -263,24 +263,30 @@ dq_status dq_dynamic_quant_get_workspace_size(const dq_tensor* x, const dq_tenso
     p.scale = static_cast<float*>(scale->data);
     p.offset = symmetric ? nullptr : static_cast<float*>(offset->data);
 
-    // Register-resident variant: rows of whole 16-byte vectors, aligned
-    // buffers, and a row that fits 16 vectors per lane of one or four waves.
+    // Register-resident variant: rows of whole 16-byte vectors and aligned
+    // buffers.  A row is split over the smallest team of waves (1, 2 or 4)
+    // that keeps it within 4 vectors per lane; wider rows take 8 or 16
+    // vectors per lane on a team of 4; longer rows go to the generic variant.
     const bool vec_ok = n % 8 == 0 && aligned(p.x, 16) && (!p.smooth || aligned(p.smooth, 16)) &&
                         aligned(p.y, p.out_kind == dq::OUT_I8 ? 8 : 4);
-    static const int kVpl[] = {1, 2, 4, 8, 12, 14, 16};
-    static const int kVplTeam[] = {8, 16};
     p.variant = dq::DQ_VAR_GENERIC;
     if (vec_ok) {
         const int64_t nvec = n / 8;
-        int v = pick_vpl((nvec + 63) / 64, kVpl, 7);
-        if (v > 0) {
-            p.variant = dq::DQ_VAR_VECTOR;
-            p.vpl = v;
-            p.team = 1;
-        } else if ((v = pick_vpl((nvec + 255) / 256, kVplTeam, 2)) > 0) {
-            p.variant = dq::DQ_VAR_VECTOR;
-            p.vpl = v;
+        static const int kTeams[] = {1, 2, 4};
+        for (int t : kTeams) {
+            if (nvec <= 4 * 64 * t) {
+                static const int kVpl[] = {1, 2, 4};
+                p.vpl = pick_vpl((nvec + 64 * t - 1) / (64 * t), kVpl, 3);
+                p.team = t;
+                p.variant = dq::DQ_VAR_VECTOR;
+                break;
+            }
+        }
+        if (p.variant != dq::DQ_VAR_VECTOR && n <= dq::kDqVecMaxTeam4) {
+            static const int kVplWide[] = {8, 16};
+            p.vpl = pick_vpl((nvec + 255) / 256, kVplWide, 2);
             p.team = 4;
+            p.variant = dq::DQ_VAR_VECTOR;
         }
     }
     *executor = e;

@@ -1,12 +1,21 @@
 // dynamic_quant.hip -- per-token dynamic quantization on gfx950
 // (aclnnDynamicQuantV2, Description and Formula).
 //
-// Vector variant: each row is owned by TEAM waves (1 or 4).  Lane l of
-// wave w loads the 16-byte vectors k = (i*TEAM + w)*64 + l, i < VPL, so
-// every load instruction covers TEAM*1 KiB of contiguous row; the row stays
-// in VGPRs as fp32 (after the smooth multiply), is reduced through DPP
-// (and LDS across the team), then quantized and stored from the same
-// registers: one HBM read per input element and one write per code.
+// Vector variant (rows of whole 16-byte vectors up to 4 waves x 16 vectors
+// per lane): persistent workgroups of four waves; TEAM waves (1, 2 or 4)
+// own one row at a time, so a workgroup converts 4/TEAM rows per step.
+// Lane l of team wave w holds the 16-byte vectors k = (i*TEAM + w)*64 + l,
+// i < VPL, so every load instruction covers contiguous row bytes; the row
+// stays in VGPRs as fp32 (after the smooth multiply), is reduced through
+// DPP (and LDS across the team), then quantized and stored from the same
+// registers: one HBM read per input element and one write per code, both
+// streamed with non-temporal accesses.  Workgroups sweep down the matrix in
+// tiles of T row groups interleaved across the grid, so all of them work
+// inside one band of rows at a time (a compact DRAM footprint) while each
+// one's consecutive rows mostly share an expert.  Each lane always owns the
+// same columns, so its smooth scales live in VGPRs and are reloaded only
+// when the row's expert changes.  With PF, the next row's loads are issued
+// before the current row is reduced.
 //
 // Generic variant (rows with N % 8 != 0, unaligned buffers, or rows longer
 // than 4 waves x 16 vectors): one workgroup per row, element loads, the row
@@ -18,11 +27,16 @@
 // correctly rounded reciprocal plus Markstein's fma correction, which
 // returns the IEEE quotient for the divisors it is used with.
 
+#include <mutex>
+
 #include "dq_device.h"
 #include "dq_internal.h"
 
 namespace dq {
 namespace {
+
+constexpr bool kDqPrefetch = true;  // issue the next row's loads before reducing this one
+constexpr int64_t kDqTile = 4;       // row groups a workgroup converts before jumping ahead
 
 struct DqArgs {
     const void* x;
@@ -35,6 +49,7 @@ struct DqArgs {
     float* scale;
     float* offset;
     int64_t nblocks;
+    int64_t tile;  // row groups per tile (vector variant)
 };
 
 // (D or scale_opt, offset_opt, code range) per output type, from the
@@ -124,119 +139,196 @@ __device__ __forceinline__ void store_codes(void* y, int64_t row, int64_t n, int
 {
     if (OUT == OUT_I8) {
         uint2* dst = reinterpret_cast<uint2*>(static_cast<int8_t*>(y) + row * n) + k;
-        *dst = make_uint2(pack4_i8(c[0], c[1], c[2], c[3]), pack4_i8(c[4], c[5], c[6], c[7]));
+        st_stream8(dst, make_uint2(pack4_i8(c[0], c[1], c[2], c[3]), pack4_i8(c[4], c[5], c[6], c[7])));
     } else {
         uint32_t* dst = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(y) + row * (n >> 1)) + k;
-        *dst = pack8_i4(c);
+        st_stream4(dst, pack8_i4(c));
     }
 }
 
-template <int XT, bool SYM, int OUT, int VPL, int TEAM>
+template <int VPL, int TEAM>
+__device__ __forceinline__ void load_x(uint4 (&raw)[VPL], const void* x, int64_t row, int64_t n, int64_t nvec,
+                                       int wit, int lane)
+{
+    const uint4* xr = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + row * n);
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+        const int64_t k = static_cast<int64_t>(i * TEAM + wit) * kWave + lane;
+        if (k < nvec)
+            raw[i] = ld_stream16(xr + k);
+    }
+}
+
+template <int XT, bool SYM, int OUT, int VPL, int TEAM, bool PF>
 __global__ __launch_bounds__(kBlock) void dq_vec_kernel(DqArgs a)
 {
-    constexpr int RPB = 4 / TEAM;
+    constexpr int RPS = 4 / TEAM;  // rows per workgroup step
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
+    const int slot = wave / TEAM;
     const int wit = wave % TEAM;
-    const int64_t row = xcd_block(blockIdx.x, a.nblocks) * RPB + wave / TEAM;
-    if (row >= a.rows)
-        return;  // wave-uniform; with TEAM = 4 the whole block leaves together
-
     const int64_t nvec = a.n >> 3;
-    const uint4* xr = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) + row * a.n);
-    uint4 raw[VPL];
-#pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-        const int64_t k = static_cast<int64_t>(i * TEAM + wit) * kWave + lane;
-        raw[i] = k < nvec ? xr[k] : make_uint4(0, 0, 0, 0);
-    }
+    const int64_t G = a.nblocks;
+    const int64_t b = blockIdx.x;
+    const int64_t T = a.tile;
+    // Step s of this workgroup converts row group ((b + (s / T) * G) * T + s % T).
+    auto row_of = [&](int64_t step) -> int64_t {
+        return ((b + (step / T) * G) * T + step % T) * RPS + slot;
+    };
+    auto group_of = [&](int64_t step) -> int64_t {
+        return (b + (step / T) * G) * T + step % T;
+    };
+    const int64_t groups = (a.rows + RPS - 1) / RPS;
 
-    const float4* sr = nullptr;
-    if (a.smooth) {
-        const int64_t e = a.gi ? expert_of_row(row, a.gi, a.n_experts, lane) : 0;
-        sr = reinterpret_cast<const float4*>(a.smooth + e * a.n);
-    }
+    // Expert bounds cached per lane (first 64 experts).
+    const bool moe = a.gi != nullptr;
+    int32_t gi_lane = 0;
+    if (moe && lane < a.n_experts)
+        gi_lane = a.gi[lane];
 
-    float v[VPL][8];
-    float s_hi = SYM ? 0.0f : -__builtin_huge_valf();
-    float s_lo = __builtin_huge_valf();
+    float sreg[VPL][8];
+    int64_t cur_e = -1;
+    __shared__ float red[2][2][4];
+
+    uint4 cur[VPL], nxt[VPL];
 #pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-        const int64_t k = static_cast<int64_t>(i * TEAM + wit) * kWave + lane;
-        widen8<XT>(raw[i], v[i]);
-        if (k < nvec) {
-            if (sr) {
-                const float4 s0 = sr[2 * k], s1 = sr[2 * k + 1];
-                v[i][0] = v[i][0] * s0.x;
-                v[i][1] = v[i][1] * s0.y;
-                v[i][2] = v[i][2] * s0.z;
-                v[i][3] = v[i][3] * s0.w;
-                v[i][4] = v[i][4] * s1.x;
-                v[i][5] = v[i][5] * s1.y;
-                v[i][6] = v[i][6] * s1.z;
-                v[i][7] = v[i][7] * s1.w;
+    for (int i = 0; i < VPL; ++i)
+        cur[i] = nxt[i] = make_uint4(0, 0, 0, 0);
+    if (group_of(0) < groups && row_of(0) < a.rows)
+        load_x<VPL, TEAM>(cur, a.x, row_of(0), a.n, nvec, wit, lane);
+
+    for (int64_t s = 0;; ++s) {
+        if (group_of(s) >= groups)
+            break;  // workgroup-uniform
+        const int64_t row = row_of(s);
+        const bool active = row < a.rows;  // team-uniform
+        if (PF) {
+            const int64_t nrow = row_of(s + 1);
+            if (group_of(s + 1) < groups && nrow < a.rows)
+                load_x<VPL, TEAM>(nxt, a.x, nrow, a.n, nvec, wit, lane);
+        }
+
+        float s_hi = SYM ? 0.0f : -__builtin_huge_valf();
+        float s_lo = __builtin_huge_valf();
+        float v[VPL][8];
+        if (active) {
+            if (a.smooth) {
+                int64_t e = 0;
+                if (moe) {
+                    if (a.n_experts <= kWave) {
+                        const unsigned long long mask = __ballot(lane < a.n_experts && row < gi_lane);
+                        e = mask ? __builtin_ctzll(mask) : a.n_experts - 1;
+                    } else {
+                        e = expert_of_row(row, a.gi, a.n_experts, lane);
+                    }
+                }
+                if (e != cur_e) {
+                    const float4* sr = reinterpret_cast<const float4*>(a.smooth + e * a.n);
+#pragma unroll
+                    for (int i = 0; i < VPL; ++i) {
+                        const int64_t k = static_cast<int64_t>(i * TEAM + wit) * kWave + lane;
+                        if (k < nvec) {
+                            const float4 s0 = sr[2 * k], s1 = sr[2 * k + 1];
+                            sreg[i][0] = s0.x;
+                            sreg[i][1] = s0.y;
+                            sreg[i][2] = s0.z;
+                            sreg[i][3] = s0.w;
+                            sreg[i][4] = s1.x;
+                            sreg[i][5] = s1.y;
+                            sreg[i][6] = s1.z;
+                            sreg[i][7] = s1.w;
+                        }
+                    }
+                    cur_e = e;
+                }
             }
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                if (SYM) {
-                    s_hi = __builtin_fmaxf(s_hi, __builtin_fabsf(v[i][j]));
-                } else {
-                    s_hi = __builtin_fmaxf(s_hi, v[i][j]);
-                    s_lo = __builtin_fminf(s_lo, v[i][j]);
+            for (int i = 0; i < VPL; ++i) {
+                const int64_t k = static_cast<int64_t>(i * TEAM + wit) * kWave + lane;
+                widen8<XT>(cur[i], v[i]);
+                if (k < nvec) {
+                    if (a.smooth) {
+#pragma unroll
+                        for (int j = 0; j < 8; ++j)
+                            v[i][j] = v[i][j] * sreg[i][j];
+                    }
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        if (SYM) {
+                            s_hi = __builtin_fmaxf(s_hi, __builtin_fabsf(v[i][j]));
+                        } else {
+                            s_hi = __builtin_fmaxf(s_hi, v[i][j]);
+                            s_lo = __builtin_fminf(s_lo, v[i][j]);
+                        }
+                    }
                 }
             }
         }
-    }
-
-    s_hi = wave_max(s_hi);
-    if (!SYM)
-        s_lo = wave_min(s_lo);
-    if (TEAM > 1) {
-        __shared__ float red[2][4];
-        if (lane == 0) {
-            red[0][wave] = s_hi;
-            red[1][wave] = s_lo;
-        }
-        __syncthreads();
-        s_hi = red[0][0];
-        s_lo = red[1][0];
-#pragma unroll
-        for (int w = 1; w < TEAM; ++w) {
-            s_hi = __builtin_fmaxf(s_hi, red[0][w]);
-            s_lo = __builtin_fminf(s_lo, red[1][w]);
-        }
-    }
-
-    const RowParams<SYM, OUT> rp(s_hi, s_lo);
-    if (wit == 0 && lane == 0) {
-        a.scale[row] = rp.scale;
+        s_hi = wave_max(s_hi);
         if (!SYM)
-            a.offset[row] = rp.offset;
-    }
-
-    if (rp.fast) {
+            s_lo = wave_min(s_lo);
+        if (TEAM > 1) {
+            // One barrier per step: partials alternate between two LDS slots,
+            // so a slot is rewritten only after every wave has passed the
+            // barrier of the step that read it.
+            const int par = static_cast<int>(s & 1);
+            if (lane == 0) {
+                red[par][0][wave] = s_hi;
+                red[par][1][wave] = s_lo;
+            }
+            __syncthreads();
+            const int w0 = slot * TEAM;
+            s_hi = red[par][0][w0];
+            s_lo = red[par][1][w0];
 #pragma unroll
-        for (int i = 0; i < VPL; ++i) {
-            const int64_t k = static_cast<int64_t>(i * TEAM + wit) * kWave + lane;
-            if (k < nvec) {
-                uint32_t c[8];
-#pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    c[j] = quant_code<SYM, OUT, true>(v[i][j], rp);
-                store_codes<OUT>(a.y, row, a.n, k, c);
+            for (int w = 1; w < TEAM; ++w) {
+                s_hi = __builtin_fmaxf(s_hi, red[par][0][w0 + w]);
+                s_lo = __builtin_fminf(s_lo, red[par][1][w0 + w]);
             }
         }
-    } else {
-#pragma unroll
-        for (int i = 0; i < VPL; ++i) {
-            const int64_t k = static_cast<int64_t>(i * TEAM + wit) * kWave + lane;
-            if (k < nvec) {
-                uint32_t c[8];
-#pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    c[j] = quant_code<SYM, OUT, false>(v[i][j], rp);
-                store_codes<OUT>(a.y, row, a.n, k, c);
+
+        if (active) {
+            const RowParams<SYM, OUT> rp(s_hi, s_lo);
+            if (wit == 0 && lane == 0) {
+                a.scale[row] = rp.scale;
+                if (!SYM)
+                    a.offset[row] = rp.offset;
             }
+            if (rp.fast) {
+#pragma unroll
+                for (int i = 0; i < VPL; ++i) {
+                    const int64_t k = static_cast<int64_t>(i * TEAM + wit) * kWave + lane;
+                    if (k < nvec) {
+                        uint32_t c[8];
+#pragma unroll
+                        for (int j = 0; j < 8; ++j)
+                            c[j] = quant_code<SYM, OUT, true>(v[i][j], rp);
+                        store_codes<OUT>(a.y, row, a.n, k, c);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < VPL; ++i) {
+                    const int64_t k = static_cast<int64_t>(i * TEAM + wit) * kWave + lane;
+                    if (k < nvec) {
+                        uint32_t c[8];
+#pragma unroll
+                        for (int j = 0; j < 8; ++j)
+                            c[j] = quant_code<SYM, OUT, false>(v[i][j], rp);
+                        store_codes<OUT>(a.y, row, a.n, k, c);
+                    }
+                }
+            }
+        }
+
+        if (PF) {
+#pragma unroll
+            for (int i = 0; i < VPL; ++i)
+                cur[i] = nxt[i];
+        } else {
+            const int64_t nrow = row_of(s + 1);
+            if (group_of(s + 1) < groups && nrow < a.rows)
+                load_x<VPL, TEAM>(cur, a.x, nrow, a.n, nvec, wit, lane);
         }
     }
 }
@@ -272,7 +364,7 @@ __global__ __launch_bounds__(kBlock) void dq_generic_kernel(DqArgs a)
 {
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
-    const int64_t row = xcd_block(blockIdx.x, a.nblocks);
+    const int64_t row = blockIdx.x;
     if (row >= a.rows)
         return;
     const uint16_t* xr = static_cast<const uint16_t*>(a.x) + row * a.n;
@@ -318,24 +410,15 @@ __global__ __launch_bounds__(kBlock) void dq_generic_kernel(DqArgs a)
 
 using KernelFn = void (*)(DqArgs);
 
-template <int XT, bool SYM, int OUT>
-KernelFn pick_vec(int vpl, int team)
+template <int XT, bool SYM, int OUT, int TEAM>
+KernelFn pick_vpl(int vpl)
 {
-    if (team == 4) {
-        switch (vpl) {
-        case 8: return dq_vec_kernel<XT, SYM, OUT, 8, 4>;
-        case 16: return dq_vec_kernel<XT, SYM, OUT, 16, 4>;
-        }
-        return nullptr;
-    }
     switch (vpl) {
-    case 1: return dq_vec_kernel<XT, SYM, OUT, 1, 1>;
-    case 2: return dq_vec_kernel<XT, SYM, OUT, 2, 1>;
-    case 4: return dq_vec_kernel<XT, SYM, OUT, 4, 1>;
-    case 8: return dq_vec_kernel<XT, SYM, OUT, 8, 1>;
-    case 12: return dq_vec_kernel<XT, SYM, OUT, 12, 1>;
-    case 14: return dq_vec_kernel<XT, SYM, OUT, 14, 1>;
-    case 16: return dq_vec_kernel<XT, SYM, OUT, 16, 1>;
+    case 1: return dq_vec_kernel<XT, SYM, OUT, 1, TEAM, kDqPrefetch>;
+    case 2: return dq_vec_kernel<XT, SYM, OUT, 2, TEAM, kDqPrefetch>;
+    case 4: return dq_vec_kernel<XT, SYM, OUT, 4, TEAM, kDqPrefetch>;
+    case 8: return dq_vec_kernel<XT, SYM, OUT, 8, TEAM, kDqPrefetch>;
+    case 16: return dq_vec_kernel<XT, SYM, OUT, 16, TEAM, kDqPrefetch>;
     }
     return nullptr;
 }
@@ -343,9 +426,14 @@ KernelFn pick_vec(int vpl, int team)
 template <int XT, bool SYM, int OUT>
 KernelFn pick(const DqPlan& p)
 {
-    if (p.variant == DQ_VAR_VECTOR)
-        return pick_vec<XT, SYM, OUT>(p.vpl, p.team);
-    return dq_generic_kernel<XT, SYM, OUT>;
+    if (p.variant != DQ_VAR_VECTOR)
+        return dq_generic_kernel<XT, SYM, OUT>;
+    switch (p.team) {
+    case 1: return pick_vpl<XT, SYM, OUT, 1>(p.vpl);
+    case 2: return pick_vpl<XT, SYM, OUT, 2>(p.vpl);
+    case 4: return pick_vpl<XT, SYM, OUT, 4>(p.vpl);
+    }
+    return nullptr;
 }
 
 template <int XT>
@@ -356,6 +444,32 @@ KernelFn pick_x(const DqPlan& p)
     return p.out_kind == OUT_I8 ? pick<XT, false, OUT_I8>(p) : pick<XT, false, OUT_I4>(p);
 }
 
+// Resident workgroups per CU for a kernel, and the CU count, looked up once
+// per device and kernel.
+int64_t resident_blocks(KernelFn fn)
+{
+    struct Entry { int device; KernelFn fn; int64_t blocks; };
+    static Entry cache[64];
+    static int used = 0;
+    static std::mutex mu;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return 0;
+    std::lock_guard<std::mutex> lock(mu);
+    for (int i = 0; i < used; ++i)
+        if (cache[i].device == dev && cache[i].fn == fn)
+            return cache[i].blocks;
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fn), kBlock, 0) !=
+            hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    const int64_t blocks = static_cast<int64_t>(per_cu > 0 ? per_cu : 1) * cus;
+    if (used < 64)
+        cache[used++] = Entry{dev, fn, blocks};
+    return blocks;
+}
+
 }  // namespace
 
 hipError_t launch_dynamic_quant(const DqPlan& p, hipStream_t stream)
@@ -363,9 +477,19 @@ hipError_t launch_dynamic_quant(const DqPlan& p, hipStream_t stream)
     KernelFn fn = p.x_type == X_F16 ? pick_x<X_F16>(p) : pick_x<X_BF16>(p);
     if (!fn)
         return hipErrorInvalidValue;
-    DqArgs a{p.x, p.smooth, p.group_index, p.n_experts, p.rows, p.n, p.y, p.scale, p.offset, 0};
-    const int64_t rows_per_block = p.variant == DQ_VAR_VECTOR ? 4 / p.team : 1;
-    a.nblocks = (p.rows + rows_per_block - 1) / rows_per_block;
+    DqArgs a{p.x, p.smooth, p.group_index, p.n_experts, p.rows, p.n, p.y, p.scale, p.offset, 0, 1};
+    if (p.variant == DQ_VAR_VECTOR) {
+        const int64_t rps = 4 / p.team;
+        const int64_t groups = (p.rows + rps - 1) / rps;
+        a.tile = kDqTile;
+        const int64_t tiles = (groups + a.tile - 1) / a.tile;
+        const int64_t resident = resident_blocks(fn);
+        if (resident <= 0)
+            return hipErrorInvalidValue;
+        a.nblocks = tiles < resident ? tiles : resident;
+    } else {
+        a.nblocks = p.rows;
+    }
     void* args[] = {&a};
     return hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3(static_cast<uint32_t>(a.nblocks)),
                            dim3(kBlock), args, 0, stream);
