@@ -4,17 +4,19 @@
 //   y  = LN * (1 + scale[b]) + shift[b];   y = y * smooth
 //   quantScale = row_max(|y|) / 127;      out = round(y / quantScale)
 //
-// Layout of the work: a workgroup owns a contiguous chunk of rows.  For each
+// Layout of the work: a workgroup owns a contiguous chunk of rows (workgroups
+// in launch order, so the running ones cover one band of rows).  For each
 // batch b its chunk touches, it first writes the per-column coefficients
 //   A_j = w_j * (1 + scale_bj) * smooth_j
 //   C_j = (bias_j * (1 + scale_bj) + shift_bj) * smooth_j
 // into LDS, so that y_j = ((x_j - mean) * rstd) * A_j + C_j is one multiply
 // and one fma per element.  Each row is then held in VGPRs by one wave
-// (16-byte loads, one HBM read per element); its statistics are Welford
-// style: every lane forms (count, mean, M2) of its own elements from the
-// registers, and the lanes merge with Chan's pairwise update in a fixed
-// butterfly.  The quantization step is the same bit-exact binary32 step as
-// symmetric INT8 DynamicQuant, applied to the fp32 y.
+// (16-byte non-temporal loads, one HBM read per element); its statistics
+// are Welford style: every lane forms (count, mean, M2) of its own elements
+// from the registers, and the lanes merge with Chan's pairwise update in a
+// fixed butterfly (a reciprocal-free form when every lane holds the same
+// count).  Statistics, normalization and modulation are fp32 with hardware
+// rsq / rcp; quantScale is the exact binary32 RN(max|y| / 127).
 //
 // Rows that are not whole 16-byte vectors or are longer than 16 vectors
 // per lane use the generic kernel (one workgroup per row, three passes over
@@ -25,6 +27,10 @@
 
 namespace dq {
 namespace {
+
+// Launch one workgroup per chunk of rows (false) or a persistent grid that
+// sweeps the chunks and rebuilds its LDS table only when the batch changes.
+constexpr bool kAdaPersistent = false;
 
 struct AdaArgs {
     const void* x;
@@ -39,6 +45,8 @@ struct AdaArgs {
     float* qs;
     int64_t rpb;
     int64_t nblocks;
+    int equal_counts;  // every lane holds the same number of elements (H % 512 == 0)
+    float inv_h;       // RN(1 / H)
 };
 
 // Modulation coefficients of column j for batch b (fp32, formula order).
@@ -79,10 +87,31 @@ __device__ __forceinline__ Stats merge(const Stats& p, const Stats& q)
     return {n, mean, m2};
 }
 
+// The same merge when both sides hold the same count n: the weights are
+// exact halves, no reciprocal is needed.
+__device__ __forceinline__ Stats merge_equal(const Stats& p, const Stats& q)
+{
+    const float mean = (p.mean + q.mean) * 0.5f;
+    const float d = q.mean - p.mean;
+    const float m2 = (p.m2 + q.m2) + d * d * (p.n * 0.5f);
+    return {p.n + q.n, mean, m2};
+}
+
 template <int CTRL>
 __device__ __forceinline__ Stats dpp_stats(const Stats& s)
 {
     return {dpp_f<CTRL>(s.n), dpp_f<CTRL>(s.mean), dpp_f<CTRL>(s.m2)};
+}
+
+__device__ __forceinline__ Stats wave_merge_equal(Stats s)
+{
+    s = merge_equal(s, dpp_stats<kDppQuadXor1>(s));
+    s = merge_equal(s, dpp_stats<kDppQuadXor2>(s));
+    s = merge_equal(s, dpp_stats<kDppHalfMirror>(s));
+    s = merge_equal(s, dpp_stats<kDppMirror>(s));
+    s = merge_equal(s, Stats{swz_xor16(s.n), swz_xor16(s.mean), swz_xor16(s.m2)});
+    return merge_equal(Stats{lane_f(s.n, 0), lane_f(s.mean, 0), lane_f(s.m2, 0)},
+                       Stats{lane_f(s.n, 32), lane_f(s.mean, 32), lane_f(s.m2, 32)});
 }
 
 __device__ __forceinline__ Stats wave_merge(Stats s)
@@ -96,14 +125,20 @@ __device__ __forceinline__ Stats wave_merge(Stats s)
                  Stats{lane_f(s.n, 32), lane_f(s.mean, 32), lane_f(s.m2, 32)});
 }
 
-// Symmetric INT8 quantization parameters of a row from max|y|.
+// Symmetric INT8 quantization of a row from max|y| (Formula steps 4-5).
+// quantScale = RN(max|y| / 127) exactly (it is an output, checked to 1e-5);
+// the codes take y * RN~(1 / quantScale), which differs from the IEEE
+// quotient by at most an ulp and moves a code only when y / quantScale sits
+// within about 2^-17 of a rounding tie -- far inside the stated bar of codes
+// within +-1 on at most 0.01 % of the elements.  Rows whose quantScale is 0,
+// tiny, huge or not finite take a true division and the saturating rule.
 struct QParams {
     float qs, recip;
     bool fast;
     __device__ __forceinline__ explicit QParams(float amax)
     {
-        qs = amax / 127.0f;
-        recip = 1.0f / qs;
+        qs = div_by_const(amax, 127.0f, 1.0f / 127.0f);
+        recip = __builtin_amdgcn_rcpf(qs);
         fast = row_divisor_in_range(qs);
     }
 };
@@ -111,8 +146,10 @@ struct QParams {
 template <bool FAST>
 __device__ __forceinline__ uint32_t q8(float y, const QParams& qp)
 {
+    // |y| <= max|y| = 127 quantScale (1 + 2^-24) and recip is within an ulp
+    // of 1 / quantScale, so |y * recip| < 127.00004: no clamp is needed.
     if (FAST)
-        return code_bits(div_by_row(y, qp.qs, qp.recip));
+        return code_bits(y * qp.recip);
     float t = y / qp.qs;
     if (t != t)
         t = 0.0f;
@@ -137,35 +174,46 @@ __global__ __launch_bounds__(kBlock) void ada_vec_kernel(AdaArgs a)
     float* tab = reinterpret_cast<float*>(tab4);
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
-    const int64_t r0 = xcd_block(blockIdx.x, a.nblocks) * a.rpb;
-    if (r0 >= a.rows)
-        return;  // block-uniform
-    const int64_t r1 = r0 + a.rpb < a.rows ? r0 + a.rpb : a.rows;
     const int64_t H = a.H;
     const int64_t nvec = H >> 3;
     const int64_t plane = nvec;  // float4 entries per plane
+    const int64_t nchunks = (a.rows + a.rpb - 1) / a.rpb;
+    int64_t tab_batch = -1;
 
+    // Chunks of rpb rows, strided over the grid (one chunk per workgroup when
+    // the grid covers them all; a sweep of persistent workgroups otherwise).
+    for (int64_t chunk = blockIdx.x; chunk < nchunks; chunk += gridDim.x) {
+    const int64_t r0 = chunk * a.rpb;
+    const int64_t r1 = r0 + a.rpb < a.rows ? r0 + a.rpb : a.rows;
     int64_t r = r0;
     int64_t b = r0 / a.S;
     while (r < r1) {
         const int64_t r_end = (b + 1) * a.S < r1 ? (b + 1) * a.S : r1;
-        __syncthreads();  // earlier readers of the table are done
-        for (int64_t j = threadIdx.x; j < H; j += kBlock) {
-            float A, C;
-            coeffs<XT>(a, b, j, A, C);
-            tab[tab_index(H, 0, j)] = A;
-            tab[tab_index(H, 1, j)] = C;
+        if (b != tab_batch) {  // workgroup-uniform
+            __syncthreads();  // earlier readers of the table are done
+            for (int64_t j = threadIdx.x; j < H; j += kBlock) {
+                float A, C;
+                coeffs<XT>(a, b, j, A, C);
+                tab[tab_index(H, 0, j)] = A;
+                tab[tab_index(H, 1, j)] = C;
+            }
+            __syncthreads();
+            tab_batch = b;
         }
-        __syncthreads();
 
         for (int64_t row = r + wave; row < r_end; row += 4) {
+            // Every load is unconditional: lanes past the row end re-load the
+            // row's last vector (their results are never stored).
             const uint4* xr = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) + row * H);
             uint4 raw[VPL];
 #pragma unroll
             for (int i = 0; i < VPL; ++i) {
                 const int64_t k = static_cast<int64_t>(i) * kWave + lane;
-                raw[i] = k < nvec ? ld_stream16(xr + k) : make_uint4(0, 0, 0, 0);
+                raw[i] = ld_stream16(xr + (k < nvec ? k : nvec - 1));
             }
+            // Welford-style statistics: each lane forms (count, mean, M2) of
+            // its own elements from the registers (two passes over them), and
+            // the lanes merge with Chan's pairwise update in a fixed butterfly.
             float v[VPL][8];
             float cnt = 0.0f, sum = 0.0f;
 #pragma unroll
@@ -194,9 +242,9 @@ __global__ __launch_bounds__(kBlock) void ada_vec_kernel(AdaArgs a)
                     }
                 }
             }
-            st = wave_merge(st);
-            const float var = st.m2 / static_cast<float>(H);
-            const float rstd = 1.0f / __builtin_sqrtf(var + a.eps);
+            st = a.equal_counts ? wave_merge_equal(st) : wave_merge(st);
+            const float var = st.m2 * a.inv_h;
+            const float rstd = __builtin_amdgcn_rsqf(var + a.eps);
             const float mean = st.mean;
 
             float amax = 0.0f;
@@ -216,7 +264,7 @@ __global__ __launch_bounds__(kBlock) void ada_vec_kernel(AdaArgs a)
                     }
                 }
             }
-            amax = wave_max(amax);
+            amax = wave_max_f(amax);
             const QParams qp(amax);
             if (lane == 0)
                 a.qs[row] = qp.qs;
@@ -238,9 +286,10 @@ __global__ __launch_bounds__(kBlock) void ada_vec_kernel(AdaArgs a)
                     st_stream8(orow + k, make_uint2(pack4_i8(c[0], c[1], c[2], c[3]), pack4_i8(c[4], c[5], c[6], c[7])));
                 }
             }
-        }
+                }
         r = r_end;
         ++b;
+    }
     }
 }
 
@@ -276,7 +325,7 @@ __global__ __launch_bounds__(kBlock) void ada_generic_kernel(AdaArgs a)
 {
     __shared__ Stats red_s[4];
     __shared__ float red_f[4];
-    const int64_t row = xcd_block(blockIdx.x, a.nblocks);
+    const int64_t row = blockIdx.x;
     if (row >= a.rows)
         return;
     const int64_t b = row / a.S;
@@ -350,6 +399,8 @@ hipError_t launch_ada_layernorm_quant(const AdaPlan& p, hipStream_t stream)
     a.eps = p.eps;
     a.out = p.out;
     a.qs = p.quant_scale;
+    a.equal_counts = (p.H % 512) == 0;
+    a.inv_h = 1.0f / static_cast<float>(p.H);
     KernelFn fn;
     size_t lds = 0;
     if (p.variant == ADA_VAR_VECTOR) {
@@ -363,6 +414,17 @@ hipError_t launch_ada_layernorm_quant(const AdaPlan& p, hipStream_t stream)
     if (!fn)
         return hipErrorInvalidValue;
     a.nblocks = (a.rows + a.rpb - 1) / a.rpb;
+    if (p.variant == ADA_VAR_VECTOR && kAdaPersistent) {
+        int per_cu = 0, cus = 0, dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fn), kBlock, lds) !=
+                hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return hipErrorInvalidValue;
+        const int64_t resident = static_cast<int64_t>(per_cu > 0 ? per_cu : 1) * cus;
+        if (a.nblocks > resident)
+            a.nblocks = resident;
+    }
     void* args[] = {&a};
     return hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3(static_cast<uint32_t>(a.nblocks)),
                            dim3(kBlock), args, lds, stream);

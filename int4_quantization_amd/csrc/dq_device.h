@@ -74,6 +74,39 @@ struct AddOp {
     __device__ float operator()(float a, float b) const { return a + b; }
 };
 
+// Order-preserving integer keys for float max / min reductions: for every
+// non-NaN x, y: x < y  <=>  key(x) < key(y) as signed integers (-0 sorts just
+// below +0).  Integer max/min need no NaN canonicalization, so each
+// butterfly step is one DPP move and one integer op.
+__device__ __forceinline__ int f2key(float f)
+{
+    const int b = __builtin_bit_cast(int, f);
+    return b ^ ((b >> 31) & 0x7FFFFFFF);
+}
+__device__ __forceinline__ float key2f(int k) { return __builtin_bit_cast(float, k ^ ((k >> 31) & 0x7FFFFFFF)); }
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v)
+{
+    return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, false);
+}
+
+template <bool MAX>
+__device__ __forceinline__ int wave_reduce_key(int v)
+{
+    auto op = [](int a, int b) { return MAX ? (a > b ? a : b) : (a < b ? a : b); };
+    v = op(v, dpp_i<0xB1>(v));
+    v = op(v, dpp_i<0x4E>(v));
+    v = op(v, dpp_i<0x141>(v));
+    v = op(v, dpp_i<0x140>(v));
+    v = op(v, __builtin_amdgcn_ds_swizzle(v, 0x401F));
+    return op(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 32));
+}
+
+// Wave-wide max / min of non-NaN floats (every lane gets the result).
+__device__ __forceinline__ float wave_max_f(float v) { return key2f(wave_reduce_key<true>(f2key(v))); }
+__device__ __forceinline__ float wave_min_f(float v) { return key2f(wave_reduce_key<false>(f2key(v))); }
+
 __device__ __forceinline__ float wave_max(float v) { return wave_reduce(v, MaxOp{}); }
 __device__ __forceinline__ float wave_min(float v) { return wave_reduce(v, MinOp{}); }
 __device__ __forceinline__ float wave_sum(float v) { return wave_reduce(v, AddOp{}); }
@@ -172,6 +205,17 @@ __device__ __forceinline__ float div_by_row(float v, float d, float r)
     const float q0 = v * r;
     const float e = __builtin_fmaf(-d, q0, v);
     return __builtin_fmaf(e, r, q0);
+}
+
+// RN(a / D) for a constant D with rD = RN(1 / D) (computed at compile time):
+// the same correction step, which returns the IEEE quotient for every a in
+// [2^-100, FLT_MAX] and D in {7, 15, 127, 255} (checked exhaustively over
+// all such binary32 a); other a (0, tiny, inf, NaN) take a true division.
+__device__ __forceinline__ float div_by_const(float a, float D, float rD)
+{
+    if (a >= 0x1p-100f && a <= 3.40282347e38f)
+        return div_by_row(a, D, rD);
+    return a / D;
 }
 
 __device__ __forceinline__ bool row_divisor_in_range(float d)

@@ -35,8 +35,9 @@
 namespace dq {
 namespace {
 
-constexpr bool kDqPrefetch = true;  // issue the next row's loads before reducing this one
-constexpr int64_t kDqTile = 4;       // row groups a workgroup converts before jumping ahead
+constexpr bool kDqPrefetch = false;  // issue the next row's loads before reducing this one
+                                      // (measured no faster once loads are unconditional)
+constexpr uint64_t kDqTile = 4;      // row groups a workgroup converts before jumping ahead (power of 2)
 
 struct DqArgs {
     const void* x;
@@ -93,16 +94,21 @@ struct RowParams {
     {
         using C = Consts<OUT>;
         if (SYM) {
-            scale = a_hi / C::offset_opt;
-            offset = 0.0f;
+            scale = div_by_const(a_hi, C::offset_opt, 1.0f / C::offset_opt);
         } else {
             const float range = a_hi - a_lo;
-            scale = range / C::scale_opt;
-            const float q_hi = a_hi / scale;
+            scale = div_by_const(range, C::scale_opt, 1.0f / C::scale_opt);
+        }
+        recip = 1.0f / scale;
+        fast = row_divisor_in_range(scale);
+        if (SYM) {
+            offset = 0.0f;
+        } else {
+            // max / scale; a quotient too small for the correction step to be
+            // exact (|q| < 2^-40) leaves offset_opt - q at offset_opt either way.
+            const float q_hi = fast ? div_by_row(a_hi, scale, recip) : a_hi / scale;
             offset = C::offset_opt - q_hi;
         }
-        fast = row_divisor_in_range(scale);
-        recip = 1.0f / scale;
     }
 };
 
@@ -146,6 +152,11 @@ __device__ __forceinline__ void store_codes(void* y, int64_t row, int64_t n, int
     }
 }
 
+// Loads of a row for one team wave.  Lanes whose vector lies past the row
+// end re-load the row's last vector: a duplicate changes neither max nor
+// min, and every load is unconditional, so each register's load is always
+// consumed before it is loaded again (no divergent paths that would force a
+// full wait on outstanding memory before the next prefetch).
 template <int VPL, int TEAM>
 __device__ __forceinline__ void load_x(uint4 (&raw)[VPL], const void* x, int64_t row, int64_t n, int64_t nvec,
                                        int wit, int lane)
@@ -154,8 +165,7 @@ __device__ __forceinline__ void load_x(uint4 (&raw)[VPL], const void* x, int64_t
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
         const int64_t k = static_cast<int64_t>(i * TEAM + wit) * kWave + lane;
-        if (k < nvec)
-            raw[i] = ld_stream16(xr + k);
+        raw[i] = ld_stream16(xr + (k < nvec ? k : nvec - 1));
     }
 }
 
@@ -168,16 +178,15 @@ __global__ __launch_bounds__(kBlock) void dq_vec_kernel(DqArgs a)
     const int slot = wave / TEAM;
     const int wit = wave % TEAM;
     const int64_t nvec = a.n >> 3;
-    const int64_t G = a.nblocks;
-    const int64_t b = blockIdx.x;
-    const int64_t T = a.tile;
+    const uint64_t G = static_cast<uint64_t>(a.nblocks);
+    const uint64_t b = blockIdx.x;
+    constexpr uint64_t T = kDqTile;
     // Step s of this workgroup converts row group ((b + (s / T) * G) * T + s % T).
-    auto row_of = [&](int64_t step) -> int64_t {
-        return ((b + (step / T) * G) * T + step % T) * RPS + slot;
-    };
     auto group_of = [&](int64_t step) -> int64_t {
-        return (b + (step / T) * G) * T + step % T;
+        const uint64_t u = static_cast<uint64_t>(step);
+        return static_cast<int64_t>((b + (u / T) * G) * T + u % T);
     };
+    auto row_of = [&](int64_t step) -> int64_t { return group_of(step) * RPS + slot; };
     const int64_t groups = (a.rows + RPS - 1) / RPS;
 
     // Expert bounds cached per lane (first 64 experts).
@@ -187,86 +196,90 @@ __global__ __launch_bounds__(kBlock) void dq_vec_kernel(DqArgs a)
         gi_lane = a.gi[lane];
 
     float sreg[VPL][8];
+#pragma unroll
+    for (int i = 0; i < VPL; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            sreg[i][j] = 1.0f;
     int64_t cur_e = -1;
     __shared__ float red[2][2][4];
 
-    uint4 cur[VPL], nxt[VPL];
+    uint4 buf0[VPL], buf1[VPL];
 #pragma unroll
     for (int i = 0; i < VPL; ++i)
-        cur[i] = nxt[i] = make_uint4(0, 0, 0, 0);
+        buf0[i] = buf1[i] = make_uint4(0, 0, 0, 0);
     if (group_of(0) < groups && row_of(0) < a.rows)
-        load_x<VPL, TEAM>(cur, a.x, row_of(0), a.n, nvec, wit, lane);
+        load_x<VPL, TEAM>(buf0, a.x, row_of(0), a.n, nvec, wit, lane);
 
-    for (int64_t s = 0;; ++s) {
+    // One step: row_of(s) is in cur; with PF the next row is requested into
+    // nxt before any arithmetic, otherwise after the stores.  Returns false
+    // when the workgroup has no more rows (workgroup-uniform).
+    auto step = [&](int64_t s, uint4 (&cur)[VPL], uint4 (&nxt)[VPL]) -> bool {
         if (group_of(s) >= groups)
-            break;  // workgroup-uniform
+            return false;
         const int64_t row = row_of(s);
         const bool active = row < a.rows;  // team-uniform
-        if (PF) {
-            const int64_t nrow = row_of(s + 1);
-            if (group_of(s + 1) < groups && nrow < a.rows)
-                load_x<VPL, TEAM>(nxt, a.x, nrow, a.n, nvec, wit, lane);
+        const int64_t nrow = row_of(s + 1);
+        const bool has_next = group_of(s + 1) < groups && nrow < a.rows;
+        if (PF && has_next)
+            load_x<VPL, TEAM>(nxt, a.x, nrow, a.n, nvec, wit, lane);
+
+        if (a.smooth && active) {
+            int64_t e = 0;
+            if (moe) {
+                if (a.n_experts <= kWave) {
+                    const unsigned long long mask = __ballot(lane < a.n_experts && row < gi_lane);
+                    e = mask ? __builtin_ctzll(mask) : a.n_experts - 1;
+                } else {
+                    e = expert_of_row(row, a.gi, a.n_experts, lane);
+                }
+            }
+            if (e != cur_e) {
+                const float4* sr = reinterpret_cast<const float4*>(a.smooth + e * a.n);
+#pragma unroll
+                for (int i = 0; i < VPL; ++i) {
+                    int64_t k = static_cast<int64_t>(i * TEAM + wit) * kWave + lane;
+                    k = k < nvec ? k : nvec - 1;
+                    const float4 s0 = sr[2 * k], s1 = sr[2 * k + 1];
+                    sreg[i][0] = s0.x;
+                    sreg[i][1] = s0.y;
+                    sreg[i][2] = s0.z;
+                    sreg[i][3] = s0.w;
+                    sreg[i][4] = s1.x;
+                    sreg[i][5] = s1.y;
+                    sreg[i][6] = s1.z;
+                    sreg[i][7] = s1.w;
+                }
+                cur_e = e;
+            }
         }
 
+        // Widen, smooth and reduce every vector, including the duplicated
+        // tail vectors and an inactive tail row (its results are dropped).
         float s_hi = SYM ? 0.0f : -__builtin_huge_valf();
         float s_lo = __builtin_huge_valf();
         float v[VPL][8];
-        if (active) {
-            if (a.smooth) {
-                int64_t e = 0;
-                if (moe) {
-                    if (a.n_experts <= kWave) {
-                        const unsigned long long mask = __ballot(lane < a.n_experts && row < gi_lane);
-                        e = mask ? __builtin_ctzll(mask) : a.n_experts - 1;
-                    } else {
-                        e = expert_of_row(row, a.gi, a.n_experts, lane);
-                    }
-                }
-                if (e != cur_e) {
-                    const float4* sr = reinterpret_cast<const float4*>(a.smooth + e * a.n);
 #pragma unroll
-                    for (int i = 0; i < VPL; ++i) {
-                        const int64_t k = static_cast<int64_t>(i * TEAM + wit) * kWave + lane;
-                        if (k < nvec) {
-                            const float4 s0 = sr[2 * k], s1 = sr[2 * k + 1];
-                            sreg[i][0] = s0.x;
-                            sreg[i][1] = s0.y;
-                            sreg[i][2] = s0.z;
-                            sreg[i][3] = s0.w;
-                            sreg[i][4] = s1.x;
-                            sreg[i][5] = s1.y;
-                            sreg[i][6] = s1.z;
-                            sreg[i][7] = s1.w;
-                        }
-                    }
-                    cur_e = e;
-                }
+        for (int i = 0; i < VPL; ++i) {
+            widen8<XT>(cur[i], v[i]);
+            if (a.smooth) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    v[i][j] = v[i][j] * sreg[i][j];
             }
 #pragma unroll
-            for (int i = 0; i < VPL; ++i) {
-                const int64_t k = static_cast<int64_t>(i * TEAM + wit) * kWave + lane;
-                widen8<XT>(cur[i], v[i]);
-                if (k < nvec) {
-                    if (a.smooth) {
-#pragma unroll
-                        for (int j = 0; j < 8; ++j)
-                            v[i][j] = v[i][j] * sreg[i][j];
-                    }
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        if (SYM) {
-                            s_hi = __builtin_fmaxf(s_hi, __builtin_fabsf(v[i][j]));
-                        } else {
-                            s_hi = __builtin_fmaxf(s_hi, v[i][j]);
-                            s_lo = __builtin_fminf(s_lo, v[i][j]);
-                        }
-                    }
+            for (int j = 0; j < 8; ++j) {
+                if (SYM) {
+                    s_hi = __builtin_fmaxf(s_hi, __builtin_fabsf(v[i][j]));
+                } else {
+                    s_hi = __builtin_fmaxf(s_hi, v[i][j]);
+                    s_lo = __builtin_fminf(s_lo, v[i][j]);
                 }
             }
         }
-        s_hi = wave_max(s_hi);
+        s_hi = wave_max_f(s_hi);
         if (!SYM)
-            s_lo = wave_min(s_lo);
+            s_lo = wave_min_f(s_lo);
         if (TEAM > 1) {
             // One barrier per step: partials alternate between two LDS slots,
             // so a slot is rewritten only after every wave has passed the
@@ -320,16 +333,16 @@ __global__ __launch_bounds__(kBlock) void dq_vec_kernel(DqArgs a)
                 }
             }
         }
+        if (!PF && has_next)
+            load_x<VPL, TEAM>(nxt, a.x, nrow, a.n, nvec, wit, lane);
+        return true;
+    };
 
-        if (PF) {
-#pragma unroll
-            for (int i = 0; i < VPL; ++i)
-                cur[i] = nxt[i];
-        } else {
-            const int64_t nrow = row_of(s + 1);
-            if (group_of(s + 1) < groups && nrow < a.rows)
-                load_x<VPL, TEAM>(cur, a.x, nrow, a.n, nvec, wit, lane);
-        }
+    for (int64_t s = 0;; s += 2) {
+        if (!step(s, buf0, buf1))
+            break;
+        if (!step(s + 1, buf1, buf0))
+            break;
     }
 }
 
@@ -481,7 +494,7 @@ hipError_t launch_dynamic_quant(const DqPlan& p, hipStream_t stream)
     if (p.variant == DQ_VAR_VECTOR) {
         const int64_t rps = 4 / p.team;
         const int64_t groups = (p.rows + rps - 1) / rps;
-        a.tile = kDqTile;
+        a.tile = static_cast<int64_t>(kDqTile);
         const int64_t tiles = (groups + a.tile - 1) / a.tile;
         const int64_t resident = resident_blocks(fn);
         if (resident <= 0)

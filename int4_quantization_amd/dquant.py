@@ -233,6 +233,65 @@ def _workspace(size: int, device) -> Optional[torch.Tensor]:
     return torch.empty(size, dtype=torch.uint8, device=device) if size > 0 else None
 
 
+# -- prepared calls: descriptors built once, both phases per call ---------------
+
+class PreparedCall:
+    """Both phases of one op with fixed tensors: the dq_tensor descriptors are
+    built once, so each call is the get-workspace-size call plus the execute
+    call (two C calls, no per-call Python marshalling of tensors).  The op
+    needs no workspace; a nonzero size raises."""
+
+    def __init__(self, phase1, execute, args, keep):
+        self._phase1 = phase1
+        self._execute = execute
+        self._ws = ctypes.c_size_t(0)
+        self._ex = _vp(None)
+        self._args = tuple(args) + (ctypes.byref(self._ws), ctypes.byref(self._ex))
+        self._keep = keep  # descriptors and tensors referenced by the args
+
+    def __call__(self, stream=None) -> None:
+        st = self._phase1(*self._args)
+        if st != SUCCESS:
+            raise DquantError(st, dq_get_last_error())
+        if self._ws.value:
+            library().dq_executor_destroy(self._ex)
+            raise DquantError(ERR_WORKSPACE, "prepared calls take ops without workspace")
+        st = self._execute(None, 0, self._ex, _stream_handle(stream))
+        if st != SUCCESS:
+            raise DquantError(st, dq_get_last_error())
+
+
+def prepare_dynamic_quant(x, smooth_scales, group_index, symmetric, y, scale, offset,
+                          out_dtype: Optional[str] = None) -> PreparedCall:
+    lib = library()
+    d = [tensor_desc(x), tensor_desc(smooth_scales), tensor_desc(group_index),
+         _y_desc(y, x.shape, out_dtype), tensor_desc(scale), tensor_desc(offset)]
+    args = [_ref(d[0]), _ref(d[1]), _ref(d[2]), 1 if symmetric else 0, _ref(d[3]), _ref(d[4]),
+            _ref(d[5])]
+    return PreparedCall(lib.dq_dynamic_quant_get_workspace_size, lib.dq_dynamic_quant, args,
+                        (d, x, smooth_scales, group_index, y, scale, offset))
+
+
+def prepare_ada_layernorm_quant(x, scale, shift, weight, bias, smooth_scales, epsilon, out,
+                                quant_scale) -> PreparedCall:
+    lib = library()
+    d = [tensor_desc(t) for t in (x, scale, shift, weight, bias, smooth_scales, out, quant_scale)]
+    args = [_ref(d[0]), _ref(d[1]), _ref(d[2]), _ref(d[3]), _ref(d[4]), _ref(d[5]),
+            ctypes.c_double(float(epsilon)), _ref(d[6]), _ref(d[7])]
+    return PreparedCall(lib.dq_ada_layernorm_quant_get_workspace_size, lib.dq_ada_layernorm_quant,
+                        args, (d, x, scale, shift, weight, bias, smooth_scales, out, quant_scale))
+
+
+def prepare_antiquantize(src, scale, offset, policy, k_dim: int, group_size: int,
+                         dst) -> PreparedCall:
+    lib = library()
+    pol = POLICIES[policy] if isinstance(policy, str) else int(policy)
+    d = [tensor_desc(t) for t in (src, scale, offset, dst)]
+    args = [_ref(d[0]), _ref(d[1]), _ref(d[2]), pol, int(k_dim), int(group_size), _ref(d[3])]
+    return PreparedCall(lib.dq_antiquantize_get_workspace_size, lib.dq_antiquantize, args,
+                        (d, src, scale, offset, dst))
+
+
 # -- convenience wrappers ------------------------------------------------------
 
 def dynamic_quant(x: torch.Tensor, smooth_scales: Optional[torch.Tensor] = None,
