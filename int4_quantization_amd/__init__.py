@@ -15,6 +15,7 @@ from .dquant import (  # noqa: F401
     dq_ada_layernorm_quant_get_workspace_size,
     dq_antiquantize,
     dq_antiquantize_get_workspace_size,
+    dq_copy_probe,
     dq_dynamic_quant,
     dq_dynamic_quant_get_workspace_size,
     dq_executor_destroy,
