@@ -157,36 +157,47 @@ def make_work(name, dev) -> Work:
 
 
 def time_work(w: Work, steps: int, warmup: int):
-    """Warm up, then time exactly `steps` launches: wall time between two
-    synchronizations, and per-launch HIP events on the launch stream."""
+    """Warm up, then time exactly `steps` back-to-back launches between two
+    synchronizations: wall time on the host, and a HIP event pair recorded on
+    the launch stream around the same launches (its mean is the kernel's
+    average launch duration: the queue stays full, so gaps are only the
+    hardware dispatch between kernels).  A second, untimed pass brackets
+    each launch with its own events for the latency distribution."""
     for i in range(warmup):
         w.launch(i)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    e0.record(stream)
     for i in range(steps):
-        ev[i][0].record(stream)
         w.launch(warmup + i)
-        ev[i][1].record(stream)
+    e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    lat = np.array([a.elapsed_time(b) for a, b in ev]) * 1e-3  # seconds per launch
-    return wall, lat
+    region = e0.elapsed_time(e1) * 1e-3
+    n = min(steps, 50)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for i in range(n):
+        ev[i][0].record(stream)
+        w.launch(warmup + steps + i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    lat = np.array([a.elapsed_time(b) for a, b in ev]) * 1e-3  # seconds per isolated launch
+    return wall, region, lat
 
 
-def summarize(w: Work, wall: float, lat: np.ndarray, steps: int) -> dict:
-    mean = float(lat.mean())
+def summarize(w: Work, wall: float, region: float, lat: np.ndarray, steps: int) -> dict:
+    mean = region / steps
     return {
         "op": w.op,
         "alg_bytes": int(w.alg_bytes),
         "rows": int(w.rows),
         "us_mean": mean * 1e6,
-        "us_p10": float(np.percentile(lat, 10)) * 1e6,
-        "us_p50": float(np.percentile(lat, 50)) * 1e6,
-        "us_p90": float(np.percentile(lat, 90)) * 1e6,
+        "us_isolated_p10": float(np.percentile(lat, 10)) * 1e6,
+        "us_isolated_p50": float(np.percentile(lat, 50)) * 1e6,
+        "us_isolated_p90": float(np.percentile(lat, 90)) * 1e6,
         "gbps_kernel": w.alg_bytes / mean / 1e9,
         "pct_peak_kernel": 100.0 * w.alg_bytes / mean / 1e9 / PEAK_GBPS,
         "gbps_wall": w.alg_bytes * steps / wall / 1e9,
@@ -292,13 +303,13 @@ def main():
 
     if args.only:
         w = make_work(args.only, dev)
-        wall, lat = time_work(w, args.steps, args.warmup)
-        print(json.dumps({"workload": args.only, **summarize(w, wall, lat, args.steps)}), flush=True)
+        wall, region, lat = time_work(w, args.steps, args.warmup)
+        print(json.dumps({"workload": args.only, **summarize(w, wall, region, lat, args.steps)}), flush=True)
         return
 
     w = make_work(HEADLINE, dev)
-    wall, lat = time_work(w, args.steps, args.warmup)
-    head = summarize(w, wall, lat, args.steps)
+    wall, region, lat = time_work(w, args.steps, args.warmup)
+    head = summarize(w, wall, region, lat, args.steps)
     w.free()
     print(f"# {HEADLINE}: {head['gbps_kernel']:.0f} GB/s ({head['pct_peak_kernel']:.1f}% of peak), "
           f"{head['us_mean']:.2f} us/launch", file=sys.stderr, flush=True)
@@ -311,8 +322,8 @@ def main():
             if name == HEADLINE:
                 continue
             wk = make_work(name, dev)
-            wl, lt = time_work(wk, args.steps, args.warmup)
-            extra[name] = summarize(wk, wl, lt, args.steps)
+            wl, rg, lt = time_work(wk, args.steps, args.warmup)
+            extra[name] = summarize(wk, wl, rg, lt, args.steps)
             wk.free()
             torch.cuda.empty_cache()
             print(f"# {name}: {extra[name]['gbps_kernel']:.0f} GB/s "
