@@ -194,7 +194,8 @@ dq_status dq_ada_layernorm_quant(void* workspace, size_t workspace_size, dq_exec
  *   k_dim      0 or 1, used by DQ_PER_GROUP only.
  *   group_size DQ_PER_GROUP: > 0 and a multiple of 32 (表2); ignored
  *              otherwise.
- *   dst        BF16 or F16 [m, n].
+ *   dst        BF16 or F16 [m, n] (表3), or F32 [m, n] (the unrounded
+ *              binary32 result, an extension of this library).
  *   n * sizeof(src) and n * sizeof(dst) must be multiples of 32 bytes and
  *   src/dst 16-byte aligned (约束说明: 32-byte aligned rows); src and dst
  *   must not overlap.  m may be 0.  Workspace size: 0.

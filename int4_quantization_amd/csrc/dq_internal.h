@@ -37,8 +37,12 @@ struct DqPlan {
     // launch choice
     int variant;
     int vpl;   // 16-byte vectors per lane (vector variant)
-    int team;  // waves per row (vector variant): 1 or 4
+    int team;  // waves per row (vector variant): 1, 2 or 4
 };
+
+// Largest grid (workgroups along x) a launch may use; the DynamicQuant
+// kernels launch one workgroup per row (generic) or per 4/TEAM rows.
+constexpr int64_t kMaxGridBlocks = 0x7FFFFFFF;
 
 // ---- AdaLayerNorm-quant ----------------------------------------------------
 enum AdaVariant : int { ADA_VAR_VECTOR = 0, ADA_VAR_GENERIC = 1 };

@@ -181,6 +181,9 @@ dq_status dq_dynamic_quant_get_workspace_size(const dq_tensor* x, const dq_tenso
     if (n < 1)
         return fail(DQ_ERR_SHAPE, "the last dimension of x must be >= 1");
     const int64_t rows = nx / n;
+    if (rows > dq::kMaxGridBlocks)
+        return fail(DQ_ERR_SHAPE, "at most %lld rows are supported, got %lld", (long long)dq::kMaxGridBlocks,
+                    (long long)rows);
 
     if (y->dtype == DQ_I8 || y->dtype == DQ_I4) {
         if (!same_dims(y, x->dims, x->ndim))
@@ -264,25 +267,16 @@ dq_status dq_dynamic_quant_get_workspace_size(const dq_tensor* x, const dq_tenso
     p.offset = symmetric ? nullptr : static_cast<float*>(offset->data);
 
     // Register-resident variant: rows of whole 16-byte vectors and aligned
-    // buffers.  Rows of up to 4096 elements go to one wave (up to 8 vectors
-    // per lane); longer ones are split over the smallest team of waves (2 or
-    // 4) that keeps them within 4 vectors per lane; wider rows take 8 or 16
-    // vectors per lane on a team of 4; longer rows go to the generic variant.
+    // buffers.  A row goes to the smallest team of waves (1, 2 or 4) that
+    // holds it within 4 vectors per lane; wider rows take 8 or 16 vectors
+    // per lane on a team of 4; longer rows go to the generic variant.
     const bool vec_ok = n % 8 == 0 && aligned(p.x, 16) && (!p.smooth || aligned(p.smooth, 16)) &&
                         aligned(p.y, p.out_kind == dq::OUT_I8 ? 8 : 4);
     p.variant = dq::DQ_VAR_GENERIC;
     if (vec_ok) {
         const int64_t nvec = n / 8;
         static const int kTeams[] = {1, 2, 4};
-        if (nvec <= 8 * 64) {
-            static const int kVpl1[] = {1, 2, 4, 8};
-            p.vpl = pick_vpl((nvec + 63) / 64, kVpl1, 4);
-            p.team = 1;
-            p.variant = dq::DQ_VAR_VECTOR;
-        }
         for (int t : kTeams) {
-            if (p.variant == dq::DQ_VAR_VECTOR)
-                break;
             if (nvec <= 4 * 64 * t) {
                 static const int kVpl[] = {1, 2, 4};
                 p.vpl = pick_vpl((nvec + 64 * t - 1) / (64 * t), kVpl, 3);

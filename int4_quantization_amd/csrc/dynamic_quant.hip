@@ -2,20 +2,23 @@
 // (aclnnDynamicQuantV2, Description and Formula).
 //
 // Vector variant (rows of whole 16-byte vectors up to 4 waves x 16 vectors
-// per lane): persistent workgroups of four waves; TEAM waves (1, 2 or 4)
-// own one row at a time, so a workgroup converts 4/TEAM rows per step.
-// Lane l of team wave w holds the 16-byte vectors k = (i*TEAM + w)*64 + l,
+// per lane): TEAM waves (1, 2 or 4) share a row, so a workgroup of four
+// waves holds 4/TEAM teams; each team converts T consecutive rows (2 for
+// rows of up to 4 vectors per lane, else 1) and the workgroup exits.  Lane
+// l of team wave w holds the 16-byte vectors k = (i*TEAM + w)*64 + l,
 // i < VPL, so every load instruction covers contiguous row bytes; the row
-// stays in VGPRs as fp32 (after the smooth multiply), is reduced through
-// DPP (and LDS across the team), then quantized and stored from the same
-// registers: one HBM read per input element and one write per code, both
-// streamed with non-temporal accesses.  Workgroups sweep down the matrix in
-// tiles of T row groups interleaved across the grid, so all of them work
-// inside one band of rows at a time (a compact DRAM footprint) while each
-// one's consecutive rows mostly share an expert.  Each lane always owns the
-// same columns, so its smooth scales live in VGPRs and are reloaded only
-// when the row's expert changes.  With PF, the next row's loads are issued
-// before the current row is reduced.
+// stays in VGPRs, is widened, smoothed and reduced through DPP (and LDS
+// across the team), then quantized and stored from the same registers: one
+// HBM read per input element and one write per code, both streamed with
+// non-temporal accesses.  The next row's loads are issued before this row
+// is reduced, and the smooth scales are loaded once per team.
+//
+// Why short-lived workgroups rather than a persistent loop over rows: the
+// vector memory counter counts stores as well as loads, so a wave that
+// loads its next row after storing the last one also waits for those stores
+// before it can use the new data; and many short workgroups let the
+// dispatcher keep every CU busy with loads while earlier ones' stores
+// drain, with the rows in flight inside a compact band of the matrix.
 //
 // Generic variant (rows with N % 8 != 0, unaligned buffers, or rows longer
 // than 4 waves x 16 vectors): one workgroup per row, element loads, the row
@@ -27,17 +30,11 @@
 // correctly rounded reciprocal plus Markstein's fma correction, which
 // returns the IEEE quotient for the divisors it is used with.
 
-#include <mutex>
-
 #include "dq_device.h"
 #include "dq_internal.h"
 
 namespace dq {
 namespace {
-
-constexpr bool kDqPrefetch = false;  // issue the next row's loads before reducing this one
-                                      // (measured no faster once loads are unconditional)
-constexpr uint64_t kDqTile = 4;      // row groups a workgroup converts before jumping ahead (power of 2)
 
 struct DqArgs {
     const void* x;
@@ -49,8 +46,6 @@ struct DqArgs {
     void* y;
     float* scale;
     float* offset;
-    int64_t nblocks;
-    int64_t tile;  // row groups per tile (vector variant)
 };
 
 // (D or scale_opt, offset_opt, code range) per output type, from the
@@ -139,16 +134,25 @@ __device__ __forceinline__ uint32_t quant_code(float v, const RowParams<SYM, OUT
     return code_bits(t);
 }
 
+// Eight codes of one vector packed for storing: INT8 as two dwords (four
+// bytes each), INT4 as one dword (eight nibbles, low nibble first).
 template <int OUT>
-__device__ __forceinline__ void store_codes(void* y, int64_t row, int64_t n, int64_t k,
-                                            const uint32_t (&c)[8])
+__device__ __forceinline__ uint2 pack_codes(const uint32_t (&c)[8])
+{
+    if (OUT == OUT_I8)
+        return make_uint2(pack4_i8(c[0], c[1], c[2], c[3]), pack4_i8(c[4], c[5], c[6], c[7]));
+    return make_uint2(pack8_i4(c), 0u);
+}
+
+template <int OUT>
+__device__ __forceinline__ void store_packed(void* y, int64_t row, int64_t n, int64_t k, uint2 pk)
 {
     if (OUT == OUT_I8) {
         uint2* dst = reinterpret_cast<uint2*>(static_cast<int8_t*>(y) + row * n) + k;
-        st_stream8(dst, make_uint2(pack4_i8(c[0], c[1], c[2], c[3]), pack4_i8(c[4], c[5], c[6], c[7])));
+        st_stream8(dst, pk);
     } else {
         uint32_t* dst = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(y) + row * (n >> 1)) + k;
-        st_stream4(dst, pack8_i4(c));
+        st_stream4(dst, pk.x);
     }
 }
 
@@ -169,180 +173,222 @@ __device__ __forceinline__ void load_x(uint4 (&raw)[VPL], const void* x, int64_t
     }
 }
 
-template <int XT, bool SYM, int OUT, int VPL, int TEAM, bool PF>
+// One vector widened to fp32 and multiplied by its smooth scales (the
+// Formula's x * smoothScales, one rounding per element).  Without smooth
+// scales the registers hold 1.0, and x * 1 is x exactly, so the code has no
+// branch here and the compiler can interleave widening with the reduction.
+template <int XT>
+__device__ __forceinline__ void smoothed(const uint4 raw, const float (&sr)[8], float (&v)[8])
+{
+    widen8<XT>(raw, v);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        v[j] = v[j] * sr[j];
+}
+
+// Expert of a row: the cached bounds of the first 64 experts (one per lane)
+// through a ballot, else the general search.  Wave-uniform.
+__device__ __forceinline__ int64_t row_expert(int64_t row, int32_t gi_lane, const DqArgs& a, int lane)
+{
+    if (a.n_experts <= kWave) {
+        // Rows fit in int32 (the host limits them), so the bound is compared
+        // without widening the loaded value, which would consume it (and
+        // wait for it) where it is loaded.
+        const unsigned long long mask = __ballot(lane < a.n_experts && static_cast<int32_t>(row) < gi_lane);
+        return mask ? __builtin_ctzll(mask) : a.n_experts - 1;
+    }
+    return expert_of_row(row, a.gi, a.n_experts, lane);
+}
+
+template <int VPL, int TEAM>
+__device__ __forceinline__ void load_smooth(float (&sreg)[VPL][8], const DqArgs& a, int64_t e, int64_t nvec,
+                                            int wit, int lane)
+{
+    if (a.smooth) {
+        const float4* sr = reinterpret_cast<const float4*>(a.smooth + e * a.n);
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) {
+            int64_t k = static_cast<int64_t>(i * TEAM + wit) * kWave + lane;
+            k = k < nvec ? k : nvec - 1;
+            const float4 s0 = sr[2 * k], s1 = sr[2 * k + 1];
+            sreg[i][0] = s0.x;
+            sreg[i][1] = s0.y;
+            sreg[i][2] = s0.z;
+            sreg[i][3] = s0.w;
+            sreg[i][4] = s1.x;
+            sreg[i][5] = s1.y;
+            sreg[i][6] = s1.z;
+            sreg[i][7] = s1.w;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < VPL; ++i)
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                sreg[i][j] = 1.0f;
+    }
+}
+
+// Reduce, quantize and store one row held in raw[] (step t of the team).
+// Straight-line code: every store is unconditional.  A lane whose vector
+// lies past the row end holds a copy of the last vector (clamped load) and
+// stores its identical codes to that vector's place; a row past the matrix
+// end is a clamped copy of the last row, written with the same bytes its
+// owner writes.  With no branch between this row's stores and the next
+// row's loads, the compiler neither moves those loads below the stores nor
+// makes their wait also wait for the stores.
+template <int XT, bool SYM, int OUT, int VPL, int TEAM>
+__device__ __forceinline__ void convert_row(const DqArgs& a, const uint4 (&raw)[VPL], const float (&sreg)[VPL][8],
+                                            int64_t row, int t, int64_t nvec, int slot, int wit, int lane,
+                                            float (&red)[2][2][4])
+{
+    float s_hi = SYM ? 0.0f : -__builtin_huge_valf();
+    float s_lo = __builtin_huge_valf();
+    float v[VPL][8];
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+        smoothed<XT>(raw[i], sreg[i], v[i]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (SYM) {
+                s_hi = __builtin_fmaxf(s_hi, __builtin_fabsf(v[i][j]));
+            } else {
+                s_hi = __builtin_fmaxf(s_hi, v[i][j]);
+                s_lo = __builtin_fminf(s_lo, v[i][j]);
+            }
+        }
+    }
+    s_hi = wave_max_f(s_hi);
+    if (!SYM)
+        s_lo = wave_min_f(s_lo);
+    if (TEAM > 1) {
+        // Partials alternate between two LDS slots by step, so a slot is
+        // rewritten only after every wave has passed the barrier of the step
+        // that read it.
+        const int par = t & 1;
+        const int wave = slot * TEAM + wit;
+        if (lane == 0) {
+            red[par][0][wave] = s_hi;
+            red[par][1][wave] = s_lo;
+        }
+        __syncthreads();
+        const int w0 = slot * TEAM;
+        s_hi = red[par][0][w0];
+        s_lo = red[par][1][w0];
+#pragma unroll
+        for (int w = 1; w < TEAM; ++w) {
+            s_hi = __builtin_fmaxf(s_hi, red[par][0][w0 + w]);
+            s_lo = __builtin_fminf(s_lo, red[par][1][w0 + w]);
+        }
+        // The values are the same in every lane; saying so keeps the row
+        // parameters in scalar registers and makes the branch below a
+        // scalar one.  (A branch the compiler takes for divergent runs both
+        // store blocks one after the other, and the wait for the next row
+        // then also waits for these stores.)
+        s_hi = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, s_hi)));
+        s_lo = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, s_lo)));
+    }
+
+    const RowParams<SYM, OUT> rp(s_hi, s_lo);
+    // Every lane of the team writes the same value to the same place.
+    a.scale[row] = rp.scale;
+    if (!SYM)
+        a.offset[row] = rp.offset;
+    // Codes are computed on one of two paths and stored after they join, so
+    // the stores are one straight sequence whichever path ran.
+    uint2 pk[VPL];
+    if (rp.fast) {
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) {
+            uint32_t c[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                c[j] = quant_code<SYM, OUT, true>(v[i][j], rp);
+            pk[i] = pack_codes<OUT>(c);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) {
+            uint32_t c[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                c[j] = quant_code<SYM, OUT, false>(v[i][j], rp);
+            pk[i] = pack_codes<OUT>(c);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+        int64_t k = static_cast<int64_t>(i * TEAM + wit) * kWave + lane;
+        k = k < nvec ? k : nvec - 1;
+        store_packed<OUT>(a.y, row, a.n, k, pk[i]);
+    }
+}
+
+// Rows each team converts in one workgroup: the second row's loads are in
+// flight while the first is reduced and stored, and the smooth scales are
+// loaded once for both.
+constexpr int dq_rows_per_team(int vpl)
+{
+    return vpl <= 4 ? 2 : 1;
+}
+
+template <int XT, bool SYM, int OUT, int VPL, int TEAM>
 __global__ __launch_bounds__(kBlock) void dq_vec_kernel(DqArgs a)
 {
-    constexpr int RPS = 4 / TEAM;  // rows per workgroup step
+    constexpr int RPS = 4 / TEAM;  // teams per workgroup
+    constexpr int T = dq_rows_per_team(VPL);
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     const int slot = wave / TEAM;
     const int wit = wave % TEAM;
     const int64_t nvec = a.n >> 3;
-    const uint64_t G = static_cast<uint64_t>(a.nblocks);
-    const uint64_t b = blockIdx.x;
-    constexpr uint64_t T = kDqTile;
-    // Step s of this workgroup converts row group ((b + (s / T) * G) * T + s % T).
-    auto group_of = [&](int64_t step) -> int64_t {
-        const uint64_t u = static_cast<uint64_t>(step);
-        return static_cast<int64_t>((b + (u / T) * G) * T + u % T);
+    // The workgroup converts rows r0 .. r0 + T*RPS - 1: step t of team
+    // `slot` takes row r0 + t*RPS + slot (clamped to the last row).
+    const int64_t r0 = static_cast<int64_t>(blockIdx.x) * (T * RPS);
+    auto row_of = [&](int t) -> int64_t {
+        const int64_t r = r0 + static_cast<int64_t>(t) * RPS + slot;
+        return r < a.rows ? r : a.rows - 1;
     };
-    auto row_of = [&](int64_t step) -> int64_t { return group_of(step) * RPS + slot; };
-    const int64_t groups = (a.rows + RPS - 1) / RPS;
-
-    // Expert bounds cached per lane (first 64 experts).
-    const bool moe = a.gi != nullptr;
-    int32_t gi_lane = 0;
-    if (moe && lane < a.n_experts)
-        gi_lane = a.gi[lane];
-
-    float sreg[VPL][8];
-#pragma unroll
-    for (int i = 0; i < VPL; ++i)
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            sreg[i][j] = 1.0f;
-    int64_t cur_e = -1;
     __shared__ float red[2][2][4];
 
-    uint4 buf0[VPL], buf1[VPL];
-#pragma unroll
-    for (int i = 0; i < VPL; ++i)
-        buf0[i] = buf1[i] = make_uint4(0, 0, 0, 0);
-    if (group_of(0) < groups && row_of(0) < a.rows)
-        load_x<VPL, TEAM>(buf0, a.x, row_of(0), a.n, nvec, wit, lane);
+    // Every load is unconditional or under a workgroup-uniform branch (a
+    // load under a divergent branch makes the compiler wait for everything
+    // outstanding where the branch ends).  Expert bounds are requested
+    // first, so the wait for them does not also wait for the row.
+    const bool moe = a.gi != nullptr;
+    int32_t gi_lane = 0;
+    if (moe)
+        gi_lane = a.gi[lane < a.n_experts ? lane : a.n_experts - 1];
 
-    // One step: row_of(s) is in cur; with PF the next row is requested into
-    // nxt before any arithmetic, otherwise after the stores.  Returns false
-    // when the workgroup has no more rows (workgroup-uniform).
-    auto step = [&](int64_t s, uint4 (&cur)[VPL], uint4 (&nxt)[VPL]) -> bool {
-        if (group_of(s) >= groups)
-            return false;
-        const int64_t row = row_of(s);
-        const bool active = row < a.rows;  // team-uniform
-        const int64_t nrow = row_of(s + 1);
-        const bool has_next = group_of(s + 1) < groups && nrow < a.rows;
-        if (PF && has_next)
-            load_x<VPL, TEAM>(nxt, a.x, nrow, a.n, nvec, wit, lane);
+    uint4 buf[2][VPL];
+    load_x<VPL, TEAM>(buf[0], a.x, row_of(0), a.n, nvec, wit, lane);
 
-        if (a.smooth && active) {
-            int64_t e = 0;
-            if (moe) {
-                if (a.n_experts <= kWave) {
-                    const unsigned long long mask = __ballot(lane < a.n_experts && row < gi_lane);
-                    e = mask ? __builtin_ctzll(mask) : a.n_experts - 1;
-                } else {
-                    e = expert_of_row(row, a.gi, a.n_experts, lane);
-                }
-            }
-            if (e != cur_e) {
-                const float4* sr = reinterpret_cast<const float4*>(a.smooth + e * a.n);
+    float sreg[VPL][8];
+    int64_t e0 = 0;
+    bool one_expert = true;
+    if (moe && a.smooth) {
+        const int64_t r_last = r0 + T * RPS - 1 < a.rows ? r0 + T * RPS - 1 : a.rows - 1;
+        e0 = row_expert(r0, gi_lane, a, lane);
+        one_expert = e0 == row_expert(r_last, gi_lane, a, lane);  // workgroup-uniform
+    }
+    if (one_expert) {
+        load_smooth<VPL, TEAM>(sreg, a, e0, nvec, wit, lane);
 #pragma unroll
-                for (int i = 0; i < VPL; ++i) {
-                    int64_t k = static_cast<int64_t>(i * TEAM + wit) * kWave + lane;
-                    k = k < nvec ? k : nvec - 1;
-                    const float4 s0 = sr[2 * k], s1 = sr[2 * k + 1];
-                    sreg[i][0] = s0.x;
-                    sreg[i][1] = s0.y;
-                    sreg[i][2] = s0.z;
-                    sreg[i][3] = s0.w;
-                    sreg[i][4] = s1.x;
-                    sreg[i][5] = s1.y;
-                    sreg[i][6] = s1.z;
-                    sreg[i][7] = s1.w;
-                }
-                cur_e = e;
-            }
+        for (int t = 0; t < T; ++t) {
+            if (t + 1 < T)
+                load_x<VPL, TEAM>(buf[(t + 1) & 1], a.x, row_of(t + 1), a.n, nvec, wit, lane);
+            __builtin_amdgcn_sched_barrier(0);
+            convert_row<XT, SYM, OUT, VPL, TEAM>(a, buf[t & 1], sreg, row_of(t), t, nvec, slot, wit, lane, red);
         }
-
-        // Widen, smooth and reduce every vector, including the duplicated
-        // tail vectors and an inactive tail row (its results are dropped).
-        float s_hi = SYM ? 0.0f : -__builtin_huge_valf();
-        float s_lo = __builtin_huge_valf();
-        float v[VPL][8];
-#pragma unroll
-        for (int i = 0; i < VPL; ++i) {
-            widen8<XT>(cur[i], v[i]);
-            if (a.smooth) {
-#pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    v[i][j] = v[i][j] * sreg[i][j];
-            }
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                if (SYM) {
-                    s_hi = __builtin_fmaxf(s_hi, __builtin_fabsf(v[i][j]));
-                } else {
-                    s_hi = __builtin_fmaxf(s_hi, v[i][j]);
-                    s_lo = __builtin_fminf(s_lo, v[i][j]);
-                }
-            }
+    } else {
+        // The rows straddle an expert boundary (rare): one row at a time,
+        // each with its own expert's smooth scales.
+        for (int t = 0; t < T; ++t) {
+            if (t > 0)
+                load_x<VPL, TEAM>(buf[0], a.x, row_of(t), a.n, nvec, wit, lane);
+            load_smooth<VPL, TEAM>(sreg, a, row_expert(row_of(t), gi_lane, a, lane), nvec, wit, lane);
+            convert_row<XT, SYM, OUT, VPL, TEAM>(a, buf[0], sreg, row_of(t), t, nvec, slot, wit, lane, red);
         }
-        s_hi = wave_max_f(s_hi);
-        if (!SYM)
-            s_lo = wave_min_f(s_lo);
-        if (TEAM > 1) {
-            // One barrier per step: partials alternate between two LDS slots,
-            // so a slot is rewritten only after every wave has passed the
-            // barrier of the step that read it.
-            const int par = static_cast<int>(s & 1);
-            if (lane == 0) {
-                red[par][0][wave] = s_hi;
-                red[par][1][wave] = s_lo;
-            }
-            __syncthreads();
-            const int w0 = slot * TEAM;
-            s_hi = red[par][0][w0];
-            s_lo = red[par][1][w0];
-#pragma unroll
-            for (int w = 1; w < TEAM; ++w) {
-                s_hi = __builtin_fmaxf(s_hi, red[par][0][w0 + w]);
-                s_lo = __builtin_fminf(s_lo, red[par][1][w0 + w]);
-            }
-        }
-
-        if (active) {
-            const RowParams<SYM, OUT> rp(s_hi, s_lo);
-            if (wit == 0 && lane == 0) {
-                a.scale[row] = rp.scale;
-                if (!SYM)
-                    a.offset[row] = rp.offset;
-            }
-            if (rp.fast) {
-#pragma unroll
-                for (int i = 0; i < VPL; ++i) {
-                    const int64_t k = static_cast<int64_t>(i * TEAM + wit) * kWave + lane;
-                    if (k < nvec) {
-                        uint32_t c[8];
-#pragma unroll
-                        for (int j = 0; j < 8; ++j)
-                            c[j] = quant_code<SYM, OUT, true>(v[i][j], rp);
-                        store_codes<OUT>(a.y, row, a.n, k, c);
-                    }
-                }
-            } else {
-#pragma unroll
-                for (int i = 0; i < VPL; ++i) {
-                    const int64_t k = static_cast<int64_t>(i * TEAM + wit) * kWave + lane;
-                    if (k < nvec) {
-                        uint32_t c[8];
-#pragma unroll
-                        for (int j = 0; j < 8; ++j)
-                            c[j] = quant_code<SYM, OUT, false>(v[i][j], rp);
-                        store_codes<OUT>(a.y, row, a.n, k, c);
-                    }
-                }
-            }
-        }
-        if (!PF && has_next)
-            load_x<VPL, TEAM>(nxt, a.x, nrow, a.n, nvec, wit, lane);
-        return true;
-    };
-
-    for (int64_t s = 0;; s += 2) {
-        if (!step(s, buf0, buf1))
-            break;
-        if (!step(s + 1, buf1, buf0))
-            break;
     }
 }
 
@@ -427,11 +473,15 @@ template <int XT, bool SYM, int OUT, int TEAM>
 KernelFn pick_vpl(int vpl)
 {
     switch (vpl) {
-    case 1: return dq_vec_kernel<XT, SYM, OUT, 1, TEAM, kDqPrefetch>;
-    case 2: return dq_vec_kernel<XT, SYM, OUT, 2, TEAM, kDqPrefetch>;
-    case 4: return dq_vec_kernel<XT, SYM, OUT, 4, TEAM, kDqPrefetch>;
-    case 8: return dq_vec_kernel<XT, SYM, OUT, 8, TEAM, kDqPrefetch>;
-    case 16: return dq_vec_kernel<XT, SYM, OUT, 16, TEAM, kDqPrefetch>;
+    case 1: return dq_vec_kernel<XT, SYM, OUT, 1, TEAM>;
+    case 2: return dq_vec_kernel<XT, SYM, OUT, 2, TEAM>;
+    case 4: return dq_vec_kernel<XT, SYM, OUT, 4, TEAM>;
+    }
+    if constexpr (TEAM == 4) {  // only the widest rows take more vectors per lane
+        if (vpl == 8)
+            return dq_vec_kernel<XT, SYM, OUT, 8, TEAM>;
+        if (vpl == 16)
+            return dq_vec_kernel<XT, SYM, OUT, 16, TEAM>;
     }
     return nullptr;
 }
@@ -457,32 +507,6 @@ KernelFn pick_x(const DqPlan& p)
     return p.out_kind == OUT_I8 ? pick<XT, false, OUT_I8>(p) : pick<XT, false, OUT_I4>(p);
 }
 
-// Resident workgroups per CU for a kernel, and the CU count, looked up once
-// per device and kernel.
-int64_t resident_blocks(KernelFn fn)
-{
-    struct Entry { int device; KernelFn fn; int64_t blocks; };
-    static Entry cache[64];
-    static int used = 0;
-    static std::mutex mu;
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess)
-        return 0;
-    std::lock_guard<std::mutex> lock(mu);
-    for (int i = 0; i < used; ++i)
-        if (cache[i].device == dev && cache[i].fn == fn)
-            return cache[i].blocks;
-    int per_cu = 0, cus = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fn), kBlock, 0) !=
-            hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-        return 0;
-    const int64_t blocks = static_cast<int64_t>(per_cu > 0 ? per_cu : 1) * cus;
-    if (used < 64)
-        cache[used++] = Entry{dev, fn, blocks};
-    return blocks;
-}
-
 }  // namespace
 
 hipError_t launch_dynamic_quant(const DqPlan& p, hipStream_t stream)
@@ -490,22 +514,15 @@ hipError_t launch_dynamic_quant(const DqPlan& p, hipStream_t stream)
     KernelFn fn = p.x_type == X_F16 ? pick_x<X_F16>(p) : pick_x<X_BF16>(p);
     if (!fn)
         return hipErrorInvalidValue;
-    DqArgs a{p.x, p.smooth, p.group_index, p.n_experts, p.rows, p.n, p.y, p.scale, p.offset, 0, 1};
-    if (p.variant == DQ_VAR_VECTOR) {
-        const int64_t rps = 4 / p.team;
-        const int64_t groups = (p.rows + rps - 1) / rps;
-        a.tile = static_cast<int64_t>(kDqTile);
-        const int64_t tiles = (groups + a.tile - 1) / a.tile;
-        const int64_t resident = resident_blocks(fn);
-        if (resident <= 0)
-            return hipErrorInvalidValue;
-        a.nblocks = tiles < resident ? tiles : resident;
-    } else {
-        a.nblocks = p.rows;
-    }
+    DqArgs a{p.x, p.smooth, p.group_index, p.n_experts, p.rows, p.n, p.y, p.scale, p.offset};
+    // Vector variant: one workgroup per T * 4/TEAM rows; generic: one per row.
+    const int64_t rpb = p.variant == DQ_VAR_VECTOR ? dq_rows_per_team(p.vpl) * (4 / p.team) : 1;
+    const int64_t blocks = (p.rows + rpb - 1) / rpb;
+    if (blocks > kMaxGridBlocks)
+        return hipErrorInvalidValue;
     void* args[] = {&a};
-    return hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3(static_cast<uint32_t>(a.nblocks)),
-                           dim3(kBlock), args, 0, stream);
+    return hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3(static_cast<uint32_t>(blocks)), dim3(kBlock),
+                           args, 0, stream);
 }
 
 }  // namespace dq
