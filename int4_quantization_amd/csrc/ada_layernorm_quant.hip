@@ -4,19 +4,23 @@
 //   y  = LN * (1 + scale[b]) + shift[b];   y = y * smooth
 //   quantScale = row_max(|y|) / 127;      out = round(y / quantScale)
 //
-// Layout of the work: a workgroup owns a contiguous chunk of rows (workgroups
-// in launch order, so the running ones cover one band of rows).  For each
-// batch b its chunk touches, it first writes the per-column coefficients
+// Layout of the work: a workgroup of four waves converts 4*T consecutive
+// rows (T = 4 per wave, each next row's loads in flight while the current
+// one is processed) and exits.  When its rows share a batch b, it first writes the
+// per-column coefficients
 //   A_j = w_j * (1 + scale_bj) * smooth_j
 //   C_j = (bias_j * (1 + scale_bj) + shift_bj) * smooth_j
-// into LDS, so that y_j = ((x_j - mean) * rstd) * A_j + C_j is one multiply
-// and one fma per element.  Each row is then held in VGPRs by one wave
-// (16-byte non-temporal loads, one HBM read per element); its statistics
-// are Welford style: every lane forms (count, mean, M2) of its own elements
-// from the registers, and the lanes merge with Chan's pairwise update in a
-// fixed butterfly (a reciprocal-free form when every lane holds the same
-// count).  Statistics, normalization and modulation are fp32 with hardware
-// rsq / rcp; quantScale is the exact binary32 RN(max|y| / 127).
+// into LDS from 16-byte parameter loads, so that
+// y_j = ((x_j - mean) * rstd) * A_j + C_j is one multiply and one fma per
+// element.  Each row is held in VGPRs by one wave (16-byte non-temporal
+// loads, one HBM read per element); its statistics are Welford style: every
+// lane forms (count, mean, M2) of its own elements from the registers, and
+// the lanes merge with Chan's pairwise update in a fixed butterfly (a
+// reciprocal-free form when every lane holds the same count).  Statistics,
+// normalization and modulation are fp32 with hardware rsq; quantScale is
+// the exact binary32 RN(max|y| / 127).  Loads and stores are unconditional
+// (clamped) so that no wait for the next row's data also waits for this
+// row's stores.
 //
 // Rows that are not whole 16-byte vectors or are longer than 16 vectors
 // per lane use the generic kernel (one workgroup per row, three passes over
@@ -27,10 +31,6 @@
 
 namespace dq {
 namespace {
-
-// Launch one workgroup per chunk of rows (false) or a persistent grid that
-// sweeps the chunks and rebuilds its LDS table only when the batch changes.
-constexpr bool kAdaPersistent = false;
 
 struct AdaArgs {
     const void* x;
@@ -43,8 +43,6 @@ struct AdaArgs {
     float eps;
     int8_t* out;
     float* qs;
-    int64_t rpb;
-    int64_t nblocks;
     int equal_counts;  // every lane holds the same number of elements (H % 512 == 0)
     float inv_h;       // RN(1 / H)
 };
@@ -156,140 +154,224 @@ __device__ __forceinline__ uint32_t q8(float y, const QParams& qp)
     return code_bits(__builtin_amdgcn_fmed3f(t, -128.0f, 127.0f));
 }
 
-// LDS table: four float4 planes of H/8 entries each: A[8k..8k+3],
-// A[8k+4..8k+7], C[8k..8k+3], C[8k+4..8k+7], so that lane k's 16-byte
-// reads of consecutive k are contiguous.
-__device__ __forceinline__ int64_t tab_index(int64_t H, int plane, int64_t j)
+// Rows each wave converts in one workgroup: each next row's loads are in
+// flight while the current one is reduced and stored, and the workgroup's
+// coefficient table serves 4 * kAdaRowsPerWave rows.
+constexpr int kAdaRowsPerWave = 4;
+
+// Eight consecutive columns 8k..8k+7 of the modulation coefficients for
+// batch b (same formula order as coeffs()), from 16-byte loads.  Every load
+// is unconditional, so all of them are in flight together: an absent
+// weight, bias or smooth vector reads a stand-in of the same size from the
+// batch's scale row (always present) and its values are replaced after.
+template <int XT>
+__device__ __forceinline__ void coeffs8(const AdaArgs& a, int64_t b, int64_t k, float (&A)[8], float (&C)[8])
 {
-    const int64_t k = j >> 3;
-    const int r = static_cast<int>(j & 7);
-    const int q = plane * 2 + (r >> 2);
-    return (q * (H >> 3) + k) * 4 + (r & 3);
+    const uint4* scrow = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.scale) + b * a.H);
+    const uint4* shrow = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.shift) + b * a.H);
+    const uint4 scv = scrow[k];
+    const uint4 shv = shrow[k];
+    const uint4 wv = (a.weight ? static_cast<const uint4*>(a.weight) : scrow)[k];
+    const uint4 bv = (a.bias ? static_cast<const uint4*>(a.bias) : shrow)[k];
+    const float4* sm4 = reinterpret_cast<const float4*>(a.smooth);
+    const float4* stand_in = reinterpret_cast<const float4*>(scrow + k);
+    const float4 s0 = *(a.smooth ? sm4 + 2 * k : stand_in);
+    const float4 s1 = *(a.smooth ? sm4 + 2 * k + 1 : stand_in);
+    float w[8], bb[8], sc[8], sh[8];
+    widen8<XT>(scv, sc);
+    widen8<XT>(shv, sh);
+    widen8<XT>(wv, w);
+    widen8<XT>(bv, bb);
+    const float sm[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const float wj = a.weight ? w[j] : 1.0f;
+        const float bj = a.bias ? bb[j] : 0.0f;
+        const float one_plus = 1.0f + sc[j];
+        A[j] = wj * one_plus;
+        C[j] = bj * one_plus;
+        C[j] = C[j] + sh[j];
+        if (a.smooth) {
+            A[j] = A[j] * sm[j];
+            C[j] = C[j] * sm[j];
+        }
+    }
 }
 
-template <int XT, int VPL>
+// LDS table of one batch's coefficients: four float4 planes of H/8 entries,
+// A[8k..8k+3], A[8k+4..8k+7], C[8k..8k+3], C[8k+4..8k+7], so that lane k's
+// 16-byte reads of consecutive k are contiguous and conflict-free.
+template <int XT>
+__device__ __forceinline__ void build_table(const AdaArgs& a, int64_t b, float4* tab4, int64_t nvec)
+{
+    // Threads past the last entry rewrite it with the same values.
+    for (int64_t k0 = 0; k0 < nvec; k0 += kBlock) {
+        int64_t k = k0 + threadIdx.x;
+        k = k < nvec ? k : nvec - 1;
+        float A[8], C[8];
+        coeffs8<XT>(a, b, k, A, C);
+        tab4[0 * nvec + k] = make_float4(A[0], A[1], A[2], A[3]);
+        tab4[1 * nvec + k] = make_float4(A[4], A[5], A[6], A[7]);
+        tab4[2 * nvec + k] = make_float4(C[0], C[1], C[2], C[3]);
+        tab4[3 * nvec + k] = make_float4(C[4], C[5], C[6], C[7]);
+    }
+}
+
+// One row held in raw[] (wave-wide): statistics, modulation, quantization
+// and stores.  FULL: every lane holds VPL whole vectors of the row (no
+// tail).  Otherwise a lane whose vector lies past the row end holds a copy
+// of the last vector (clamped load): it is left out of the statistics, and
+// its y values and codes equal those of the vector it copies, so it changes
+// neither max|y| nor the bytes stored (it writes that vector's codes again).
+// Coefficients come from the LDS table.  Straight-line except the
+// row-uniform fast/slow choice, whose paths join before the stores.
+template <int XT, int VPL, bool FULL>
+__device__ __forceinline__ void ada_row(const AdaArgs& a, const uint4 (&raw)[VPL], int64_t row, int64_t nvec,
+                                        int lane, const float4* tab4)
+{
+    float v[VPL][8];
+    float sum = 0.0f, cnt = 0.0f;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+        widen8<XT>(raw[i], v[i]);
+        const bool ok = FULL || static_cast<int64_t>(i) * kWave + lane < nvec;
+        if (!FULL)
+            cnt += ok ? 8.0f : 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            sum += FULL ? v[i][j] : (ok ? v[i][j] : 0.0f);
+    }
+    if (FULL)
+        cnt = 8.0f * VPL;
+    // Welford-style statistics: (count, mean, M2) of the lane's own elements
+    // from the registers, then Chan's pairwise merge across the lanes.
+    Stats st{cnt, 0.0f, 0.0f};
+    st.mean = cnt > 0.0f ? sum / cnt : 0.0f;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+        const bool ok = FULL || static_cast<int64_t>(i) * kWave + lane < nvec;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float d = FULL ? v[i][j] - st.mean : (ok ? v[i][j] - st.mean : 0.0f);
+            st.m2 = __builtin_fmaf(d, d, st.m2);
+        }
+    }
+    st = (FULL || a.equal_counts) ? wave_merge_equal(st) : wave_merge(st);
+    const float var = st.m2 * a.inv_h;
+    const float rstd = __builtin_amdgcn_rsqf(var + a.eps);
+    const float mean = st.mean;
+
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+        int64_t k = static_cast<int64_t>(i) * kWave + lane;
+        if (!FULL)
+            k = k < nvec ? k : nvec - 1;
+        const float4 A0 = tab4[0 * nvec + k], A1 = tab4[1 * nvec + k];
+        const float4 C0 = tab4[2 * nvec + k], C1 = tab4[3 * nvec + k];
+        const float Av[8] = {A0.x, A0.y, A0.z, A0.w, A1.x, A1.y, A1.z, A1.w};
+        const float Cv[8] = {C0.x, C0.y, C0.z, C0.w, C1.x, C1.y, C1.z, C1.w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float nrm = (v[i][j] - mean) * rstd;
+            v[i][j] = __builtin_fmaf(nrm, Av[j], Cv[j]);
+            amax = __builtin_fmaxf(amax, __builtin_fabsf(v[i][j]));
+        }
+    }
+    amax = wave_max_f(amax);
+    const QParams qp(amax);
+    a.qs[row] = qp.qs;  // every lane writes the same value
+    uint2 pk[VPL];
+    if (qp.fast) {
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) {
+            uint32_t c[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                c[j] = q8<true>(v[i][j], qp);
+            pk[i] = make_uint2(pack4_i8(c[0], c[1], c[2], c[3]), pack4_i8(c[4], c[5], c[6], c[7]));
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) {
+            uint32_t c[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                c[j] = q8<false>(v[i][j], qp);
+            pk[i] = make_uint2(pack4_i8(c[0], c[1], c[2], c[3]), pack4_i8(c[4], c[5], c[6], c[7]));
+        }
+    }
+    uint2* orow = reinterpret_cast<uint2*>(a.out + row * a.H);
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+        int64_t k = static_cast<int64_t>(i) * kWave + lane;
+        if (!FULL)
+            k = k < nvec ? k : nvec - 1;
+        st_stream8(orow + k, pk[i]);
+    }
+}
+
+template <int VPL, bool FULL>
+__device__ __forceinline__ void ada_load(uint4 (&raw)[VPL], const AdaArgs& a, int64_t row, int64_t nvec, int lane)
+{
+    const uint4* xr = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) + row * a.H);
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+        int64_t k = static_cast<int64_t>(i) * kWave + lane;
+        if (!FULL)
+            k = k < nvec ? k : nvec - 1;
+        raw[i] = ld_stream16(xr + k);
+    }
+}
+
+// A workgroup converts rows r0 .. r0 + 4T - 1 (T = kAdaRowsPerWave): step t
+// of wave w takes row r0 + 4t + w (clamped to the last row, whose duplicate
+// writes the bytes its owner writes).  When all of them belong to one
+// batch, the workgroup writes that batch's coefficients into LDS once and
+// streams its rows; otherwise (rows across a batch boundary, e.g. S < 4T)
+// it goes through the batches its rows touch, one table each.
+template <int XT, int VPL, bool FULL>
 __global__ __launch_bounds__(kBlock) void ada_vec_kernel(AdaArgs a)
 {
     extern __shared__ float4 tab4[];
-    float* tab = reinterpret_cast<float*>(tab4);
+    constexpr int T = kAdaRowsPerWave;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
-    const int64_t H = a.H;
-    const int64_t nvec = H >> 3;
-    const int64_t plane = nvec;  // float4 entries per plane
-    const int64_t nchunks = (a.rows + a.rpb - 1) / a.rpb;
-    int64_t tab_batch = -1;
+    const int64_t nvec = a.H >> 3;
+    const int64_t r0 = static_cast<int64_t>(blockIdx.x) * (4 * T);
+    auto row_of = [&](int t) -> int64_t {
+        const int64_t r = r0 + 4 * t + wave;
+        return r < a.rows ? r : a.rows - 1;
+    };
+    const int64_t r_last = r0 + 4 * T - 1 < a.rows ? r0 + 4 * T - 1 : a.rows - 1;
+    const int64_t b0 = r0 / a.S, b_last = r_last / a.S;
 
-    // Chunks of rpb rows, strided over the grid (one chunk per workgroup when
-    // the grid covers them all; a sweep of persistent workgroups otherwise).
-    for (int64_t chunk = blockIdx.x; chunk < nchunks; chunk += gridDim.x) {
-    const int64_t r0 = chunk * a.rpb;
-    const int64_t r1 = r0 + a.rpb < a.rows ? r0 + a.rpb : a.rows;
-    int64_t r = r0;
-    int64_t b = r0 / a.S;
-    while (r < r1) {
-        const int64_t r_end = (b + 1) * a.S < r1 ? (b + 1) * a.S : r1;
-        if (b != tab_batch) {  // workgroup-uniform
-            __syncthreads();  // earlier readers of the table are done
-            for (int64_t j = threadIdx.x; j < H; j += kBlock) {
-                float A, C;
-                coeffs<XT>(a, b, j, A, C);
-                tab[tab_index(H, 0, j)] = A;
-                tab[tab_index(H, 1, j)] = C;
-            }
-            __syncthreads();
-            tab_batch = b;
+    if (b0 == b_last) {  // workgroup-uniform
+        uint4 buf[2][VPL];
+        ada_load<VPL, FULL>(buf[0], a, row_of(0), nvec, lane);
+        build_table<XT>(a, b0, tab4, nvec);
+        __syncthreads();
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            if (t + 1 < T)
+                ada_load<VPL, FULL>(buf[(t + 1) & 1], a, row_of(t + 1), nvec, lane);
+            __builtin_amdgcn_sched_barrier(0);
+            ada_row<XT, VPL, FULL>(a, buf[t & 1], row_of(t), nvec, lane, tab4);
         }
-
-        for (int64_t row = r + wave; row < r_end; row += 4) {
-            // Every load is unconditional: lanes past the row end re-load the
-            // row's last vector (their results are never stored).
-            const uint4* xr = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) + row * H);
-            uint4 raw[VPL];
-#pragma unroll
-            for (int i = 0; i < VPL; ++i) {
-                const int64_t k = static_cast<int64_t>(i) * kWave + lane;
-                raw[i] = ld_stream16(xr + (k < nvec ? k : nvec - 1));
-            }
-            // Welford-style statistics: each lane forms (count, mean, M2) of
-            // its own elements from the registers (two passes over them), and
-            // the lanes merge with Chan's pairwise update in a fixed butterfly.
-            float v[VPL][8];
-            float cnt = 0.0f, sum = 0.0f;
-#pragma unroll
-            for (int i = 0; i < VPL; ++i) {
-                const int64_t k = static_cast<int64_t>(i) * kWave + lane;
-                widen8<XT>(raw[i], v[i]);
-                if (k < nvec) {
-                    cnt += 8.0f;
-#pragma unroll
-                    for (int j = 0; j < 8; ++j)
-                        sum += v[i][j];
+    } else {
+        for (int64_t b = b0; b <= b_last; ++b) {
+            __syncthreads();  // the previous table's readers are done
+            build_table<XT>(a, b, tab4, nvec);
+            __syncthreads();
+            for (int t = 0; t < T; ++t) {
+                const int64_t r = r0 + 4 * t + wave;
+                if (r < a.rows && r / a.S == b) {
+                    uint4 raw[VPL];
+                    ada_load<VPL, FULL>(raw, a, r, nvec, lane);
+                    ada_row<XT, VPL, FULL>(a, raw, r, nvec, lane, tab4);
                 }
             }
-            Stats st{cnt, 0.0f, 0.0f};
-            if (cnt > 0.0f) {
-                st.mean = sum / cnt;
-#pragma unroll
-                for (int i = 0; i < VPL; ++i) {
-                    const int64_t k = static_cast<int64_t>(i) * kWave + lane;
-                    if (k < nvec) {
-#pragma unroll
-                        for (int j = 0; j < 8; ++j) {
-                            const float d = v[i][j] - st.mean;
-                            st.m2 = __builtin_fmaf(d, d, st.m2);
-                        }
-                    }
-                }
-            }
-            st = a.equal_counts ? wave_merge_equal(st) : wave_merge(st);
-            const float var = st.m2 * a.inv_h;
-            const float rstd = __builtin_amdgcn_rsqf(var + a.eps);
-            const float mean = st.mean;
-
-            float amax = 0.0f;
-#pragma unroll
-            for (int i = 0; i < VPL; ++i) {
-                const int64_t k = static_cast<int64_t>(i) * kWave + lane;
-                if (k < nvec) {
-                    const float4 A0 = tab4[0 * plane + k], A1 = tab4[1 * plane + k];
-                    const float4 C0 = tab4[2 * plane + k], C1 = tab4[3 * plane + k];
-                    const float Av[8] = {A0.x, A0.y, A0.z, A0.w, A1.x, A1.y, A1.z, A1.w};
-                    const float Cv[8] = {C0.x, C0.y, C0.z, C0.w, C1.x, C1.y, C1.z, C1.w};
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        const float nrm = (v[i][j] - mean) * rstd;
-                        v[i][j] = __builtin_fmaf(nrm, Av[j], Cv[j]);
-                        amax = __builtin_fmaxf(amax, __builtin_fabsf(v[i][j]));
-                    }
-                }
-            }
-            amax = wave_max_f(amax);
-            const QParams qp(amax);
-            if (lane == 0)
-                a.qs[row] = qp.qs;
-            uint2* orow = reinterpret_cast<uint2*>(a.out + row * H);
-#pragma unroll
-            for (int i = 0; i < VPL; ++i) {
-                const int64_t k = static_cast<int64_t>(i) * kWave + lane;
-                if (k < nvec) {
-                    uint32_t c[8];
-                    if (qp.fast) {
-#pragma unroll
-                        for (int j = 0; j < 8; ++j)
-                            c[j] = q8<true>(v[i][j], qp);
-                    } else {
-#pragma unroll
-                        for (int j = 0; j < 8; ++j)
-                            c[j] = q8<false>(v[i][j], qp);
-                    }
-                    st_stream8(orow + k, make_uint2(pack4_i8(c[0], c[1], c[2], c[3]), pack4_i8(c[4], c[5], c[6], c[7])));
-                }
-            }
-                }
-        r = r_end;
-        ++b;
-    }
+        }
     }
 }
 
@@ -367,19 +449,25 @@ __global__ __launch_bounds__(kBlock) void ada_generic_kernel(AdaArgs a)
 
 using KernelFn = void (*)(AdaArgs);
 
-template <int XT>
+template <int XT, bool FULL>
 KernelFn pick_vec(int vpl)
 {
     switch (vpl) {
-    case 1: return ada_vec_kernel<XT, 1>;
-    case 2: return ada_vec_kernel<XT, 2>;
-    case 4: return ada_vec_kernel<XT, 4>;
-    case 6: return ada_vec_kernel<XT, 6>;
-    case 8: return ada_vec_kernel<XT, 8>;
-    case 12: return ada_vec_kernel<XT, 12>;
-    case 16: return ada_vec_kernel<XT, 16>;
+    case 1: return ada_vec_kernel<XT, 1, FULL>;
+    case 2: return ada_vec_kernel<XT, 2, FULL>;
+    case 4: return ada_vec_kernel<XT, 4, FULL>;
+    case 6: return ada_vec_kernel<XT, 6, FULL>;
+    case 8: return ada_vec_kernel<XT, 8, FULL>;
+    case 12: return ada_vec_kernel<XT, 12, FULL>;
+    case 16: return ada_vec_kernel<XT, 16, FULL>;
     }
     return nullptr;
+}
+
+template <int XT>
+KernelFn pick_vec_x(int vpl, bool full)
+{
+    return full ? pick_vec<XT, true>(vpl) : pick_vec<XT, false>(vpl);
 }
 
 }  // namespace
@@ -403,31 +491,23 @@ hipError_t launch_ada_layernorm_quant(const AdaPlan& p, hipStream_t stream)
     a.inv_h = 1.0f / static_cast<float>(p.H);
     KernelFn fn;
     size_t lds = 0;
+    int64_t rows_per_block = 1;
     if (p.variant == ADA_VAR_VECTOR) {
-        fn = p.x_type == X_F16 ? pick_vec<X_F16>(p.vpl) : pick_vec<X_BF16>(p.vpl);
-        a.rpb = p.rows_per_block;
+        const bool full = p.H == static_cast<int64_t>(p.vpl) * kWave * 8;
+        fn = p.x_type == X_F16 ? pick_vec_x<X_F16>(p.vpl, full) : pick_vec_x<X_BF16>(p.vpl, full);
+        rows_per_block = 4 * kAdaRowsPerWave;
         lds = static_cast<size_t>(p.H) * 2 * sizeof(float);
     } else {
         fn = p.x_type == X_F16 ? ada_generic_kernel<X_F16> : ada_generic_kernel<X_BF16>;
-        a.rpb = 1;
     }
     if (!fn)
         return hipErrorInvalidValue;
-    a.nblocks = (a.rows + a.rpb - 1) / a.rpb;
-    if (p.variant == ADA_VAR_VECTOR && kAdaPersistent) {
-        int per_cu = 0, cus = 0, dev = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fn), kBlock, lds) !=
-                hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-            return hipErrorInvalidValue;
-        const int64_t resident = static_cast<int64_t>(per_cu > 0 ? per_cu : 1) * cus;
-        if (a.nblocks > resident)
-            a.nblocks = resident;
-    }
+    const int64_t blocks = (a.rows + rows_per_block - 1) / rows_per_block;
+    if (blocks > kMaxGridBlocks)
+        return hipErrorInvalidValue;
     void* args[] = {&a};
-    return hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3(static_cast<uint32_t>(a.nblocks)),
-                           dim3(kBlock), args, lds, stream);
+    return hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3(static_cast<uint32_t>(blocks)), dim3(kBlock),
+                           args, lds, stream);
 }
 
 }  // namespace dq

@@ -61,7 +61,6 @@ struct AdaPlan {
     float* quant_scale;
     int variant;
     int vpl;
-    int rows_per_block;
 };
 
 // ---- AntiQuantize ---------------------------------------------------------

@@ -405,17 +405,14 @@ dq_status dq_ada_layernorm_quant_get_workspace_size(const dq_tensor* x, const dq
     p.quant_scale = static_cast<float*>(quant_scale->data);
 
     static const int kVpl[] = {1, 2, 4, 6, 8, 12, 16};
-    const bool vec_ok = H % 8 == 0 && aligned(p.x, 16) && aligned(p.out, 8);
+    // The vector variant reads eight columns of every parameter with one
+    // 16-byte load, so they need 16-byte alignment too.
+    const bool vec_ok = H % 8 == 0 && aligned(p.x, 16) && aligned(p.out, 8) && aligned(p.scale, 16) &&
+                        aligned(p.shift, 16) && (!p.weight || aligned(p.weight, 16)) &&
+                        (!p.bias || aligned(p.bias, 16)) && (!p.smooth || aligned(p.smooth, 16));
     int v = vec_ok ? pick_vpl((H / 8 + 63) / 64, kVpl, 7) : -1;
     p.variant = v > 0 ? dq::ADA_VAR_VECTOR : dq::ADA_VAR_GENERIC;
     p.vpl = v;
-    // Rows per workgroup: enough rows per block to amortize the per-batch
-    // parameter table, while keeping well over 4 blocks per CU.
-    const int64_t rows = B * S;
-    int rpb = 4;
-    while (rpb < 64 && rows / (rpb * 2) >= 1024)
-        rpb *= 2;
-    p.rows_per_block = rpb;
     *executor = e;
     return ok();
 }

@@ -106,9 +106,13 @@ def ada_tolerance_ok(out: np.ndarray, qs: np.ndarray, rout: np.ndarray, rqs: np.
     return bool(qs_ok), int(diff.max(initial=0)), int(np.count_nonzero(diff)), allowed
 
 
-def check_ada_layernorm_quant(orc, inp):
+def check_ada_layernorm_quant(orc, inp, dev_override=None):
+    """dev_override: device tensors to pass instead of copies of inp's (same
+    values, e.g. an unaligned view)."""
     names = ("x", "scale", "shift", "weight", "bias", "smooth")
-    out, qs = dq.ada_layernorm_quant(*[to_dev(inp[k]) for k in names], epsilon=inp["eps"])
+    dev = {k: to_dev(inp[k]) for k in names}
+    dev.update(dev_override or {})
+    out, qs = dq.ada_layernorm_quant(*[dev[k] for k in names], epsilon=inp["eps"])
     sm = None if inp["smooth"] is None else inp["smooth"].numpy()
     rout, rqs = orc.ada_layernorm_quant(inp["x"], inp["scale"], inp["shift"], inp["weight"],
                                         inp["bias"], sm, inp["eps"])

@@ -3,7 +3,8 @@ at the stated tolerance (quantScale within 1e-5 relative; codes within +-1,
 differing on at most 0.01 % of elements): register-resident rows of 1..16
 vectors per lane, the generic path (H not a multiple of 8, H > 8192),
 optional weight / bias / smooth, [B,1,H] and [B,H] modulation, fp16 / bf16,
-chunks of rows that straddle batches."""
+workgroups whose rows straddle batches (down to one row per batch), and an
+unaligned parameter vector."""
 import numpy as np
 import pytest
 import torch
@@ -15,7 +16,7 @@ pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
 
 SHAPES = [(2, 37, 3072), (1, 5, 256), (3, 7, 1000), (2, 9, 64), (1, 4, 8192), (5, 3, 512),
-          (2, 3, 250), (1, 3, 10000), (2, 11, 6144)]
+          (2, 3, 250), (1, 3, 10000), (2, 11, 6144), (6, 1, 1024), (3, 40, 2048)]
 
 
 @pytest.mark.parametrize("B,S,H", SHAPES, ids=[f"{b}x{s}x{h}" for b, s, h in SHAPES])
@@ -50,6 +51,17 @@ def test_ada_special_rows(orc):
     check_ada_layernorm_quant(orc, inp)
     inp["scale"] = -torch.ones_like(inp["scale"])
     check_ada_layernorm_quant(orc, inp)
+
+
+def test_ada_unaligned_weight(orc):
+    """A weight vector that is not 16-byte aligned takes the generic path."""
+    announce("ada_layernorm_quant unaligned weight")
+    inp = synth.ada_inputs(2, 9, 1024, 61)
+    backing = torch.empty(1024 + 1, dtype=inp["weight"].dtype, device=DEV)
+    backing[1:] = inp["weight"].to(DEV)
+    w = backing[1:]
+    assert w.data_ptr() % 16 != 0
+    check_ada_layernorm_quant(orc, inp, dev_override={"weight": w})
 
 
 def test_ada_deterministic():
