@@ -2,22 +2,22 @@
 // (AntiQuantize, 功能说明: PER_TENSOR / PER_CHANNEL / PER_TOKEN / PER_GROUP,
 // 表1 kDim, 表2 groupSize).
 //
-// Each wave owns one 1024-column strip and every G-th row of it (G = waves
-// per strip), so at any moment all waves work inside one band of rows that
-// sweeps down the matrix -- a compact DRAM footprint, which measured far
-// faster than giving each wave a contiguous block of rows.  A wave keeps
-// kPD of its rows in flight: before it converts row i it has already
-// requested the next kPD-1, and right after converting row i it requests
-// the one kPD steps ahead.  Lanes own E-element
-// chunks, E = 8 for bf16/fp16 output (16 bytes) and E = 4 for fp32: chunk c
-// of lane l covers columns strip*1024 + c*64*E + l*E, so every store
-// instruction of the wave writes 1 KiB of contiguous output and every load
-// instruction reads 64*E contiguous source bytes.  Source and destination
-// are streamed with non-temporal accesses.  Parameters that vary along n
-// are loaded once per wave (PER_CHANNEL) or once per group of rows
-// (PER_GROUP with kDim = 0); a chunk never straddles a group because
-// groupSize is a multiple of 32.  PER_TOKEN parameters are wave-uniform per
-// row; PER_GROUP with kDim = 1 needs one parameter per chunk per row.
+// A flat grid of short-lived threads: each converts one chunk of E
+// consecutive elements of a row (E = 8 for bf16/fp16 output, 4 for fp32),
+// so a lane reads 8 (or 4) source bytes and writes 16 output bytes, and
+// every load and store instruction of a wave covers contiguous memory.
+// That shape -- one narrow load and one 16-byte store per thread, many
+// small workgroups -- measured fastest for this one-read, two-write
+// traffic; every extra load or store a thread keeps in flight cost
+// several percent.  Policies whose parameters vary along n (PER_CHANNEL,
+// PER_GROUP with kDim = 0) instead give a thread R consecutive rows of one
+// chunk, so the thread's parameter vectors are loaded once for R rows;
+// PER_TOKEN and PER_GROUP with kDim = 1 load one parameter pair per chunk,
+// PER_TENSOR one for the whole launch.  Row and column come from one
+// multiply-shift division by the chunks per row (exact for indices below
+// 2^31; larger inputs are split over several launches).  Threads past the
+// end repeat the last chunk, so every access is unconditional.  Source and
+// destination are streamed with non-temporal accesses.
 //
 // Arithmetic (the page omits the formula; the library's reading):
 //   dst = RN(RN(src + offset) * scale)   or   RN(src * scale)
@@ -30,30 +30,54 @@
 namespace dq {
 namespace {
 
-constexpr int kPD = 2;               // rows of loads in flight per wave
-constexpr int64_t kTargetWaves = 16384;  // 256 CUs x 64 waves
-
 enum AqPolicyKind : int { PK_TENSOR = 0, PK_CHANNEL = 1, PK_TOKEN = 2, PK_GROUP_N = 3, PK_GROUP_M = 4 };
+
+constexpr int kAqRowsPerThread = 8;  // PER_CHANNEL / PER_GROUP kDim = 0 (divides every groupSize)
+
+// floor(x / d) = (x * mult) >> shift for 0 <= x < 2^31, with
+// shift = 31 + ceil(log2 d) and mult = ceil(2^shift / d) (at most 2^32):
+// the round-up reciprocal of Granlund and Montgomery's division by
+// invariant integers.
+struct DivMagic {
+    uint64_t mult;
+    int shift;
+};
+
+DivMagic div_magic(uint64_t d)
+{
+    int l = 0;
+    while ((uint64_t{1} << l) < d)
+        ++l;
+    const unsigned __int128 num = static_cast<unsigned __int128>(1) << (31 + l);
+    return DivMagic{static_cast<uint64_t>((num + d - 1) / d), 31 + l};
+}
+
+__device__ __forceinline__ uint32_t div_by(uint32_t x, const DivMagic& m)
+{
+    return static_cast<uint32_t>((static_cast<uint64_t>(x) * m.mult) >> m.shift);
+}
 
 struct AqArgs {
     const void* src;
     const float* scale;
     const float* offset;
     int64_t m, n;
-    int64_t gs;        // group size (PER_GROUP)
-    int64_t n_groups;  // ceil(n / gs) for kDim = 1
+    int64_t row0;       // first row of this launch
+    int64_t rows;       // rows of this launch
+    int64_t gs;         // group size (PER_GROUP)
+    int64_t n_groups;   // ceil(n / gs) for kDim = 1
     void* dst;
-    int64_t strips;         // ceil(n / 1024)
-    int64_t row_step;       // G: waves per strip, the stride between a wave's rows
-    int64_t waves;          // strips * G
-    int64_t nblocks;
+    uint32_t cpr;       // chunks per row (n / E)
+    uint32_t units;     // work units of this launch (threads that do work)
+    DivMagic by_cpr;    // division by cpr
+    DivMagic by_gsc;    // division by gs / E (chunks per group, kDim = 1)
+    DivMagic by_gs;     // division by gs (rows per group, kDim = 0)
 };
 
 template <int DST>
 struct Chunk {
-    static constexpr int E = DST == DST_F32 ? 4 : 8;       // elements per chunk
-    static constexpr int NCH = 1024 / (kWave * E);         // chunks per lane per row
-    static constexpr int W = E / 4;                        // source dwords per chunk
+    static constexpr int E = DST == DST_F32 ? 4 : 8;  // elements per chunk
+    static constexpr int W = E / 4;                   // source dwords per chunk
 };
 
 // Four source bytes -> four floats (exact).
@@ -126,137 +150,95 @@ __device__ __forceinline__ void load_params(const float* p, float* v)
     }
 }
 
-template <int NCH, int W>
-__device__ __forceinline__ void load_row(uint32_t (&raw)[NCH][W], const uint8_t* row, const int64_t (&jc)[NCH],
-                                         const bool (&okc)[NCH])
+template <int W>
+__device__ __forceinline__ void load_chunk(uint32_t (&raw)[W], const uint8_t* p)
 {
+    if (W == 2) {
+        const uint2 w2 = ld_stream8(p);
+        raw[0] = w2.x;
+        raw[W - 1] = w2.y;
+    } else {
+        raw[0] = ld_stream4(p);
+    }
+}
+
+template <int SRC, int DST, bool OFF>
+__device__ __forceinline__ void convert_store(const uint32_t (&raw)[Chunk<DST>::W], const float* sv, const float* ov,
+                                              void* out)
+{
+    constexpr int E = Chunk<DST>::E, W = Chunk<DST>::W;
+    float v[E];
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-        if (okc[c]) {
-            if (W == 2) {
-                const uint2 w2 = ld_stream8(row + jc[c]);
-                raw[c][0] = w2.x;
-                raw[c][W - 1] = w2.y;
-            } else {
-                raw[c][0] = ld_stream4(row + jc[c]);
-            }
+    for (int w = 0; w < W; ++w)
+        decode4<SRC>(raw[w], v + 4 * w);
+    float t[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        if (OFF) {
+            const float u = v[e] + ov[e];
+            t[e] = u * sv[e];
+        } else {
+            t[e] = v[e] * sv[e];
         }
     }
+    store_chunk<DST>(out, t);
 }
 
 template <int SRC, int DST, int PK, bool OFF>
 __global__ __launch_bounds__(kBlock) void aq_kernel(AqArgs a)
 {
     using C = Chunk<DST>;
-    constexpr int E = C::E, NCH = C::NCH, W = C::W;
+    constexpr int E = C::E, W = C::W;
     constexpr bool kPerElem = PK == PK_CHANNEL || PK == PK_GROUP_M;
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
-    const int64_t wid = xcd_block(blockIdx.x, a.nblocks) * 4 + wave;
-    if (wid >= a.waves)
-        return;
-    const int64_t strip = wid % a.strips;
-    const int64_t G = a.row_step;
-    const int64_t r0 = wid / a.strips;
-    const int64_t r1 = a.m;
-    if (r0 >= r1)
-        return;
-    int64_t jc[NCH];
-    bool okc[NCH];
-    int64_t gcol[NCH];  // PER_GROUP kDim = 1: the chunk's group
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-        jc[c] = strip * 1024 + (c * kWave + lane) * E;
-        okc[c] = jc[c] < a.n;  // n is a multiple of 16, so a chunk is whole or absent
-        gcol[c] = PK == PK_GROUP_N ? jc[c] / a.gs : 0;
-    }
+    constexpr int R = kPerElem ? kAqRowsPerThread : 1;
+    const int64_t out_elem = DST == DST_F32 ? 4 : 2;
     const uint8_t* src = static_cast<const uint8_t*>(a.src);
     uint8_t* dst = static_cast<uint8_t*>(a.dst);
-    const int64_t out_elem = DST == DST_F32 ? 4 : 2;
 
-    // Rows r0 .. r0 + kPD - 1 in flight before any arithmetic.
-    uint32_t raw[kPD][NCH][W];
-#pragma unroll
-    for (int k = 0; k < kPD; ++k)
-        if (r0 + k * G < r1)
-            load_row<NCH, W>(raw[k], src + (r0 + k * G) * a.n, jc, okc);
+    // Work unit u = (row block, chunk); a thread past the end repeats the
+    // last unit (same bytes).
+    uint32_t u = blockIdx.x * kBlock + threadIdx.x;
+    u = u < a.units ? u : a.units - 1;
+    const uint32_t rb = div_by(u, a.by_cpr);
+    const uint32_t jc = u - rb * a.cpr;  // chunk within the row
+    const int64_t j = static_cast<int64_t>(jc) * E;
+    const int64_t i0 = a.row0 + static_cast<int64_t>(rb) * R;
 
-    // Parameters fixed over many rows.
-    float sv[NCH][E], ov[NCH][E];
-    float s_u = 0.0f, o_u = 0.0f;
-    int64_t g_lo = 0, g_hi = 0;  // PER_GROUP kDim = 0: rows of the group held in sv / ov
-    auto load_vec_params = [&](int64_t row_base) {
+    float sv[E], ov[E];
+    if (PK == PK_TENSOR || PK == PK_TOKEN || PK == PK_GROUP_N) {
+        int64_t p = 0;
+        if (PK == PK_TOKEN)
+            p = i0;
+        if (PK == PK_GROUP_N)
+            p = i0 * a.n_groups + div_by(jc, a.by_gsc);
+        const float s1 = a.scale[p];
+        const float o1 = OFF ? a.offset[p] : 0.0f;
 #pragma unroll
-        for (int c = 0; c < NCH; ++c) {
-            if (okc[c]) {
-                load_params<E>(a.scale + row_base + jc[c], sv[c]);
-                if (OFF)
-                    load_params<E>(a.offset + row_base + jc[c], ov[c]);
-            }
+        for (int e = 0; e < E; ++e) {
+            sv[e] = s1;
+            ov[e] = o1;
         }
-    };
-    if (PK == PK_TENSOR) {
-        s_u = a.scale[0];
+    } else {
+        // The R rows share the group: R divides groupSize and the row
+        // blocks start at multiples of R.
+        const int64_t base = PK == PK_GROUP_M ? static_cast<int64_t>(div_by(static_cast<uint32_t>(i0), a.by_gs)) * a.n : 0;
+        load_params<E>(a.scale + base + j, sv);
         if (OFF)
-            o_u = a.offset[0];
-    } else if (PK == PK_CHANNEL) {
-        load_vec_params(0);
-    } else if (PK == PK_GROUP_M) {
-        const int64_t g = r0 / a.gs;
-        load_vec_params(g * a.n);
-        g_lo = g * a.gs;
-        g_hi = g_lo + a.gs;
+            load_params<E>(a.offset + base + j, ov);
     }
 
-    for (int64_t r = r0; r < r1; r += kPD * G) {
+    uint32_t raw[R][W];
 #pragma unroll
-        for (int k = 0; k < kPD; ++k) {
-            const int64_t i = r + k * G;
-            if (i >= r1)
-                continue;
-            if (PK == PK_GROUP_M && (i < g_lo || i >= g_hi)) {
-                const int64_t g = i / a.gs;
-                load_vec_params(g * a.n);
-                g_lo = g * a.gs;
-                g_hi = g_lo + a.gs;
-            }
-            float s1 = s_u, o1 = o_u;
-            if (PK == PK_TOKEN) {
-                s1 = a.scale[i];
-                if (OFF)
-                    o1 = a.offset[i];
-            }
+    for (int r = 0; r < R; ++r) {
+        int64_t i = i0 + r;
+        i = i < a.row0 + a.rows ? i : a.row0 + a.rows - 1;  // past the end: repeat the last row
+        load_chunk<W>(raw[r], src + i * a.n + j);
+    }
 #pragma unroll
-            for (int c = 0; c < NCH; ++c) {
-                if (!okc[c])
-                    continue;
-                if (PK == PK_GROUP_N) {
-                    const int64_t p = i * a.n_groups + gcol[c];
-                    s1 = a.scale[p];
-                    if (OFF)
-                        o1 = a.offset[p];
-                }
-                float v[E];
-#pragma unroll
-                for (int w = 0; w < W; ++w)
-                    decode4<SRC>(raw[k][c][w], v + 4 * w);
-                float t[E];
-#pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    const float s = kPerElem ? sv[c][e] : s1;
-                    if (OFF) {
-                        const float o = kPerElem ? ov[c][e] : o1;
-                        const float u = v[e] + o;
-                        t[e] = u * s;
-                    } else {
-                        t[e] = v[e] * s;
-                    }
-                }
-                store_chunk<DST>(dst + (i * a.n + jc[c]) * out_elem, t);
-            }
-            if (i + kPD * G < r1)
-                load_row<NCH, W>(raw[k], src + (i + kPD * G) * a.n, jc, okc);
-        }
+    for (int r = 0; r < R; ++r) {
+        int64_t i = i0 + r;
+        i = i < a.row0 + a.rows ? i : a.row0 + a.rows - 1;
+        convert_store<SRC, DST, OFF>(raw[r], sv, ov, dst + (i * a.n + j) * out_elem);
     }
 }
 
@@ -303,6 +285,8 @@ hipError_t launch_antiquantize(const AqPlan& p, hipStream_t stream)
                                        : pick_dst<SRC_F8E4M3>(p.dst_kind, pk, p.offset != nullptr);
     if (!fn)
         return hipErrorInvalidValue;
+    const int64_t E = p.dst_kind == DST_F32 ? 4 : 8;
+    const int64_t R = (pk == PK_CHANNEL || pk == PK_GROUP_M) ? kAqRowsPerThread : 1;
     AqArgs a{};
     a.src = p.src;
     a.scale = p.scale;
@@ -312,16 +296,30 @@ hipError_t launch_antiquantize(const AqPlan& p, hipStream_t stream)
     a.gs = p.group_size > 0 ? p.group_size : 1;
     a.n_groups = (p.n + a.gs - 1) / a.gs;
     a.dst = p.dst;
-    a.strips = (p.n + 1023) / 1024;
-    int64_t G = (kTargetWaves + a.strips - 1) / a.strips;  // waves per strip
-    if (G > p.m)
-        G = p.m;
-    a.row_step = G;
-    a.waves = a.strips * G;
-    a.nblocks = (a.waves + 3) / 4;
-    void* args[] = {&a};
-    return hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3(static_cast<uint32_t>(a.nblocks)),
-                           dim3(kBlock), args, 0, stream);
+    const int64_t cpr = p.n / E;  // n is a multiple of E (32-byte rows)
+    if (cpr < 1 || cpr >= (int64_t{1} << 31))
+        return hipErrorInvalidValue;
+    a.cpr = static_cast<uint32_t>(cpr);
+    a.by_cpr = div_magic(static_cast<uint64_t>(cpr));
+    a.by_gsc = div_magic(static_cast<uint64_t>(a.gs >= E ? a.gs / E : 1));
+    a.by_gs = div_magic(static_cast<uint64_t>(a.gs));
+    // Row ranges of at most 2^31 - 1 work units, a multiple of R rows each
+    // (so the PER_GROUP kDim = 0 row blocks stay aligned to R).
+    const int64_t max_blocks_rows = ((int64_t{1} << 31) - 1) / cpr;  // row blocks per launch
+    const int64_t max_rows = (max_blocks_rows > (int64_t{1} << 24) ? (int64_t{1} << 24) : max_blocks_rows) * R;
+    for (int64_t row0 = 0; row0 < p.m; row0 += max_rows) {
+        a.row0 = row0;
+        a.rows = p.m - row0 < max_rows ? p.m - row0 : max_rows;
+        const int64_t units = (a.rows + R - 1) / R * cpr;
+        a.units = static_cast<uint32_t>(units);
+        const int64_t blocks = (units + kBlock - 1) / kBlock;
+        void* args[] = {&a};
+        const hipError_t err = hipLaunchKernel(reinterpret_cast<const void*>(fn),
+                                               dim3(static_cast<uint32_t>(blocks)), dim3(kBlock), args, 0, stream);
+        if (err != hipSuccess)
+            return err;
+    }
+    return hipSuccess;
 }
 
 }  // namespace dq

@@ -40,8 +40,8 @@ struct DqPlan {
     int team;  // waves per row (vector variant): 1, 2 or 4
 };
 
-// Largest grid (workgroups along x) a launch may use; the DynamicQuant
-// kernels launch one workgroup per row (generic) or per 4/TEAM rows.
+// Largest grid (workgroups along x) a launch may use, and the largest row
+// count any operation accepts (row indices stay below 2^31 in the kernels).
 constexpr int64_t kMaxGridBlocks = 0x7FFFFFFF;
 
 // ---- AdaLayerNorm-quant ----------------------------------------------------
@@ -78,7 +78,6 @@ struct AqPlan {
     int src_kind;
     int dst_kind;
     void* dst;
-    int rows_per_tile;
 };
 
 // Kernel launchers (defined in the .hip files).  They enqueue on `stream`

@@ -365,6 +365,8 @@ dq_status dq_ada_layernorm_quant_get_workspace_size(const dq_tensor* x, const dq
     if (x->ndim != 3)
         return fail(DQ_ERR_SHAPE, "x must be [B, S, H]");
     const int64_t B = x->dims[0], S = x->dims[1], H = x->dims[2];
+    if (S > 0 && B > dq::kMaxGridBlocks / S)
+        return fail(DQ_ERR_SHAPE, "at most %lld rows (B * S) are supported", (long long)dq::kMaxGridBlocks);
     if (H < 1)
         return fail(DQ_ERR_SHAPE, "H must be >= 1");
     if (!(is_shape(scale, {B, 1, H}) || is_shape(scale, {B, H})))
@@ -471,6 +473,9 @@ dq_status dq_antiquantize_get_workspace_size(const dq_tensor* src, const dq_tens
     if (src->ndim != 2)
         return fail(DQ_ERR_SHAPE, "src must be 2-D [m, n] (got %d dims)", src->ndim);
     const int64_t m = src->dims[0], n = src->dims[1];
+    if (m > dq::kMaxGridBlocks)
+        return fail(DQ_ERR_SHAPE, "at most %lld rows are supported, got %lld", (long long)dq::kMaxGridBlocks,
+                    (long long)m);
     if (!same_dims(dst, src->dims, 2))
         return fail(DQ_ERR_SHAPE, "dst must have the shape of src");
     if (policy < DQ_PER_TENSOR || policy > DQ_PER_GROUP)
@@ -540,7 +545,6 @@ dq_status dq_antiquantize_get_workspace_size(const dq_tensor* src, const dq_tens
     p.src_kind = src->dtype == DQ_I8 ? dq::SRC_I8 : dq::SRC_F8E4M3;
     p.dst_kind = dst->dtype == DQ_BF16 ? dq::DST_BF16 : dst->dtype == DQ_F16 ? dq::DST_F16 : dq::DST_F32;
     p.dst = dst->data;
-    p.rows_per_tile = 16;
     *executor = e;
     return ok();
 }

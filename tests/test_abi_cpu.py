@@ -107,6 +107,9 @@ def good_dq():
     ({"x": desc(D.BF16, [0, N]), "y": desc(D.I8, [0, N]), "sc": desc(D.F32, [0])}, D.SUCCESS),
     ({"x": desc(D.F16, [2, 3, N]), "y": desc(D.I8, [2, 3, N]), "sc": desc(D.F32, [2, 3])}, D.SUCCESS),
     ({"x": desc(D.F16, [2, 3, N]), "y": desc(D.I8, [2, 3, N]), "sc": desc(D.F32, [6])}, D.ERR_SHAPE),
+    ({"x": desc(D.BF16, [2**31, 8]), "y": desc(D.I8, [2**31, 8]), "sc": desc(D.F32, [2**31])}, D.ERR_SHAPE),
+    ({"x": desc(D.BF16, [2**31 - 1, 8]), "y": desc(D.I8, [2**31 - 1, 8]), "sc": desc(D.F32, [2**31 - 1])},
+     D.SUCCESS),
 ])
 def test_dynamic_quant_validation(lib, change, status):
     a = good_dq()
@@ -163,6 +166,8 @@ def ada_ws(lib, a):
     ({"eps": -1.0}, D.ERR_PARAM),
     ({"eps": float("inf")}, D.ERR_PARAM),
     ({"eps": float("nan")}, D.ERR_PARAM),
+    ({"x": desc(D.BF16, [2**16, 2**15, H]), "sc": desc(D.BF16, [2**16, 1, H]), "sh": desc(D.BF16, [2**16, 1, H]),
+      "out": desc(D.I8, [2**16, 2**15, H]), "qs": desc(D.F32, [2**16, 2**15])}, D.ERR_SHAPE),   # B*S = 2^31
 ])
 def test_ada_validation(lib, change, status):
     a = good_ada()
@@ -232,6 +237,7 @@ def test_antiquantize_policy_shapes(lib, pol, kdim, gs, sshape, status):
     (desc(D.I8, [M, NN], SRC_PTR), desc(D.BF16, [M, NN], SRC_PTR + 64), None, D.ERR_OVERLAP),
     (desc(D.I8, [M, NN], SRC_PTR), desc(D.BF16, [M, NN], SRC_PTR - 2 * M * NN + 16), None, D.ERR_OVERLAP),
     (desc(D.I8, [0, NN], SRC_PTR), desc(D.BF16, [0, NN], DST_PTR), None, D.SUCCESS),
+    (desc(D.I8, [2**31, 32], SRC_PTR), desc(D.BF16, [2**31, 32], DST_PTR), None, D.ERR_SHAPE),  # rows
 ])
 def test_antiquantize_types_alignment_overlap(lib, src, dst, off, status):
     sc = desc(D.F32, [1], 0x20000)
