@@ -87,9 +87,15 @@ hipError_t launch_ada_layernorm_quant(const AdaPlan& p, hipStream_t stream);
 hipError_t launch_antiquantize(const AqPlan& p, hipStream_t stream);
 hipError_t launch_copy_probe(void* dst, const void* src, size_t bytes, hipStream_t stream);
 
-// Largest row (in elements) the register-resident DynamicQuant variant
-// holds: 16 vectors of 8 elements per lane, 64 lanes, TEAM waves.
+// DynamicQuant vector variant: waves per workgroup (the largest team), the
+// most 16-byte vectors per lane a team takes before the next team size is
+// used, rows a team has in flight ahead of the one it converts, and the
+// largest row (in elements) it holds: 16 vectors of 8 elements per lane,
+// 64 lanes, kDqWaves waves.
+constexpr int kDqWaves = 4;
+constexpr int kDqTeamVpl = 4;
+constexpr int kDqPrefetch = 1;
 constexpr int64_t kDqVecMaxPerWave = 16 * 8 * 64;
-constexpr int64_t kDqVecMaxTeam4 = 4 * kDqVecMaxPerWave;
+constexpr int64_t kDqVecMaxRow = kDqWaves * kDqVecMaxPerWave;
 
 }  // namespace dq

@@ -275,9 +275,8 @@ dq_status dq_dynamic_quant_get_workspace_size(const dq_tensor* x, const dq_tenso
     p.variant = dq::DQ_VAR_GENERIC;
     if (vec_ok) {
         const int64_t nvec = n / 8;
-        static const int kTeams[] = {1, 2, 4};
-        for (int t : kTeams) {
-            if (nvec <= 4 * 64 * t) {
+        for (int t = 1; t <= dq::kDqWaves; t *= 2) {
+            if (nvec <= dq::kDqTeamVpl * 64 * t) {
                 static const int kVpl[] = {1, 2, 4};
                 p.vpl = pick_vpl((nvec + 64 * t - 1) / (64 * t), kVpl, 3);
                 p.team = t;
@@ -285,10 +284,10 @@ dq_status dq_dynamic_quant_get_workspace_size(const dq_tensor* x, const dq_tenso
                 break;
             }
         }
-        if (p.variant != dq::DQ_VAR_VECTOR && n <= dq::kDqVecMaxTeam4) {
+        if (p.variant != dq::DQ_VAR_VECTOR && n <= dq::kDqVecMaxRow) {
             static const int kVplWide[] = {8, 16};
-            p.vpl = pick_vpl((nvec + 255) / 256, kVplWide, 2);
-            p.team = 4;
+            p.vpl = pick_vpl((nvec + 64 * dq::kDqWaves - 1) / (64 * dq::kDqWaves), kVplWide, 2);
+            p.team = dq::kDqWaves;
             p.variant = dq::DQ_VAR_VECTOR;
         }
     }

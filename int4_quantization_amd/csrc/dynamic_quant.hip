@@ -240,7 +240,7 @@ __device__ __forceinline__ void load_smooth(float (&sreg)[VPL][8], const DqArgs&
 template <int XT, bool SYM, int OUT, int VPL, int TEAM>
 __device__ __forceinline__ void convert_row(const DqArgs& a, const uint4 (&raw)[VPL], const float (&sreg)[VPL][8],
                                             int64_t row, int t, int64_t nvec, int slot, int wit, int lane,
-                                            float (&red)[2][2][4])
+                                            float (&red)[2][2][kDqWaves])
 {
     float s_hi = SYM ? 0.0f : -__builtin_huge_valf();
     float s_lo = __builtin_huge_valf();
@@ -324,19 +324,21 @@ __device__ __forceinline__ void convert_row(const DqArgs& a, const uint4 (&raw)[
     }
 }
 
-// Rows each team converts in one workgroup: the second row's loads are in
-// flight while the first is reduced and stored, and the smooth scales are
-// loaded once for both.
-constexpr int dq_rows_per_team(int vpl)
+// Rows each team converts in one workgroup, one after another, with the
+// next kDqPrefetch rows' loads in flight while a row is reduced and stored;
+// the smooth scales are loaded once for all of them.
+constexpr int dq_rows_per_team(int vpl, int team)
 {
-    return vpl <= 4 ? 2 : 1;
+    return vpl > 4 ? 1 : team >= 4 ? 4 : 2;
 }
 
 template <int XT, bool SYM, int OUT, int VPL, int TEAM>
-__global__ __launch_bounds__(kBlock) void dq_vec_kernel(DqArgs a)
+__global__ __launch_bounds__(kDqWaves * kWave) void dq_vec_kernel(DqArgs a)
 {
-    constexpr int RPS = 4 / TEAM;  // teams per workgroup
-    constexpr int T = dq_rows_per_team(VPL);
+    constexpr int RPS = kDqWaves / TEAM;  // teams per workgroup
+    constexpr int T = dq_rows_per_team(VPL, TEAM);
+    constexpr int PD = kDqPrefetch < T ? kDqPrefetch : (T > 1 ? T - 1 : 1);
+    constexpr int NB = PD + 1;  // row buffers
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     const int slot = wave / TEAM;
@@ -349,7 +351,7 @@ __global__ __launch_bounds__(kBlock) void dq_vec_kernel(DqArgs a)
         const int64_t r = r0 + static_cast<int64_t>(t) * RPS + slot;
         return r < a.rows ? r : a.rows - 1;
     };
-    __shared__ float red[2][2][4];
+    __shared__ float red[2][2][kDqWaves];
 
     // Every load is unconditional or under a workgroup-uniform branch (a
     // load under a divergent branch makes the compiler wait for everything
@@ -360,7 +362,7 @@ __global__ __launch_bounds__(kBlock) void dq_vec_kernel(DqArgs a)
     if (moe)
         gi_lane = a.gi[lane < a.n_experts ? lane : a.n_experts - 1];
 
-    uint4 buf[2][VPL];
+    uint4 buf[NB][VPL];
     load_x<VPL, TEAM>(buf[0], a.x, row_of(0), a.n, nvec, wit, lane);
 
     float sreg[VPL][8];
@@ -374,11 +376,14 @@ __global__ __launch_bounds__(kBlock) void dq_vec_kernel(DqArgs a)
     if (one_expert) {
         load_smooth<VPL, TEAM>(sreg, a, e0, nvec, wit, lane);
 #pragma unroll
+        for (int t = 1; t < PD && t < T; ++t)
+            load_x<VPL, TEAM>(buf[t % NB], a.x, row_of(t), a.n, nvec, wit, lane);
+#pragma unroll
         for (int t = 0; t < T; ++t) {
-            if (t + 1 < T)
-                load_x<VPL, TEAM>(buf[(t + 1) & 1], a.x, row_of(t + 1), a.n, nvec, wit, lane);
+            if (t + PD < T)
+                load_x<VPL, TEAM>(buf[(t + PD) % NB], a.x, row_of(t + PD), a.n, nvec, wit, lane);
             __builtin_amdgcn_sched_barrier(0);
-            convert_row<XT, SYM, OUT, VPL, TEAM>(a, buf[t & 1], sreg, row_of(t), t, nvec, slot, wit, lane, red);
+            convert_row<XT, SYM, OUT, VPL, TEAM>(a, buf[t % NB], sreg, row_of(t), t, nvec, slot, wit, lane, red);
         }
     } else {
         // The rows straddle an expert boundary (rare): one row at a time,
@@ -477,7 +482,7 @@ KernelFn pick_vpl(int vpl)
     case 2: return dq_vec_kernel<XT, SYM, OUT, 2, TEAM>;
     case 4: return dq_vec_kernel<XT, SYM, OUT, 4, TEAM>;
     }
-    if constexpr (TEAM == 4) {  // only the widest rows take more vectors per lane
+    if constexpr (TEAM == kDqWaves) {  // only the widest rows take more vectors per lane
         if (vpl == 8)
             return dq_vec_kernel<XT, SYM, OUT, 8, TEAM>;
         if (vpl == 16)
@@ -495,6 +500,10 @@ KernelFn pick(const DqPlan& p)
     case 1: return pick_vpl<XT, SYM, OUT, 1>(p.vpl);
     case 2: return pick_vpl<XT, SYM, OUT, 2>(p.vpl);
     case 4: return pick_vpl<XT, SYM, OUT, 4>(p.vpl);
+    }
+    if constexpr (kDqWaves >= 8) {
+        if (p.team == 8)
+            return pick_vpl<XT, SYM, OUT, 8>(p.vpl);
     }
     return nullptr;
 }
@@ -516,12 +525,13 @@ hipError_t launch_dynamic_quant(const DqPlan& p, hipStream_t stream)
         return hipErrorInvalidValue;
     DqArgs a{p.x, p.smooth, p.group_index, p.n_experts, p.rows, p.n, p.y, p.scale, p.offset};
     // Vector variant: one workgroup per T * 4/TEAM rows; generic: one per row.
-    const int64_t rpb = p.variant == DQ_VAR_VECTOR ? dq_rows_per_team(p.vpl) * (4 / p.team) : 1;
+    const int64_t rpb = p.variant == DQ_VAR_VECTOR ? dq_rows_per_team(p.vpl, p.team) * (kDqWaves / p.team) : 1;
     const int64_t blocks = (p.rows + rpb - 1) / rpb;
     if (blocks > kMaxGridBlocks)
         return hipErrorInvalidValue;
     void* args[] = {&a};
-    return hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3(static_cast<uint32_t>(blocks)), dim3(kBlock),
+    const int threads = p.variant == DQ_VAR_VECTOR ? kDqWaves * kWave : kBlock;
+    return hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3(static_cast<uint32_t>(blocks)), dim3(threads),
                            args, 0, stream);
 }
 
