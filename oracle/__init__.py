@@ -30,6 +30,10 @@ LIBRARY = os.path.join(HERE, "liboracle.so")
 
 # The oracle's own type codes (see the enum in dquant_oracle.c).
 F32, F16, BF16, I8, I4, I32, F8E4M3 = 0, 1, 2, 3, 4, 5, 6
+F8E5M2, F4E2M1, E8M0 = 8, 9, 10
+# Raw byte codes passed as (name, uint8 ndarray) pairs.
+_BYTE_CODES = {"float8_e4m3fn": F8E4M3, "float8_e5m2": F8E5M2, "float4_e2m1x2": F4E2M1,
+               "float8_e8m0": E8M0}
 _OUT_CODES = {"int8": I8, "int4": I4, "int32": I32}
 _FLOAT_CODES = {"float32": F32, "float16": F16, "bfloat16": BF16}
 POLICIES = {"per_tensor": 0, "per_channel": 1, "per_token": 2, "per_group": 3}
@@ -85,6 +89,8 @@ def _buffer(t) -> Tuple[Optional[np.ndarray], int]:
     """
     if t is None:
         return None, F32
+    if isinstance(t, tuple):
+        return np.ascontiguousarray(t[1], dtype=np.uint8), _BYTE_CODES[t[0]]
     try:
         import torch
     except ImportError:  # pragma: no cover - torch is always present here
@@ -97,6 +103,8 @@ def _buffer(t) -> Tuple[Optional[np.ndarray], int]:
             return t.view(torch.int16).numpy().view(np.uint16), F16
         if t.dtype == torch.float8_e4m3fn:
             return t.view(torch.uint8).numpy(), F8E4M3
+        if t.dtype == torch.float8_e5m2:
+            return t.view(torch.uint8).numpy(), F8E5M2
         t = t.numpy()
     a = np.ascontiguousarray(t)
     if a.dtype == np.float32:
@@ -132,10 +140,18 @@ class Oracle:
         return out.reshape(a.shape)
 
     def e4m3_to_f32(self, codes: np.ndarray) -> np.ndarray:
+        return self.bytes_to_f32(codes, "float8_e4m3fn")
+
+    def bytes_to_f32(self, codes: np.ndarray, kind: str) -> np.ndarray:
+        """Decode byte codes of kind 'float8_e4m3fn', 'float8_e5m2',
+        'float8_e8m0' (one value per byte) or 'float4_e2m1x2' (two values per
+        byte, low nibble first: the result has twice the bytes' count)."""
         a = np.ascontiguousarray(codes, dtype=np.uint8)
-        out = np.empty(a.size, dtype=np.float32)
-        self.lib.orc_convert_to_f32(_ptr(a), F8E4M3, a.size, _ptr(out))
-        return out.reshape(a.shape)
+        code = _BYTE_CODES[kind]
+        count = a.size * (2 if code == F4E2M1 else 1)
+        out = np.empty(count, dtype=np.float32)
+        self.lib.orc_convert_to_f32(_ptr(a), code, count, _ptr(out))
+        return out
 
     # -- aclnnDynamicQuantV2 --------------------------------------------------
     def dynamic_quant(self, x, smooth=None, group_index=None, symmetric=True, out="int8"):
@@ -206,16 +222,18 @@ class Oracle:
                      group_size=0, dst="bfloat16") -> np.ndarray:
         """Return dst [m, n]: raw uint16 bits for bf16/fp16, float32 for 'float32'.
 
-        src: int8 [m, n] numpy/torch, or torch float8_e4m3fn, or
-        ('float8_e4m3fn', uint8 codes ndarray).
+        src: int8 [m, n] numpy/torch, torch float8_e4m3fn / float8_e5m2, or a
+        (kind, uint8 codes) pair with kind 'float8_e4m3fn', 'float8_e5m2' or
+        'float4_e2m1x2' (codes [m, n/2], two per byte, low nibble first).
+        scale / offset: float32, float16 or bfloat16 arrays, or
+        ('float8_e8m0', uint8 codes) for the float4 case.
         """
-        if isinstance(src, tuple):
-            sa, scode = np.ascontiguousarray(src[1], dtype=np.uint8), F8E4M3
-        else:
-            sa, scode = _buffer(src)
+        sa, scode = _buffer(src)
         if sa.ndim != 2:
             raise ValueError("oracle: AntiQuantize src must be 2-D")
         m, n = (int(d) for d in sa.shape)
+        if scode == F4E2M1:
+            n *= 2
         sc, scc = _buffer(scale)
         of, ofc = _buffer(offset)
         dcode = {"bfloat16": BF16, "float16": F16, "float32": F32}[dst]

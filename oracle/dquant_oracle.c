@@ -5,8 +5,8 @@
  * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may call, link or
  * load this file: it is used by tests/, by the smoke check and by the CPU
  * baseline leg of bench.py.  It shares no code, header, table or constant
- * with the HIP library; its element conversions (bf16, fp16, fp8-e4m3fn)
- * are written here from the format definitions.
+ * with the HIP library; its element conversions (bf16, fp16, fp8-e4m3fn,
+ * fp8-e5m2, fp4-e2m1, e8m0) are written here from the format definitions.
  *
  * Arithmetic rules (built with -O2 -ffp-contract=off -fno-fast-math, SSE
  * scalar float on x86-64, so FLT_EVAL_METHOD == 0):
@@ -45,7 +45,10 @@ enum {
     ORC_I4 = 4,
     ORC_I32 = 5,
     ORC_F8E4M3 = 6,
-    ORC_F64 = 7
+    ORC_F64 = 7,
+    ORC_F8E5M2 = 8,
+    ORC_F4E2M1 = 9, /* two codes per byte, element 2k in the low nibble */
+    ORC_E8M0 = 10
 };
 
 /* ------------------------------------------------------------------------ */
@@ -108,6 +111,48 @@ float orc_e4m3fn_to_f32(uint8_t b)
     return (float)(sign ? -v : v);
 }
 
+/* OCP fp8 E5M2: 1 sign, 5 exponent (bias 15), 2 fraction bits, IEEE-style
+ * infinities (exponent 31, fraction 0) and NaNs (exponent 31, fraction
+ * nonzero); largest finite 57344. */
+float orc_e5m2_to_f32(uint8_t b)
+{
+    int sign = (b >> 7) & 1;
+    int e = (b >> 2) & 0x1F;
+    int f = b & 3;
+    double v;
+    if (e == 31)
+        return f ? nanf("") : (sign ? -INFINITY : INFINITY);
+    if (e == 0)
+        v = ldexp((double)f, -16); /* (f/4) * 2^-14 */
+    else
+        v = ldexp((double)(4 + f), e - 17); /* (1 + f/4) * 2^(e-15) */
+    return (float)(sign ? -v : v);
+}
+
+/* OCP MX fp4 E2M1: 1 sign, 2 exponent (bias 1), 1 fraction bit, no
+ * infinities or NaNs; magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6. */
+float orc_e2m1_to_f32(uint8_t nibble)
+{
+    int sign = (nibble >> 3) & 1;
+    int e = (nibble >> 1) & 3;
+    int f = nibble & 1;
+    double v;
+    if (e == 0)
+        v = 0.5 * f; /* subnormal: (f/2) * 2^(1-1) */
+    else
+        v = ldexp((double)(2 + f), e - 2); /* (1 + f/2) * 2^(e-1) */
+    return (float)(sign ? -v : v);
+}
+
+/* OCP MX E8M0 scale: an unsigned biased exponent, value 2^(b - 127); 0xFF
+ * is NaN. */
+float orc_e8m0_to_f32(uint8_t b)
+{
+    if (b == 0xFF)
+        return nanf("");
+    return (float)ldexp(1.0, (int)b - 127);
+}
+
 /* Round a binary32 to bfloat16, nearest-even.  Works on the bit pattern:
  * the kept upper 16 bits are incremented when the dropped lower 16 bits are
  * above half, or exactly half and the kept part is odd. */
@@ -166,6 +211,14 @@ static float load_as_f32(const void* p, int dtype, int64_t i)
         return (float)((const int8_t*)p)[i];
     case ORC_F8E4M3:
         return orc_e4m3fn_to_f32(((const uint8_t*)p)[i]);
+    case ORC_F8E5M2:
+        return orc_e5m2_to_f32(((const uint8_t*)p)[i]);
+    case ORC_F4E2M1: {
+        uint8_t byte = ((const uint8_t*)p)[i / 2];
+        return orc_e2m1_to_f32((uint8_t)((i & 1) ? byte >> 4 : byte & 0xF));
+    }
+    case ORC_E8M0:
+        return orc_e8m0_to_f32(((const uint8_t*)p)[i]);
     default:
         return nanf("");
     }
@@ -444,8 +497,17 @@ enum { ORC_PER_TENSOR = 0, ORC_PER_CHANNEL = 1, ORC_PER_TOKEN = 2, ORC_PER_GROUP
  * dst = RN(v * s).  The binary32 result is rounded once to dst's type
  * (bf16 or fp16, nearest-even; F32 keeps it).
  *
- * src_dtype ORC_I8 or ORC_F8E4M3; scale/offset F32, F16 or BF16 (widened
- * exactly); offset may be NULL.
+ * src_dtype ORC_I8, ORC_F8E4M3 or ORC_F8E5M2 (the b8 cases of 表3);
+ * scale/offset F32, F16 or BF16 (widened exactly); offset may be NULL.
+ *
+ * The float4 case of 表3 (PER_GROUP, fp4x2 source, fp8_e8m0 scale, no
+ * offset -- 约束说明): src_dtype ORC_F4E2M1 (two codes per byte, element
+ * 2k in the low nibble; n even), scale_dtype ORC_E8M0, offset NULL.  Its
+ * formula is missing from the page too; reading: the e8m0 scale is the
+ * power of two 2^(e - 127) that multiplies the decoded element, so
+ * dst = RN(decode(src) * 2^(e - 127)) -- exact in binary32 except where it
+ * overflows to infinity -- then rounded once to dst's type.  The same code
+ * path computes it: v and s are the decoded values, t = RN(v * s).
  */
 void oracle_antiquantize(const void* src, int src_dtype, int64_t m, int64_t n,
                          const void* scale, int scale_dtype,

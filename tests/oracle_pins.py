@@ -470,6 +470,83 @@ def pin_aq_fp8_source(orc):
     assert np.array_equal(d[~nan], ref[~nan])
 
 
+def pin_aq_e5m2_source(orc):
+    """An fp8-e5m2 source is decoded exactly: e5m2 is the upper byte of a
+    binary16, so with scale 1 and offset 0 the fp32 result equals numpy's
+    float16 of bits (code << 8) for all 256 codes (infinities included, NaN
+    codes stay NaN); the fp16 destination then holds exactly those bits."""
+    codes = np.arange(256, dtype=np.uint8).reshape(8, 32)
+    ref = (codes.astype(np.uint16) << 8).view(np.float16).astype(np.float32)
+    nan = np.isnan(ref)
+    d = orc.antiquantize(("float8_e5m2", codes), np.ones(1, f32), np.zeros(1, f32),
+                         "per_tensor", dst="float32")
+    assert np.array_equal(np.isnan(d), nan)
+    assert np.array_equal(d[~nan], ref[~nan])
+    h = orc.antiquantize(("float8_e5m2", codes), np.ones(1, f32), None, "per_tensor", dst="float16")
+    assert np.array_equal(h[~nan], (codes.astype(np.uint16) << 8)[~nan])
+
+
+# The OCP Microscaling (MX) v1.0 table of FP4 E2M1 values, codes 0..15.
+OCP_E2M1 = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0,
+            -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0]
+
+
+def pin_aq_float4_per_group_worked(orc):
+    """The float4 case of 表3 (PER_GROUP, fp4x2 e2m1 source, e8m0 scale, no
+    offset), worked by hand.  Row 0: group 0 has e8m0 127 (x1), group 1 has
+    130 (x8); row 1: 126 (x0.5) and 255 (NaN).  Codes, two per byte with the
+    first element in the low nibble: row 0 starts 0x71 -> [0.5, 6], its
+    second group 0xB3 -> [1.5, -1.5] x 8 = [12, -12]; row 1 starts 0x6E ->
+    [-4, 4] x 0.5 = [-2, 2]; its second group is NaN.  kDim = 0 with groups
+    of 32 rows: rows 0..31 take scale row 0."""
+    m, n, gs = 2, 64, 32
+    src = np.zeros((m, n // 2), np.uint8)
+    src[0, 0], src[0, 16], src[1, 0], src[1, 16] = 0x71, 0xB3, 0x6E, 0x22
+    sc = np.array([[127, 130], [126, 255]], np.uint8)
+    d = orc.antiquantize(("float4_e2m1x2", src), ("float8_e8m0", sc), None, "per_group", kdim=1,
+                         group_size=gs, dst="float32")
+    assert d.shape == (m, n)
+    assert d[0, :2].tolist() == [0.5, 6.0] and d[0, 32:34].tolist() == [12.0, -12.0]
+    assert d[1, :2].tolist() == [-2.0, 2.0] and np.all(np.isnan(d[1, 32:]))
+    assert np.all(d[0, 2:32] == 0) and np.all(d[0, 34:] == 0) and np.all(d[1, 2:32] == 0)
+    sc0 = np.full((1, n), 127, np.uint8)
+    sc0[0, 33] = 131  # x16 on column 33 for both rows
+    d0 = orc.antiquantize(("float4_e2m1x2", src), ("float8_e8m0", sc0), None, "per_group", kdim=0,
+                          group_size=gs, dst="float32")
+    assert d0[0, :2].tolist() == [0.5, 6.0] and d0[0, 32:34].tolist() == [1.5, -24.0]
+    assert d0[1, :2].tolist() == [-4.0, 4.0] and d0[1, 32:34].tolist() == [1.0, 16.0]
+
+
+def pin_aq_float4_table_and_scaling(orc):
+    """With e8m0 127 (x1) every code decodes to the OCP E2M1 table, for both
+    nibble positions, and the bf16 / fp16 destinations hold those values
+    exactly; e8m0 k multiplies by 2^(k - 127) exactly down to 2^-127 (a
+    binary32 subnormal), and products of 2^128 or more overflow to infinity
+    (2 x 2^127 does, 1.5 x 2^127 does not)."""
+    codes = np.arange(256, dtype=np.uint8).reshape(8, 32)
+    lo, hi = codes & 0xF, codes >> 4
+    want = np.empty((8, 64), np.float64)
+    want[:, 0::2] = np.array(OCP_E2M1)[lo]
+    want[:, 1::2] = np.array(OCP_E2M1)[hi]
+    one = ("float8_e8m0", np.full((8, 2), 127, np.uint8))
+    d = orc.antiquantize(("float4_e2m1x2", codes), one, None, "per_group", kdim=1, group_size=32,
+                         dst="float32")
+    assert np.array_equal(d.astype(np.float64), want)
+    assert np.array_equal(np.signbit(d), np.signbit(want))
+    for dst, cast in (("bfloat16", _bits_to_bf16_f32), ("float16", _bits_to_f16_f32)):
+        b = orc.antiquantize(("float4_e2m1x2", codes), one, None, "per_group", kdim=1,
+                             group_size=32, dst=dst)
+        assert np.array_equal(cast(b).astype(np.float64), want)
+    for k in (0, 1, 100, 127, 200, 253, 254):
+        sc = ("float8_e8m0", np.full((8, 2), k, np.uint8))
+        d = orc.antiquantize(("float4_e2m1x2", codes), sc, None, "per_group", kdim=1, group_size=32,
+                             dst="float32")
+        with np.errstate(over="ignore"):
+            exact = (want * 2.0 ** (k - 127)).astype(np.float32)  # exact product, one rounding
+        assert np.array_equal(d, exact)
+    assert np.isinf(exact[np.abs(want) >= 2.0]).all() and np.isfinite(exact[np.abs(want) < 2.0]).all()
+
+
 def pin_roundtrip_dq_asym_aq_token(orc):
     """Round trip: AntiQuantize PER_TOKEN of DynamicQuant's asymmetric INT8
     output, with scale = scaleOut and offset = -offsetOut, reproduces x to
@@ -504,7 +581,9 @@ def pin_conversions_against_libraries(orc):
     """bf16 rounding equals torch's float32 -> bfloat16 cast; fp16 rounding
     equals numpy's float32 -> float16 cast; widening of both equals torch's;
     the e4m3fn decode equals torch's float8_e4m3fn -> float32 for all 256
-    codes (0x7E = 448, 0x01 = 2^-9, 0x08 = 2^-6, 0x7F / 0xFF NaN)."""
+    codes (0x7E = 448, 0x01 = 2^-9, 0x08 = 2^-6, 0x7F / 0xFF NaN); the e5m2
+    decode equals torch's float8_e5m2 and binary16's upper byte; e8m0 is
+    2^(k - 127); e2m1 is the OCP table."""
     rng = np.random.default_rng(51)
     a = _interesting_f32(rng, 20000)
     fin = ~np.isnan(a)
@@ -532,6 +611,23 @@ def pin_conversions_against_libraries(orc):
     assert np.array_equal(np.isnan(e), nan) and np.array_equal(e[~nan], ref[~nan])
     assert e[0x7E] == 448 and e[0x01] == 2.0 ** -9 and e[0x08] == 2.0 ** -6
     assert np.isnan(e[0x7F]) and np.isnan(e[0xFF])
+    # e5m2 equals torch's float8_e5m2 decode and binary16's top byte.
+    e5 = orc.bytes_to_f32(codes, "float8_e5m2")
+    ref = torch.from_numpy(codes.copy()).view(torch.float8_e5m2).float().numpy()
+    ref16 = (codes.astype(np.uint16) << 8).view(np.float16).astype(np.float32)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(e5), nan) and np.array_equal(np.isnan(ref16), nan)
+    assert np.array_equal(e5[~nan], ref[~nan]) and np.array_equal(e5[~nan], ref16[~nan])
+    assert e5[0x7B] == 57344 and e5[0x01] == 2.0 ** -16 and e5[0x7C] == np.inf
+    # e8m0: 2^(k - 127), 0xFF NaN (closed form).
+    e8 = orc.bytes_to_f32(codes, "float8_e8m0")
+    assert np.isnan(e8[255])
+    assert np.array_equal(e8[:255].astype(np.float64), np.ldexp(1.0, np.arange(255) - 127))
+    # e2m1: the OCP table, low nibble first.
+    e2 = orc.bytes_to_f32(np.array([0x10, 0x32, 0x54, 0x76, 0x98, 0xBA, 0xDC, 0xFE], np.uint8),
+                          "float4_e2m1x2")
+    assert np.array_equal(e2, np.array(OCP_E2M1, np.float32))
+    assert np.array_equal(np.signbit(e2), np.signbit(np.array(OCP_E2M1)))
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

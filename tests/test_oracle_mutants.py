@@ -58,6 +58,13 @@ MUTANTS = [
     ("f16_trunc", "double q = nearbyint(ldexp(a, 10 - E));", "double q = floor(ldexp(a, 10 - E));"),
     ("e4m3_bias8", "v = ldexp((double)(8 + f), e - 10);", "v = ldexp((double)(8 + f), e - 11);"),
     ("e4m3_no_subnormal", "v = ldexp((double)f, -9);", "v = 0.0;"),
+    ("e5m2_bias16", "v = ldexp((double)(4 + f), e - 17);", "v = ldexp((double)(4 + f), e - 18);"),
+    ("e5m2_no_inf", "return f ? nanf(\"\") : (sign ? -INFINITY : INFINITY);", "return nanf(\"\");"),
+    ("e2m1_high_nibble_first", "return orc_e2m1_to_f32((uint8_t)((i & 1) ? byte >> 4 : byte & 0xF));",
+     "return orc_e2m1_to_f32((uint8_t)((i & 1) ? byte & 0xF : byte >> 4));"),
+    ("e2m1_subnormal_one", "v = 0.5 * f;", "v = 1.0 * f;"),
+    ("e2m1_bias2", "v = ldexp((double)(2 + f), e - 2);", "v = ldexp((double)(2 + f), e - 3);"),
+    ("e8m0_bias128", "return (float)ldexp(1.0, (int)b - 127);", "return (float)ldexp(1.0, (int)b - 128);"),
     ("bf16_widen_shift", "return bits_to_f32((uint32_t)h << 16);",
      "return bits_to_f32((uint32_t)h << 15);"),
 ]
