@@ -46,6 +46,24 @@ def nbytes(t) -> int:
     return 0 if t is None else t.numel() * t.element_size()
 
 
+_BYTE_FORMATS = (torch.float4_e2m1fn_x2, torch.float8_e8m0fnu)
+
+
+def to_device(t, dev):
+    """Device copy; 1-byte formats torch cannot copy or clone travel as bytes."""
+    if t is None:
+        return None
+    if t.dtype in _BYTE_FORMATS:
+        return t.view(torch.uint8).to(dev).view(t.dtype)
+    return t.to(dev)
+
+
+def clone(t):
+    if t.dtype in _BYTE_FORMATS:
+        return t.view(torch.uint8).clone().view(t.dtype)
+    return t.clone()
+
+
 # ---------------------------------------------------------------------------
 # Workload preparation: device buffer sets and one launch per step.
 # ---------------------------------------------------------------------------
@@ -79,6 +97,9 @@ class Work:
         else:
             src = host["src"]
             m, n = src.shape
+            if src.dtype == torch.float4_e2m1fn_x2:
+                n *= 2  # two codes per byte
+            self.dst_shape = (m, n)
             self.rows = m
             dbytes = m * n * 2
             self.alg_bytes = nbytes(src) + nbytes(host["scale"]) + nbytes(host["offset"]) + dbytes
@@ -117,12 +138,12 @@ class Work:
                 qs = torch.empty((B, S), dtype=torch.float32, device=dev)
                 self.bufs.append((x, p, out, qs))
         else:
-            src0 = h["src"].to(dev)
-            sc = h["scale"].to(dev)
-            of = None if h["offset"] is None else h["offset"].to(dev)
+            src0 = to_device(h["src"], dev)
+            sc = to_device(h["scale"], dev)
+            of = to_device(h["offset"], dev)
             for i in range(self.sets):
-                src = src0 if i == 0 else src0.clone()
-                dst = torch.empty(src.shape, dtype=torch.bfloat16, device=dev)
+                src = src0 if i == 0 else clone(src0)
+                dst = torch.empty(self.dst_shape, dtype=torch.bfloat16, device=dev)
                 self.bufs.append((src, sc, of, dst))
 
     def prepare(self):

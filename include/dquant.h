@@ -63,14 +63,18 @@ typedef enum dq_dtype {
     DQ_I8 = 3,
     DQ_I4 = 4,     /* two 4-bit codes per byte, the even element in the low nibble */
     DQ_I32 = 5,    /* int32; as a DynamicQuant output: eight 4-bit codes per word  */
-    DQ_F8E4M3 = 6  /* OCP fp8 E4M3FN (no infinities, max 448)                      */
+    DQ_F8E4M3 = 6, /* OCP fp8 E4M3FN (no infinities, max 448)                      */
+    DQ_F8E5M2 = 7, /* OCP fp8 E5M2 (IEEE-style infinities and NaNs, max 57344)      */
+    DQ_F4E2M1 = 8, /* OCP MX fp4 E2M1, two codes per byte, the even element in the
+                    * low nibble (values 0, 0.5, 1, 1.5, 2, 3, 4, 6 and negatives) */
+    DQ_E8M0 = 9    /* OCP MX E8M0 scale: one byte, value 2^(b - 127), 0xFF is NaN  */
 } dq_dtype;
 
 #define DQ_MAX_DIMS 8
 
 /* A dense row-major tensor in device memory.  dims[0..ndim-1] are element
- * counts; for DQ_I4 they count 4-bit codes (the buffer holds half as many
- * bytes along the last dimension). */
+ * counts; for DQ_I4 and DQ_F4E2M1 they count 4-bit codes (the buffer holds
+ * half as many bytes along the last dimension). */
 typedef struct dq_tensor {
     void* data;
     dq_dtype dtype;
@@ -189,19 +193,33 @@ dq_status dq_ada_layernorm_quant(void* workspace, size_t workspace_size, dq_exec
  * offset is this library's reading (it is the value that undoes
  * DynamicQuant's "+ offset" when passed negated).
  *
- *   src        I8 or F8E4M3, exactly 2-D (the page: at most two dims).
- *   scale      F32, policy shape.   offset: NULL or F32, same shape.
+ * The float4 case of 表3 (fp4x2 source, fp8_e8m0 scale, PER_GROUP only,
+ * no offset -- 约束说明) reads its missing formula the same way:
+ *   dst[i, j] = decode(src[i, j]) * 2^(scale[p] - 127)
+ * as one correctly rounded fp32 multiply (exact unless it overflows to
+ * infinity; scale 0xFF is NaN), then rounded once to dst's type.
+ *
+ *   src        I8, F8E4M3 or F8E5M2 (the b8 cases of 表3), or F4E2M1 (the
+ *              float4 case), exactly 2-D [m, n] (the page: at most two
+ *              dims); for F4E2M1 n counts 4-bit codes and must be even.
+ *   scale      b8 sources: F32, F16 or BF16 (widened exactly), policy
+ *              shape.  F4E2M1: E8M0.
+ *   offset     NULL, or the scale's dtype and shape; NULL for F4E2M1.
  *   k_dim      0 or 1, used by DQ_PER_GROUP only.
  *   group_size DQ_PER_GROUP: > 0 and a multiple of 32 (表2); ignored
  *              otherwise.
- *   dst        BF16 or F16 [m, n] (表3), or F32 [m, n] (the unrounded
- *              binary32 result, an extension of this library).
+ *   dst        BF16 or F16 [m, n] (表3), or, for b8 sources, F32 [m, n]
+ *              (the unrounded binary32 result, an extension of this
+ *              library).
  *   n * sizeof(src) and n * sizeof(dst) must be multiples of 32 bytes and
- *   src/dst 16-byte aligned (约束说明: 32-byte aligned rows); src and dst
- *   must not overlap.  m may be 0.  Workspace size: 0.
- * Errors: DQ_ERR_NULLPTR, DQ_ERR_DTYPE, DQ_ERR_SHAPE (ndim != 2, param
- *   shape), DQ_ERR_ALIGN, DQ_ERR_PARAM (policy, k_dim, group_size),
- *   DQ_ERR_OVERLAP.
+ *   src/dst 16-byte aligned (约束说明: 32-byte aligned rows); PER_CHANNEL
+ *   and PER_GROUP k_dim = 0 parameters 16-byte aligned (8 for E8M0); src
+ *   and dst must not overlap.  m may be 0.  Workspace size: 0.
+ * Errors: DQ_ERR_NULLPTR, DQ_ERR_DTYPE (including an F4E2M1 source with a
+ *   non-E8M0 scale, an offset, or an F32 dst), DQ_ERR_SHAPE (ndim != 2,
+ *   param shape, odd n for F4E2M1), DQ_ERR_ALIGN, DQ_ERR_PARAM (policy,
+ *   k_dim, group_size, an F4E2M1 source with a policy other than
+ *   PER_GROUP), DQ_ERR_OVERLAP.
  * ------------------------------------------------------------------------ */
 dq_status dq_antiquantize_get_workspace_size(const dq_tensor* src, const dq_tensor* scale,
                                              const dq_tensor* offset, dq_antiquant_policy policy,

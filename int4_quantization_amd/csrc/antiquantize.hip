@@ -13,7 +13,9 @@
 // PER_GROUP with kDim = 0) instead give a thread R consecutive rows of one
 // chunk, so the thread's parameter vectors are loaded once for R rows;
 // PER_TOKEN and PER_GROUP with kDim = 1 load one parameter pair per chunk,
-// PER_TENSOR one for the whole launch.  Row and column come from one
+// PER_TENSOR one for the whole launch.  Sources: int8, fp8 E4M3FN and E5M2
+// (the b8 cases of 表3), and fp4 E2M1 two codes per byte with e8m0 scales
+// (the float4 case); parameters fp32, fp16, bf16 or e8m0, widened exactly.  Row and column come from one
 // multiply-shift division by the chunks per row (exact for indices below
 // 2^31; larger inputs are split over several launches).  Threads past the
 // end repeat the last chunk, so every access is unconditional.  Source and
@@ -59,8 +61,8 @@ __device__ __forceinline__ uint32_t div_by(uint32_t x, const DivMagic& m)
 
 struct AqArgs {
     const void* src;
-    const float* scale;
-    const float* offset;
+    const void* scale;
+    const void* offset;
     int64_t m, n;
     int64_t row0;       // first row of this launch
     int64_t rows;       // rows of this launch
@@ -74,10 +76,11 @@ struct AqArgs {
     DivMagic by_gs;     // division by gs (rows per group, kDim = 0)
 };
 
-template <int DST>
+template <int SRC, int DST>
 struct Chunk {
-    static constexpr int E = DST == DST_F32 ? 4 : 8;  // elements per chunk
-    static constexpr int W = E / 4;                   // source dwords per chunk
+    static constexpr int E = DST == DST_F32 ? 4 : 8;                 // elements per chunk
+    static constexpr int SB = SRC == SRC_F4E2M1 ? E / 2 : E;         // source bytes per chunk
+    static constexpr int W = SB / 4;                                 // source dwords per chunk
 };
 
 // Four source bytes -> four floats (exact).
@@ -89,7 +92,7 @@ __device__ __forceinline__ void decode4(uint32_t w, float* v)
         v[1] = static_cast<float>(static_cast<int8_t>((w >> 8) & 0xFFu));
         v[2] = static_cast<float>(static_cast<int8_t>((w >> 16) & 0xFFu));
         v[3] = static_cast<float>(static_cast<int8_t>(w >> 24));
-    } else {
+    } else if (SRC == SRC_F8E4M3) {
         // gfx950 converts OCP E4M3FN (NaN only at 0x7F / 0xFF, max 448).
         const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), false);
         const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), true);
@@ -97,7 +100,33 @@ __device__ __forceinline__ void decode4(uint32_t w, float* v)
         v[1] = lo[1];
         v[2] = hi[0];
         v[3] = hi[1];
+    } else {
+        // OCP E5M2 (bf8 in the ISA's naming).
+        const auto lo = __builtin_amdgcn_cvt_pk_f32_bf8(static_cast<int>(w), false);
+        const auto hi = __builtin_amdgcn_cvt_pk_f32_bf8(static_cast<int>(w), true);
+        v[0] = lo[0];
+        v[1] = lo[1];
+        v[2] = hi[0];
+        v[3] = hi[1];
     }
+}
+
+// Eight fp4 E2M1 codes (one dword, element 2k in the low nibble of byte k)
+// -> eight floats, exact: the hardware conversion with a scale of 1.
+__device__ __forceinline__ void decode8_fp4(uint32_t w, float* v)
+{
+    const auto b0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+    const auto b1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+    const auto b2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+    const auto b3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+    v[0] = b0[0];
+    v[1] = b0[1];
+    v[2] = b1[0];
+    v[3] = b1[1];
+    v[4] = b2[0];
+    v[5] = b2[1];
+    v[6] = b3[0];
+    v[7] = b3[1];
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b)
@@ -136,17 +165,75 @@ __device__ __forceinline__ void store_chunk(void* p, const float* t)
     }
 }
 
-template <int E>
-__device__ __forceinline__ void load_params(const float* p, float* v)
+// Parameters (scale, offset) widened exactly to fp32; the kind is a
+// template argument, so the kernel has no branch around these loads.
+__device__ __forceinline__ float e8m0_to_f32(uint32_t b)
 {
-    const float4* q = reinterpret_cast<const float4*>(p);
+    // 2^(b - 127): the exponent field itself, 2^-127 as a subnormal, 0xFF NaN.
+    const uint32_t bits = b == 0xFFu ? 0x7FC00000u : b == 0u ? 0x00400000u : b << 23;
+    return __builtin_bit_cast(float, bits);
+}
+
+template <int P>
+__device__ __forceinline__ float param1(const void* p, int64_t idx)
+{
+    if constexpr (P == PARAM_F32) {
+        return static_cast<const float*>(p)[idx];
+    } else if constexpr (P == PARAM_E8M0) {
+        return e8m0_to_f32(static_cast<const uint8_t*>(p)[idx]);
+    } else {
+        const uint16_t h = static_cast<const uint16_t*>(p)[idx];
+        return P == PARAM_F16 ? widen1<0>(h) : widen1<1>(h);
+    }
+}
+
+// E consecutive parameters starting at idx (a multiple of E), one or two
+// vector loads.
+template <int E, int P>
+__device__ __forceinline__ void param_vec(const void* p, int64_t idx, float* v)
+{
+    if constexpr (P == PARAM_F32) {
+        const float4* q = reinterpret_cast<const float4*>(static_cast<const float*>(p) + idx);
 #pragma unroll
-    for (int i = 0; i < E / 4; ++i) {
-        const float4 f = q[i];
-        v[4 * i + 0] = f.x;
-        v[4 * i + 1] = f.y;
-        v[4 * i + 2] = f.z;
-        v[4 * i + 3] = f.w;
+        for (int i = 0; i < E / 4; ++i) {
+            const float4 f = q[i];
+            v[4 * i + 0] = f.x;
+            v[4 * i + 1] = f.y;
+            v[4 * i + 2] = f.z;
+            v[4 * i + 3] = f.w;
+        }
+    } else if constexpr (P == PARAM_E8M0) {
+        const uint8_t* q = static_cast<const uint8_t*>(p) + idx;
+        uint32_t w[E / 4];
+        if (E == 8) {
+            const uint2 u = *reinterpret_cast<const uint2*>(q);
+            w[0] = u.x;
+            w[E / 4 - 1] = u.y;
+        } else {
+            w[0] = *reinterpret_cast<const uint32_t*>(q);
+        }
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            v[e] = e8m0_to_f32((w[e / 4] >> (8 * (e % 4))) & 0xFFu);
+    } else {
+        const uint16_t* q = static_cast<const uint16_t*>(p) + idx;
+        uint32_t w[E / 2];
+        if (E == 8) {
+            const uint4 u = *reinterpret_cast<const uint4*>(q);
+            w[0] = u.x;
+            w[1] = u.y;
+            w[E / 2 - 2] = u.z;
+            w[E / 2 - 1] = u.w;
+        } else {
+            const uint2 u = *reinterpret_cast<const uint2*>(q);
+            w[0] = u.x;
+            w[E / 2 - 1] = u.y;
+        }
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const uint16_t h = static_cast<uint16_t>((w[e / 2] >> (16 * (e % 2))) & 0xFFFFu);
+            v[e] = P == PARAM_F16 ? widen1<0>(h) : widen1<1>(h);
+        }
     }
 }
 
@@ -163,14 +250,18 @@ __device__ __forceinline__ void load_chunk(uint32_t (&raw)[W], const uint8_t* p)
 }
 
 template <int SRC, int DST, bool OFF>
-__device__ __forceinline__ void convert_store(const uint32_t (&raw)[Chunk<DST>::W], const float* sv, const float* ov,
-                                              void* out)
+__device__ __forceinline__ void convert_store(const uint32_t (&raw)[Chunk<SRC, DST>::W], const float* sv,
+                                              const float* ov, void* out)
 {
-    constexpr int E = Chunk<DST>::E, W = Chunk<DST>::W;
+    constexpr int E = Chunk<SRC, DST>::E, W = Chunk<SRC, DST>::W;
     float v[E];
+    if constexpr (SRC == SRC_F4E2M1) {
+        decode8_fp4(raw[0], v);
+    } else {
 #pragma unroll
-    for (int w = 0; w < W; ++w)
-        decode4<SRC>(raw[w], v + 4 * w);
+        for (int w = 0; w < W; ++w)
+            decode4<SRC>(raw[w], v + 4 * w);
+    }
     float t[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) {
@@ -184,11 +275,11 @@ __device__ __forceinline__ void convert_store(const uint32_t (&raw)[Chunk<DST>::
     store_chunk<DST>(out, t);
 }
 
-template <int SRC, int DST, int PK, bool OFF>
+template <int SRC, int DST, int PK, bool OFF, int P>
 __global__ __launch_bounds__(kBlock) void aq_kernel(AqArgs a)
 {
-    using C = Chunk<DST>;
-    constexpr int E = C::E, W = C::W;
+    using C = Chunk<SRC, DST>;
+    constexpr int E = C::E, W = C::W, SB = C::SB;
     constexpr bool kPerElem = PK == PK_CHANNEL || PK == PK_GROUP_M;
     constexpr int R = kPerElem ? kAqRowsPerThread : 1;
     const int64_t out_elem = DST == DST_F32 ? 4 : 2;
@@ -204,6 +295,16 @@ __global__ __launch_bounds__(kBlock) void aq_kernel(AqArgs a)
     const int64_t j = static_cast<int64_t>(jc) * E;
     const int64_t i0 = a.row0 + static_cast<int64_t>(rb) * R;
 
+    // Source loads first, then the parameters: all are in flight together.
+    const int64_t src_row = a.n / E * SB;  // source bytes per row
+    uint32_t raw[R][W];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        int64_t i = i0 + r;
+        i = i < a.row0 + a.rows ? i : a.row0 + a.rows - 1;  // past the end: repeat the last row
+        load_chunk<W>(raw[r], src + i * src_row + static_cast<int64_t>(jc) * SB);
+    }
+
     float sv[E], ov[E];
     if (PK == PK_TENSOR || PK == PK_TOKEN || PK == PK_GROUP_N) {
         int64_t p = 0;
@@ -211,8 +312,8 @@ __global__ __launch_bounds__(kBlock) void aq_kernel(AqArgs a)
             p = i0;
         if (PK == PK_GROUP_N)
             p = i0 * a.n_groups + div_by(jc, a.by_gsc);
-        const float s1 = a.scale[p];
-        const float o1 = OFF ? a.offset[p] : 0.0f;
+        const float s1 = param1<P>(a.scale, p);
+        const float o1 = OFF ? param1<P>(a.offset, p) : 0.0f;
 #pragma unroll
         for (int e = 0; e < E; ++e) {
             sv[e] = s1;
@@ -222,17 +323,9 @@ __global__ __launch_bounds__(kBlock) void aq_kernel(AqArgs a)
         // The R rows share the group: R divides groupSize and the row
         // blocks start at multiples of R.
         const int64_t base = PK == PK_GROUP_M ? static_cast<int64_t>(div_by(static_cast<uint32_t>(i0), a.by_gs)) * a.n : 0;
-        load_params<E>(a.scale + base + j, sv);
+        param_vec<E, P>(a.scale, base + j, sv);
         if (OFF)
-            load_params<E>(a.offset + base + j, ov);
-    }
-
-    uint32_t raw[R][W];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        int64_t i = i0 + r;
-        i = i < a.row0 + a.rows ? i : a.row0 + a.rows - 1;  // past the end: repeat the last row
-        load_chunk<W>(raw[r], src + i * a.n + j);
+            param_vec<E, P>(a.offset, base + j, ov);
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -244,32 +337,71 @@ __global__ __launch_bounds__(kBlock) void aq_kernel(AqArgs a)
 
 using KernelFn = void (*)(AqArgs);
 
-template <int SRC, int DST, bool OFF>
+template <int SRC, int DST, bool OFF, int P>
 KernelFn pick_pk(int pk)
 {
     switch (pk) {
-    case PK_TENSOR: return aq_kernel<SRC, DST, PK_TENSOR, OFF>;
-    case PK_CHANNEL: return aq_kernel<SRC, DST, PK_CHANNEL, OFF>;
-    case PK_TOKEN: return aq_kernel<SRC, DST, PK_TOKEN, OFF>;
-    case PK_GROUP_N: return aq_kernel<SRC, DST, PK_GROUP_N, OFF>;
-    case PK_GROUP_M: return aq_kernel<SRC, DST, PK_GROUP_M, OFF>;
+    case PK_TENSOR: return aq_kernel<SRC, DST, PK_TENSOR, OFF, P>;
+    case PK_CHANNEL: return aq_kernel<SRC, DST, PK_CHANNEL, OFF, P>;
+    case PK_TOKEN: return aq_kernel<SRC, DST, PK_TOKEN, OFF, P>;
+    case PK_GROUP_N: return aq_kernel<SRC, DST, PK_GROUP_N, OFF, P>;
+    case PK_GROUP_M: return aq_kernel<SRC, DST, PK_GROUP_M, OFF, P>;
     }
     return nullptr;
 }
 
-template <int SRC, int DST>
+template <int SRC, int DST, int P>
 KernelFn pick_off(int pk, bool off)
 {
-    return off ? pick_pk<SRC, DST, true>(pk) : pick_pk<SRC, DST, false>(pk);
+    return off ? pick_pk<SRC, DST, true, P>(pk) : pick_pk<SRC, DST, false, P>(pk);
 }
 
-template <int SRC>
+template <int SRC, int P>
 KernelFn pick_dst(int dst, int pk, bool off)
 {
     switch (dst) {
-    case DST_BF16: return pick_off<SRC, DST_BF16>(pk, off);
-    case DST_F16: return pick_off<SRC, DST_F16>(pk, off);
-    case DST_F32: return pick_off<SRC, DST_F32>(pk, off);
+    case DST_BF16: return pick_off<SRC, DST_BF16, P>(pk, off);
+    case DST_F16: return pick_off<SRC, DST_F16, P>(pk, off);
+    case DST_F32: return pick_off<SRC, DST_F32, P>(pk, off);
+    }
+    return nullptr;
+}
+
+template <int SRC>
+KernelFn pick_param(int param, int dst, int pk, bool off)
+{
+    switch (param) {
+    case PARAM_F32: return pick_dst<SRC, PARAM_F32>(dst, pk, off);
+    case PARAM_F16: return pick_dst<SRC, PARAM_F16>(dst, pk, off);
+    case PARAM_BF16: return pick_dst<SRC, PARAM_BF16>(dst, pk, off);
+    }
+    return nullptr;
+}
+
+// The float4 case: PER_GROUP only, e8m0 scales, no offset, bf16 or fp16
+// output.
+KernelFn pick_fp4(int dst, int pk)
+{
+    const bool n_dir = pk == PK_GROUP_N;
+    if (pk != PK_GROUP_N && pk != PK_GROUP_M)
+        return nullptr;
+    if (dst == DST_BF16)
+        return n_dir ? aq_kernel<SRC_F4E2M1, DST_BF16, PK_GROUP_N, false, PARAM_E8M0>
+                     : aq_kernel<SRC_F4E2M1, DST_BF16, PK_GROUP_M, false, PARAM_E8M0>;
+    if (dst == DST_F16)
+        return n_dir ? aq_kernel<SRC_F4E2M1, DST_F16, PK_GROUP_N, false, PARAM_E8M0>
+                     : aq_kernel<SRC_F4E2M1, DST_F16, PK_GROUP_M, false, PARAM_E8M0>;
+    return nullptr;
+}
+
+KernelFn pick_src(const AqPlan& p, int pk)
+{
+    const bool off = p.offset != nullptr;
+    switch (p.src_kind) {
+    case SRC_I8: return pick_param<SRC_I8>(p.param_kind, p.dst_kind, pk, off);
+    case SRC_F8E4M3: return pick_param<SRC_F8E4M3>(p.param_kind, p.dst_kind, pk, off);
+    case SRC_F8E5M2: return pick_param<SRC_F8E5M2>(p.param_kind, p.dst_kind, pk, off);
+    case SRC_F4E2M1: return off || p.param_kind != PARAM_E8M0 ? nullptr : pick_fp4(p.dst_kind, pk);
     }
     return nullptr;
 }
@@ -281,8 +413,7 @@ hipError_t launch_antiquantize(const AqPlan& p, hipStream_t stream)
     int pk = p.policy;  // DQ_PER_TENSOR .. DQ_PER_TOKEN map to the same numbers
     if (p.policy == DQ_PER_GROUP)
         pk = p.k_dim == 1 ? PK_GROUP_N : PK_GROUP_M;
-    KernelFn fn = p.src_kind == SRC_I8 ? pick_dst<SRC_I8>(p.dst_kind, pk, p.offset != nullptr)
-                                       : pick_dst<SRC_F8E4M3>(p.dst_kind, pk, p.offset != nullptr);
+    KernelFn fn = pick_src(p, pk);
     if (!fn)
         return hipErrorInvalidValue;
     const int64_t E = p.dst_kind == DST_F32 ? 4 : 8;

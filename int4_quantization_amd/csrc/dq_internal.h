@@ -64,13 +64,15 @@ struct AdaPlan {
 };
 
 // ---- AntiQuantize ---------------------------------------------------------
-enum SrcKind : int { SRC_I8 = 0, SRC_F8E4M3 = 1 };
+enum SrcKind : int { SRC_I8 = 0, SRC_F8E4M3 = 1, SRC_F8E5M2 = 2, SRC_F4E2M1 = 3 };
+enum ParamKind : int { PARAM_F32 = 0, PARAM_F16 = 1, PARAM_BF16 = 2, PARAM_E8M0 = 3 };
 enum DstKind : int { DST_BF16 = 0, DST_F16 = 1, DST_F32 = 2 };
 
 struct AqPlan {
     const void* src;
-    const float* scale;
-    const float* offset;  // nullptr: hasOffset = false
+    const void* scale;
+    const void* offset;  // nullptr: hasOffset = false
+    int param_kind;      // ParamKind of scale and offset
     int64_t m, n;
     int policy;  // dq_antiquant_policy
     int k_dim;

@@ -55,6 +55,9 @@ const char* dtype_name(dq_dtype d)
     case DQ_I4: return "I4";
     case DQ_I32: return "I32";
     case DQ_F8E4M3: return "F8E4M3";
+    case DQ_F8E5M2: return "F8E5M2";
+    case DQ_F4E2M1: return "F4E2M1";
+    case DQ_E8M0: return "E8M0";
     }
     return "unknown";
 }
@@ -118,8 +121,8 @@ int64_t elem_bytes_x16(dq_dtype d)  // bytes per element times 2 (I4 is half a b
     switch (d) {
     case DQ_F32: case DQ_I32: return 8;
     case DQ_F16: case DQ_BF16: return 4;
-    case DQ_I8: case DQ_F8E4M3: return 2;
-    case DQ_I4: return 1;
+    case DQ_I8: case DQ_F8E4M3: case DQ_F8E5M2: case DQ_E8M0: return 2;
+    case DQ_I4: case DQ_F4E2M1: return 1;
     }
     return 0;
 }
@@ -461,17 +464,23 @@ dq_status dq_antiquantize_get_workspace_size(const dq_tensor* src, const dq_tens
     if ((st = check_tensor(dst, "dst", &ndst)) != DQ_SUCCESS) return st;
     if (offset && (st = check_tensor(offset, "offset", nullptr)) != DQ_SUCCESS) return st;
 
-    if (src->dtype != DQ_I8 && src->dtype != DQ_F8E4M3)
-        return fail(DQ_ERR_DTYPE, "src must be I8 or F8E4M3, got %s", dtype_name(src->dtype));
-    if (dst->dtype != DQ_BF16 && dst->dtype != DQ_F16 && dst->dtype != DQ_F32)
-        return fail(DQ_ERR_DTYPE, "dst must be BF16, F16 or F32, got %s", dtype_name(dst->dtype));
-    if (scale->dtype != DQ_F32)
-        return fail(DQ_ERR_DTYPE, "scale must be F32, got %s", dtype_name(scale->dtype));
-    if (offset && offset->dtype != DQ_F32)
-        return fail(DQ_ERR_DTYPE, "offset must be F32, got %s", dtype_name(offset->dtype));
+    const bool fp4 = src->dtype == DQ_F4E2M1;
+    if (src->dtype != DQ_I8 && src->dtype != DQ_F8E4M3 && src->dtype != DQ_F8E5M2 && !fp4)
+        return fail(DQ_ERR_DTYPE, "src must be I8, F8E4M3, F8E5M2 or F4E2M1, got %s", dtype_name(src->dtype));
+    if (dst->dtype != DQ_BF16 && dst->dtype != DQ_F16 && (dst->dtype != DQ_F32 || fp4))
+        return fail(DQ_ERR_DTYPE, "dst must be BF16 or F16%s, got %s", fp4 ? " for an F4E2M1 source" : " or F32",
+                    dtype_name(dst->dtype));
+    if (fp4 ? scale->dtype != DQ_E8M0
+            : (scale->dtype != DQ_F32 && scale->dtype != DQ_F16 && scale->dtype != DQ_BF16))
+        return fail(DQ_ERR_DTYPE, "scale must be %s, got %s", fp4 ? "E8M0 for an F4E2M1 source" : "F32, F16 or BF16",
+                    dtype_name(scale->dtype));
+    if (offset && (fp4 || offset->dtype != scale->dtype))
+        return fail(DQ_ERR_DTYPE, fp4 ? "an F4E2M1 source takes no offset" : "offset must have the scale's dtype");
     if (src->ndim != 2)
         return fail(DQ_ERR_SHAPE, "src must be 2-D [m, n] (got %d dims)", src->ndim);
     const int64_t m = src->dims[0], n = src->dims[1];
+    if (fp4 && n % 2 != 0)
+        return fail(DQ_ERR_SHAPE, "an F4E2M1 source needs an even n, got %lld", (long long)n);
     if (m > dq::kMaxGridBlocks)
         return fail(DQ_ERR_SHAPE, "at most %lld rows are supported, got %lld", (long long)dq::kMaxGridBlocks,
                     (long long)m);
@@ -479,6 +488,8 @@ dq_status dq_antiquantize_get_workspace_size(const dq_tensor* src, const dq_tens
         return fail(DQ_ERR_SHAPE, "dst must have the shape of src");
     if (policy < DQ_PER_TENSOR || policy > DQ_PER_GROUP)
         return fail(DQ_ERR_PARAM, "unknown policy %d", (int)policy);
+    if (fp4 && policy != DQ_PER_GROUP)
+        return fail(DQ_ERR_PARAM, "an F4E2M1 source supports PER_GROUP only");
     if (policy == DQ_PER_GROUP) {
         if (k_dim != 0 && k_dim != 1)
             return fail(DQ_ERR_PARAM, "k_dim must be 0 or 1 for PER_GROUP, got %d", k_dim);
@@ -517,8 +528,9 @@ dq_status dq_antiquantize_get_workspace_size(const dq_tensor* src, const dq_tens
         if (!aligned(src->data, 16) || !aligned(dst->data, 16))
             return fail(DQ_ERR_ALIGN, "src and dst must be 16-byte aligned");
         const bool vec_params = policy == DQ_PER_CHANNEL || (policy == DQ_PER_GROUP && k_dim == 0);
-        if (vec_params && (!aligned(scale->data, 16) || (offset && !aligned(offset->data, 16))))
-            return fail(DQ_ERR_ALIGN, "scale/offset must be 16-byte aligned for this policy");
+        const uintptr_t pa = fp4 ? 8 : 16;
+        if (vec_params && (!aligned(scale->data, pa) || (offset && !aligned(offset->data, pa))))
+            return fail(DQ_ERR_ALIGN, "scale/offset must be %d-byte aligned for this policy", (int)pa);
         const uintptr_t s0 = reinterpret_cast<uintptr_t>(src->data);
         const uintptr_t s1 = s0 + static_cast<uintptr_t>(nsrc * elem_bytes_x16(src->dtype) / 2);
         const uintptr_t d0 = reinterpret_cast<uintptr_t>(dst->data);
@@ -534,14 +546,17 @@ dq_status dq_antiquantize_get_workspace_size(const dq_tensor* src, const dq_tens
         return fail(DQ_ERR_RUNTIME, "out of host memory");
     dq::AqPlan& p = e->aq;
     p.src = src->data;
-    p.scale = static_cast<const float*>(scale->data);
-    p.offset = offset ? static_cast<const float*>(offset->data) : nullptr;
+    p.scale = scale->data;
+    p.offset = offset ? offset->data : nullptr;
+    p.param_kind = scale->dtype == DQ_F16 ? dq::PARAM_F16 : scale->dtype == DQ_BF16 ? dq::PARAM_BF16
+                 : scale->dtype == DQ_E8M0 ? dq::PARAM_E8M0 : dq::PARAM_F32;
     p.m = m;
     p.n = n;
     p.policy = policy;
     p.k_dim = policy == DQ_PER_GROUP ? k_dim : 1;
     p.group_size = policy == DQ_PER_GROUP ? gs : 0;
-    p.src_kind = src->dtype == DQ_I8 ? dq::SRC_I8 : dq::SRC_F8E4M3;
+    p.src_kind = src->dtype == DQ_I8 ? dq::SRC_I8 : src->dtype == DQ_F8E4M3 ? dq::SRC_F8E4M3
+               : src->dtype == DQ_F8E5M2 ? dq::SRC_F8E5M2 : dq::SRC_F4E2M1;
     p.dst_kind = dst->dtype == DQ_BF16 ? dq::DST_BF16 : dst->dtype == DQ_F16 ? dq::DST_F16 : dq::DST_F32;
     p.dst = dst->data;
     *executor = e;

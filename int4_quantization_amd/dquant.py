@@ -28,7 +28,7 @@ SUCCESS, ERR_NULLPTR, ERR_DTYPE, ERR_SHAPE, ERR_ALIGN, ERR_PARAM, ERR_OVERLAP, E
 STATUS_NAMES = ["DQ_SUCCESS", "DQ_ERR_NULLPTR", "DQ_ERR_DTYPE", "DQ_ERR_SHAPE", "DQ_ERR_ALIGN",
                 "DQ_ERR_PARAM", "DQ_ERR_OVERLAP", "DQ_ERR_WORKSPACE", "DQ_ERR_RUNTIME"]
 # dq_dtype
-F32, F16, BF16, I8, I4, I32, F8E4M3 = range(7)
+F32, F16, BF16, I8, I4, I32, F8E4M3, F8E5M2, F4E2M1, E8M0 = range(10)
 # dq_antiquant_policy
 POLICIES = {"per_tensor": 0, "per_channel": 1, "per_token": 2, "per_group": 3}
 
@@ -105,7 +105,8 @@ def _check(status: int) -> None:
 
 _TORCH_CODES = {
     torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16, torch.int8: I8,
-    torch.int32: I32, torch.float8_e4m3fn: F8E4M3,
+    torch.int32: I32, torch.float8_e4m3fn: F8E4M3, torch.float8_e5m2: F8E5M2,
+    torch.float4_e2m1fn_x2: F4E2M1, torch.float8_e8m0fnu: E8M0,
 }
 
 
@@ -114,7 +115,8 @@ def tensor_desc(t: Optional[torch.Tensor], dtype: Optional[int] = None,
     """Descriptor of a dense row-major tensor (None stays None).
 
     ``dtype`` / ``dims`` override the tensor's own; an INT4 output travels as
-    a uint8 tensor of packed bytes with dtype=I4 and its logical dims.
+    a uint8 tensor of packed bytes with dtype=I4 and its logical dims, and a
+    torch.float4_e2m1fn_x2 tensor [..., k] describes k * 2 codes.
     """
     if t is None:
         return None
@@ -124,6 +126,8 @@ def tensor_desc(t: Optional[torch.Tensor], dtype: Optional[int] = None,
     d.data = t.data_ptr() if t.numel() > 0 else None
     d.dtype = _TORCH_CODES[t.dtype] if dtype is None else dtype
     shape = list(t.shape) if dims is None else list(dims)
+    if dims is None and t.dtype == torch.float4_e2m1fn_x2 and shape:
+        shape[-1] *= 2  # each element holds two 4-bit codes
     if len(shape) > MAX_DIMS:
         raise ValueError("at most 8 dimensions")
     d.ndim = len(shape)
@@ -337,8 +341,14 @@ def ada_layernorm_quant(x: torch.Tensor, scale: torch.Tensor, shift: torch.Tenso
 def antiquantize(src: torch.Tensor, scale: torch.Tensor, offset: Optional[torch.Tensor] = None,
                  policy="per_tensor", k_dim: int = 1, group_size: int = 0,
                  dst_dtype: torch.dtype = torch.bfloat16, stream=None) -> torch.Tensor:
-    """Dequantize src [m, n] (int8 or float8_e4m3fn) into dst_dtype."""
-    dst = torch.empty(src.shape, dtype=dst_dtype, device=src.device)
+    """Dequantize src [m, n] into dst_dtype.  src: int8, float8_e4m3fn,
+    float8_e5m2, or float4_e2m1fn_x2 [m, n/2] (two codes per byte, with a
+    float8_e8m0fnu PER_GROUP scale and no offset); scale / offset float32,
+    float16 or bfloat16 for the 8-bit sources."""
+    shape = list(src.shape)
+    if src.dtype == torch.float4_e2m1fn_x2:
+        shape[-1] *= 2
+    dst = torch.empty(shape, dtype=dst_dtype, device=src.device)
     ws, ex = dq_antiquantize_get_workspace_size(src, scale, offset, policy, k_dim, group_size, dst)
     dq_antiquantize(_workspace(ws, src.device), ws, ex, stream)
     return dst

@@ -3,8 +3,9 @@
 This module holds random draws and dtype narrowing only -- none of the
 quantization arithmetic.  Every generator uses numpy's PCG64
 ``default_rng(seed)``, draws in the order written, produces values in
-float32 and narrows them to bf16 / fp16 / fp8-e4m3fn with torch's
-round-to-nearest-even casts.  Tensors are returned on the CPU.
+float32 and narrows them to bf16 / fp16 / fp8 with torch's
+round-to-nearest-even casts (fp4 and e8m0 inputs are drawn as codes).
+Tensors are returned on the CPU.
 
 The full-size workloads are the ones the benchmark and the large parity
 tests use (rows x columns):
@@ -17,6 +18,10 @@ tests use (rows x columns):
 * ``ada_ln_quant_bf16_4x4096x3072`` AdaLayerNorm + smooth + INT8
 * ``aq_{per_tensor,per_channel,per_token,per_group}_int8_16384x8192`` and
   ``aq_per_group_fp8e4m3_16384x8192``  AntiQuantize to bf16
+* ``aq_per_channel_fp8e5m2_bf16param_16384x8192``  fp8-e5m2 source, bf16
+                                    scale / offset (a 表3 combination)
+* ``aq_per_group_fp4e2m1_e8m0_16384x8192``  the float4 case: fp4 e2m1 codes,
+                                    e8m0 scales per 32 columns, no offset
 """
 from __future__ import annotations
 
@@ -98,24 +103,42 @@ def aq_param_shape(policy: str, m: int, n: int, kdim: int = 1, group_size: int =
 
 
 def aq_inputs(m: int, n: int, policy: str, seed: int, *, src: str = "int8", kdim: int = 1,
-              group_size: int = 128, offset: bool = True) -> Dict[str, object]:
+              group_size: int = 128, offset: bool = True,
+              param_dtype: str = "float32") -> Dict[str, object]:
     """Inputs of one AntiQuantize call.
 
-    Draw order: src (int8 uniform over [-128, 127], or fp8-e4m3fn from
-    N(0, 4) clipped to +-448 then rounded to nearest even); scale ~ U(0.001,
-    0.05) and offset ~ U(-8, 8), both fp32, in the policy's shape.
+    Draw order: src, then scale, then offset.
+      src 'int8': uniform over [-128, 127].
+      src 'float8_e4m3fn' / 'float8_e5m2': N(0, 4) clipped to the format's
+        largest finite value (448 / 57344), then rounded to nearest even.
+      src 'float4_e2m1': bytes uniform over [0, 255] (two codes each),
+        [m, n/2], as torch.float4_e2m1fn_x2.
+    b8 sources: scale ~ U(0.001, 0.05) and offset ~ U(-8, 8) in fp32, in the
+    policy's shape, then rounded to param_dtype ('float32', 'float16',
+    'bfloat16').  float4: scale = e8m0 codes uniform over [117, 137]
+    (2^-10 .. 2^10) as torch.float8_e8m0fnu; no offset.
     """
     rng = np.random.default_rng(seed)
+    shape = aq_param_shape(policy, m, n, kdim, group_size)
+    gs = group_size if policy == "per_group" else 0
+    if src == "float4_e2m1":
+        codes = rng.integers(0, 256, (m, n // 2)).astype(np.uint8)
+        sc = rng.integers(117, 138, shape).astype(np.uint8)
+        return {"src": torch.from_numpy(codes).view(torch.float4_e2m1fn_x2),
+                "scale": torch.from_numpy(sc).view(torch.float8_e8m0fnu), "offset": None,
+                "policy": policy, "kdim": kdim, "group_size": gs}
     if src == "int8":
         s = torch.from_numpy(rng.integers(-128, 128, (m, n)).astype(np.int8))
     else:
-        v = np.clip(rng.normal(0.0, 4.0, (m, n)).astype(np.float32), -448.0, 448.0)
-        s = torch.from_numpy(v).to(torch.float8_e4m3fn)
-    shape = aq_param_shape(policy, m, n, kdim, group_size)
-    scale = torch.from_numpy(rng.uniform(0.001, 0.05, shape).astype(np.float32))
-    off = torch.from_numpy(rng.uniform(-8.0, 8.0, shape).astype(np.float32)) if offset else None
+        fmt = getattr(torch, src)
+        top = float(torch.finfo(fmt).max)
+        v = np.clip(rng.normal(0.0, 4.0, (m, n)).astype(np.float32), -top, top)
+        s = torch.from_numpy(v).to(fmt)
+    pdt = getattr(torch, param_dtype)
+    scale = torch.from_numpy(rng.uniform(0.001, 0.05, shape).astype(np.float32)).to(pdt)
+    off = torch.from_numpy(rng.uniform(-8.0, 8.0, shape).astype(np.float32)).to(pdt) if offset else None
     return {"src": s, "scale": scale, "offset": off, "policy": policy, "kdim": kdim,
-            "group_size": group_size if policy == "per_group" else 0}
+            "group_size": gs}
 
 
 # Full-size workloads: name -> (op, builder).
@@ -148,4 +171,10 @@ WORKLOADS = {
     "aq_per_group_fp8e4m3_16384x8192": (
         "antiquantize",
         lambda: aq_inputs(16384, 8192, "per_group", 6, src="float8_e4m3fn", group_size=128)),
+    "aq_per_channel_fp8e5m2_bf16param_16384x8192": (
+        "antiquantize",
+        lambda: aq_inputs(16384, 8192, "per_channel", 7, src="float8_e5m2", param_dtype="bfloat16")),
+    "aq_per_group_fp4e2m1_e8m0_16384x8192": (
+        "antiquantize",
+        lambda: aq_inputs(16384, 8192, "per_group", 8, src="float4_e2m1", group_size=32)),
 }

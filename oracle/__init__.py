@@ -105,6 +105,10 @@ def _buffer(t) -> Tuple[Optional[np.ndarray], int]:
             return t.view(torch.uint8).numpy(), F8E4M3
         if t.dtype == torch.float8_e5m2:
             return t.view(torch.uint8).numpy(), F8E5M2
+        if t.dtype == torch.float4_e2m1fn_x2:
+            return t.view(torch.uint8).numpy(), F4E2M1
+        if t.dtype == torch.float8_e8m0fnu:
+            return t.view(torch.uint8).numpy(), E8M0
         t = t.numpy()
     a = np.ascontiguousarray(t)
     if a.dtype == np.float32:

@@ -46,8 +46,16 @@ def first_mismatch(a: np.ndarray, b: np.ndarray) -> str:
     return f"{len(idx)} mismatches, first at {i}: gpu={a[i]} ref={b[i]}"
 
 
+_BYTE_VIEWS = (torch.float4_e2m1fn_x2, torch.float8_e8m0fnu)
+
+
 def to_dev(t):
-    return None if t is None else t.to(DEV)
+    """Copy to the GPU; 1-byte formats torch cannot copy travel as bytes."""
+    if t is None:
+        return None
+    if t.dtype in _BYTE_VIEWS:
+        return t.view(torch.uint8).to(DEV).view(t.dtype)
+    return t.to(DEV)
 
 
 def check_dynamic_quant(orc, x, smooth=None, group_index=None, symmetric=True, out="int8",
@@ -84,8 +92,7 @@ def check_antiquantize(orc, src, scale, offset=None, policy="per_tensor", k_dim=
                        dst_dtype=torch.bfloat16):
     d = dq.antiquantize(to_dev(src), to_dev(scale), to_dev(offset), policy, k_dim, group_size,
                         dst_dtype)
-    ref = orc.antiquantize(src, scale.numpy(), None if offset is None else offset.numpy(), policy,
-                           k_dim, group_size, _DST_NAMES[dst_dtype])
+    ref = orc.antiquantize(src, scale, offset, policy, k_dim, group_size, _DST_NAMES[dst_dtype])
     torch.cuda.synchronize()
     g = aq_bits(d)
     if dst_dtype == torch.float32:

@@ -244,6 +244,46 @@ def test_antiquantize_types_alignment_overlap(lib, src, dst, off, status):
     assert aq_ws(lib, src, sc, off, 0, -1, 0, dst) == status
 
 
+@pytest.mark.parametrize("src,sc,off,pol,kdim,gs,dst,status", [
+    # b8 sources with fp16 / bf16 parameters (表3), and e5m2
+    (D.F8E5M2, (D.F32, [1]), None, 0, -1, 0, D.BF16, D.SUCCESS),
+    (D.F8E5M2, (D.F16, [1, NN]), (D.F16, [1, NN]), 1, 1, 0, D.F16, D.SUCCESS),
+    (D.I8, (D.BF16, [M, 1]), (D.BF16, [M, 1]), 2, 1, 0, D.F32, D.SUCCESS),
+    (D.I8, (D.F16, [1]), (D.F32, [1]), 0, -1, 0, D.BF16, D.ERR_DTYPE),      # offset dtype != scale
+    (D.I8, (D.E8M0, [M, NN // 32]), None, 3, 1, 32, D.BF16, D.ERR_DTYPE),   # e8m0 is for fp4 only
+    # the float4 case: PER_GROUP, e8m0 scale, no offset, bf16 / fp16 dst
+    (D.F4E2M1, (D.E8M0, [M, NN // 32]), None, 3, 1, 32, D.BF16, D.SUCCESS),
+    (D.F4E2M1, (D.E8M0, [2, NN]), None, 3, 0, 32, D.F16, D.SUCCESS),
+    (D.F4E2M1, (D.E8M0, [M, NN // 32]), (D.E8M0, [M, NN // 32]), 3, 1, 32, D.BF16, D.ERR_DTYPE),
+    (D.F4E2M1, (D.F32, [M, NN // 32]), None, 3, 1, 32, D.BF16, D.ERR_DTYPE),
+    (D.F4E2M1, (D.E8M0, [M, NN // 32]), None, 3, 1, 32, D.F32, D.ERR_DTYPE),
+    (D.F4E2M1, (D.E8M0, [M, 1]), None, 2, 1, 0, D.BF16, D.ERR_PARAM),       # PER_TOKEN
+    (D.F4E2M1, (D.E8M0, [1]), None, 0, -1, 0, D.BF16, D.ERR_PARAM),         # PER_TENSOR
+])
+def test_antiquantize_new_types(lib, src, sc, off, pol, kdim, gs, dst, status):
+    s = desc(src, [M, NN], SRC_PTR)
+    d = desc(dst, [M, NN], DST_PTR)
+    scd = desc(sc[0], sc[1], 0x20000)
+    ofd = None if off is None else desc(off[0], off[1], 0x40000)
+    assert aq_ws(lib, s, scd, ofd, pol, kdim, gs, d) == status
+
+
+def test_antiquantize_float4_shape_and_alignment(lib):
+    """fp4: n even (SHAPE) and n/2 bytes per row a multiple of 32 (ALIGN);
+    kDim = 0 e8m0 scales need 8-byte alignment."""
+    e8 = lambda shape, ptr=0x20000: desc(D.E8M0, shape, ptr)
+    assert aq_ws(lib, desc(D.F4E2M1, [M, 65], SRC_PTR), e8([M, 3]), None, 3, 1, 32,
+                 desc(D.BF16, [M, 65], DST_PTR)) == D.ERR_SHAPE
+    assert aq_ws(lib, desc(D.F4E2M1, [M, 32], SRC_PTR), e8([M, 1]), None, 3, 1, 32,
+                 desc(D.BF16, [M, 32], DST_PTR)) == D.ERR_ALIGN
+    assert aq_ws(lib, desc(D.F4E2M1, [M, 64], SRC_PTR), e8([M, 2]), None, 3, 1, 32,
+                 desc(D.BF16, [M, 64], DST_PTR)) == D.SUCCESS
+    assert aq_ws(lib, desc(D.F4E2M1, [M, NN], SRC_PTR), e8([2, NN], 0x20008), None, 3, 0, 32,
+                 desc(D.BF16, [M, NN], DST_PTR)) == D.SUCCESS
+    assert aq_ws(lib, desc(D.F4E2M1, [M, NN], SRC_PTR), e8([2, NN], 0x20004), None, 3, 0, 32,
+                 desc(D.BF16, [M, NN], DST_PTR)) == D.ERR_ALIGN
+
+
 def test_antiquantize_channel_params_alignment(lib):
     src = desc(D.I8, [M, NN], SRC_PTR)
     dst = desc(D.BF16, [M, NN], DST_PTR)

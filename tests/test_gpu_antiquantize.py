@@ -1,8 +1,10 @@
 """AntiQuantize on the GPU (through the C ABI) against the CPU oracle,
 bit-exact: every policy (PER_GROUP along n and along m, with a short last
-group), int8 and fp8-e4m3fn sources, bf16 / fp16 / fp32 destinations, with
-and without offset, on a ragged tile grid; the page's worked example; every
-fp8 code."""
+group), int8, fp8-e4m3fn and fp8-e5m2 sources, fp32 / fp16 / bf16
+parameters, bf16 / fp16 / fp32 destinations, with and without offset, on a
+ragged grid; the page's worked example; every fp8 code of both formats; the
+float4 case (fp4 e2m1 source, e8m0 scales, PER_GROUP along n and along m)
+on every byte value and every e8m0 code."""
 import numpy as np
 import pytest
 import torch
@@ -21,7 +23,7 @@ DSTS = [torch.bfloat16, torch.float16, torch.float32]
 
 
 @pytest.mark.parametrize("policy,kdim,gs", POLICIES, ids=[f"{p}-k{k}-g{g}" for p, k, g in POLICIES])
-@pytest.mark.parametrize("src", ["int8", "float8_e4m3fn"])
+@pytest.mark.parametrize("src", ["int8", "float8_e4m3fn", "float8_e5m2"])
 @pytest.mark.parametrize("dst", DSTS, ids=["bf16", "f16", "f32"])
 @pytest.mark.parametrize("with_offset", [True, False], ids=["offset", "no_offset"])
 def test_antiquantize_parity(orc, policy, kdim, gs, src, dst, with_offset):
@@ -29,6 +31,49 @@ def test_antiquantize_parity(orc, policy, kdim, gs, src, dst, with_offset):
     q = synth.aq_inputs(37, 2080, policy, 100 + gs + kdim, src=src, kdim=kdim,
                         group_size=gs or 128, offset=with_offset)
     check_antiquantize(orc, q["src"], q["scale"], q["offset"], policy, kdim, q["group_size"], dst)
+
+
+@pytest.mark.parametrize("policy,kdim,gs", POLICIES, ids=[f"{p}-k{k}-g{g}" for p, k, g in POLICIES])
+@pytest.mark.parametrize("pdt", ["float16", "bfloat16"])
+@pytest.mark.parametrize("src", ["int8", "float8_e5m2"])
+def test_antiquantize_half_params(orc, policy, kdim, gs, pdt, src):
+    """fp16 / bf16 scale and offset (表3's half and bfloat16_t ScaleT /
+    OffsetT), widened exactly, into the same dtype and into fp32."""
+    announce("antiquantize half params", policy, kdim, gs, pdt, src)
+    q = synth.aq_inputs(37, 2080, policy, 300 + gs + kdim, src=src, kdim=kdim,
+                        group_size=gs or 128, param_dtype=pdt)
+    for dst in (getattr(torch, pdt), torch.float32):
+        check_antiquantize(orc, q["src"], q["scale"], q["offset"], policy, kdim, q["group_size"], dst)
+
+
+FP4_CASES = [(1, 32), (1, 96), (0, 32), (0, 64)]
+
+
+@pytest.mark.parametrize("kdim,gs", FP4_CASES, ids=[f"k{k}-g{g}" for k, g in FP4_CASES])
+@pytest.mark.parametrize("dst", [torch.bfloat16, torch.float16], ids=["bf16", "f16"])
+def test_antiquantize_float4(orc, kdim, gs, dst):
+    """The float4 case on a ragged grid (37 rows: a partial block of 8 rows
+    for kDim = 0; n = 2112 with groups of 96 leaves a short last group)."""
+    announce("antiquantize float4", kdim, gs, dst)
+    q = synth.aq_inputs(37, 2112, "per_group", 400 + gs + kdim, src="float4_e2m1", kdim=kdim,
+                        group_size=gs)
+    check_antiquantize(orc, q["src"], q["scale"], None, "per_group", kdim, gs, dst)
+
+
+def test_antiquantize_float4_all_codes(orc):
+    """Every fp4 byte in every position, against every e8m0 code (0 gives
+    2^-127, 254 overflows to infinity, 255 is NaN): row r takes e8m0 code r
+    for its groups of 32."""
+    announce("antiquantize float4 codes")
+    codes = np.tile(np.arange(256, dtype=np.uint8), (256, 1))          # [256 rows, 512 codes]
+    sc = np.repeat(np.arange(256, dtype=np.uint8)[:, None], 16, axis=1)  # [256, 512 / 32]
+    src = torch.from_numpy(codes).view(torch.float4_e2m1fn_x2)
+    scale = torch.from_numpy(sc).view(torch.float8_e8m0fnu)
+    for dst in (torch.bfloat16, torch.float16):
+        check_antiquantize(orc, src, scale, None, "per_group", 1, 32, dst)
+    sc0 = np.tile(np.arange(256, dtype=np.uint8), 2)[None, :].repeat(8, axis=0)  # [256 / 32, 512]
+    check_antiquantize(orc, src, torch.from_numpy(np.ascontiguousarray(sc0)).view(torch.float8_e8m0fnu),
+                       None, "per_group", 0, 32, torch.bfloat16)
 
 
 def test_antiquantize_page_example(orc):
@@ -42,9 +87,10 @@ def test_antiquantize_page_example(orc):
         assert torch.equal(d.cpu().float(), src.float())
 
 
-def test_antiquantize_all_fp8_codes(orc):
-    announce("antiquantize fp8 codes")
-    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8).reshape(8, 32).view(torch.float8_e4m3fn)
+@pytest.mark.parametrize("fmt", ["float8_e4m3fn", "float8_e5m2"])
+def test_antiquantize_all_fp8_codes(orc, fmt):
+    announce("antiquantize fp8 codes", fmt)
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8).reshape(8, 32).view(getattr(torch, fmt))
     for dst in DSTS:
         check_antiquantize(orc, codes, torch.ones(1), torch.zeros(1), "per_tensor", 1, 0, dst)
         check_antiquantize(orc, codes, torch.full((1,), 0.75), None, "per_tensor", 1, 0, dst)
