@@ -1,5 +1,5 @@
-"""CPU oracle for per-token dynamic quantization, AdaLayerNorm-quant and
-AntiQuantize -- TEST INFRASTRUCTURE ONLY.
+"""CPU oracle for per-token dynamic quantization, AdaLayerNorm-quant,
+AntiQuantize and mx block quantization -- TEST INFRASTRUCTURE ONLY.
 
 Only ``tests/``, the smoke check in ``__graft_entry__`` and the CPU-baseline
 leg of ``bench.py`` may import this package.  The product path (the HIP
@@ -14,6 +14,8 @@ the passage of the pages it follows:
 * ``ada_layernorm_modulate``  -- aclnnAdaLayerNormQuant, Formula steps 1-3.
 * ``ada_layernorm_quant``     -- aclnnAdaLayerNormQuant, Formula steps 1-5.
 * ``antiquantize``            -- AntiQuantize, 功能说明 / 表1-表3.
+* ``mx_quantize``             -- aclnnQuantBatchMatmulInplaceAdd, 计算公式
+  (mx量化), read as the OCP Microscaling v1.0 conversion.
 """
 from __future__ import annotations
 
@@ -70,6 +72,8 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_antiquantize.argtypes = [_vp, _int, _i64, _i64, _vp, _int, _vp, _int,
                                         _int, _int, _i64, _int, _vp]
     lib.oracle_antiquantize.restype = None
+    lib.oracle_mx_quantize.argtypes = [_vp, _int, _i64, _i64, _int, _int, _vp, _vp]
+    lib.oracle_mx_quantize.restype = None
     lib.orc_convert_to_f32.argtypes = [_vp, _int, _i64, _vp]
     lib.orc_convert_to_f32.restype = None
     lib.orc_convert_from_f32.argtypes = [_vp, _i64, _int, _vp]
@@ -246,6 +250,31 @@ class Oracle:
                                      POLICIES[policy], int(kdim), int(group_size), dcode,
                                      _ptr(out))
         return out
+
+    # -- mx block quantization ------------------------------------------------
+    def mx_quantize(self, x, elem="float8_e4m3fn", axis=1):
+        """Return (codes, scale), both uint8.
+
+        x: [rows, n] fp16/bf16.  elem: 'float8_e4m3fn', 'float8_e5m2' or
+        'float4_e2m1x2' (codes [rows, n/2], two per byte, low nibble first).
+        axis 1: blocks of 32 along n, scale [rows, ceil(n/32)]; axis 0:
+        blocks of 32 along rows, scale [ceil(rows/32), n].
+        """
+        xa, xcode = _buffer(x)
+        if xa.ndim != 2:
+            raise ValueError("oracle: mx quantize x must be 2-D")
+        rows, n = (int(d) for d in xa.shape)
+        ecode = _BYTE_CODES[elem]
+        if ecode == F4E2M1 and n % 2:
+            raise ValueError("oracle: float4 codes need an even last dimension")
+        y = np.zeros((rows, n // 2 if ecode == F4E2M1 else n), np.uint8)
+        if axis == 1:
+            scale = np.empty((rows, (n + 31) // 32), np.uint8)
+        else:
+            scale = np.empty(((rows + 31) // 32, n), np.uint8)
+        self.lib.oracle_mx_quantize(_ptr(xa), xcode, rows, n, ecode, int(axis), _ptr(y),
+                                    _ptr(scale))
+        return y, scale
 
 
 _default: Optional[Oracle] = None

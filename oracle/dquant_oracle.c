@@ -1,6 +1,7 @@
 /*
  * dquant_oracle.c -- plain, slow, single-threaded CPU oracle for per-token
- * dynamic quantization, its AdaLayerNorm fusion and AntiQuantize.
+ * dynamic quantization, its AdaLayerNorm fusion, AntiQuantize and mx block
+ * quantization.
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may call, link or
  * load this file: it is used by tests/, by the smoke check and by the CPU
@@ -26,6 +27,9 @@
  *          PER_TENSOR / PER_CHANNEL / PER_TOKEN / PER_GROUP shapes, kDim),
  *          表1 (AntiQuantizeConfig), 表2 (AntiQuantizeParams), 表3 (dtype
  *          combinations), 调用示例 (the worked example).
+ *   [MX]   aclnnQuantBatchMatmulInplaceAdd, 计算公式 (mx量化: blocks of
+ *          gsK = 32 along K, FLOAT8_E8M0 block scales), the consumer whose
+ *          operands the mx block quantizer produces.
  *
  * Readings taken where the pages are silent or garbled are stated next to
  * the step that depends on them.
@@ -545,6 +549,153 @@ void oracle_antiquantize(const void* src, int src_dtype, int64_t m, int64_t n,
                 ((uint16_t*)dst)[i * n + j] = orc_f32_to_bf16(t);
             else
                 ((uint16_t*)dst)[i * n + j] = orc_f32_to_f16(t);
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* [MX] mx block quantization (producer of the mx operands)                  */
+/* ------------------------------------------------------------------------ */
+
+/* Parameters of an OCP element format: width in bits, fraction bits,
+ * exponent bias, the largest finite magnitude, and emax = floor(log2(largest
+ * finite)). */
+struct orc_elem_fmt {
+    int bits;
+    int mbits;
+    int bias;
+    double maxv;
+    int emax;
+};
+
+static struct orc_elem_fmt orc_fmt_of(int dtype)
+{
+    struct orc_elem_fmt f;
+    if (dtype == ORC_F8E4M3) {
+        f.bits = 8; f.mbits = 3; f.bias = 7; f.maxv = 448.0; f.emax = 8;     /* 1.75 * 2^8 */
+    } else if (dtype == ORC_F8E5M2) {
+        f.bits = 8; f.mbits = 2; f.bias = 15; f.maxv = 57344.0; f.emax = 15; /* 1.75 * 2^15 */
+    } else {
+        f.bits = 4; f.mbits = 1; f.bias = 1; f.maxv = 6.0; f.emax = 2;       /* 1.5 * 2^2 */
+    }
+    return f;
+}
+
+/* Encode a finite, non-negative magnitude a into the exponent and fraction
+ * fields of an element format: nearest representable value with ties to the
+ * even fraction, a result beyond the largest finite magnitude saturating to
+ * it.  Every step is exact in double (a is a binary32 value scaled by a power
+ * of two, and the quanta are powers of two). */
+static unsigned orc_encode_magnitude(double a, struct orc_elem_fmt f)
+{
+    if (a == 0.0)
+        return 0;
+    int emin = 1 - f.bias; /* exponent of the smallest normal */
+    int e;
+    frexp(a, &e);
+    int E = e - 1; /* a in [2^E, 2^(E+1)) */
+    if (E < emin)
+        E = emin; /* the subnormals share the smallest normal's quantum */
+    double q = nearbyint(ldexp(a, f.mbits - E)); /* a in quanta of 2^(E - mbits) */
+    double v = ldexp(q, E - f.mbits);            /* the rounded value */
+    if (v > f.maxv)
+        v = f.maxv;
+    if (v < ldexp(1.0, emin)) /* subnormal (or zero): exponent field 0 */
+        return (unsigned)ldexp(v, f.mbits - emin);
+    frexp(v, &e);
+    E = e - 1;
+    unsigned frac = (unsigned)(ldexp(v, f.mbits - E) - ldexp(1.0, f.mbits));
+    return ((unsigned)(E + f.bias) << f.mbits) | frac;
+}
+
+static void orc_store_code(void* y, int elem_dtype, int64_t i, unsigned code)
+{
+    if (elem_dtype == ORC_F4E2M1) {
+        uint8_t* b = (uint8_t*)y + i / 2;
+        if (i & 1)
+            *b = (uint8_t)((*b & 0x0F) | (code << 4));
+        else
+            *b = (uint8_t)((*b & 0xF0) | (code & 0x0F));
+    } else {
+        ((uint8_t*)y)[i] = (uint8_t)code;
+    }
+}
+
+/*
+ * mx block quantization: the producer of the operands that the mx formula of
+ * aclnnQuantBatchMatmulInplaceAdd (计算公式, mx量化) consumes.  That formula
+ * multiplies, per block of gsK = 32 consecutive elements along the
+ * contraction axis (kLoops = ceil(K / 32) blocks, the last one possibly
+ * shorter), the element codes by one FLOAT8_E8M0 scale per block: scale1[m, j]
+ * for x1 [M, K], scale2[j, n] for x2 [K, N].  The pages print no producer.
+ * Reading (the OCP Microscaling Formats v1.0 conversion, section 6.3): per
+ * block,
+ *     shared = floor(log2(max |v|)) - emax(element format),
+ *              clamped to the e8m0 range [-127, 127];
+ *     scale code = shared + 127;
+ *     code_i = nearest element value to v_i / 2^shared, ties to even,
+ *              saturating at the largest finite element magnitude, the sign
+ *              of v_i kept (also on a zero result).
+ * An all-zero block has max |v| = 0: floor(log2 0) = -inf clamps to -127
+ * (scale code 0) and every code is a zero of v's sign.  A block holding a NaN
+ * or an infinity gets the NaN scale 0xFF and all-zero codes (reading: the
+ * NaN scale makes the whole block NaN whatever its codes).
+ *
+ *   x          [rows, n] of x_dtype (F16 or BF16), row-major.
+ *   elem_dtype ORC_F8E4M3, ORC_F8E5M2 or ORC_F4E2M1 (n even; two codes per
+ *              byte along n, element 2k in the low nibble).
+ *   axis       1: blocks run along n (the x1 layout), scale [rows, ceil(n/32)];
+ *              0: blocks run along rows (the x2 layout), scale [ceil(rows/32), n].
+ *   y          codes, [rows, n] bytes (fp8) or [rows, n/2] bytes (fp4).
+ *   scale      e8m0 bytes.
+ */
+void oracle_mx_quantize(const void* x, int x_dtype, int64_t rows, int64_t n,
+                        int elem_dtype, int axis, void* y, uint8_t* scale)
+{
+    const int64_t gs = 32;
+    struct orc_elem_fmt f = orc_fmt_of(elem_dtype);
+    /* A block is (outer index o, block index j) and holds elements k = 0..31
+     * at (r, c) = axis 1 ? (o, j*32 + k) : (j*32 + k, o). */
+    int64_t outer = axis == 1 ? rows : n;
+    int64_t along = axis == 1 ? n : rows;
+    int64_t blocks = (along + gs - 1) / gs;
+    for (int64_t o = 0; o < outer; ++o) {
+        for (int64_t j = 0; j < blocks; ++j) {
+            int64_t len = along - j * gs < gs ? along - j * gs : gs;
+            double amax = 0.0;
+            int finite = 1;
+            for (int64_t k = 0; k < len; ++k) {
+                int64_t r = axis == 1 ? o : j * gs + k;
+                int64_t c = axis == 1 ? j * gs + k : o;
+                float v = load_as_f32(x, x_dtype, r * n + c);
+                if (!isfinite(v))
+                    finite = 0;
+                else if (fabs((double)v) > amax)
+                    amax = fabs((double)v);
+            }
+            int64_t si = axis == 1 ? o * blocks + j : j * n + o;
+            int shared = -127;
+            if (finite && amax > 0.0) {
+                int e;
+                frexp(amax, &e);
+                shared = (e - 1) - f.emax; /* floor(log2 amax) - emax */
+                if (shared < -127)
+                    shared = -127;
+                if (shared > 127)
+                    shared = 127;
+            }
+            scale[si] = finite ? (uint8_t)(shared + 127) : 0xFF;
+            for (int64_t k = 0; k < len; ++k) {
+                int64_t r = axis == 1 ? o : j * gs + k;
+                int64_t c = axis == 1 ? j * gs + k : o;
+                unsigned code = 0;
+                if (finite) {
+                    double t = ldexp((double)load_as_f32(x, x_dtype, r * n + c), -shared);
+                    unsigned sign = signbit(t) ? 1u << (f.bits - 1) : 0u;
+                    code = sign | orc_encode_magnitude(fabs(t), f);
+                }
+                orc_store_code(y, elem_dtype, r * n + c, code);
+            }
         }
     }
 }

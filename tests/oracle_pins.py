@@ -564,6 +564,266 @@ def pin_roundtrip_dq_asym_aq_token(orc):
 
 
 # ---------------------------------------------------------------------------
+# mx block quantization (aclnnQuantBatchMatmulInplaceAdd, 计算公式 mx量化,
+# read as the OCP Microscaling v1.0 conversion)
+# ---------------------------------------------------------------------------
+
+MX_KINDS = ("float8_e4m3fn", "float8_e5m2", "float4_e2m1x2")
+
+
+def _mx_table(kind):
+    """Values of every code of an element format, from torch's fp8 decoders
+    and the OCP E2M1 table (not from the oracle), NaN / inf marked
+    non-finite."""
+    if kind == "float4_e2m1x2":
+        return np.array(OCP_E2M1, np.float64)
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    dt = torch.float8_e4m3fn if kind == "float8_e4m3fn" else torch.float8_e5m2
+    return codes.view(dt).float().numpy().astype(np.float64)
+
+
+def _mx_brute(block, kind):
+    """Reference quantization of one block by search: the scale exponent is
+    the smallest k in [-127, 127] with max|v| < 2^(emax + 1 + k), emax being
+    the binade of the largest finite code; each code is the finite code of
+    v's sign nearest to v / 2^k (ties to the code with an even last bit).
+    Returns (scale byte, codes)."""
+    vals = _mx_table(kind)
+    fin = np.isfinite(vals)
+    emax = int(np.frexp(vals[fin].max())[1]) - 1
+    block = np.asarray(block, np.float64)
+    if not np.all(np.isfinite(block)):
+        return 0xFF, np.zeros(block.size, np.int64)
+    amax = np.abs(block).max()
+    k = next(k for k in range(-127, 128) if amax < 2.0 ** (emax + 1 + k))
+    t = block * 2.0 ** -k
+    codes = np.arange(vals.size)
+    out = []
+    for ti in t:
+        ok = fin & (np.signbit(vals) == np.signbit(ti))
+        d = np.where(ok, np.abs(vals - ti), np.inf)
+        best = codes[d == d.min()]
+        if best.size > 1:
+            best = best[best % 2 == 0]
+        assert best.size == 1
+        out.append(int(best[0]))
+    return k + 127, np.array(out)
+
+
+def _unpack_fp4(y):
+    y = np.asarray(y, np.uint8)
+    out = np.empty(y.shape[:-1] + (2 * y.shape[-1],), np.int64)
+    out[..., 0::2] = y & 0xF
+    out[..., 1::2] = y >> 4
+    return out
+
+
+def _mx_codes(y, kind):
+    return _unpack_fp4(y) if kind == "float4_e2m1x2" else np.asarray(y, np.int64)
+
+
+def pin_mx_worked_blocks(orc):
+    """Worked by hand.  Block [12, 3, -5, 0.5, 1.5, 0.75, -0, 9, 11, 7, 0...]:
+    max 12 has binade 3.  fp4 (emax 2): shared 1, scale byte 128, quotients
+    6, 1.5, -2.5, 0.25, 0.75, 0.375, -0, 4.5, 5.5, 3.5 -> codes 7, 3, 0xC
+    (2.5 ties to 2), 0 (0.25 ties to 0), 2 (0.75 ties to 1.0), 1, 8 (-0), 6
+    (4.5 -> 4), 7 (5.5 -> 6), 6 (3.5 ties to 4).  fp8 e4m3 (emax 8): shared
+    -5, byte 122, 12 x 32 = 384 = 1.5 x 2^8 -> 0x7C.  fp8 e5m2 (emax 15):
+    shared -12, byte 115, 12 x 4096 = 1.5 x 2^15 -> 0x7A."""
+    row = [12, 3, -5, 0.5, 1.5, 0.75, -0.0, 9, 11, 7] + [0.0] * 22
+    for mk in (_bf16, _f16):
+        x = mk([row])
+        y, s = orc.mx_quantize(x, "float4_e2m1x2")
+        assert s.tolist() == [[128]]
+        assert y[0, :5].tolist() == [0x37, 0x0C, 0x12, 0x68, 0x67] and not y[0, 5:].any()
+        y, s = orc.mx_quantize(x, "float8_e4m3fn")
+        assert s.tolist() == [[122]] and y[0, 0] == 0x7C and y[0, 6] == 0x80
+        y, s = orc.mx_quantize(x, "float8_e5m2")
+        assert s.tolist() == [[115]] and y[0, 0] == 0x7A and y[0, 6] == 0x80
+
+
+def _mx_random_blocks(rng, nblk, dtype):
+    """Blocks whose magnitudes span the input format: each block draws a
+    binade, normal values around it and a few zeros and sign flips."""
+    lo, hi = (-140, 120) if dtype == torch.bfloat16 else (-24, 15)
+    e = rng.integers(lo, hi, nblk)
+    v = rng.standard_normal((nblk, 32)) * np.exp2(e)[:, None]
+    v[rng.random((nblk, 32)) < 0.05] = 0.0
+    return torch.from_numpy(v.astype(np.float32)).to(dtype)
+
+
+def pin_mx_brute_force_nearest(orc):
+    """Random blocks over the whole input range, both input types, all three
+    element formats: scale bytes and codes equal the search in _mx_brute."""
+    rng = np.random.default_rng(61)
+    for dtype in (torch.bfloat16, torch.float16):
+        x = _mx_random_blocks(rng, 96, dtype).reshape(12, 256)
+        xv = x.float().numpy().astype(np.float64)
+        for kind in MX_KINDS:
+            y, s = orc.mx_quantize(x, kind)
+            c = _mx_codes(y, kind)
+            for r in range(12):
+                for j in range(8):
+                    ws, wc = _mx_brute(xv[r, 32 * j:32 * j + 32], kind)
+                    assert s[r, j] == ws, (kind, r, j)
+                    assert np.array_equal(c[r, 32 * j:32 * j + 32], wc), (kind, r, j)
+
+
+def pin_mx_ties_and_saturation(orc):
+    """Blocks built on the element grid: the first element is the largest
+    finite code times 2^k (so the scale byte is k + 127 for the format's
+    emax), the rest are midpoints between adjacent codes (ties, which go to
+    the even code) and values between the largest code and the next binade
+    (which saturate)."""
+    rng = np.random.default_rng(62)
+    for kind in MX_KINDS:
+        vals = _mx_table(kind)
+        fin = np.isfinite(vals) & ~np.signbit(vals)
+        pos = np.sort(vals[fin])
+        top = pos[-1]
+        emax = int(np.frexp(top)[1]) - 1
+        for k in (-20, 0, 7):
+            mids = (pos[:-1] + pos[1:]) / 2
+            pick = rng.choice(mids, 24)
+            over = top + (2.0 ** (emax + 1) - top) * (0.01 + 0.98 * rng.random(7))
+            blk = np.concatenate([[top], pick, over]) * rng.choice([-1.0, 1.0], 32)
+            x = torch.from_numpy((blk * 2.0 ** k)[None].astype(np.float32)).to(torch.bfloat16)
+            blk = x.float().numpy()[0].astype(np.float64) * 2.0 ** -k  # bf16-rounded
+            assert np.all(np.abs(blk[25:]) > top) and np.all(np.abs(blk) < 2.0 ** (emax + 1))
+            y, s = orc.mx_quantize(x, kind)
+            ws, wc = _mx_brute(blk * 2.0 ** k, kind)
+            assert s[0, 0] == ws == k + 127
+            assert np.array_equal(_mx_codes(y, kind)[0], wc)
+            got = vals[_mx_codes(y, kind)[0]]
+            assert np.all(np.abs(got[25:]) == top)  # saturated
+
+
+def pin_mx_fp8_matches_torch_cast(orc):
+    """For fp8 elements the code of v equals torch's float32 -> float8 cast of
+    v / 2^shared (a library rounding, nearest-even), wherever that quotient
+    is within the format's finite range."""
+    rng = np.random.default_rng(63)
+    x = _mx_random_blocks(rng, 256, torch.bfloat16).reshape(32, 256)
+    xv = x.float().numpy().astype(np.float64)
+    for kind, dt in (("float8_e4m3fn", torch.float8_e4m3fn), ("float8_e5m2", torch.float8_e5m2)):
+        y, s = orc.mx_quantize(x, kind)
+        q = xv.reshape(32, 8, 32) * np.exp2(127.0 - s.astype(np.float64))[:, :, None]
+        q = q.reshape(32, 256).astype(np.float32)
+        ref = torch.from_numpy(q).to(dt).view(torch.uint8).numpy()
+        ok = np.abs(q) <= torch.finfo(dt).max
+        assert ok.mean() > 0.9
+        assert np.array_equal(y[ok], ref[ok])
+
+
+def pin_mx_power_of_two_shift(orc):
+    """Scaling the input by 2^m adds m to every scale byte and leaves every
+    code unchanged, as long as no block's exponent leaves [-127, 127]."""
+    rng = np.random.default_rng(64)
+    v = rng.standard_normal((8, 96)) * np.exp2(rng.integers(-8, 8, (8, 1)))
+    x = torch.from_numpy(v.astype(np.float32)).to(torch.bfloat16)
+    for kind in MX_KINDS:
+        y0, s0 = orc.mx_quantize(x, kind)
+        for m in (-60, -1, 1, 60):
+            y1, s1 = orc.mx_quantize(x * 2.0 ** m, kind)
+            assert np.array_equal(y1, y0)
+            assert np.array_equal(s1.astype(int), s0.astype(int) + m)
+
+
+def pin_mx_roundtrip_through_antiquantize(orc):
+    """Producer against consumer: grid values (a code times 2^(e - 127), each
+    block holding one code of the top binade) decoded by the AntiQuantize
+    float4 path (PER_GROUP, groups of 32, e8m0 scale), or for fp8 by torch's
+    decoder, quantize back to the same codes and scale bytes."""
+    rng = np.random.default_rng(65)
+    rows, n = 6, 128
+    codes = rng.integers(0, 16, (rows, n)).astype(np.uint8)
+    codes[:, ::32] = rng.choice([6, 7, 14, 15], (rows, n // 32))  # top binade [4, 8)
+    sc = rng.integers(100, 150, (rows, n // 32)).astype(np.uint8)
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    d = orc.antiquantize(("float4_e2m1x2", packed), ("float8_e8m0", sc), None, "per_group",
+                         kdim=1, group_size=32, dst="bfloat16")
+    x = torch.from_numpy(d.view(np.int16).copy()).view(torch.bfloat16)
+    y, s = orc.mx_quantize(x, "float4_e2m1x2")
+    assert np.array_equal(s, sc)
+    # zero codes may come back as the other zero; compare values and signs
+    want = np.where(codes & 7, codes, codes & 8)
+    assert np.array_equal(_unpack_fp4(y), want)
+    for kind in ("float8_e4m3fn", "float8_e5m2"):
+        vals = _mx_table(kind)
+        fin = np.flatnonzero(np.isfinite(vals))
+        top = fin[np.frexp(np.abs(vals[fin]))[1] - 1 == np.frexp(np.nanmax(vals[fin]))[1] - 1]
+        c = rng.choice(fin, (rows, n))
+        c[:, ::32] = rng.choice(top, (rows, n // 32))
+        e = rng.integers(100, 150, (rows, n // 32))
+        v = vals[c] * np.exp2(np.repeat(e, 32, axis=1) - 127.0)
+        x = torch.from_numpy(v.astype(np.float32)).to(torch.bfloat16)
+        assert np.array_equal(x.float().numpy(), v.astype(np.float32))
+        y, s = orc.mx_quantize(x, kind)
+        assert np.array_equal(s.astype(np.int64), e)
+        back = vals[y.astype(np.int64)]
+        assert np.array_equal(back, vals[c])
+        assert np.array_equal(np.signbit(back), np.signbit(vals[c]))
+
+
+def pin_mx_special_blocks(orc):
+    """An all-zero block: scale byte 0 (the exponent clamps to -127), codes
+    are zeros of each element's sign.  A block with a NaN or an infinity:
+    scale byte 0xFF, all codes 0.  Tiny blocks: bf16 2^-130 has binade -130,
+    so e4m3's exponent -138 clamps to -127 and the quotient 2^-3 encodes as
+    0x20; fp16 2^-24 has exponent -32 and quotient 2^8 -> 0x78."""
+    z = _bf16([[0.0] * 16 + [-0.0] * 16])
+    for kind in MX_KINDS:
+        y, s = orc.mx_quantize(z, kind)
+        assert s.tolist() == [[0]]
+        c = _mx_codes(y, kind)[0]
+        sign = 0x8 if kind == "float4_e2m1x2" else 0x80
+        assert np.all(c[:16] == 0) and np.all(c[16:] == sign)
+    for bad in (float("nan"), float("inf"), float("-inf")):
+        x = _bf16([[1.0] * 32 + [bad] + [2.0] * 31])
+        for kind in MX_KINDS:
+            y, s = orc.mx_quantize(x, kind)
+            assert s[0, 1] == 0xFF and s[0, 0] != 0xFF
+            assert not _mx_codes(y, kind)[0, 32:].any()
+    y, s = orc.mx_quantize(_bf16([[2.0 ** -130] * 32]), "float8_e4m3fn")
+    assert s.tolist() == [[0]] and np.all(y == 0x20)
+    y, s = orc.mx_quantize(_f16([[2.0 ** -24] + [0.0] * 31]), "float8_e4m3fn")
+    assert s.tolist() == [[127 - 32]] and y[0, 0] == 0x78
+
+
+def pin_mx_short_block_and_axis(orc):
+    """n = 72: blocks [0, 32), [32, 64), [64, 72); the short block's scale
+    follows its own 8 elements.  Axis 0 (blocks down the rows) on x equals
+    axis 1 on x transposed, codes and scales transposed back."""
+    rng = np.random.default_rng(66)
+    v = rng.standard_normal((5, 72))
+    v[:, :64] *= 1000.0
+    x = torch.from_numpy(v.astype(np.float32)).to(torch.bfloat16)
+    xv = x.float().numpy().astype(np.float64)
+    for kind in MX_KINDS:
+        y, s = orc.mx_quantize(x, kind)
+        assert s.shape == (5, 3)
+        c = _mx_codes(y, kind)
+        for r in range(5):
+            ws, wc = _mx_brute(xv[r, 64:], kind)
+            assert s[r, 2] == ws and np.array_equal(c[r, 64:], wc)
+        xt = x.t().contiguous()  # [72, 5]; axis 0 -> blocks along 72
+        if kind != "float4_e2m1x2":
+            y0, s0 = orc.mx_quantize(xt, kind, axis=0)
+            assert s0.shape == (3, 5)
+            assert np.array_equal(s0, s.T) and np.array_equal(y0, y.T)
+    x2 = torch.from_numpy(rng.standard_normal((72, 6)).astype(np.float32)).to(torch.bfloat16)
+    y0, s0 = orc.mx_quantize(x2, "float4_e2m1x2", axis=0)
+    y1, s1 = orc.mx_quantize(x2.t().contiguous(), "float8_e4m3fn")
+    assert s0.shape == (3, 6) and np.array_equal(s0.astype(int), s1.T.astype(int) + 6)
+    xv2 = x2.float().numpy().astype(np.float64)
+    c0 = _unpack_fp4(y0)
+    for col in range(6):
+        for j in range(3):
+            ws, wc = _mx_brute(xv2[32 * j:32 * j + 32, col], "float4_e2m1x2")
+            assert s0[j, col] == ws and np.array_equal(c0[32 * j:32 * j + 32, col], wc)
+
+
+# ---------------------------------------------------------------------------
 # Element conversions against library routines
 # ---------------------------------------------------------------------------
 

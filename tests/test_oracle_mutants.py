@@ -67,6 +67,29 @@ MUTANTS = [
     ("e8m0_bias128", "return (float)ldexp(1.0, (int)b - 127);", "return (float)ldexp(1.0, (int)b - 128);"),
     ("bf16_widen_shift", "return bits_to_f32((uint32_t)h << 16);",
      "return bits_to_f32((uint32_t)h << 15);"),
+    ("mx_e4m3_emax_7", "f.maxv = 448.0; f.emax = 8;", "f.maxv = 448.0; f.emax = 7;"),
+    ("mx_e2m1_emax_3", "f.maxv = 6.0; f.emax = 2;", "f.maxv = 6.0; f.emax = 3;"),
+    ("mx_e5m2_saturates_to_inf", "f.maxv = 57344.0;", "f.maxv = 65536.0;"),
+    ("mx_ceil_log2", "shared = (e - 1) - f.emax;", "shared = e - f.emax;"),
+    ("mx_no_saturation", "if (v > f.maxv)\n        v = f.maxv;", "if (v > 2 * f.maxv)\n        v = f.maxv;"),
+    ("mx_round_half_away", "double q = nearbyint(ldexp(a, f.mbits - E));",
+     "double q = round(ldexp(a, f.mbits - E));"),
+    ("mx_subnormal_quantum", "if (E < emin)\n        E = emin;",
+     "if (E < emin - 1)\n        E = emin - 1;"),
+    ("mx_fp4_nibble_order", "uint8_t* b = (uint8_t*)y + i / 2;\n        if (i & 1)",
+     "uint8_t* b = (uint8_t*)y + i / 2;\n        if (!(i & 1))"),
+    ("mx_clamp_fp32_min", "if (shared < -127)\n                    shared = -127;",
+     "if (shared < -126)\n                    shared = -126;"),
+    ("mx_inf_not_flagged", "if (!isfinite(v))\n                    finite = 0;",
+     "if (isnan(v))\n                    finite = 0;"),
+    ("mx_zero_sign_dropped", "unsigned sign = signbit(t) ? 1u << (f.bits - 1) : 0u;",
+     "unsigned sign = t < 0 ? 1u << (f.bits - 1) : 0u;"),
+    ("mx_scale_floor_count", "int64_t si = axis == 1 ? o * blocks + j : j * n + o;",
+     "int64_t si = axis == 1 ? o * (along / gs) + j : j * n + o;"),
+    ("mx_axis0_scale_index", "int64_t si = axis == 1 ? o * blocks + j : j * n + o;",
+     "int64_t si = axis == 1 ? o * blocks + j : o * blocks + j;"),
+    ("mx_amax_signed", "else if (fabs((double)v) > amax)\n                    amax = fabs((double)v);",
+     "else if ((double)v > amax)\n                    amax = (double)v;"),
 ]
 
 
