@@ -14,7 +14,8 @@ the previous one.  Every launch in the timed region is bracketed by HIP
 events on the stream it runs on; "roofline.achieved" is the algorithmic
 bytes of one launch over the mean event-measured launch time.  The other
 workloads (MoE asymmetric INT8/INT4, AdaLayerNorm-quant, AntiQuantize in
-every policy, the tiny fp16 case) are measured the same way and reported
+every policy, mx block quantization, the tiny fp16 case) are measured the
+same way and reported
 under "workloads"; a plain device copy gives the achievable-bandwidth
 ceiling.  "cpu_baseline" is the single-threaded CPU oracle timed on the
 host over a bounded sample of the same workload.
@@ -94,6 +95,15 @@ class Work:
                                               ("scale", "shift", "weight", "bias", "smooth"))
                               + B * S * H + B * S * 4)
             per_set = nbytes(x) + B * S * H
+        elif op == "mx_quantize":
+            x = host["x"]
+            rows, n = x.shape
+            self.rows = rows
+            fp4 = host["elem"] == "float4_e2m1x2"
+            ybytes = rows * n // 2 if fp4 else rows * n
+            sshape = dq.mx_scale_shape(rows, n, host["axis"])
+            self.alg_bytes = nbytes(x) + ybytes + sshape[0] * sshape[1]
+            per_set = nbytes(x) + ybytes
         else:
             src = host["src"]
             m, n = src.shape
@@ -137,6 +147,17 @@ class Work:
                 out = torch.empty(x.shape, dtype=torch.int8, device=dev)
                 qs = torch.empty((B, S), dtype=torch.float32, device=dev)
                 self.bufs.append((x, p, out, qs))
+        elif self.op == "mx_quantize":
+            xd = h["x"].to(dev)
+            rows, n = xd.shape
+            fp4 = h["elem"] == "float4_e2m1x2"
+            for i in range(self.sets):
+                x = xd if i == 0 else xd.clone()
+                y = torch.empty((rows, n // 2 if fp4 else n), dtype=torch.uint8, device=dev)
+                y = y.view(torch.float4_e2m1fn_x2 if fp4 else getattr(torch, h["elem"]))
+                sc = torch.empty(dq.mx_scale_shape(rows, n, h["axis"]), dtype=torch.uint8,
+                                 device=dev).view(torch.float8_e8m0fnu)
+                self.bufs.append((x, y, sc))
         else:
             src0 = to_device(h["src"], dev)
             sc = to_device(h["scale"], dev)
@@ -159,6 +180,9 @@ class Work:
                 x, p, out, qs = b
                 self.calls.append(dq.dquant.prepare_ada_layernorm_quant(
                     x, p["scale"], p["shift"], p["weight"], p["bias"], p["smooth"], h["eps"], out, qs))
+            elif self.op == "mx_quantize":
+                x, y, sc = b
+                self.calls.append(dq.dquant.prepare_mx_quantize(x, h["axis"], y, sc))
             else:
                 src, sc, of, dst = b
                 self.calls.append(dq.dquant.prepare_antiquantize(src, sc, of, h["policy"], h["kdim"],

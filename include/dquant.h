@@ -1,6 +1,7 @@
 /*
  * dquant.h -- C ABI of libdquant: per-token dynamic quantization, its
- * AdaLayerNorm fusion and AntiQuantize on AMD MI355X (gfx950).
+ * AdaLayerNorm fusion, AntiQuantize and mx block quantization on AMD MI355X
+ * (gfx950).
  *
  * Calling convention (after the two-phase form of the aclnn host ops,
  * "Each operator has two calls": a get-workspace-size call that returns
@@ -228,6 +229,48 @@ dq_status dq_antiquantize_get_workspace_size(const dq_tensor* src, const dq_tens
                                              dq_executor** executor);
 dq_status dq_antiquantize(void* workspace, size_t workspace_size, dq_executor* executor,
                           hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * mx block quantization -- the producer of the block-scaled operands that
+ * the mx formula of aclnnQuantBatchMatmulInplaceAdd (计算公式, mx量化)
+ * consumes: one FLOAT8_E8M0 scale per block of gsK = 32 consecutive
+ * elements along the contraction axis, the last block possibly short.  The
+ * pages print only that consumer; the conversion is the OCP Microscaling
+ * v1.0 one.  Per block of elements v:
+ *   shared = floor(log2(max |v|)) - emax, clamped to [-127, 127]
+ *            (emax = 8 for F8E4M3, 15 for F8E5M2, 2 for F4E2M1)
+ *   scale  = shared + 127                         (E8M0 byte)
+ *   y_i    = the element value nearest to v_i / 2^shared, ties to even,
+ *            saturated to the largest finite magnitude (448, 57344, 6),
+ *            the sign of v_i kept also on a zero result.
+ * An all-zero block gets scale 0 and zero codes; a block holding a NaN or
+ * an infinity gets scale 0xFF (NaN) and all-zero codes.  Decoding
+ * y_i * 2^(scale - 127) -- AntiQuantize's float4 case, or the mx formula --
+ * gives back the nearest representable value of every element.
+ *
+ *   x      F16 or BF16, exactly 2-D [rows, n]; rows may be 0, n >= 1,
+ *          n < 2^31.
+ *   axis   1: blocks run along n (the x1 [M, K] layout of the mx formula):
+ *             scale [rows, ceil(n/32)], scale[r, j] covers x[r, 32j .. 32j+31].
+ *          0: blocks run down the rows (the x2 [K, N] layout): scale
+ *             [ceil(rows/32), n], scale[j, c] covers x[32j .. 32j+31, c].
+ *   y      F8E4M3 or F8E5M2 [rows, n] (one code per byte), or F4E2M1
+ *          [rows, n] (n even; two codes per byte along n, the even element
+ *          in the low nibble -- the layout AntiQuantize reads).
+ *   scale  E8M0, the shape given by axis.
+ *   No alignment is required.  The vector kernels are used when n % 8 == 0,
+ *   x is 16-byte aligned and y 8-byte (fp8) or 4-byte (fp4) aligned, and,
+ *   for axis 0, scale is 8-byte aligned; otherwise a generic kernel runs.
+ *   y and scale must not overlap x or each other.  Workspace size: 0.
+ * Errors: DQ_ERR_NULLPTR, DQ_ERR_DTYPE, DQ_ERR_SHAPE (ndim != 2, shapes,
+ *   n == 0, n >= 2^31, odd n for F4E2M1), DQ_ERR_PARAM (axis not 0 or 1),
+ *   DQ_ERR_OVERLAP.
+ * ------------------------------------------------------------------------ */
+dq_status dq_mx_quantize_get_workspace_size(const dq_tensor* x, int32_t axis, const dq_tensor* y,
+                                            const dq_tensor* scale, size_t* workspace_size,
+                                            dq_executor** executor);
+dq_status dq_mx_quantize(void* workspace, size_t workspace_size, dq_executor* executor,
+                         hipStream_t stream);
 
 /* Release an executor that was never passed to an execute call.  NULL is a
  * no-op. */

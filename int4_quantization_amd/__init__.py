@@ -1,5 +1,6 @@
 """libdquant for MI355X (gfx950): per-token dynamic quantization
-(DynamicQuantV2), its AdaLayerNorm fusion, and AntiQuantize.
+(DynamicQuantV2), its AdaLayerNorm fusion, AntiQuantize, and mx block
+quantization (e8m0 scales per 32 elements).
 
 The compute runs in hand-written HIP kernels inside ``libdquant.so``, reached
 through the C ABI declared in ``include/dquant.h``.  This package is the thin
@@ -20,7 +21,11 @@ from .dquant import (  # noqa: F401
     dq_dynamic_quant_get_workspace_size,
     dq_executor_destroy,
     dq_get_last_error,
+    dq_mx_quantize,
+    dq_mx_quantize_get_workspace_size,
     dynamic_quant,
     library,
     library_path,
+    mx_quantize,
+    mx_scale_shape,
 )

@@ -36,29 +36,6 @@ enum AqPolicyKind : int { PK_TENSOR = 0, PK_CHANNEL = 1, PK_TOKEN = 2, PK_GROUP_
 
 constexpr int kAqRowsPerThread = 8;  // PER_CHANNEL / PER_GROUP kDim = 0 (divides every groupSize)
 
-// floor(x / d) = (x * mult) >> shift for 0 <= x < 2^31, with
-// shift = 31 + ceil(log2 d) and mult = ceil(2^shift / d) (at most 2^32):
-// the round-up reciprocal of Granlund and Montgomery's division by
-// invariant integers.
-struct DivMagic {
-    uint64_t mult;
-    int shift;
-};
-
-DivMagic div_magic(uint64_t d)
-{
-    int l = 0;
-    while ((uint64_t{1} << l) < d)
-        ++l;
-    const unsigned __int128 num = static_cast<unsigned __int128>(1) << (31 + l);
-    return DivMagic{static_cast<uint64_t>((num + d - 1) / d), 31 + l};
-}
-
-__device__ __forceinline__ uint32_t div_by(uint32_t x, const DivMagic& m)
-{
-    return static_cast<uint32_t>((static_cast<uint64_t>(x) * m.mult) >> m.shift);
-}
-
 struct AqArgs {
     const void* src;
     const void* scale;

@@ -24,6 +24,32 @@ __device__ __forceinline__ int64_t xcd_block(int64_t bid, int64_t nb)
 }
 
 // ---------------------------------------------------------------------------
+// Division by a launch constant.
+// floor(x / d) = (x * mult) >> shift for 0 <= x < 2^31, with
+// shift = 31 + ceil(log2 d) and mult = ceil(2^shift / d) (at most 2^32):
+// the round-up reciprocal of Granlund and Montgomery's division by
+// invariant integers.
+struct DivMagic {
+    uint64_t mult;
+    int shift;
+};
+
+inline DivMagic div_magic(uint64_t d)
+{
+    int l = 0;
+    while ((uint64_t{1} << l) < d)
+        ++l;
+    const unsigned __int128 num = static_cast<unsigned __int128>(1) << (31 + l);
+    return DivMagic{static_cast<uint64_t>((num + d - 1) / d), 31 + l};
+}
+
+__device__ __forceinline__ uint32_t div_by(uint32_t x, const DivMagic& m)
+{
+    return static_cast<uint32_t>((static_cast<uint64_t>(x) * m.mult) >> m.shift);
+}
+
+
+// ---------------------------------------------------------------------------
 // Wave-wide reductions.  Lanes combine in a fixed butterfly: quad swaps and
 // row mirrors through DPP, the 16-lane swap through ds_swizzle, and the two
 // 32-lane halves through readlane.  Every lane ends with the same value and

@@ -82,11 +82,31 @@ struct AqPlan {
     void* dst;
 };
 
+// ---- mx block quantization ---------------------------------------------------
+enum MxElem : int { MX_E4M3 = 0, MX_E5M2 = 1, MX_E2M1 = 2 };
+enum MxVariant : int {
+    MX_VAR_ROW = 0,      // axis 1, 16-byte loads, four lanes per 32-element block
+    MX_VAR_COL = 1,      // axis 0, one lane per 8 columns of a 32-row block
+    MX_VAR_GENERIC = 2,  // any shape and alignment, one thread per block
+};
+
+struct MxPlan {
+    const void* x;
+    int x_type;  // XType
+    int64_t rows, n;
+    int elem;    // MxElem
+    int axis;    // 1: blocks along n; 0: blocks along rows
+    void* y;
+    uint8_t* scale;
+    int variant;
+};
+
 // Kernel launchers (defined in the .hip files).  They enqueue on `stream`
 // and return the launch status; they never synchronize.
 hipError_t launch_dynamic_quant(const DqPlan& p, hipStream_t stream);
 hipError_t launch_ada_layernorm_quant(const AdaPlan& p, hipStream_t stream);
 hipError_t launch_antiquantize(const AqPlan& p, hipStream_t stream);
+hipError_t launch_mx_quantize(const MxPlan& p, hipStream_t stream);
 hipError_t launch_copy_probe(void* dst, const void* src, size_t bytes, hipStream_t stream);
 
 // DynamicQuant vector variant: waves per workgroup (the largest team), the

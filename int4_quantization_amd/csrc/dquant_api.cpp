@@ -15,13 +15,14 @@
 
 #include "dq_internal.h"
 
-enum ExecOp : int { OP_DYNAMIC_QUANT = 1, OP_ADA_LAYERNORM_QUANT = 2, OP_ANTIQUANTIZE = 3 };
+enum ExecOp : int { OP_DYNAMIC_QUANT = 1, OP_ADA_LAYERNORM_QUANT = 2, OP_ANTIQUANTIZE = 3, OP_MX_QUANTIZE = 4 };
 
 struct dq_executor {
     int op;
     dq::DqPlan dq;
     dq::AdaPlan ada;
     dq::AqPlan aq;
+    dq::MxPlan mx;
 };
 
 namespace {
@@ -582,6 +583,99 @@ dq_status dq_antiquantize(void* workspace, size_t workspace_size, dq_executor* e
     hipError_t err = dq::launch_antiquantize(p, stream);
     if (err != hipSuccess)
         return fail(DQ_ERR_RUNTIME, "antiquantize launch failed: %s", hipGetErrorString(err));
+    return ok();
+}
+
+// ---------------------------------------------------------------------------
+// mx block quantization
+// ---------------------------------------------------------------------------
+dq_status dq_mx_quantize_get_workspace_size(const dq_tensor* x, int32_t axis, const dq_tensor* y,
+                                            const dq_tensor* scale, size_t* workspace_size,
+                                            dq_executor** executor)
+{
+    if (!workspace_size || !executor)
+        return fail(DQ_ERR_NULLPTR, "workspace_size and executor must not be NULL");
+    *executor = nullptr;
+    *workspace_size = 0;
+    dq_status st;
+    int64_t nx = 0, ny = 0, ns = 0;
+    if ((st = check_tensor(x, "x", &nx)) != DQ_SUCCESS) return st;
+    if ((st = check_tensor(y, "y", &ny)) != DQ_SUCCESS) return st;
+    if ((st = check_tensor(scale, "scale", &ns)) != DQ_SUCCESS) return st;
+    if (x->dtype != DQ_F16 && x->dtype != DQ_BF16)
+        return fail(DQ_ERR_DTYPE, "x must be F16 or BF16, got %s", dtype_name(x->dtype));
+    if (y->dtype != DQ_F8E4M3 && y->dtype != DQ_F8E5M2 && y->dtype != DQ_F4E2M1)
+        return fail(DQ_ERR_DTYPE, "y must be F8E4M3, F8E5M2 or F4E2M1, got %s", dtype_name(y->dtype));
+    if (scale->dtype != DQ_E8M0)
+        return fail(DQ_ERR_DTYPE, "scale must be E8M0, got %s", dtype_name(scale->dtype));
+    if (axis != 0 && axis != 1)
+        return fail(DQ_ERR_PARAM, "axis must be 0 or 1, got %d", axis);
+    if (x->ndim != 2)
+        return fail(DQ_ERR_SHAPE, "x must be 2-D [rows, n], got ndim %d", x->ndim);
+    const int64_t rows = x->dims[0], n = x->dims[1];
+    if (n < 1 || n > dq::kMaxGridBlocks)
+        return fail(DQ_ERR_SHAPE, "the last dimension of x must be in [1, 2^31 - 1], got %lld", (long long)n);
+    const bool fp4 = y->dtype == DQ_F4E2M1;
+    if (fp4 && n % 2 != 0)
+        return fail(DQ_ERR_SHAPE, "F4E2M1 codes need an even last dimension, got %lld", (long long)n);
+    if (!same_dims(y, x->dims, 2))
+        return fail(DQ_ERR_SHAPE, "y must have the shape of x");
+    const int64_t blk = 32;
+    const bool scale_ok = axis == 1 ? is_shape(scale, {rows, (n + blk - 1) / blk})
+                                    : is_shape(scale, {(rows + blk - 1) / blk, n});
+    if (!scale_ok)
+        return fail(DQ_ERR_SHAPE, axis == 1 ? "scale must be [rows, ceil(n/32)]" : "scale must be [ceil(rows/32), n]");
+
+    if (nx > 0) {
+        const uintptr_t x0 = reinterpret_cast<uintptr_t>(x->data), x1 = x0 + static_cast<uintptr_t>(nx) * 2;
+        const uintptr_t y0 = reinterpret_cast<uintptr_t>(y->data);
+        const uintptr_t y1 = y0 + static_cast<uintptr_t>(fp4 ? nx / 2 : nx);
+        const uintptr_t s0 = reinterpret_cast<uintptr_t>(scale->data), s1 = s0 + static_cast<uintptr_t>(ns);
+        if ((x0 < y1 && y0 < x1) || (x0 < s1 && s0 < x1) || (y0 < s1 && s0 < y1))
+            return fail(DQ_ERR_OVERLAP, "x, y and scale must not overlap");
+    }
+
+    dq_executor* e = new_executor(OP_MX_QUANTIZE);
+    if (!e)
+        return fail(DQ_ERR_RUNTIME, "out of host memory");
+    dq::MxPlan& p = e->mx;
+    p.x = x->data;
+    p.x_type = x->dtype == DQ_BF16 ? dq::X_BF16 : dq::X_F16;
+    p.rows = rows;
+    p.n = n;
+    p.elem = y->dtype == DQ_F8E4M3 ? dq::MX_E4M3 : y->dtype == DQ_F8E5M2 ? dq::MX_E5M2 : dq::MX_E2M1;
+    p.axis = axis;
+    p.y = y->data;
+    p.scale = static_cast<uint8_t*>(scale->data);
+    const bool vec = n % 8 == 0 && aligned(x->data, 16) && aligned(y->data, fp4 ? 4 : 8);
+    if (vec && axis == 1)
+        p.variant = dq::MX_VAR_ROW;
+    else if (vec && aligned(scale->data, 8))
+        p.variant = dq::MX_VAR_COL;
+    else
+        p.variant = dq::MX_VAR_GENERIC;
+    *executor = e;
+    return ok();
+}
+
+dq_status dq_mx_quantize(void* workspace, size_t workspace_size, dq_executor* executor, hipStream_t stream)
+{
+    (void)workspace;
+    (void)workspace_size;
+    if (!executor)
+        return fail(DQ_ERR_NULLPTR, "executor is NULL");
+    dq_executor* e = executor;
+    if (e->op != OP_MX_QUANTIZE) {
+        delete e;
+        return fail(DQ_ERR_PARAM, "executor was not made by dq_mx_quantize_get_workspace_size");
+    }
+    dq::MxPlan p = e->mx;
+    delete e;
+    if (p.rows == 0)
+        return ok();
+    hipError_t err = dq::launch_mx_quantize(p, stream);
+    if (err != hipSuccess)
+        return fail(DQ_ERR_RUNTIME, "mx quantize launch failed: %s", hipGetErrorString(err));
     return ok();
 }
 

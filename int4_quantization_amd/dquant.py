@@ -38,6 +38,7 @@ EXPORTS = [
     "dq_dynamic_quant_get_workspace_size", "dq_dynamic_quant",
     "dq_ada_layernorm_quant_get_workspace_size", "dq_ada_layernorm_quant",
     "dq_antiquantize_get_workspace_size", "dq_antiquantize",
+    "dq_mx_quantize_get_workspace_size", "dq_mx_quantize",
     "dq_executor_destroy", "dq_get_last_error", "dq_copy_probe",
 ]
 
@@ -80,7 +81,11 @@ def library() -> ctypes.CDLL:
             _P(DqTensor), _P(DqTensor), _P(DqTensor), ctypes.c_int, ctypes.c_int32, ctypes.c_uint32,
             _P(DqTensor), _P(ctypes.c_size_t), _P(_vp)]
         lib.dq_antiquantize_get_workspace_size.restype = st
-        for name in ("dq_dynamic_quant", "dq_ada_layernorm_quant", "dq_antiquantize"):
+        lib.dq_mx_quantize_get_workspace_size.argtypes = [
+            _P(DqTensor), ctypes.c_int32, _P(DqTensor), _P(DqTensor), _P(ctypes.c_size_t), _P(_vp)]
+        lib.dq_mx_quantize_get_workspace_size.restype = st
+        for name in ("dq_dynamic_quant", "dq_ada_layernorm_quant", "dq_antiquantize",
+                     "dq_mx_quantize"):
             fn = getattr(lib, name)
             fn.argtypes = [_vp, ctypes.c_size_t, _vp, _vp]
             fn.restype = st
@@ -215,6 +220,21 @@ def dq_antiquantize(workspace, workspace_size: int, executor: int, stream=None) 
                                      _stream_handle(stream)))
 
 
+def dq_mx_quantize_get_workspace_size(x, axis: int, y, scale) -> Tuple[int, int]:
+    lib = library()
+    d = [tensor_desc(t) for t in (x, y, scale)]
+    ws = ctypes.c_size_t(0)
+    ex = _vp(None)
+    _check(lib.dq_mx_quantize_get_workspace_size(_ref(d[0]), int(axis), _ref(d[1]), _ref(d[2]),
+                                                 ctypes.byref(ws), ctypes.byref(ex)))
+    return ws.value, ex.value
+
+
+def dq_mx_quantize(workspace, workspace_size: int, executor: int, stream=None) -> None:
+    _check(library().dq_mx_quantize(_ws_ptr(workspace), workspace_size, executor,
+                                    _stream_handle(stream)))
+
+
 def dq_executor_destroy(executor: int) -> None:
     library().dq_executor_destroy(executor)
 
@@ -296,6 +316,14 @@ def prepare_antiquantize(src, scale, offset, policy, k_dim: int, group_size: int
                         (d, src, scale, offset, dst))
 
 
+def prepare_mx_quantize(x, axis: int, y, scale) -> PreparedCall:
+    lib = library()
+    d = [tensor_desc(t) for t in (x, y, scale)]
+    args = [_ref(d[0]), int(axis), _ref(d[1]), _ref(d[2])]
+    return PreparedCall(lib.dq_mx_quantize_get_workspace_size, lib.dq_mx_quantize, args,
+                        (d, x, y, scale))
+
+
 # -- convenience wrappers ------------------------------------------------------
 
 def dynamic_quant(x: torch.Tensor, smooth_scales: Optional[torch.Tensor] = None,
@@ -352,3 +380,27 @@ def antiquantize(src: torch.Tensor, scale: torch.Tensor, offset: Optional[torch.
     ws, ex = dq_antiquantize_get_workspace_size(src, scale, offset, policy, k_dim, group_size, dst)
     dq_antiquantize(_workspace(ws, src.device), ws, ex, stream)
     return dst
+
+
+def mx_scale_shape(rows: int, n: int, axis: int = 1) -> Tuple[int, int]:
+    """Shape of the e8m0 scale of an mx-quantized [rows, n] tensor."""
+    return (rows, (n + 31) // 32) if axis == 1 else ((rows + 31) // 32, n)
+
+
+def mx_quantize(x: torch.Tensor, elem: torch.dtype = torch.float8_e4m3fn, axis: int = 1,
+                stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """mx block quantization of x [rows, n] (float16 / bfloat16): returns
+    (codes, scale).  elem: torch.float8_e4m3fn or torch.float8_e5m2 (codes
+    [rows, n]) or torch.float4_e2m1fn_x2 (codes [rows, n/2], two per byte,
+    the even element in the low nibble).  scale: float8_e8m0fnu, one per
+    block of 32 along n (axis 1) or down the rows (axis 0)."""
+    rows, n = x.shape
+    if elem == torch.float4_e2m1fn_x2:
+        y = torch.empty((rows, n // 2), dtype=torch.uint8, device=x.device).view(elem)
+    else:
+        y = torch.empty((rows, n), dtype=elem, device=x.device)
+    scale = torch.empty(mx_scale_shape(rows, n, axis), dtype=torch.uint8,
+                        device=x.device).view(torch.float8_e8m0fnu)
+    ws, ex = dq_mx_quantize_get_workspace_size(x, axis, y, scale)
+    dq_mx_quantize(_workspace(ws, x.device), ws, ex, stream)
+    return y, scale

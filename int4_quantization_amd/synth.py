@@ -22,6 +22,11 @@ tests use (rows x columns):
                                     scale / offset (a 表3 combination)
 * ``aq_per_group_fp4e2m1_e8m0_16384x8192``  the float4 case: fp4 e2m1 codes,
                                     e8m0 scales per 32 columns, no offset
+* ``mx_{e4m3,e2m1}_bf16_8192x7168``  mx block quantization of an activation
+                                    [M, K] (x as in the 8192x7168 DynamicQuant
+                                    workload), blocks of 32 along K
+* ``mx_e4m3_axis0_bf16_7168x8192``  mx block quantization of a weight [K, N],
+                                    blocks of 32 down K
 """
 from __future__ import annotations
 
@@ -141,6 +146,33 @@ def aq_inputs(m: int, n: int, policy: str, seed: int, *, src: str = "int8", kdim
             "group_size": gs}
 
 
+MX_ELEMS = ("float8_e4m3fn", "float8_e5m2", "float4_e2m1x2")
+
+
+def mx_inputs(rows: int, n: int, seed: int, *, dtype: str = "bfloat16",
+              elem: str = "float8_e4m3fn", axis: int = 1, outlier_frac: float = 0.001,
+              spread: int = 0) -> Dict[str, object]:
+    """Inputs of one mx block quantization call.
+
+    Draw order: x ~ N(0, 1) [rows, n]; if outlier_frac > 0: positions
+    (without replacement), signs, magnitudes U(20, 60) as in dq_inputs; if
+    spread > 0: one exponent per row ~ U{-spread, .., spread} multiplying
+    the row by 2^e (blocks of very different magnitudes).
+    """
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((rows, n), dtype=np.float32)
+    if outlier_frac > 0.0 and rows * n > 0:
+        k = int(round(rows * n * outlier_frac))
+        pos = rng.choice(rows * n, size=k, replace=False)
+        sign = rng.integers(0, 2, size=k).astype(np.float32) * 2.0 - 1.0
+        mag = rng.uniform(20.0, 60.0, size=k).astype(np.float32)
+        x.reshape(-1)[pos] = sign * mag
+    if spread > 0:
+        e = rng.integers(-spread, spread + 1, size=(rows, 1))
+        x = x * np.exp2(e).astype(np.float32)
+    return {"x": _narrow(x, dtype), "elem": elem, "axis": axis}
+
+
 # Full-size workloads: name -> (op, builder).
 WORKLOADS = {
     "dq_sym_f16_64x256": (
@@ -177,4 +209,10 @@ WORKLOADS = {
     "aq_per_group_fp4e2m1_e8m0_16384x8192": (
         "antiquantize",
         lambda: aq_inputs(16384, 8192, "per_group", 8, src="float4_e2m1", group_size=32)),
+    "mx_e4m3_bf16_8192x7168": (
+        "mx_quantize", lambda: mx_inputs(8192, 7168, 9, elem="float8_e4m3fn")),
+    "mx_e2m1_bf16_8192x7168": (
+        "mx_quantize", lambda: mx_inputs(8192, 7168, 9, elem="float4_e2m1x2")),
+    "mx_e4m3_axis0_bf16_7168x8192": (
+        "mx_quantize", lambda: mx_inputs(7168, 8192, 10, elem="float8_e4m3fn", axis=0)),
 }

@@ -5,6 +5,7 @@ Bars:
 * DynamicQuant, AntiQuantize: bit-exact -- codes / packed bytes identical,
   scale / offset / dst bits identical (two NaNs compare equal: x86 and the
   GPU produce different default-NaN payloads).
+* mx block quantization: bit-exact codes and scale bytes.
 * AdaLayerNormQuant: |quantScale - ref| <= 1e-5 * ref, codes within +-1
   everywhere and different on at most 0.01 % of the elements (rounded up to
   a whole element for small cases).
@@ -129,3 +130,22 @@ def check_ada_layernorm_quant(orc, inp, dev_override=None):
     assert dmax <= 1, f"code difference {dmax} > 1"
     assert nflip <= allowed, f"{nflip} codes differ by 1 (allowed {allowed})"
     return out, qs, nflip
+
+
+MX_TORCH = {"float8_e4m3fn": torch.float8_e4m3fn, "float8_e5m2": torch.float8_e5m2,
+            "float4_e2m1x2": torch.float4_e2m1fn_x2}
+
+
+def check_mx_quantize(orc, x, kind, axis=1, x_dev=None):
+    """GPU codes and e8m0 scale bytes equal the oracle's, byte for byte.
+    x_dev: the device input to use instead of a fresh copy of x (for
+    unaligned views)."""
+    xd = to_dev(x) if x_dev is None else x_dev
+    y, s = dq.mx_quantize(xd, MX_TORCH[kind], axis)
+    torch.cuda.synchronize()
+    ry, rs = orc.mx_quantize(x, kind, axis)
+    gy = y.view(torch.uint8).cpu().numpy()
+    gs = s.view(torch.uint8).cpu().numpy()
+    assert gs.shape == rs.shape and gy.shape == ry.shape
+    assert np.array_equal(gs, rs), "scale: " + first_mismatch(gs, rs)
+    assert np.array_equal(gy, ry), "codes: " + first_mismatch(gy, ry)

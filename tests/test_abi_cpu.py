@@ -291,6 +291,65 @@ def test_antiquantize_channel_params_alignment(lib):
     assert aq_ws(lib, src, desc(D.F32, [M, 1], 0x20004), None, 2, 1, 0, dst) == D.SUCCESS
 
 
+# ---- mx block quantization ----------------------------------------------------
+
+def mx_ws(lib, x, axis, y, sc):
+    ws = ctypes.c_size_t(99)
+    ex = ctypes.c_void_p(None)
+    st = lib.dq_mx_quantize_get_workspace_size(ref(x), axis, ref(y), ref(sc), ctypes.byref(ws),
+                                               ctypes.byref(ex))
+    if st == D.SUCCESS:
+        assert ex.value and ws.value == 0
+        lib.dq_executor_destroy(ex)
+    else:
+        assert ex.value is None
+        assert lib.dq_get_last_error().decode() != ""
+    return st
+
+
+X_PTR, Y_PTR, S_PTR = 0x100000, 0x900000, 0xF00000
+
+
+@pytest.mark.parametrize("xdt,ydt,sdt,shape,axis,sshape,status", [
+    (D.BF16, D.F8E4M3, D.E8M0, [4, 64], 1, [4, 2], D.SUCCESS),
+    (D.F16, D.F8E5M2, D.E8M0, [4, 64], 1, [4, 2], D.SUCCESS),
+    (D.BF16, D.F4E2M1, D.E8M0, [4, 64], 1, [4, 2], D.SUCCESS),
+    (D.BF16, D.F8E4M3, D.E8M0, [4, 70], 1, [4, 3], D.SUCCESS),      # short last block
+    (D.BF16, D.F8E4M3, D.E8M0, [40, 6], 0, [2, 6], D.SUCCESS),      # axis 0
+    (D.BF16, D.F8E4M3, D.E8M0, [0, 64], 1, [0, 2], D.SUCCESS),      # no rows
+    (D.BF16, D.F4E2M1, D.E8M0, [4, 65], 1, [4, 3], D.ERR_SHAPE),    # fp4 needs even n
+    (D.BF16, D.F8E4M3, D.E8M0, [4, 64], 1, [4, 3], D.ERR_SHAPE),
+    (D.BF16, D.F8E4M3, D.E8M0, [40, 6], 0, [1, 6], D.ERR_SHAPE),
+    (D.BF16, D.F8E4M3, D.E8M0, [4, 0], 1, [4, 0], D.ERR_SHAPE),
+    (D.BF16, D.F8E4M3, D.E8M0, [4, 64], 2, [4, 2], D.ERR_PARAM),
+    (D.F32, D.F8E4M3, D.E8M0, [4, 64], 1, [4, 2], D.ERR_DTYPE),
+    (D.BF16, D.I8, D.E8M0, [4, 64], 1, [4, 2], D.ERR_DTYPE),
+    (D.BF16, D.F8E4M3, D.F32, [4, 64], 1, [4, 2], D.ERR_DTYPE),
+])
+def test_mx_quantize_validation(lib, xdt, ydt, sdt, shape, axis, sshape, status):
+    assert mx_ws(lib, desc(xdt, shape, X_PTR), axis, desc(ydt, shape, Y_PTR),
+                 desc(sdt, sshape, S_PTR)) == status
+
+
+def test_mx_quantize_rank_overlap_and_nulls(lib):
+    x = desc(D.BF16, [4, 64], X_PTR)
+    y = desc(D.F8E4M3, [4, 64], Y_PTR)
+    s = desc(D.E8M0, [4, 2], S_PTR)
+    assert mx_ws(lib, desc(D.BF16, [256], X_PTR), 1, desc(D.F8E4M3, [256], Y_PTR),
+                 desc(D.E8M0, [8], S_PTR)) == D.ERR_SHAPE
+    assert mx_ws(lib, x, 1, desc(D.F8E4M3, [4, 64], X_PTR + 100), s) == D.ERR_OVERLAP
+    assert mx_ws(lib, x, 1, y, desc(D.E8M0, [4, 2], Y_PTR + 255)) == D.ERR_OVERLAP
+    assert mx_ws(lib, x, 1, y, desc(D.E8M0, [4, 2], Y_PTR + 256)) == D.SUCCESS
+    assert mx_ws(lib, x, 1, desc(D.F8E4M3, [4, 64], 0), s) == D.ERR_NULLPTR
+    assert mx_ws(lib, None, 1, y, s) == D.ERR_NULLPTR
+    assert lib.dq_mx_quantize(None, 0, None, None) == D.ERR_NULLPTR
+
+
+def test_mx_binding_shapes():
+    assert D.mx_scale_shape(5, 70, 1) == (5, 3)
+    assert D.mx_scale_shape(70, 5, 0) == (3, 5)
+
+
 # ---- execute-phase errors that never reach the device -------------------------
 
 def test_execute_null_executor(lib):

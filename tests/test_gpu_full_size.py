@@ -1,14 +1,15 @@
 """Every benchmark workload at its full size, element by element, through the
 same C-ABI calls and launch configuration the benchmark times, against the
-CPU oracle: DynamicQuant and AntiQuantize bit-exact, AdaLayerNorm-quant at
-the stated tolerance.  Also: two launches give identical bits."""
+CPU oracle: DynamicQuant, AntiQuantize and mx block quantization bit-exact,
+AdaLayerNorm-quant at the stated tolerance.  Also: two launches give identical bits."""
 import numpy as np
 import pytest
 import torch
 
 import int4_quantization_amd as dq
 from int4_quantization_amd import synth
-from parity import DEV, announce, check_ada_layernorm_quant, check_antiquantize, check_dynamic_quant
+from parity import (DEV, announce, check_ada_layernorm_quant, check_antiquantize, check_dynamic_quant,
+                    check_mx_quantize)
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
@@ -24,6 +25,8 @@ def test_full_size_parity(orc, name):
     elif op == "ada_layernorm_quant":
         _, _, nflip = check_ada_layernorm_quant(orc, h)
         print(f"{name}: {nflip} of {h['x'].numel()} codes differ by 1", flush=True)
+    elif op == "mx_quantize":
+        check_mx_quantize(orc, h["x"], h["elem"], h["axis"])
     else:
         check_antiquantize(orc, h["src"], h["scale"], h["offset"], h["policy"], h["kdim"],
                            h["group_size"], torch.bfloat16)
