@@ -38,9 +38,10 @@
 //                      Each lane stores one scale byte per four vector slots,
 //                      and the wave's scale stores cover 64 consecutive bytes.
 //   mx_col_kernel      axis 0, last dimension a multiple of 8.  A lane holds
-//                      8 adjacent columns of one 32-row block: 32 16-byte
-//                      loads, an in-lane maximum per column, and 8 scale
-//                      bytes in one 8-byte store.
+//                      8 adjacent columns, and each wave of a workgroup a
+//                      slice of rows of one 32-row block: in-lane maxima per
+//                      column, combined across the waves through LDS, and 8
+//                      scale bytes per lane in one 8-byte store.
 //   mx_generic_kernel  any shape or alignment: one thread per block (axis 1)
 //                      or per block and column pair (axis 0), 2-byte loads.
 
@@ -52,6 +53,7 @@ namespace {
 
 constexpr int kMxBlock = 32;   // elements per scale block (gsK)
 constexpr int kMxRowVecs = 4;  // vector slots per lane in mx_row_kernel
+constexpr int kMxColRows = 8;  // rows per wave in mx_col_kernel (4 waves per 32-row block)
 constexpr int64_t kMaxGridY = 65535;
 
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
@@ -233,19 +235,26 @@ __global__ __launch_bounds__(kBlock) void mx_row_kernel(const MxRowArgs a)
         }
     }
 
-    // Lane (q, p) stores the scale byte of slot p: the wave's 64 stores cover
-    // units base .. base + 63.
-    static_assert(V == 4, "one scale byte per lane per four vector slots");
-    const uint32_t s = part == 0 ? sbyte[0] : part == 1 ? sbyte[1] : part == 2 ? sbyte[2] : sbyte[3];
-    uint32_t u = base + part * 16u + quad;
-    u = u < a.units ? u : a.units - 1;
-    __builtin_nontemporal_store(static_cast<uint8_t>(s), a.scale + u);
+    // Lane (q, p) stores the scale bytes of slots p, p + 4, ...: each store
+    // instruction of the wave covers 64 consecutive units.
+    static_assert(V % 4 == 0, "one scale byte per lane per four vector slots");
+#pragma unroll
+    for (int h = 0; h < V / 4; ++h) {
+        const uint32_t s = part == 0 ? sbyte[4 * h] : part == 1 ? sbyte[4 * h + 1]
+                         : part == 2 ? sbyte[4 * h + 2] : sbyte[4 * h + 3];
+        uint32_t u = base + (4 * h + part) * 16u + quad;
+        u = u < a.units ? u : a.units - 1;
+        __builtin_nontemporal_store(static_cast<uint8_t>(s), a.scale + u);
+    }
 }
 
 // ---------------------------------------------------------------------------
-// Axis 0, vectors.  Thread (x: column vector, y: 32-row block) holds columns
-// 8cv .. 8cv + 7 of rows 32jb .. 32jb + 31.  Rows past the end repeat the
-// last row (the maximum is unchanged and the stores repeat identical bytes).
+// Axis 0, vectors.  A workgroup holds 64 adjacent column vectors (8 columns
+// each) of one 32-row block; wave w holds rows w*R .. w*R + R - 1, so every
+// load and store of a wave covers 1 KB (or its code bytes) of one row.  The
+// waves combine their per-column maxima through LDS.  Rows past the end
+// repeat the last row: the maximum is unchanged and the stores repeat
+// identical bytes.
 // ---------------------------------------------------------------------------
 struct MxColArgs {
     const uint16_t* x;
@@ -256,25 +265,39 @@ struct MxColArgs {
     uint32_t nvec;
 };
 
-template <int XT, int ELEM>
-__global__ __launch_bounds__(kBlock) void mx_col_kernel(const MxColArgs a)
+template <int XT, int ELEM, int R>
+__global__ __launch_bounds__(kMxBlock / R * kWave) void mx_col_kernel(const MxColArgs a)
 {
-    const uint32_t cv0 = blockIdx.x * kBlock + threadIdx.x;
+    constexpr int W = kMxBlock / R;  // waves per workgroup
+    __shared__ uint32_t part[W][4][kWave];
+    const uint32_t lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+    const uint32_t cv0 = blockIdx.x * kWave + lane;
     const int64_t col = static_cast<int64_t>(cv0 < a.nvec ? cv0 : a.nvec - 1) * 8;
-    const int64_t r0 = static_cast<int64_t>(blockIdx.y) * kMxBlock;
-    uint4 raw[kMxBlock];
+    const int64_t r0 = static_cast<int64_t>(blockIdx.y) * kMxBlock + w * R;
+    uint4 raw[R];
 #pragma unroll
-    for (int k = 0; k < kMxBlock; ++k) {
+    for (int k = 0; k < R; ++k) {
         const int64_t r = r0 + k < a.rows ? r0 + k : a.rows - 1;
         raw[k] = ld_stream16(a.x + r * a.n + col);
     }
     uint32_t acc[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int k = 0; k < kMxBlock; ++k) {
+    for (int k = 0; k < R; ++k) {
         acc[0] = max_u16x2(acc[0], abs2(raw[k].x));
         acc[1] = max_u16x2(acc[1], abs2(raw[k].y));
         acc[2] = max_u16x2(acc[2], abs2(raw[k].z));
         acc[3] = max_u16x2(acc[3], abs2(raw[k].w));
+    }
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+        part[w][d][lane] = acc[d];
+    __syncthreads();
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        acc[d] = part[0][d][lane];
+#pragma unroll
+        for (int q = 1; q < W; ++q)
+            acc[d] = max_u16x2(acc[d], part[q][d][lane]);
     }
     uint32_t c[8];
     float inv[8];
@@ -283,7 +306,7 @@ __global__ __launch_bounds__(kBlock) void mx_col_kernel(const MxColArgs a)
         c[2 * d] = mx_scale_byte<XT, ELEM>(acc[d] & 0xFFFFu);
         c[2 * d + 1] = mx_scale_byte<XT, ELEM>(acc[d] >> 16);
     }
-    uint2 keep;  // per-column code masks: zero for a NaN-scale column
+    uint2 keep;
     if constexpr (ELEM == MX_E2M1) {
         keep.x = 0;
 #pragma unroll
@@ -301,10 +324,13 @@ __global__ __launch_bounds__(kBlock) void mx_col_kernel(const MxColArgs a)
 #pragma unroll
     for (int i = 0; i < 8; ++i)
         inv[i] = mx_inv_scale(c[i]);
-    const uint2 sb = make_uint2(c[0] | c[1] << 8 | c[2] << 16 | c[3] << 24, c[4] | c[5] << 8 | c[6] << 16 | c[7] << 24);
-    st_stream8(a.scale + static_cast<int64_t>(blockIdx.y) * a.n + col, sb);
+    if (w == 0) {
+        const uint2 sb = make_uint2(c[0] | c[1] << 8 | c[2] << 16 | c[3] << 24,
+                                    c[4] | c[5] << 8 | c[6] << 16 | c[7] << 24);
+        st_stream8(a.scale + static_cast<int64_t>(blockIdx.y) * a.n + col, sb);
+    }
 #pragma unroll
-    for (int k = 0; k < kMxBlock; ++k) {
+    for (int k = 0; k < R; ++k) {
         const int64_t r = r0 + k < a.rows ? r0 + k : a.rows - 1;
         float t[8];
         widen8<XT>(raw[k], t);
@@ -443,7 +469,8 @@ hipError_t launch_typed(const MxPlan& p, hipStream_t stream)
     }
     if (p.variant == MX_VAR_COL) {
         const int64_t nvec = p.n / 8;
-        const int64_t gx = (nvec + kBlock - 1) / kBlock;
+        const int64_t per_block = kWave;  // column vectors per workgroup
+        const int64_t gx = (nvec + per_block - 1) / per_block;
         const int64_t nbr = (p.rows + kMxBlock - 1) / kMxBlock;
         for (int64_t j0 = 0; j0 < nbr; j0 += kMaxGridY) {
             const int64_t jc = nbr - j0 < kMaxGridY ? nbr - j0 : kMaxGridY;
@@ -455,8 +482,8 @@ hipError_t launch_typed(const MxPlan& p, hipStream_t stream)
             a.rows = p.rows - r0 < jc * kMxBlock ? p.rows - r0 : jc * kMxBlock;
             a.n = p.n;
             a.nvec = static_cast<uint32_t>(nvec);
-            hipLaunchKernelGGL((mx_col_kernel<XT, ELEM>), dim3(static_cast<uint32_t>(gx), static_cast<uint32_t>(jc)),
-                               dim3(kBlock), 0, stream, a);
+            hipLaunchKernelGGL((mx_col_kernel<XT, ELEM, kMxColRows>), dim3(static_cast<uint32_t>(gx), static_cast<uint32_t>(jc)),
+                               dim3(kMxBlock / kMxColRows * kWave), 0, stream, a);
             const hipError_t err = hipGetLastError();
             if (err != hipSuccess)
                 return err;
