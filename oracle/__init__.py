@@ -1,5 +1,6 @@
 """CPU oracle for per-token dynamic quantization, AdaLayerNorm-quant,
-AntiQuantize and mx block quantization -- TEST INFRASTRUCTURE ONLY.
+AntiQuantize, mx block quantization and the weight-quantized matmul -- TEST
+INFRASTRUCTURE ONLY.
 
 Only ``tests/``, the smoke check in ``__graft_entry__`` and the CPU-baseline
 leg of ``bench.py`` may import this package.  The product path (the HIP
@@ -16,6 +17,8 @@ the passage of the pages it follows:
 * ``antiquantize``            -- AntiQuantize, 功能说明 / 表1-表3.
 * ``mx_quantize``             -- aclnnQuantBatchMatmulInplaceAdd, 计算公式
   (mx量化), read as the OCP Microscaling v1.0 conversion.
+* ``weight_dequant`` / ``weight_quant_matmul`` -- aclnnWeightQuantMatmulAllReduce
+  on one rank (API function, constraints).
 """
 from __future__ import annotations
 
@@ -74,6 +77,14 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_antiquantize.restype = None
     lib.oracle_mx_quantize.argtypes = [_vp, _int, _i64, _i64, _int, _int, _vp, _vp]
     lib.oracle_mx_quantize.restype = None
+    lib.oracle_weight_dequant.argtypes = [_vp, _int, _i64, _i64, _int, _vp, _vp, _int, _int,
+                                          _i64, _vp]
+    lib.oracle_weight_dequant.restype = None
+    lib.oracle_weight_quant_matmul.argtypes = [_vp, _int, _i64, _i64, _i64, _vp, _vp, _vp, _vp,
+                                               _vp]
+    lib.oracle_weight_quant_matmul.restype = None
+    lib.orc_convert_f64_to_half.argtypes = [_vp, _i64, _int, _vp]
+    lib.orc_convert_f64_to_half.restype = None
     lib.orc_convert_to_f32.argtypes = [_vp, _int, _i64, _vp]
     lib.orc_convert_to_f32.restype = None
     lib.orc_convert_from_f32.argtypes = [_vp, _i64, _int, _vp]
@@ -275,6 +286,58 @@ class Oracle:
         self.lib.oracle_mx_quantize(_ptr(xa), xcode, rows, n, ecode, int(axis), _ptr(y),
                                     _ptr(scale))
         return y, scale
+
+    # -- weight-quantized matmul ------------------------------------------------
+    def _weight(self, x2, transpose_x2):
+        """(buffer, code, k, n) of an int8 array or an ('int4', uint8 bytes) pair."""
+        if isinstance(x2, tuple):
+            assert x2[0] == "int4"
+            wa = np.ascontiguousarray(x2[1], dtype=np.uint8)
+            r, c = wa.shape
+            code, shape = I4, (r, 2 * c)
+        else:
+            wa, code = _buffer(x2)
+            if code != I8:
+                raise TypeError("oracle: weights are int8 or ('int4', bytes)")
+            shape = wa.shape
+        k, n = (shape[1], shape[0]) if transpose_x2 else shape
+        return wa, code, int(k), int(n)
+
+    def weight_dequant(self, x2, scale, offset=None, policy="per_channel", group_size=0,
+                       transpose_x2=False) -> np.ndarray:
+        """W [k, n] as raw bf16 / fp16 bits (the parameters' dtype)."""
+        wa, wcode, k, n = self._weight(x2, transpose_x2)
+        sc, scode = _buffer(scale)
+        of, _ = _buffer(offset)
+        W = np.empty((k, n), np.uint16)
+        self.lib.oracle_weight_dequant(_ptr(wa), wcode, k, n, 1 if transpose_x2 else 0, _ptr(sc),
+                                       _ptr(of), scode, POLICIES[policy], int(group_size), _ptr(W))
+        return W
+
+    def weight_quant_matmul(self, x1, x2, scale, offset=None, policy="per_channel", group_size=0,
+                            transpose_x2=False, bias=None, x3=None):
+        """Return (out, mag, W): out = x1 @ W + bias + x3 and sum |x1 * W|, both
+        float64 [m, n] and unrounded; W as in weight_dequant."""
+        xa, xcode = _buffer(x1)
+        m, k = (int(d) for d in xa.shape)
+        W = self.weight_dequant(x2, scale, offset, policy, group_size, transpose_x2)
+        n = W.shape[1]
+        if W.shape[0] != k:
+            raise ValueError("oracle: x1 and x2 disagree on k")
+        ba, _ = _buffer(bias)
+        x3a, _ = _buffer(x3)
+        out = np.empty((m, n), np.float64)
+        mag = np.empty((m, n), np.float64)
+        self.lib.oracle_weight_quant_matmul(_ptr(xa), xcode, m, k, n, _ptr(W), _ptr(ba), _ptr(x3a),
+                                            _ptr(out), _ptr(mag))
+        return out, mag, W
+
+    def f64_to_half(self, a: np.ndarray, dtype: str) -> np.ndarray:
+        """Round binary64 values once to 'bfloat16' or 'float16'; raw uint16 bits."""
+        a = np.ascontiguousarray(a, dtype=np.float64)
+        out = np.empty(a.size, np.uint16)
+        self.lib.orc_convert_f64_to_half(_ptr(a), a.size, _FLOAT_CODES[dtype], _ptr(out))
+        return out.reshape(a.shape)
 
 
 _default: Optional[Oracle] = None

@@ -1,7 +1,7 @@
 /*
  * dquant_oracle.c -- plain, slow, single-threaded CPU oracle for per-token
- * dynamic quantization, its AdaLayerNorm fusion, AntiQuantize and mx block
- * quantization.
+ * dynamic quantization, its AdaLayerNorm fusion, AntiQuantize, mx block
+ * quantization and the weight-quantized matmul.
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may call, link or
  * load this file: it is used by tests/, by the smoke check and by the CPU
@@ -30,6 +30,9 @@
  *   [MX]   aclnnQuantBatchMatmulInplaceAdd, 计算公式 (mx量化: blocks of
  *          gsK = 32 along K, FLOAT8_E8M0 block scales), the consumer whose
  *          operands the mx block quantizer produces.
+ *   [WQ]   aclnnWeightQuantMatmulAllReduce, API function and constraints
+ *          (x2 fake-quantized per tensor / channel / group, then the
+ *          matmul; parameter shapes; the empty-k case).
  *
  * Readings taken where the pages are silent or garbled are stated next to
  * the step that depends on them.
@@ -698,4 +701,147 @@ void oracle_mx_quantize(const void* x, int x_dtype, int64_t rows, int64_t n,
             }
         }
     }
+}
+
+/* ------------------------------------------------------------------------ */
+/* [WQ] weight-quantized matmul                                              */
+/* ------------------------------------------------------------------------ */
+
+/* Round a double to bfloat16 or binary16, nearest-even, from the definition
+ * (the quantum of the target binade; no intermediate binary32 rounding). */
+static uint16_t orc_f64_to_half(double x, int dtype)
+{
+    const int mbits = dtype == ORC_BF16 ? 7 : 10;
+    const int ebits = dtype == ORC_BF16 ? 8 : 5;
+    const int bias = (1 << (ebits - 1)) - 1;
+    uint16_t sign = signbit(x) ? (uint16_t)(1u << 15) : 0;
+    uint16_t inf = (uint16_t)(((1u << ebits) - 1) << mbits);
+    if (isnan(x))
+        return (uint16_t)(sign | inf | (1u << (mbits - 1)));
+    double a = fabs(x);
+    if (isinf(x))
+        return (uint16_t)(sign | inf);
+    if (a == 0.0)
+        return sign;
+    int e;
+    frexp(a, &e);
+    int E = e - 1;
+    int emin = 1 - bias;
+    if (E < emin)
+        E = emin;
+    double q = nearbyint(ldexp(a, mbits - E)); /* quanta of 2^(E - mbits) */
+    if (q >= ldexp(1.0, mbits + 1)) {          /* carried into the next binade */
+        q = ldexp(q, -1);
+        E += 1;
+    }
+    if (E > bias) /* beyond the largest finite value */
+        return (uint16_t)(sign | inf);
+    if (q < ldexp(1.0, mbits)) /* subnormal */
+        return (uint16_t)(sign | (uint16_t)q);
+    return (uint16_t)(sign | (uint16_t)((E + bias) << mbits) | (uint16_t)(q - ldexp(1.0, mbits)));
+}
+
+/* Signed weight code x2[kk, nn] of an int8 or int4 weight held as [k, n]
+ * (transpose_x2 == 0) or as [n, k] (transpose_x2 != 0).  int4 codes sit two
+ * per byte along the stored last dimension, the even element in the low
+ * nibble, and are sign-extended from 4 bits. */
+static int weight_code(const void* x2, int w_dtype, int transpose_x2, int64_t k, int64_t n,
+                       int64_t kk, int64_t nn)
+{
+    int64_t i = transpose_x2 ? nn * k + kk : kk * n + nn;
+    if (w_dtype == ORC_I8)
+        return ((const int8_t*)x2)[i];
+    uint8_t byte = ((const uint8_t*)x2)[i / 2];
+    int v = (i & 1) ? byte >> 4 : byte & 0xF;
+    return v >= 8 ? v - 16 : v;
+}
+
+/*
+ * The fake-quantized weight of aclnnWeightQuantMatmulAllReduce (API
+ * function: x2 is fake-quantized, then multiplied), per tensor, per channel
+ * or per group down k.  The formula is missing from the page; reading: the
+ * AntiQuantize arithmetic with kDim = 0,
+ *     W[kk, nn] = RN_T(RN(RN(x2 + offset) * scale))   (offset given)
+ *     W[kk, nn] = RN_T(RN(x2 * scale))                 (no offset)
+ * in binary32, rounded once to T, the dtype of x1 and the parameters (the
+ * constraints make x1, antiquantScale, antiquantOffset, bias, x3 and the
+ * output one dtype).  Parameter index by policy (shapes from the
+ * constraints): per tensor [1]: 0; per channel [n]: nn; per group
+ * [ceil(k/gs), n]: (kk / gs) * n + nn, or, with x2 transposed (the
+ * parameters transposed with it), [n, ceil(k/gs)]: nn * ceil(k/gs) + kk / gs.
+ *
+ *   W   T bits, [k, n] row-major whatever x2's layout.
+ */
+void oracle_weight_dequant(const void* x2, int w_dtype, int64_t k, int64_t n, int transpose_x2,
+                           const void* scale, const void* offset, int param_dtype, int policy,
+                           int64_t group_size, uint16_t* W)
+{
+    int64_t groups = policy == ORC_PER_GROUP ? (k + group_size - 1) / group_size : 1;
+    for (int64_t kk = 0; kk < k; ++kk) {
+        for (int64_t nn = 0; nn < n; ++nn) {
+            int64_t p;
+            if (policy == ORC_PER_TENSOR)
+                p = 0;
+            else if (policy == ORC_PER_CHANNEL)
+                p = nn;
+            else
+                p = transpose_x2 ? nn * groups + kk / group_size : (kk / group_size) * n + nn;
+            float v = (float)weight_code(x2, w_dtype, transpose_x2, k, n, kk, nn);
+            float s = load_as_f32(scale, param_dtype, p);
+            float t;
+            if (offset) {
+                float u = v + load_as_f32(offset, param_dtype, p);
+                t = u * s;
+            } else {
+                t = v * s;
+            }
+            W[kk * n + nn] = param_dtype == ORC_BF16 ? orc_f32_to_bf16(t) : orc_f32_to_f16(t);
+        }
+    }
+}
+
+/*
+ * out = x1 @ W + bias + x3 for the W above (aclnnWeightQuantMatmulAllReduce
+ * on one rank, where the AllReduce is the identity; the page's empty-k case
+ * gives bias + x3).  Reading: one product of the exact inputs, the sum
+ * accumulated in binary64 here (the device accumulates in binary32), bias
+ * [n] and x3 [m, n] added, no intermediate rounding; the result is returned
+ * unrounded in binary64 (rounding to T, and the device's accumulation error,
+ * are the tests' tolerance).  Also returns sum_kk |x1 * W| per element, the
+ * scale of the accumulation error bound.
+ *
+ *   x1        [m, k] of x_dtype (F16 / BF16).
+ *   W         T bits [k, n] from oracle_weight_dequant.
+ *   bias, x3  NULL or T [n] / [m, n].
+ *   out, mag  binary64 [m, n].
+ */
+void oracle_weight_quant_matmul(const void* x1, int x_dtype, int64_t m, int64_t k, int64_t n,
+                                const uint16_t* W, const void* bias, const void* x3,
+                                double* out, double* mag)
+{
+    for (int64_t mm = 0; mm < m; ++mm) {
+        for (int64_t nn = 0; nn < n; ++nn) {
+            double acc = 0.0, am = 0.0;
+            for (int64_t kk = 0; kk < k; ++kk) {
+                double a = (double)load_as_f32(x1, x_dtype, mm * k + kk);
+                double w = (double)load_as_f32(W, x_dtype, kk * n + nn);
+                acc += a * w; /* exact product (at most 22 significant bits) */
+                am += fabs(a * w);
+            }
+            if (bias)
+                acc += (double)load_as_f32(bias, x_dtype, nn);
+            if (x3)
+                acc += (double)load_as_f32(x3, x_dtype, mm * n + nn);
+            out[mm * n + nn] = acc;
+            if (mag)
+                mag[mm * n + nn] = am;
+        }
+    }
+}
+
+/* Vector form of the double -> bf16 / fp16 rounding, for the tests. */
+void orc_convert_f64_to_half(const double* src, int64_t count, int dst_dtype, uint16_t* dst)
+{
+    for (int64_t i = 0; i < count; ++i)
+        dst[i] = orc_f64_to_half(src[i], dst_dtype);
 }

@@ -824,6 +824,168 @@ def pin_mx_short_block_and_axis(orc):
 
 
 # ---------------------------------------------------------------------------
+# Weight-quantized matmul (aclnnWeightQuantMatmulAllReduce on one rank)
+# ---------------------------------------------------------------------------
+
+def _pack_int4(codes: np.ndarray) -> np.ndarray:
+    """Signed 4-bit codes [r, 2c] -> bytes [r, c], the even element low."""
+    u = (codes.astype(np.int16) & 0xF).astype(np.uint8)
+    return (u[:, 0::2] | (u[:, 1::2] << 4)).astype(np.uint8)
+
+
+def _wq_case(rng, k, n, policy, gs, dtype, w="int8", offset=True, transpose=False):
+    """Random weights and parameters; returns the oracle arguments and, for
+    the reference, the signed codes [k, n] and parameters as float32."""
+    lo, hi = (-128, 128) if w == "int8" else (-8, 8)
+    codes = rng.integers(lo, hi, (k, n)).astype(np.int8)
+    if policy == "per_tensor":
+        pshape = (1,)
+    elif policy == "per_channel":
+        pshape = (n,)
+    else:
+        pshape = (-(-k // gs), n)
+    sc = torch.from_numpy(rng.uniform(0.01, 0.1, pshape).astype(np.float32)).to(dtype)
+    of = torch.from_numpy(rng.uniform(-4, 4, pshape).astype(np.float32)).to(dtype) if offset else None
+    stored = codes.T.copy() if transpose else codes
+    x2 = stored if w == "int8" else ("int4", _pack_int4(stored))
+    if transpose and policy == "per_group":
+        sc_arg = sc.t().contiguous()
+        of_arg = None if of is None else of.t().contiguous()
+    else:
+        sc_arg, of_arg = sc, of
+    return x2, sc_arg, of_arg, codes, sc.float().numpy(), None if of is None else of.float().numpy()
+
+
+def _numpy_dequant(codes, s, o, policy, gs, dtype):
+    """W from numpy float32 arithmetic and torch's float32 -> T cast."""
+    k, n = codes.shape
+    if policy == "per_tensor":
+        S = np.full((k, n), s[0], np.float32)
+        O = None if o is None else np.full((k, n), o[0], np.float32)
+    elif policy == "per_channel":
+        S = np.broadcast_to(s, (k, n))
+        O = None if o is None else np.broadcast_to(o, (k, n))
+    else:
+        S = np.repeat(s, gs, axis=0)[:k]
+        O = None if o is None else np.repeat(o, gs, axis=0)[:k]
+    v = codes.astype(np.float32)
+    t = (v + O) * S if O is not None else v * S
+    return torch.from_numpy(t.astype(np.float32)).to(dtype)
+
+
+def pin_wq_empty_k_is_bias_plus_x3(orc):
+    """The page's empty-tensor case: with k = 0 the output is bias + x3."""
+    rng = np.random.default_rng(71)
+    x1 = torch.zeros((3, 0), dtype=torch.bfloat16)
+    x2 = np.zeros((0, 8), np.int8)
+    bias = _bf16(rng.standard_normal(8).tolist())
+    x3 = _bf16(rng.standard_normal((3, 8)).tolist())
+    sc = _bf16([0.5] * 8)
+    out, mag, W = orc.weight_quant_matmul(x1, x2, sc, bias=bias, x3=x3)
+    assert W.shape == (0, 8) and np.all(mag == 0)
+    want = bias.double().numpy()[None, :] + x3.double().numpy()
+    assert np.array_equal(out, want)
+
+
+def pin_wq_identity_weight(orc):
+    """x2 = identity, scale 1 per tensor, no offset: the output is x1 exactly
+    (plus bias and x3)."""
+    rng = np.random.default_rng(72)
+    for mk in (_bf16, _f16):
+        x1 = mk(rng.standard_normal((5, 64)).tolist())
+        eye = np.eye(64, dtype=np.int8)
+        out, _, _ = orc.weight_quant_matmul(x1, eye, mk([1.0]), policy="per_tensor")
+        assert np.array_equal(out, x1.double().numpy())
+        out, _, _ = orc.weight_quant_matmul(x1, ("int4", _pack_int4(eye)), mk([1.0]), policy="per_tensor")
+        assert np.array_equal(out, x1.double().numpy())
+
+
+def pin_wq_int4_nibbles_worked(orc):
+    """int4 weights [1, 6] from bytes 0x7F 0x80 0x19: low nibble first,
+    sign-extended: 0xF -> -1, 7, 0, 0x8 -> -8, 0x9 -> -7, 1.  Scale 1."""
+    W = orc.weight_dequant(("int4", np.array([[0x7F, 0x80, 0x19]], np.uint8)), _bf16([1.0]),
+                           policy="per_tensor")
+    assert _bits_to_bf16_f32(W).tolist() == [[-1.0, 7.0, 0.0, -8.0, -7.0, 1.0]]
+    Wt = orc.weight_dequant(("int4", np.array([[0x7F], [0x80], [0x19]], np.uint8)), _bf16([1.0]),
+                            policy="per_tensor", transpose_x2=True)
+    assert _bits_to_bf16_f32(Wt).tolist() == [[-1.0, 0.0, -7.0], [7.0, -8.0, 1.0]]
+
+
+def pin_wq_dequant_matches_numpy(orc):
+    """W equals numpy's float32 (x2 + offset) * scale cast to T by torch, for
+    every policy, int8 and int4, with and without offset, both layouts and
+    both dtypes (a short last group included)."""
+    rng = np.random.default_rng(73)
+    k, n = 96, 40
+    for dtype in (torch.bfloat16, torch.float16):
+        for policy, gs in (("per_tensor", 0), ("per_channel", 0), ("per_group", 64), ("per_group", 32)):
+            for w in ("int8", "int4"):
+                for off in (True, False):
+                    for tr in (False, True):
+                        x2, sc, of, codes, s, o = _wq_case(rng, k, n, policy, gs, dtype, w, off, tr)
+                        W = orc.weight_dequant(x2, sc, of, policy, gs, tr)
+                        ref = _numpy_dequant(codes, s, o, policy, gs, dtype)
+                        assert np.array_equal(W, ref.view(torch.int16).numpy().view(np.uint16)), \
+                            (dtype, policy, gs, w, off, tr)
+
+
+def pin_wq_matmul_matches_numpy(orc):
+    """out equals numpy's float64 x1 @ W + bias + x3 on the decoded values
+    (to 1e-12 relative: the summation orders differ), and mag is
+    |x1| @ |W|."""
+    rng = np.random.default_rng(74)
+    m, k, n = 7, 160, 24
+    x2, sc, of, codes, s, o = _wq_case(rng, k, n, "per_group", 32, torch.bfloat16, "int4", True, False)
+    x1 = _bf16(rng.standard_normal((m, k)).tolist())
+    bias = _bf16(rng.standard_normal(n).tolist())
+    x3 = _bf16(rng.standard_normal((m, n)).tolist())
+    out, mag, W = orc.weight_quant_matmul(x1, x2, sc, of, "per_group", 32, bias=bias, x3=x3)
+    Wd = _bits_to_bf16_f32(W).astype(np.float64)
+    xd = x1.double().numpy()
+    ref = xd @ Wd + bias.double().numpy()[None, :] + x3.double().numpy()
+    assert np.allclose(out, ref, rtol=1e-12, atol=1e-12 * np.abs(xd) @ np.abs(Wd))
+    assert np.allclose(mag, np.abs(xd) @ np.abs(Wd), rtol=1e-12)
+
+
+def pin_wq_policy_reductions(orc):
+    """Per group with gs >= k is per channel with the group row; per channel
+    with a constant vector is per tensor; the transposed layout (weights and
+    group parameters transposed together) gives the same W."""
+    rng = np.random.default_rng(75)
+    k, n = 64, 48
+    codes = rng.integers(-128, 128, (k, n)).astype(np.int8)
+    s = _bf16(rng.uniform(0.01, 0.1, (1, n)).tolist())
+    o = _bf16(rng.uniform(-4, 4, (1, n)).tolist())
+    a = orc.weight_dequant(codes, s, o, "per_group", 64)
+    b = orc.weight_dequant(codes, s[0], o[0], "per_channel")
+    assert np.array_equal(a, b)
+    c = orc.weight_dequant(codes, _bf16([0.03] * n), _bf16([1.5] * n), "per_channel")
+    d = orc.weight_dequant(codes, _bf16([0.03]), _bf16([1.5]), "per_tensor")
+    assert np.array_equal(c, d)
+    s4 = _bf16(rng.uniform(0.01, 0.1, (2, n)).tolist())
+    e = orc.weight_dequant(codes, s4, None, "per_group", 32)
+    f = orc.weight_dequant(codes.T.copy(), s4.t().contiguous(), None, "per_group", 32, transpose_x2=True)
+    assert np.array_equal(e, f)
+
+
+def pin_f64_to_half_rounding(orc):
+    """binary64 -> bf16 / fp16 rounds once: it equals torch's cast for values
+    that are binary32 already; 1 + 2^-8 + 2^-30 rounds up to 1 + 2^-7 in
+    bf16 (a detour through binary32 would land on the tie and round to 1);
+    numpy's float64 -> float16 cast agrees on random doubles."""
+    rng = np.random.default_rng(76)
+    a = (rng.standard_normal(4000) * np.exp2(rng.integers(-30, 30, 4000))).astype(np.float32).astype(np.float64)
+    ref = torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(orc.f64_to_half(a, "bfloat16"), ref)
+    x = np.array([1 + 2.0 ** -8 + 2.0 ** -30, 1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8])
+    got = _bits_to_bf16_f32(orc.f64_to_half(x, "bfloat16")).tolist()
+    assert got == [1 + 2.0 ** -7, 1.0, 1 + 2.0 ** -6]
+    d = rng.standard_normal(4000) * np.exp2(rng.integers(-26, 16, 4000))
+    with np.errstate(over="ignore"):
+        assert np.array_equal(orc.f64_to_half(d, "float16"), d.astype(np.float16).view(np.uint16))
+
+
+# ---------------------------------------------------------------------------
 # Element conversions against library routines
 # ---------------------------------------------------------------------------
 

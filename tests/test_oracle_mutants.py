@@ -74,8 +74,10 @@ MUTANTS = [
     ("mx_no_saturation", "if (v > f.maxv)\n        v = f.maxv;", "if (v > 2 * f.maxv)\n        v = f.maxv;"),
     ("mx_round_half_away", "double q = nearbyint(ldexp(a, f.mbits - E));",
      "double q = round(ldexp(a, f.mbits - E));"),
-    ("mx_subnormal_quantum", "if (E < emin)\n        E = emin;",
-     "if (E < emin - 1)\n        E = emin - 1;"),
+    ("mx_subnormal_quantum", "if (E < emin)\n        E = emin; /* the subnormals share",
+     "if (E < emin - 1)\n        E = emin - 1; /* the subnormals share"),
+    ("f64_half_subnormal_quantum", "if (E < emin)\n        E = emin;\n    double q = nearbyint(ldexp(a, mbits - E)); /* quanta",
+     "if (E < emin - 1)\n        E = emin - 1;\n    double q = nearbyint(ldexp(a, mbits - E)); /* quanta"),
     ("mx_fp4_nibble_order", "uint8_t* b = (uint8_t*)y + i / 2;\n        if (i & 1)",
      "uint8_t* b = (uint8_t*)y + i / 2;\n        if (!(i & 1))"),
     ("mx_clamp_fp32_min", "if (shared < -127)\n                    shared = -127;",
@@ -88,6 +90,21 @@ MUTANTS = [
      "int64_t si = axis == 1 ? o * (along / gs) + j : j * n + o;"),
     ("mx_axis0_scale_index", "int64_t si = axis == 1 ? o * blocks + j : j * n + o;",
      "int64_t si = axis == 1 ? o * blocks + j : o * blocks + j;"),
+    ("wq_offset_subtracted", "float u = v + load_as_f32(offset, param_dtype, p);",
+     "float u = v - load_as_f32(offset, param_dtype, p);"),
+    ("wq_group_index_transposed", "p = transpose_x2 ? nn * groups + kk / group_size : (kk / group_size) * n + nn;",
+     "p = nn * groups + kk / group_size;"),
+    ("wq_int4_unsigned", "return v >= 8 ? v - 16 : v;", "return v;"),
+    ("wq_int4_high_first", "int v = (i & 1) ? byte >> 4 : byte & 0xF;", "int v = (i & 1) ? byte & 0xF : byte >> 4;"),
+    ("wq_weight_layout_ignored", "int64_t i = transpose_x2 ? nn * k + kk : kk * n + nn;", "int64_t i = kk * n + nn;"),
+    ("wq_bf16_truncated", "W[kk * n + nn] = param_dtype == ORC_BF16 ? orc_f32_to_bf16(t) : orc_f32_to_f16(t);",
+     "W[kk * n + nn] = param_dtype == ORC_BF16 ? (uint16_t)(f32_to_bits(t) >> 16) : orc_f32_to_f16(t);"),
+    ("wq_bias_dropped", "acc += (double)load_as_f32(bias, x_dtype, nn);", "acc += 0.0;"),
+    ("wq_x3_dropped", "acc += (double)load_as_f32(x3, x_dtype, mm * n + nn);", "acc += 0.0;"),
+    ("wq_x1_row_index", "double a = (double)load_as_f32(x1, x_dtype, mm * k + kk);",
+     "double a = (double)load_as_f32(x1, x_dtype, kk);"),
+    ("f64_half_via_f32", "    double a = fabs(x);\n    if (isinf(x))\n        return (uint16_t)(sign | inf);",
+     "    double a = fabs((double)(float)x);\n    if (isinf(x))\n        return (uint16_t)(sign | inf);"),
     ("mx_amax_signed", "else if (fabs((double)v) > amax)\n                    amax = fabs((double)v);",
      "else if ((double)v > amax)\n                    amax = (double)v;"),
 ]
