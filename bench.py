@@ -14,8 +14,9 @@ the previous one.  Every launch in the timed region is bracketed by HIP
 events on the stream it runs on; "roofline.achieved" is the algorithmic
 bytes of one launch over the mean event-measured launch time.  The other
 workloads (MoE asymmetric INT8/INT4, AdaLayerNorm-quant, AntiQuantize in
-every policy, mx block quantization, the tiny fp16 case) are measured the
-same way and reported
+every policy, mx block quantization, the weight-quantized matmul in a
+decode and a prefill shape, the tiny fp16 case) are measured the same way
+and reported
 under "workloads"; a plain device copy gives the achievable-bandwidth
 ceiling.  "cpu_baseline" is the single-threaded CPU oracle timed on the
 host over a bounded sample of the same workload.
@@ -38,6 +39,7 @@ import int4_quantization_amd as dq  # noqa: E402
 from int4_quantization_amd import synth  # noqa: E402
 
 PEAK_GBPS = 8000.0           # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 / fp16 matrix-core peak
 ROTATE_BYTES = 1 << 30       # buffer-set rotation footprint (> 4x the 256 MB MALL)
 HEADLINE = "dq_sym_smooth_bf16_8192x7168"
 METRIC = "achieved HBM GB/s (% of peak) + rows/s, per-token bf16→int8 dynamic quant"
@@ -95,6 +97,16 @@ class Work:
                                               ("scale", "shift", "weight", "bias", "smooth"))
                               + B * S * H + B * S * 4)
             per_set = nbytes(x) + B * S * H
+        elif op == "weight_quant_matmul":
+            x1, x2 = host["x1"], host["x2"]
+            k = x1.shape[-1]
+            m = x1.numel() // max(k, 1)
+            n = x2.shape[0] if host["transpose_x2"] else x2.shape[1] * (2 if host["weight"] == "int4" else 1)
+            self.rows = m
+            self.alg_flops = 2 * m * k * n
+            self.alg_bytes = (nbytes(x1) + nbytes(x2) + nbytes(host["scale"]) + nbytes(host["offset"])
+                              + nbytes(host["bias"]) + nbytes(host["x3"]) + m * n * 2)
+            per_set = nbytes(x1) + nbytes(x2) + m * n * 2
         elif op == "mx_quantize":
             x = host["x"]
             rows, n = x.shape
@@ -147,6 +159,14 @@ class Work:
                 out = torch.empty(x.shape, dtype=torch.int8, device=dev)
                 qs = torch.empty((B, S), dtype=torch.float32, device=dev)
                 self.bufs.append((x, p, out, qs))
+        elif self.op == "weight_quant_matmul":
+            p = {k: (None if h[k] is None else h[k].to(dev)) for k in ("x1", "x2", "scale", "offset", "bias", "x3")}
+            n = p["x2"].shape[0] if h["transpose_x2"] else p["x2"].shape[1] * (2 if h["weight"] == "int4" else 1)
+            for i in range(self.sets):
+                x1 = p["x1"] if i == 0 else p["x1"].clone()
+                x2 = p["x2"] if i == 0 else p["x2"].clone()
+                out = torch.empty(tuple(x1.shape[:-1]) + (n,), dtype=x1.dtype, device=dev)
+                self.bufs.append((x1, x2, p, out))
         elif self.op == "mx_quantize":
             xd = h["x"].to(dev)
             rows, n = xd.shape
@@ -180,6 +200,11 @@ class Work:
                 x, p, out, qs = b
                 self.calls.append(dq.dquant.prepare_ada_layernorm_quant(
                     x, p["scale"], p["shift"], p["weight"], p["bias"], p["smooth"], h["eps"], out, qs))
+            elif self.op == "weight_quant_matmul":
+                x1, x2, p, out = b
+                self.calls.append(dq.dquant.prepare_weight_quant_matmul(
+                    x1, x2, h["transpose_x2"], p["scale"], p["offset"], h["group_size"], p["bias"], p["x3"],
+                    out, h["weight"]))
             elif self.op == "mx_quantize":
                 x, y, sc = b
                 self.calls.append(dq.dquant.prepare_mx_quantize(x, h["axis"], y, sc))
@@ -248,6 +273,9 @@ def summarize(w: Work, wall: float, region: float, lat: np.ndarray, steps: int) 
         "gbps_wall": w.alg_bytes * steps / wall / 1e9,
         "rows_per_s": w.rows / mean,
         "buffer_sets": w.sets,
+        **({"alg_flops": int(w.alg_flops), "tflops_kernel": w.alg_flops / mean / 1e12,
+            "pct_peak_mfma_bf16": 100.0 * w.alg_flops / mean / 1e12 / PEAK_BF16_TFLOPS}
+           if getattr(w, "alg_flops", None) else {}),
     }
 
 

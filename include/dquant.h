@@ -1,7 +1,7 @@
 /*
  * dquant.h -- C ABI of libdquant: per-token dynamic quantization, its
- * AdaLayerNorm fusion, AntiQuantize and mx block quantization on AMD MI355X
- * (gfx950).
+ * AdaLayerNorm fusion, AntiQuantize, mx block quantization and the
+ * weight-quantized matmul on AMD MI355X (gfx950).
  *
  * Calling convention (after the two-phase form of the aclnn host ops,
  * "Each operator has two calls": a get-workspace-size call that returns
@@ -18,6 +18,7 @@
  * Ownership
  *   - The caller owns every tensor buffer, the workspace and the stream.
  *     The library never allocates device memory and never synchronizes.
+ *     Only the weight-quantized matmul ever asks for a workspace.
  *   - Tensors are dense, row-major (last dimension contiguous) device
  *     buffers described by dq_tensor; the library keeps only the pointers.
  *   - An executor is host memory owned by the library.  The execute call
@@ -271,6 +272,60 @@ dq_status dq_mx_quantize_get_workspace_size(const dq_tensor* x, int32_t axis, co
                                             dq_executor** executor);
 dq_status dq_mx_quantize(void* workspace, size_t workspace_size, dq_executor* executor,
                          hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Weight-quantized matmul -- aclnnWeightQuantMatmulAllReduce on one GPU
+ * (API function: the weight x2 is fake-quantized, then multiplied; the
+ * all-reduce over ranks is the identity on one rank; constraints: shapes,
+ * dtypes, parameter shapes, the empty-k case).  The page's formula is
+ * missing; this library reads it with the AntiQuantize arithmetic:
+ *   W[k, n]   = RN_T((x2[k, n] + offset[p]) * scale[p])   (two binary32
+ *               operations, or one without offset, rounded once to T)
+ *   out[m, n] = RN_T(sum_k x1[m, k] * W[k, n] + bias[n] + x3[m, n])
+ * with the sum accumulated in binary32 (any order) and one final rounding;
+ * T is x1's dtype.  With k == 0 the output is bias + x3 (the page's empty
+ * case).  The result is within gamma_{k+2} * (sum_k |x1 W| + |bias| + |x3|)
+ * + half an ulp of T of the exact value, gamma_j = j 2^-24 / (1 - j 2^-24).
+ *
+ *   x1            F16 or BF16, [m, k] or [b, s, k]; m = prod(leading dims)
+ *                 may be 0.  k in [0, 65535].
+ *   x2            I8, or I4 (two signed 4-bit codes per byte along the
+ *                 stored last dimension, the even element in the low
+ *                 nibble).  transpose_x2 == 0: [k, n] in memory;
+ *                 transpose_x2 != 0: [n, k] in memory (x2 given as its
+ *                 transpose, the nn.Linear layout).  n in [1, 65535].
+ *   antiquant_scale   x1's dtype.  group_size == 0: [1] (per tensor) or
+ *                 [n] / [1, n] (per channel).  group_size > 0 (a multiple
+ *                 of 32): [ceil(k/gs), n], or [n, ceil(k/gs)] when
+ *                 transpose_x2 (the parameters transposed with x2).
+ *   antiquant_offset  NULL, or the scale's dtype and shape.
+ *   bias          NULL or x1's dtype [n].
+ *   x3            NULL or x1's dtype with out's shape.
+ *   out           x1's dtype, x1.shape[:-1] + [n]; must not overlap an input.
+ *   The matrix-core kernel runs when transpose_x2 is set, k % 32 == 0 (I8)
+ *   or k % 64 == 0 (I4), and x1 and x2 are 16-byte aligned; otherwise a
+ *   generic kernel (one thread per output element) computes the same
+ *   arithmetic much more slowly.
+ *   Workspace: 0 bytes, except when the output has few tiles (small m):
+ *   then k is split across workgroups and the workspace holds the binary32
+ *   partial sums, splits * m * n * 4 bytes (16-byte aligned, owned by the
+ *   caller, contents scratch).  The partial sums are added in split order,
+ *   so results stay bit-reproducible.
+ * Errors: DQ_ERR_NULLPTR, DQ_ERR_DTYPE, DQ_ERR_SHAPE (ranks, shapes, k or n
+ *   out of range, odd stored last dimension for I4), DQ_ERR_PARAM
+ *   (group_size negative or not a multiple of 32), DQ_ERR_OVERLAP;
+ *   execute: DQ_ERR_WORKSPACE (workspace NULL or smaller than returned),
+ *   DQ_ERR_ALIGN (workspace not 16-byte aligned).
+ * ------------------------------------------------------------------------ */
+dq_status dq_weight_quant_matmul_get_workspace_size(const dq_tensor* x1, const dq_tensor* x2,
+                                                    int32_t transpose_x2,
+                                                    const dq_tensor* antiquant_scale,
+                                                    const dq_tensor* antiquant_offset,
+                                                    int64_t group_size, const dq_tensor* bias,
+                                                    const dq_tensor* x3, const dq_tensor* out,
+                                                    size_t* workspace_size, dq_executor** executor);
+dq_status dq_weight_quant_matmul(void* workspace, size_t workspace_size, dq_executor* executor,
+                                 hipStream_t stream);
 
 /* Release an executor that was never passed to an execute call.  NULL is a
  * no-op. */

@@ -1,6 +1,7 @@
 """libdquant for MI355X (gfx950): per-token dynamic quantization
-(DynamicQuantV2), its AdaLayerNorm fusion, AntiQuantize, and mx block
-quantization (e8m0 scales per 32 elements).
+(DynamicQuantV2), its AdaLayerNorm fusion, AntiQuantize, mx block
+quantization (e8m0 scales per 32 elements), and the weight-quantized
+matmul (int8 / int4 weights dequantized into the matrix cores).
 
 The compute runs in hand-written HIP kernels inside ``libdquant.so``, reached
 through the C ABI declared in ``include/dquant.h``.  This package is the thin
@@ -23,9 +24,12 @@ from .dquant import (  # noqa: F401
     dq_get_last_error,
     dq_mx_quantize,
     dq_mx_quantize_get_workspace_size,
+    dq_weight_quant_matmul,
+    dq_weight_quant_matmul_get_workspace_size,
     dynamic_quant,
     library,
     library_path,
     mx_quantize,
     mx_scale_shape,
+    weight_quant_matmul,
 )

@@ -25,7 +25,7 @@ LIBRARY = os.path.join(HERE, "libdquant.so")
 ARCH = "gfx950"
 
 SOURCES = ["dquant_api.cpp", "dynamic_quant.hip", "ada_layernorm_quant.hip", "antiquantize.hip",
-           "mx_quantize.hip", "copy_probe.hip"]
+           "mx_quantize.hip", "weight_quant_matmul.hip", "copy_probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",

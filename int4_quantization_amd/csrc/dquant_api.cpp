@@ -15,7 +15,13 @@
 
 #include "dq_internal.h"
 
-enum ExecOp : int { OP_DYNAMIC_QUANT = 1, OP_ADA_LAYERNORM_QUANT = 2, OP_ANTIQUANTIZE = 3, OP_MX_QUANTIZE = 4 };
+enum ExecOp : int {
+    OP_DYNAMIC_QUANT = 1,
+    OP_ADA_LAYERNORM_QUANT = 2,
+    OP_ANTIQUANTIZE = 3,
+    OP_MX_QUANTIZE = 4,
+    OP_WEIGHT_QUANT_MATMUL = 5
+};
 
 struct dq_executor {
     int op;
@@ -23,6 +29,7 @@ struct dq_executor {
     dq::AdaPlan ada;
     dq::AqPlan aq;
     dq::MxPlan mx;
+    dq::WqPlan wq;
 };
 
 namespace {
@@ -137,6 +144,9 @@ dq_executor* new_executor(int op)
     }
     return e;
 }
+
+// Workgroups the weight-quantized matmul aims for when splitting k.
+constexpr int64_t kWqTargetBlocks = 2048;
 
 int pick_vpl(int64_t per_lane, const int* choices, int count)
 {
@@ -676,6 +686,183 @@ dq_status dq_mx_quantize(void* workspace, size_t workspace_size, dq_executor* ex
     hipError_t err = dq::launch_mx_quantize(p, stream);
     if (err != hipSuccess)
         return fail(DQ_ERR_RUNTIME, "mx quantize launch failed: %s", hipGetErrorString(err));
+    return ok();
+}
+
+// ---------------------------------------------------------------------------
+// Weight-quantized matmul
+// ---------------------------------------------------------------------------
+dq_status dq_weight_quant_matmul_get_workspace_size(const dq_tensor* x1, const dq_tensor* x2,
+                                                    int32_t transpose_x2,
+                                                    const dq_tensor* antiquant_scale,
+                                                    const dq_tensor* antiquant_offset,
+                                                    int64_t group_size, const dq_tensor* bias,
+                                                    const dq_tensor* x3, const dq_tensor* out,
+                                                    size_t* workspace_size, dq_executor** executor)
+{
+    if (!workspace_size || !executor)
+        return fail(DQ_ERR_NULLPTR, "workspace_size and executor must not be NULL");
+    *executor = nullptr;
+    *workspace_size = 0;
+    dq_status st;
+    int64_t nx1 = 0, nx2 = 0, ns = 0, no = 0;
+    if ((st = check_tensor(x1, "x1", &nx1)) != DQ_SUCCESS) return st;
+    if ((st = check_tensor(x2, "x2", &nx2)) != DQ_SUCCESS) return st;
+    if ((st = check_tensor(antiquant_scale, "antiquant_scale", &ns)) != DQ_SUCCESS) return st;
+    if ((st = check_tensor(out, "out", &no)) != DQ_SUCCESS) return st;
+    const dq_dtype T = x1->dtype;
+    if (T != DQ_F16 && T != DQ_BF16)
+        return fail(DQ_ERR_DTYPE, "x1 must be F16 or BF16, got %s", dtype_name(T));
+    if (x2->dtype != DQ_I8 && x2->dtype != DQ_I4)
+        return fail(DQ_ERR_DTYPE, "x2 must be I8 or I4, got %s", dtype_name(x2->dtype));
+    if (antiquant_scale->dtype != T || out->dtype != T)
+        return fail(DQ_ERR_DTYPE, "antiquant_scale and out must have x1's dtype %s", dtype_name(T));
+    if (x1->ndim != 2 && x1->ndim != 3)
+        return fail(DQ_ERR_SHAPE, "x1 must be [m, k] or [b, s, k], got ndim %d", x1->ndim);
+    if (x2->ndim != 2)
+        return fail(DQ_ERR_SHAPE, "x2 must be 2-D, got ndim %d", x2->ndim);
+    const int64_t k = x1->dims[x1->ndim - 1];
+    const int64_t m = k > 0 ? nx1 / k : [&] { int64_t r = 1; for (int i = 0; i + 1 < x1->ndim; ++i) r *= x1->dims[i]; return r; }();
+    const int64_t xk = transpose_x2 ? x2->dims[1] : x2->dims[0];
+    const int64_t n = transpose_x2 ? x2->dims[0] : x2->dims[1];
+    if (xk != k)
+        return fail(DQ_ERR_SHAPE, "x1 and x2 disagree on k (%lld vs %lld)", (long long)k, (long long)xk);
+    if (k > 65535 || n < 1 || n > 65535)
+        return fail(DQ_ERR_SHAPE, "k must be in [0, 65535] and n in [1, 65535] (k %lld, n %lld)", (long long)k,
+                    (long long)n);
+    if (m > dq::kMaxGridBlocks)
+        return fail(DQ_ERR_SHAPE, "at most 2^31 - 1 rows of x1 are supported");
+    if (x2->dtype == DQ_I4 && x2->dims[1] % 2 != 0)
+        return fail(DQ_ERR_SHAPE, "I4 weights need an even stored last dimension");
+    int64_t want[DQ_MAX_DIMS];
+    std::memcpy(want, x1->dims, sizeof want);
+    want[x1->ndim - 1] = n;
+    if (!same_dims(out, want, x1->ndim))
+        return fail(DQ_ERR_SHAPE, "out must be x1.shape[:-1] + [n]");
+    if (group_size < 0 || group_size % 32 != 0)
+        return fail(DQ_ERR_PARAM, "group_size must be 0 or a positive multiple of 32, got %lld", (long long)group_size);
+    int policy;
+    if (group_size > 0) {
+        policy = DQ_PER_GROUP;
+        const int64_t G = (k + group_size - 1) / group_size;
+        if (!(transpose_x2 ? is_shape(antiquant_scale, {n, G}) : is_shape(antiquant_scale, {G, n})))
+            return fail(DQ_ERR_SHAPE, transpose_x2 ? "per-group scale must be [n, ceil(k/gs)]"
+                                                   : "per-group scale must be [ceil(k/gs), n]");
+    } else if (ns == 1 && (antiquant_scale->ndim == 1 || (antiquant_scale->ndim == 2 && n == 1))) {
+        policy = DQ_PER_TENSOR;
+    } else if (is_shape(antiquant_scale, {n}) || is_shape(antiquant_scale, {1, n})) {
+        policy = DQ_PER_CHANNEL;
+    } else {
+        return fail(DQ_ERR_SHAPE, "antiquant_scale must be [1], [n] or [1, n] without a group size");
+    }
+    if (antiquant_offset) {
+        int64_t nof = 0;
+        if ((st = check_tensor(antiquant_offset, "antiquant_offset", &nof)) != DQ_SUCCESS) return st;
+        if (antiquant_offset->dtype != T)
+            return fail(DQ_ERR_DTYPE, "antiquant_offset must have x1's dtype");
+        if (!same_dims(antiquant_offset, antiquant_scale->dims, antiquant_scale->ndim))
+            return fail(DQ_ERR_SHAPE, "antiquant_offset must have the scale's shape");
+    }
+    if (bias) {
+        int64_t nb = 0;
+        if ((st = check_tensor(bias, "bias", &nb)) != DQ_SUCCESS) return st;
+        if (bias->dtype != T)
+            return fail(DQ_ERR_DTYPE, "bias must have x1's dtype");
+        if (!is_shape(bias, {n}))
+            return fail(DQ_ERR_SHAPE, "bias must be [n]");
+    }
+    if (x3) {
+        int64_t n3 = 0;
+        if ((st = check_tensor(x3, "x3", &n3)) != DQ_SUCCESS) return st;
+        if (x3->dtype != T)
+            return fail(DQ_ERR_DTYPE, "x3 must have x1's dtype");
+        if (!same_dims(x3, want, x1->ndim))
+            return fail(DQ_ERR_SHAPE, "x3 must have out's shape");
+    }
+    if (no > 0) {
+        const uintptr_t o0 = reinterpret_cast<uintptr_t>(out->data), o1 = o0 + static_cast<uintptr_t>(no) * 2;
+        auto hits = [&](const dq_tensor* t, int64_t bytes) {
+            if (!t || bytes <= 0)
+                return false;
+            const uintptr_t t0 = reinterpret_cast<uintptr_t>(t->data), t1 = t0 + static_cast<uintptr_t>(bytes);
+            return t0 < o1 && o0 < t1;
+        };
+        const int64_t w_bytes = x2->dtype == DQ_I4 ? nx2 / 2 : nx2;
+        if (hits(x1, nx1 * 2) || hits(x2, w_bytes) || hits(antiquant_scale, ns * 2) ||
+            hits(antiquant_offset, antiquant_offset ? ns * 2 : 0) || hits(bias, bias ? n * 2 : 0) ||
+            hits(x3, x3 ? no * 2 : 0))
+            return fail(DQ_ERR_OVERLAP, "out overlaps an input");
+    }
+
+    dq_executor* e = new_executor(OP_WEIGHT_QUANT_MATMUL);
+    if (!e)
+        return fail(DQ_ERR_RUNTIME, "out of host memory");
+    dq::WqPlan& p = e->wq;
+    p.x1 = x1->data;
+    p.x2 = x2->data;
+    p.scale = antiquant_scale->data;
+    p.offset = antiquant_offset ? antiquant_offset->data : nullptr;
+    p.bias = bias ? bias->data : nullptr;
+    p.x3 = x3 ? x3->data : nullptr;
+    p.out = out->data;
+    p.m = m;
+    p.k = k;
+    p.n = n;
+    p.group_size = group_size;
+    p.x_type = T == DQ_BF16 ? dq::X_BF16 : dq::X_F16;
+    p.w_type = x2->dtype == DQ_I8 ? dq::WQ_I8 : dq::WQ_I4;
+    p.policy = policy;
+    p.transpose_x2 = transpose_x2 != 0;
+    const bool kfit = x2->dtype == DQ_I8 ? k % 32 == 0 : k % 64 == 0;
+    p.variant = p.transpose_x2 && kfit && aligned(x1->data, 16) && aligned(x2->data, 16) ? dq::WQ_VAR_MFMA
+                                                                                       : dq::WQ_VAR_GENERIC;
+    p.tile = m <= 16 ? dq::WQ_TILE_DECODE : m <= 128 ? dq::WQ_TILE_2x2 : dq::WQ_TILE_4x4;
+    // Few output tiles: split k so that about 2048 workgroups stream the
+    // weights; the binary32 partial sums [splits, m, n] live in the workspace.
+    p.splits = 1;
+    p.k_chunk = k;
+    if (p.variant == dq::WQ_VAR_MFMA) {
+        const int64_t tiles = ((n + dq::wq_tile_cols(p.tile) - 1) / dq::wq_tile_cols(p.tile)) *
+                              ((m + dq::wq_tile_rows(p.tile) - 1) / dq::wq_tile_rows(p.tile));
+        const int64_t batch_k = static_cast<int64_t>(dq::wq_batch(p.tile)) * dq::kWqSuperK;
+        const int64_t batches = (k + batch_k - 1) / batch_k;
+        int64_t want = tiles < kWqTargetBlocks ? (kWqTargetBlocks + tiles - 1) / tiles : 1;
+        want = want < batches ? want : batches;
+        if (want > 1) {
+            p.k_chunk = ((batches + want - 1) / want) * batch_k;
+            p.splits = static_cast<int>((k + p.k_chunk - 1) / p.k_chunk);
+        }
+        if (p.splits > 1)
+            *workspace_size = static_cast<size_t>(p.splits) * static_cast<size_t>(m) * static_cast<size_t>(n) * 4;
+    }
+    *executor = e;
+    return ok();
+}
+
+dq_status dq_weight_quant_matmul(void* workspace, size_t workspace_size, dq_executor* executor,
+                                 hipStream_t stream)
+{
+    if (!executor)
+        return fail(DQ_ERR_NULLPTR, "executor is NULL");
+    dq_executor* e = executor;
+    if (e->op != OP_WEIGHT_QUANT_MATMUL) {
+        delete e;
+        return fail(DQ_ERR_PARAM, "executor was not made by dq_weight_quant_matmul_get_workspace_size");
+    }
+    dq::WqPlan p = e->wq;
+    delete e;
+    if (p.m == 0)
+        return ok();
+    if (p.splits > 1) {
+        const size_t need = static_cast<size_t>(p.splits) * static_cast<size_t>(p.m) * static_cast<size_t>(p.n) * 4;
+        if (!workspace || workspace_size < need)
+            return fail(DQ_ERR_WORKSPACE, "the workspace must hold %zu bytes, got %zu", need, workspace_size);
+        if (!aligned(workspace, 16))
+            return fail(DQ_ERR_ALIGN, "the workspace must be 16-byte aligned");
+    }
+    hipError_t err = dq::launch_weight_quant_matmul(p, workspace, stream);
+    if (err != hipSuccess)
+        return fail(DQ_ERR_RUNTIME, "weight quant matmul launch failed: %s", hipGetErrorString(err));
     return ok();
 }
 

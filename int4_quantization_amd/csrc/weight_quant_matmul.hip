@@ -1,0 +1,762 @@
+// weight_quant_matmul.hip -- x1 @ dequant(x2) + bias + x3 on gfx950: int8 or
+// int4 weights fake-quantized per tensor, per channel or per group down k,
+// then multiplied on the matrix cores.
+//
+// aclnnWeightQuantMatmulAllReduce (API function, constraints) fake-quantizes
+// the weight x2, multiplies, and all-reduces over ranks; on one GPU the
+// all-reduce is the identity.  Its formula is missing from the page; this
+// library reads it with the AntiQuantize arithmetic (kDim = 0):
+//   W[k, n]   = RN_T(RN(RN(x2 + offset) * scale))    (binary32; no offset: RN(x2 * scale))
+//   out[m, n] = RN_T(sum_k x1[m, k] * W[k, n] + bias[n] + x3[m, n])
+// where T is x1's dtype (the constraints give the parameters, bias, x3 and
+// the output that dtype) and the sum is accumulated in binary32.  Products
+// of two bf16 or two fp16 values are exact in binary32, so W is bit-exact
+// and only the order of the binary32 additions differs from an exact sum.
+//
+// wq_mfma_kernel (weights stored [n, k], i.e. x2 transposed, k contiguous):
+//   - A wave computes a (16 RM) x (16 RN) block of out with
+//     v_mfma_f32_16x16x32_{bf16,f16}.  Lane l supplies row (or column) l % 16
+//     and eight k values per instruction, and receives rows 4 (l / 16) ..
+//     + 3 of column l % 16.
+//   - The k axis is walked in supersteps of 128.  Since a dot product does
+//     not depend on the order of k, lane group g = l / 16 takes the 32
+//     consecutive k of [32 g, 32 g + 32) and splits them over the four
+//     instructions of the superstep; x1 uses the same assignment.  Each
+//     lane's weight load is therefore one contiguous 32-byte (int8) or
+//     16-byte (int4) run of its column, and its x1 load four 16-byte runs of
+//     its row.  No LDS is needed: the dequantized weight goes straight from
+//     registers into the matrix cores, and each wave owns its columns.
+//   - Dequantization follows the formula step by step in binary32 (signed
+//     byte or nibble -> binary32, + offset, * scale, round to T), so W is
+//     exact.  A group of 32 k never straddles a parameter group (the group
+//     size is a multiple of 32).
+//   - Rows past m repeat the last row (their results are not stored);
+//     columns past n repeat the last column (likewise).  k runs in whole
+//     groups of 32 (int8) or 64 (int4) elements.
+// wq_generic_kernel: any layout and alignment, one thread per output
+// element, binary32 accumulation in k order.  It is the path for weights
+// stored [k, n].
+
+#include "dq_device.h"
+#include "dq_internal.h"
+
+namespace dq {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWqSuper = kWqSuperK;  // k per superstep: 4 lane groups x 32
+
+// Buffer loads: a 128-bit resource (base, size in bytes) and a 32-bit
+// per-lane offset, so address arithmetic stays 32-bit and constant steps
+// fold into the instruction's offset field.  Reads past the size return 0.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+constexpr int kBufNonTemporal = 2;  // glc/slc/nt bits of the aux operand: nt
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, static_cast<int>(bytes), 0x00020000);
+}
+template <int AUX>
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    const i32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX);
+    return make_uint4(static_cast<uint32_t>(v.x), static_cast<uint32_t>(v.y), static_cast<uint32_t>(v.z),
+                      static_cast<uint32_t>(v.w));
+}
+__device__ __forceinline__ uint16_t buf_load2(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+
+struct WqArgs {
+    const uint16_t* x1;    // [m, k] T
+    const uint8_t* x2;     // int8 [n, k] or int4 [n, k / 2] (fast); [k, n] or [k, n / 2] (generic)
+    const uint16_t* scale;
+    const uint16_t* offset;  // nullptr: none
+    const uint16_t* bias;    // nullptr: none
+    const uint16_t* x3;      // nullptr: none
+    uint16_t* out;           // [m, n] T
+    int64_t m, k, n;
+    int64_t group_size;      // per group only
+    int64_t groups;          // ceil(k / group_size), per group only
+    int64_t k_chunk;         // k per split (a multiple of the batch)
+    float* partial;          // splits > 1: binary32 partial sums [splits, m, n]
+    DivMagic by_gs;          // division by group_size (k indices below 2^31)
+};
+
+template <int XT>
+__device__ __forceinline__ float t_to_f32(uint16_t h) { return widen1<XT>(h); }
+
+// Round a binary32 to T (nearest even), as raw bits.  The empty asm keeps
+// the binary32 value: without it hipcc folds "binary32 multiply or add, then
+// convert to fp16" into v_fma_mix*, which rounds only once.
+template <int XT>
+__device__ __forceinline__ uint16_t f32_to_t(float v)
+{
+    asm("" : "+v"(v));
+    if constexpr (XT == X_BF16) {
+        return __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));
+    } else {
+        return __builtin_bit_cast(uint16_t, static_cast<_Float16>(v));
+    }
+}
+
+// Parameter index of weight column c for the group holding k index kk.
+template <int POL>
+__device__ __forceinline__ int64_t param_index(const WqArgs& a, int64_t c, int64_t kk, bool trans)
+{
+    if constexpr (POL == DQ_PER_TENSOR)
+        return 0;
+    else if constexpr (POL == DQ_PER_CHANNEL)
+        return c;
+    else
+        return trans ? c * a.groups + kk / a.group_size : (kk / a.group_size) * a.n + c;
+}
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two binary32 values rounded to T (nearest even) in one packed conversion
+// (v_cvt_pk_bf16_f32 / v_cvt_pk_f16_f32).  For fp16 the empty asm keeps the
+// binary32 inputs: otherwise hipcc may fold "binary32 multiply, then
+// convert to fp16" into v_fma_mix*, which rounds only once.
+template <int XT>
+__device__ __forceinline__ uint32_t pack2_t(float a, float b)
+{
+    const f32x2 v = {a, b};
+    if constexpr (XT == X_BF16) {
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+    } else {
+        asm("" : "+v"(a), "+v"(b));
+        const f32x2 w = {a, b};
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(w, f16x2));
+    }
+}
+
+// Eight binary32 values rounded to T and packed as one MFMA operand.
+template <int XT>
+__device__ __forceinline__ uint4 pack8_t(const float (&w)[8])
+{
+    return make_uint4(pack2_t<XT>(w[0], w[1]), pack2_t<XT>(w[2], w[3]), pack2_t<XT>(w[4], w[5]),
+                      pack2_t<XT>(w[6], w[7]));
+}
+
+template <int XT>
+__device__ __forceinline__ f32x4 mfma16(const uint4& a, const uint4& b, const f32x4& c)
+{
+    if constexpr (XT == X_BF16)
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                       0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
+                                                      0, 0, 0);
+}
+
+// The integer codes of a lane's 32 consecutive k of one column, as
+// binary32, each converted from a sign-extended byte in one instruction
+// (v_cvt_f32_i32 with an SDWA byte select).  int8: the codes themselves.
+// int4: each nibble is first moved to the high half of a byte, so the byte
+// reads 16 * code; the caller folds the factor 16 back exactly.
+template <int WT>
+__device__ __forceinline__ void decode32(const uint4& lo, const uint4& hi, float (&v)[32])
+{
+    if constexpr (WT == WQ_I8) {
+        const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+        for (int i = 0; i < 32; ++i)
+            v[i] = static_cast<float>(static_cast<int8_t>(w[i / 4] >> (8 * (i % 4))));
+    } else {
+        const uint32_t w[4] = {lo.x, lo.y, lo.z, lo.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t even = (w[q] << 4) & 0xF0F0F0F0u;  // nibbles 0, 2, 4, 6
+            const uint32_t odd = w[q] & 0xF0F0F0F0u;          // nibbles 1, 3, 5, 7
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                v[8 * q + 2 * j] = static_cast<float>(static_cast<int8_t>(even >> (8 * j)));
+                v[8 * q + 2 * j + 1] = static_cast<float>(static_cast<int8_t>(odd >> (8 * j)));
+            }
+        }
+    }
+}
+
+// Eight of the 32 codes (sub-step s of a lane's run), as decode32 gives them.
+template <int WT>
+__device__ __forceinline__ void decode8(const uint4& lo, const uint4& hi, int s, float (&v)[8])
+{
+    if constexpr (WT == WQ_I8) {
+        const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            v[i] = static_cast<float>(static_cast<int8_t>(w[2 * s + i / 4] >> (8 * (i % 4))));
+    } else {
+        const uint32_t w[4] = {lo.x, lo.y, lo.z, lo.w};
+        const uint32_t even = (w[s] << 4) & 0xF0F0F0F0u, odd = w[s] & 0xF0F0F0F0u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            v[2 * j] = static_cast<float>(static_cast<int8_t>(even >> (8 * j)));
+            v[2 * j + 1] = static_cast<float>(static_cast<int8_t>(odd >> (8 * j)));
+        }
+    }
+}
+
+// One weight, from the decoded value d (the code, or 16 * code for int4):
+//   offset: RN(RN(code + o) * s)        no offset: RN(code * s)
+// For int4 without offset the scale arrives as s / 16, an exact power-of-two
+// scaling of a bf16 / fp16 value (binary32 keeps its bits down to 2^-149),
+// so d * (s / 16) is the same real product.  With offset the code is
+// recovered exactly as d / 16 first.
+template <int WT, bool OFF>
+__device__ __forceinline__ float dequant1(float d, float s, float o)
+{
+    if constexpr (OFF) {
+        const float code = WT == WQ_I4 ? d * 0.0625f : d;
+        const float u = code + o;
+        return u * s;
+    } else {
+        return d * s;
+    }
+}
+
+template <int XT, int WT, int POL, bool OFF, int RM, int RN, int U>
+__global__ __launch_bounds__(kBlock) void wq_mfma_kernel(const WqArgs a)
+{
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const int li = lane % 16, g = lane / 16;
+    const int64_t m0 = static_cast<int64_t>(blockIdx.y) * (16 * RM);
+    const int64_t n0 = (static_cast<int64_t>(blockIdx.x) * (kBlock / kWave) + wave) * (16 * RN);
+    constexpr int64_t kBytes32 = WT == WQ_I8 ? 32 : 16;  // weight bytes of 32 k
+
+    const uint16_t* arow[RM];
+#pragma unroll
+    for (int r = 0; r < RM; ++r) {
+        const int64_t row = m0 + 16 * r + li;
+        arow[r] = a.x1 + (row < a.m ? row : a.m - 1) * a.k;
+    }
+    const uint8_t* bcol[RN];
+    int64_t col[RN];
+#pragma unroll
+    for (int t = 0; t < RN; ++t) {
+        const int64_t c = n0 + 16 * t + li;
+        col[t] = c < a.n ? c : a.n - 1;
+        bcol[t] = a.x2 + col[t] * (a.k / 32) * kBytes32;
+    }
+    float s_chan[RN] = {}, o_chan[RN] = {};
+    if constexpr (POL != DQ_PER_GROUP) {
+#pragma unroll
+        for (int t = 0; t < RN; ++t) {
+            const int64_t p = param_index<POL>(a, col[t], 0, true);
+            s_chan[t] = t_to_f32<XT>(a.scale[p]);
+            o_chan[t] = OFF ? t_to_f32<XT>(a.offset[p]) : 0.0f;
+        }
+    }
+
+    f32x4 acc[RM][RN];
+#pragma unroll
+    for (int r = 0; r < RM; ++r)
+#pragma unroll
+        for (int t = 0; t < RN; ++t)
+            acc[r][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    // U supersteps per batch: every load of the batch is issued before any
+    // arithmetic, so U weight runs and U x1 runs per lane are in flight.
+    const int64_t k_beg = static_cast<int64_t>(blockIdx.z) * a.k_chunk;
+    const int64_t k_end = k_beg + a.k_chunk < a.k ? k_beg + a.k_chunk : a.k;
+    for (int64_t kb = k_beg; kb < k_end; kb += U * kWqSuper) {
+        uint4 bw[U][RN][2];
+        uint4 av[U][RM][4];
+        int64_t kcs[U];
+        bool live[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t kg = kb + u * kWqSuper + 32 * g;  // this lane group's 32 k
+            live[u] = kg < k_end;                               // k is a multiple of 32
+            kcs[u] = live[u] ? kg : 0;
+#pragma unroll
+            for (int t = 0; t < RN; ++t) {
+                const uint8_t* p = bcol[t] + (kcs[u] / 32) * kBytes32;
+                bw[u][t][0] = ld_stream16(p);
+                bw[u][t][1] = WT == WQ_I8 ? ld_stream16(p + 16) : make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+            for (int r = 0; r < RM; ++r)
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+                    av[u][r][s] = *reinterpret_cast<const uint4*>(arow[r] + kcs[u] + 8 * s);
+        }
+        float sg[U][RN], og[U][RN];
+        if constexpr (POL == DQ_PER_GROUP) {
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int t = 0; t < RN; ++t) {
+                    const int64_t p = param_index<POL>(a, col[t], kcs[u], true);
+                    sg[u][t] = t_to_f32<XT>(a.scale[p]);
+                    og[u][t] = OFF ? t_to_f32<XT>(a.offset[p]) : 0.0f;
+                }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            uint4 bv[RN][4];
+#pragma unroll
+            for (int t = 0; t < RN; ++t) {
+                float sc = POL == DQ_PER_GROUP ? sg[u][t] : s_chan[t];
+                const float of = POL == DQ_PER_GROUP ? og[u][t] : o_chan[t];
+                if constexpr (WT == WQ_I4 && !OFF)
+                    sc *= 0.0625f;  // the decoded values are 16 * code
+                float v[32];
+                decode32<WT>(bw[u][t][0], bw[u][t][1], v);
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    float w[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        w[j] = dequant1<WT, OFF>(v[8 * s + j], sc, of);
+                    bv[t][s] = pack8_t<XT>(w);
+                }
+            }
+            if (!live[u]) {
+#pragma unroll
+                for (int r = 0; r < RM; ++r)
+#pragma unroll
+                    for (int s = 0; s < 4; ++s)
+                        av[u][r][s] = make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int r = 0; r < RM; ++r)
+#pragma unroll
+                    for (int t = 0; t < RN; ++t)
+                        acc[r][t] = mfma16<XT>(av[u][r][s], bv[t][s], acc[r][t]);
+        }
+    }
+
+    // Epilogue: lane holds rows 4 g .. 4 g + 3 of column li of each block.
+    // With several splits of k, each writes its binary32 partial sums and
+    // wq_reduce_kernel finishes the sum, bias and x3 in a fixed order.
+    if (a.partial) {
+#pragma unroll
+        for (int t = 0; t < RN; ++t) {
+            const int64_t c = n0 + 16 * t + li;
+            if (c >= a.n)
+                continue;
+#pragma unroll
+            for (int r = 0; r < RM; ++r)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int64_t row = m0 + 16 * r + 4 * g + i;
+                    if (row < a.m)
+                        a.partial[(static_cast<int64_t>(blockIdx.z) * a.m + row) * a.n + c] = acc[r][t][i];
+                }
+        }
+        return;
+    }
+#pragma unroll
+    for (int t = 0; t < RN; ++t) {
+        const int64_t c = n0 + 16 * t + li;
+        if (c >= a.n)
+            continue;
+        const float b = a.bias ? t_to_f32<XT>(a.bias[c]) : 0.0f;
+#pragma unroll
+        for (int r = 0; r < RM; ++r) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int64_t row = m0 + 16 * r + 4 * g + i;
+                if (row >= a.m)
+                    continue;
+                float v = acc[r][t][i] + b;
+                if (a.x3)
+                    v += t_to_f32<XT>(a.x3[row * a.n + c]);
+                a.out[row * a.n + c] = f32_to_t<XT>(v);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Decode-shaped kernel: at most 16 rows of x1, so the weights dominate the
+// traffic.  A wave owns 16 RN columns; a workgroup (four waves) stages the
+// x1 k-slice of each batch (U supersteps) in LDS once for its four waves,
+// double-buffered, and each wave keeps the next batch's weight and
+// parameter loads in flight while it dequantizes and multiplies the
+// current one.  k is split across workgroups (blockIdx.z) as planned on the
+// host.
+// ---------------------------------------------------------------------------
+template <int XT, int WT, int POL, bool OFF, int RN, int U>
+__global__ __launch_bounds__(kBlock) void wq_decode_kernel(const WqArgs a)
+{
+    constexpr int BK = U * kWqSuper;       // k per batch
+    constexpr int ROWB = BK * 2 + 16;      // LDS bytes per staged x1 row (16-byte pad: no bank conflicts)
+    constexpr int XV = BK / 8;             // 16-byte x1 vectors per row and batch
+    constexpr int XP = 16 * XV / kBlock;   // staged vectors per thread and batch
+    static_assert(XP * kBlock == 16 * XV, "a batch of 16 rows divides over the workgroup");
+    constexpr int64_t kBytes32 = WT == WQ_I8 ? 32 : 16;  // weight bytes of 32 k
+    constexpr int WV = WT == WQ_I8 ? 2 : 1;              // 16-byte weight loads per 32 k
+    __shared__ __align__(16) uint8_t xs[2][16 * ROWB];
+
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int li = lane % 16, g = lane / 16;
+    const int64_t n0 = (static_cast<int64_t>(blockIdx.x) * (kBlock / kWave) + wave) * (16 * RN);
+    const int64_t k_beg = static_cast<int64_t>(blockIdx.z) * a.k_chunk;
+    const int64_t k_end = k_beg + a.k_chunk < a.k ? k_beg + a.k_chunk : a.k;
+    const int nb = static_cast<int>((k_end - k_beg + BK - 1) / BK);
+
+    // Weight rows of at most 65535 x 65535 codes fit 32-bit byte offsets.
+    const __amdgpu_buffer_rsrc_t wrs = make_rsrc(a.x2, static_cast<uint32_t>(a.n * (a.k / 32) * kBytes32));
+    const __amdgpu_buffer_rsrc_t xrs = make_rsrc(a.x1, static_cast<uint32_t>(a.m * a.k * 2));
+    uint32_t wcol[RN];  // byte offset of this lane's column and lane group
+    int64_t col[RN];
+#pragma unroll
+    for (int t = 0; t < RN; ++t) {
+        const int64_t c = n0 + 16 * t + li;
+        col[t] = c < a.n ? c : a.n - 1;
+        wcol[t] = static_cast<uint32_t>(col[t] * (a.k / 32) * kBytes32);
+    }
+    float s_chan[RN], o_chan[RN];
+#pragma unroll
+    for (int t = 0; t < RN; ++t) {
+        s_chan[t] = 0.0f;
+        o_chan[t] = 0.0f;
+    }
+    if constexpr (POL != DQ_PER_GROUP) {
+#pragma unroll
+        for (int t = 0; t < RN; ++t) {
+            const int64_t p = param_index<POL>(a, col[t], 0, true);
+            s_chan[t] = t_to_f32<XT>(a.scale[p]);
+            o_chan[t] = OFF ? t_to_f32<XT>(a.offset[p]) : 0.0f;
+        }
+    }
+    const __amdgpu_buffer_rsrc_t srs = make_rsrc(a.scale, static_cast<uint32_t>(a.n * a.groups * 2));
+    const __amdgpu_buffer_rsrc_t ors = make_rsrc(OFF ? a.offset : a.scale, static_cast<uint32_t>(a.n * a.groups * 2));
+
+    // Loads of batch b (clamped to the last batch: a repeat is harmless).
+    // x1: vector q = p * kBlock + tid of the 16 x XV grid; rows past m and
+    // k past the split are zeros.
+    auto load_x = [&](int b, uint4 (&xr)[XP]) {
+        const int bb = b < nb ? b : nb - 1;
+#pragma unroll
+        for (int p = 0; p < XP; ++p) {
+            const int q = p * kBlock + tid, row = q / XV, kv = q % XV;
+            const uint32_t kk = static_cast<uint32_t>(k_beg + static_cast<int64_t>(bb) * BK) + kv * 8;
+            const bool ok = row < a.m && kk < k_end;
+            const uint32_t rr = static_cast<uint32_t>(row < a.m ? row : a.m - 1);
+            const uint32_t kc = ok ? kk : static_cast<uint32_t>(k_beg);
+            const uint4 v = buf_load16<0>(xrs, (rr * static_cast<uint32_t>(a.k) + kc) * 2);
+            xr[p] = ok ? v : make_uint4(0, 0, 0, 0);
+        }
+    };
+    auto store_x = [&](int buf, const uint4 (&xr)[XP]) {
+#pragma unroll
+        for (int p = 0; p < XP; ++p) {
+            const int q = p * kBlock + tid, row = q / XV, kv = q % XV;
+            *reinterpret_cast<uint4*>(&xs[buf][row * ROWB + kv * 16]) = xr[p];
+        }
+    };
+    // Weights (and per-group parameters) of batch b for this lane: 32 k per
+    // superstep, at k = batch start + 128 u + 32 g.
+    auto load_w = [&](int b, uint4 (&w)[U][RN][WV], float (&sg)[U][RN], float (&og)[U][RN]) {
+        const int bb = b < nb ? b : nb - 1;
+        const uint32_t kb = static_cast<uint32_t>(k_beg + static_cast<int64_t>(bb) * BK);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t kg = kb + u * kWqSuper + 32 * g;
+            const uint32_t kc = kg < k_end ? kg : static_cast<uint32_t>(k_beg);
+#pragma unroll
+            for (int t = 0; t < RN; ++t) {
+                const uint32_t off = wcol[t] + (kc / 32) * static_cast<uint32_t>(kBytes32);
+                w[u][t][0] = buf_load16<kBufNonTemporal>(wrs, off);
+                if constexpr (WV == 2)
+                    w[u][t][WV - 1] = buf_load16<kBufNonTemporal>(wrs, off + 16);
+                if constexpr (POL == DQ_PER_GROUP) {
+                    const uint32_t pi = static_cast<uint32_t>(col[t] * a.groups) + div_by(kc, a.by_gs);
+                    sg[u][t] = t_to_f32<XT>(buf_load2(srs, pi * 2));
+                    og[u][t] = OFF ? t_to_f32<XT>(buf_load2(ors, pi * 2)) : 0.0f;
+                }
+            }
+        }
+    };
+
+    f32x4 acc[RN];
+#pragma unroll
+    for (int t = 0; t < RN; ++t)
+        acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    auto compute = [&](int buf, const uint4 (&w)[U][RN][WV], const float (&sg)[U][RN], const float (&og)[U][RN]) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            uint4 av[4];
+#pragma unroll
+            for (int s2 = 0; s2 < 4; ++s2)
+                av[s2] = *reinterpret_cast<const uint4*>(&xs[buf][li * ROWB + (u * kWqSuper + 32 * g + 8 * s2) * 2]);
+#pragma unroll
+            for (int t = 0; t < RN; ++t) {
+                float sc = s_chan[t], of = o_chan[t];
+                if constexpr (POL == DQ_PER_GROUP) {
+                    sc = sg[u][t];
+                    of = og[u][t];
+                }
+                uint4 bv[4];
+                if constexpr (WT == WQ_I4 && OFF) {
+                    // v = 16 code: RN(v + 16 o) = 16 RN(code + o) and s / 16 is
+                    // exact, so RN(RN(v + 16 o) * (s / 16)) is the formula,
+                    // unless 16 o overflows (|o| near the binary32 limit).
+                    const float o16 = of * 16.0f, s16 = sc * 0.0625f;
+                    const bool huge = __builtin_isinf(o16);
+#pragma unroll
+                    for (int s2 = 0; s2 < 4; ++s2) {
+                        float v[8], wv[8];
+                        decode8<WT>(w[u][t][0], w[u][t][WV - 1], s2, v);
+                        if (__builtin_expect(huge, 0)) {
+#pragma unroll 1
+                            for (int j = 0; j < 8; ++j)
+                                wv[j] = dequant1<WT, true>(v[j], sc, of);
+                        } else {
+#pragma unroll
+                            for (int j = 0; j < 8; ++j)
+                                wv[j] = (v[j] + o16) * s16;
+                        }
+                        bv[s2] = pack8_t<XT>(wv);
+                    }
+                } else {
+                    const float sc_eff = WT == WQ_I4 ? sc * 0.0625f : sc;
+#pragma unroll
+                    for (int s2 = 0; s2 < 4; ++s2) {
+                        float v[8], wv[8];
+                        decode8<WT>(w[u][t][0], w[u][t][WV - 1], s2, v);
+#pragma unroll
+                        for (int j = 0; j < 8; ++j)
+                            wv[j] = dequant1<WQ_I8, OFF>(v[j], sc_eff, of);
+                        bv[s2] = pack8_t<XT>(wv);
+                    }
+                }
+#pragma unroll
+                for (int s2 = 0; s2 < 4; ++s2)
+                    acc[t] = mfma16<XT>(av[s2], bv[s2], acc[t]);
+            }
+        }
+    };
+
+    // Two register sets and two LDS buffers alternate: batch b + 1 is loaded
+    // while batch b is computed.  nb is uniform (no batch when k is empty).
+    if (nb > 0) {
+        uint4 wA[U][RN][WV], wB[U][RN][WV];
+        float sA[U][RN], oA[U][RN], sB[U][RN], oB[U][RN];
+        uint4 xr[XP];
+        load_x(0, xr);
+        load_w(0, wA, sA, oA);
+        store_x(0, xr);
+        __syncthreads();
+        for (int b = 0; b < nb; b += 2) {
+            load_x(b + 1, xr);
+            load_w(b + 1, wB, sB, oB);
+            compute(0, wA, sA, oA);
+            store_x(1, xr);
+            __syncthreads();
+            if (b + 1 >= nb)
+                break;
+            load_x(b + 2, xr);
+            load_w(b + 2, wA, sA, oA);
+            compute(1, wB, sB, oB);
+            store_x(0, xr);
+            __syncthreads();
+        }
+    }
+
+    // Epilogue: lane holds rows 4 g .. 4 g + 3 of column li.
+#pragma unroll
+    for (int t = 0; t < RN; ++t) {
+        const int64_t c = n0 + 16 * t + li;
+        if (c >= a.n)
+            continue;
+        const float bias = a.bias && !a.partial ? t_to_f32<XT>(a.bias[c]) : 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t row = 4 * g + i;
+            if (row >= a.m)
+                continue;
+            if (a.partial) {
+                a.partial[(static_cast<int64_t>(blockIdx.z) * a.m + row) * a.n + c] = acc[t][i];
+            } else {
+                float v = acc[t][i] + bias;
+                if (a.x3)
+                    v += t_to_f32<XT>(a.x3[row * a.n + c]);
+                a.out[row * a.n + c] = f32_to_t<XT>(v);
+            }
+        }
+    }
+}
+
+template <int XT, int WT>
+__global__ __launch_bounds__(kBlock) void wq_generic_kernel(const WqArgs a, int pol, bool trans)
+{
+    const int64_t idx = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
+    if (idx >= a.m * a.n)
+        return;
+    const int64_t row = idx / a.n, c = idx - row * a.n;
+    float acc = 0.0f;
+    float s = 0.0f, o = 0.0f;
+    if (pol != DQ_PER_GROUP) {
+        const int64_t p = pol == DQ_PER_TENSOR ? 0 : c;
+        s = t_to_f32<XT>(a.scale[p]);
+        o = a.offset ? t_to_f32<XT>(a.offset[p]) : 0.0f;
+    }
+    for (int64_t kk = 0; kk < a.k; ++kk) {
+        if (pol == DQ_PER_GROUP && kk % a.group_size == 0) {
+            const int64_t p = trans ? c * a.groups + kk / a.group_size : (kk / a.group_size) * a.n + c;
+            s = t_to_f32<XT>(a.scale[p]);
+            o = a.offset ? t_to_f32<XT>(a.offset[p]) : 0.0f;
+        }
+        const int64_t e = trans ? c * a.k + kk : kk * a.n + c;
+        float v;
+        if constexpr (WT == WQ_I8) {
+            v = static_cast<float>(reinterpret_cast<const int8_t*>(a.x2)[e]);
+        } else {
+            const uint32_t byte = a.x2[e / 2];
+            const int32_t nib = static_cast<int32_t>((e & 1) ? byte >> 4 : byte & 0xFu);
+            v = static_cast<float>(nib >= 8 ? nib - 16 : nib);
+        }
+        const float w = a.offset ? dequant1<WQ_I8, true>(v, s, o) : dequant1<WQ_I8, false>(v, s, o);
+        const float wt = t_to_f32<XT>(f32_to_t<XT>(w));
+        acc += t_to_f32<XT>(a.x1[row * a.k + kk]) * wt;
+    }
+    if (a.bias)
+        acc += t_to_f32<XT>(a.bias[c]);
+    if (a.x3)
+        acc += t_to_f32<XT>(a.x3[row * a.n + c]);
+    a.out[idx] = f32_to_t<XT>(acc);
+}
+
+// out = RN_T(((partial[0] + partial[1]) + ...) + bias + x3), splits in order.
+template <int XT>
+__global__ __launch_bounds__(kBlock) void wq_reduce_kernel(const WqArgs a, int splits)
+{
+    const int64_t idx = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
+    const int64_t total = a.m * a.n;
+    if (idx >= total)
+        return;
+    float v = a.partial[idx];
+    for (int z = 1; z < splits; ++z)
+        v += a.partial[static_cast<int64_t>(z) * total + idx];
+    if (a.bias)
+        v += t_to_f32<XT>(a.bias[idx % a.n]);
+    if (a.x3)
+        v += t_to_f32<XT>(a.x3[idx]);
+    a.out[idx] = f32_to_t<XT>(v);
+}
+
+template <int XT, int WT, int POL, bool OFF, int RM, int RN, int U>
+hipError_t launch_mfma(const WqArgs& a, int splits, hipStream_t stream)
+{
+    const int64_t cols = static_cast<int64_t>(kBlock / kWave) * 16 * RN;
+    const int64_t gx = (a.n + cols - 1) / cols;
+    const int64_t rows = 16 * RM;
+    const int64_t gy_total = (a.m + rows - 1) / rows;
+    constexpr int64_t kMaxY = 65535;
+    if (splits > 1 && gy_total > kMaxY)
+        return hipErrorInvalidConfiguration;  // split k is planned for few rows only
+    for (int64_t y0 = 0; y0 < gy_total; y0 += kMaxY) {
+        WqArgs c = a;
+        c.x1 = a.x1 + y0 * rows * a.k;
+        c.out = a.out + y0 * rows * a.n;
+        c.x3 = a.x3 ? a.x3 + y0 * rows * a.n : nullptr;
+        c.m = a.m - y0 * rows < kMaxY * rows ? a.m - y0 * rows : kMaxY * rows;
+        const int64_t gy = (c.m + rows - 1) / rows;
+        hipLaunchKernelGGL((wq_mfma_kernel<XT, WT, POL, OFF, RM, RN, U>),
+                           dim3(static_cast<uint32_t>(gx), static_cast<uint32_t>(gy), static_cast<uint32_t>(splits)),
+                           dim3(kBlock), 0, stream, c);
+        const hipError_t err = hipGetLastError();
+        if (err != hipSuccess)
+            return err;
+    }
+    if (splits > 1) {
+        const int64_t blocks = (a.m * a.n + kBlock - 1) / kBlock;
+        hipLaunchKernelGGL((wq_reduce_kernel<XT>), dim3(static_cast<uint32_t>(blocks)), dim3(kBlock), 0, stream, a,
+                           splits);
+        return hipGetLastError();
+    }
+    return hipSuccess;
+}
+
+template <int XT, int WT, int POL, bool OFF, int RN, int U>
+hipError_t launch_decode(const WqArgs& a, int splits, hipStream_t stream)
+{
+    const int64_t cols = static_cast<int64_t>(kBlock / kWave) * 16 * RN;
+    const int64_t gx = (a.n + cols - 1) / cols;
+    hipLaunchKernelGGL((wq_decode_kernel<XT, WT, POL, OFF, RN, U>),
+                       dim3(static_cast<uint32_t>(gx), 1, static_cast<uint32_t>(splits)), dim3(kBlock), 0, stream, a);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess || splits == 1)
+        return err;
+    const int64_t blocks = (a.m * a.n + kBlock - 1) / kBlock;
+    hipLaunchKernelGGL((wq_reduce_kernel<XT>), dim3(static_cast<uint32_t>(blocks)), dim3(kBlock), 0, stream, a, splits);
+    return hipGetLastError();
+}
+
+template <int XT, int WT, int POL, bool OFF>
+hipError_t pick_tile(const WqPlan& p, const WqArgs& a, hipStream_t stream)
+{
+    if (p.tile == WQ_TILE_DECODE)
+        return launch_decode<XT, WT, POL, OFF, kWqDecodeCols, wq_batch(WQ_TILE_DECODE)>(a, p.splits, stream);
+    if (p.tile == WQ_TILE_2x2)
+        return launch_mfma<XT, WT, POL, OFF, 2, 2, wq_batch(WQ_TILE_2x2)>(a, p.splits, stream);
+    return launch_mfma<XT, WT, POL, OFF, 4, 4, wq_batch(WQ_TILE_4x4)>(a, p.splits, stream);
+}
+
+template <int XT, int WT, int POL>
+hipError_t pick_off(const WqPlan& p, const WqArgs& a, hipStream_t stream)
+{
+    return a.offset ? pick_tile<XT, WT, POL, true>(p, a, stream) : pick_tile<XT, WT, POL, false>(p, a, stream);
+}
+
+template <int XT, int WT>
+hipError_t launch_wt(const WqPlan& p, const WqArgs& a, hipStream_t stream)
+{
+    if (p.variant == WQ_VAR_GENERIC) {
+        const int64_t total = a.m * a.n;
+        const int64_t blocks = (total + kBlock - 1) / kBlock;
+        if (blocks > kMaxGridBlocks)
+            return hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL((wq_generic_kernel<XT, WT>), dim3(static_cast<uint32_t>(blocks)), dim3(kBlock), 0, stream, a,
+                           p.policy, p.transpose_x2);
+        return hipGetLastError();
+    }
+    switch (p.policy) {
+    case DQ_PER_TENSOR: return pick_off<XT, WT, DQ_PER_TENSOR>(p, a, stream);
+    case DQ_PER_CHANNEL: return pick_off<XT, WT, DQ_PER_CHANNEL>(p, a, stream);
+    default: return pick_off<XT, WT, DQ_PER_GROUP>(p, a, stream);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_weight_quant_matmul(const WqPlan& p, void* workspace, hipStream_t stream)
+{
+    if (p.m == 0 || p.n == 0)
+        return hipSuccess;
+    WqArgs a;
+    a.x1 = static_cast<const uint16_t*>(p.x1);
+    a.x2 = static_cast<const uint8_t*>(p.x2);
+    a.scale = static_cast<const uint16_t*>(p.scale);
+    a.offset = static_cast<const uint16_t*>(p.offset);
+    a.bias = static_cast<const uint16_t*>(p.bias);
+    a.x3 = static_cast<const uint16_t*>(p.x3);
+    a.out = static_cast<uint16_t*>(p.out);
+    a.m = p.m;
+    a.k = p.k;
+    a.n = p.n;
+    a.group_size = p.group_size > 0 ? p.group_size : 1;
+    a.groups = p.group_size > 0 ? (p.k + p.group_size - 1) / p.group_size : 1;
+    a.k_chunk = p.k_chunk;
+    a.partial = p.splits > 1 ? static_cast<float*>(workspace) : nullptr;
+    a.by_gs = div_magic(static_cast<uint64_t>(a.group_size));
+    if (p.x_type == X_BF16)
+        return p.w_type == WQ_I8 ? launch_wt<X_BF16, WQ_I8>(p, a, stream) : launch_wt<X_BF16, WQ_I4>(p, a, stream);
+    return p.w_type == WQ_I8 ? launch_wt<X_F16, WQ_I8>(p, a, stream) : launch_wt<X_F16, WQ_I4>(p, a, stream);
+}
+
+}  // namespace dq

@@ -39,6 +39,7 @@ EXPORTS = [
     "dq_ada_layernorm_quant_get_workspace_size", "dq_ada_layernorm_quant",
     "dq_antiquantize_get_workspace_size", "dq_antiquantize",
     "dq_mx_quantize_get_workspace_size", "dq_mx_quantize",
+    "dq_weight_quant_matmul_get_workspace_size", "dq_weight_quant_matmul",
     "dq_executor_destroy", "dq_get_last_error", "dq_copy_probe",
 ]
 
@@ -84,8 +85,12 @@ def library() -> ctypes.CDLL:
         lib.dq_mx_quantize_get_workspace_size.argtypes = [
             _P(DqTensor), ctypes.c_int32, _P(DqTensor), _P(DqTensor), _P(ctypes.c_size_t), _P(_vp)]
         lib.dq_mx_quantize_get_workspace_size.restype = st
+        lib.dq_weight_quant_matmul_get_workspace_size.argtypes = [
+            _P(DqTensor), _P(DqTensor), ctypes.c_int32, _P(DqTensor), _P(DqTensor), ctypes.c_int64,
+            _P(DqTensor), _P(DqTensor), _P(DqTensor), _P(ctypes.c_size_t), _P(_vp)]
+        lib.dq_weight_quant_matmul_get_workspace_size.restype = st
         for name in ("dq_dynamic_quant", "dq_ada_layernorm_quant", "dq_antiquantize",
-                     "dq_mx_quantize"):
+                     "dq_mx_quantize", "dq_weight_quant_matmul"):
             fn = getattr(lib, name)
             fn.argtypes = [_vp, ctypes.c_size_t, _vp, _vp]
             fn.restype = st
@@ -235,6 +240,40 @@ def dq_mx_quantize(workspace, workspace_size: int, executor: int, stream=None) -
                                     _stream_handle(stream)))
 
 
+def _w_desc(x2, weight: Optional[str]):
+    """int8 weights as they are; int4 weights travel as uint8 bytes holding two
+    codes each along the stored last dimension."""
+    if weight is None:
+        weight = "int8" if x2.dtype == torch.int8 else "int4"
+    if weight == "int4":
+        r, c = x2.shape
+        return tensor_desc(x2, I4, [r, 2 * c])
+    return tensor_desc(x2, I8)
+
+
+def _wq_descs(x1, x2, antiquant_scale, antiquant_offset, bias, x3, out, weight):
+    return [tensor_desc(x1), _w_desc(x2, weight), tensor_desc(antiquant_scale),
+            tensor_desc(antiquant_offset), tensor_desc(bias), tensor_desc(x3), tensor_desc(out)]
+
+
+def dq_weight_quant_matmul_get_workspace_size(x1, x2, transpose_x2, antiquant_scale,
+                                              antiquant_offset, group_size, bias, x3, out,
+                                              weight: Optional[str] = None) -> Tuple[int, int]:
+    lib = library()
+    d = _wq_descs(x1, x2, antiquant_scale, antiquant_offset, bias, x3, out, weight)
+    ws = ctypes.c_size_t(0)
+    ex = _vp(None)
+    _check(lib.dq_weight_quant_matmul_get_workspace_size(
+        _ref(d[0]), _ref(d[1]), 1 if transpose_x2 else 0, _ref(d[2]), _ref(d[3]), int(group_size),
+        _ref(d[4]), _ref(d[5]), _ref(d[6]), ctypes.byref(ws), ctypes.byref(ex)))
+    return ws.value, ex.value
+
+
+def dq_weight_quant_matmul(workspace, workspace_size: int, executor: int, stream=None) -> None:
+    _check(library().dq_weight_quant_matmul(_ws_ptr(workspace), workspace_size, executor,
+                                            _stream_handle(stream)))
+
+
 def dq_executor_destroy(executor: int) -> None:
     library().dq_executor_destroy(executor)
 
@@ -262,25 +301,34 @@ def _workspace(size: int, device) -> Optional[torch.Tensor]:
 class PreparedCall:
     """Both phases of one op with fixed tensors: the dq_tensor descriptors are
     built once, so each call is the get-workspace-size call plus the execute
-    call (two C calls, no per-call Python marshalling of tensors).  The op
-    needs no workspace; a nonzero size raises."""
+    call (two C calls, no per-call Python marshalling of tensors).  A
+    workspace, when the op asks for one, is allocated on the first call and
+    reused while it is large enough."""
 
-    def __init__(self, phase1, execute, args, keep):
+    def __init__(self, phase1, execute, args, keep, device=None):
         self._phase1 = phase1
         self._execute = execute
         self._ws = ctypes.c_size_t(0)
         self._ex = _vp(None)
         self._args = tuple(args) + (ctypes.byref(self._ws), ctypes.byref(self._ex))
         self._keep = keep  # descriptors and tensors referenced by the args
+        self._device = device
+        self._workspace: Optional[torch.Tensor] = None
 
     def __call__(self, stream=None) -> None:
         st = self._phase1(*self._args)
         if st != SUCCESS:
             raise DquantError(st, dq_get_last_error())
-        if self._ws.value:
-            library().dq_executor_destroy(self._ex)
-            raise DquantError(ERR_WORKSPACE, "prepared calls take ops without workspace")
-        st = self._execute(None, 0, self._ex, _stream_handle(stream))
+        size = self._ws.value
+        ptr = None
+        if size:
+            if self._device is None:
+                library().dq_executor_destroy(self._ex)
+                raise DquantError(ERR_WORKSPACE, "this prepared call has no device for a workspace")
+            if self._workspace is None or self._workspace.numel() < size:
+                self._workspace = torch.empty(size, dtype=torch.uint8, device=self._device)
+            ptr = self._workspace.data_ptr()
+        st = self._execute(ptr, size, self._ex, _stream_handle(stream))
         if st != SUCCESS:
             raise DquantError(st, dq_get_last_error())
 
@@ -322,6 +370,17 @@ def prepare_mx_quantize(x, axis: int, y, scale) -> PreparedCall:
     args = [_ref(d[0]), int(axis), _ref(d[1]), _ref(d[2])]
     return PreparedCall(lib.dq_mx_quantize_get_workspace_size, lib.dq_mx_quantize, args,
                         (d, x, y, scale))
+
+
+def prepare_weight_quant_matmul(x1, x2, transpose_x2, antiquant_scale, antiquant_offset, group_size,
+                                bias, x3, out, weight: Optional[str] = None) -> PreparedCall:
+    lib = library()
+    d = _wq_descs(x1, x2, antiquant_scale, antiquant_offset, bias, x3, out, weight)
+    args = [_ref(d[0]), _ref(d[1]), 1 if transpose_x2 else 0, _ref(d[2]), _ref(d[3]),
+            ctypes.c_int64(int(group_size)), _ref(d[4]), _ref(d[5]), _ref(d[6])]
+    return PreparedCall(lib.dq_weight_quant_matmul_get_workspace_size, lib.dq_weight_quant_matmul,
+                        args, (d, x1, x2, antiquant_scale, antiquant_offset, bias, x3, out),
+                        device=out.device)
 
 
 # -- convenience wrappers ------------------------------------------------------
@@ -404,3 +463,20 @@ def mx_quantize(x: torch.Tensor, elem: torch.dtype = torch.float8_e4m3fn, axis: 
     ws, ex = dq_mx_quantize_get_workspace_size(x, axis, y, scale)
     dq_mx_quantize(_workspace(ws, x.device), ws, ex, stream)
     return y, scale
+
+
+def weight_quant_matmul(x1: torch.Tensor, x2: torch.Tensor, antiquant_scale: torch.Tensor,
+                        antiquant_offset: Optional[torch.Tensor] = None, group_size: int = 0,
+                        bias: Optional[torch.Tensor] = None, x3: Optional[torch.Tensor] = None,
+                        transpose_x2: bool = True, weight: Optional[str] = None,
+                        stream=None) -> torch.Tensor:
+    """x1 @ dequant(x2) + bias + x3 in x1's dtype.  x2: int8 [n, k]
+    (transpose_x2) or [k, n]; int4 weights as uint8 bytes [n, k/2] or
+    [k, n/2] (weight='int4' or any uint8 tensor)."""
+    n = x2.shape[0] if transpose_x2 else x2.shape[1] * (2 if x2.dtype == torch.uint8 else 1)
+    out = torch.empty(tuple(x1.shape[:-1]) + (n,), dtype=x1.dtype, device=x1.device)
+    ws, ex = dq_weight_quant_matmul_get_workspace_size(x1, x2, transpose_x2, antiquant_scale,
+                                                       antiquant_offset, group_size, bias, x3, out,
+                                                       weight)
+    dq_weight_quant_matmul(_workspace(ws, x1.device), ws, ex, stream)
+    return out

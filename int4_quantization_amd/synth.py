@@ -27,6 +27,11 @@ tests use (rows x columns):
                                     workload), blocks of 32 along K
 * ``mx_e4m3_axis0_bf16_7168x8192``  mx block quantization of a weight [K, N],
                                     blocks of 32 down K
+* ``wq_int4_g128_bf16_16x8192x28672``  weight-quantized matmul, decode-shaped:
+                                    16 tokens, int4 weights [n, k] with
+                                    per-group (128) scale and offset, bias
+* ``wq_int8_channel_bf16_4096x8192x8192``  prefill-shaped: 4096 tokens, int8
+                                    weights [n, k], per-channel scale, bias
 """
 from __future__ import annotations
 
@@ -173,6 +178,52 @@ def mx_inputs(rows: int, n: int, seed: int, *, dtype: str = "bfloat16",
     return {"x": _narrow(x, dtype), "elem": elem, "axis": axis}
 
 
+def _pack_nibbles(codes: np.ndarray) -> np.ndarray:
+    """Signed 4-bit codes [r, 2c] -> bytes [r, c], the even element in the low
+    nibble (storage only, no arithmetic of the method)."""
+    u = (codes.astype(np.int16) & 0xF).astype(np.uint8)
+    return np.ascontiguousarray(u[:, 0::2] | (u[:, 1::2] << 4))
+
+
+def wq_inputs(m: int, k: int, n: int, seed: int, *, dtype: str = "bfloat16", weight: str = "int8",
+              group_size: int = 0, per_tensor: bool = False, offset: bool = True, bias: bool = True,
+              x3: bool = False, transpose_x2: bool = True) -> Dict[str, object]:
+    """Inputs of one weight-quantized matmul.
+
+    Draw order: x1 ~ N(0, 1) [m, k]; weight codes ~ U{-128..127} (int8) or
+    U{-8..7} (int4) [k, n]; scale ~ U(0.002, 0.02) and offset ~ U(-2, 2) in
+    the policy's shape ([1]; [n]; or [ceil(k/gs), n]); bias ~ N(0, 1) [n];
+    x3 ~ N(0, 1) [m, n].  With transpose_x2 the codes are stored [n, k] and
+    per-group parameters [n, ceil(k/gs)].  int4 codes travel packed two per
+    byte along the stored last dimension.
+    """
+    rng = np.random.default_rng(seed)
+    x1 = rng.standard_normal((m, k), dtype=np.float32)
+    lo, hi = (-128, 128) if weight == "int8" else (-8, 8)
+    codes = rng.integers(lo, hi, (k, n)).astype(np.int8)
+    if per_tensor:
+        pshape = (1,)
+    elif group_size == 0:
+        pshape = (n,)
+    else:
+        pshape = (-(-k // group_size), n)
+    sc = rng.uniform(0.002, 0.02, pshape).astype(np.float32)
+    of = rng.uniform(-2.0, 2.0, pshape).astype(np.float32) if offset else None
+    b = rng.standard_normal(n).astype(np.float32) if bias else None
+    x3v = rng.standard_normal((m, n)).astype(np.float32) if x3 else None
+    stored = np.ascontiguousarray(codes.T) if transpose_x2 else codes
+    if weight == "int4":
+        x2 = torch.from_numpy(_pack_nibbles(stored))
+    else:
+        x2 = torch.from_numpy(stored)
+    if transpose_x2 and group_size > 0 and not per_tensor:
+        sc, of = np.ascontiguousarray(sc.T), (None if of is None else np.ascontiguousarray(of.T))
+    return {"x1": _narrow(x1, dtype), "x2": x2, "weight": weight, "transpose_x2": transpose_x2,
+            "scale": _narrow(sc, dtype), "offset": None if of is None else _narrow(of, dtype),
+            "group_size": group_size, "bias": None if b is None else _narrow(b, dtype),
+            "x3": None if x3v is None else _narrow(x3v, dtype)}
+
+
 # Full-size workloads: name -> (op, builder).
 WORKLOADS = {
     "dq_sym_f16_64x256": (
@@ -215,4 +266,10 @@ WORKLOADS = {
         "mx_quantize", lambda: mx_inputs(8192, 7168, 9, elem="float4_e2m1x2")),
     "mx_e4m3_axis0_bf16_7168x8192": (
         "mx_quantize", lambda: mx_inputs(7168, 8192, 10, elem="float8_e4m3fn", axis=0)),
+    "wq_int4_g128_bf16_16x8192x28672": (
+        "weight_quant_matmul",
+        lambda: wq_inputs(16, 8192, 28672, 11, weight="int4", group_size=128)),
+    "wq_int8_channel_bf16_4096x8192x8192": (
+        "weight_quant_matmul",
+        lambda: wq_inputs(4096, 8192, 8192, 12, weight="int8", offset=False)),
 }

@@ -6,6 +6,10 @@ Bars:
   scale / offset / dst bits identical (two NaNs compare equal: x86 and the
   GPU produce different default-NaN payloads).
 * mx block quantization: bit-exact codes and scale bytes.
+* Weight-quantized matmul: every element within the binary32 summation
+  bound gamma_{k+2} * (sum |x1 W| + |bias| + |x3|) plus half an ulp of the
+  output type of the oracle's binary64 result, and at least 90% of the
+  elements equal to that result rounded once to the output type.
 * AdaLayerNormQuant: |quantScale - ref| <= 1e-5 * ref, codes within +-1
   everywhere and different on at most 0.01 % of the elements (rounded up to
   a whole element for small cases).
@@ -149,3 +153,66 @@ def check_mx_quantize(orc, x, kind, axis=1, x_dev=None):
     assert gs.shape == rs.shape and gy.shape == ry.shape
     assert np.array_equal(gs, rs), "scale: " + first_mismatch(gs, rs)
     assert np.array_equal(gy, ry), "codes: " + first_mismatch(gy, ry)
+
+
+def half_ulp(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Half the spacing of bf16 / fp16 values at magnitude |x| (subnormal
+    spacing below the smallest normal)."""
+    mbits, emin = (7, -126) if dtype == "bfloat16" else (10, -14)
+    a = np.maximum(np.abs(x), 2.0 ** emin)
+    e = np.floor(np.log2(a))
+    return np.exp2(e - mbits - 1)
+
+
+def wq_oracle_args(q):
+    """The oracle's view of a wq_inputs dict (int4 bytes as a tagged pair)."""
+    x2 = ("int4", q["x2"].numpy()) if q["weight"] == "int4" else q["x2"]
+    if q["group_size"] > 0:
+        policy = "per_group"
+    elif q["scale"].numel() == 1 and q["scale"].dim() == 1:
+        policy = "per_tensor"
+    else:
+        policy = "per_channel"
+    return x2, policy
+
+
+def check_weight_quant_matmul(orc, q, rows=None, dev=None):
+    """GPU out against the oracle; rows: indices of x1 rows to check (all by
+    default), the oracle computing only those.  dev: device inputs to use."""
+    d = dev or {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in q.items()}
+    out = dq.weight_quant_matmul(d["x1"], d["x2"], d["scale"], d["offset"], q["group_size"], d["bias"],
+                                 d["x3"], q["transpose_x2"], q["weight"])
+    torch.cuda.synchronize()
+    m_all = int(np.prod(q["x1"].shape[:-1]))
+    k, n = q["x1"].shape[-1], out.shape[-1]
+    x1 = q["x1"].reshape(m_all, k)
+    x3 = None if q["x3"] is None else q["x3"].reshape(m_all, n)
+    if rows is not None:
+        x1 = x1[rows].contiguous()
+        x3 = None if x3 is None else x3[rows].contiguous()
+    x2, policy = wq_oracle_args(q)
+    ref, mag, _ = orc.weight_quant_matmul(x1, x2, q["scale"], q["offset"], policy, q["group_size"],
+                                          q["transpose_x2"], q["bias"], x3)
+    g = out.reshape(m_all, n).float().cpu().numpy().astype(np.float64)
+    if rows is not None:
+        g = g[rows]
+    tname = "bfloat16" if q["x1"].dtype == torch.bfloat16 else "float16"
+    gamma = (k + 2) * 2.0 ** -24 / (1 - (k + 2) * 2.0 ** -24)
+    extra = np.zeros_like(ref)
+    if q["bias"] is not None:
+        extra += np.abs(q["bias"].double().numpy())[None, :]
+    if x3 is not None:
+        extra += np.abs(x3.double().numpy())
+    bound = gamma * (mag + extra) + half_ulp(np.maximum(np.abs(g), np.abs(ref)), tname)
+    err = np.abs(g - ref)
+    assert np.all(np.isfinite(g)), "non-finite output"
+    bad = err > bound
+    assert not bad.any(), f"{bad.sum()} elements beyond the bound; worst err {err.max():.3g}, bound there " \
+                          f"{bound.reshape(-1)[np.argmax(err)]:.3g}"
+    rounded = orc.f64_to_half(ref, tname)
+    gb = out.reshape(m_all, n).view(torch.int16).cpu().numpy().view(np.uint16)
+    if rows is not None:
+        gb = gb[rows]
+    frac = float(np.mean(gb == rounded)) if gb.size else 1.0
+    assert frac >= 0.9, f"only {frac:.3f} of the elements equal the once-rounded exact result"
+    return frac

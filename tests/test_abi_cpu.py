@@ -350,10 +350,91 @@ def test_mx_binding_shapes():
     assert D.mx_scale_shape(70, 5, 0) == (3, 5)
 
 
+# ---- weight-quantized matmul ----------------------------------------------------
+
+def wq_ws(lib, x1, x2, trans, sc, of, gs, bias, x3, out, keep=False):
+    ws = ctypes.c_size_t(99)
+    ex = ctypes.c_void_p(None)
+    st = lib.dq_weight_quant_matmul_get_workspace_size(ref(x1), ref(x2), trans, ref(sc), ref(of), gs, ref(bias),
+                                                       ref(x3), ref(out), ctypes.byref(ws), ctypes.byref(ex))
+    if st == D.SUCCESS:
+        assert ex.value
+        if keep:
+            return st, ws.value, ex
+        lib.dq_executor_destroy(ex)
+    else:
+        assert ex.value is None
+        assert lib.dq_get_last_error().decode() != ""
+    return st
+
+
+A1, A2, A3, A4 = 0x1000000, 0x3000000, 0x5000000, 0x7000000
+
+
+@pytest.mark.parametrize("xdt,wdt,trans,sshape,gs,status", [
+    (D.BF16, D.I8, 1, [64], 0, D.SUCCESS),                 # per channel, [n, k] weights
+    (D.BF16, D.I8, 1, [1], 0, D.SUCCESS),                  # per tensor
+    (D.F16, D.I4, 1, [64, 2], 128, D.SUCCESS),             # per group, transposed params
+    (D.BF16, D.I4, 0, [2, 64], 128, D.SUCCESS),            # per group, [k, n] weights
+    (D.BF16, D.I8, 1, [2, 64], 128, D.ERR_SHAPE),          # group params not transposed with x2
+    (D.BF16, D.I8, 1, [64, 2], 100, D.ERR_PARAM),          # group size not a multiple of 32
+    (D.BF16, D.I8, 1, [64, 8], -32, D.ERR_PARAM),
+    (D.BF16, D.I8, 1, [7], 0, D.ERR_SHAPE),
+    (D.BF16, D.F32, 1, [64], 0, D.ERR_DTYPE),
+    (D.F32, D.I8, 1, [64], 0, D.ERR_DTYPE),
+])
+def test_wq_validation(lib, xdt, wdt, trans, sshape, gs, status):
+    m, k, n = 16, 256, 64
+    x1 = desc(xdt, [m, k], A1)
+    x2 = desc(wdt, [n, k] if trans else [k, n], A2)
+    sc = desc(xdt if xdt in (D.BF16, D.F16) else D.BF16, sshape, A3)
+    out = desc(xdt, [m, n], A4)
+    assert wq_ws(lib, x1, x2, trans, sc, None, gs, None, None, out) == status
+
+
+def test_wq_shapes_dtypes_overlap(lib):
+    m, k, n = 16, 256, 64
+    x1 = desc(D.BF16, [m, k], A1)
+    x2 = desc(D.I8, [n, k], A2)
+    sc = desc(D.BF16, [n], A3)
+    out = desc(D.BF16, [m, n], A4)
+    assert wq_ws(lib, x1, desc(D.I8, [n, k + 32], A2), 1, sc, None, 0, None, None, out) == D.ERR_SHAPE
+    assert wq_ws(lib, x1, x2, 1, desc(D.F16, [n], A3), None, 0, None, None, out) == D.ERR_DTYPE
+    assert wq_ws(lib, x1, x2, 1, sc, desc(D.BF16, [1], A3 + 0x1000), 0, None, None, out) == D.ERR_SHAPE
+    assert wq_ws(lib, x1, x2, 1, sc, None, 0, desc(D.BF16, [n + 1], A3 + 0x2000), None, out) == D.ERR_SHAPE
+    assert wq_ws(lib, x1, x2, 1, sc, None, 0, None, desc(D.BF16, [m, n + 1], A3 + 0x4000), out) == D.ERR_SHAPE
+    assert wq_ws(lib, x1, x2, 1, sc, None, 0, None, None, desc(D.BF16, [m, n], A1 + 64)) == D.ERR_OVERLAP
+    assert wq_ws(lib, x1, desc(D.I4, [n, 63], A2), 1, sc, None, 0, None, None, out) == D.ERR_SHAPE
+    big = desc(D.I8, [70000, k], A2)
+    assert wq_ws(lib, x1, big, 1, desc(D.BF16, [70000], A3), None, 0, None, None,
+                 desc(D.BF16, [m, 70000], A4)) == D.ERR_SHAPE
+    # 3-D x1 and the empty-k case
+    assert wq_ws(lib, desc(D.BF16, [2, 8, k], A1), x2, 1, sc, None, 0, None, None,
+                 desc(D.BF16, [2, 8, n], A4)) == D.SUCCESS
+    assert wq_ws(lib, desc(D.BF16, [m, 0], A1), desc(D.I8, [n, 0], A2), 1, sc, None, 0, None, None,
+                 out) == D.SUCCESS
+
+
+def test_wq_split_k_workspace(lib):
+    """Few output tiles ask for a workspace of binary32 partial sums; executing
+    without it fails before any launch."""
+    m, k, n = 16, 8192, 256
+    st, ws, ex = wq_ws(lib, desc(D.BF16, [m, k], A1), desc(D.I8, [n, k], A2), 1, desc(D.BF16, [n], A3), None, 0,
+                       None, None, desc(D.BF16, [m, n], A4), keep=True)
+    assert st == D.SUCCESS and ws > 0 and ws % (m * n * 4) == 0
+    assert lib.dq_weight_quant_matmul(None, 0, ex, None) == D.ERR_WORKSPACE
+    n2 = 8192  # enough output tiles: no split, no workspace
+    st, ws2, ex = wq_ws(lib, desc(D.BF16, [4096, k], A1), desc(D.I8, [n2, k], A2), 1, desc(D.BF16, [n2], 0x9000000),
+                        None, 0, None, None, desc(D.BF16, [4096, n2], 0x10000000), keep=True)
+    assert st == D.SUCCESS and ws2 == 0
+    lib.dq_executor_destroy(ex)
+
+
 # ---- execute-phase errors that never reach the device -------------------------
 
 def test_execute_null_executor(lib):
-    for fn in (lib.dq_dynamic_quant, lib.dq_ada_layernorm_quant, lib.dq_antiquantize):
+    for fn in (lib.dq_dynamic_quant, lib.dq_ada_layernorm_quant, lib.dq_antiquantize, lib.dq_mx_quantize,
+               lib.dq_weight_quant_matmul):
         assert fn(None, 0, None, None) == D.ERR_NULLPTR
 
 

@@ -1,0 +1,146 @@
+"""Weight-quantized matmul on the GPU (through the C ABI) against the CPU
+oracle: every element within the binary32 summation bound of the oracle's
+binary64 result, and at least 90% equal to it rounded once.
+
+Covered: int8 and int4 weights stored [n, k] (the matrix-core kernel) and
+[k, n] (the generic kernel); per-tensor, per-channel and per-group (32, 64,
+128, a short last group) parameters, with and without offset; bias and x3;
+bf16 and fp16; m from 1 to several tiles with ragged edges, n ragged, k not
+a multiple of the 128-wide superstep; 3-D x1; the page's empty-k case;
+unaligned x1; the full-size workloads on sampled rows."""
+import numpy as np
+import pytest
+import torch
+
+from int4_quantization_amd import synth
+from parity import DEV, announce, check_weight_quant_matmul
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+SHAPES = [(1, 128, 64), (5, 160, 100), (16, 256, 48), (37, 384, 300), (200, 192, 130)]
+PARAMS = [("tensor", 0), ("channel", 0), ("group", 32), ("group", 64), ("group", 128)]
+
+
+@pytest.mark.parametrize("m,k,n", SHAPES, ids=[f"{m}x{k}x{n}" for m, k, n in SHAPES])
+@pytest.mark.parametrize("kind,gs", PARAMS, ids=[f"{p}{g}" for p, g in PARAMS])
+@pytest.mark.parametrize("weight", ["int8", "int4"])
+def test_wq_mfma(orc, m, k, n, kind, gs, weight):
+    if weight == "int4" and k % 64:
+        k += 32  # int4 rows are whole 64-code runs on the matrix-core path
+    announce("wq mfma", m, k, n, kind, gs, weight)
+    q = synth.wq_inputs(m, k, n, 1000 + m + k + n + gs, weight=weight, group_size=gs,
+                        per_tensor=kind == "tensor", offset=(m + gs) % 2 == 0, bias=True, x3=m % 2 == 1)
+    check_weight_quant_matmul(orc, q)
+
+
+@pytest.mark.parametrize("dtype", ["bfloat16", "float16"])
+@pytest.mark.parametrize("weight", ["int8", "int4"])
+@pytest.mark.parametrize("kind,gs", [("tensor", 0), ("channel", 0), ("group", 64)])
+@pytest.mark.parametrize("offset", [True, False])
+def test_wq_identity_exposes_weight(orc, dtype, weight, kind, gs, offset):
+    """x1 = identity [k, k]: each output is one exact product W[k, n] * 1 plus
+    zeros, so out must equal the oracle's dequantized W bit for bit (the
+    dequantization itself is exact, whatever the summation order)."""
+    announce("wq identity", dtype, weight, kind, gs, offset)
+    k, n = 128, 96
+    q = synth.wq_inputs(k, k, n, 4000 + gs, dtype=dtype, weight=weight, group_size=gs,
+                        per_tensor=kind == "tensor", offset=offset, bias=False)
+    q["x1"] = torch.eye(k, dtype=q["x1"].dtype)
+    d = {key: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for key, v in q.items()}
+    import int4_quantization_amd as dq
+    out = dq.weight_quant_matmul(d["x1"], d["x2"], d["scale"], d["offset"], gs, None, None, True, weight)
+    from parity import wq_oracle_args
+    x2, policy = wq_oracle_args(q)
+    W = orc.weight_dequant(x2, q["scale"], q["offset"], policy, gs, True)
+    got = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, W), f"{int((got != W).sum())} of {W.size} weights differ"
+
+
+@pytest.mark.parametrize("dtype", ["float16", "bfloat16"])
+@pytest.mark.parametrize("offset,bias,x3", [(True, False, False), (False, True, True), (True, True, True)])
+def test_wq_dtypes_and_epilogue(orc, dtype, offset, bias, x3):
+    announce("wq dtype/epilogue", dtype, offset, bias, x3)
+    q = synth.wq_inputs(48, 512, 96, 2000, dtype=dtype, weight="int8", group_size=128, offset=offset,
+                        bias=bias, x3=x3)
+    check_weight_quant_matmul(orc, q)
+
+
+@pytest.mark.parametrize("weight", ["int8", "int4"])
+@pytest.mark.parametrize("kind,gs", [("channel", 0), ("group", 32), ("group", 96)])
+def test_wq_generic_layout(orc, weight, kind, gs):
+    """Weights stored [k, n]: the generic kernel.  gs = 96 leaves a short last
+    group (k = 160)."""
+    announce("wq generic", weight, kind, gs)
+    q = synth.wq_inputs(7, 160, 72, 3000 + gs, weight=weight, group_size=gs, offset=True, bias=True, x3=True,
+                        transpose_x2=False)
+    check_weight_quant_matmul(orc, q)
+
+
+def test_wq_ragged_k_generic(orc):
+    """k not a multiple of 32 with weights [n, k]: the generic kernel."""
+    announce("wq ragged k")
+    q = synth.wq_inputs(9, 100, 40, 3100, weight="int8", group_size=32, offset=True)
+    check_weight_quant_matmul(orc, q)
+
+
+def test_wq_three_d_x1(orc):
+    announce("wq 3-D")
+    q = synth.wq_inputs(2 * 24, 256, 80, 3200, weight="int4", group_size=64, x3=True)
+    q["x1"] = q["x1"].reshape(2, 24, 256)
+    q["x3"] = q["x3"].reshape(2, 24, 80)
+    check_weight_quant_matmul(orc, q)
+
+
+def test_wq_unaligned_x1(orc):
+    announce("wq unaligned x1")
+    q = synth.wq_inputs(6, 128, 64, 3300, weight="int8", group_size=0)
+    d = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in q.items()}
+    buf = torch.empty(q["x1"].numel() + 8, dtype=q["x1"].dtype, device=DEV)
+    x1 = buf[1:1 + q["x1"].numel()].view(q["x1"].shape)
+    x1.copy_(d["x1"])
+    assert x1.data_ptr() % 16 != 0
+    d["x1"] = x1
+    check_weight_quant_matmul(orc, q, dev=d)
+
+
+@pytest.mark.parametrize("m,k,n", [(1, 4096, 256), (16, 8192, 192), (24, 2048, 64)])
+def test_wq_split_k(orc, m, k, n):
+    """Few output tiles: k is split across workgroups (binary32 partial sums
+    in the workspace, added in split order by a second kernel)."""
+    announce("wq split k", m, k, n)
+    q = synth.wq_inputs(m, k, n, 5000 + m, weight="int4", group_size=128, bias=True, x3=True)
+    check_weight_quant_matmul(orc, q)
+
+
+def test_wq_split_k_deterministic():
+    """Two calls give identical bits (the split sums are added in order)."""
+    announce("wq split k determinism")
+    q = synth.wq_inputs(16, 8192, 512, 5100, weight="int8", group_size=0, bias=True)
+    d = {key: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for key, v in q.items()}
+    import int4_quantization_amd as dq
+    args = (d["x1"], d["x2"], d["scale"], d["offset"], 0, d["bias"], None, True, "int8")
+    a, b = dq.weight_quant_matmul(*args), dq.weight_quant_matmul(*args)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_wq_empty_k(orc):
+    """The page's empty case: k = 0 gives bias + x3."""
+    announce("wq k=0")
+    q = synth.wq_inputs(5, 0, 32, 3400, weight="int8", group_size=0, bias=True, x3=True)
+    check_weight_quant_matmul(orc, q)
+
+
+@pytest.mark.parametrize("name", ["wq_int4_g128_bf16_16x8192x28672", "wq_int8_channel_bf16_4096x8192x8192"])
+def test_wq_full_size_sampled(orc, name):
+    """The benchmark workloads: every column of a sample of rows (4 of the 16
+    decode rows; 24 rows spread over the prefill shape, including the first
+    and last), the oracle computing only those rows."""
+    announce("wq full size", name)
+    q = synth.WORKLOADS[name][1]()
+    m = q["x1"].shape[0]
+    count = 4 if m <= 16 else 24
+    rows = np.unique(np.linspace(0, m - 1, count).astype(int))
+    frac = check_weight_quant_matmul(orc, q, rows=rows)
+    print(f"{name}: {frac:.4f} of sampled outputs equal the once-rounded exact result", flush=True)
