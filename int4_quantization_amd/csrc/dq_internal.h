@@ -107,10 +107,10 @@ enum WqVariant : int {
     WQ_VAR_MFMA = 0,     // weights stored [n, k], matrix cores, no LDS
     WQ_VAR_GENERIC = 1,  // any layout: one thread per output element
 };
-enum WqTile : int {  // 16x16 output blocks per wave
-    WQ_TILE_2x2 = 1,
-    WQ_TILE_4x4 = 2,
+enum WqTile : int {
+    WQ_TILE_2x2 = 1,     // 17..128 rows: 2 x 2 blocks of 16 x 16 per wave, operands from global
     WQ_TILE_DECODE = 3,  // at most 16 rows: kWqDecodeCols blocks per wave, x1 staged in LDS
+    WQ_TILE_GEMM = 4,    // more rows: 128 x 128 workgroup tiles, x1 and dequantized weights in LDS
 };
 
 struct WqPlan {
@@ -139,15 +139,15 @@ constexpr int kWqSuperK = 128;
 constexpr int kWqDecodeCols = 1;  // 16-column blocks per wave in the decode kernel
 constexpr int wq_batch(int tile)
 {
-    return tile == WQ_TILE_DECODE ? 2 : tile == WQ_TILE_2x2 ? 2 : 1;
+    return tile == WQ_TILE_DECODE ? 2 : tile == WQ_TILE_2x2 ? 2 : 1;  // GEMM: one k-step of 128
 }
 constexpr int wq_tile_rows(int tile)
 {
-    return tile == WQ_TILE_DECODE ? 16 : tile == WQ_TILE_2x2 ? 32 : 64;
+    return tile == WQ_TILE_DECODE ? 16 : tile == WQ_TILE_2x2 ? 32 : tile == WQ_TILE_GEMM ? 128 : 64;
 }
 constexpr int wq_tile_cols(int tile)  // four waves side by side
 {
-    return tile == WQ_TILE_DECODE ? 4 * 16 * kWqDecodeCols : 4 * wq_tile_rows(tile);
+    return tile == WQ_TILE_DECODE ? 4 * 16 * kWqDecodeCols : tile == WQ_TILE_GEMM ? 128 : 4 * wq_tile_rows(tile);
 }
 
 // Kernel launchers (defined in the .hip files).  They enqueue on `stream`

@@ -816,7 +816,7 @@ dq_status dq_weight_quant_matmul_get_workspace_size(const dq_tensor* x1, const d
     const bool kfit = x2->dtype == DQ_I8 ? k % 32 == 0 : k % 64 == 0;
     p.variant = p.transpose_x2 && kfit && aligned(x1->data, 16) && aligned(x2->data, 16) ? dq::WQ_VAR_MFMA
                                                                                        : dq::WQ_VAR_GENERIC;
-    p.tile = m <= 16 ? dq::WQ_TILE_DECODE : m <= 128 ? dq::WQ_TILE_2x2 : dq::WQ_TILE_4x4;
+    p.tile = m <= 16 ? dq::WQ_TILE_DECODE : m <= 128 ? dq::WQ_TILE_2x2 : dq::WQ_TILE_GEMM;
     // Few output tiles: split k so that about 2048 workgroups stream the
     // weights; the binary32 partial sums [splits, m, n] live in the workspace.
     p.splits = 1;

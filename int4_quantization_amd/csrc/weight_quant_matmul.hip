@@ -13,7 +13,8 @@
 // of two bf16 or two fp16 values are exact in binary32, so W is bit-exact
 // and only the order of the binary32 additions differs from an exact sum.
 //
-// wq_mfma_kernel (weights stored [n, k], i.e. x2 transposed, k contiguous):
+// wq_mfma_kernel (17 to 128 rows; weights stored [n, k], i.e. x2 transposed,
+// k contiguous):
 //   - A wave computes a (16 RM) x (16 RN) block of out with
 //     v_mfma_f32_16x16x32_{bf16,f16}.  Lane l supplies row (or column) l % 16
 //     and eight k values per instruction, and receives rows 4 (l / 16) ..
@@ -33,6 +34,8 @@
 //   - Rows past m repeat the last row (their results are not stored);
 //     columns past n repeat the last column (likewise).  k runs in whole
 //     groups of 32 (int8) or 64 (int4) elements.
+// wq_decode_kernel (at most 16 rows) and wq_gemm_kernel (more than 128 rows)
+// are described where they are defined.
 // wq_generic_kernel: any layout and alignment, one thread per output
 // element, binary32 accumulation in k order.  It is the path for weights
 // stored [k, n].
@@ -591,6 +594,210 @@ __global__ __launch_bounds__(kBlock) void wq_decode_kernel(const WqArgs a)
     }
 }
 
+// ---------------------------------------------------------------------------
+// Prefill-shaped kernel: a 128 x 128 output tile per workgroup, four waves
+// in a 2 x 2 grid, each 64 x 64 (4 x 4 blocks of 16 x 16).  Per k-step of
+// 128 the x1 tile and the dequantized weight tile are staged in LDS, so every
+// weight is dequantized once per 128 rows and every x1 element read once
+// per 128 columns; the next step's global loads are in flight during the
+// current step's matrix-core work.  LDS rows are padded by 16 bytes, which
+// keeps the 16-lane operand reads free of bank conflicts.  (Measured: 256-row
+// tiles lose more to occupancy than they save in dequantization; k-steps of
+// 128 beat 64.)
+// ---------------------------------------------------------------------------
+constexpr int kGemmBM = 128, kGemmBN = 128, kGemmBK = 128;
+constexpr int kGemmThreads = kGemmBM / 64 * 2 * kWave;  // waves in a (BM / 64) x 2 grid
+
+template <int XT, int WT, int POL, bool OFF>
+__global__ __launch_bounds__(kGemmThreads) void wq_gemm_kernel(const WqArgs a)
+{
+    constexpr int BM = kGemmBM, BN = kGemmBN, BK = kGemmBK, LR = kGemmBK + 8, NT = kGemmThreads;
+    constexpr int AV = BM * (BK / 8) / NT;                         // 16-byte x1 vectors per thread
+    constexpr int KPV = WT == WQ_I8 ? 16 : 32;                      // k per 16-byte weight vector
+    constexpr int BQ = BN * (BK / KPV);                             // weight vectors per tile
+    constexpr int BV = BQ >= NT ? BQ / NT : 1;                      // ... per thread (waves past BQ idle)
+    static_assert(AV * NT == BM * BK / 8 && (BQ >= NT ? BV * NT == BQ : NT % BQ == 0 && BQ % kWave == 0),
+                  "tile divides over threads");
+    static_assert(BN == 128, "two 64-column wave slots");
+    constexpr int kStage = (BM + BN) * LR, kEpi = NT / kWave * 64 * 72;
+    __shared__ __align__(16) uint16_t smem[kStage > kEpi ? kStage : kEpi];
+    uint16_t* const As = smem;            // [BM][LR]: x1 rows
+    uint16_t* const Bs = smem + BM * LR;  // [BN][LR]: dequantized weight columns
+
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int li = lane % 16, g = lane / 16;
+    const int wm = wave / 2, wn = wave % 2;
+    const int64_t m0 = static_cast<int64_t>(blockIdx.y) * BM;
+    const int64_t n0 = static_cast<int64_t>(blockIdx.x) * BN;
+    const int64_t k_beg = static_cast<int64_t>(blockIdx.z) * a.k_chunk;
+    const int64_t k_end = k_beg + a.k_chunk < a.k ? k_beg + a.k_chunk : a.k;
+    const int nk = static_cast<int>((k_end - k_beg + BK - 1) / BK);
+    constexpr int64_t kBytes32 = WT == WQ_I8 ? 32 : 16;
+
+    // Global loads of step kt into registers: x1 vectors (zeros past k_end)
+    // and weight vectors (clamped in k: their x1 partner is zero).
+    auto load = [&](int kt, uint4 (&ar)[AV], uint4 (&br)[BV], float (&bs)[BV], float (&bo)[BV]) {
+        const int64_t kb = k_beg + static_cast<int64_t>(kt) * BK;
+#pragma unroll
+        for (int p = 0; p < AV; ++p) {
+            const int q = p * NT + tid, row = q / (BK / 8), kv = q % (BK / 8);
+            const int64_t r = m0 + row < a.m ? m0 + row : a.m - 1;
+            const int64_t kk = kb + kv * 8;
+            const uint4 v = *reinterpret_cast<const uint4*>(a.x1 + r * a.k + (kk < k_end ? kk : k_beg));
+            ar[p] = kk < k_end ? v : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int p = 0; p < BV; ++p) {
+            const int q = p * NT + tid, cl = (q % BQ) / (BK / KPV), kv = q % (BK / KPV);
+            const int64_t c = n0 + cl < a.n ? n0 + cl : a.n - 1;
+            int64_t kk = kb + static_cast<int64_t>(kv) * KPV;
+            kk = kk < k_end ? kk : k_beg;
+            br[p] = ld_stream16(a.x2 + c * (a.k / 32) * kBytes32 + kk * kBytes32 / 32);
+            if constexpr (POL == DQ_PER_GROUP) {
+                const int64_t pi = c * a.groups + div_by(static_cast<uint32_t>(kk), a.by_gs);
+                bs[p] = t_to_f32<XT>(a.scale[pi]);
+                bo[p] = OFF ? t_to_f32<XT>(a.offset[pi]) : 0.0f;
+            } else {
+                const int64_t pi = POL == DQ_PER_TENSOR ? 0 : c;
+                bs[p] = t_to_f32<XT>(a.scale[pi]);
+                bo[p] = OFF ? t_to_f32<XT>(a.offset[pi]) : 0.0f;
+            }
+        }
+    };
+    // Registers -> LDS: x1 as is; weights dequantized (exact binary32 steps,
+    // one rounding to T) into the [column][k] layout the operands read.
+    auto store = [&](const uint4 (&ar)[AV], const uint4 (&br)[BV], const float (&bs)[BV], const float (&bo)[BV]) {
+#pragma unroll
+        for (int p = 0; p < AV; ++p) {
+            const int q = p * NT + tid, row = q / (BK / 8), kv = q % (BK / 8);
+            *reinterpret_cast<uint4*>(&As[row * LR + kv * 8]) = ar[p];
+        }
+#pragma unroll
+        for (int p = 0; p < BV; ++p) {
+            const int q = p * NT + tid, cl = q / (BK / KPV), kv = q % (BK / KPV);
+            if (q >= BQ)  // uniform per wave
+                break;
+            const float sc = WT == WQ_I4 && !OFF ? bs[p] * 0.0625f : bs[p];
+            const float of = bo[p];
+#pragma unroll
+            for (int s2 = 0; s2 < KPV / 8; ++s2) {
+                float v[8], w[8];
+                if constexpr (WT == WQ_I8)
+                    decode8<WT>(br[p], br[p], s2, v);  // bytes 8 s2 .. 8 s2 + 7 of the vector
+                else
+                    decode8<WT>(br[p], br[p], s2, v);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    if constexpr (WT == WQ_I4 && OFF)
+                        w[j] = dequant1<WT, true>(v[j], sc, of);
+                    else
+                        w[j] = dequant1<WQ_I8, OFF>(v[j], sc, of);
+                }
+                *reinterpret_cast<uint4*>(&Bs[cl * LR + kv * KPV + 8 * s2]) = pack8_t<XT>(w);
+            }
+        }
+    };
+
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+            acc[r][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    if (nk > 0) {
+        uint4 ar[AV], br[BV];
+        float bs[BV], bo[BV];
+        load(0, ar, br, bs, bo);
+        for (int kt = 0; kt < nk; ++kt) {
+            __syncthreads();  // the previous step's operand reads are done
+            store(ar, br, bs, bo);
+            __syncthreads();
+            load(kt + 1 < nk ? kt + 1 : kt, ar, br, bs, bo);  // in flight during the matrix-core work
+#pragma unroll
+            for (int s2 = 0; s2 < BK / 32; ++s2) {
+                uint4 av[4], bv[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    av[r] = *reinterpret_cast<const uint4*>(&As[(wm * 64 + 16 * r + li) * LR + 32 * s2 + 8 * g]);
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    bv[t] = *reinterpret_cast<const uint4*>(&Bs[(wn * 64 + 16 * t + li) * LR + 32 * s2 + 8 * g]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+                        acc[r][t] = mfma16<XT>(av[r], bv[t], acc[r][t]);
+            }
+        }
+    }
+
+    if (a.partial) {  // split k: binary32 partial sums, finished by wq_reduce_kernel
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int64_t c = n0 + wn * 64 + 16 * t + li;
+            if (c >= a.n)
+                continue;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int64_t row = m0 + wm * 64 + 16 * r + 4 * g + i;
+                    if (row < a.m)
+                        a.partial[(static_cast<int64_t>(blockIdx.z) * a.m + row) * a.n + c] = acc[r][t][i];
+                }
+        }
+        return;
+    }
+
+    // Epilogue through LDS: each wave writes its 64 x 64 sums (+ bias) as T
+    // into a row-major tile of 64 rows of 72 in the staging memory, then
+    // stores whole 16-byte row pieces (+ x3).
+    __syncthreads();
+    uint16_t* tile = smem + wave * (64 * 72);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const int64_t c = n0 + wn * 64 + 16 * t + li;
+        const float b = a.bias && c < a.n ? t_to_f32<XT>(a.bias[c]) : 0.0f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int rr = 16 * r + 4 * g + i, cc = 16 * t + li;
+                float v = acc[r][t][i] + b;
+                if (a.x3) {
+                    const int64_t row = m0 + wm * 64 + rr;
+                    if (row < a.m && c < a.n)
+                        v += t_to_f32<XT>(a.x3[row * a.n + c]);
+                }
+                tile[rr * 72 + cc] = f32_to_t<XT>(v);
+            }
+    }
+    __syncthreads();
+    // 64 rows x 8 pieces of 8 elements per wave tile: 8 pieces per lane.
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+        const int q = p * kWave + lane, rr = q / 8, pc = q % 8;
+        const int64_t row = m0 + wm * 64 + rr;
+        const int64_t c0 = n0 + wn * 64 + pc * 8;
+        if (row >= a.m)
+            continue;
+        const uint4 v = *reinterpret_cast<const uint4*>(&tile[rr * 72 + pc * 8]);
+        uint16_t* dst = a.out + row * a.n + c0;
+        if (c0 + 8 <= a.n && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+            *reinterpret_cast<uint4*>(dst) = v;
+        } else {
+            const uint16_t e[8] = {static_cast<uint16_t>(v.x), static_cast<uint16_t>(v.x >> 16),
+                                   static_cast<uint16_t>(v.y), static_cast<uint16_t>(v.y >> 16),
+                                   static_cast<uint16_t>(v.z), static_cast<uint16_t>(v.z >> 16),
+                                   static_cast<uint16_t>(v.w), static_cast<uint16_t>(v.w >> 16)};
+            for (int j = 0; j < 8; ++j)
+                if (c0 + j < a.n)
+                    dst[j] = e[j];
+        }
+    }
+}
+
 template <int XT, int WT>
 __global__ __launch_bounds__(kBlock) void wq_generic_kernel(const WqArgs a, int pol, bool trans)
 {
@@ -698,13 +905,44 @@ hipError_t launch_decode(const WqArgs& a, int splits, hipStream_t stream)
 }
 
 template <int XT, int WT, int POL, bool OFF>
+hipError_t launch_gemm(const WqArgs& a, int splits, hipStream_t stream)
+{
+    const int64_t gx = (a.n + kGemmBN - 1) / kGemmBN;
+    const int64_t gy_total = (a.m + kGemmBM - 1) / kGemmBM;
+    constexpr int64_t kMaxY = 65535;
+    if (splits > 1 && gy_total > kMaxY)
+        return hipErrorInvalidConfiguration;  // split k is planned for few tiles only
+    for (int64_t y0 = 0; y0 < gy_total; y0 += kMaxY) {
+        WqArgs c = a;
+        c.x1 = a.x1 + y0 * kGemmBM * a.k;
+        c.out = a.out + y0 * kGemmBM * a.n;
+        c.x3 = a.x3 ? a.x3 + y0 * kGemmBM * a.n : nullptr;
+        c.m = a.m - y0 * kGemmBM < kMaxY * kGemmBM ? a.m - y0 * kGemmBM : kMaxY * kGemmBM;
+        const int64_t gy = (c.m + kGemmBM - 1) / kGemmBM;
+        hipLaunchKernelGGL((wq_gemm_kernel<XT, WT, POL, OFF>),
+                           dim3(static_cast<uint32_t>(gx), static_cast<uint32_t>(gy), static_cast<uint32_t>(splits)),
+                           dim3(kGemmThreads), 0, stream, c);
+        const hipError_t err = hipGetLastError();
+        if (err != hipSuccess)
+            return err;
+    }
+    if (splits > 1) {
+        const int64_t blocks = (a.m * a.n + kBlock - 1) / kBlock;
+        hipLaunchKernelGGL((wq_reduce_kernel<XT>), dim3(static_cast<uint32_t>(blocks)), dim3(kBlock), 0, stream, a,
+                           splits);
+        return hipGetLastError();
+    }
+    return hipSuccess;
+}
+
+template <int XT, int WT, int POL, bool OFF>
 hipError_t pick_tile(const WqPlan& p, const WqArgs& a, hipStream_t stream)
 {
+    if (p.tile == WQ_TILE_GEMM)
+        return launch_gemm<XT, WT, POL, OFF>(a, p.splits, stream);
     if (p.tile == WQ_TILE_DECODE)
         return launch_decode<XT, WT, POL, OFF, kWqDecodeCols, wq_batch(WQ_TILE_DECODE)>(a, p.splits, stream);
-    if (p.tile == WQ_TILE_2x2)
-        return launch_mfma<XT, WT, POL, OFF, 2, 2, wq_batch(WQ_TILE_2x2)>(a, p.splits, stream);
-    return launch_mfma<XT, WT, POL, OFF, 4, 4, wq_batch(WQ_TILE_4x4)>(a, p.splits, stream);
+    return launch_mfma<XT, WT, POL, OFF, 2, 2, wq_batch(WQ_TILE_2x2)>(a, p.splits, stream);
 }
 
 template <int XT, int WT, int POL>
