@@ -1,0 +1,82 @@
+// dq_ext_internal.h -- plans shared between the host validation layer
+// (dquant_api.cpp) and the kernel launchers of mx block quantization and the
+// weight-quantized matmul.  Not installed.  (Kept apart from dq_internal.h,
+// which the row-quantization kernels include.)
+#pragma once
+
+#include "dq_internal.h"
+
+namespace dq {
+
+// ---- mx block quantization ---------------------------------------------------
+enum MxElem : int { MX_E4M3 = 0, MX_E5M2 = 1, MX_E2M1 = 2 };
+enum MxVariant : int {
+    MX_VAR_ROW = 0,      // axis 1, 16-byte loads, four lanes per 32-element block
+    MX_VAR_COL = 1,      // axis 0, one lane per 8 columns of a 32-row block
+    MX_VAR_GENERIC = 2,  // any shape and alignment, one thread per block
+};
+
+struct MxPlan {
+    const void* x;
+    int x_type;  // XType
+    int64_t rows, n;
+    int elem;    // MxElem
+    int axis;    // 1: blocks along n; 0: blocks along rows
+    void* y;
+    uint8_t* scale;
+    int variant;
+};
+
+// ---- weight-quantized matmul -------------------------------------------------
+enum WqWeight : int { WQ_I8 = 0, WQ_I4 = 1 };
+enum WqVariant : int {
+    WQ_VAR_MFMA = 0,     // weights stored [n, k], matrix cores, no LDS
+    WQ_VAR_GENERIC = 1,  // any layout: one thread per output element
+};
+enum WqTile : int {
+    WQ_TILE_2x2 = 1,     // 17..128 rows: 2 x 2 blocks of 16 x 16 per wave, operands from global
+    WQ_TILE_DECODE = 3,  // at most 16 rows: kWqDecodeCols blocks per wave, x1 staged in LDS
+    WQ_TILE_GEMM = 4,    // more rows: 128 x 128 workgroup tiles, x1 and dequantized weights in LDS
+};
+
+struct WqPlan {
+    const void* x1;
+    const void* x2;
+    const void* scale;
+    const void* offset;  // nullptr: none
+    const void* bias;    // nullptr: none
+    const void* x3;      // nullptr: none
+    void* out;
+    int64_t m, k, n;
+    int64_t group_size;  // > 0: per group
+    int x_type;          // XType of x1, the parameters, bias, x3 and out
+    int w_type;          // WqWeight
+    int policy;          // dq_antiquant_policy: PER_TENSOR, PER_CHANNEL or PER_GROUP
+    bool transpose_x2;   // weights stored [n, k]
+    int variant;
+    int tile;
+    int splits;       // > 1: k split across workgroups, partial sums in the workspace
+    int64_t k_chunk;  // k per split
+};
+
+// Matrix-core kernel geometry: k per superstep (four lane groups of 32) and
+// supersteps whose loads are issued together, per register tile.
+constexpr int kWqSuperK = 128;
+constexpr int kWqDecodeCols = 1;  // 16-column blocks per wave in the decode kernel
+constexpr int wq_batch(int tile)
+{
+    return tile == WQ_TILE_DECODE ? 2 : tile == WQ_TILE_2x2 ? 2 : 1;  // GEMM: one k-step of 128
+}
+constexpr int wq_tile_rows(int tile)
+{
+    return tile == WQ_TILE_DECODE ? 16 : tile == WQ_TILE_2x2 ? 32 : tile == WQ_TILE_GEMM ? 128 : 64;
+}
+constexpr int wq_tile_cols(int tile)  // four waves side by side
+{
+    return tile == WQ_TILE_DECODE ? 4 * 16 * kWqDecodeCols : tile == WQ_TILE_GEMM ? 128 : 4 * wq_tile_rows(tile);
+}
+
+hipError_t launch_mx_quantize(const MxPlan& p, hipStream_t stream);
+hipError_t launch_weight_quant_matmul(const WqPlan& p, void* workspace, hipStream_t stream);
+
+}  // namespace dq

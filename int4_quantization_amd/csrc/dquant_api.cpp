@@ -13,7 +13,7 @@
 #include <new>
 #include <string>
 
-#include "dq_internal.h"
+#include "dq_ext_internal.h"
 
 enum ExecOp : int {
     OP_DYNAMIC_QUANT = 1,

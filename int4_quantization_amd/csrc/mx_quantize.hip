@@ -46,7 +46,7 @@
 //                      or per block and column pair (axis 0), 2-byte loads.
 
 #include "dq_device.h"
-#include "dq_internal.h"
+#include "dq_ext_internal.h"
 
 namespace dq {
 namespace {

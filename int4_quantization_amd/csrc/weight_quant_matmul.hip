@@ -41,7 +41,7 @@
 // stored [k, n].
 
 #include "dq_device.h"
-#include "dq_internal.h"
+#include "dq_ext_internal.h"
 
 namespace dq {
 namespace {

@@ -1,7 +1,10 @@
 """Every benchmark workload at its full size, element by element, through the
 same C-ABI calls and launch configuration the benchmark times, against the
 CPU oracle: DynamicQuant, AntiQuantize and mx block quantization bit-exact,
-AdaLayerNorm-quant at the stated tolerance.  Also: two launches give identical bits."""
+AdaLayerNorm-quant at the stated tolerance.  Also: two launches give identical bits.
+The weight-quantized matmul workloads are checked on sampled rows in
+test_gpu_weight_quant_matmul.py (the oracle's binary64 matmul is too slow for
+every row)."""
 import numpy as np
 import pytest
 import torch
@@ -15,7 +18,7 @@ pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
 
 
-@pytest.mark.parametrize("name", list(synth.WORKLOADS))
+@pytest.mark.parametrize("name", [w for w, (op, _) in synth.WORKLOADS.items() if op != "weight_quant_matmul"])
 def test_full_size_parity(orc, name):
     announce("full size", name)
     op, build = synth.WORKLOADS[name]
