@@ -508,8 +508,10 @@ __global__ __launch_bounds__(kBlock) void wq_decode_kernel(const WqArgs a)
                     // v = 16 code: RN(v + 16 o) = 16 RN(code + o) and s / 16 is
                     // exact, so RN(RN(v + 16 o) * (s / 16)) is the formula,
                     // unless 16 o overflows (|o| near the binary32 limit).
+                    // The test is made wave-uniform: a per-lane condition
+                    // would be if-converted, computing every weight both ways.
                     const float o16 = of * 16.0f, s16 = sc * 0.0625f;
-                    const bool huge = __builtin_isinf(o16);
+                    const bool huge = __any(__builtin_isinf(o16));
 #pragma unroll
                     for (int s2 = 0; s2 < 4; ++s2) {
                         float v[8], wv[8];
@@ -600,18 +602,60 @@ __global__ __launch_bounds__(kBlock) void wq_decode_kernel(const WqArgs a)
 // 128 the x1 tile and the dequantized weight tile are staged in LDS, so every
 // weight is dequantized once per 128 rows and every x1 element read once
 // per 128 columns; the next step's global loads are in flight during the
-// current step's matrix-core work.  LDS rows are padded by 16 bytes, which
-// keeps the 16-lane operand reads free of bank conflicts.  (Measured: 256-row
-// tiles lose more to occupancy than they save in dequantization; k-steps of
-// 128 beat 64.)
-// ---------------------------------------------------------------------------
+// current step's matrix-core work.  (Measured: 256-row tiles lose more to
+// occupancy than they save in dequantization; k-steps of 128 beat 64; eight
+// waves split into four that dequantize the next step and four that run the
+// matrix cores were no faster, as the second LDS buffer halves occupancy.)
+//
+// LDS layout of the prefill tiles.  Rows (x1 rows, weight columns) are
+// padded by 32 bytes: on gfx950 the 16-byte operand reads of 16 rows by
+// 4 lane groups are free of bank conflicts at that stride and not at a
+// 16-byte pad.  16-byte stores are serviced 8 lanes at a time over 32
+// banks, so in every 8-lane store each of the 4 weight columns it touches
+// must receive two chunks whose slots differ in bit 0: the lanes of a
+// column are assigned in pairs (wq_bmap), and the 8-element k-chunks of a
+// row are stored in a permuted order (wq_phys_chunk).  x1 rows take the same
+// permutation, so the matrix cores still pair equal k; a dot product's
+// k order is free.
+constexpr int kLdsPad = 16;  // elements
+
+// Physical slot of logical k-chunk c in a BK-wide row.
+template <int WT, int BK>
+__device__ __forceinline__ constexpr int wq_phys_chunk(int c)
+{
+    constexpr int CPL = WT == WQ_I8 ? 2 : 4;  // chunks per 16-byte weight vector
+    constexpr int LPC = BK / 8 / CPL;         // weight vectors per column row
+    return (c % CPL) * LPC + c / CPL;
+}
+
+// Logical k-chunk held by physical slot p (the inverse of wq_phys_chunk);
+// x1 lanes walk the slots in order, so 8 lanes fill 8 consecutive slots.
+template <int WT, int BK>
+__device__ __forceinline__ constexpr int wq_logical_chunk(int p)
+{
+    constexpr int CPL = WT == WQ_I8 ? 2 : 4;
+    constexpr int LPC = BK / 8 / CPL;
+    return (p % LPC) * CPL + p / LPC;
+}
+
+// Weight vector q of a tile -> column cl and vector kv within the column.
+template <int WT, int BK>
+__device__ __forceinline__ void wq_bmap(int q, int& cl, int& kv)
+{
+    constexpr int LPC = BK / (WT == WQ_I8 ? 16 : 32);
+    static_assert(LPC >= 2 && LPC % 2 == 0, "two vectors per column and pass");
+    const int a = q / 8, b = q % 8;
+    cl = 4 * (a / (LPC / 2)) + b / 2;
+    kv = 2 * (a % (LPC / 2)) + b % 2;
+}
+
 constexpr int kGemmBM = 128, kGemmBN = 128, kGemmBK = 128;
 constexpr int kGemmThreads = kGemmBM / 64 * 2 * kWave;  // waves in a (BM / 64) x 2 grid
 
 template <int XT, int WT, int POL, bool OFF>
 __global__ __launch_bounds__(kGemmThreads) void wq_gemm_kernel(const WqArgs a)
 {
-    constexpr int BM = kGemmBM, BN = kGemmBN, BK = kGemmBK, LR = kGemmBK + 8, NT = kGemmThreads;
+    constexpr int BM = kGemmBM, BN = kGemmBN, BK = kGemmBK, LR = kGemmBK + kLdsPad, NT = kGemmThreads;
     constexpr int AV = BM * (BK / 8) / NT;                         // 16-byte x1 vectors per thread
     constexpr int KPV = WT == WQ_I8 ? 16 : 32;                      // k per 16-byte weight vector
     constexpr int BQ = BN * (BK / KPV);                             // weight vectors per tile
@@ -640,7 +684,7 @@ __global__ __launch_bounds__(kGemmThreads) void wq_gemm_kernel(const WqArgs a)
         const int64_t kb = k_beg + static_cast<int64_t>(kt) * BK;
 #pragma unroll
         for (int p = 0; p < AV; ++p) {
-            const int q = p * NT + tid, row = q / (BK / 8), kv = q % (BK / 8);
+            const int q = p * NT + tid, row = q / (BK / 8), kv = wq_logical_chunk<WT, BK>(q % (BK / 8));
             const int64_t r = m0 + row < a.m ? m0 + row : a.m - 1;
             const int64_t kk = kb + kv * 8;
             const uint4 v = *reinterpret_cast<const uint4*>(a.x1 + r * a.k + (kk < k_end ? kk : k_beg));
@@ -648,7 +692,9 @@ __global__ __launch_bounds__(kGemmThreads) void wq_gemm_kernel(const WqArgs a)
         }
 #pragma unroll
         for (int p = 0; p < BV; ++p) {
-            const int q = p * NT + tid, cl = (q % BQ) / (BK / KPV), kv = q % (BK / KPV);
+            const int q = p * NT + tid;
+            int cl, kv;
+            wq_bmap<WT, BK>(q % BQ, cl, kv);
             const int64_t c = n0 + cl < a.n ? n0 + cl : a.n - 1;
             int64_t kk = kb + static_cast<int64_t>(kv) * KPV;
             kk = kk < k_end ? kk : k_beg;
@@ -669,14 +715,16 @@ __global__ __launch_bounds__(kGemmThreads) void wq_gemm_kernel(const WqArgs a)
     auto store = [&](const uint4 (&ar)[AV], const uint4 (&br)[BV], const float (&bs)[BV], const float (&bo)[BV]) {
 #pragma unroll
         for (int p = 0; p < AV; ++p) {
-            const int q = p * NT + tid, row = q / (BK / 8), kv = q % (BK / 8);
-            *reinterpret_cast<uint4*>(&As[row * LR + kv * 8]) = ar[p];
+            const int q = p * NT + tid, row = q / (BK / 8);
+            *reinterpret_cast<uint4*>(&As[row * LR + 8 * (q % (BK / 8))]) = ar[p];
         }
 #pragma unroll
         for (int p = 0; p < BV; ++p) {
-            const int q = p * NT + tid, cl = q / (BK / KPV), kv = q % (BK / KPV);
+            const int q = p * NT + tid;
             if (q >= BQ)  // uniform per wave
                 break;
+            int cl, kv;
+            wq_bmap<WT, BK>(q, cl, kv);
             const float sc = WT == WQ_I4 && !OFF ? bs[p] * 0.0625f : bs[p];
             const float of = bo[p];
 #pragma unroll
@@ -693,7 +741,7 @@ __global__ __launch_bounds__(kGemmThreads) void wq_gemm_kernel(const WqArgs a)
                     else
                         w[j] = dequant1<WQ_I8, OFF>(v[j], sc, of);
                 }
-                *reinterpret_cast<uint4*>(&Bs[cl * LR + kv * KPV + 8 * s2]) = pack8_t<XT>(w);
+                *reinterpret_cast<uint4*>(&Bs[cl * LR + 8 * wq_phys_chunk<WT, BK>(kv * (KPV / 8) + s2)]) = pack8_t<XT>(w);
             }
         }
     };

@@ -18,7 +18,7 @@ from parity import DEV, announce, check_weight_quant_matmul
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
 
-SHAPES = [(1, 128, 64), (5, 160, 100), (16, 256, 48), (37, 384, 300), (200, 192, 130)]
+SHAPES = [(1, 128, 64), (5, 160, 100), (16, 256, 48), (37, 384, 300), (200, 192, 130), (300, 640, 200)]
 PARAMS = [("tensor", 0), ("channel", 0), ("group", 32), ("group", 64), ("group", 128)]
 
 
@@ -38,12 +38,15 @@ def test_wq_mfma(orc, m, k, n, kind, gs, weight):
 @pytest.mark.parametrize("weight", ["int8", "int4"])
 @pytest.mark.parametrize("kind,gs", [("tensor", 0), ("channel", 0), ("group", 64)])
 @pytest.mark.parametrize("offset", [True, False])
-def test_wq_identity_exposes_weight(orc, dtype, weight, kind, gs, offset):
+@pytest.mark.parametrize("k", [128, 384])
+def test_wq_identity_exposes_weight(orc, dtype, weight, kind, gs, offset, k):
     """x1 = identity [k, k]: each output is one exact product W[k, n] * 1 plus
     zeros, so out must equal the oracle's dequantized W bit for bit (the
-    dequantization itself is exact, whatever the summation order)."""
-    announce("wq identity", dtype, weight, kind, gs, offset)
-    k, n = 128, 96
+    dequantization itself is exact, whatever the summation order).  k = 384
+    gives more than 128 rows, the LDS-tiled kernel, where a k slot of x1
+    paired with the wrong slot of W would move a weight."""
+    announce("wq identity", dtype, weight, kind, gs, offset, k)
+    n = 96
     q = synth.wq_inputs(k, k, n, 4000 + gs, dtype=dtype, weight=weight, group_size=gs,
                         per_tensor=kind == "tensor", offset=offset, bias=False)
     q["x1"] = torch.eye(k, dtype=q["x1"].dtype)
