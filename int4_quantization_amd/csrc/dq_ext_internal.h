@@ -63,17 +63,19 @@ struct WqPlan {
 // supersteps whose loads are issued together, per register tile.
 constexpr int kWqSuperK = 128;
 constexpr int kWqDecodeCols = 1;  // 16-column blocks per wave in the decode kernel
+// LDS-tiled kernel: output tile and k-step (a divisor of kWqSuperK).
+constexpr int kWqGemmRows = 128, kWqGemmCols = 128, kWqGemmK = 128;
 constexpr int wq_batch(int tile)
 {
-    return tile == WQ_TILE_DECODE ? 2 : tile == WQ_TILE_2x2 ? 2 : 1;  // GEMM: one k-step of 128
+    return tile == WQ_TILE_DECODE ? 2 : tile == WQ_TILE_2x2 ? 2 : 1;  // GEMM: k splits in steps of 128
 }
 constexpr int wq_tile_rows(int tile)
 {
-    return tile == WQ_TILE_DECODE ? 16 : tile == WQ_TILE_2x2 ? 32 : tile == WQ_TILE_GEMM ? 128 : 64;
+    return tile == WQ_TILE_DECODE ? 16 : tile == WQ_TILE_2x2 ? 32 : tile == WQ_TILE_GEMM ? kWqGemmRows : 64;
 }
 constexpr int wq_tile_cols(int tile)  // four waves side by side
 {
-    return tile == WQ_TILE_DECODE ? 4 * 16 * kWqDecodeCols : tile == WQ_TILE_GEMM ? 128 : 4 * wq_tile_rows(tile);
+    return tile == WQ_TILE_DECODE ? 4 * 16 * kWqDecodeCols : tile == WQ_TILE_GEMM ? kWqGemmCols : 4 * wq_tile_rows(tile);
 }
 
 hipError_t launch_mx_quantize(const MxPlan& p, hipStream_t stream);

@@ -649,7 +649,8 @@ __device__ __forceinline__ void wq_bmap(int q, int& cl, int& kv)
     kv = 2 * (a % (LPC / 2)) + b % 2;
 }
 
-constexpr int kGemmBM = 128, kGemmBN = 128, kGemmBK = 128;
+constexpr int kGemmBM = kWqGemmRows, kGemmBN = kWqGemmCols, kGemmBK = kWqGemmK;
+static_assert(kWqSuperK % kGemmBK == 0, "k splits fall on k-step boundaries");
 constexpr int kGemmThreads = kGemmBM / 64 * 2 * kWave;  // waves in a (BM / 64) x 2 grid
 
 template <int XT, int WT, int POL, bool OFF>
@@ -662,8 +663,9 @@ __global__ __launch_bounds__(kGemmThreads) void wq_gemm_kernel(const WqArgs a)
     constexpr int BV = BQ >= NT ? BQ / NT : 1;                      // ... per thread (waves past BQ idle)
     static_assert(AV * NT == BM * BK / 8 && (BQ >= NT ? BV * NT == BQ : NT % BQ == 0 && BQ % kWave == 0),
                   "tile divides over threads");
-    static_assert(BN == 128, "two 64-column wave slots");
-    constexpr int kStage = (BM + BN) * LR, kEpi = NT / kWave * 64 * 72;
+    constexpr int WN = BN / 2, TN = WN / 16, ER = WN + 8;         // wave columns, their 16-blocks, epilogue row
+    static_assert(BN % 32 == 0 && BM == 128, "2 x 2 waves of 64 rows x BN / 2 columns");
+    constexpr int kStage = (BM + BN) * LR, kEpi = NT / kWave * 64 * ER;
     __shared__ __align__(16) uint16_t smem[kStage > kEpi ? kStage : kEpi];
     uint16_t* const As = smem;            // [BM][LR]: x1 rows
     uint16_t* const Bs = smem + BM * LR;  // [BN][LR]: dequantized weight columns
@@ -698,7 +700,11 @@ __global__ __launch_bounds__(kGemmThreads) void wq_gemm_kernel(const WqArgs a)
             const int64_t c = n0 + cl < a.n ? n0 + cl : a.n - 1;
             int64_t kk = kb + static_cast<int64_t>(kv) * KPV;
             kk = kk < k_end ? kk : k_beg;
-            br[p] = ld_stream16(a.x2 + c * (a.k / 32) * kBytes32 + kk * kBytes32 / 32);
+            // Cached, unlike the decode and 2 x 2 kernels that read each weight
+            // once: every 128-row tile re-reads these (the non-temporal hint
+            // cost 14% on 4096 x 8192 x 8192).
+            const u32x4 v = *reinterpret_cast<const u32x4*>(a.x2 + c * (a.k / 32) * kBytes32 + kk * kBytes32 / 32);
+            br[p] = make_uint4(v.x, v.y, v.z, v.w);
             if constexpr (POL == DQ_PER_GROUP) {
                 const int64_t pi = c * a.groups + div_by(static_cast<uint32_t>(kk), a.by_gs);
                 bs[p] = t_to_f32<XT>(a.scale[pi]);
@@ -746,11 +752,11 @@ __global__ __launch_bounds__(kGemmThreads) void wq_gemm_kernel(const WqArgs a)
         }
     };
 
-    f32x4 acc[4][4];
+    f32x4 acc[4][TN];
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+        for (int t = 0; t < TN; ++t)
             acc[r][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
     if (nk > 0) {
@@ -764,17 +770,17 @@ __global__ __launch_bounds__(kGemmThreads) void wq_gemm_kernel(const WqArgs a)
             load(kt + 1 < nk ? kt + 1 : kt, ar, br, bs, bo);  // in flight during the matrix-core work
 #pragma unroll
             for (int s2 = 0; s2 < BK / 32; ++s2) {
-                uint4 av[4], bv[4];
+                uint4 av[4], bv[TN];
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     av[r] = *reinterpret_cast<const uint4*>(&As[(wm * 64 + 16 * r + li) * LR + 32 * s2 + 8 * g]);
 #pragma unroll
-                for (int t = 0; t < 4; ++t)
-                    bv[t] = *reinterpret_cast<const uint4*>(&Bs[(wn * 64 + 16 * t + li) * LR + 32 * s2 + 8 * g]);
+                for (int t = 0; t < TN; ++t)
+                    bv[t] = *reinterpret_cast<const uint4*>(&Bs[(wn * WN + 16 * t + li) * LR + 32 * s2 + 8 * g]);
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
 #pragma unroll
-                    for (int t = 0; t < 4; ++t)
+                    for (int t = 0; t < TN; ++t)
                         acc[r][t] = mfma16<XT>(av[r], bv[t], acc[r][t]);
             }
         }
@@ -782,8 +788,8 @@ __global__ __launch_bounds__(kGemmThreads) void wq_gemm_kernel(const WqArgs a)
 
     if (a.partial) {  // split k: binary32 partial sums, finished by wq_reduce_kernel
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int64_t c = n0 + wn * 64 + 16 * t + li;
+        for (int t = 0; t < TN; ++t) {
+            const int64_t c = n0 + wn * WN + 16 * t + li;
             if (c >= a.n)
                 continue;
 #pragma unroll
@@ -798,14 +804,14 @@ __global__ __launch_bounds__(kGemmThreads) void wq_gemm_kernel(const WqArgs a)
         return;
     }
 
-    // Epilogue through LDS: each wave writes its 64 x 64 sums (+ bias) as T
-    // into a row-major tile of 64 rows of 72 in the staging memory, then
+    // Epilogue through LDS: each wave writes its 64 x WN sums (+ bias) as T
+    // into a row-major tile of 64 rows of WN + 8 in the staging memory, then
     // stores whole 16-byte row pieces (+ x3).
     __syncthreads();
-    uint16_t* tile = smem + wave * (64 * 72);
+    uint16_t* tile = smem + wave * (64 * ER);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        const int64_t c = n0 + wn * 64 + 16 * t + li;
+    for (int t = 0; t < TN; ++t) {
+        const int64_t c = n0 + wn * WN + 16 * t + li;
         const float b = a.bias && c < a.n ? t_to_f32<XT>(a.bias[c]) : 0.0f;
 #pragma unroll
         for (int r = 0; r < 4; ++r)
@@ -818,19 +824,19 @@ __global__ __launch_bounds__(kGemmThreads) void wq_gemm_kernel(const WqArgs a)
                     if (row < a.m && c < a.n)
                         v += t_to_f32<XT>(a.x3[row * a.n + c]);
                 }
-                tile[rr * 72 + cc] = f32_to_t<XT>(v);
+                tile[rr * ER + cc] = f32_to_t<XT>(v);
             }
     }
     __syncthreads();
-    // 64 rows x 8 pieces of 8 elements per wave tile: 8 pieces per lane.
+    // 64 rows x WN / 8 pieces of 8 elements per wave tile: WN / 8 pieces per lane.
 #pragma unroll
-    for (int p = 0; p < 8; ++p) {
-        const int q = p * kWave + lane, rr = q / 8, pc = q % 8;
+    for (int p = 0; p < WN / 8; ++p) {
+        const int q = p * kWave + lane, rr = q / (WN / 8), pc = q % (WN / 8);
         const int64_t row = m0 + wm * 64 + rr;
-        const int64_t c0 = n0 + wn * 64 + pc * 8;
+        const int64_t c0 = n0 + wn * WN + pc * 8;
         if (row >= a.m)
             continue;
-        const uint4 v = *reinterpret_cast<const uint4*>(&tile[rr * 72 + pc * 8]);
+        const uint4 v = *reinterpret_cast<const uint4*>(&tile[rr * ER + pc * 8]);
         uint16_t* dst = a.out + row * a.n + c0;
         if (c0 + 8 <= a.n && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
             *reinterpret_cast<uint4*>(dst) = v;
