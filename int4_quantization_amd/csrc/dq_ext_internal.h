@@ -34,7 +34,6 @@ enum WqVariant : int {
     WQ_VAR_GENERIC = 1,  // any layout: one thread per output element
 };
 enum WqTile : int {
-    WQ_TILE_2x2 = 1,     // 17..128 rows: 2 x 2 blocks of 16 x 16 per wave, operands from global
     WQ_TILE_DECODE = 3,  // at most 16 rows: kWqDecodeCols blocks per wave, x1 staged in LDS
     WQ_TILE_GEMM = 4,    // more rows: 128 x 128 workgroup tiles, x1 and dequantized weights in LDS
 };
@@ -67,15 +66,15 @@ constexpr int kWqDecodeCols = 1;  // 16-column blocks per wave in the decode ker
 constexpr int kWqGemmRows = 128, kWqGemmCols = 128, kWqGemmK = 128;
 constexpr int wq_batch(int tile)
 {
-    return tile == WQ_TILE_DECODE ? 2 : tile == WQ_TILE_2x2 ? 2 : 1;  // GEMM: k splits in steps of 128
+    return tile == WQ_TILE_DECODE ? 2 : 1;  // GEMM: k splits in steps of 128
 }
 constexpr int wq_tile_rows(int tile)
 {
-    return tile == WQ_TILE_DECODE ? 16 : tile == WQ_TILE_2x2 ? 32 : tile == WQ_TILE_GEMM ? kWqGemmRows : 64;
+    return tile == WQ_TILE_DECODE ? 16 : kWqGemmRows;
 }
-constexpr int wq_tile_cols(int tile)  // four waves side by side
+constexpr int wq_tile_cols(int tile)
 {
-    return tile == WQ_TILE_DECODE ? 4 * 16 * kWqDecodeCols : tile == WQ_TILE_GEMM ? kWqGemmCols : 4 * wq_tile_rows(tile);
+    return tile == WQ_TILE_DECODE ? 4 * 16 * kWqDecodeCols : kWqGemmCols;  // decode: four waves side by side
 }
 
 hipError_t launch_mx_quantize(const MxPlan& p, hipStream_t stream);

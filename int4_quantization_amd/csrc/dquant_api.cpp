@@ -146,7 +146,10 @@ dq_executor* new_executor(int op)
 }
 
 // Workgroups the weight-quantized matmul aims for when splitting k.
-constexpr int64_t kWqTargetBlocks = 2048;
+// Split-k targets (workgroups), measured: the decode kernel streams weights
+// once and wants the whole chip busy; the LDS-tiled kernel pays for each
+// split with a binary32 partial tile, so it stops at fewer.
+constexpr int64_t kWqTargetBlocks = 2048, kWqGemmTargetBlocks = 512;
 
 int pick_vpl(int64_t per_lane, const int* choices, int count)
 {
@@ -816,9 +819,10 @@ dq_status dq_weight_quant_matmul_get_workspace_size(const dq_tensor* x1, const d
     const bool kfit = x2->dtype == DQ_I8 ? k % 32 == 0 : k % 64 == 0;
     p.variant = p.transpose_x2 && kfit && aligned(x1->data, 16) && aligned(x2->data, 16) ? dq::WQ_VAR_MFMA
                                                                                        : dq::WQ_VAR_GENERIC;
-    p.tile = m <= 16 ? dq::WQ_TILE_DECODE : m <= 128 ? dq::WQ_TILE_2x2 : dq::WQ_TILE_GEMM;
-    // Few output tiles: split k so that about 2048 workgroups stream the
-    // weights; the binary32 partial sums [splits, m, n] live in the workspace.
+    p.tile = m <= 16 ? dq::WQ_TILE_DECODE : dq::WQ_TILE_GEMM;
+    // Few output tiles: split k so that about the target number of
+    // workgroups run; the binary32 partial sums [splits, m, n] live in the
+    // workspace.
     p.splits = 1;
     p.k_chunk = k;
     if (p.variant == dq::WQ_VAR_MFMA) {
@@ -826,7 +830,8 @@ dq_status dq_weight_quant_matmul_get_workspace_size(const dq_tensor* x1, const d
                               ((m + dq::wq_tile_rows(p.tile) - 1) / dq::wq_tile_rows(p.tile));
         const int64_t batch_k = static_cast<int64_t>(dq::wq_batch(p.tile)) * dq::kWqSuperK;
         const int64_t batches = (k + batch_k - 1) / batch_k;
-        int64_t want = tiles < kWqTargetBlocks ? (kWqTargetBlocks + tiles - 1) / tiles : 1;
+        const int64_t target = p.tile == dq::WQ_TILE_DECODE ? kWqTargetBlocks : kWqGemmTargetBlocks;
+        int64_t want = tiles < target ? (target + tiles - 1) / tiles : 1;
         want = want < batches ? want : batches;
         if (want > 1) {
             p.k_chunk = ((batches + want - 1) / want) * batch_k;

@@ -13,29 +13,27 @@
 // of two bf16 or two fp16 values are exact in binary32, so W is bit-exact
 // and only the order of the binary32 additions differs from an exact sum.
 //
-// wq_mfma_kernel (17 to 128 rows; weights stored [n, k], i.e. x2 transposed,
-// k contiguous):
-//   - A wave computes a (16 RM) x (16 RN) block of out with
-//     v_mfma_f32_16x16x32_{bf16,f16}.  Lane l supplies row (or column) l % 16
+// Matrix-core kernels (weights stored [n, k], i.e. x2 transposed, k
+// contiguous):
+//   - v_mfma_f32_16x16x32_{bf16,f16}: lane l supplies row (or column) l % 16
 //     and eight k values per instruction, and receives rows 4 (l / 16) ..
 //     + 3 of column l % 16.
-//   - The k axis is walked in supersteps of 128.  Since a dot product does
-//     not depend on the order of k, lane group g = l / 16 takes the 32
-//     consecutive k of [32 g, 32 g + 32) and splits them over the four
-//     instructions of the superstep; x1 uses the same assignment.  Each
-//     lane's weight load is therefore one contiguous 32-byte (int8) or
-//     16-byte (int4) run of its column, and its x1 load four 16-byte runs of
-//     its row.  No LDS is needed: the dequantized weight goes straight from
-//     registers into the matrix cores, and each wave owns its columns.
 //   - Dequantization follows the formula step by step in binary32 (signed
 //     byte or nibble -> binary32, + offset, * scale, round to T), so W is
-//     exact.  A group of 32 k never straddles a parameter group (the group
+//     exact.  A run of 32 k never straddles a parameter group (the group
 //     size is a multiple of 32).
 //   - Rows past m repeat the last row (their results are not stored);
 //     columns past n repeat the last column (likewise).  k runs in whole
 //     groups of 32 (int8) or 64 (int4) elements.
-// wq_decode_kernel (at most 16 rows) and wq_gemm_kernel (more than 128 rows)
-// are described where they are defined.
+//   - wq_decode_kernel (at most 16 rows) walks k in supersteps of 128.
+//     Since a dot product does not depend on the order of k, lane group
+//     g = l / 16 takes the 32 consecutive k of [32 g, 32 g + 32) and splits
+//     them over the superstep's four instructions, and x1 uses the same
+//     assignment: each lane's weight load is one contiguous 32-byte (int8)
+//     or 16-byte (int4) run of its column, and the dequantized weights go
+//     from registers straight into the matrix cores.
+//   - wq_gemm_kernel (more rows) stages 128 x 128 tiles in LDS.
+//   Both are described further where they are defined.
 // wq_generic_kernel: any layout and alignment, one thread per output
 // element, binary32 accumulation in k order.  It is the path for weights
 // stored [k, n].
@@ -164,30 +162,8 @@ __device__ __forceinline__ f32x4 mfma16(const uint4& a, const uint4& b, const f3
 // (v_cvt_f32_i32 with an SDWA byte select).  int8: the codes themselves.
 // int4: each nibble is first moved to the high half of a byte, so the byte
 // reads 16 * code; the caller folds the factor 16 back exactly.
-template <int WT>
-__device__ __forceinline__ void decode32(const uint4& lo, const uint4& hi, float (&v)[32])
-{
-    if constexpr (WT == WQ_I8) {
-        const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-#pragma unroll
-        for (int i = 0; i < 32; ++i)
-            v[i] = static_cast<float>(static_cast<int8_t>(w[i / 4] >> (8 * (i % 4))));
-    } else {
-        const uint32_t w[4] = {lo.x, lo.y, lo.z, lo.w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const uint32_t even = (w[q] << 4) & 0xF0F0F0F0u;  // nibbles 0, 2, 4, 6
-            const uint32_t odd = w[q] & 0xF0F0F0F0u;          // nibbles 1, 3, 5, 7
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                v[8 * q + 2 * j] = static_cast<float>(static_cast<int8_t>(even >> (8 * j)));
-                v[8 * q + 2 * j + 1] = static_cast<float>(static_cast<int8_t>(odd >> (8 * j)));
-            }
-        }
-    }
-}
-
-// Eight of the 32 codes (sub-step s of a lane's run), as decode32 gives them.
+// Eight of a lane's 32 codes (sub-step s of its run) as binary32: the code,
+// or 16 * code for int4 (the nibble moved to the high half of a byte).
 template <int WT>
 __device__ __forceinline__ void decode8(const uint4& lo, const uint4& hi, int s, float (&v)[8])
 {
@@ -222,162 +198,6 @@ __device__ __forceinline__ float dequant1(float d, float s, float o)
         return u * s;
     } else {
         return d * s;
-    }
-}
-
-template <int XT, int WT, int POL, bool OFF, int RM, int RN, int U>
-__global__ __launch_bounds__(kBlock) void wq_mfma_kernel(const WqArgs a)
-{
-    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-    const int li = lane % 16, g = lane / 16;
-    const int64_t m0 = static_cast<int64_t>(blockIdx.y) * (16 * RM);
-    const int64_t n0 = (static_cast<int64_t>(blockIdx.x) * (kBlock / kWave) + wave) * (16 * RN);
-    constexpr int64_t kBytes32 = WT == WQ_I8 ? 32 : 16;  // weight bytes of 32 k
-
-    const uint16_t* arow[RM];
-#pragma unroll
-    for (int r = 0; r < RM; ++r) {
-        const int64_t row = m0 + 16 * r + li;
-        arow[r] = a.x1 + (row < a.m ? row : a.m - 1) * a.k;
-    }
-    const uint8_t* bcol[RN];
-    int64_t col[RN];
-#pragma unroll
-    for (int t = 0; t < RN; ++t) {
-        const int64_t c = n0 + 16 * t + li;
-        col[t] = c < a.n ? c : a.n - 1;
-        bcol[t] = a.x2 + col[t] * (a.k / 32) * kBytes32;
-    }
-    float s_chan[RN] = {}, o_chan[RN] = {};
-    if constexpr (POL != DQ_PER_GROUP) {
-#pragma unroll
-        for (int t = 0; t < RN; ++t) {
-            const int64_t p = param_index<POL>(a, col[t], 0, true);
-            s_chan[t] = t_to_f32<XT>(a.scale[p]);
-            o_chan[t] = OFF ? t_to_f32<XT>(a.offset[p]) : 0.0f;
-        }
-    }
-
-    f32x4 acc[RM][RN];
-#pragma unroll
-    for (int r = 0; r < RM; ++r)
-#pragma unroll
-        for (int t = 0; t < RN; ++t)
-            acc[r][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-
-    // U supersteps per batch: every load of the batch is issued before any
-    // arithmetic, so U weight runs and U x1 runs per lane are in flight.
-    const int64_t k_beg = static_cast<int64_t>(blockIdx.z) * a.k_chunk;
-    const int64_t k_end = k_beg + a.k_chunk < a.k ? k_beg + a.k_chunk : a.k;
-    for (int64_t kb = k_beg; kb < k_end; kb += U * kWqSuper) {
-        uint4 bw[U][RN][2];
-        uint4 av[U][RM][4];
-        int64_t kcs[U];
-        bool live[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t kg = kb + u * kWqSuper + 32 * g;  // this lane group's 32 k
-            live[u] = kg < k_end;                               // k is a multiple of 32
-            kcs[u] = live[u] ? kg : 0;
-#pragma unroll
-            for (int t = 0; t < RN; ++t) {
-                const uint8_t* p = bcol[t] + (kcs[u] / 32) * kBytes32;
-                bw[u][t][0] = ld_stream16(p);
-                bw[u][t][1] = WT == WQ_I8 ? ld_stream16(p + 16) : make_uint4(0, 0, 0, 0);
-            }
-#pragma unroll
-            for (int r = 0; r < RM; ++r)
-#pragma unroll
-                for (int s = 0; s < 4; ++s)
-                    av[u][r][s] = *reinterpret_cast<const uint4*>(arow[r] + kcs[u] + 8 * s);
-        }
-        float sg[U][RN], og[U][RN];
-        if constexpr (POL == DQ_PER_GROUP) {
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-#pragma unroll
-                for (int t = 0; t < RN; ++t) {
-                    const int64_t p = param_index<POL>(a, col[t], kcs[u], true);
-                    sg[u][t] = t_to_f32<XT>(a.scale[p]);
-                    og[u][t] = OFF ? t_to_f32<XT>(a.offset[p]) : 0.0f;
-                }
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            uint4 bv[RN][4];
-#pragma unroll
-            for (int t = 0; t < RN; ++t) {
-                float sc = POL == DQ_PER_GROUP ? sg[u][t] : s_chan[t];
-                const float of = POL == DQ_PER_GROUP ? og[u][t] : o_chan[t];
-                if constexpr (WT == WQ_I4 && !OFF)
-                    sc *= 0.0625f;  // the decoded values are 16 * code
-                float v[32];
-                decode32<WT>(bw[u][t][0], bw[u][t][1], v);
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    float w[8];
-#pragma unroll
-                    for (int j = 0; j < 8; ++j)
-                        w[j] = dequant1<WT, OFF>(v[8 * s + j], sc, of);
-                    bv[t][s] = pack8_t<XT>(w);
-                }
-            }
-            if (!live[u]) {
-#pragma unroll
-                for (int r = 0; r < RM; ++r)
-#pragma unroll
-                    for (int s = 0; s < 4; ++s)
-                        av[u][r][s] = make_uint4(0, 0, 0, 0);
-            }
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-#pragma unroll
-                for (int r = 0; r < RM; ++r)
-#pragma unroll
-                    for (int t = 0; t < RN; ++t)
-                        acc[r][t] = mfma16<XT>(av[u][r][s], bv[t][s], acc[r][t]);
-        }
-    }
-
-    // Epilogue: lane holds rows 4 g .. 4 g + 3 of column li of each block.
-    // With several splits of k, each writes its binary32 partial sums and
-    // wq_reduce_kernel finishes the sum, bias and x3 in a fixed order.
-    if (a.partial) {
-#pragma unroll
-        for (int t = 0; t < RN; ++t) {
-            const int64_t c = n0 + 16 * t + li;
-            if (c >= a.n)
-                continue;
-#pragma unroll
-            for (int r = 0; r < RM; ++r)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int64_t row = m0 + 16 * r + 4 * g + i;
-                    if (row < a.m)
-                        a.partial[(static_cast<int64_t>(blockIdx.z) * a.m + row) * a.n + c] = acc[r][t][i];
-                }
-        }
-        return;
-    }
-#pragma unroll
-    for (int t = 0; t < RN; ++t) {
-        const int64_t c = n0 + 16 * t + li;
-        if (c >= a.n)
-            continue;
-        const float b = a.bias ? t_to_f32<XT>(a.bias[c]) : 0.0f;
-#pragma unroll
-        for (int r = 0; r < RM; ++r) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int64_t row = m0 + 16 * r + 4 * g + i;
-                if (row >= a.m)
-                    continue;
-                float v = acc[r][t][i] + b;
-                if (a.x3)
-                    v += t_to_f32<XT>(a.x3[row * a.n + c]);
-                a.out[row * a.n + c] = f32_to_t<XT>(v);
-            }
-        }
     }
 }
 
@@ -700,9 +520,9 @@ __global__ __launch_bounds__(kGemmThreads) void wq_gemm_kernel(const WqArgs a)
             const int64_t c = n0 + cl < a.n ? n0 + cl : a.n - 1;
             int64_t kk = kb + static_cast<int64_t>(kv) * KPV;
             kk = kk < k_end ? kk : k_beg;
-            // Cached, unlike the decode and 2 x 2 kernels that read each weight
-            // once: every 128-row tile re-reads these (the non-temporal hint
-            // cost 14% on 4096 x 8192 x 8192).
+            // Cached, unlike the decode kernel that reads each weight once:
+            // every 128-row tile re-reads these (the non-temporal hint cost
+            // 14% on 4096 x 8192 x 8192).
             const u32x4 v = *reinterpret_cast<const u32x4*>(a.x2 + c * (a.k / 32) * kBytes32 + kk * kBytes32 / 32);
             br[p] = make_uint4(v.x, v.y, v.z, v.w);
             if constexpr (POL == DQ_PER_GROUP) {
@@ -910,39 +730,6 @@ __global__ __launch_bounds__(kBlock) void wq_reduce_kernel(const WqArgs a, int s
     a.out[idx] = f32_to_t<XT>(v);
 }
 
-template <int XT, int WT, int POL, bool OFF, int RM, int RN, int U>
-hipError_t launch_mfma(const WqArgs& a, int splits, hipStream_t stream)
-{
-    const int64_t cols = static_cast<int64_t>(kBlock / kWave) * 16 * RN;
-    const int64_t gx = (a.n + cols - 1) / cols;
-    const int64_t rows = 16 * RM;
-    const int64_t gy_total = (a.m + rows - 1) / rows;
-    constexpr int64_t kMaxY = 65535;
-    if (splits > 1 && gy_total > kMaxY)
-        return hipErrorInvalidConfiguration;  // split k is planned for few rows only
-    for (int64_t y0 = 0; y0 < gy_total; y0 += kMaxY) {
-        WqArgs c = a;
-        c.x1 = a.x1 + y0 * rows * a.k;
-        c.out = a.out + y0 * rows * a.n;
-        c.x3 = a.x3 ? a.x3 + y0 * rows * a.n : nullptr;
-        c.m = a.m - y0 * rows < kMaxY * rows ? a.m - y0 * rows : kMaxY * rows;
-        const int64_t gy = (c.m + rows - 1) / rows;
-        hipLaunchKernelGGL((wq_mfma_kernel<XT, WT, POL, OFF, RM, RN, U>),
-                           dim3(static_cast<uint32_t>(gx), static_cast<uint32_t>(gy), static_cast<uint32_t>(splits)),
-                           dim3(kBlock), 0, stream, c);
-        const hipError_t err = hipGetLastError();
-        if (err != hipSuccess)
-            return err;
-    }
-    if (splits > 1) {
-        const int64_t blocks = (a.m * a.n + kBlock - 1) / kBlock;
-        hipLaunchKernelGGL((wq_reduce_kernel<XT>), dim3(static_cast<uint32_t>(blocks)), dim3(kBlock), 0, stream, a,
-                           splits);
-        return hipGetLastError();
-    }
-    return hipSuccess;
-}
-
 template <int XT, int WT, int POL, bool OFF, int RN, int U>
 hipError_t launch_decode(const WqArgs& a, int splits, hipStream_t stream)
 {
@@ -992,11 +779,9 @@ hipError_t launch_gemm(const WqArgs& a, int splits, hipStream_t stream)
 template <int XT, int WT, int POL, bool OFF>
 hipError_t pick_tile(const WqPlan& p, const WqArgs& a, hipStream_t stream)
 {
-    if (p.tile == WQ_TILE_GEMM)
-        return launch_gemm<XT, WT, POL, OFF>(a, p.splits, stream);
     if (p.tile == WQ_TILE_DECODE)
         return launch_decode<XT, WT, POL, OFF, kWqDecodeCols, wq_batch(WQ_TILE_DECODE)>(a, p.splits, stream);
-    return launch_mfma<XT, WT, POL, OFF, 2, 2, wq_batch(WQ_TILE_2x2)>(a, p.splits, stream);
+    return launch_gemm<XT, WT, POL, OFF>(a, p.splits, stream);
 }
 
 template <int XT, int WT, int POL>
