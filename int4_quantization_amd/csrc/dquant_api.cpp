@@ -146,10 +146,10 @@ dq_executor* new_executor(int op)
 }
 
 // Workgroups the weight-quantized matmul aims for when splitting k.
-// Split-k targets (workgroups), measured: the decode kernel streams weights
-// once and wants the whole chip busy; the LDS-tiled kernel pays for each
-// split with a binary32 partial tile, so it stops at fewer.
-constexpr int64_t kWqTargetBlocks = 2048, kWqGemmTargetBlocks = 512;
+// Split-k targets (workgroups), measured: k is split only while the output
+// tiles alone would leave the chip short of work, since every split costs a
+// binary32 partial tile and a reduce launch.
+constexpr int64_t kWqTargetBlocks = 384, kWqGemmTargetBlocks = 512;
 
 int pick_vpl(int64_t per_lane, const int* choices, int count)
 {
