@@ -107,12 +107,17 @@ def test_wq_unaligned_x1(orc):
     check_weight_quant_matmul(orc, q, dev=d)
 
 
-@pytest.mark.parametrize("m,k,n", [(1, 4096, 256), (16, 8192, 192), (24, 2048, 64)])
-def test_wq_split_k(orc, m, k, n):
+@pytest.mark.parametrize("m,k,n,weight", [(1, 4096, 256, "int4"), (16, 8192, 192, "int4"), (24, 2048, 64, "int4"),
+                                          (130, 1024, 96, "int4"), (17, 608, 72, "int8"), (260, 2048, 136, "int8")])
+def test_wq_split_k(orc, m, k, n, weight):
     """Few output tiles: k is split across workgroups (binary32 partial sums
-    in the workspace, added in split order by a second kernel)."""
-    announce("wq split k", m, k, n)
-    q = synth.wq_inputs(m, k, n, 5000 + m, weight="int4", group_size=128, bias=True, x3=True)
+    in the workspace, added in split order by a second kernel), for the
+    decode kernel and for the LDS-tiled one with one, two and three
+    128-row tiles (ragged), ragged columns and k not a multiple of the
+    split."""
+    announce("wq split k", m, k, n, weight)
+    q = synth.wq_inputs(m, k, n, 5000 + m, weight=weight, group_size=128 if weight == "int4" else 64,
+                        bias=True, x3=True)
     check_weight_quant_matmul(orc, q)
 
 
