@@ -61,7 +61,8 @@ struct WqPlan {
 // Matrix-core kernel geometry: k per superstep (four lane groups of 32) and
 // supersteps whose loads are issued together, per register tile.
 constexpr int kWqSuperK = 128;
-constexpr int kWqDecodeCols = 1;  // 16-column blocks per wave in the decode kernel
+constexpr int kWqDecodeCols = 1;   // 16-column blocks per wave in the decode kernel
+constexpr int kWqDecodeWaves = 4;  // waves per decode workgroup (they share one x1 staging)
 // LDS-tiled kernel: output tile and k-step (a divisor of kWqSuperK).
 constexpr int kWqGemmRows = 128, kWqGemmCols = 128, kWqGemmK = 128;
 constexpr int wq_batch(int tile)
@@ -74,7 +75,7 @@ constexpr int wq_tile_rows(int tile)
 }
 constexpr int wq_tile_cols(int tile)
 {
-    return tile == WQ_TILE_DECODE ? 4 * 16 * kWqDecodeCols : kWqGemmCols;  // decode: four waves side by side
+    return tile == WQ_TILE_DECODE ? kWqDecodeWaves * 16 * kWqDecodeCols : kWqGemmCols;  // decode: waves side by side
 }
 
 hipError_t launch_mx_quantize(const MxPlan& p, hipStream_t stream);

@@ -210,21 +210,34 @@ __device__ __forceinline__ float dequant1(float d, float s, float o)
 // current one.  k is split across workgroups (blockIdx.z) as planned on the
 // host.
 // ---------------------------------------------------------------------------
-template <int XT, int WT, int POL, bool OFF, int RN, int U>
-__global__ __launch_bounds__(kBlock) void wq_decode_kernel(const WqArgs a)
+// PAIR: per-group parameters with groups of 128 (one per superstep) and an
+// even group count, so the two groups of a batch are adjacent in a column's
+// parameter row and one 4-byte load fetches both (the loads of the per-group
+// parameters cost as much time as the weight stream when made one by one).
+template <int XT, int WT, int POL, bool OFF, int RN, int U, bool PAIR>
+__global__ __launch_bounds__(kWqDecodeWaves * kWave) void wq_decode_kernel(const WqArgs a)
 {
+    static_assert(!PAIR || (POL == DQ_PER_GROUP && U == 2), "paired parameters: two supersteps of 128 per batch");
+    constexpr int NT = kWqDecodeWaves * kWave;
     constexpr int BK = U * kWqSuper;       // k per batch
-    constexpr int ROWB = BK * 2 + 16;      // LDS bytes per staged x1 row (16-byte pad: no bank conflicts)
+    constexpr int ROWB = BK * 2 + 32;      // LDS bytes per staged x1 row (a 32-byte pad, see below)
     constexpr int XV = BK / 8;             // 16-byte x1 vectors per row and batch
-    constexpr int XP = 16 * XV / kBlock;   // staged vectors per thread and batch
-    static_assert(XP * kBlock == 16 * XV, "a batch of 16 rows divides over the workgroup");
+    constexpr int XP = 16 * XV / NT;       // staged vectors per thread and batch
+    static_assert(XP * NT == 16 * XV, "a batch of 16 rows divides over the workgroup");
+    // The operand read of superstep u and sub-step s2 takes, in lane group g,
+    // the 8 k of chunk 16 u + 4 g + s2.  The chunks are stored in slot
+    // 16 u + 4 s2 + g (the two 2-bit fields swapped), so the 4 lane groups
+    // read 4 adjacent 16-byte slots of 16 rows: at a row stride of 8 modulo
+    // 16 dwords that is free of bank conflicts on gfx950.  Slot and chunk
+    // map to each other by the same swap.
+    auto swap_chunk = [](int c) { return (c & ~15) | ((c & 3) << 2) | ((c >> 2) & 3); };
     constexpr int64_t kBytes32 = WT == WQ_I8 ? 32 : 16;  // weight bytes of 32 k
     constexpr int WV = WT == WQ_I8 ? 2 : 1;              // 16-byte weight loads per 32 k
     __shared__ __align__(16) uint8_t xs[2][16 * ROWB];
 
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const int li = lane % 16, g = lane / 16;
-    const int64_t n0 = (static_cast<int64_t>(blockIdx.x) * (kBlock / kWave) + wave) * (16 * RN);
+    const int64_t n0 = (static_cast<int64_t>(blockIdx.x) * kWqDecodeWaves + wave) * (16 * RN);
     const int64_t k_beg = static_cast<int64_t>(blockIdx.z) * a.k_chunk;
     const int64_t k_end = k_beg + a.k_chunk < a.k ? k_beg + a.k_chunk : a.k;
     const int nb = static_cast<int>((k_end - k_beg + BK - 1) / BK);
@@ -258,13 +271,13 @@ __global__ __launch_bounds__(kBlock) void wq_decode_kernel(const WqArgs a)
     const __amdgpu_buffer_rsrc_t ors = make_rsrc(OFF ? a.offset : a.scale, static_cast<uint32_t>(a.n * a.groups * 2));
 
     // Loads of batch b (clamped to the last batch: a repeat is harmless).
-    // x1: vector q = p * kBlock + tid of the 16 x XV grid; rows past m and
-    // k past the split are zeros.
+    // x1: slot q = p * NT + tid of the 16 x XV grid, holding chunk
+    // swap_chunk(slot); rows past m and k past the split are zeros.
     auto load_x = [&](int b, uint4 (&xr)[XP]) {
         const int bb = b < nb ? b : nb - 1;
 #pragma unroll
         for (int p = 0; p < XP; ++p) {
-            const int q = p * kBlock + tid, row = q / XV, kv = q % XV;
+            const int q = p * NT + tid, row = q / XV, kv = swap_chunk(q % XV);
             const uint32_t kk = static_cast<uint32_t>(k_beg + static_cast<int64_t>(bb) * BK) + kv * 8;
             const bool ok = row < a.m && kk < k_end;
             const uint32_t rr = static_cast<uint32_t>(row < a.m ? row : a.m - 1);
@@ -276,8 +289,8 @@ __global__ __launch_bounds__(kBlock) void wq_decode_kernel(const WqArgs a)
     auto store_x = [&](int buf, const uint4 (&xr)[XP]) {
 #pragma unroll
         for (int p = 0; p < XP; ++p) {
-            const int q = p * kBlock + tid, row = q / XV, kv = q % XV;
-            *reinterpret_cast<uint4*>(&xs[buf][row * ROWB + kv * 16]) = xr[p];
+            const int q = p * NT + tid, row = q / XV;
+            *reinterpret_cast<uint4*>(&xs[buf][row * ROWB + (q % XV) * 16]) = xr[p];
         }
     };
     // Weights (and per-group parameters) of batch b for this lane: 32 k per
@@ -285,6 +298,22 @@ __global__ __launch_bounds__(kBlock) void wq_decode_kernel(const WqArgs a)
     auto load_w = [&](int b, uint4 (&w)[U][RN][WV], float (&sg)[U][RN], float (&og)[U][RN]) {
         const int bb = b < nb ? b : nb - 1;
         const uint32_t kb = static_cast<uint32_t>(k_beg + static_cast<int64_t>(bb) * BK);
+        if constexpr (PAIR) {
+#pragma unroll
+            for (int t = 0; t < RN; ++t) {
+                const uint32_t pi = static_cast<uint32_t>(col[t] * a.groups) + kb / kWqSuper;  // even
+                const uint32_t sv = __builtin_amdgcn_raw_buffer_load_b32(srs, pi * 2, 0, 0);
+                sg[0][t] = t_to_f32<XT>(static_cast<uint16_t>(sv));
+                sg[1][t] = t_to_f32<XT>(static_cast<uint16_t>(sv >> 16));
+                if constexpr (OFF) {
+                    const uint32_t ov = __builtin_amdgcn_raw_buffer_load_b32(ors, pi * 2, 0, 0);
+                    og[0][t] = t_to_f32<XT>(static_cast<uint16_t>(ov));
+                    og[1][t] = t_to_f32<XT>(static_cast<uint16_t>(ov >> 16));
+                } else {
+                    og[0][t] = og[1][t] = 0.0f;
+                }
+            }
+        }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const uint32_t kg = kb + u * kWqSuper + 32 * g;
@@ -295,7 +324,7 @@ __global__ __launch_bounds__(kBlock) void wq_decode_kernel(const WqArgs a)
                 w[u][t][0] = buf_load16<kBufNonTemporal>(wrs, off);
                 if constexpr (WV == 2)
                     w[u][t][WV - 1] = buf_load16<kBufNonTemporal>(wrs, off + 16);
-                if constexpr (POL == DQ_PER_GROUP) {
+                if constexpr (POL == DQ_PER_GROUP && !PAIR) {
                     const uint32_t pi = static_cast<uint32_t>(col[t] * a.groups) + div_by(kc, a.by_gs);
                     sg[u][t] = t_to_f32<XT>(buf_load2(srs, pi * 2));
                     og[u][t] = OFF ? t_to_f32<XT>(buf_load2(ors, pi * 2)) : 0.0f;
@@ -315,7 +344,7 @@ __global__ __launch_bounds__(kBlock) void wq_decode_kernel(const WqArgs a)
             uint4 av[4];
 #pragma unroll
             for (int s2 = 0; s2 < 4; ++s2)
-                av[s2] = *reinterpret_cast<const uint4*>(&xs[buf][li * ROWB + (u * kWqSuper + 32 * g + 8 * s2) * 2]);
+                av[s2] = *reinterpret_cast<const uint4*>(&xs[buf][li * ROWB + (16 * u + 4 * s2 + g) * 16]);
 #pragma unroll
             for (int t = 0; t < RN; ++t) {
                 float sc = s_chan[t], of = o_chan[t];
@@ -733,10 +762,21 @@ __global__ __launch_bounds__(kBlock) void wq_reduce_kernel(const WqArgs a, int s
 template <int XT, int WT, int POL, bool OFF, int RN, int U>
 hipError_t launch_decode(const WqArgs& a, int splits, hipStream_t stream)
 {
-    const int64_t cols = static_cast<int64_t>(kBlock / kWave) * 16 * RN;
+    const int64_t cols = static_cast<int64_t>(kWqDecodeWaves) * 16 * RN;
     const int64_t gx = (a.n + cols - 1) / cols;
-    hipLaunchKernelGGL((wq_decode_kernel<XT, WT, POL, OFF, RN, U>),
-                       dim3(static_cast<uint32_t>(gx), 1, static_cast<uint32_t>(splits)), dim3(kBlock), 0, stream, a);
+    const dim3 grid(static_cast<uint32_t>(gx), 1, static_cast<uint32_t>(splits));
+    // Batch starts (k_chunk is a multiple of the batch) fall on even groups.
+    if constexpr (POL == DQ_PER_GROUP && U == 2) {
+        if (a.group_size == kWqSuper && a.groups % 2 == 0 && a.k_chunk % (U * kWqSuper) == 0)
+            hipLaunchKernelGGL((wq_decode_kernel<XT, WT, POL, OFF, RN, U, true>), grid, dim3(kWqDecodeWaves * kWave),
+                               0, stream, a);
+        else
+            hipLaunchKernelGGL((wq_decode_kernel<XT, WT, POL, OFF, RN, U, false>), grid,
+                               dim3(kWqDecodeWaves * kWave), 0, stream, a);
+    } else {
+        hipLaunchKernelGGL((wq_decode_kernel<XT, WT, POL, OFF, RN, U, false>), grid, dim3(kWqDecodeWaves * kWave), 0,
+                           stream, a);
+    }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || splits == 1)
         return err;
