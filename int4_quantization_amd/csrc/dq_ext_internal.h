@@ -65,6 +65,10 @@ constexpr int kWqDecodeCols = 1;   // 16-column blocks per wave in the decode ke
 constexpr int kWqDecodeWaves = 4;  // waves per decode workgroup (they share one x1 staging)
 // LDS-tiled kernel: output tile and k-step (a divisor of kWqSuperK).
 constexpr int kWqGemmRows = 128, kWqGemmCols = 128, kWqGemmK = 128;
+// Per-group parameters of the LDS-tiled kernel come in windows of this many
+// groups when groups are one k-step long; k splits are then planned in
+// multiples of the window.
+constexpr int kWqParamWindow = 8;
 constexpr int wq_batch(int tile)
 {
     return tile == WQ_TILE_DECODE ? 2 : 1;  // GEMM: k splits in steps of 128

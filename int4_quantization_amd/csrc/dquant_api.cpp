@@ -835,6 +835,10 @@ dq_status dq_weight_quant_matmul_get_workspace_size(const dq_tensor* x1, const d
         want = want < batches ? want : batches;
         if (want > 1) {
             p.k_chunk = ((batches + want - 1) / want) * batch_k;
+            // Keep whole parameter windows per split where the kernel uses them.
+            const int64_t window = static_cast<int64_t>(dq::kWqParamWindow) * dq::kWqGemmK;
+            if (p.tile == dq::WQ_TILE_GEMM && policy == DQ_PER_GROUP && group_size == dq::kWqGemmK)
+                p.k_chunk = (p.k_chunk + window - 1) / window * window;
             p.splits = static_cast<int>((k + p.k_chunk - 1) / p.k_chunk);
         }
         if (p.splits > 1)

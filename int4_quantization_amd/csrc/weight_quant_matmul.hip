@@ -502,7 +502,13 @@ constexpr int kGemmBM = kWqGemmRows, kGemmBN = kWqGemmCols, kGemmBK = kWqGemmK;
 static_assert(kWqSuperK % kGemmBK == 0, "k splits fall on k-step boundaries");
 constexpr int kGemmThreads = kGemmBM / 64 * 2 * kWave;  // waves in a (BM / 64) x 2 grid
 
-template <int XT, int WT, int POL, bool OFF>
+// PW (per-group parameters, groups of one k-step, kWqParamWindow-group
+// aligned splits): once per kWqParamWindow steps, half of the threads load
+// a window of consecutive scales of one column with one 16-byte load and the
+// other half the offsets, into an LDS table; otherwise every weight vector
+// loads its own 2-byte parameters each step, each such load touching one
+// cache line per column (15-18% of the kernel on int4 g128 shapes).
+template <int XT, int WT, int POL, bool OFF, bool PW>
 __global__ __launch_bounds__(kGemmThreads) void wq_gemm_kernel(const WqArgs a)
 {
     constexpr int BM = kGemmBM, BN = kGemmBN, BK = kGemmBK, LR = kGemmBK + kLdsPad, NT = kGemmThreads;
@@ -518,6 +524,9 @@ __global__ __launch_bounds__(kGemmThreads) void wq_gemm_kernel(const WqArgs a)
     __shared__ __align__(16) uint16_t smem[kStage > kEpi ? kStage : kEpi];
     uint16_t* const As = smem;            // [BM][LR]: x1 rows
     uint16_t* const Bs = smem + BM * LR;  // [BN][LR]: dequantized weight columns
+    constexpr int GW = kWqParamWindow;
+    static_assert(!PW || (POL == DQ_PER_GROUP && NT >= 2 * BN), "a parameter window per column and tensor");
+    __shared__ __align__(16) uint16_t pws[PW && OFF ? 2 : 1][PW ? BN : 1][PW ? GW : 1];  // [tensor][column][group]
 
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const int li = lane % 16, g = lane / 16;
@@ -554,20 +563,40 @@ __global__ __launch_bounds__(kGemmThreads) void wq_gemm_kernel(const WqArgs a)
             // 14% on 4096 x 8192 x 8192).
             const u32x4 v = *reinterpret_cast<const u32x4*>(a.x2 + c * (a.k / 32) * kBytes32 + kk * kBytes32 / 32);
             br[p] = make_uint4(v.x, v.y, v.z, v.w);
-            if constexpr (POL == DQ_PER_GROUP) {
+            if constexpr (POL == DQ_PER_GROUP && !PW) {
                 const int64_t pi = c * a.groups + div_by(static_cast<uint32_t>(kk), a.by_gs);
                 bs[p] = t_to_f32<XT>(a.scale[pi]);
                 bo[p] = OFF ? t_to_f32<XT>(a.offset[pi]) : 0.0f;
-            } else {
+            } else if constexpr (POL != DQ_PER_GROUP) {
+                // Reloaded each step (cached): keeping them in registers
+                // across the loop measured 7% slower.
                 const int64_t pi = POL == DQ_PER_TENSOR ? 0 : c;
                 bs[p] = t_to_f32<XT>(a.scale[pi]);
                 bo[p] = OFF ? t_to_f32<XT>(a.offset[pi]) : 0.0f;
             }
         }
     };
+    // The parameter window of steps kt .. kt + GW - 1 (kt a multiple of GW):
+    // thread j < BN takes column j's scales, BN + j its offsets.
+    uint4 pwr = make_uint4(0, 0, 0, 0);
+    auto load_pw = [&](int kt) {
+        if (PW && tid < (OFF ? 2 : 1) * BN) {
+            const int j = tid % BN;
+            const int64_t c = n0 + j < a.n ? n0 + j : a.n - 1;
+            const int64_t g0 = k_beg / BK + kt;  // groups are one step long
+            const uint16_t* src = (tid < BN ? a.scale : a.offset) + c * a.groups + g0;
+            const u32x4 v = *reinterpret_cast<const u32x4*>(src);
+            pwr = make_uint4(v.x, v.y, v.z, v.w);
+        }
+    };
+    auto store_pw = [&]() {
+        if (PW && tid < (OFF ? 2 : 1) * BN)
+            *reinterpret_cast<uint4*>(&pws[tid / BN][tid % BN][0]) = pwr;
+    };
     // Registers -> LDS: x1 as is; weights dequantized (exact binary32 steps,
     // one rounding to T) into the [column][k] layout the operands read.
-    auto store = [&](const uint4 (&ar)[AV], const uint4 (&br)[BV], const float (&bs)[BV], const float (&bo)[BV]) {
+    auto store = [&](int kt, const uint4 (&ar)[AV], const uint4 (&br)[BV], const float (&bs)[BV],
+                     const float (&bo)[BV]) {
 #pragma unroll
         for (int p = 0; p < AV; ++p) {
             const int q = p * NT + tid, row = q / (BK / 8);
@@ -580,15 +609,16 @@ __global__ __launch_bounds__(kGemmThreads) void wq_gemm_kernel(const WqArgs a)
                 break;
             int cl, kv;
             wq_bmap<WT, BK>(q, cl, kv);
-            const float sc = WT == WQ_I4 && !OFF ? bs[p] * 0.0625f : bs[p];
-            const float of = bo[p];
+            float s0 = bs[p], of = bo[p];
+            if constexpr (PW) {
+                s0 = t_to_f32<XT>(pws[0][cl][kt % GW]);
+                of = OFF ? t_to_f32<XT>(pws[OFF ? 1 : 0][cl][kt % GW]) : 0.0f;
+            }
+            const float sc = WT == WQ_I4 && !OFF ? s0 * 0.0625f : s0;
 #pragma unroll
             for (int s2 = 0; s2 < KPV / 8; ++s2) {
                 float v[8], w[8];
-                if constexpr (WT == WQ_I8)
-                    decode8<WT>(br[p], br[p], s2, v);  // bytes 8 s2 .. 8 s2 + 7 of the vector
-                else
-                    decode8<WT>(br[p], br[p], s2, v);
+                decode8<WT>(br[p], br[p], s2, v);  // the vector's codes 8 s2 .. 8 s2 + 7
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     if constexpr (WT == WQ_I4 && OFF)
@@ -612,11 +642,18 @@ __global__ __launch_bounds__(kGemmThreads) void wq_gemm_kernel(const WqArgs a)
         uint4 ar[AV], br[BV];
         float bs[BV], bo[BV];
         load(0, ar, br, bs, bo);
+        load_pw(0);
         for (int kt = 0; kt < nk; ++kt) {
             __syncthreads();  // the previous step's operand reads are done
-            store(ar, br, bs, bo);
+            if (PW && kt % GW == 0) {  // a new parameter window (uniform)
+                store_pw();
+                __syncthreads();
+            }
+            store(kt, ar, br, bs, bo);
             __syncthreads();
             load(kt + 1 < nk ? kt + 1 : kt, ar, br, bs, bo);  // in flight during the matrix-core work
+            if (PW && (kt + 1) % GW == 0 && kt + 1 < nk)
+                load_pw(kt + 1);
 #pragma unroll
             for (int s2 = 0; s2 < BK / 32; ++s2) {
                 uint4 av[4], bv[TN];
@@ -785,6 +822,19 @@ hipError_t launch_decode(const WqArgs& a, int splits, hipStream_t stream)
     return hipGetLastError();
 }
 
+// Whether the LDS-tiled kernel can take per-group parameters in windows:
+// groups of one k-step, whole windows per column and per split, and 16-byte
+// aligned parameter rows.
+template <int POL, bool OFF>
+bool gemm_param_window(const WqArgs& a)
+{
+    if (POL != DQ_PER_GROUP)
+        return false;
+    const auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+    return a.group_size == kGemmBK && a.groups % kWqParamWindow == 0 && a.k_chunk % (kWqParamWindow * kGemmBK) == 0 &&
+           al16(a.scale) && (!OFF || al16(a.offset));
+}
+
 template <int XT, int WT, int POL, bool OFF>
 hipError_t launch_gemm(const WqArgs& a, int splits, hipStream_t stream)
 {
@@ -800,9 +850,15 @@ hipError_t launch_gemm(const WqArgs& a, int splits, hipStream_t stream)
         c.x3 = a.x3 ? a.x3 + y0 * kGemmBM * a.n : nullptr;
         c.m = a.m - y0 * kGemmBM < kMaxY * kGemmBM ? a.m - y0 * kGemmBM : kMaxY * kGemmBM;
         const int64_t gy = (c.m + kGemmBM - 1) / kGemmBM;
-        hipLaunchKernelGGL((wq_gemm_kernel<XT, WT, POL, OFF>),
-                           dim3(static_cast<uint32_t>(gx), static_cast<uint32_t>(gy), static_cast<uint32_t>(splits)),
-                           dim3(kGemmThreads), 0, stream, c);
+        const dim3 grid(static_cast<uint32_t>(gx), static_cast<uint32_t>(gy), static_cast<uint32_t>(splits));
+        if constexpr (POL == DQ_PER_GROUP) {
+            if (gemm_param_window<POL, OFF>(a))
+                hipLaunchKernelGGL((wq_gemm_kernel<XT, WT, POL, OFF, true>), grid, dim3(kGemmThreads), 0, stream, c);
+            else
+                hipLaunchKernelGGL((wq_gemm_kernel<XT, WT, POL, OFF, false>), grid, dim3(kGemmThreads), 0, stream, c);
+        } else {
+            hipLaunchKernelGGL((wq_gemm_kernel<XT, WT, POL, OFF, false>), grid, dim3(kGemmThreads), 0, stream, c);
+        }
         const hipError_t err = hipGetLastError();
         if (err != hipSuccess)
             return err;

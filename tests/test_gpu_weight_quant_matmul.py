@@ -121,6 +121,37 @@ def test_wq_split_k(orc, m, k, n, weight):
     check_weight_quant_matmul(orc, q)
 
 
+@pytest.mark.parametrize("m,k,n,weight,offset", [(130, 1024, 96, "int4", True), (300, 1024, 1100, "int4", True),
+                                                 (260, 4096, 136, "int4", True), (140, 2048, 256, "int8", False)])
+def test_wq_group128_windows(orc, m, k, n, weight, offset):
+    """Groups of 128 with a multiple of 8 groups: the LDS-tiled kernel takes
+    the per-group parameters in windows of 8 groups per column (k splits,
+    if any, planned in whole windows); unsplit and split, ragged m and n."""
+    announce("wq g128 windows", m, k, n, weight, offset)
+    q = synth.wq_inputs(m, k, n, 5200 + m, weight=weight, group_size=128, offset=offset, bias=True, x3=m % 2 == 0)
+    check_weight_quant_matmul(orc, q)
+
+
+@pytest.mark.parametrize("weight", ["int8", "int4"])
+@pytest.mark.parametrize("offset", [True, False])
+def test_wq_identity_group128_windows(orc, weight, offset):
+    """x1 = identity [1024, 1024] with groups of 128: out must be the
+    oracle's dequantized W bit for bit, so a parameter taken from the wrong
+    slot of a window would show."""
+    announce("wq identity g128", weight, offset)
+    k, n = 1024, 80
+    q = synth.wq_inputs(k, k, n, 4300, weight=weight, group_size=128, offset=offset, bias=False)
+    q["x1"] = torch.eye(k, dtype=q["x1"].dtype)
+    d = {key: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for key, v in q.items()}
+    import int4_quantization_amd as dq
+    out = dq.weight_quant_matmul(d["x1"], d["x2"], d["scale"], d["offset"], 128, None, None, True, weight)
+    from parity import wq_oracle_args
+    x2, policy = wq_oracle_args(q)
+    W = orc.weight_dequant(x2, q["scale"], q["offset"], policy, 128, True)
+    got = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, W), f"{int((got != W).sum())} of {W.size} weights differ"
+
+
 def test_wq_split_k_deterministic():
     """Two calls give identical bits (the split sums are added in order)."""
     announce("wq split k determinism")
