@@ -306,8 +306,9 @@ dq_status dq_mx_quantize(void* workspace, size_t workspace_size, dq_executor* ex
  *   or k % 64 == 0 (I4), and x1 and x2 are 16-byte aligned; otherwise a
  *   generic kernel (one thread per output element) computes the same
  *   arithmetic much more slowly.
- *   Workspace: 0 bytes, except when the output has few tiles (small m):
- *   then k is split across workgroups and the workspace holds the binary32
+ *   Workspace: 0 bytes, except when the output has too few tiles to fill
+ *   the GPU (small m * n): then k is split across workgroups and the
+ *   workspace holds the binary32
  *   partial sums, splits * m * n * 4 bytes (16-byte aligned, owned by the
  *   caller, contents scratch).  The partial sums are added in split order,
  *   so results stay bit-reproducible.
