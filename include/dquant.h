@@ -308,10 +308,9 @@ dq_status dq_mx_quantize(void* workspace, size_t workspace_size, dq_executor* ex
  *   arithmetic much more slowly.
  *   Workspace: 0 bytes, except when the output has too few tiles to fill
  *   the GPU (small m * n): then k is split across workgroups and the
- *   workspace holds the binary32
- *   partial sums, splits * m * n * 4 bytes (16-byte aligned, owned by the
- *   caller, contents scratch).  The partial sums are added in split order,
- *   so results stay bit-reproducible.
+ *   workspace holds the binary32 partial sums, splits * m * n * 4 bytes
+ *   (16-byte aligned, owned by the caller, contents scratch).  The partial
+ *   sums are added in split order, so results stay bit-reproducible.
  * Errors: DQ_ERR_NULLPTR, DQ_ERR_DTYPE, DQ_ERR_SHAPE (ranks, shapes, k or n
  *   out of range, odd stored last dimension for I4), DQ_ERR_PARAM
  *   (group_size negative or not a multiple of 32), DQ_ERR_OVERLAP;
