@@ -344,11 +344,17 @@ __global__ __launch_bounds__(kDqWaves * kWave) void dq_vec_kernel(DqArgs a)
     const int slot = wave / TEAM;
     const int wit = wave % TEAM;
     const int64_t nvec = a.n >> 3;
-    // The workgroup converts rows r0 .. r0 + T*RPS - 1: step t of team
-    // `slot` takes row r0 + t*RPS + slot (clamped to the last row).
+    // MoE: the workgroup converts rows r0 .. r0 + T*RPS - 1 (rows are
+    // sorted by expert, so they share smooth rows): step t of team `slot`
+    // takes row r0 + t*RPS + slot.  Otherwise step t takes row group
+    // blockIdx.x + t * gridDim.x, so the resident workgroups sweep one
+    // compact band of rows at a time (measured 2.7% faster on bf16
+    // [8192, 7168] than consecutive rows per workgroup).  Rows past the end
+    // clamp to the last row, which is then written twice with equal values.
     const int64_t r0 = static_cast<int64_t>(blockIdx.x) * (T * RPS);
     auto row_of = [&](int t) -> int64_t {
-        const int64_t r = r0 + static_cast<int64_t>(t) * RPS + slot;
+        const int64_t r = a.gi ? r0 + static_cast<int64_t>(t) * RPS + slot
+                               : (static_cast<int64_t>(blockIdx.x) + static_cast<int64_t>(t) * gridDim.x) * RPS + slot;
         return r < a.rows ? r : a.rows - 1;
     };
     __shared__ float red[2][2][kDqWaves];
