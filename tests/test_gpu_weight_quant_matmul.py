@@ -121,14 +121,31 @@ def test_wq_split_k(orc, m, k, n, weight):
     check_weight_quant_matmul(orc, q)
 
 
-@pytest.mark.parametrize("m,k,n,weight,offset", [(130, 1024, 96, "int4", True), (300, 1024, 1100, "int4", True),
-                                                 (260, 4096, 136, "int4", True), (140, 2048, 256, "int8", False)])
-def test_wq_group128_windows(orc, m, k, n, weight, offset):
+@pytest.mark.parametrize("m,k,n,weight,offset,dtype", [(130, 1024, 96, "int4", True, "bfloat16"),
+                                                       (300, 1024, 1100, "int4", True, "bfloat16"),
+                                                       (260, 4096, 136, "int4", True, "bfloat16"),
+                                                       (140, 2048, 256, "int8", False, "bfloat16"),
+                                                       (150, 2048, 200, "int4", True, "float16")])
+def test_wq_group128_windows(orc, m, k, n, weight, offset, dtype):
     """Groups of 128 with a multiple of 8 groups: the LDS-tiled kernel takes
     the per-group parameters in windows of 8 groups per column (k splits,
-    if any, planned in whole windows); unsplit and split, ragged m and n."""
-    announce("wq g128 windows", m, k, n, weight, offset)
-    q = synth.wq_inputs(m, k, n, 5200 + m, weight=weight, group_size=128, offset=offset, bias=True, x3=m % 2 == 0)
+    if any, planned in whole windows); unsplit and split, ragged m and n,
+    bf16 and fp16."""
+    announce("wq g128 windows", m, k, n, weight, offset, dtype)
+    q = synth.wq_inputs(m, k, n, 5200 + m, dtype=dtype, weight=weight, group_size=128, offset=offset, bias=True,
+                        x3=m % 2 == 0)
+    check_weight_quant_matmul(orc, q)
+
+
+@pytest.mark.parametrize("m,k,n,weight,offset,dtype", [(16, 4096, 96, "int4", True, "float16"),
+                                                       (3, 2048, 200, "int4", False, "bfloat16"),
+                                                       (9, 8192, 72, "int8", True, "float16")])
+def test_wq_decode_paired_groups(orc, m, k, n, weight, offset, dtype):
+    """At most 16 rows with groups of 128 and an even group count: the decode
+    kernel loads the two parameter groups of a batch with one load."""
+    announce("wq decode paired groups", m, k, n, weight, offset, dtype)
+    q = synth.wq_inputs(m, k, n, 5300 + m, dtype=dtype, weight=weight, group_size=128, offset=offset, bias=True,
+                        x3=True)
     check_weight_quant_matmul(orc, q)
 
 
