@@ -32,6 +32,8 @@ tests use (rows x columns):
                                     per-group (128) scale and offset, bias
 * ``wq_int8_channel_bf16_4096x8192x8192``  prefill-shaped: 4096 tokens, int8
                                     weights [n, k], per-channel scale, bias
+* ``wq_int4_g128_bf16_512x8192x28672``  prefill-shaped with int4 weights and
+                                    per-group (128) scale and offset, bias
 """
 from __future__ import annotations
 
@@ -272,4 +274,7 @@ WORKLOADS = {
     "wq_int8_channel_bf16_4096x8192x8192": (
         "weight_quant_matmul",
         lambda: wq_inputs(4096, 8192, 8192, 12, weight="int8", offset=False)),
+    "wq_int4_g128_bf16_512x8192x28672": (
+        "weight_quant_matmul",
+        lambda: wq_inputs(512, 8192, 28672, 14, weight="int4", group_size=128)),
 }

@@ -188,15 +188,17 @@ def test_wq_empty_k(orc):
     check_weight_quant_matmul(orc, q)
 
 
-@pytest.mark.parametrize("name", ["wq_int4_g128_bf16_16x8192x28672", "wq_int8_channel_bf16_4096x8192x8192"])
+@pytest.mark.parametrize("name", ["wq_int4_g128_bf16_16x8192x28672", "wq_int8_channel_bf16_4096x8192x8192",
+                                  "wq_int4_g128_bf16_512x8192x28672"])
 def test_wq_full_size_sampled(orc, name):
     """The benchmark workloads: every column of a sample of rows (4 of the 16
-    decode rows; 24 rows spread over the prefill shape, including the first
-    and last), the oracle computing only those rows."""
+    decode rows; 24 rows spread over the 4096-row prefill shape and 12 over
+    the 512-row one, including the first and last), the oracle computing only
+    those rows."""
     announce("wq full size", name)
     q = synth.WORKLOADS[name][1]()
     m = q["x1"].shape[0]
-    count = 4 if m <= 16 else 24
+    count = 4 if m <= 16 else 12 if m <= 512 else 24
     rows = np.unique(np.linspace(0, m - 1, count).astype(int))
     frac = check_weight_quant_matmul(orc, q, rows=rows)
     print(f"{name}: {frac:.4f} of sampled outputs equal the once-rounded exact result", flush=True)
