@@ -53,7 +53,7 @@ namespace {
 
 constexpr int kMxBlock = 32;   // elements per scale block (gsK)
 constexpr int kMxRowVecs = 4;  // vector slots per lane in mx_row_kernel
-constexpr int kMxColRows = 8;  // rows per wave in mx_col_kernel (4 waves per 32-row block)
+constexpr int kMxColRows = 4;  // rows per wave in mx_col_kernel (8 waves per 32-row block)
 constexpr int64_t kMaxGridY = 65535;
 
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
