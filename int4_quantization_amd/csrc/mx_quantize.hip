@@ -228,8 +228,10 @@ __global__ __launch_bounds__(kBlock) void mx_row_kernel(const MxRowArgs a)
         codes.x &= keep;
         codes.y &= keep;
         if (FLAT || valid[v]) {
+            // fp4: a plain 4-byte store (measured 2.5% faster than a
+            // non-temporal one on bf16 [8192, 7168]).
             if constexpr (ELEM == MX_E2M1)
-                st_stream4(a.y + off[v] / 2, codes.x);
+                *reinterpret_cast<uint32_t*>(a.y + off[v] / 2) = codes.x;
             else
                 st_stream8(a.y + off[v], codes);
         }
