@@ -76,7 +76,8 @@ typedef enum dq_dtype {
 
 /* A dense row-major tensor in device memory.  dims[0..ndim-1] are element
  * counts; for DQ_I4 and DQ_F4E2M1 they count 4-bit codes (the buffer holds
- * half as many bytes along the last dimension). */
+ * half as many bytes along the last dimension).  A descriptor whose non-zero
+ * dims multiply to more than 2^48 is rejected with DQ_ERR_SHAPE. */
 typedef struct dq_tensor {
     void* data;
     dq_dtype dtype;

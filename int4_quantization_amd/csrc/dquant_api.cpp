@@ -70,18 +70,32 @@ const char* dtype_name(dq_dtype d)
     return "unknown";
 }
 
-// Checks ndim range and non-negative dims; returns the element count.
+// Largest element count a tensor may describe (2^48, far beyond any HBM).
+// Bounding the product of the non-zero dims keeps every element, byte and
+// row count derived from a shape inside int64, for empty tensors too.
+constexpr int64_t kMaxElems = int64_t(1) << 48;
+
+// Checks ndim range, non-negative dims and the element-count bound; returns
+// the element count.
 bool shape_ok(const dq_tensor* t, int64_t* numel)
 {
     if (t->ndim < 0 || t->ndim > DQ_MAX_DIMS)
         return false;
-    int64_t n = 1;
+    int64_t nonzero = 1;
+    bool empty = false;
     for (int i = 0; i < t->ndim; ++i) {
-        if (t->dims[i] < 0)
+        const int64_t d = t->dims[i];
+        if (d < 0)
             return false;
-        n *= t->dims[i];
+        if (d == 0) {
+            empty = true;
+            continue;
+        }
+        if (nonzero > kMaxElems / d)
+            return false;
+        nonzero *= d;
     }
-    *numel = n;
+    *numel = empty ? 0 : nonzero;
     return true;
 }
 
@@ -747,7 +761,7 @@ dq_status dq_weight_quant_matmul_get_workspace_size(const dq_tensor* x1, const d
     int policy;
     if (group_size > 0) {
         policy = DQ_PER_GROUP;
-        const int64_t G = (k + group_size - 1) / group_size;
+        const int64_t G = k > 0 ? (k - 1) / group_size + 1 : 0;  // ceil, without k + group_size overflowing
         if (!(transpose_x2 ? is_shape(antiquant_scale, {n, G}) : is_shape(antiquant_scale, {G, n})))
             return fail(DQ_ERR_SHAPE, transpose_x2 ? "per-group scale must be [n, ceil(k/gs)]"
                                                    : "per-group scale must be [ceil(k/gs), n]");
@@ -825,7 +839,7 @@ dq_status dq_weight_quant_matmul_get_workspace_size(const dq_tensor* x1, const d
     // workspace.
     p.splits = 1;
     p.k_chunk = k;
-    if (p.variant == dq::WQ_VAR_MFMA) {
+    if (p.variant == dq::WQ_VAR_MFMA && m > 0) {  // m == 0 launches nothing
         const int64_t tiles = ((n + dq::wq_tile_cols(p.tile) - 1) / dq::wq_tile_cols(p.tile)) *
                               ((m + dq::wq_tile_rows(p.tile) - 1) / dq::wq_tile_rows(p.tile));
         const int64_t batch_k = static_cast<int64_t>(dq::wq_batch(p.tile)) * dq::kWqSuperK;

@@ -1,0 +1,315 @@
+"""Property-based fuzzing of phase 1 (host-side validation) of every entry
+point, without a GPU.
+
+Each case starts from a descriptor set that validates and applies a few random
+mutations: a tensor dropped or replaced, a dtype outside or inside the enum,
+ndim outside [0, DQ_MAX_DIMS], a negative, zero or huge dimension, a NULL or
+unaligned pointer, a scalar argument out of its domain.  Whatever the input,
+phase 1 must
+
+  * return one of the status codes the header defines,
+  * hand back an executor exactly when it returns DQ_SUCCESS, and a zero
+    workspace size and a non-empty last-error message otherwise,
+  * accept only shapes whose element counts are representable (no wrapped
+    products), and
+  * give the same verdict when asked twice.
+
+No pointer is ever dereferenced by phase 1, so the fake addresses are safe.
+The examples are derandomized, so a failure reproduces on the next run."""
+import ctypes
+import os
+import math
+
+import pytest
+from hypothesis import HealthCheck, given, settings
+from hypothesis import strategies as st
+
+from int4_quantization_amd import dquant as D
+
+STATUSES = set(range(9))  # DQ_SUCCESS .. DQ_ERR_RUNTIME
+MAX_ELEMS = 1 << 48
+A = [0x1000000 * (2 * i + 1) for i in range(10)]  # far-apart fake device addresses
+
+FUZZ = settings(max_examples=300, deadline=None, derandomize=True, database=None,
+                suppress_health_check=[HealthCheck.too_slow])
+
+
+def _lib():
+    if not os.path.exists(D.library_path):
+        from int4_quantization_amd import build
+        build.build(verbose=False)
+    return D.library()
+
+
+# ---- descriptors -------------------------------------------------------------
+
+class T:
+    """A plain-Python tensor descriptor, turned into a DqTensor per call."""
+
+    def __init__(self, dtype, dims, ptr):
+        self.dtype, self.dims, self.ptr = dtype, list(dims), ptr
+        self.ndim = len(dims)
+
+    def copy(self):
+        t = T(self.dtype, self.dims, self.ptr)
+        t.ndim = self.ndim
+        return t
+
+    def to_c(self):
+        d = D.DqTensor()
+        d.data = self.ptr
+        d.dtype = self.dtype
+        d.ndim = self.ndim
+        for i in range(D.MAX_DIMS):
+            d.dims[i] = self.dims[i] if i < len(self.dims) else 0
+        return d
+
+    def representable(self):
+        if not 0 <= self.ndim <= D.MAX_DIMS:
+            return False
+        dims = self.dims[:self.ndim]
+        if any(d < 0 for d in dims):
+            return False
+        return math.prod(d for d in dims if d) <= MAX_ELEMS
+
+
+INT64 = (-(1 << 63), (1 << 63) - 1)
+dtypes = st.one_of(st.integers(D.F32, D.E8M0), st.sampled_from([-1, 10, 1 << 20]))
+dims = st.one_of(
+    st.sampled_from([0, 1, 2, 3, 4, 6, 7, 8, 16, 31, 32, 33, 64, 65, 128, 256, 65535, 65536]),
+    st.integers(0, 300),
+    st.sampled_from([-1, INT64[0], 2**31 - 1, 2**31, 2**32, 2**40, 2**47, 2**48, 2**48 + 1, 2**62, INT64[1]]),
+)
+pointers = st.sampled_from([0, 1, 2, 8, A[8], A[8] + 2, A[8] + 8, A[9], A[0] + 64, 0x7F0000000000])
+
+
+@st.composite
+def mutated(draw, base, scalars):
+    """Apply 1..3 random mutations to a copy of `base` (a dict of T / None /
+    scalars); `scalars` maps scalar argument names to strategies."""
+    args = {k: (v.copy() if isinstance(v, T) else v) for k, v in base.items()}
+    tensor_names = [k for k in base if k not in scalars]
+    for _ in range(draw(st.integers(1, 3))):
+        if draw(st.integers(0, 3)) == 0:
+            # one dimension value replaced in every tensor, so that shapes stay
+            # consistent with each other and reach the size checks
+            present = sorted({d for v in args.values() if isinstance(v, T) for d in v.dims})
+            if present:
+                old, new = draw(st.sampled_from(present)), draw(dims)
+                for v in args.values():
+                    if isinstance(v, T):
+                        v.dims = [new if d == old else d for d in v.dims]
+            continue
+        name = draw(st.sampled_from(sorted(args)))
+        if name in scalars:
+            args[name] = draw(scalars[name])
+            continue
+        t = args[name]
+        kind = draw(st.sampled_from(["none", "new", "dtype", "ndim", "dim", "ptr", "alias"]))
+        if kind == "none":
+            args[name] = None
+        elif kind == "new" or t is None:
+            shape = draw(st.lists(dims, min_size=0, max_size=D.MAX_DIMS))
+            args[name] = T(draw(dtypes), shape, draw(pointers))
+        elif kind == "dtype":
+            t.dtype = draw(dtypes)
+        elif kind == "ndim":
+            t.ndim = draw(st.integers(-2, D.MAX_DIMS + 2))
+        elif kind == "dim":
+            if not t.dims:
+                t.dims = [0]
+                t.ndim = 1
+            t.dims[draw(st.integers(0, len(t.dims) - 1))] = draw(dims)
+        elif kind == "ptr":
+            t.ptr = draw(pointers)
+        else:  # another tensor's address: overlap
+            other = args[draw(st.sampled_from(tensor_names))]
+            if other is not None:
+                t.ptr = other.ptr + draw(st.sampled_from([0, 16, 64]))
+    return args
+
+
+def check(lib, call, args, order):
+    """Call phase 1 twice with `args` in argument `order` and check the
+    properties in the module docstring.  Returns the status."""
+    c_args = []
+    keep = []
+    for k in order:
+        v = args[k]
+        if isinstance(v, T):
+            d = v.to_c()
+            keep.append(d)
+            c_args.append(ctypes.byref(d))
+        else:
+            c_args.append(v)
+    verdicts = []
+    for _ in range(2):
+        ws = ctypes.c_size_t(12345)
+        ex = ctypes.c_void_p(None)
+        status = call(*c_args, ctypes.byref(ws), ctypes.byref(ex))
+        assert status in STATUSES
+        if status == D.SUCCESS:
+            assert ex.value
+            assert ws.value < (1 << 48)
+            lib.dq_executor_destroy(ex)
+            for k in order:
+                if isinstance(args[k], T):
+                    assert args[k].representable(), (k, args[k].__dict__)
+        else:
+            assert ex.value is None
+            assert ws.value == 0
+            assert lib.dq_get_last_error().decode() != ""
+        verdicts.append((status, ws.value))
+    assert verdicts[0] == verdicts[1]
+    return verdicts[0][0]
+
+
+# ---- per-op baselines (each validates as given) ------------------------------
+
+def dq_base(kind):
+    b = dict(x=T(D.BF16, [6, 64], A[0]), sm=None, gi=None, sym=1, y=T(D.I8, [6, 64], A[1]),
+             sc=T(D.F32, [6], A[2]), off=None)
+    if kind == "moe":
+        b.update(sm=T(D.F32, [4, 64], A[3]), gi=T(D.I32, [4], A[4]))
+    elif kind == "asym":
+        b.update(sym=0, off=T(D.F32, [6], A[5]), y=T(D.I4, [6, 64], A[1]))
+    return b
+
+
+DQ_ORDER = ["x", "sm", "gi", "sym", "y", "sc", "off"]
+DQ_SCALARS = {"sym": st.sampled_from([0, 1, 2, -1])}
+
+
+def ada_base():
+    B, S, H = 2, 3, 64
+    return dict(x=T(D.BF16, [B, S, H], A[0]), sc=T(D.BF16, [B, 1, H], A[1]), sh=T(D.BF16, [B, 1, H], A[2]),
+                w=T(D.BF16, [H], A[3]), b=T(D.BF16, [H], A[4]), sm=T(D.F32, [H], A[5]), eps=1e-5,
+                out=T(D.I8, [B, S, H], A[6]), qs=T(D.F32, [B, S], A[7]))
+
+
+ADA_ORDER = ["x", "sc", "sh", "w", "b", "sm", "eps", "out", "qs"]
+ADA_SCALARS = {"eps": st.sampled_from([1e-5, 0.0, -1.0, float("nan"), float("inf"), 1e30])}
+
+
+def aq_base(kind):
+    if kind == "group":
+        # k_dim 0: groups of 128 rows, parameters [ceil(m / 128), n]
+        return dict(src=T(D.I8, [256, 64], A[0]), sc=T(D.F32, [2, 64], A[1]), off=T(D.F32, [2, 64], A[2]),
+                    pol=3, kdim=0, gs=128, dst=T(D.BF16, [256, 64], A[3]))
+    return dict(src=T(D.I8, [8, 128], A[0]), sc=T(D.F32, [1], A[1]), off=None, pol=0, kdim=-1, gs=0,
+                dst=T(D.BF16, [8, 128], A[3]))
+
+
+AQ_ORDER = ["src", "sc", "off", "pol", "kdim", "gs", "dst"]
+AQ_SCALARS = {"pol": st.integers(-1, 5), "kdim": st.integers(-2, 2),
+              "gs": st.sampled_from([0, 1, 32, 64, 100, 128, 2**31, 2**32 - 1])}
+
+
+def mx_base(kind):
+    if kind == "fp4":
+        return dict(x=T(D.BF16, [4, 64], A[0]), axis=1, y=T(D.F4E2M1, [4, 64], A[1]), s=T(D.E8M0, [4, 2], A[2]))
+    return dict(x=T(D.BF16, [4, 64], A[0]), axis=1, y=T(D.F8E4M3, [4, 64], A[1]), s=T(D.E8M0, [4, 2], A[2]))
+
+
+MX_ORDER = ["x", "axis", "y", "s"]
+MX_SCALARS = {"axis": st.integers(-2, 3)}
+
+
+def wq_base(kind):
+    m, k, n = 16, 256, 64
+    b = dict(x1=T(D.BF16, [m, k], A[0]), x2=T(D.I8, [n, k], A[1]), trans=1, sc=T(D.BF16, [n], A[2]), of=None,
+             gs=0, bias=None, x3=None, out=T(D.BF16, [m, n], A[3]))
+    if kind == "group":
+        b.update(x2=T(D.I4, [n, k], A[1]), sc=T(D.BF16, [n, 2], A[2]), of=T(D.BF16, [n, 2], A[4]), gs=128,
+                 bias=T(D.BF16, [n], A[5]), x3=T(D.BF16, [m, n], A[6]))
+    return b
+
+
+WQ_ORDER = ["x1", "x2", "trans", "sc", "of", "gs", "bias", "x3", "out"]
+WQ_SCALARS = {"trans": st.integers(-1, 2),
+              "gs": st.sampled_from([0, 32, 64, 128, 100, -32, 2**40, INT64[0], INT64[1]])}
+
+
+OPS = {
+    "dq": ("dq_dynamic_quant_get_workspace_size", DQ_ORDER, DQ_SCALARS),
+    "ada": ("dq_ada_layernorm_quant_get_workspace_size", ADA_ORDER, ADA_SCALARS),
+    "aq": ("dq_antiquantize_get_workspace_size", AQ_ORDER, AQ_SCALARS),
+    "mx": ("dq_mx_quantize_get_workspace_size", MX_ORDER, MX_SCALARS),
+    "wq": ("dq_weight_quant_matmul_get_workspace_size", WQ_ORDER, WQ_SCALARS),
+}
+
+BASES = {
+    ("dq", "plain"): dq_base("plain"), ("dq", "moe"): dq_base("moe"), ("dq", "asym"): dq_base("asym"),
+    ("ada", "plain"): ada_base(),
+    ("aq", "tensor"): aq_base("tensor"), ("aq", "group"): aq_base("group"),
+    ("mx", "fp8"): mx_base("fp8"), ("mx", "fp4"): mx_base("fp4"),
+    ("wq", "channel"): wq_base("channel"), ("wq", "group"): wq_base("group"),
+}
+
+
+@pytest.mark.parametrize("op,kind", sorted(BASES))
+def test_baseline_validates(op, kind):
+    lib = _lib()
+    name, order, _ = OPS[op]
+    assert check(lib, getattr(lib, name), BASES[(op, kind)], order) == D.SUCCESS, D.dq_get_last_error()
+
+
+def _fuzz(op, kind):
+    lib = _lib()
+    name, order, scalars = OPS[op]
+
+    @FUZZ
+    @given(args=mutated(BASES[(op, kind)], scalars))
+    def run(args):
+        check(lib, getattr(lib, name), args, order)
+
+    run()
+
+
+@pytest.mark.parametrize("op,kind", sorted(BASES))
+def test_phase1_fuzz(op, kind):
+    _fuzz(op, kind)
+
+
+def test_wrapped_element_counts_are_rejected():
+    """Dims whose product wraps int64 (2^32 * 2^32 = 2^64 -> 0) must not pass
+    as an empty tensor, nor as a small one."""
+    lib = _lib()
+    name, order, _ = OPS["dq"]
+    b = dq_base("plain")
+    b.update(x=T(D.BF16, [2**32, 2**32, 64], A[0]), y=T(D.I8, [2**32, 2**32, 64], A[1]),
+             sc=T(D.F32, [2**32, 2**32], A[2]))
+    assert check(lib, getattr(lib, name), b, order) == D.ERR_SHAPE
+    b = wq_base("channel")
+    b.update(x1=T(D.BF16, [2**40, 2**40, 0], A[0]), x2=T(D.I8, [64, 0], A[1]),
+             out=T(D.BF16, [2**40, 2**40, 64], A[3]))
+    name, order, _ = OPS["wq"]
+    assert check(lib, getattr(lib, name), b, order) == D.ERR_SHAPE
+
+
+@pytest.mark.parametrize("kind", ["channel", "group"])
+def test_wq_empty_batch_plans_without_split(kind):
+    """m = 0 on the matrix-core path: no output tiles, so the k-split planner
+    must not run (it divides by the tile count)."""
+    lib = _lib()
+    name, order, _ = OPS["wq"]
+    b = wq_base(kind)
+    b["x1"] = T(D.BF16, [0, 256], A[0])
+    b["out"] = T(D.BF16, [0, 64], A[3])
+    if b["x3"] is not None:
+        b["x3"] = T(D.BF16, [0, 64], A[6])
+    assert check(lib, getattr(lib, name), b, order) == D.SUCCESS
+
+
+def test_wq_group_size_near_int64_max():
+    """A group size that is a multiple of 32 but near 2^63 must be judged
+    against the scale's shape (one group), not overflow computing the group
+    count."""
+    lib = _lib()
+    name, order, _ = OPS["wq"]
+    b = wq_base("group")
+    b["gs"] = (1 << 63) - 32
+    assert check(lib, getattr(lib, name), b, order) == D.ERR_SHAPE  # scale is [n, 2], one group wants [n, 1]
+    b["sc"] = T(D.BF16, [64, 1], A[2])
+    b["of"] = T(D.BF16, [64, 1], A[4])
+    assert check(lib, getattr(lib, name), b, order) == D.SUCCESS

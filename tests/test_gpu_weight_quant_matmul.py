@@ -188,6 +188,15 @@ def test_wq_empty_k(orc):
     check_weight_quant_matmul(orc, q)
 
 
+@pytest.mark.parametrize("weight,gs", [("int4", 128), ("int8", 0)])
+def test_wq_empty_batch(orc, weight, gs):
+    """m = 0 (an empty batch) on the matrix-core layout: an empty output and
+    no launch."""
+    announce("wq m=0", weight)
+    q = synth.wq_inputs(0, 256, 64, 3500, weight=weight, group_size=gs, bias=True, x3=True)
+    check_weight_quant_matmul(orc, q)
+
+
 @pytest.mark.parametrize("name", ["wq_int4_g128_bf16_16x8192x28672", "wq_int8_channel_bf16_4096x8192x8192",
                                   "wq_int4_g128_bf16_512x8192x28672"])
 def test_wq_full_size_sampled(orc, name):
