@@ -72,6 +72,33 @@ def test_dynamic_quant_many_experts(orc):
     check_dynamic_quant(orc, inp["x"], inp["smooth"], gi, False, "int8")
 
 
+def _arbitrary_index(kind: str, rows: int, experts: int, seed: int) -> torch.Tensor:
+    """group_index contents the header allows but a sorted MoE batch never
+    has: the kernel must still pick the first e with row < gi[e] (the last
+    expert when there is none), as the oracle's linear scan does."""
+    rng = np.random.default_rng(seed)
+    if kind == "unsorted":
+        gi = rng.integers(-5, rows + 6, size=experts)
+    elif kind == "extremes":
+        gi = rng.choice([np.iinfo(np.int32).min, -1, 0, rows // 3, rows, np.iinfo(np.int32).max], size=experts)
+    elif kind == "all_negative":   # no row below any end: every row to the last expert
+        gi = -rng.integers(1, 1000, size=experts)
+    else:                          # "all_huge": every row to expert 0
+        gi = np.full(experts, np.iinfo(np.int32).max)
+    return torch.from_numpy(gi.astype(np.int32))
+
+
+@pytest.mark.parametrize("rows,n", [(300, 512), (37, 7168), (5, 12288), (9, 40000)])
+@pytest.mark.parametrize("experts", [5, 70])
+@pytest.mark.parametrize("kind", ["unsorted", "extremes", "all_negative", "all_huge"])
+def test_dynamic_quant_arbitrary_group_index(orc, rows, n, experts, kind):
+    announce("dynamic_quant arbitrary group_index", rows, n, experts, kind)
+    seed = rows * 31 + n + experts
+    inp = synth.dq_inputs(rows, n, seed, smooth="experts", experts=experts)
+    gi = _arbitrary_index(kind, rows, experts, seed)
+    check_dynamic_quant(orc, inp["x"], inp["smooth"], gi, experts % 2 == 1, "int8" if n % 2 else "int4")
+
+
 def _special_rows(n: int) -> torch.Tensor:
     rng = np.random.default_rng(5)
     rows = [
