@@ -30,7 +30,7 @@ struct MxPlan {
 // ---- weight-quantized matmul -------------------------------------------------
 enum WqWeight : int { WQ_I8 = 0, WQ_I4 = 1 };
 enum WqVariant : int {
-    WQ_VAR_MFMA = 0,     // weights stored [n, k], matrix cores, no LDS
+    WQ_VAR_MFMA = 0,     // weights stored [n, k], matrix cores (decode or LDS-tiled kernel)
     WQ_VAR_GENERIC = 1,  // any layout: one thread per output element
 };
 enum WqTile : int {

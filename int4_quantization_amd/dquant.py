@@ -132,6 +132,8 @@ def tensor_desc(t: Optional[torch.Tensor], dtype: Optional[int] = None,
         return None
     if not t.is_contiguous():
         raise ValueError("libdquant takes dense row-major tensors")
+    if t.numel() > 0 and not t.is_cuda:
+        raise ValueError(f"libdquant takes tensors in GPU memory, got one on {t.device}")
     d = DqTensor()
     d.data = t.data_ptr() if t.numel() > 0 else None
     d.dtype = _TORCH_CODES[t.dtype] if dtype is None else dtype
@@ -146,6 +148,16 @@ def tensor_desc(t: Optional[torch.Tensor], dtype: Optional[int] = None,
     return d
 
 
+def _one_device(*tensors) -> Optional[torch.device]:
+    """The device all non-empty tensors of one call share; raises if they
+    are spread over several (a kernel runs on one device and reads its own
+    memory)."""
+    devs = {t.device for t in tensors if t is not None and t.numel() > 0}
+    if len(devs) > 1:
+        raise ValueError(f"the tensors of one call must be on one device, got {sorted(map(str, devs))}")
+    return devs.pop() if devs else None
+
+
 def _ref(d: Optional[DqTensor]):
     return None if d is None else ctypes.byref(d)
 
@@ -156,6 +168,14 @@ def _stream_handle(stream) -> Optional[int]:
     if isinstance(stream, int):
         return stream
     return stream.cuda_stream
+
+
+def _stream_on(stream, device):
+    """The caller's stream, else the current stream of the device the
+    tensors live on (not of whichever device is current)."""
+    if stream is not None or device is None or device.type != "cuda":
+        return stream
+    return torch.cuda.current_stream(device)
 
 
 def _y_desc(y: torch.Tensor, x_shape, out_dtype: Optional[str]):
@@ -175,6 +195,7 @@ def dq_dynamic_quant_get_workspace_size(x, smooth_scales, group_index, symmetric
     """Returns (workspace_size, executor handle).  ``y`` is int8 (INT8),
     uint8 [..., N/2] (INT4) or int32 [..., N/8] (INT32)."""
     lib = library()
+    _one_device(x, smooth_scales, group_index, y, scale, offset)
     descs = [tensor_desc(x), tensor_desc(smooth_scales), tensor_desc(group_index),
              _y_desc(y, x.shape, out_dtype), tensor_desc(scale), tensor_desc(offset)]
     ws = ctypes.c_size_t(0)
@@ -193,6 +214,7 @@ def dq_dynamic_quant(workspace, workspace_size: int, executor: int, stream=None)
 def dq_ada_layernorm_quant_get_workspace_size(x, scale, shift, weight, bias, smooth_scales,
                                               epsilon: float, out, quant_scale) -> Tuple[int, int]:
     lib = library()
+    _one_device(x, scale, shift, weight, bias, smooth_scales, out, quant_scale)
     d = [tensor_desc(t) for t in (x, scale, shift, weight, bias, smooth_scales, out, quant_scale)]
     ws = ctypes.c_size_t(0)
     ex = _vp(None)
@@ -211,6 +233,7 @@ def dq_antiquantize_get_workspace_size(src, scale, offset, policy, k_dim: int, g
                                        dst) -> Tuple[int, int]:
     lib = library()
     pol = POLICIES[policy] if isinstance(policy, str) else int(policy)
+    _one_device(src, scale, offset, dst)
     d = [tensor_desc(t) for t in (src, scale, offset, dst)]
     ws = ctypes.c_size_t(0)
     ex = _vp(None)
@@ -227,6 +250,7 @@ def dq_antiquantize(workspace, workspace_size: int, executor: int, stream=None) 
 
 def dq_mx_quantize_get_workspace_size(x, axis: int, y, scale) -> Tuple[int, int]:
     lib = library()
+    _one_device(x, y, scale)
     d = [tensor_desc(t) for t in (x, y, scale)]
     ws = ctypes.c_size_t(0)
     ex = _vp(None)
@@ -252,6 +276,7 @@ def _w_desc(x2, weight: Optional[str]):
 
 
 def _wq_descs(x1, x2, antiquant_scale, antiquant_offset, bias, x3, out, weight):
+    _one_device(x1, x2, antiquant_scale, antiquant_offset, bias, x3, out)
     return [tensor_desc(x1), _w_desc(x2, weight), tensor_desc(antiquant_scale),
             tensor_desc(antiquant_offset), tensor_desc(bias), tensor_desc(x3), tensor_desc(out)]
 
@@ -281,6 +306,8 @@ def dq_executor_destroy(executor: int) -> None:
 def dq_copy_probe(dst: torch.Tensor, src: torch.Tensor, nbytes: Optional[int] = None,
                   stream=None) -> None:
     n = src.numel() * src.element_size() if nbytes is None else nbytes
+    if not (src.is_cuda and dst.is_cuda) or _one_device(dst, src) is None:
+        raise ValueError("the copy probe takes two non-empty tensors on one GPU")
     _check(library().dq_copy_probe(dst.data_ptr(), src.data_ptr(), n, _stream_handle(stream)))
 
 
@@ -336,6 +363,7 @@ class PreparedCall:
 def prepare_dynamic_quant(x, smooth_scales, group_index, symmetric, y, scale, offset,
                           out_dtype: Optional[str] = None) -> PreparedCall:
     lib = library()
+    _one_device(x, smooth_scales, group_index, y, scale, offset)
     d = [tensor_desc(x), tensor_desc(smooth_scales), tensor_desc(group_index),
          _y_desc(y, x.shape, out_dtype), tensor_desc(scale), tensor_desc(offset)]
     args = [_ref(d[0]), _ref(d[1]), _ref(d[2]), 1 if symmetric else 0, _ref(d[3]), _ref(d[4]),
@@ -347,6 +375,7 @@ def prepare_dynamic_quant(x, smooth_scales, group_index, symmetric, y, scale, of
 def prepare_ada_layernorm_quant(x, scale, shift, weight, bias, smooth_scales, epsilon, out,
                                 quant_scale) -> PreparedCall:
     lib = library()
+    _one_device(x, scale, shift, weight, bias, smooth_scales, out, quant_scale)
     d = [tensor_desc(t) for t in (x, scale, shift, weight, bias, smooth_scales, out, quant_scale)]
     args = [_ref(d[0]), _ref(d[1]), _ref(d[2]), _ref(d[3]), _ref(d[4]), _ref(d[5]),
             ctypes.c_double(float(epsilon)), _ref(d[6]), _ref(d[7])]
@@ -358,6 +387,7 @@ def prepare_antiquantize(src, scale, offset, policy, k_dim: int, group_size: int
                          dst) -> PreparedCall:
     lib = library()
     pol = POLICIES[policy] if isinstance(policy, str) else int(policy)
+    _one_device(src, scale, offset, dst)
     d = [tensor_desc(t) for t in (src, scale, offset, dst)]
     args = [_ref(d[0]), _ref(d[1]), _ref(d[2]), pol, int(k_dim), int(group_size), _ref(d[3])]
     return PreparedCall(lib.dq_antiquantize_get_workspace_size, lib.dq_antiquantize, args,
@@ -366,6 +396,7 @@ def prepare_antiquantize(src, scale, offset, policy, k_dim: int, group_size: int
 
 def prepare_mx_quantize(x, axis: int, y, scale) -> PreparedCall:
     lib = library()
+    _one_device(x, y, scale)
     d = [tensor_desc(t) for t in (x, y, scale)]
     args = [_ref(d[0]), int(axis), _ref(d[1]), _ref(d[2])]
     return PreparedCall(lib.dq_mx_quantize_get_workspace_size, lib.dq_mx_quantize, args,
@@ -406,7 +437,7 @@ def dynamic_quant(x: torch.Tensor, smooth_scales: Optional[torch.Tensor] = None,
     offset = None if symmetric else torch.empty(lead, dtype=torch.float32, device=dev)
     ws, ex = dq_dynamic_quant_get_workspace_size(x, smooth_scales, group_index, symmetric, y, scale,
                                                  offset, out_dtype)
-    dq_dynamic_quant(_workspace(ws, dev), ws, ex, stream)
+    dq_dynamic_quant(_workspace(ws, dev), ws, ex, _stream_on(stream, dev))
     return y, scale, offset
 
 
@@ -421,7 +452,7 @@ def ada_layernorm_quant(x: torch.Tensor, scale: torch.Tensor, shift: torch.Tenso
     qs = torch.empty((B, S), dtype=torch.float32, device=x.device)
     ws, ex = dq_ada_layernorm_quant_get_workspace_size(x, scale, shift, weight, bias, smooth_scales,
                                                        epsilon, out, qs)
-    dq_ada_layernorm_quant(_workspace(ws, x.device), ws, ex, stream)
+    dq_ada_layernorm_quant(_workspace(ws, x.device), ws, ex, _stream_on(stream, x.device))
     return out, qs
 
 
@@ -437,7 +468,7 @@ def antiquantize(src: torch.Tensor, scale: torch.Tensor, offset: Optional[torch.
         shape[-1] *= 2
     dst = torch.empty(shape, dtype=dst_dtype, device=src.device)
     ws, ex = dq_antiquantize_get_workspace_size(src, scale, offset, policy, k_dim, group_size, dst)
-    dq_antiquantize(_workspace(ws, src.device), ws, ex, stream)
+    dq_antiquantize(_workspace(ws, src.device), ws, ex, _stream_on(stream, src.device))
     return dst
 
 
@@ -461,7 +492,7 @@ def mx_quantize(x: torch.Tensor, elem: torch.dtype = torch.float8_e4m3fn, axis: 
     scale = torch.empty(mx_scale_shape(rows, n, axis), dtype=torch.uint8,
                         device=x.device).view(torch.float8_e8m0fnu)
     ws, ex = dq_mx_quantize_get_workspace_size(x, axis, y, scale)
-    dq_mx_quantize(_workspace(ws, x.device), ws, ex, stream)
+    dq_mx_quantize(_workspace(ws, x.device), ws, ex, _stream_on(stream, x.device))
     return y, scale
 
 
@@ -478,5 +509,5 @@ def weight_quant_matmul(x1: torch.Tensor, x2: torch.Tensor, antiquant_scale: tor
     ws, ex = dq_weight_quant_matmul_get_workspace_size(x1, x2, transpose_x2, antiquant_scale,
                                                        antiquant_offset, group_size, bias, x3, out,
                                                        weight)
-    dq_weight_quant_matmul(_workspace(ws, x1.device), ws, ex, stream)
+    dq_weight_quant_matmul(_workspace(ws, x1.device), ws, ex, _stream_on(stream, x1.device))
     return out

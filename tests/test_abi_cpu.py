@@ -459,9 +459,34 @@ def test_copy_probe_validation(lib):
 
 
 def test_python_binding_raises_without_gpu_launch(lib):
-    x = torch.zeros(4, 7, dtype=torch.bfloat16)
+    # empty tensors: no pointer, so the binding passes them on from the host
+    x = torch.zeros(0, 7, dtype=torch.bfloat16)
     with pytest.raises(D.DquantError) as e:
-        D.dq_dynamic_quant_get_workspace_size(x, None, None, True, torch.zeros(4, 3, dtype=torch.uint8),
-                                              torch.zeros(4), None, "int4")
+        D.dq_dynamic_quant_get_workspace_size(x, None, None, True, torch.zeros(0, 3, dtype=torch.uint8),
+                                              torch.zeros(0), None, "int4")
     assert e.value.status == D.ERR_SHAPE
     assert "even" in str(e.value)
+
+
+def test_binding_rejects_host_tensors(lib):
+    """Host memory never reaches a kernel: the binding refuses CPU tensors
+    (empty ones carry no pointer and pass) before any C call."""
+    import int4_quantization_amd as dq
+    x = torch.randn(4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU memory"):
+        dq.dynamic_quant(x)
+    with pytest.raises(ValueError, match="GPU memory"):
+        dq.mx_quantize(x)
+    with pytest.raises(ValueError, match="GPU memory"):
+        dq.antiquantize(torch.zeros(4, 64, dtype=torch.int8), torch.ones(1))
+    with pytest.raises(ValueError, match="GPU memory"):
+        dq.weight_quant_matmul(x, torch.zeros(32, 64, dtype=torch.int8), torch.ones(32, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="on one GPU"):
+        D.dq_copy_probe(torch.empty(16, dtype=torch.uint8), torch.empty(16, dtype=torch.uint8))
+    assert D.tensor_desc(torch.empty(0, 64)).data is None
+
+
+def test_binding_rejects_mixed_devices():
+    with pytest.raises(ValueError, match="one device"):
+        D._one_device(torch.empty(2, device="meta"), torch.empty(2))
+    assert D._one_device(torch.empty(0), None, torch.empty(3)) == torch.device("cpu")
