@@ -313,3 +313,49 @@ def test_wq_group_size_near_int64_max():
     b["sc"] = T(D.BF16, [64, 1], A[2])
     b["of"] = T(D.BF16, [64, 1], A[4])
     assert check(lib, getattr(lib, name), b, order) == D.SUCCESS
+
+
+def test_last_error_is_per_thread():
+    """Threads failing phase 1 for different reasons each read their own
+    message (the header promises a per-thread last error).  ctypes releases
+    the GIL around foreign calls, so the threads overlap inside the
+    library."""
+    import threading
+    lib = _lib()
+    name, order, _ = OPS["dq"]
+    call = getattr(lib, name)
+    cases = []
+    for reason, change, expect in [
+        ("dtype", {"x": T(D.F32, [6, 64], A[0])}, "x must be F16 or BF16"),
+        ("shape", {"sc": T(D.F32, [7], A[2])}, "scale"),
+        ("null", {"y": None}, "y is NULL"),
+        ("ok", {}, ""),
+    ]:
+        b = dq_base("plain")
+        b.update(change)
+        cases.append((reason, b, expect))
+    errors = []
+
+    def worker(reason, args, expect):
+        descs = [args[k].to_c() if isinstance(args[k], T) else args[k] for k in order]
+        c_args = [ctypes.byref(d) if isinstance(d, D.DqTensor) else d for d in descs]
+        for _ in range(2000):
+            ws, ex = ctypes.c_size_t(0), ctypes.c_void_p(None)
+            st = call(*c_args, ctypes.byref(ws), ctypes.byref(ex))
+            if st == D.SUCCESS:
+                lib.dq_executor_destroy(ex)
+                if reason != "ok":
+                    errors.append((reason, "unexpected success"))
+                    return
+                continue
+            msg = lib.dq_get_last_error().decode()
+            if reason == "ok" or expect not in msg:
+                errors.append((reason, msg))
+                return
+
+    threads = [threading.Thread(target=worker, args=c) for c in cases for _ in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors[:4]
