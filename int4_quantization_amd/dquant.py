@@ -323,6 +323,18 @@ def _workspace(size: int, device) -> Optional[torch.Tensor]:
     return torch.empty(size, dtype=torch.uint8, device=device) if size > 0 else None
 
 
+def _release_after(workspace: Optional[torch.Tensor], stream) -> None:
+    """A workspace dropped on return goes back to torch's caching allocator,
+    which may hand it out again on the stream it was allocated on while the
+    kernel that uses it still runs on `stream`: record that stream on it so
+    the memory is reused only after the work queued there so far."""
+    if workspace is None or stream is None:
+        return
+    if isinstance(stream, int):
+        stream = torch.cuda.ExternalStream(stream, device=workspace.device)
+    workspace.record_stream(stream)
+
+
 # -- prepared calls: descriptors built once, both phases per call ---------------
 
 class PreparedCall:
@@ -330,7 +342,8 @@ class PreparedCall:
     built once, so each call is the get-workspace-size call plus the execute
     call (two C calls, no per-call Python marshalling of tensors).  A
     workspace, when the op asks for one, is allocated on the first call and
-    reused while it is large enough."""
+    reused while it is large enough, so calls of one PreparedCall on
+    different streams must be ordered by the caller."""
 
     def __init__(self, phase1, execute, args, keep, device=None):
         self._phase1 = phase1
@@ -437,7 +450,10 @@ def dynamic_quant(x: torch.Tensor, smooth_scales: Optional[torch.Tensor] = None,
     offset = None if symmetric else torch.empty(lead, dtype=torch.float32, device=dev)
     ws, ex = dq_dynamic_quant_get_workspace_size(x, smooth_scales, group_index, symmetric, y, scale,
                                                  offset, out_dtype)
-    dq_dynamic_quant(_workspace(ws, dev), ws, ex, _stream_on(stream, dev))
+    s = _stream_on(stream, dev)
+    w = _workspace(ws, dev)
+    dq_dynamic_quant(w, ws, ex, s)
+    _release_after(w, s)
     return y, scale, offset
 
 
@@ -452,7 +468,10 @@ def ada_layernorm_quant(x: torch.Tensor, scale: torch.Tensor, shift: torch.Tenso
     qs = torch.empty((B, S), dtype=torch.float32, device=x.device)
     ws, ex = dq_ada_layernorm_quant_get_workspace_size(x, scale, shift, weight, bias, smooth_scales,
                                                        epsilon, out, qs)
-    dq_ada_layernorm_quant(_workspace(ws, x.device), ws, ex, _stream_on(stream, x.device))
+    s = _stream_on(stream, x.device)
+    w = _workspace(ws, x.device)
+    dq_ada_layernorm_quant(w, ws, ex, s)
+    _release_after(w, s)
     return out, qs
 
 
@@ -468,7 +487,10 @@ def antiquantize(src: torch.Tensor, scale: torch.Tensor, offset: Optional[torch.
         shape[-1] *= 2
     dst = torch.empty(shape, dtype=dst_dtype, device=src.device)
     ws, ex = dq_antiquantize_get_workspace_size(src, scale, offset, policy, k_dim, group_size, dst)
-    dq_antiquantize(_workspace(ws, src.device), ws, ex, _stream_on(stream, src.device))
+    s = _stream_on(stream, src.device)
+    w = _workspace(ws, src.device)
+    dq_antiquantize(w, ws, ex, s)
+    _release_after(w, s)
     return dst
 
 
@@ -492,7 +514,10 @@ def mx_quantize(x: torch.Tensor, elem: torch.dtype = torch.float8_e4m3fn, axis: 
     scale = torch.empty(mx_scale_shape(rows, n, axis), dtype=torch.uint8,
                         device=x.device).view(torch.float8_e8m0fnu)
     ws, ex = dq_mx_quantize_get_workspace_size(x, axis, y, scale)
-    dq_mx_quantize(_workspace(ws, x.device), ws, ex, _stream_on(stream, x.device))
+    s = _stream_on(stream, x.device)
+    w = _workspace(ws, x.device)
+    dq_mx_quantize(w, ws, ex, s)
+    _release_after(w, s)
     return y, scale
 
 
@@ -509,5 +534,8 @@ def weight_quant_matmul(x1: torch.Tensor, x2: torch.Tensor, antiquant_scale: tor
     ws, ex = dq_weight_quant_matmul_get_workspace_size(x1, x2, transpose_x2, antiquant_scale,
                                                        antiquant_offset, group_size, bias, x3, out,
                                                        weight)
-    dq_weight_quant_matmul(_workspace(ws, x1.device), ws, ex, _stream_on(stream, x1.device))
+    s = _stream_on(stream, x1.device)
+    w = _workspace(ws, x1.device)
+    dq_weight_quant_matmul(w, ws, ex, s)
+    _release_after(w, s)
     return out
