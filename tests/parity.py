@@ -193,9 +193,10 @@ def check_weight_quant_matmul(orc, q, rows=None, dev=None):
     x2, policy = wq_oracle_args(q)
     ref, mag, _ = orc.weight_quant_matmul(x1, x2, q["scale"], q["offset"], policy, q["group_size"],
                                           q["transpose_x2"], q["bias"], x3)
-    g = out.reshape(m_all, n).float().cpu().numpy().astype(np.float64)
-    if rows is not None:
-        g = g[rows]
+    sel = out.reshape(m_all, n)
+    if rows is not None:  # select on the device: the whole output may be many GB
+        sel = sel[torch.as_tensor(np.asarray(rows), device=out.device)]
+    g = sel.float().cpu().numpy().astype(np.float64)
     tname = "bfloat16" if q["x1"].dtype == torch.bfloat16 else "float16"
     gamma = (k + 2) * 2.0 ** -24 / (1 - (k + 2) * 2.0 ** -24)
     extra = np.zeros_like(ref)
@@ -210,9 +211,7 @@ def check_weight_quant_matmul(orc, q, rows=None, dev=None):
     assert not bad.any(), f"{bad.sum()} elements beyond the bound; worst err {err.max():.3g}, bound there " \
                           f"{bound.reshape(-1)[np.argmax(err)]:.3g}"
     rounded = orc.f64_to_half(ref, tname)
-    gb = out.reshape(m_all, n).view(torch.int16).cpu().numpy().view(np.uint16)
-    if rows is not None:
-        gb = gb[rows]
+    gb = sel.view(torch.int16).cpu().numpy().view(np.uint16)
     frac = float(np.mean(gb == rounded)) if gb.size else 1.0
     assert frac >= 0.9, f"only {frac:.3f} of the elements equal the once-rounded exact result"
     return frac
