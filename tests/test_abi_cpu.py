@@ -490,3 +490,15 @@ def test_binding_rejects_mixed_devices():
     with pytest.raises(ValueError, match="one device"):
         D._one_device(torch.empty(2, device="meta"), torch.empty(2))
     assert D._one_device(torch.empty(0), None, torch.empty(3)) == torch.device("cpu")
+
+
+def test_binding_rejects_strided_tensors():
+    """Descriptors describe dense row-major memory only: a transposed or
+    sliced view raises before any C call instead of being read as if
+    dense."""
+    base = torch.zeros(8, 64, dtype=torch.bfloat16)
+    for view in (base.t(), base[:, ::2], base[:, 1:]):
+        with pytest.raises(ValueError, match="dense row-major"):
+            D.tensor_desc(view)
+    with pytest.raises(ValueError, match="GPU memory"):  # a row slice is dense: only its memory is refused
+        D.tensor_desc(base[2:5])
