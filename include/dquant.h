@@ -118,10 +118,11 @@ typedef enum dq_antiquant_policy {
  *   group_index   NULL, or I32 [E] (E >= 1) holding cumulative per-expert
  *                 row ends: expert e owns rows [gi[e-1], gi[e]); the owner
  *                 of row r is the first e with r < gi[e], and rows at or
- *                 past gi[E-1] belong to expert E-1 ("In the MOE scenario,
- *                 smoothScalesOptional for each expert is different and is
- *                 distinguished by groupIndexOptional").  Requires
- *                 smooth_scales.  Its device contents are not validated.
+ *                 past gi[E-1] belong to expert E-1.  (aclnnDynamicQuantV2,
+ *                 Description: in the MoE case every expert has its own
+ *                 smooth-scale row, and the group index tells which rows
+ *                 use which.)  Requires smooth_scales.  Its device contents
+ *                 are not validated.
  *   symmetric     nonzero: symmetric; 0: asymmetric.
  *   y             output.  DQ_I8 [..., N]; DQ_I4 [..., N] with N even
  *                 (N/2 bytes per row); DQ_I32 [..., N/8] with N % 8 == 0

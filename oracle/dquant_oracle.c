@@ -36,6 +36,14 @@
  *
  * Readings taken where the pages are silent or garbled are stated next to
  * the step that depends on them.
+ *
+ * Pinning: every function here is checked by tests/oracle_pins.py against
+ * values fixed independently of this file (hand-worked rows, the pages'
+ * worked example, closed forms, invariants, and numpy float32 / torch
+ * evaluations of each formula), and tests/test_oracle_mutants.py shows that
+ * planted mistakes fail those checks.  What no page value fixes is the sign
+ * convention of the AntiQuantize offset: that is a reading (stated at
+ * oracle_antiquantize), and its parity is unpinned by the pages.
  */
 #include <math.h>
 #include <stddef.h>

@@ -252,6 +252,181 @@ def pin_dq_leading_dims(orc):
     assert np.array_equal(a[1].reshape(15), b[1]) and np.array_equal(a[2].reshape(15), b[2])
 
 
+
+# ---------------------------------------------------------------------------
+# aclnnDynamicQuantV2 -- the whole formula against numpy float32 (Formula)
+#
+# numpy evaluates every step as one IEEE binary32 operation (np.float32
+# `*`, `/`, `+`, `-` round to nearest even) and np.rint rounds half to
+# even, so it is an independent, vectorized statement of the Formula.  The
+# rows are built so that division and reciprocal multiplication disagree:
+# x is +-1 and the smooth scales carry arbitrary binary32 magnitudes, placed
+# within a few ulps of the points where a quotient crosses k + 1/2.  Each
+# pin first checks, in numpy, that its inputs tell RN(v / scale) apart from
+# RN(v * RN(1 / scale)), and only then compares the oracle.
+# ---------------------------------------------------------------------------
+
+_DQ_CONST = {"int8": (255.0, 127.0, -128, 127), "int4": (15.0, 7.0, -8, 7)}
+
+
+def _ulp_walk(center: np.ndarray, steps) -> np.ndarray:
+    """Positive binary32 values `d` ulps from each center, for d in steps."""
+    bits = np.abs(center.astype(f32)).view(np.int32).astype(np.int64)
+    out = [(bits + d).astype(np.int32).view(f32) for d in steps]
+    return np.concatenate(out)
+
+
+def _np_dq(x, smooth, owner, symmetric, out, recip=False):
+    """numpy float32 statement of the Formula for rows x (torch bf16/fp16),
+    smooth rows `smooth[owner[r]]` (or none).  `recip` swaps every division
+    by the row scale for a multiplication by RN(1 / scale) -- used only to
+    show that an input discriminates."""
+    opt_s, opt_o, lo, hi = (f32(v) for v in _DQ_CONST[out])
+    with np.errstate(all="ignore"):
+        v = x.float().numpy().astype(f32)
+        if smooth is not None:
+            v = (v * smooth[owner]).astype(f32)
+        div = (lambda a, b: a * (f32(1) / b)) if recip else (lambda a, b: a / b)
+        if symmetric:
+            sc = np.abs(v).max(axis=1) / opt_o
+            t = div(v, sc[:, None])
+            off = None
+        else:
+            vmax, vmin = v.max(axis=1), v.min(axis=1)
+            sc = (vmax - vmin) / opt_s
+            off = opt_o - div(vmax, sc)
+            t = div(v, sc[:, None]) + off[:, None]
+        t = np.where(np.isnan(t), f32(0), t)
+        c = np.clip(np.rint(t), lo, hi).astype(np.int64)
+    return c, sc.astype(f32), None if off is None else off.astype(f32)
+
+
+def _codes_of(y, out):
+    return y.astype(np.int64) if out == "int8" else _unpack_int4(y)
+
+
+def _sym_row_magnitudes(rng, n, out):
+    """|v| of one symmetric row: an absmax A and values around (k + 1/2) *
+    RN(A / D) for every code step k."""
+    _, D, _, top = _DQ_CONST[out]
+    A = f32(rng.uniform(1.0, 2.0) * 2.0 ** rng.integers(-20, 20))
+    sc = A / f32(D)
+    k = np.arange(top, dtype=np.float64)
+    near = _ulp_walk((k + 0.5) * np.float64(sc), range(-3, 4))
+    near = near[near < A]
+    row = np.concatenate([[A], near, rng.uniform(0, 1, n).astype(f32) * A])[:n]
+    return rng.permutation(row).astype(f32)
+
+
+def _asym_row_magnitudes(rng, n, out):
+    """Signed v of one asymmetric row: max hi, min lo and values around
+    the points where RN(v / scale) + offset crosses k + 1/2."""
+    opt_s, opt_o, lo_c, hi_c = _DQ_CONST[out]
+    hi = f32(rng.uniform(1.0, 2.0) * 2.0 ** rng.integers(-12, 12))
+    lo = f32(-hi * rng.uniform(0.3, 3.0))
+    sc = (hi - lo) / f32(opt_s)
+    off = f32(opt_o) - hi / sc
+    k = np.arange(lo_c, hi_c, dtype=np.float64)
+    centers = (k + 0.5 - np.float64(off)) * np.float64(sc)
+    near = np.concatenate([np.sign(c) * _ulp_walk(np.array([c]), range(-3, 4)) for c in centers])
+    near = near[(near > lo) & (near < hi)].astype(f32)
+    row = np.concatenate([[hi, lo], near, rng.uniform(lo, hi, n).astype(f32)])[:n]
+    return rng.permutation(row).astype(f32)
+
+
+def _signed_inputs(v: np.ndarray):
+    """x = sign(v) as bf16 and smooth = |v| (x * smooth = v exactly)."""
+    x = torch.from_numpy(np.where(v < 0, -1.0, 1.0).astype(np.float32)).to(torch.bfloat16)
+    return x, np.abs(v).astype(f32)
+
+
+def pin_dq_matches_numpy_float32(orc):
+    """Symmetric and asymmetric, INT8 and INT4, with a smooth vector: codes,
+    scale and offset equal numpy's binary32 evaluation bit for bit, on rows
+    where true division and reciprocal multiplication disagree."""
+    rng = np.random.default_rng(17)
+    R, N = 24, 1024
+    for out in ("int8", "int4"):
+        for sym in (True, False):
+            build = _sym_row_magnitudes if sym else _asym_row_magnitudes
+            v = np.stack([build(rng, N, out) for _ in range(R)])
+            if sym:
+                v = v * np.where(rng.random(v.shape) < 0.5, f32(-1), f32(1))
+            # Each row has its own smooth row: R experts, one row each.
+            x, sm = _signed_inputs(v)
+            gi = np.arange(1, R + 1, dtype=np.int32)
+            owner = np.arange(R)
+            want = _np_dq(x, sm, owner, sym, out)
+            alt = _np_dq(x, sm, owner, sym, out, recip=True)
+            assert not np.array_equal(want[0], alt[0]), "inputs must tell division from reciprocal"
+            y, s, o = orc.dynamic_quant(x, smooth=sm, group_index=gi, symmetric=sym, out=out)
+            assert np.array_equal(_codes_of(y, out), want[0]), (out, sym)
+            assert np.array_equal(s.view(np.uint32), want[1].view(np.uint32)), (out, sym)
+            if not sym:
+                assert np.array_equal(o.view(np.uint32), want[2].view(np.uint32)), (out, sym)
+
+
+def pin_dq_scale_is_true_quotient(orc):
+    """scale = RN(row_max|in| / 127) and RN(RN(max - min) / 255) (7 and 15
+    for INT4) are true binary32 quotients: on rows where the quotient and
+    the reciprocal product RN(a * RN(1 / D)) differ, the oracle's scale
+    equals the quotient."""
+    rng = np.random.default_rng(18)
+    K = 64
+    gi = np.arange(1, K + 1, dtype=np.int32)
+    for out in ("int8", "int4"):
+        opt_s, opt_o, _, _ = _DQ_CONST[out]
+        A = (rng.uniform(1.0, 2.0, 200000) * 2.0 ** rng.integers(-30, 30, 200000)).astype(f32)
+        A = A[(A / f32(opt_o)) != A * (f32(1) / f32(opt_o))][:K]
+        assert A.size == K
+        row = np.repeat(A[:, None] * f32(0.25), 8, axis=1)
+        row[:, 0] = A
+        x, sm = _signed_inputs(row)
+        _, s, _ = orc.dynamic_quant(x, smooth=sm, group_index=gi, out=out)
+        assert np.array_equal(s.view(np.uint32), (A / f32(opt_o)).view(np.uint32)), out
+        # Asymmetric: max hi and min lo, with RN(hi - lo) / scale_opt discriminating.
+        hi = (rng.uniform(1.0, 2.0, 200000) * 2.0 ** rng.integers(-30, 30, 200000)).astype(f32)
+        lo = (-hi * rng.uniform(0.1, 2.0, 200000)).astype(f32)
+        rg = (hi - lo).astype(f32)
+        keep = (rg / f32(opt_s)) != rg * (f32(1) / f32(opt_s))
+        hi, lo, rg = hi[keep][:K], lo[keep][:K], rg[keep][:K]
+        assert hi.size == K
+        row = np.repeat(((hi + lo) * f32(0.5))[:, None], 8, axis=1).astype(f32)
+        row[:, 0], row[:, 1] = hi, lo
+        x, sm = _signed_inputs(row)
+        _, s, o = orc.dynamic_quant(x, smooth=sm, group_index=gi, symmetric=False, out=out)
+        assert np.array_equal(s.view(np.uint32), (rg / f32(opt_s)).view(np.uint32)), out
+        want = _np_dq(x, sm, np.arange(K), False, out)
+        assert np.array_equal(o.view(np.uint32), want[2].view(np.uint32)), out
+
+
+def pin_dq_natural_rows_match_numpy(orc):
+    """Random bf16 and fp16 rows with 0.1 % outliers, without smooth, with a
+    smooth vector and with MoE expert rows (an empty expert, rows past the
+    last bound): every output equals numpy's binary32 evaluation, with the
+    owner of row r taken as numpy's searchsorted over the row ends."""
+    rng = np.random.default_rng(19)
+    R, N, E = 40, 320, 6
+    for dtype in (torch.bfloat16, torch.float16):
+        xf = rng.standard_normal((R, N)).astype(f32)
+        pos = rng.choice(R * N, 13, replace=False)
+        xf.reshape(-1)[pos] = rng.uniform(20, 60, 13).astype(f32) * np.where(rng.random(13) < 0.5, -1, 1)
+        x = torch.from_numpy(xf).to(dtype)
+        sm_e = rng.uniform(0.5, 2.0, (E, N)).astype(f32)
+        gi = np.array([5, 5, 12, 20, 31, 36], np.int32)  # expert 1 empty; rows 36..39 past the end
+        owner = np.minimum(np.searchsorted(gi, np.arange(R), side="right"), E - 1)
+        for out in ("int8", "int4"):
+            for sym in (True, False):
+                for smooth, g, own in ((None, None, None), (sm_e[3], None, np.zeros(R, np.int64)),
+                                       (sm_e, gi, owner)):
+                    sm_rows = None if smooth is None else (smooth if smooth.ndim == 2 else smooth[None])
+                    want = _np_dq(x, sm_rows, own, sym, out)
+                    y, s, o = orc.dynamic_quant(x, smooth=smooth, group_index=g, symmetric=sym, out=out)
+                    assert np.array_equal(_codes_of(y, out), want[0]), (dtype, out, sym)
+                    assert np.array_equal(s.view(np.uint32), want[1].view(np.uint32))
+                    if not sym:
+                        assert np.array_equal(o.view(np.uint32), want[2].view(np.uint32))
+
 # ---------------------------------------------------------------------------
 # aclnnAdaLayerNormQuant
 # ---------------------------------------------------------------------------
@@ -361,6 +536,92 @@ def pin_ada_absmax_code(orc):
     assert np.all(err <= qs[..., None] * (0.5 + 2.0 ** -16))
 
 
+
+def _discriminating_absmax(rng, D):
+    """A binary32 A with RN(A / D) != RN(A * RN(1 / D))."""
+    while True:
+        A = (rng.uniform(1.0, 2.0, 4096) * 2.0 ** rng.integers(-20, 20, 4096)).astype(f32)
+        A = A[(A / f32(D)) != A * (f32(1) / f32(D))]
+        if A.size:
+            return A[0]
+
+
+def pin_ada_quant_steps_match_numpy_float32(orc):
+    """Steps 4-5 in binary32 (R14: y rounded once to binary32, then
+    quantScale = RN(max|y| / 127) and out = rne(RN(y / quantScale))) against
+    numpy float32.  With scale = -1 the LayerNorm term vanishes and
+    y = shift * smooth exactly in binary64, so y can be placed at will:
+      - shift = +-1: y is the binary32 smooth value; the row maximum makes
+        RN(A / 127) differ from A * RN(1 / 127), and the other values sit
+        within a few ulps of the points where y / quantScale crosses k + 1/2,
+        where division and reciprocal multiplication disagree;
+      - shift = +-1.5: y = 1.5 * smooth needs 25 bits, and the values are
+        chosen where rounding y to binary32 first moves the quotient across
+        k + 1/2, so deciding the code from the binary64 y would differ.
+    Then random rows through the whole formula, steps 4-5 applied by numpy
+    to the oracle's binary64 y (steps 1-3 are pinned against torch)."""
+    rng = np.random.default_rng(25)
+    B, S, H = 3, 2, 1024
+    A = _discriminating_absmax(rng, 127.0)
+    sc32 = A / f32(127)
+    k = np.arange(127, dtype=np.float64)
+    near = _ulp_walk((k + 0.5) * np.float64(sc32), range(-3, 4))
+    near = near[near < A]
+    mags = rng.permutation(np.concatenate([[A], near, rng.uniform(0, 1, H).astype(f32) * A])[:H]).astype(f32)
+    signs = np.where(rng.random((B, 1, H)) < 0.5, -1.0, 1.0).astype(np.float32)
+    sh = torch.from_numpy(signs).to(torch.bfloat16)
+    minus = -torch.ones(B, 1, H, dtype=torch.bfloat16)
+    x = _rand_bf16(rng, (B, S, H))
+    out, qs = orc.ada_layernorm_quant(x, minus, sh, None, None, mags)
+    y32 = (signs * mags).astype(f32)  # exact: +-1 times a binary32
+    want_qs = np.abs(y32).max(axis=2) / f32(127)
+    assert not np.array_equal(want_qs, (np.abs(y32).max(axis=2) * (f32(1) / f32(127))).astype(f32))
+    with np.errstate(all="ignore"):
+        want = np.clip(np.rint(y32 / want_qs[..., None]), -128, 127)
+        alt = np.clip(np.rint(y32 * (f32(1) / want_qs[..., None])), -128, 127)
+    assert not np.array_equal(want, alt), "inputs must tell division from reciprocal"
+    for s in range(S):
+        assert np.array_equal(out[:, s, :].astype(np.int64), want[:, 0, :].astype(np.int64))
+        assert np.array_equal(qs[:, s].view(np.uint32), want_qs[:, 0].view(np.uint32))
+    # shift = +-1.5: the binary32 rounding of y decides codes.
+    A = f32(rng.uniform(1.0, 2.0) * 2.0 ** 3)
+    q32 = (f32(1.5) * A).astype(f32) / f32(127)  # RN(RN(1.5 A) / 127), the quantScale
+    cand = []
+    for kk in range(127):
+        c = (kk + 0.5) * np.float64(q32) / 1.5
+        for d in range(-40, 41):
+            sm = _ulp_walk(np.array([c]), [d])[0]
+            y64 = 1.5 * np.float64(sm)
+            y32 = np.float32(y64)
+            if y64 < 1.5 * np.float64(A) and np.rint(np.float64(y32 / q32)) != np.rint(y64 / np.float64(q32)):
+                cand.append(sm)
+    assert len(cand) > 0
+    mags = np.concatenate([[A], np.array(cand, f32), rng.uniform(0, 1, H).astype(f32) * A])[:H].astype(f32)
+    mags = rng.permutation(mags)
+    signs = np.where(rng.random((1, 1, H)) < 0.5, -1.5, 1.5).astype(np.float32)
+    sh = torch.from_numpy(signs).to(torch.bfloat16)
+    out, qs = orc.ada_layernorm_quant(x[:1], -torch.ones(1, 1, H, dtype=torch.bfloat16), sh, None, None, mags)
+    y64 = signs.astype(np.float64) * mags.astype(np.float64)
+    y32 = y64.astype(f32)
+    want_qs = np.abs(y32).max(axis=2) / f32(127)
+    want = np.clip(np.rint(y32 / want_qs[..., None]), -128, 127).astype(np.int64)
+    wide = np.clip(np.rint(y64 / want_qs[..., None].astype(np.float64)), -128, 127).astype(np.int64)
+    assert not np.array_equal(want, wide), "inputs must tell a binary32 decision from a binary64 one"
+    for s in range(S):
+        assert np.array_equal(out[:, s, :].astype(np.int64), want[:, 0, :])
+        assert np.array_equal(qs[:, s].view(np.uint32), want_qs[:, 0].view(np.uint32))
+    # Random rows, every optional tensor present.
+    B, S, H = 2, 6, 320
+    x = _rand_bf16(rng, (B, S, H))
+    sc, sh, w, b = _ada_params(rng, B, H)
+    sm = rng.uniform(0.5, 2.0, H).astype(f32)
+    out, qs, y = orc.ada_layernorm_quant(x, sc, sh, w, b, sm, want_y=True)
+    y32 = y.astype(f32)
+    want_qs = np.abs(y32).max(axis=2) / f32(127)
+    want = np.clip(np.rint(y32 / want_qs[..., None]), -128, 127).astype(np.int64)
+    assert np.array_equal(out.astype(np.int64), want)
+    assert np.array_equal(qs.view(np.uint32), want_qs.view(np.uint32))
+
 # ---------------------------------------------------------------------------
 # AntiQuantize
 # ---------------------------------------------------------------------------
@@ -468,6 +729,77 @@ def pin_aq_fp8_source(orc):
     nan = np.isnan(ref)
     assert np.array_equal(np.isnan(d), nan)
     assert np.array_equal(d[~nan], ref[~nan])
+
+
+def _np_aq_params(policy, m, n, kdim, gs, s, o):
+    """Broadcast a parameter tensor of the policy's shape to [m, n]."""
+    if policy == "per_tensor":
+        return np.full((m, n), s.reshape(-1)[0]), None if o is None else np.full((m, n), o.reshape(-1)[0])
+    if policy == "per_channel":
+        idx = (np.zeros((m, n), np.int64), np.broadcast_to(np.arange(n), (m, n)))
+    elif policy == "per_token":
+        idx = (np.broadcast_to(np.arange(m)[:, None], (m, n)), np.zeros((m, n), np.int64))
+    elif kdim == 1:
+        idx = (np.broadcast_to(np.arange(m)[:, None], (m, n)), np.broadcast_to(np.arange(n) // gs, (m, n)))
+    else:
+        idx = (np.broadcast_to((np.arange(m) // gs)[:, None], (m, n)), np.broadcast_to(np.arange(n), (m, n)))
+    return s[idx], None if o is None else o[idx]
+
+
+def pin_aq_matches_numpy_float32(orc):
+    """Every policy (per-tensor, per-channel, per-token, per-group along n
+    and along m with a short last group), int8 / e4m3fn / e5m2 sources,
+    fp32 / fp16 / bf16 parameters, with and without offset: dst equals
+    numpy's binary32 (v + o) * s (or v * s), rounded once by torch's bf16
+    cast or numpy's fp16 cast, or kept in fp32.  The scales are not powers
+    of two, and the inputs are checked to tell (v + o) * s apart from
+    v * s + o * s and from a fused multiply-add."""
+    rng = np.random.default_rng(33)
+    m, n, gs = 70, 96, 32
+    srcs = {
+        "int8": rng.integers(-128, 128, (m, n)).astype(np.int8),
+        "float8_e4m3fn": torch.from_numpy(np.clip(rng.normal(0, 4, (m, n)), -448, 448).astype(np.float32))
+                             .to(torch.float8_e4m3fn),
+        "float8_e5m2": torch.from_numpy(np.clip(rng.normal(0, 4, (m, n)), -57344, 57344).astype(np.float32))
+                           .to(torch.float8_e5m2),
+    }
+    shapes = {"per_tensor": ((1,), 1, 0), "per_channel": ((1, n), 1, 0), "per_token": ((m, 1), 1, 0),
+              "per_group1": ((m, -(-n // gs)), 1, gs), "per_group0": ((-(-m // gs), n), 0, gs)}
+    told_apart = [False, False]
+    for sname, src in srcs.items():
+        v = src.astype(np.float32) if isinstance(src, np.ndarray) else src.float().numpy()
+        for pname, (shape, kdim, g) in shapes.items():
+            policy = pname[:-1] if pname.startswith("per_group") else pname
+            s32 = rng.uniform(0.001, 0.05, shape).astype(f32)
+            o32 = rng.uniform(-8, 8, shape).astype(f32)
+            for pdt in ("float32", "float16", "bfloat16"):
+                if pdt == "float32":
+                    s, o = s32, o32
+                    sw, ow = s32, o32
+                elif pdt == "float16":
+                    s, o = s32.astype(np.float16), o32.astype(np.float16)
+                    sw, ow = s.astype(f32), o.astype(f32)
+                else:
+                    s, o = _bf16(s32), _bf16(o32)
+                    sw, ow = s.float().numpy(), o.float().numpy()
+                S_, O_ = _np_aq_params(policy, m, n, kdim, g, sw, ow)
+                for with_off in (True, False):
+                    t = ((v + O_).astype(f32) * S_).astype(f32) if with_off else (v * S_).astype(f32)
+                    if with_off:
+                        dist = ((v * S_).astype(f32) + (O_ * S_).astype(f32)).astype(f32)
+                        fma = (v.astype(np.float64) * S_ + (O_ * S_).astype(f32)).astype(f32)
+                        told_apart[0] |= not np.array_equal(t, dist)
+                        told_apart[1] |= not np.array_equal(t, fma)
+                    kw = {"kdim": kdim, "group_size": g} if policy == "per_group" else {}
+                    oo = o if with_off else None
+                    d32 = orc.antiquantize(src, s, oo, policy, dst="float32", **kw)
+                    assert np.array_equal(d32.view(np.uint32), t.view(np.uint32)), (sname, pname, pdt)
+                    dbf = orc.antiquantize(src, s, oo, policy, dst="bfloat16", **kw)
+                    want_bf = torch.from_numpy(t).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+                    assert np.array_equal(dbf, want_bf), (sname, pname, pdt)
+                    dh = orc.antiquantize(src, s, oo, policy, dst="float16", **kw)
+                    assert np.array_equal(dh, t.astype(np.float16).view(np.uint16)), (sname, pname, pdt)
+    assert all(told_apart), "inputs must tell the two-step form from the distributed and fused forms"
 
 
 def pin_aq_e5m2_source(orc):

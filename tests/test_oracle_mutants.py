@@ -105,6 +105,26 @@ MUTANTS = [
      "double a = (double)load_as_f32(x1, x_dtype, kk);"),
     ("f64_half_via_f32", "    double a = fabs(x);\n    if (isinf(x))\n        return (uint16_t)(sign | inf);",
      "    double a = fabs((double)(float)x);\n    if (isinf(x))\n        return (uint16_t)(sign | inf);"),
+    ("sym_codes_by_reciprocal", "c[j] = sat_rne(v[j] / sc, code_lo, code_hi);",
+     "c[j] = sat_rne(v[j] * (1.0f / sc), code_lo, code_hi);"),
+    ("asym_codes_by_reciprocal", "float q = v[j] / sc;", "float q = v[j] * (1.0f / sc);"),
+    ("asym_qhi_by_reciprocal", "float q_hi = hi / sc;", "float q_hi = hi * (1.0f / sc);"),
+    ("sym_scale_by_reciprocal", "float sc = amax / offset_opt;", "float sc = amax * (1.0f / offset_opt);"),
+    ("asym_scale_by_reciprocal", "float sc = range / scale_opt;", "float sc = range * (1.0f / scale_opt);"),
+    ("asym_offset_one_rounding", "float off = offset_opt - q_hi;",
+     "float off = (float)((double)offset_opt - (double)hi / (double)sc);"),
+    ("asym_code_one_rounding", "float t = q + off;", "float t = (float)((double)v[j] / (double)sc + (double)off);"),
+    ("ada_codes_by_reciprocal", "out[row * H + j] = (int8_t)sat_rne((float)yr[j] / qs, -128, 127);",
+     "out[row * H + j] = (int8_t)sat_rne((float)yr[j] * (1.0f / qs), -128, 127);"),
+    ("ada_scale_by_reciprocal", "float qs = amax / 127.0f;", "float qs = amax * (1.0f / 127.0f);"),
+    ("ada_codes_in_binary64", "out[row * H + j] = (int8_t)sat_rne((float)yr[j] / qs, -128, 127);",
+     "out[row * H + j] = (int8_t)sat_rne((float)(yr[j] / (double)qs), -128, 127);"),
+    ("aq_distributed_offset", "float u = v + o;\n                t = u * s;",
+     "float u = v * s;\n                t = u + o * s;"),
+    ("aq_fused_offset", "float u = v + o;\n                t = u * s;",
+     "float u = o * s;\n                t = fmaf(v, s, u);"),
+    ("aq_binary64_affine", "float u = v + o;\n                t = u * s;",
+     "double u = (double)v + o;\n                t = (float)(u * s);"),
     ("mx_amax_signed", "else if (fabs((double)v) > amax)\n                    amax = fabs((double)v);",
      "else if ((double)v > amax)\n                    amax = (double)v;"),
 ]
