@@ -80,7 +80,7 @@ typedef enum dq_dtype {
  * dims multiply to more than 2^48 is rejected with DQ_ERR_SHAPE. */
 typedef struct dq_tensor {
     void* data;
-    dq_dtype dtype;
+    int32_t dtype; /* a dq_dtype value; any other value is rejected (DQ_ERR_DTYPE) */
     int32_t ndim;
     int64_t dims[DQ_MAX_DIMS];
 } dq_tensor;
@@ -209,6 +209,7 @@ dq_status dq_ada_layernorm_quant(void* workspace, size_t workspace_size, dq_exec
  *   scale      b8 sources: F32, F16 or BF16 (widened exactly), policy
  *              shape.  F4E2M1: E8M0.
  *   offset     NULL, or the scale's dtype and shape; NULL for F4E2M1.
+ *   policy     a dq_antiquant_policy value (anything else: DQ_ERR_PARAM).
  *   k_dim      0 or 1, used by DQ_PER_GROUP only.
  *   group_size DQ_PER_GROUP: > 0 and a multiple of 32 (表2); ignored
  *              otherwise.
@@ -226,7 +227,7 @@ dq_status dq_ada_layernorm_quant(void* workspace, size_t workspace_size, dq_exec
  *   PER_GROUP), DQ_ERR_OVERLAP.
  * ------------------------------------------------------------------------ */
 dq_status dq_antiquantize_get_workspace_size(const dq_tensor* src, const dq_tensor* scale,
-                                             const dq_tensor* offset, dq_antiquant_policy policy,
+                                             const dq_tensor* offset, int32_t policy,
                                              int32_t k_dim, uint32_t group_size,
                                              const dq_tensor* dst, size_t* workspace_size,
                                              dq_executor** executor);

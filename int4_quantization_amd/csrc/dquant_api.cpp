@@ -53,7 +53,7 @@ dq_status ok()
     return DQ_SUCCESS;
 }
 
-const char* dtype_name(dq_dtype d)
+const char* dtype_name(int32_t d)
 {
     switch (d) {
     case DQ_F32: return "F32";
@@ -138,7 +138,7 @@ bool is_shape(const dq_tensor* t, std::initializer_list<int64_t> want)
     return true;
 }
 
-int64_t elem_bytes_x16(dq_dtype d)  // bytes per element times 2 (I4 is half a byte)
+int64_t elem_bytes_x16(int32_t d)  // bytes per element times 2 (I4 is half a byte)
 {
     switch (d) {
     case DQ_F32: case DQ_I32: return 8;
@@ -476,7 +476,7 @@ dq_status dq_ada_layernorm_quant(void* workspace, size_t workspace_size, dq_exec
 // AntiQuantize
 // ---------------------------------------------------------------------------
 dq_status dq_antiquantize_get_workspace_size(const dq_tensor* src, const dq_tensor* scale,
-                                             const dq_tensor* offset, dq_antiquant_policy policy,
+                                             const dq_tensor* offset, int32_t policy,
                                              int32_t k_dim, uint32_t group_size,
                                              const dq_tensor* dst, size_t* workspace_size,
                                              dq_executor** executor)
@@ -727,7 +727,7 @@ dq_status dq_weight_quant_matmul_get_workspace_size(const dq_tensor* x1, const d
     if ((st = check_tensor(x2, "x2", &nx2)) != DQ_SUCCESS) return st;
     if ((st = check_tensor(antiquant_scale, "antiquant_scale", &ns)) != DQ_SUCCESS) return st;
     if ((st = check_tensor(out, "out", &no)) != DQ_SUCCESS) return st;
-    const dq_dtype T = x1->dtype;
+    const int32_t T = x1->dtype;
     if (T != DQ_F16 && T != DQ_BF16)
         return fail(DQ_ERR_DTYPE, "x1 must be F16 or BF16, got %s", dtype_name(T));
     if (x2->dtype != DQ_I8 && x2->dtype != DQ_I4)

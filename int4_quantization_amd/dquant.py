@@ -20,7 +20,9 @@ from typing import Optional, Sequence, Tuple
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-library_path = os.path.join(_HERE, "libdquant.so")
+# DQ_LIBRARY selects another build of the library (the CPU sanitizer test
+# loads a host-only AddressSanitizer / UBSan build of the validation layer).
+library_path = os.environ.get("DQ_LIBRARY") or os.path.join(_HERE, "libdquant.so")
 
 # dq_status
 SUCCESS, ERR_NULLPTR, ERR_DTYPE, ERR_SHAPE, ERR_ALIGN, ERR_PARAM, ERR_OVERLAP, ERR_WORKSPACE, \

@@ -31,7 +31,9 @@ import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 SOURCE = os.path.join(HERE, "dquant_oracle.c")
-LIBRARY = os.path.join(HERE, "liboracle.so")
+# DQ_ORACLE_LIBRARY points at another build of the same source (the sanitizer
+# test loads an AddressSanitizer / UBSan build this way).
+LIBRARY = os.environ.get("DQ_ORACLE_LIBRARY") or os.path.join(HERE, "liboracle.so")
 
 # The oracle's own type codes (see the enum in dquant_oracle.c).
 F32, F16, BF16, I8, I4, I32, F8E4M3 = 0, 1, 2, 3, 4, 5, 6
