@@ -330,6 +330,37 @@ dq_status dq_weight_quant_matmul_get_workspace_size(const dq_tensor* x1, const d
 dq_status dq_weight_quant_matmul(void* workspace, size_t workspace_size, dq_executor* executor,
                                  hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Allocation-free weight-quantized matmul.
+ *
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * validation, plan, kernels and results as the two-phase pair above, in one
+ * call that allocates nothing, neither device memory nor host memory (no
+ * executor).  Where the plan splits k, the binary32 partial sums go to a
+ * scratch array the library owns, DQ_WQ_SCRATCH_BYTES (32 MiB) per GPU,
+ * held on each GPU the call runs on until the process ends; it needs no
+ * clearing (every split writes all of its partial sums).
+ *
+ *   Arguments as for dq_weight_quant_matmul_get_workspace_size, plus the
+ *   stream, whose device must be the current device.
+ *   Errors: those of dq_weight_quant_matmul_get_workspace_size;
+ *   DQ_ERR_WORKSPACE when the partial sums would exceed DQ_WQ_SCRATCH_BYTES
+ *   (splits * m * n * 4 bytes: decode shapes need at most about 2 MiB, and
+ *   only prefill shapes with few output tiles come near the limit); use the
+ *   two-phase pair with a caller workspace then.  DQ_ERR_PARAM when the
+ *   stream belongs to another device; DQ_ERR_RUNTIME on a launch failure.
+ *   Every call on one GPU shares that GPU's scratch array: calls that
+ *   overlap on one GPU (concurrent streams, or graphs replayed
+ *   concurrently) race on it and must be serialized by the caller.
+ * ------------------------------------------------------------------------ */
+#define DQ_WQ_SCRATCH_BYTES ((size_t)32 << 20)
+dq_status dq_weight_quant_matmul_noalloc(const dq_tensor* x1, const dq_tensor* x2, int32_t transpose_x2,
+                                         const dq_tensor* antiquant_scale,
+                                         const dq_tensor* antiquant_offset, int64_t group_size,
+                                         const dq_tensor* bias, const dq_tensor* x3, const dq_tensor* out,
+                                         hipStream_t stream);
+
 /* Release an executor that was never passed to an execute call.  NULL is a
  * no-op. */
 void dq_executor_destroy(dq_executor* executor);

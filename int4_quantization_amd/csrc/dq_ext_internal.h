@@ -85,4 +85,11 @@ constexpr int wq_tile_cols(int tile)
 hipError_t launch_mx_quantize(const MxPlan& p, hipStream_t stream);
 hipError_t launch_weight_quant_matmul(const WqPlan& p, void* workspace, hipStream_t stream);
 
+// Library-owned split-k scratch of the allocation-free matmul entry point:
+// its size, the most devices it is tracked on, and its address on the
+// current device (looked up once per device, then cached).
+constexpr size_t kWqScratchBytes = size_t{32} << 20;
+constexpr int kWqScratchDevices = 64;
+hipError_t wq_scratch_address(void** ptr);
+
 }  // namespace dq

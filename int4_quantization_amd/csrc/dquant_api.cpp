@@ -709,17 +709,18 @@ dq_status dq_mx_quantize(void* workspace, size_t workspace_size, dq_executor* ex
 // ---------------------------------------------------------------------------
 // Weight-quantized matmul
 // ---------------------------------------------------------------------------
-dq_status dq_weight_quant_matmul_get_workspace_size(const dq_tensor* x1, const dq_tensor* x2,
-                                                    int32_t transpose_x2,
-                                                    const dq_tensor* antiquant_scale,
-                                                    const dq_tensor* antiquant_offset,
-                                                    int64_t group_size, const dq_tensor* bias,
-                                                    const dq_tensor* x3, const dq_tensor* out,
-                                                    size_t* workspace_size, dq_executor** executor)
+}  // extern "C"
+
+namespace {
+
+// Validation and launch plan of the weight-quantized matmul, shared by the
+// two-phase pair and the allocation-free entry point.  Host only; writes
+// the plan and the split-k workspace size (0 when k is not split).
+dq_status plan_weight_quant_matmul(const dq_tensor* x1, const dq_tensor* x2, int32_t transpose_x2,
+                                   const dq_tensor* antiquant_scale, const dq_tensor* antiquant_offset,
+                                   int64_t group_size, const dq_tensor* bias, const dq_tensor* x3,
+                                   const dq_tensor* out, dq::WqPlan& p, size_t* workspace_size)
 {
-    if (!workspace_size || !executor)
-        return fail(DQ_ERR_NULLPTR, "workspace_size and executor must not be NULL");
-    *executor = nullptr;
     *workspace_size = 0;
     dq_status st;
     int64_t nx1 = 0, nx2 = 0, ns = 0, no = 0;
@@ -811,10 +812,7 @@ dq_status dq_weight_quant_matmul_get_workspace_size(const dq_tensor* x1, const d
             return fail(DQ_ERR_OVERLAP, "out overlaps an input");
     }
 
-    dq_executor* e = new_executor(OP_WEIGHT_QUANT_MATMUL);
-    if (!e)
-        return fail(DQ_ERR_RUNTIME, "out of host memory");
-    dq::WqPlan& p = e->wq;
+    p = dq::WqPlan{};
     p.x1 = x1->data;
     p.x2 = x2->data;
     p.scale = antiquant_scale->data;
@@ -858,6 +856,36 @@ dq_status dq_weight_quant_matmul_get_workspace_size(const dq_tensor* x1, const d
         if (p.splits > 1)
             *workspace_size = static_cast<size_t>(p.splits) * static_cast<size_t>(m) * static_cast<size_t>(n) * 4;
     }
+    return DQ_SUCCESS;
+}
+
+}  // namespace
+
+extern "C" {
+
+dq_status dq_weight_quant_matmul_get_workspace_size(const dq_tensor* x1, const dq_tensor* x2,
+                                                    int32_t transpose_x2,
+                                                    const dq_tensor* antiquant_scale,
+                                                    const dq_tensor* antiquant_offset,
+                                                    int64_t group_size, const dq_tensor* bias,
+                                                    const dq_tensor* x3, const dq_tensor* out,
+                                                    size_t* workspace_size, dq_executor** executor)
+{
+    if (!workspace_size || !executor)
+        return fail(DQ_ERR_NULLPTR, "workspace_size and executor must not be NULL");
+    *executor = nullptr;
+    *workspace_size = 0;
+    dq::WqPlan plan;
+    size_t ws = 0;
+    const dq_status st = plan_weight_quant_matmul(x1, x2, transpose_x2, antiquant_scale, antiquant_offset,
+                                                  group_size, bias, x3, out, plan, &ws);
+    if (st != DQ_SUCCESS)
+        return st;
+    dq_executor* e = new_executor(OP_WEIGHT_QUANT_MATMUL);
+    if (!e)
+        return fail(DQ_ERR_RUNTIME, "out of host memory");
+    e->wq = plan;
+    *workspace_size = ws;
     *executor = e;
     return ok();
 }
@@ -884,6 +912,44 @@ dq_status dq_weight_quant_matmul(void* workspace, size_t workspace_size, dq_exec
             return fail(DQ_ERR_ALIGN, "the workspace must be 16-byte aligned");
     }
     hipError_t err = dq::launch_weight_quant_matmul(p, workspace, stream);
+    if (err != hipSuccess)
+        return fail(DQ_ERR_RUNTIME, "weight quant matmul launch failed: %s", hipGetErrorString(err));
+    return ok();
+}
+
+dq_status dq_weight_quant_matmul_noalloc(const dq_tensor* x1, const dq_tensor* x2, int32_t transpose_x2,
+                                         const dq_tensor* antiquant_scale, const dq_tensor* antiquant_offset,
+                                         int64_t group_size, const dq_tensor* bias, const dq_tensor* x3,
+                                         const dq_tensor* out, hipStream_t stream)
+{
+    dq::WqPlan p;
+    size_t ws = 0;
+    const dq_status st = plan_weight_quant_matmul(x1, x2, transpose_x2, antiquant_scale, antiquant_offset,
+                                                  group_size, bias, x3, out, p, &ws);
+    if (st != DQ_SUCCESS)
+        return st;
+    if (ws > dq::kWqScratchBytes)
+        return fail(DQ_ERR_WORKSPACE,
+                    "the split-k partial sums need %zu bytes, more than the library's %zu-byte scratch; "
+                    "call dq_weight_quant_matmul with a workspace instead", ws, dq::kWqScratchBytes);
+    if (p.m == 0)
+        return ok();
+    void* scr = nullptr;
+    if (ws > 0) {
+        int cur = -1, sdev = -1;
+        hipError_t err = hipGetDevice(&cur);
+        if (err == hipSuccess)
+            err = hipStreamGetDevice(stream, &sdev);
+        if (err != hipSuccess)
+            return fail(DQ_ERR_RUNTIME, "cannot query the current device: %s", hipGetErrorString(err));
+        if (cur != sdev)
+            return fail(DQ_ERR_PARAM, "the stream's device (%d) must be the current device (%d)", sdev, cur);
+        err = dq::wq_scratch_address(&scr);
+        if (err != hipSuccess)
+            return fail(DQ_ERR_RUNTIME, "cannot locate the scratch array on device %d: %s", cur,
+                        hipGetErrorString(err));
+    }
+    hipError_t err = dq::launch_weight_quant_matmul(p, scr, stream);
     if (err != hipSuccess)
         return fail(DQ_ERR_RUNTIME, "weight quant matmul launch failed: %s", hipGetErrorString(err));
     return ok();

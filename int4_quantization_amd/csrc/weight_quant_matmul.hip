@@ -38,6 +38,8 @@
 // element, binary32 accumulation in k order.  It is the path for weights
 // stored [k, n].
 
+#include <atomic>
+
 #include "dq_device.h"
 #include "dq_ext_internal.h"
 
@@ -906,6 +908,38 @@ hipError_t launch_wt(const WqPlan& p, const WqArgs& a, hipStream_t stream)
 }
 
 }  // namespace
+
+// ---------------------------------------------------------------------------
+// Split-k scratch of dq_weight_quant_matmul_noalloc: binary32 partial sums
+// [splits, m, n] in a file-scope device array, one per GPU, held until the
+// process ends.  Every split writes each valid partial sum before the reduce
+// kernel reads it, so the array needs no clearing.  The array's name is a
+// host-side stand-in: host code uses only the per-device address that
+// hipGetSymbolAddress returns for it.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[kWqScratchBytes];
+
+hipError_t wq_scratch_address(void** ptr)
+{
+    static std::atomic<void*> cache[kWqScratchDevices];
+    int dev = -1;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess)
+        return err;
+    if (dev < 0 || dev >= kWqScratchDevices)
+        return hipErrorInvalidDevice;
+    void* p = cache[dev].load(std::memory_order_acquire);
+    if (!p) {
+        err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (err != hipSuccess)
+            return err;
+        if (!p)
+            return hipErrorInvalidSymbol;
+        cache[dev].store(p, std::memory_order_release);
+    }
+    *ptr = p;
+    return hipSuccess;
+}
 
 hipError_t launch_weight_quant_matmul(const WqPlan& p, void* workspace, hipStream_t stream)
 {

@@ -43,6 +43,7 @@ EXPORTS = [
     "dq_mx_quantize_get_workspace_size", "dq_mx_quantize",
     "dq_weight_quant_matmul_get_workspace_size", "dq_weight_quant_matmul",
     "dq_executor_destroy", "dq_get_last_error", "dq_copy_probe",
+    "dq_weight_quant_matmul_noalloc",
 ]
 
 
@@ -91,6 +92,10 @@ def library() -> ctypes.CDLL:
             _P(DqTensor), _P(DqTensor), ctypes.c_int32, _P(DqTensor), _P(DqTensor), ctypes.c_int64,
             _P(DqTensor), _P(DqTensor), _P(DqTensor), _P(ctypes.c_size_t), _P(_vp)]
         lib.dq_weight_quant_matmul_get_workspace_size.restype = st
+        lib.dq_weight_quant_matmul_noalloc.argtypes = [
+            _P(DqTensor), _P(DqTensor), ctypes.c_int32, _P(DqTensor), _P(DqTensor), ctypes.c_int64,
+            _P(DqTensor), _P(DqTensor), _P(DqTensor), _vp]
+        lib.dq_weight_quant_matmul_noalloc.restype = st
         for name in ("dq_dynamic_quant", "dq_ada_layernorm_quant", "dq_antiquantize",
                      "dq_mx_quantize", "dq_weight_quant_matmul"):
             fn = getattr(lib, name)
@@ -299,6 +304,20 @@ def dq_weight_quant_matmul_get_workspace_size(x1, x2, transpose_x2, antiquant_sc
 def dq_weight_quant_matmul(workspace, workspace_size: int, executor: int, stream=None) -> None:
     _check(library().dq_weight_quant_matmul(_ws_ptr(workspace), workspace_size, executor,
                                             _stream_handle(stream)))
+
+
+def dq_weight_quant_matmul_noalloc(x1, x2, transpose_x2, antiquant_scale, antiquant_offset, group_size,
+                                   bias, x3, out, stream=None, weight: Optional[str] = None) -> None:
+    """The allocation-free call: split-k partial sums go to the library's
+    per-GPU scratch array (at most WQ_SCRATCH_BYTES); out is written in place."""
+    lib = library()
+    d = _wq_descs(x1, x2, antiquant_scale, antiquant_offset, bias, x3, out, weight)
+    _check(lib.dq_weight_quant_matmul_noalloc(
+        _ref(d[0]), _ref(d[1]), 1 if transpose_x2 else 0, _ref(d[2]), _ref(d[3]), int(group_size),
+        _ref(d[4]), _ref(d[5]), _ref(d[6]), _stream_handle(stream)))
+
+
+WQ_SCRATCH_BYTES = 32 << 20  # DQ_WQ_SCRATCH_BYTES in include/dquant.h
 
 
 def dq_executor_destroy(executor: int) -> None:

@@ -502,3 +502,33 @@ def test_binding_rejects_strided_tensors():
             D.tensor_desc(view)
     with pytest.raises(ValueError, match="GPU memory"):  # a row slice is dense: only its memory is refused
         D.tensor_desc(base[2:5])
+
+
+# ---- allocation-free matmul ----------------------------------------------------
+
+def _wq_noalloc(lib, m, k, n, x3=False, gs=0, w_dtype=None):
+    x1 = desc(D.BF16, [m, k], 0x100000)
+    x2 = desc(w_dtype or D.I8, [n, k], 0x40000000)
+    sc = desc(D.BF16, [n, -(-k // gs)] if gs else [n], 0x80000000)
+    out = desc(D.BF16, [m, n], 0xC0000000)
+    x3d = desc(D.BF16, [m, n], 0xE0000000) if x3 else None
+    return lib.dq_weight_quant_matmul_noalloc(ref(x1), ref(x2), 1, ref(sc), None, gs, None,
+                                              ref(x3d) if x3d else None, ref(out), None)
+
+
+def test_noalloc_validation_without_gpu(lib):
+    """Validation and the scratch-size limit are host-side: they answer
+    without touching a GPU (the scratch address is looked up only for a
+    call that launches)."""
+    assert lib.dq_weight_quant_matmul_noalloc(None, None, 1, None, None, 0, None, None, None, None) == D.ERR_NULLPTR
+    x1 = desc(D.F32, [4, 128], 0x100000)
+    x2 = desc(D.I8, [64, 128], 0x40000000)
+    sc = desc(D.BF16, [64], 0x80000000)
+    out = desc(D.BF16, [4, 64], 0xC0000000)
+    assert lib.dq_weight_quant_matmul_noalloc(ref(x1), ref(x2), 1, ref(sc), None, 0, None, None, ref(out),
+                                              None) == D.ERR_DTYPE
+    # 384 x 4096 output, k 4096: 96 tiles of 128 x 128, split 6 ways -> 6 * 384 * 4096 * 4 bytes > 32 MiB.
+    assert _wq_noalloc(lib, 384, 4096, 4096) == D.ERR_WORKSPACE
+    assert "scratch" in lib.dq_get_last_error().decode()
+    # m == 0 launches nothing.
+    assert _wq_noalloc(lib, 0, 4096, 4096) == D.SUCCESS

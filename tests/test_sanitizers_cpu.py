@@ -30,6 +30,7 @@ hipError_t launch_antiquantize(const AqPlan&, hipStream_t) { return hipErrorNotS
 hipError_t launch_copy_probe(void*, const void*, size_t, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_mx_quantize(const MxPlan&, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_weight_quant_matmul(const WqPlan&, void*, hipStream_t) { return hipErrorNotSupported; }
+hipError_t wq_scratch_address(void**) { return hipErrorNotSupported; }
 }
 """
 
