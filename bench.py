@@ -41,6 +41,7 @@ from int4_quantization_amd import synth  # noqa: E402
 PEAK_GBPS = 8000.0           # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 / fp16 matrix-core peak
 ROTATE_BYTES = 1 << 30       # buffer-set rotation footprint (> 4x the 256 MB MALL)
+ISOLATED_LAUNCHES = 100      # individually event-timed launches for p10/p50/p90 (any --steps)
 HEADLINE = "dq_sym_smooth_bf16_8192x7168"
 METRIC = "achieved HBM GB/s (% of peak) + rows/s, per-token bf16→int8 dynamic quant"
 
@@ -232,7 +233,8 @@ def time_work(w: Work, steps: int, warmup: int):
     the launch stream around the same launches (its mean is the kernel's
     average launch duration: the queue stays full, so gaps are only the
     hardware dispatch between kernels).  A second, untimed pass brackets
-    each launch with its own events for the latency distribution."""
+    each launch with its own events for the latency distribution
+    (ISOLATED_LAUNCHES of them, whatever `steps` is)."""
     for i in range(warmup):
         w.launch(i)
     torch.cuda.synchronize()
@@ -247,7 +249,7 @@ def time_work(w: Work, steps: int, warmup: int):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     region = e0.elapsed_time(e1) * 1e-3
-    n = min(steps, 50)
+    n = ISOLATED_LAUNCHES
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
     for i in range(n):
         ev[i][0].record(stream)
@@ -273,6 +275,7 @@ def summarize(w: Work, wall: float, region: float, lat: np.ndarray, steps: int) 
         "gbps_wall": w.alg_bytes * steps / wall / 1e9,
         "rows_per_s": w.rows / mean,
         "buffer_sets": w.sets,
+        "traffic_bytes": recorded_traffic(w.name, w.op),
         **({"alg_flops": int(w.alg_flops), "tflops_kernel": w.alg_flops / mean / 1e12,
             "pct_peak_mfma_bf16": 100.0 * w.alg_flops / mean / 1e12 / PEAK_BF16_TFLOPS}
            if getattr(w, "alg_flops", None) else {}),
@@ -297,26 +300,36 @@ def copy_ceiling(dev, steps: int = 50) -> float:
     return 2 * nb / t / 1e9
 
 
-def kernel_source_hash() -> str:
-    """Hash of the sources the headline kernel is built from; HBM traffic
-    recorded under profiles/ is reported only while it still matches."""
+# Sources each op's kernels are built from; HBM traffic recorded under
+# profiles/ is reported only while they still hash to the recorded value.
+KERNEL_SOURCES = {
+    "dynamic_quant": ("dynamic_quant.hip", "dq_device.h", "dq_div.h", "dq_internal.h"),
+    "ada_layernorm_quant": ("ada_layernorm_quant.hip", "dq_device.h", "dq_div.h", "dq_internal.h"),
+    "antiquantize": ("antiquantize.hip", "dq_device.h", "dq_div.h", "dq_internal.h"),
+    "mx_quantize": ("mx_quantize.hip", "dq_device.h", "dq_div.h", "dq_ext_internal.h"),
+    "weight_quant_matmul": ("weight_quant_matmul.hip", "dq_device.h", "dq_div.h", "dq_ext_internal.h"),
+}
+
+
+def kernel_source_hash(op: str = "dynamic_quant") -> str:
+    """sha256 (first 16 hex digits) of the sources op's kernels are built from."""
     import hashlib
     csrc = os.path.join(ROOT, "int4_quantization_amd", "csrc")
     h = hashlib.sha256()
-    for f in ("dynamic_quant.hip", "dq_device.h", "dq_internal.h"):
+    for f in KERNEL_SOURCES[op]:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(name: str):
-    """HBM bytes per launch of `name` from profiles/hbm_traffic.txt (FETCH_SIZE
-    and WRITE_SIZE counters scaled by the copy-kernel calibration), or None
-    if absent or taken on other kernel sources."""
+def recorded_traffic(name: str, op: str):
+    """HBM bytes per launch of workload `name` from profiles/hbm_traffic.txt
+    (FETCH_SIZE and WRITE_SIZE counters scaled by the copy-kernel
+    calibration), or None if absent or taken on other kernel sources."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
     if not os.path.exists(path):
         return None
-    src = kernel_source_hash()
+    src = kernel_source_hash(op)
     with open(path) as f:
         for line in f:
             parts = line.split()
@@ -346,7 +359,20 @@ def cpu_baseline(name: str, max_rows: int) -> dict:
     alg = rows * n * 2 + nbytes(h["smooth"]) + rows * n + rows * 4
     return {"value": alg / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"{rows} of {x.shape[0]} rows of {name} (single-threaded C oracle, "
-                      f"{dt:.2f} s)", "rows_per_s": rows / dt}
+                      f"{dt:.2f} s)", "rows_per_s": rows / dt,
+            "host_cpu": host_cpu_model(), "host_nproc": os.cpu_count()}
+
+
+def host_cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
 
 def main():
@@ -404,7 +430,7 @@ def main():
                   file=sys.stderr, flush=True)
 
     cpu = cpu_baseline(HEADLINE, args.cpu_rows)
-    traffic = recorded_traffic(HEADLINE)
+    traffic = recorded_traffic(HEADLINE, "dynamic_quant")
     line = {
         "metric": METRIC,
         "value": round(head["alg_bytes"] * args.steps / wall / 1e9, 2),
@@ -424,7 +450,7 @@ def main():
         "rows_per_s": head["rows"] * args.steps / wall,
         "roofline": {"bound": "hbm", "achieved": round(head["gbps_kernel"], 2), "peak": PEAK_GBPS,
                      "unit": "GB/s", "frac": round(head["gbps_kernel"] / PEAK_GBPS, 4),
-                     "traffic": traffic, "kernel_source_sha": kernel_source_hash(),
+                     "traffic": traffic, "kernel_source_sha": kernel_source_hash("dynamic_quant"),
                      "kernel_us_mean": round(head["us_mean"], 3),
                      "alg_bytes_per_launch": head["alg_bytes"]},
         "cpu_baseline": cpu,
