@@ -214,6 +214,18 @@ __device__ __forceinline__ void param_vec(const void* p, int64_t idx, float* v)
     }
 }
 
+// Wave-uniform fp32 parameters through the scalar memory path: the index
+// (and so the address) is the same in every lane, so one scalar load serves
+// the wave instead of a vector load per lane, which leaves the vector memory
+// pipeline to the source and destination streams.  The address space cast
+// makes the load a scalar one; it needs a 4-byte aligned pointer.
+typedef const __attribute__((address_space(4))) uint32_t const_u32;
+
+__device__ __forceinline__ float param1_scalar_f32(const void* p, int64_t idx)
+{
+    return __builtin_bit_cast(float, ((const_u32*)p)[idx]);
+}
+
 template <int W>
 __device__ __forceinline__ void load_chunk(uint32_t (&raw)[W], const uint8_t* p)
 {
@@ -252,7 +264,12 @@ __device__ __forceinline__ void convert_store(const uint32_t (&raw)[Chunk<SRC, D
     store_chunk<DST>(out, t);
 }
 
-template <int SRC, int DST, int PK, bool OFF, int P>
+// UNI: every wave lies inside one row (chunks per row a multiple of 64), so
+// PER_TOKEN parameters are wave-uniform and are read with scalar loads
+// (measured 2.3% faster on int8 [16384, 8192]).  PER_GROUP parameters are
+// not: a wave's four groups of 128 are its own, so scalar loads of them all
+// miss the scalar cache (measured 20% slower), and they stay vector loads.
+template <int SRC, int DST, int PK, bool OFF, int P, bool UNI>
 __global__ __launch_bounds__(kBlock) void aq_kernel(AqArgs a)
 {
     using C = Chunk<SRC, DST>;
@@ -283,7 +300,16 @@ __global__ __launch_bounds__(kBlock) void aq_kernel(AqArgs a)
     }
 
     float sv[E], ov[E];
-    if (PK == PK_TENSOR || PK == PK_TOKEN || PK == PK_GROUP_N) {
+    if constexpr (UNI && PK == PK_TOKEN) {
+        const int64_t p = a.row0 + static_cast<int64_t>(__builtin_amdgcn_readfirstlane(rb));
+        const float s1 = param1_scalar_f32(a.scale, p);
+        const float o1 = OFF ? param1_scalar_f32(a.offset, p) : 0.0f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            sv[e] = s1;
+            ov[e] = o1;
+        }
+    } else if constexpr (PK == PK_TENSOR || PK == PK_TOKEN || PK == PK_GROUP_N) {
         int64_t p = 0;
         if (PK == PK_TOKEN)
             p = i0;
@@ -315,42 +341,46 @@ __global__ __launch_bounds__(kBlock) void aq_kernel(AqArgs a)
 using KernelFn = void (*)(AqArgs);
 
 template <int SRC, int DST, bool OFF, int P>
-KernelFn pick_pk(int pk)
+KernelFn pick_pk(int pk, bool uni)
 {
     switch (pk) {
-    case PK_TENSOR: return aq_kernel<SRC, DST, PK_TENSOR, OFF, P>;
-    case PK_CHANNEL: return aq_kernel<SRC, DST, PK_CHANNEL, OFF, P>;
-    case PK_TOKEN: return aq_kernel<SRC, DST, PK_TOKEN, OFF, P>;
-    case PK_GROUP_N: return aq_kernel<SRC, DST, PK_GROUP_N, OFF, P>;
-    case PK_GROUP_M: return aq_kernel<SRC, DST, PK_GROUP_M, OFF, P>;
+    case PK_TENSOR: return aq_kernel<SRC, DST, PK_TENSOR, OFF, P, false>;
+    case PK_CHANNEL: return aq_kernel<SRC, DST, PK_CHANNEL, OFF, P, false>;
+    case PK_TOKEN:
+        if constexpr (P == PARAM_F32)
+            if (uni)
+                return aq_kernel<SRC, DST, PK_TOKEN, OFF, P, true>;
+        return aq_kernel<SRC, DST, PK_TOKEN, OFF, P, false>;
+    case PK_GROUP_N: return aq_kernel<SRC, DST, PK_GROUP_N, OFF, P, false>;
+    case PK_GROUP_M: return aq_kernel<SRC, DST, PK_GROUP_M, OFF, P, false>;
     }
     return nullptr;
 }
 
 template <int SRC, int DST, int P>
-KernelFn pick_off(int pk, bool off)
+KernelFn pick_off(int pk, bool off, bool uni)
 {
-    return off ? pick_pk<SRC, DST, true, P>(pk) : pick_pk<SRC, DST, false, P>(pk);
+    return off ? pick_pk<SRC, DST, true, P>(pk, uni) : pick_pk<SRC, DST, false, P>(pk, uni);
 }
 
 template <int SRC, int P>
-KernelFn pick_dst(int dst, int pk, bool off)
+KernelFn pick_dst(int dst, int pk, bool off, bool uni)
 {
     switch (dst) {
-    case DST_BF16: return pick_off<SRC, DST_BF16, P>(pk, off);
-    case DST_F16: return pick_off<SRC, DST_F16, P>(pk, off);
-    case DST_F32: return pick_off<SRC, DST_F32, P>(pk, off);
+    case DST_BF16: return pick_off<SRC, DST_BF16, P>(pk, off, uni);
+    case DST_F16: return pick_off<SRC, DST_F16, P>(pk, off, uni);
+    case DST_F32: return pick_off<SRC, DST_F32, P>(pk, off, uni);
     }
     return nullptr;
 }
 
 template <int SRC>
-KernelFn pick_param(int param, int dst, int pk, bool off)
+KernelFn pick_param(int param, int dst, int pk, bool off, bool uni)
 {
     switch (param) {
-    case PARAM_F32: return pick_dst<SRC, PARAM_F32>(dst, pk, off);
-    case PARAM_F16: return pick_dst<SRC, PARAM_F16>(dst, pk, off);
-    case PARAM_BF16: return pick_dst<SRC, PARAM_BF16>(dst, pk, off);
+    case PARAM_F32: return pick_dst<SRC, PARAM_F32>(dst, pk, off, uni);
+    case PARAM_F16: return pick_dst<SRC, PARAM_F16>(dst, pk, off, uni);
+    case PARAM_BF16: return pick_dst<SRC, PARAM_BF16>(dst, pk, off, uni);
     }
     return nullptr;
 }
@@ -363,21 +393,21 @@ KernelFn pick_fp4(int dst, int pk)
     if (pk != PK_GROUP_N && pk != PK_GROUP_M)
         return nullptr;
     if (dst == DST_BF16)
-        return n_dir ? aq_kernel<SRC_F4E2M1, DST_BF16, PK_GROUP_N, false, PARAM_E8M0>
-                     : aq_kernel<SRC_F4E2M1, DST_BF16, PK_GROUP_M, false, PARAM_E8M0>;
+        return n_dir ? aq_kernel<SRC_F4E2M1, DST_BF16, PK_GROUP_N, false, PARAM_E8M0, false>
+                     : aq_kernel<SRC_F4E2M1, DST_BF16, PK_GROUP_M, false, PARAM_E8M0, false>;
     if (dst == DST_F16)
-        return n_dir ? aq_kernel<SRC_F4E2M1, DST_F16, PK_GROUP_N, false, PARAM_E8M0>
-                     : aq_kernel<SRC_F4E2M1, DST_F16, PK_GROUP_M, false, PARAM_E8M0>;
+        return n_dir ? aq_kernel<SRC_F4E2M1, DST_F16, PK_GROUP_N, false, PARAM_E8M0, false>
+                     : aq_kernel<SRC_F4E2M1, DST_F16, PK_GROUP_M, false, PARAM_E8M0, false>;
     return nullptr;
 }
 
-KernelFn pick_src(const AqPlan& p, int pk)
+KernelFn pick_src(const AqPlan& p, int pk, bool uni)
 {
     const bool off = p.offset != nullptr;
     switch (p.src_kind) {
-    case SRC_I8: return pick_param<SRC_I8>(p.param_kind, p.dst_kind, pk, off);
-    case SRC_F8E4M3: return pick_param<SRC_F8E4M3>(p.param_kind, p.dst_kind, pk, off);
-    case SRC_F8E5M2: return pick_param<SRC_F8E5M2>(p.param_kind, p.dst_kind, pk, off);
+    case SRC_I8: return pick_param<SRC_I8>(p.param_kind, p.dst_kind, pk, off, uni);
+    case SRC_F8E4M3: return pick_param<SRC_F8E4M3>(p.param_kind, p.dst_kind, pk, off, uni);
+    case SRC_F8E5M2: return pick_param<SRC_F8E5M2>(p.param_kind, p.dst_kind, pk, off, uni);
     case SRC_F4E2M1: return off || p.param_kind != PARAM_E8M0 ? nullptr : pick_fp4(p.dst_kind, pk);
     }
     return nullptr;
@@ -390,10 +420,16 @@ hipError_t launch_antiquantize(const AqPlan& p, hipStream_t stream)
     int pk = p.policy;  // DQ_PER_TENSOR .. DQ_PER_TOKEN map to the same numbers
     if (p.policy == DQ_PER_GROUP)
         pk = p.k_dim == 1 ? PK_GROUP_N : PK_GROUP_M;
-    KernelFn fn = pick_src(p, pk);
+    const int64_t E = p.dst_kind == DST_F32 ? 4 : 8;
+    // Scalar PER_TOKEN parameter loads: fp32 parameters, 4-byte aligned,
+    // and every wave inside one row.
+    const bool rows_of_waves = p.n % (E * kWave) == 0;
+    const bool f32_aligned = p.param_kind == PARAM_F32 &&
+                             ((reinterpret_cast<uintptr_t>(p.scale) | reinterpret_cast<uintptr_t>(p.offset)) & 3) == 0;
+    const bool uni = rows_of_waves && f32_aligned && pk == PK_TOKEN;
+    KernelFn fn = pick_src(p, pk, uni);
     if (!fn)
         return hipErrorInvalidValue;
-    const int64_t E = p.dst_kind == DST_F32 ? 4 : 8;
     const int64_t R = (pk == PK_CHANNEL || pk == PK_GROUP_M) ? kAqRowsPerThread : 1;
     AqArgs a{};
     a.src = p.src;

@@ -46,6 +46,21 @@ def test_antiquantize_half_params(orc, policy, kdim, gs, pdt, src):
         check_antiquantize(orc, q["src"], q["scale"], q["offset"], policy, kdim, q["group_size"], dst)
 
 
+# Rows of whole waves (n a multiple of 512, or of 256 for fp32 output) with
+# fp32 parameters: PER_TOKEN takes scalar parameter loads; PER_GROUP along n
+# on the same shapes (groups of 128 / 384, a short last group) for contrast.
+SCALAR_PATH = [("per_token", 0, 2048), ("per_token", 0, 1536), ("per_group", 128, 2048),
+               ("per_group", 384, 2560)]
+
+
+@pytest.mark.parametrize("policy,gs,n", SCALAR_PATH, ids=[f"{p}-g{g}-n{n}" for p, g, n in SCALAR_PATH])
+@pytest.mark.parametrize("dst", DSTS, ids=["bf16", "f16", "f32"])
+@pytest.mark.parametrize("with_offset", [True, False], ids=["offset", "no_offset"])
+def test_antiquantize_scalar_parameter_path(orc, policy, gs, n, dst, with_offset):
+    announce("antiquantize scalar params", policy, gs, n, dst, with_offset)
+    q = synth.aq_inputs(37, n, policy, 500 + gs + n, kdim=1, group_size=gs or 128, offset=with_offset)
+    check_antiquantize(orc, q["src"], q["scale"], q["offset"], policy, 1, q["group_size"], dst)
+
 FP4_CASES = [(1, 32), (1, 96), (0, 32), (0, 64)]
 
 
