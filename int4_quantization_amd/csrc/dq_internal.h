@@ -19,6 +19,7 @@ enum OutKind : int { OUT_I8 = 0, OUT_I4 = 1 };  // INT32 output shares the INT4 
 enum DqVariant : int {
     DQ_VAR_VECTOR = 0,   // row held in VGPRs, 16-byte loads, TEAM waves per row
     DQ_VAR_GENERIC = 1,  // one workgroup per row, element loads, two passes
+    DQ_VAR_TEAM = 2,     // a workgroup is one team whose waves cover the row exactly
 };
 
 struct DqPlan {
@@ -36,8 +37,8 @@ struct DqPlan {
     float* offset;
     // launch choice
     int variant;
-    int vpl;   // 16-byte vectors per lane (vector variant)
-    int team;  // waves per row (vector variant): 1, 2 or 4
+    int vpl;   // 16-byte vectors per lane (vector and team variants)
+    int team;  // waves per row: 1, 2 or 4 (vector variant), 2 .. kDqMaxTeam (team variant)
 };
 
 // Largest grid (workgroups along x) a launch may use, and the largest row
@@ -95,6 +96,10 @@ hipError_t launch_copy_probe(void* dst, const void* src, size_t bytes, hipStream
 // largest row (in elements) it holds: 16 vectors of 8 elements per lane,
 // 64 lanes, kDqWaves waves.
 constexpr int kDqWaves = 4;
+// Team variant: the most waves a team (one workgroup) has, and the rows each
+// team converts before the workgroup exits.
+constexpr int kDqMaxTeam = 16;
+constexpr int kDqTeamRows = 4;
 constexpr int kDqTeamVpl = 4;
 constexpr int kDqPrefetch = 1;
 constexpr int64_t kDqVecMaxPerWave = 16 * 8 * 64;

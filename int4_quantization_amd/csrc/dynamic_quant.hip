@@ -161,14 +161,14 @@ __device__ __forceinline__ void store_packed(void* y, int64_t row, int64_t n, in
 // min, and every load is unconditional, so each register's load is always
 // consumed before it is loaded again (no divergent paths that would force a
 // full wait on outstanding memory before the next prefetch).
-template <int VPL, int TEAM>
+template <int VPL>
 __device__ __forceinline__ void load_x(uint4 (&raw)[VPL], const void* x, int64_t row, int64_t n, int64_t nvec,
-                                       int wit, int lane)
+                                       int team, int wit, int lane)
 {
     const uint4* xr = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + row * n);
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
-        const int64_t k = static_cast<int64_t>(i * TEAM + wit) * kWave + lane;
+        const int64_t k = static_cast<int64_t>(i * team + wit) * kWave + lane;
         raw[i] = ld_stream16(xr + (k < nvec ? k : nvec - 1));
     }
 }
@@ -200,15 +200,15 @@ __device__ __forceinline__ int64_t row_expert(int64_t row, int32_t gi_lane, cons
     return expert_of_row(row, a.gi, a.n_experts, lane);
 }
 
-template <int VPL, int TEAM>
+template <int VPL>
 __device__ __forceinline__ void load_smooth(float (&sreg)[VPL][8], const DqArgs& a, int64_t e, int64_t nvec,
-                                            int wit, int lane)
+                                            int team, int wit, int lane)
 {
     if (a.smooth) {
         const float4* sr = reinterpret_cast<const float4*>(a.smooth + e * a.n);
 #pragma unroll
         for (int i = 0; i < VPL; ++i) {
-            int64_t k = static_cast<int64_t>(i * TEAM + wit) * kWave + lane;
+            int64_t k = static_cast<int64_t>(i * team + wit) * kWave + lane;
             k = k < nvec ? k : nvec - 1;
             const float4 s0 = sr[2 * k], s1 = sr[2 * k + 1];
             sreg[i][0] = s0.x;
@@ -237,10 +237,11 @@ __device__ __forceinline__ void load_smooth(float (&sreg)[VPL][8], const DqArgs&
 // owner writes.  With no branch between this row's stores and the next
 // row's loads, the compiler neither moves those loads below the stores nor
 // makes their wait also wait for the stores.
-template <int XT, bool SYM, int OUT, int VPL, int TEAM>
+// TMAX: the largest team the caller has (1: a wave per row, no exchange).
+template <int XT, bool SYM, int OUT, int VPL, int TMAX>
 __device__ __forceinline__ void convert_row(const DqArgs& a, const uint4 (&raw)[VPL], const float (&sreg)[VPL][8],
-                                            int64_t row, int t, int64_t nvec, int slot, int wit, int lane,
-                                            float (&red)[2][2][kDqWaves])
+                                            int64_t row, int t, int64_t nvec, int slot, int team, int wit, int lane,
+                                            float2 (&red)[2][kDqMaxTeam])
 {
     float s_hi = SYM ? 0.0f : -__builtin_huge_valf();
     float s_lo = __builtin_huge_valf();
@@ -261,24 +262,24 @@ __device__ __forceinline__ void convert_row(const DqArgs& a, const uint4 (&raw)[
     s_hi = wave_max_f(s_hi);
     if (!SYM)
         s_lo = wave_min_f(s_lo);
-    if (TEAM > 1) {
+    if (TMAX > 1) {
         // Partials alternate between two LDS slots by step, so a slot is
         // rewritten only after every wave has passed the barrier of the step
-        // that read it.
+        // that read it.  All TMAX slots are read at once (slots past the
+        // team repeat the first), so the reads do not wait on one another.
         const int par = t & 1;
-        const int wave = slot * TEAM + wit;
-        if (lane == 0) {
-            red[par][0][wave] = s_hi;
-            red[par][1][wave] = s_lo;
-        }
+        const int w0 = slot * team;
+        if (lane == 0)
+            red[par][w0 + wit] = make_float2(s_hi, s_lo);
         __syncthreads();
-        const int w0 = slot * TEAM;
-        s_hi = red[par][0][w0];
-        s_lo = red[par][1][w0];
+        const float2 p0 = red[par][w0];
+        s_hi = p0.x;
+        s_lo = p0.y;
 #pragma unroll
-        for (int w = 1; w < TEAM; ++w) {
-            s_hi = __builtin_fmaxf(s_hi, red[par][0][w0 + w]);
-            s_lo = __builtin_fminf(s_lo, red[par][1][w0 + w]);
+        for (int w = 1; w < TMAX; ++w) {
+            const float2 pw = red[par][w0 + (w < team ? w : 0)];
+            s_hi = __builtin_fmaxf(s_hi, pw.x);
+            s_lo = __builtin_fminf(s_lo, pw.y);
         }
         // The values are the same in every lane; saying so keeps the row
         // parameters in scalar registers and makes the branch below a
@@ -290,10 +291,14 @@ __device__ __forceinline__ void convert_row(const DqArgs& a, const uint4 (&raw)[
     }
 
     const RowParams<SYM, OUT> rp(s_hi, s_lo);
-    // Every lane of the team writes the same value to the same place.
-    a.scale[row] = rp.scale;
-    if (!SYM)
-        a.offset[row] = rp.offset;
+    // The team's first wave writes the row parameters (all its lanes the same
+    // value to the same place): one store instruction per row, under a
+    // wave-uniform branch.
+    if (__builtin_amdgcn_readfirstlane(wit) == 0) {
+        a.scale[row] = rp.scale;
+        if (!SYM)
+            a.offset[row] = rp.offset;
+    }
     // Codes are computed on one of two paths and stored after they join, so
     // the stores are one straight sequence whichever path ran.
     uint2 pk[VPL];
@@ -318,7 +323,7 @@ __device__ __forceinline__ void convert_row(const DqArgs& a, const uint4 (&raw)[
     }
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
-        int64_t k = static_cast<int64_t>(i * TEAM + wit) * kWave + lane;
+        int64_t k = static_cast<int64_t>(i * team + wit) * kWave + lane;
         k = k < nvec ? k : nvec - 1;
         store_packed<OUT>(a.y, row, a.n, k, pk[i]);
     }
@@ -357,7 +362,7 @@ __global__ __launch_bounds__(kDqWaves * kWave) void dq_vec_kernel(DqArgs a)
                                : (static_cast<int64_t>(blockIdx.x) + static_cast<int64_t>(t) * gridDim.x) * RPS + slot;
         return r < a.rows ? r : a.rows - 1;
     };
-    __shared__ float red[2][2][kDqWaves];
+    __shared__ float2 red[2][kDqMaxTeam];
 
     // Every load is unconditional or under a workgroup-uniform branch (a
     // load under a divergent branch makes the compiler wait for everything
@@ -369,7 +374,7 @@ __global__ __launch_bounds__(kDqWaves * kWave) void dq_vec_kernel(DqArgs a)
         gi_lane = a.gi[lane < a.n_experts ? lane : a.n_experts - 1];
 
     uint4 buf[NB][VPL];
-    load_x<VPL, TEAM>(buf[0], a.x, row_of(0), a.n, nvec, wit, lane);
+    load_x<VPL>(buf[0], a.x, row_of(0), a.n, nvec, TEAM, wit, lane);
 
     float sreg[VPL][8];
     int64_t e0 = 0;
@@ -380,25 +385,82 @@ __global__ __launch_bounds__(kDqWaves * kWave) void dq_vec_kernel(DqArgs a)
         one_expert = e0 == row_expert(r_last, gi_lane, a, lane);  // workgroup-uniform
     }
     if (one_expert) {
-        load_smooth<VPL, TEAM>(sreg, a, e0, nvec, wit, lane);
+        load_smooth<VPL>(sreg, a, e0, nvec, TEAM, wit, lane);
 #pragma unroll
         for (int t = 1; t < PD && t < T; ++t)
-            load_x<VPL, TEAM>(buf[t % NB], a.x, row_of(t), a.n, nvec, wit, lane);
+            load_x<VPL>(buf[t % NB], a.x, row_of(t), a.n, nvec, TEAM, wit, lane);
 #pragma unroll
         for (int t = 0; t < T; ++t) {
             if (t + PD < T)
-                load_x<VPL, TEAM>(buf[(t + PD) % NB], a.x, row_of(t + PD), a.n, nvec, wit, lane);
+                load_x<VPL>(buf[(t + PD) % NB], a.x, row_of(t + PD), a.n, nvec, TEAM, wit, lane);
             __builtin_amdgcn_sched_barrier(0);
-            convert_row<XT, SYM, OUT, VPL, TEAM>(a, buf[t % NB], sreg, row_of(t), t, nvec, slot, wit, lane, red);
+            convert_row<XT, SYM, OUT, VPL, TEAM>(a, buf[t % NB], sreg, row_of(t), t, nvec, slot, TEAM, wit, lane, red);
         }
     } else {
         // The rows straddle an expert boundary (rare): one row at a time,
         // each with its own expert's smooth scales.
         for (int t = 0; t < T; ++t) {
             if (t > 0)
-                load_x<VPL, TEAM>(buf[0], a.x, row_of(t), a.n, nvec, wit, lane);
-            load_smooth<VPL, TEAM>(sreg, a, row_expert(row_of(t), gi_lane, a, lane), nvec, wit, lane);
-            convert_row<XT, SYM, OUT, VPL, TEAM>(a, buf[0], sreg, row_of(t), t, nvec, slot, wit, lane, red);
+                load_x<VPL>(buf[0], a.x, row_of(t), a.n, nvec, TEAM, wit, lane);
+            load_smooth<VPL>(sreg, a, row_expert(row_of(t), gi_lane, a, lane), nvec, TEAM, wit, lane);
+            convert_row<XT, SYM, OUT, VPL, TEAM>(a, buf[0], sreg, row_of(t), t, nvec, slot, TEAM, wit, lane, red);
+        }
+    }
+}
+
+// Team variant: a workgroup is one team of W = blockDim.x / 64 waves whose
+// W * VPL * 64 lanes' vectors cover the row exactly (the host picks it when
+// the vector variant's fixed teams of 1, 2 or 4 waves would leave lanes
+// holding duplicate vectors: bf16 [*, 7168] is 896 vectors, 7 waves of 2
+// per lane instead of 4 waves of 4 with 128 duplicates).  Each team converts
+// kDqTeamRows rows with the next row's loads in flight, then the workgroup
+// exits; rows are assigned as in the vector variant.
+template <int XT, bool SYM, int OUT, int VPL>
+__global__ __launch_bounds__(kDqMaxTeam * kWave) void dq_team_kernel(DqArgs a)
+{
+    constexpr int T = kDqTeamRows;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wit = threadIdx.x / kWave;
+    const int team = blockDim.x / kWave;
+    const int64_t nvec = a.n >> 3;
+    const int64_t r0 = static_cast<int64_t>(blockIdx.x) * T;
+    auto row_of = [&](int t) -> int64_t {
+        const int64_t r = a.gi ? r0 + t : static_cast<int64_t>(blockIdx.x) + static_cast<int64_t>(t) * gridDim.x;
+        return r < a.rows ? r : a.rows - 1;
+    };
+    __shared__ float2 red[2][kDqMaxTeam];
+
+    const bool moe = a.gi != nullptr;
+    int32_t gi_lane = 0;
+    if (moe)
+        gi_lane = a.gi[lane < a.n_experts ? lane : a.n_experts - 1];
+
+    uint4 buf[2][VPL];
+    load_x<VPL>(buf[0], a.x, row_of(0), a.n, nvec, team, wit, lane);
+
+    float sreg[VPL][8];
+    int64_t e0 = 0;
+    bool one_expert = true;
+    if (moe && a.smooth) {
+        const int64_t r_last = r0 + T - 1 < a.rows ? r0 + T - 1 : a.rows - 1;
+        e0 = row_expert(r0, gi_lane, a, lane);
+        one_expert = e0 == row_expert(r_last, gi_lane, a, lane);  // workgroup-uniform
+    }
+    if (one_expert) {
+        load_smooth<VPL>(sreg, a, e0, nvec, team, wit, lane);
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            if (t + 1 < T)
+                load_x<VPL>(buf[(t + 1) & 1], a.x, row_of(t + 1), a.n, nvec, team, wit, lane);
+            __builtin_amdgcn_sched_barrier(0);
+            convert_row<XT, SYM, OUT, VPL, kDqMaxTeam>(a, buf[t & 1], sreg, row_of(t), t, nvec, 0, team, wit, lane, red);
+        }
+    } else {
+        for (int t = 0; t < T; ++t) {
+            if (t > 0)
+                load_x<VPL>(buf[0], a.x, row_of(t), a.n, nvec, team, wit, lane);
+            load_smooth<VPL>(sreg, a, row_expert(row_of(t), gi_lane, a, lane), nvec, team, wit, lane);
+            convert_row<XT, SYM, OUT, VPL, kDqMaxTeam>(a, buf[0], sreg, row_of(t), t, nvec, 0, team, wit, lane, red);
         }
     }
 }
@@ -500,6 +562,13 @@ KernelFn pick_vpl(int vpl)
 template <int XT, bool SYM, int OUT>
 KernelFn pick(const DqPlan& p)
 {
+    if (p.variant == DQ_VAR_TEAM) {
+        switch (p.vpl) {
+        case 1: return dq_team_kernel<XT, SYM, OUT, 1>;
+        case 2: return dq_team_kernel<XT, SYM, OUT, 2>;
+        }
+        return nullptr;
+    }
     if (p.variant != DQ_VAR_VECTOR)
         return dq_generic_kernel<XT, SYM, OUT>;
     switch (p.team) {
@@ -530,13 +599,23 @@ hipError_t launch_dynamic_quant(const DqPlan& p, hipStream_t stream)
     if (!fn)
         return hipErrorInvalidValue;
     DqArgs a{p.x, p.smooth, p.group_index, p.n_experts, p.rows, p.n, p.y, p.scale, p.offset};
-    // Vector variant: one workgroup per T * 4/TEAM rows; generic: one per row.
-    const int64_t rpb = p.variant == DQ_VAR_VECTOR ? dq_rows_per_team(p.vpl, p.team) * (kDqWaves / p.team) : 1;
+    // Vector variant: one workgroup per T * 4/TEAM rows; team variant: one
+    // per kDqTeamRows rows; generic: one per row.
+    int64_t rpb = 1;
+    int threads = kBlock;
+    if (p.variant == DQ_VAR_VECTOR) {
+        rpb = dq_rows_per_team(p.vpl, p.team) * (kDqWaves / p.team);
+        threads = kDqWaves * kWave;
+    } else if (p.variant == DQ_VAR_TEAM) {
+        if (p.team < 2 || p.team > kDqMaxTeam)
+            return hipErrorInvalidValue;
+        rpb = kDqTeamRows;
+        threads = p.team * kWave;
+    }
     const int64_t blocks = (p.rows + rpb - 1) / rpb;
     if (blocks > kMaxGridBlocks)
         return hipErrorInvalidValue;
     void* args[] = {&a};
-    const int threads = p.variant == DQ_VAR_VECTOR ? kDqWaves * kWave : kBlock;
     return hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3(static_cast<uint32_t>(blocks)), dim3(threads),
                            args, 0, stream);
 }

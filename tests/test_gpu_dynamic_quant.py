@@ -14,10 +14,14 @@ pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
 
 # (rows, n): widths chosen to hit each register-resident size (1, 2, 4, 8,
-# 12, 14, 16 vectors per lane), the four-wave variant (12288, 32768), and the
-# generic variant (40000 > 32768, 250 and 7 not multiples of 8).
+# 12, 14, 16 vectors per lane), the four-wave variant (8192, 32768), the team
+# variant whose waves cover the row exactly (3072: 6 waves x 1 vector per
+# lane, 2560: 5 x 1, 3584: 7 x 1, 5632: 11 x 1, 5120: 5 x 2, 7168: 7 x 2,
+# 12288: 12 x 2, 14336: 14 x 2), and the generic variant (40000 > 32768, 250
+# and 7 not multiples of 8).  Row counts leave partial row groups.
 SHAPES = [(37, 64), (37, 256), (19, 1000), (29, 3072), (33, 4096), (6, 5632), (21, 7168),
-          (9, 8192), (5, 12288), (3, 32768), (3, 40000), (13, 250), (7, 7)]
+          (9, 8192), (5, 12288), (3, 32768), (3, 40000), (13, 250), (7, 7), (37, 2560), (33, 3584),
+          (11, 5120), (7, 14336)]
 
 
 def _moe_index(rows: int, experts: int, seed: int) -> torch.Tensor:
