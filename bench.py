@@ -42,6 +42,8 @@ PEAK_GBPS = 8000.0           # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 / fp16 matrix-core peak
 ROTATE_BYTES = 1 << 30       # buffer-set rotation footprint (> 4x the 256 MB MALL)
 ISOLATED_LAUNCHES = 100      # individually event-timed launches for p10/p50/p90 (any --steps)
+EXTRA_MIN_STEPS = 200        # timed launches of each non-headline workload, at least
+EXTRA_MIN_WARMUP = 20
 HEADLINE = "dq_sym_smooth_bf16_8192x7168"
 METRIC = "achieved HBM GB/s (% of peak) + rows/s, per-token bf16→int8 dynamic quant"
 
@@ -415,14 +417,19 @@ def main():
     ceiling = copy_ceiling(dev)
     print(f"# copy ceiling {ceiling:.0f} GB/s", file=sys.stderr, flush=True)
 
+    # The other workloads are context, not the headline: each is timed over
+    # at least EXTRA_MIN_STEPS launches after at least EXTRA_MIN_WARMUP, so a
+    # short headline run does not leave them with a few noisy launches.
+    extra_steps = max(args.steps, EXTRA_MIN_STEPS)
+    extra_warmup = max(args.warmup, EXTRA_MIN_WARMUP)
     extra = {}
     if not args.no_extra:
         for name in synth.WORKLOADS:
             if name == HEADLINE:
                 continue
             wk = make_work(name, dev)
-            wl, rg, lt = time_work(wk, args.steps, args.warmup)
-            extra[name] = summarize(wk, wl, rg, lt, args.steps)
+            wl, rg, lt = time_work(wk, extra_steps, extra_warmup)
+            extra[name] = summarize(wk, wl, rg, lt, extra_steps)
             wk.free()
             torch.cuda.empty_cache()
             print(f"# {name}: {extra[name]['gbps_kernel']:.0f} GB/s "
@@ -455,6 +462,7 @@ def main():
                      "alg_bytes_per_launch": head["alg_bytes"]},
         "cpu_baseline": cpu,
         "copy_ceiling_gbps": round(ceiling, 1),
+        "extra_workloads_steps": extra_steps,
         "headline_detail": head,
         "workloads": extra,
     }
