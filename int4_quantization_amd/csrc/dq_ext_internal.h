@@ -69,9 +69,13 @@ constexpr int kWqGemmRows = 128, kWqGemmCols = 128, kWqGemmK = 128;
 // groups when groups are one k-step long; k splits are then planned in
 // multiples of the window.
 constexpr int kWqParamWindow = 8;
-constexpr int wq_batch(int tile)
+// Supersteps per batch.  Decode: 256 bytes of each column's weights per
+// batch (four supersteps of int4, two of int8); shorter runs per column
+// (two int4 supersteps) and longer ones (eight), or more batches in flight,
+// all measured slower.  GEMM: k splits in steps of 128.
+constexpr int wq_batch(int tile, int weight)
 {
-    return tile == WQ_TILE_DECODE ? 2 : 1;  // GEMM: k splits in steps of 128
+    return tile == WQ_TILE_DECODE ? (weight == WQ_I4 ? 4 : 2) : 1;
 }
 constexpr int wq_tile_rows(int tile)
 {

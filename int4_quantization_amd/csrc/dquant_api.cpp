@@ -856,7 +856,7 @@ dq_status plan_weight_quant_matmul(const dq_tensor* x1, const dq_tensor* x2, int
     if (p.variant == dq::WQ_VAR_MFMA && m > 0) {  // m == 0 launches nothing
         const int64_t tiles = ((n + dq::wq_tile_cols(p.tile) - 1) / dq::wq_tile_cols(p.tile)) *
                               ((m + dq::wq_tile_rows(p.tile) - 1) / dq::wq_tile_rows(p.tile));
-        const int64_t batch_k = static_cast<int64_t>(dq::wq_batch(p.tile)) * dq::kWqSuperK;
+        const int64_t batch_k = static_cast<int64_t>(dq::wq_batch(p.tile, p.w_type)) * dq::kWqSuperK;
         const int64_t batches = (k + batch_k - 1) / batch_k;
         const int64_t target = p.tile == dq::WQ_TILE_DECODE ? kWqTargetBlocks : kWqGemmTargetBlocks;
         int64_t want = tiles < target ? (target + tiles - 1) / tiles : 1;

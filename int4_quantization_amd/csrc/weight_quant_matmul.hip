@@ -20,8 +20,11 @@
 //     + 3 of column l % 16.
 //   - Dequantization follows the formula step by step in binary32 (signed
 //     byte or nibble -> binary32, + offset, * scale, round to T), so W is
-//     exact.  A run of 32 k never straddles a parameter group (the group
-//     size is a multiple of 32).
+//     exact.  The decode kernel, where that arithmetic bounds the time,
+//     takes the offset and scale in one FMA where wq_fma.h shows it exact
+//     (nearly always) and the step-by-step form otherwise.  A run of 32 k
+//     never straddles a parameter group (the group size is a multiple of
+//     32).
 //   - Rows past m repeat the last row (their results are not stored);
 //     columns past n repeat the last column (likewise).  k runs in whole
 //     groups of 32 (int8) or 64 (int4) elements.
@@ -42,6 +45,7 @@
 
 #include "dq_device.h"
 #include "dq_ext_internal.h"
+#include "wq_fma.h"
 
 namespace dq {
 namespace {
@@ -72,6 +76,25 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t o
 __device__ __forceinline__ uint16_t buf_load2(__amdgpu_buffer_rsrc_t r, uint32_t off)
 {
     return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+// N = 1, 2 or 4 consecutive dwords with one load (off a multiple of 4 N).
+template <int N>
+__device__ __forceinline__ void buf_load_words(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t (&w)[N])
+{
+    if constexpr (N == 1) {
+        w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+    } else if constexpr (N == 2) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+        w[0] = static_cast<uint32_t>(v[0]);
+        w[1] = static_cast<uint32_t>(v[1]);
+    } else {
+        static_assert(N == 4, "one load of 4, 8 or 16 bytes");
+        const i32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+        w[0] = static_cast<uint32_t>(v.x);
+        w[1] = static_cast<uint32_t>(v.y);
+        w[2] = static_cast<uint32_t>(v.z);
+        w[3] = static_cast<uint32_t>(v.w);
+    }
 }
 
 struct WqArgs {
@@ -203,6 +226,14 @@ __device__ __forceinline__ float dequant1(float d, float s, float o)
     }
 }
 
+// The one-FMA form of the dequantization with offset and when it is exact
+// (wq_fma.h), for this kernel's code width and T.
+template <int WT, int XT>
+__device__ __forceinline__ bool fma_exact(float o, float s, float os)
+{
+    return wq_fma_exact(o, s, os, wq_fma_offset_floor(WT == WQ_I4, XT == X_BF16));
+}
+
 // ---------------------------------------------------------------------------
 // Decode-shaped kernel: at most 16 rows of x1, so the weights dominate the
 // traffic.  A wave owns 16 RN columns; a workgroup (four waves) stages the
@@ -212,14 +243,16 @@ __device__ __forceinline__ float dequant1(float d, float s, float o)
 // current one.  k is split across workgroups (blockIdx.z) as planned on the
 // host.
 // ---------------------------------------------------------------------------
-// PAIR: per-group parameters with groups of 128 (one per superstep) and an
-// even group count, so the two groups of a batch are adjacent in a column's
-// parameter row and one 4-byte load fetches both (the loads of the per-group
-// parameters cost as much time as the weight stream when made one by one).
+// PAIR: per-group parameters with groups of 128 (one per superstep) and a
+// group count that is a multiple of U, so the U groups of a batch are
+// adjacent in a column's parameter row and one load of 2 U bytes fetches
+// them all (the loads of the per-group parameters cost as much time as the
+// weight stream when made one by one).
 template <int XT, int WT, int POL, bool OFF, int RN, int U, bool PAIR>
 __global__ __launch_bounds__(kWqDecodeWaves * kWave) void wq_decode_kernel(const WqArgs a)
 {
-    static_assert(!PAIR || (POL == DQ_PER_GROUP && U == 2), "paired parameters: two supersteps of 128 per batch");
+    static_assert(!PAIR || (POL == DQ_PER_GROUP && (U == 2 || U == 4 || U == 8)),
+                  "grouped parameters: 2, 4 or 8 supersteps of 128 per batch, one load of 4, 8 or 16 bytes");
     constexpr int NT = kWqDecodeWaves * kWave;
     constexpr int BK = U * kWqSuper;       // k per batch
     constexpr int ROWB = BK * 2 + 32;      // LDS bytes per staged x1 row (a 32-byte pad, see below)
@@ -261,13 +294,17 @@ __global__ __launch_bounds__(kWqDecodeWaves * kWave) void wq_decode_kernel(const
         s_chan[t] = 0.0f;
         o_chan[t] = 0.0f;
     }
+    bool chan_fma = false;  // per-tensor or per-channel: every column's parameters pass fma_exact
     if constexpr (POL != DQ_PER_GROUP) {
+        bool ok = true;
 #pragma unroll
         for (int t = 0; t < RN; ++t) {
             const int64_t p = param_index<POL>(a, col[t], 0, true);
             s_chan[t] = t_to_f32<XT>(a.scale[p]);
             o_chan[t] = OFF ? t_to_f32<XT>(a.offset[p]) : 0.0f;
+            ok = ok && fma_exact<WT, XT>(o_chan[t], s_chan[t], o_chan[t] * s_chan[t]);
         }
+        chan_fma = __all(ok);
     }
     const __amdgpu_buffer_rsrc_t srs = make_rsrc(a.scale, static_cast<uint32_t>(a.n * a.groups * 2));
     const __amdgpu_buffer_rsrc_t ors = make_rsrc(OFF ? a.offset : a.scale, static_cast<uint32_t>(a.n * a.groups * 2));
@@ -303,16 +340,15 @@ __global__ __launch_bounds__(kWqDecodeWaves * kWave) void wq_decode_kernel(const
         if constexpr (PAIR) {
 #pragma unroll
             for (int t = 0; t < RN; ++t) {
-                const uint32_t pi = static_cast<uint32_t>(col[t] * a.groups) + kb / kWqSuper;  // even
-                const uint32_t sv = __builtin_amdgcn_raw_buffer_load_b32(srs, pi * 2, 0, 0);
-                sg[0][t] = t_to_f32<XT>(static_cast<uint16_t>(sv));
-                sg[1][t] = t_to_f32<XT>(static_cast<uint16_t>(sv >> 16));
-                if constexpr (OFF) {
-                    const uint32_t ov = __builtin_amdgcn_raw_buffer_load_b32(ors, pi * 2, 0, 0);
-                    og[0][t] = t_to_f32<XT>(static_cast<uint16_t>(ov));
-                    og[1][t] = t_to_f32<XT>(static_cast<uint16_t>(ov >> 16));
-                } else {
-                    og[0][t] = og[1][t] = 0.0f;
+                const uint32_t pi = static_cast<uint32_t>(col[t] * a.groups) + kb / kWqSuper;  // a multiple of U
+                uint32_t sv[U / 2], ov[U / 2];
+                buf_load_words<U / 2>(srs, pi * 2, sv);
+                if constexpr (OFF)
+                    buf_load_words<U / 2>(ors, pi * 2, ov);
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    sg[u][t] = t_to_f32<XT>(static_cast<uint16_t>(sv[u / 2] >> (16 * (u % 2))));
+                    og[u][t] = OFF ? t_to_f32<XT>(static_cast<uint16_t>(ov[u / 2] >> (16 * (u % 2)))) : 0.0f;
                 }
             }
         }
@@ -355,7 +391,27 @@ __global__ __launch_bounds__(kWqDecodeWaves * kWave) void wq_decode_kernel(const
                     of = og[u][t];
                 }
                 uint4 bv[4];
-                if constexpr (WT == WQ_I4 && OFF) {
+                // The test is wave-uniform, so the slower exact paths below
+                // are a scalar branch taken only when some lane needs them.
+                bool use_fma = false;
+                float os = 0.0f;
+                if constexpr (OFF) {
+                    os = of * sc;
+                    use_fma = POL == DQ_PER_GROUP ? __all(fma_exact<WT, XT>(of, sc, os)) : chan_fma;
+                }
+                if (use_fma) {
+                    // int4 decodes to 16 code, and s / 16 is exact.
+                    const float s_eff = WT == WQ_I4 ? sc * 0.0625f : sc;
+#pragma unroll
+                    for (int s2 = 0; s2 < 4; ++s2) {
+                        float v[8], wv[8];
+                        decode8<WT>(w[u][t][0], w[u][t][WV - 1], s2, v);
+#pragma unroll
+                        for (int j = 0; j < 8; ++j)
+                            wv[j] = __builtin_fmaf(v[j], s_eff, os);
+                        bv[s2] = pack8_t<XT>(wv);
+                    }
+                } else if constexpr (WT == WQ_I4 && OFF) {
                     // v = 16 code: RN(v + 16 o) = 16 RN(code + o) and s / 16 is
                     // exact, so RN(RN(v + 16 o) * (s / 16)) is the formula,
                     // unless 16 o overflows (|o| near the binary32 limit).
@@ -398,7 +454,8 @@ __global__ __launch_bounds__(kWqDecodeWaves * kWave) void wq_decode_kernel(const
     };
 
     // Two register sets and two LDS buffers alternate: batch b + 1 is loaded
-    // while batch b is computed.  nb is uniform (no batch when k is empty).
+    // while batch b is computed (two or three batches ahead measured slower).
+    // nb is uniform (no batch when k is empty).
     if (nb > 0) {
         uint4 wA[U][RN][WV], wB[U][RN][WV];
         float sA[U][RN], oA[U][RN], sB[U][RN], oB[U][RN];
@@ -804,9 +861,10 @@ hipError_t launch_decode(const WqArgs& a, int splits, hipStream_t stream)
     const int64_t cols = static_cast<int64_t>(kWqDecodeWaves) * 16 * RN;
     const int64_t gx = (a.n + cols - 1) / cols;
     const dim3 grid(static_cast<uint32_t>(gx), 1, static_cast<uint32_t>(splits));
-    // Batch starts (k_chunk is a multiple of the batch) fall on even groups.
-    if constexpr (POL == DQ_PER_GROUP && U == 2) {
-        if (a.group_size == kWqSuper && a.groups % 2 == 0 && a.k_chunk % (U * kWqSuper) == 0)
+    // Batch starts (k_chunk is a multiple of the batch) fall on multiples
+    // of U groups.
+    if constexpr (POL == DQ_PER_GROUP && (U == 2 || U == 4 || U == 8)) {
+        if (a.group_size == kWqSuper && a.groups % U == 0 && a.k_chunk % (U * kWqSuper) == 0)
             hipLaunchKernelGGL((wq_decode_kernel<XT, WT, POL, OFF, RN, U, true>), grid, dim3(kWqDecodeWaves * kWave),
                                0, stream, a);
         else
@@ -878,7 +936,7 @@ template <int XT, int WT, int POL, bool OFF>
 hipError_t pick_tile(const WqPlan& p, const WqArgs& a, hipStream_t stream)
 {
     if (p.tile == WQ_TILE_DECODE)
-        return launch_decode<XT, WT, POL, OFF, kWqDecodeCols, wq_batch(WQ_TILE_DECODE)>(a, p.splits, stream);
+        return launch_decode<XT, WT, POL, OFF, kWqDecodeCols, wq_batch(WQ_TILE_DECODE, WT)>(a, p.splits, stream);
     return launch_gemm<XT, WT, POL, OFF>(a, p.splits, stream);
 }
 

@@ -169,6 +169,59 @@ def test_wq_identity_group128_windows(orc, weight, offset):
     assert np.array_equal(got, W), f"{int((got != W).sum())} of {W.size} weights differ"
 
 
+@pytest.mark.parametrize("dtype", ["bfloat16", "float16"])
+@pytest.mark.parametrize("weight", ["int8", "int4"])
+@pytest.mark.parametrize("kind,gs", [("tensor", 0), ("channel", 0), ("group", 64), ("group", 128)])
+@pytest.mark.parametrize("offset", [True, False])
+@pytest.mark.parametrize("wide", [False, True])
+def test_wq_decode_exposes_weight(orc, dtype, weight, kind, gs, offset, wide):
+    """At most 16 rows (the decode kernel): row i of x1 is the unit vector
+    e_(16 b + i), so one call returns rows 16 b .. 16 b + 15 of W exactly and
+    k / 16 calls return all of it, bit for bit against the oracle's
+    dequantized W.  wide = True spreads the parameters over the type's
+    range (bf16: offsets from 2^-20 to 2^126, where 16 o overflows
+    binary32, and scales down to 2^-126; fp16: offsets from the subnormals
+    to 2^15, scales down to the subnormals), on both sides of the bounds
+    where the kernel takes offset and scale in one FMA, keeping every
+    weight finite: a zero of x1 times an infinite weight would be NaN."""
+    announce("wq decode exposes weight", dtype, weight, kind, gs, offset, wide)
+    k, n = 512, 80
+    q = synth.wq_inputs(16, k, n, 4700 + gs, dtype=dtype, weight=weight, group_size=gs,
+                        per_tensor=kind == "tensor", offset=offset, bias=False)
+    if wide:
+        g = torch.Generator().manual_seed(4711 + gs)
+        shape = q["scale"].shape
+        fp16 = dtype == "float16"
+        # Exponents: |W| stays below 2^15 (fp16) or 2^70 (bf16) for |code| <= 128.
+        e_o = torch.empty(shape).uniform_(-16.0 if fp16 else -20.0, 15.0 if fp16 else 126.0, generator=g).floor()
+        if q["offset"] is None:
+            e_o = torch.zeros(shape)
+        e_s = torch.empty(shape).uniform_(-20.0 if fp16 else -60.0, 7.0 if fp16 else 60.0, generator=g).floor()
+        e_s = (e_s - e_o.clamp(min=0.0)).clamp(-24.0 if fp16 else -126.0, 14.0 if fp16 else 120.0)
+        mant = 1.0 + torch.rand(shape, generator=g)
+        sgn = torch.where(torch.rand(shape, generator=g) < 0.5, -1.0, 1.0)
+        q["scale"] = (sgn * mant * torch.exp2(e_s)).to(q["scale"].dtype)
+        if q["offset"] is not None:
+            mo = 1.0 + torch.rand(shape, generator=g)
+            so = torch.where(torch.rand(shape, generator=g) < 0.5, -1.0, 1.0)
+            q["offset"] = (so * mo * torch.exp2(e_o)).to(q["offset"].dtype)
+    d = {key: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for key, v in q.items()}
+    import int4_quantization_amd as dq
+    from parity import wq_oracle_args
+    x2, policy = wq_oracle_args(q)
+    W = orc.weight_dequant(x2, q["scale"], q["offset"], policy, gs, True)
+    eye = torch.eye(k, dtype=q["x1"].dtype)
+    got = np.empty_like(W)
+    for b in range(k // 16):
+        x1 = eye[16 * b:16 * b + 16].contiguous().to(DEV)
+        out = dq.weight_quant_matmul(x1, d["x2"], d["scale"], d["offset"], gs, None, None, True, weight)
+        got[16 * b:16 * b + 16] = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    # A weight of -0 (code 0 under a negative scale) sums to +0 with the
+    # zero products of the other k, so zeros compare without their sign.
+    zero = lambda a: np.where((a & 0x7FFF) == 0, 0, a)
+    assert np.array_equal(zero(got), zero(W)), f"{int((zero(got) != zero(W)).sum())} of {W.size} weights differ"
+
+
 def test_wq_split_k_deterministic():
     """Two calls give identical bits (the split sums are added in order)."""
     announce("wq split k determinism")
