@@ -309,7 +309,7 @@ KERNEL_SOURCES = {
     "ada_layernorm_quant": ("ada_layernorm_quant.hip", "dq_device.h", "dq_div.h", "dq_internal.h"),
     "antiquantize": ("antiquantize.hip", "dq_device.h", "dq_div.h", "dq_internal.h"),
     "mx_quantize": ("mx_quantize.hip", "dq_device.h", "dq_div.h", "dq_ext_internal.h"),
-    "weight_quant_matmul": ("weight_quant_matmul.hip", "dq_device.h", "dq_div.h", "dq_ext_internal.h"),
+    "weight_quant_matmul": ("weight_quant_matmul.hip", "wq_fma.h", "dq_device.h", "dq_div.h", "dq_ext_internal.h"),
 }
 
 
