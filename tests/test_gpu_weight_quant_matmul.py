@@ -174,18 +174,20 @@ def test_wq_identity_group128_windows(orc, weight, offset):
 @pytest.mark.parametrize("kind,gs", [("tensor", 0), ("channel", 0), ("group", 64), ("group", 128)])
 @pytest.mark.parametrize("offset", [True, False])
 @pytest.mark.parametrize("wide", [False, True])
-def test_wq_decode_exposes_weight(orc, dtype, weight, kind, gs, offset, wide):
+@pytest.mark.parametrize("k", [512, 576])
+def test_wq_decode_exposes_weight(orc, dtype, weight, kind, gs, offset, wide, k):
     """At most 16 rows (the decode kernel): row i of x1 is the unit vector
     e_(16 b + i), so one call returns rows 16 b .. 16 b + 15 of W exactly and
     k / 16 calls return all of it, bit for bit against the oracle's
-    dequantized W.  wide = True spreads the parameters over the type's
+    dequantized W.  k = 576 ends in a partial batch, whose lanes past k
+    take clamped weights and parameters.  wide = True spreads the parameters over the type's
     range (bf16: offsets from 2^-20 to 2^126, where 16 o overflows
     binary32, and scales down to 2^-126; fp16: offsets from the subnormals
     to 2^15, scales down to the subnormals), on both sides of the bounds
     where the kernel takes offset and scale in one FMA, keeping every
     weight finite: a zero of x1 times an infinite weight would be NaN."""
-    announce("wq decode exposes weight", dtype, weight, kind, gs, offset, wide)
-    k, n = 512, 80
+    announce("wq decode exposes weight", dtype, weight, kind, gs, offset, wide, k)
+    n = 80
     q = synth.wq_inputs(16, k, n, 4700 + gs, dtype=dtype, weight=weight, group_size=gs,
                         per_tensor=kind == "tensor", offset=offset, bias=False)
     if wide:
