@@ -35,6 +35,13 @@ namespace {
 enum AqPolicyKind : int { PK_TENSOR = 0, PK_CHANNEL = 1, PK_TOKEN = 2, PK_GROUP_N = 3, PK_GROUP_M = 4 };
 
 constexpr int kAqRowsPerThread = 8;  // PER_CHANNEL / PER_GROUP kDim = 0 (divides every groupSize)
+constexpr int kAqGroupNUnits = 2;    // work units per thread with groups along n
+
+// Work units per thread: two for groups along n (see aq_kernel), else one.
+constexpr int aq_units_per_thread(int pk)
+{
+    return pk == PK_GROUP_N ? kAqGroupNUnits : 1;
+}
 
 struct AqArgs {
     const void* src;
@@ -281,60 +288,76 @@ __global__ __launch_bounds__(kBlock) void aq_kernel(AqArgs a)
     uint8_t* dst = static_cast<uint8_t*>(a.dst);
 
     // Work unit u = (row block, chunk); a thread past the end repeats the
-    // last unit (same bytes).
-    uint32_t u = blockIdx.x * kBlock + threadIdx.x;
-    u = u < a.units ? u : a.units - 1;
-    const uint32_t rb = div_by(u, a.by_cpr);
-    const uint32_t jc = u - rb * a.cpr;  // chunk within the row
-    const int64_t j = static_cast<int64_t>(jc) * E;
-    const int64_t i0 = a.row0 + static_cast<int64_t>(rb) * R;
-
-    // Source loads first, then the parameters: all are in flight together.
+    // last unit (same bytes).  A thread takes CPT units kBlock apart, so a
+    // workgroup covers kBlock * CPT consecutive units: with groups along n,
+    // 4096 elements, whose parameters (32 groups of 128 at 4 bytes) fill
+    // whole 128-byte lines that no other workgroup reads.
+    constexpr int CPT = aq_units_per_thread(PK);
     const int64_t src_row = a.n / E * SB;  // source bytes per row
-    uint32_t raw[R][W];
+    uint32_t rb[CPT], jc[CPT];
+    int64_t i0[CPT];
+    uint32_t raw[CPT][R][W];
+    // Source loads first, then the parameters: all are in flight together.
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-        int64_t i = i0 + r;
-        i = i < a.row0 + a.rows ? i : a.row0 + a.rows - 1;  // past the end: repeat the last row
-        load_chunk<W>(raw[r], src + i * src_row + static_cast<int64_t>(jc) * SB);
+    for (int c = 0; c < CPT; ++c) {
+        uint32_t u = blockIdx.x * (kBlock * CPT) + c * kBlock + threadIdx.x;
+        u = u < a.units ? u : a.units - 1;
+        rb[c] = div_by(u, a.by_cpr);
+        jc[c] = u - rb[c] * a.cpr;  // chunk within the row
+        i0[c] = a.row0 + static_cast<int64_t>(rb[c]) * R;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            int64_t i = i0[c] + r;
+            i = i < a.row0 + a.rows ? i : a.row0 + a.rows - 1;  // past the end: repeat the last row
+            load_chunk<W>(raw[c][r], src + i * src_row + static_cast<int64_t>(jc[c]) * SB);
+        }
     }
 
-    float sv[E], ov[E];
-    if constexpr (UNI && PK == PK_TOKEN) {
-        const int64_t p = a.row0 + static_cast<int64_t>(__builtin_amdgcn_readfirstlane(rb));
-        const float s1 = param1_scalar_f32(a.scale, p);
-        const float o1 = OFF ? param1_scalar_f32(a.offset, p) : 0.0f;
+    float sv[CPT][E], ov[CPT][E];
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-            sv[e] = s1;
-            ov[e] = o1;
-        }
-    } else if constexpr (PK == PK_TENSOR || PK == PK_TOKEN || PK == PK_GROUP_N) {
-        int64_t p = 0;
-        if (PK == PK_TOKEN)
-            p = i0;
-        if (PK == PK_GROUP_N)
-            p = i0 * a.n_groups + div_by(jc, a.by_gsc);
-        const float s1 = param1<P>(a.scale, p);
-        const float o1 = OFF ? param1<P>(a.offset, p) : 0.0f;
+    for (int c = 0; c < CPT; ++c) {
+        const int64_t j = static_cast<int64_t>(jc[c]) * E;
+        if constexpr (UNI && PK == PK_TOKEN) {
+            const int64_t p = a.row0 + static_cast<int64_t>(__builtin_amdgcn_readfirstlane(rb[c]));
+            const float s1 = param1_scalar_f32(a.scale, p);
+            const float o1 = OFF ? param1_scalar_f32(a.offset, p) : 0.0f;
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-            sv[e] = s1;
-            ov[e] = o1;
+            for (int e = 0; e < E; ++e) {
+                sv[c][e] = s1;
+                ov[c][e] = o1;
+            }
+        } else if constexpr (PK == PK_TENSOR || PK == PK_TOKEN || PK == PK_GROUP_N) {
+            int64_t p = 0;
+            if (PK == PK_TOKEN)
+                p = i0[c];
+            if (PK == PK_GROUP_N)
+                p = i0[c] * a.n_groups + div_by(jc[c], a.by_gsc);
+            const float s1 = param1<P>(a.scale, p);
+            const float o1 = OFF ? param1<P>(a.offset, p) : 0.0f;
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                sv[c][e] = s1;
+                ov[c][e] = o1;
+            }
+        } else {
+            // The R rows share the group: R divides groupSize and the row
+            // blocks start at multiples of R.
+            const int64_t base =
+                PK == PK_GROUP_M ? static_cast<int64_t>(div_by(static_cast<uint32_t>(i0[c]), a.by_gs)) * a.n : 0;
+            param_vec<E, P>(a.scale, base + j, sv[c]);
+            if (OFF)
+                param_vec<E, P>(a.offset, base + j, ov[c]);
         }
-    } else {
-        // The R rows share the group: R divides groupSize and the row
-        // blocks start at multiples of R.
-        const int64_t base = PK == PK_GROUP_M ? static_cast<int64_t>(div_by(static_cast<uint32_t>(i0), a.by_gs)) * a.n : 0;
-        param_vec<E, P>(a.scale, base + j, sv);
-        if (OFF)
-            param_vec<E, P>(a.offset, base + j, ov);
     }
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-        int64_t i = i0 + r;
-        i = i < a.row0 + a.rows ? i : a.row0 + a.rows - 1;
-        convert_store<SRC, DST, OFF>(raw[r], sv, ov, dst + (i * a.n + j) * out_elem);
+    for (int c = 0; c < CPT; ++c) {
+        const int64_t j = static_cast<int64_t>(jc[c]) * E;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            int64_t i = i0[c] + r;
+            i = i < a.row0 + a.rows ? i : a.row0 + a.rows - 1;
+            convert_store<SRC, DST, OFF>(raw[c][r], sv[c], ov[c], dst + (i * a.n + j) * out_elem);
+        }
     }
 }
 
@@ -456,7 +479,8 @@ hipError_t launch_antiquantize(const AqPlan& p, hipStream_t stream)
         a.rows = p.m - row0 < max_rows ? p.m - row0 : max_rows;
         const int64_t units = (a.rows + R - 1) / R * cpr;
         a.units = static_cast<uint32_t>(units);
-        const int64_t blocks = (units + kBlock - 1) / kBlock;
+        const int64_t per_block = kBlock * aq_units_per_thread(pk);
+        const int64_t blocks = (units + per_block - 1) / per_block;
         void* args[] = {&a};
         const hipError_t err = hipLaunchKernel(reinterpret_cast<const void*>(fn),
                                                dim3(static_cast<uint32_t>(blocks)), dim3(kBlock), args, 0, stream);
