@@ -141,8 +141,10 @@ def test_wq_group128_windows(orc, m, k, n, weight, offset, dtype):
                                                        (3, 2048, 200, "int4", False, "bfloat16"),
                                                        (9, 8192, 72, "int8", True, "float16")])
 def test_wq_decode_paired_groups(orc, m, k, n, weight, offset, dtype):
-    """At most 16 rows with groups of 128 and an even group count: the decode
-    kernel loads the two parameter groups of a batch with one load."""
+    """At most 16 rows with groups of 128 and a group count that is a
+    multiple of the batch (4 supersteps for int4, 2 for int8): the decode
+    kernel loads all parameter groups of a batch with one load.  The small
+    n splits k, so each split starts on a batch boundary."""
     announce("wq decode paired groups", m, k, n, weight, offset, dtype)
     q = synth.wq_inputs(m, k, n, 5300 + m, dtype=dtype, weight=weight, group_size=128, offset=offset, bias=True,
                         x3=True)
