@@ -44,6 +44,10 @@ ROTATE_BYTES = 1 << 30       # buffer-set rotation footprint (> 4x the 256 MB MA
 ISOLATED_LAUNCHES = 100      # individually event-timed launches for p10/p50/p90 (any --steps)
 EXTRA_MIN_STEPS = 200        # timed launches of each non-headline workload, at least
 EXTRA_MIN_WARMUP = 20
+# ... and after at least this long of back-to-back launches: after idling
+# (each workload's inputs are generated on the host first) the chip takes
+# about 20 ms of load to settle, and kernels run 5-20% slower meanwhile.
+EXTRA_MIN_WARMUP_S = 0.06
 HEADLINE = "dq_sym_smooth_bf16_8192x7168"
 METRIC = "achieved HBM GB/s (% of peak) + rows/s, per-token bf16→int8 dynamic quant"
 
@@ -229,17 +233,24 @@ def make_work(name, dev) -> Work:
     return Work(name, op, builder(), dev)
 
 
-def time_work(w: Work, steps: int, warmup: int):
+def time_work(w: Work, steps: int, warmup: int, min_warmup_s: float = 0.0):
     """Warm up, then time exactly `steps` back-to-back launches between two
     synchronizations: wall time on the host, and a HIP event pair recorded on
     the launch stream around the same launches (its mean is the kernel's
     average launch duration: the queue stays full, so gaps are only the
     hardware dispatch between kernels).  A second, untimed pass brackets
     each launch with its own events for the latency distribution
-    (ISOLATED_LAUNCHES of them, whatever `steps` is)."""
+    (ISOLATED_LAUNCHES of them, whatever `steps` is).  With min_warmup_s the
+    warm-up continues in groups of 20 launches until that long has passed."""
     for i in range(warmup):
         w.launch(i)
     torch.cuda.synchronize()
+    t_warm = time.perf_counter()
+    while time.perf_counter() - t_warm < min_warmup_s:
+        for _ in range(20):
+            w.launch(warmup)
+            warmup += 1
+        torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -418,8 +429,9 @@ def main():
     print(f"# copy ceiling {ceiling:.0f} GB/s", file=sys.stderr, flush=True)
 
     # The other workloads are context, not the headline: each is timed over
-    # at least EXTRA_MIN_STEPS launches after at least EXTRA_MIN_WARMUP, so a
-    # short headline run does not leave them with a few noisy launches.
+    # at least EXTRA_MIN_STEPS launches after at least EXTRA_MIN_WARMUP and
+    # EXTRA_MIN_WARMUP_S of warm-up, so a short headline run does not leave
+    # them with a few noisy launches taken while the chip settles.
     extra_steps = max(args.steps, EXTRA_MIN_STEPS)
     extra_warmup = max(args.warmup, EXTRA_MIN_WARMUP)
     extra = {}
@@ -428,7 +440,7 @@ def main():
             if name == HEADLINE:
                 continue
             wk = make_work(name, dev)
-            wl, rg, lt = time_work(wk, extra_steps, extra_warmup)
+            wl, rg, lt = time_work(wk, extra_steps, extra_warmup, EXTRA_MIN_WARMUP_S)
             extra[name] = summarize(wk, wl, rg, lt, extra_steps)
             wk.free()
             torch.cuda.empty_cache()
@@ -463,6 +475,7 @@ def main():
         "cpu_baseline": cpu,
         "copy_ceiling_gbps": round(ceiling, 1),
         "extra_workloads_steps": extra_steps,
+        "extra_workloads_min_warmup_s": EXTRA_MIN_WARMUP_S,
         "headline_detail": head,
         "workloads": extra,
     }
