@@ -58,7 +58,16 @@ struct AqArgs {
     DivMagic by_cpr;    // division by cpr
     DivMagic by_gsc;    // division by gs / E (chunks per group, kDim = 1)
     DivMagic by_gs;     // division by gs (rows per group, kDim = 0)
+    uint32_t tiles_c;      // per channel in 2-D tiles: column tiles of kAqTileChunks chunks (0: flat order)
+    DivMagic by_tiles_c;   // division by tiles_c
 };
+
+// Per channel with a row of whole column tiles: a workgroup takes
+// kAqTileChunks chunks of kAqTileRowBlocks row blocks (64 x 4, 32 rows),
+// wave w the tile's chunks 16 w .. 16 w + 15 in its 4 row blocks.  Each wave
+// then loads the parameters of 16 chunks, not 64, and still reads whole
+// 128-byte source lines and writes 256-byte output segments per row.
+constexpr int kAqTileChunks = 64, kAqTileRowBlocks = 4;
 
 template <int SRC, int DST>
 struct Chunk {
@@ -301,6 +310,13 @@ __global__ __launch_bounds__(kBlock) void aq_kernel(AqArgs a)
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
         uint32_t u = blockIdx.x * (kBlock * CPT) + c * kBlock + threadIdx.x;
+        if (PK == PK_CHANNEL && a.tiles_c) {  // uniform
+            static_assert(kBlock == 4 * kWave && kAqTileChunks == 4 * 16 && kAqTileRowBlocks * 16 == kWave,
+                          "four waves of 16 chunks x 4 row blocks");
+            const uint32_t tr = div_by(blockIdx.x, a.by_tiles_c), tc = blockIdx.x - tr * a.tiles_c;
+            const uint32_t wv = threadIdx.x / kWave, ln = threadIdx.x % kWave;
+            u = (tr * kAqTileRowBlocks + ln / 16) * a.cpr + tc * kAqTileChunks + wv * 16 + ln % 16;
+        }
         u = u < a.units ? u : a.units - 1;
         rb[c] = div_by(u, a.by_cpr);
         jc[c] = u - rb[c] * a.cpr;  // chunk within the row
@@ -480,7 +496,14 @@ hipError_t launch_antiquantize(const AqPlan& p, hipStream_t stream)
         const int64_t units = (a.rows + R - 1) / R * cpr;
         a.units = static_cast<uint32_t>(units);
         const int64_t per_block = kBlock * aq_units_per_thread(pk);
-        const int64_t blocks = (units + per_block - 1) / per_block;
+        int64_t blocks = (units + per_block - 1) / per_block;
+        a.tiles_c = 0;
+        if (pk == PK_CHANNEL && cpr % kAqTileChunks == 0) {
+            const int64_t row_blocks = (a.rows + R - 1) / R;
+            a.tiles_c = static_cast<uint32_t>(cpr / kAqTileChunks);
+            a.by_tiles_c = div_magic(a.tiles_c);
+            blocks = (row_blocks + kAqTileRowBlocks - 1) / kAqTileRowBlocks * a.tiles_c;
+        }
         void* args[] = {&a};
         const hipError_t err = hipLaunchKernel(reinterpret_cast<const void*>(fn),
                                                dim3(static_cast<uint32_t>(blocks)), dim3(kBlock), args, 0, stream);
