@@ -61,6 +61,26 @@ def test_antiquantize_scalar_parameter_path(orc, policy, gs, n, dst, with_offset
     q = synth.aq_inputs(37, n, policy, 500 + gs + n, kdim=1, group_size=gs or 128, offset=with_offset)
     check_antiquantize(orc, q["src"], q["scale"], q["offset"], policy, 1, q["group_size"], dst)
 
+
+# PER_CHANNEL in 2-D tiles (64 chunks x 32 rows per workgroup): n a multiple
+# of 512 (256 for fp32 output); 37 and 100 rows leave a partial last row tile,
+# 4608 columns an odd number of column tiles.
+TILE_SHAPES = [(37, 2048), (100, 1536), (37, 4608)]
+
+
+TILE_TYPES = [("float32", torch.bfloat16), ("float32", torch.float16), ("float32", torch.float32),
+              ("bfloat16", torch.bfloat16), ("bfloat16", torch.float32)]
+
+
+@pytest.mark.parametrize("m,n", TILE_SHAPES, ids=[f"{m}x{n}" for m, n in TILE_SHAPES])
+@pytest.mark.parametrize("pdt,dst", TILE_TYPES, ids=["f32-bf16", "f32-f16", "f32-f32", "bf16-bf16", "bf16-f32"])
+@pytest.mark.parametrize("with_offset", [True, False], ids=["offset", "no_offset"])
+def test_antiquantize_per_channel_tiles(orc, m, n, pdt, dst, with_offset):
+    announce("antiquantize per-channel tiles", m, n, dst, pdt, with_offset)
+    q = synth.aq_inputs(m, n, "per_channel", 700 + m + n, kdim=1, offset=with_offset, param_dtype=pdt)
+    check_antiquantize(orc, q["src"], q["scale"], q["offset"], "per_channel", 1, q["group_size"], dst)
+
+
 FP4_CASES = [(1, 32), (1, 96), (0, 32), (0, 64)]
 
 
