@@ -295,14 +295,20 @@ def summarize(w: Work, wall: float, region: float, lat: np.ndarray, steps: int) 
     }
 
 
-def copy_ceiling(dev, steps: int = 50) -> float:
-    """Plain device copy of 512 MiB (read + write = 1 GiB of traffic)."""
+def copy_ceiling(dev, steps: int = 50, min_warmup_s: float = 0.0) -> float:
+    """Plain device copy of 512 MiB (read + write = 1 GiB of traffic), timed
+    after at least min_warmup_s of back-to-back copies."""
     nb = 512 << 20
     src = torch.empty(nb, dtype=torch.uint8, device=dev).random_(0, 255)
     dst = torch.empty_like(src)
     for _ in range(5):
         dq.dq_copy_probe(dst, src)
     torch.cuda.synchronize()
+    t_warm = time.perf_counter()
+    while time.perf_counter() - t_warm < min_warmup_s:
+        for _ in range(20):
+            dq.dq_copy_probe(dst, src)
+        torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
     for _ in range(steps):
@@ -409,7 +415,7 @@ def main():
     dev = torch.device("cuda:0")
 
     if args.copy_only:
-        print(json.dumps({"copy_ceiling_gbps": round(copy_ceiling(dev, args.steps), 1),
+        print(json.dumps({"copy_ceiling_gbps": round(copy_ceiling(dev, args.steps, EXTRA_MIN_WARMUP_S), 1),
                           "bytes_per_launch": 2 * (512 << 20)}), flush=True)
         return
 
@@ -419,14 +425,19 @@ def main():
         print(json.dumps({"workload": args.only, **summarize(w, wall, region, lat, args.steps)}), flush=True)
         return
 
+    # The headline's buffers are filled first (host generation, copies), then
+    # the copy probe runs for at least EXTRA_MIN_WARMUP_S: it measures the
+    # copy ceiling and brings the idle chip to its loaded state, so the
+    # headline's W warm-up and K timed launches run under load as every
+    # other workload's do.  The headline itself still gets exactly W and K.
     w = make_work(HEADLINE, dev)
+    ceiling = copy_ceiling(dev, min_warmup_s=EXTRA_MIN_WARMUP_S)
+    print(f"# copy ceiling {ceiling:.0f} GB/s", file=sys.stderr, flush=True)
     wall, region, lat = time_work(w, args.steps, args.warmup)
     head = summarize(w, wall, region, lat, args.steps)
     w.free()
     print(f"# {HEADLINE}: {head['gbps_kernel']:.0f} GB/s ({head['pct_peak_kernel']:.1f}% of peak), "
           f"{head['us_mean']:.2f} us/launch", file=sys.stderr, flush=True)
-    ceiling = copy_ceiling(dev)
-    print(f"# copy ceiling {ceiling:.0f} GB/s", file=sys.stderr, flush=True)
 
     # The other workloads are context, not the headline: each is timed over
     # at least EXTRA_MIN_STEPS launches after at least EXTRA_MIN_WARMUP and

@@ -333,6 +333,7 @@ dq_status dq_dynamic_quant_get_workspace_size(const dq_tensor* x, const dq_tenso
                     p.variant = dq::DQ_VAR_TEAM;
                     p.vpl = v;
                     p.team = static_cast<int>(w);
+                    p.long_rows = !p.group_index && rows >= dq::kDqTeamLongMinRows;
                     break;
                 }
             }

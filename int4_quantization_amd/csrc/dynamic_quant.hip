@@ -413,12 +413,17 @@ __global__ __launch_bounds__(kDqWaves * kWave) void dq_vec_kernel(DqArgs a)
 // the vector variant's fixed teams of 1, 2 or 4 waves would leave lanes
 // holding duplicate vectors: bf16 [*, 7168] is 896 vectors, 7 waves of 2
 // per lane instead of 4 waves of 4 with 128 duplicates).  Each team converts
-// kDqTeamRows rows with the next row's loads in flight, then the workgroup
-// exits; rows are assigned as in the vector variant.
-template <int XT, bool SYM, int OUT, int VPL>
+// T rows with the next PD rows' loads in flight, then the workgroup exits;
+// rows are assigned as in the vector variant.  T = 4, PD = 1 in general;
+// long inputs without a group index take T = 16, PD = 2: about two
+// workgroups per compute unit, each with up to three rows of loads
+// outstanding (bf16 [8192, 7168]: 30.8-30.9 against 31.3-31.4 us in
+// interleaved runs; deeper prefetch measured slower: 31.5 us with PD = 3,
+// 32.2 with 4).
+template <int XT, bool SYM, int OUT, int VPL, int T, int PD>
 __global__ __launch_bounds__(kDqMaxTeam * kWave) void dq_team_kernel(DqArgs a)
 {
-    constexpr int T = kDqTeamRows;
+    constexpr int NB = PD + 1;  // row buffers
     const int lane = threadIdx.x & (kWave - 1);
     const int wit = threadIdx.x / kWave;
     const int team = blockDim.x / kWave;
@@ -435,7 +440,7 @@ __global__ __launch_bounds__(kDqMaxTeam * kWave) void dq_team_kernel(DqArgs a)
     if (moe)
         gi_lane = a.gi[lane < a.n_experts ? lane : a.n_experts - 1];
 
-    uint4 buf[2][VPL];
+    uint4 buf[NB][VPL];
     load_x<VPL>(buf[0], a.x, row_of(0), a.n, nvec, team, wit, lane);
 
     float sreg[VPL][8];
@@ -449,11 +454,15 @@ __global__ __launch_bounds__(kDqMaxTeam * kWave) void dq_team_kernel(DqArgs a)
     if (one_expert) {
         load_smooth<VPL>(sreg, a, e0, nvec, team, wit, lane);
 #pragma unroll
+        for (int t = 1; t < PD && t < T; ++t)
+            load_x<VPL>(buf[t % NB], a.x, row_of(t), a.n, nvec, team, wit, lane);
+#pragma unroll
         for (int t = 0; t < T; ++t) {
-            if (t + 1 < T)
-                load_x<VPL>(buf[(t + 1) & 1], a.x, row_of(t + 1), a.n, nvec, team, wit, lane);
+            if (t + PD < T)
+                load_x<VPL>(buf[(t + PD) % NB], a.x, row_of(t + PD), a.n, nvec, team, wit, lane);
             __builtin_amdgcn_sched_barrier(0);
-            convert_row<XT, SYM, OUT, VPL, kDqMaxTeam>(a, buf[t & 1], sreg, row_of(t), t, nvec, 0, team, wit, lane, red);
+            convert_row<XT, SYM, OUT, VPL, kDqMaxTeam>(a, buf[t % NB], sreg, row_of(t), t, nvec, 0, team, wit, lane,
+                                                       red);
         }
     } else {
         for (int t = 0; t < T; ++t) {
@@ -563,9 +572,10 @@ template <int XT, bool SYM, int OUT>
 KernelFn pick(const DqPlan& p)
 {
     if (p.variant == DQ_VAR_TEAM) {
+        constexpr int TL = kDqTeamRowsLong, PL = kDqTeamPrefetchLong;
         switch (p.vpl) {
-        case 1: return dq_team_kernel<XT, SYM, OUT, 1>;
-        case 2: return dq_team_kernel<XT, SYM, OUT, 2>;
+        case 1: return p.long_rows ? dq_team_kernel<XT, SYM, OUT, 1, TL, PL> : dq_team_kernel<XT, SYM, OUT, 1, kDqTeamRows, 1>;
+        case 2: return p.long_rows ? dq_team_kernel<XT, SYM, OUT, 2, TL, PL> : dq_team_kernel<XT, SYM, OUT, 2, kDqTeamRows, 1>;
         }
         return nullptr;
     }
@@ -600,7 +610,7 @@ hipError_t launch_dynamic_quant(const DqPlan& p, hipStream_t stream)
         return hipErrorInvalidValue;
     DqArgs a{p.x, p.smooth, p.group_index, p.n_experts, p.rows, p.n, p.y, p.scale, p.offset};
     // Vector variant: one workgroup per T * 4/TEAM rows; team variant: one
-    // per kDqTeamRows rows; generic: one per row.
+    // per kDqTeamRows (or kDqTeamRowsLong) rows; generic: one per row.
     int64_t rpb = 1;
     int threads = kBlock;
     if (p.variant == DQ_VAR_VECTOR) {
@@ -609,7 +619,9 @@ hipError_t launch_dynamic_quant(const DqPlan& p, hipStream_t stream)
     } else if (p.variant == DQ_VAR_TEAM) {
         if (p.team < 2 || p.team > kDqMaxTeam)
             return hipErrorInvalidValue;
-        rpb = kDqTeamRows;
+        if (p.long_rows && p.group_index)
+            return hipErrorInvalidValue;
+        rpb = p.long_rows ? kDqTeamRowsLong : kDqTeamRows;
         threads = p.team * kWave;
     }
     const int64_t blocks = (p.rows + rpb - 1) / rpb;

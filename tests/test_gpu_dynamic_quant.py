@@ -103,6 +103,49 @@ def test_dynamic_quant_arbitrary_group_index(orc, rows, n, experts, kind):
     check_dynamic_quant(orc, inp["x"], inp["smooth"], gi, experts % 2 == 1, "int8" if n % 2 else "int4")
 
 
+# Inputs of at least 8192 rows without a group index take the team variant's
+# long schedule (16 rows per team, two rows in flight ahead of the one being
+# converted): ragged row counts, teams of 5, 6, 7 and 14 waves.
+LONG_SHAPES = [(8192 + 37, 7168), (8192 + 5, 5120), (8200, 3072), (8192 + 15, 14336)]
+LONG_MODES = [(True, "int8", "vector"), (False, "int4", "none"), (False, "int8", "vector"),
+              (True, "int32", "none")]
+
+
+@pytest.mark.parametrize("rows,n", LONG_SHAPES)
+@pytest.mark.parametrize("sym,out,smooth", LONG_MODES)
+def test_dynamic_quant_long_team_schedule(orc, rows, n, sym, out, smooth):
+    announce("dynamic_quant long team schedule", rows, n, sym, out, smooth)
+    inp = synth.dq_inputs(rows, n, rows + n, smooth=None if smooth == "none" else "vector",
+                          outlier_frac=0.001)
+    check_dynamic_quant(orc, inp["x"], inp["smooth"], None, sym, out)
+
+
+def test_dynamic_quant_long_team_schedule_degenerate_rows(orc):
+    """Rows whose divisor leaves the fast range (zero, tiny, huge, overflowing)
+    spread over the long schedule's teams and steps."""
+    announce("dynamic_quant long team schedule degenerate")
+    rows, n = 8192 + 3, 7168
+    inp = synth.dq_inputs(rows, n, 4242, smooth="vector")
+    x = inp["x"].clone()
+    special = _special_rows(n)
+    for i, r in enumerate(range(1, rows, rows // (3 * special.shape[0]))):
+        x[r] = special[i % special.shape[0]]
+    x[rows - 1] = special[0]
+    for sym, out in ((True, "int8"), (False, "int8"), (False, "int4")):
+        check_dynamic_quant(orc, x, inp["smooth"], None, sym, out)
+        check_dynamic_quant(orc, x, None, None, sym, out)
+
+
+def test_dynamic_quant_long_moe_keeps_short_schedule(orc):
+    """MoE inputs of many rows keep 4 consecutive rows per team (they share
+    an expert's smooth row); parity across expert boundaries."""
+    announce("dynamic_quant long moe")
+    rows, n = 8192 + 21, 7168
+    inp = synth.dq_inputs(rows, n, 99, smooth="experts", experts=7)
+    check_dynamic_quant(orc, inp["x"], inp["smooth"], inp["group_index"], True, "int8")
+    check_dynamic_quant(orc, inp["x"], inp["smooth"], inp["group_index"], False, "int4")
+
+
 def _special_rows(n: int) -> torch.Tensor:
     rng = np.random.default_rng(5)
     rows = [
