@@ -36,6 +36,7 @@ enum WqVariant : int {
 enum WqTile : int {
     WQ_TILE_DECODE = 3,  // at most 16 rows: kWqDecodeCols blocks per wave, x1 staged in LDS
     WQ_TILE_GEMM = 4,    // more rows: 128 x 128 workgroup tiles, x1 and dequantized weights in LDS
+    WQ_TILE_WIDE = 5,    // many rows: 256 x 256 workgroup tiles, x1 in LDS, weights straight to the operands
 };
 
 struct WqPlan {
@@ -65,6 +66,11 @@ constexpr int kWqDecodeCols = 1;   // 16-column blocks per wave in the decode ke
 constexpr int kWqDecodeWaves = 4;  // waves per decode workgroup (they share one x1 staging)
 // LDS-tiled kernel: output tile and k-step (a divisor of kWqSuperK).
 constexpr int kWqGemmRows = 128, kWqGemmCols = 128, kWqGemmK = 128;
+// Wide kernel: output tile and k-step.  It is planned for at least 256 rows
+// when the 256 x 256 tiles alone give kWqWideMinTiles workgroups or more
+// (no k split), k is a multiple of two k-steps and the group size of one.
+constexpr int kWqWideRows = 256, kWqWideCols = 256, kWqWideK = 64;
+constexpr int64_t kWqWideMinTiles = 128;
 // Per-group parameters of the LDS-tiled kernel come in windows of this many
 // groups when groups are one k-step long; k splits are then planned in
 // multiples of the window.

@@ -849,12 +849,22 @@ dq_status plan_weight_quant_matmul(const dq_tensor* x1, const dq_tensor* x2, int
     p.variant = p.transpose_x2 && kfit && aligned(x1->data, 16) && aligned(x2->data, 16) ? dq::WQ_VAR_MFMA
                                                                                        : dq::WQ_VAR_GENERIC;
     p.tile = m <= 16 ? dq::WQ_TILE_DECODE : dq::WQ_TILE_GEMM;
+    if (p.variant == dq::WQ_VAR_MFMA && m >= dq::kWqWideRows && k % (2 * dq::kWqWideK) == 0 &&
+        (policy != DQ_PER_GROUP || group_size % dq::kWqWideK == 0)) {
+        const int64_t wide_tiles = ((n + dq::kWqWideCols - 1) / dq::kWqWideCols) *
+                                   ((m + dq::kWqWideRows - 1) / dq::kWqWideRows);
+        const int64_t groups = policy == DQ_PER_GROUP ? k / group_size : 1;
+        const int64_t kw = x2->dtype == DQ_I4 ? k / 2 : k;  // weight bytes per column
+        if (wide_tiles >= dq::kWqWideMinTiles && n * groups < (int64_t{1} << 31) &&
+            int64_t{dq::kWqWideRows} * k * 2 < (int64_t{1} << 31) && int64_t{dq::kWqWideCols} * kw < (int64_t{1} << 31))
+            p.tile = dq::WQ_TILE_WIDE;
+    }
     // Few output tiles: split k so that about the target number of
     // workgroups run; the binary32 partial sums [splits, m, n] live in the
     // workspace.
     p.splits = 1;
     p.k_chunk = k;
-    if (p.variant == dq::WQ_VAR_MFMA && m > 0) {  // m == 0 launches nothing
+    if (p.variant == dq::WQ_VAR_MFMA && m > 0 && p.tile != dq::WQ_TILE_WIDE) {  // m == 0 launches nothing
         const int64_t tiles = ((n + dq::wq_tile_cols(p.tile) - 1) / dq::wq_tile_cols(p.tile)) *
                               ((m + dq::wq_tile_rows(p.tile) - 1) / dq::wq_tile_rows(p.tile));
         const int64_t batch_k = static_cast<int64_t>(dq::wq_batch(p.tile, p.w_type)) * dq::kWqSuperK;

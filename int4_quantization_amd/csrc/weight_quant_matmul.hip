@@ -42,6 +42,7 @@
 // stored [k, n].
 
 #include <atomic>
+#include <type_traits>
 
 #include "dq_device.h"
 #include "dq_ext_internal.h"
@@ -855,6 +856,347 @@ __global__ __launch_bounds__(kBlock) void wq_reduce_kernel(const WqArgs a, int s
     a.out[idx] = f32_to_t<XT>(v);
 }
 
+// ---------------------------------------------------------------------------
+// Wide prefill kernel: a 256 x 256 output tile per workgroup of four waves.
+// Wave w owns the 64 columns 64 w .. 64 w + 63 over all 256 rows (8 x 2
+// blocks of 32 x 32 on v_mfma_f32_32x32x16, 256 binary32 sums per lane in
+// the accumulation registers), so each weight is loaded and dequantized by
+// exactly one wave, straight from global memory into the matrix-core
+// operand registers, and only x1 goes through LDS (double-buffered, one
+// barrier per k-step of 64).  Per k-step a wave runs 64 matrix-core
+// instructions (2048 cycles) against 32 KB of x1 operand reads per wave and
+// 32 KB of staging stores per workgroup: LDS time is about three quarters
+// of the matrix-core time, where the 128 x 128 tile above needs twice it.
+// (With 16 x 16 blocks the same tile left the compiler copying accumulators
+// between register files every step; 32 x 32 blocks keep them in place.)
+//
+// Operand layout of v_mfma_f32_32x32x16: lane l supplies row (or column)
+// l % 32 and 8 k values; it receives rows 8 j + 4 (l / 32) + i (j, i < 4) of
+// column l % 32.  k order inside a step: lane half h = l / 32 holds the 32
+// consecutive k of [32 h, 32 h + 32), slice s (of 4) taking the 8 k from
+// 32 h + 8 s, for x1 and for the weights alike, so a lane's weights of a
+// step are one contiguous run of its column (32 bytes of int8, 16 of int4).
+// x1 rows sit in LDS as 8 chunks of 8 k per row, chunk c of row r in slot
+// c ^ (r % 8): the staging stores (8 lanes on one row) and the operand
+// reads (8 lanes on 8 rows, one chunk) each touch 8 distinct 16-byte slots
+// of a 128-byte window, free of bank conflicts without padding.
+// ---------------------------------------------------------------------------
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+template <int XT>
+__device__ __forceinline__ f32x16 mfma32(const uint4& a, const uint4& b, const f32x16& c)
+{
+    if constexpr (XT == X_BF16)
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                       0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
+                                                      0, 0, 0);
+}
+
+template <int WT>
+struct WideRaw;
+template <>
+struct WideRaw<WQ_I8> {
+    uint4 lo, hi;  // 32 codes
+};
+template <>
+struct WideRaw<WQ_I4> {
+    uint4 lo;  // 32 codes
+};
+
+template <int XT, int WT, int POL, bool OFF>
+__global__ __launch_bounds__(kWave * 4, 1) void wq_wide_kernel(const WqArgs a)
+{
+    constexpr int BM = kWqWideRows, BN = kWqWideCols, BK = kWqWideK, NT = kWave * 4;
+    constexpr int RB = BM / 32;             // row blocks (all rows, every wave)
+    constexpr int CB = BN / 4 / 32;         // column blocks per wave
+    constexpr int SL = BK / 16;             // k slices per step
+    constexpr int AV = BM * (BK / 8) / NT;  // 16-byte x1 vectors staged per thread and step
+    constexpr int WSTEP = WT == WQ_I8 ? BK : BK / 2;  // weight bytes per column and step
+    constexpr int ER = 64 + 4;              // epilogue tile row (binary32), padded
+    constexpr int kStage = 2 * BM * (BK / 8) * 16, kEpi = 4 * 32 * ER * 4;
+    static_assert(AV * NT == BM * BK / 8 && AV == 8, "x1 tile divides over threads");
+    static_assert(RB == 8 && CB == 2 && SL == 4, "32 row-block iterations per step, 2 column blocks per wave");
+    __shared__ __align__(16) unsigned char smem[kStage > kEpi ? kStage : kEpi];
+    uint4* const As = reinterpret_cast<uint4*>(smem);  // [2][BM * 8] 16-byte chunks
+
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int li = lane % 32, h = lane / 32;
+    const int64_t m0 = static_cast<int64_t>(blockIdx.y) * BM;
+    const int64_t n0 = static_cast<int64_t>(blockIdx.x) * BN;
+    const int64_t k_beg = static_cast<int64_t>(blockIdx.z) * a.k_chunk;
+    const int64_t k_end = k_beg + a.k_chunk < a.k ? k_beg + a.k_chunk : a.k;
+    const int nk = static_cast<int>((k_end - k_beg) / BK);  // the host plans whole pairs of steps
+
+    // Buffer resources over this tile's x1 rows and weight columns (the host
+    // keeps 256 rows of x1 and 256 weight columns below 2^31 bytes): loads
+    // past the last row or column return zeros, whose results are not stored.
+    const int64_t kw = WT == WQ_I8 ? a.k : a.k / 2;  // weight bytes per column
+    const int64_t rows_left = a.m - m0 < BM ? a.m - m0 : BM, cols_left = a.n - n0 < BN ? a.n - n0 : BN;
+    const __amdgpu_buffer_rsrc_t xrs =
+        make_rsrc(a.x1 + m0 * a.k + k_beg, static_cast<uint32_t>((rows_left * a.k - k_beg) * 2));
+    const __amdgpu_buffer_rsrc_t wrs =
+        make_rsrc(a.x2 + n0 * kw + (k_beg / BK) * WSTEP, static_cast<uint32_t>(cols_left * kw - (k_beg / BK) * WSTEP));
+    // x1 vector p of thread tid: row tid / 8 + 32 p, chunk tid % 8.
+    const uint32_t a_off = static_cast<uint32_t>((tid / 8) * a.k * 2 + (tid % 8) * 16);
+    const uint32_t a_pstride = static_cast<uint32_t>(32 * a.k * 2);
+    const int a_slot = (tid / 16) % 8;  // (row / 2) % 8 of every staged row of this thread
+    // This lane's weight runs: column block cb is column 64 wave + 32 cb + li of the tile.
+    const uint32_t w_off = static_cast<uint32_t>((64 * wave + li) * kw + h * (WSTEP / 2));
+    const uint32_t w_cbstride = static_cast<uint32_t>(32 * kw);
+    // Parameter row offsets of this lane's columns (the host keeps n * groups
+    // below 2^31).
+    uint32_t prow[CB];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+        const int64_t c = n0 + 64 * wave + 32 * cb + li;
+        prow[cb] = static_cast<uint32_t>((c < a.n ? c : a.n - 1) * (POL == DQ_PER_GROUP ? a.groups : 1));
+    }
+
+    auto load_a = [&](int kt, uint4 (&ar)[AV]) {
+#pragma unroll
+        for (int p = 0; p < AV; ++p)
+            ar[p] = buf_load16<0>(xrs, a_off + p * a_pstride + static_cast<uint32_t>(kt) * (BK * 2));
+    };
+    auto store_a1 = [&](int buf, int p, const uint4 (&ar)[AV]) {
+        const int row = tid / 8 + 32 * p;
+        As[buf * (BM * 8) + row * 8 + ((tid % 8) ^ a_slot)] = ar[p];
+    };
+    auto load_w = [&](int kt, WideRaw<WT> (&wr)[CB]) {
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+            const uint32_t off = w_off + cb * w_cbstride + static_cast<uint32_t>(kt) * WSTEP;
+            wr[cb].lo = buf_load16<0>(wrs, off);
+            if constexpr (WT == WQ_I8)
+                wr[cb].hi = buf_load16<0>(wrs, off + 16);
+        }
+    };
+    // Per-group parameters of step kt (groups are whole steps long), kept as
+    // their T bits until the dequantization that uses them, so the loads are
+    // not waited for where they are issued.
+    auto load_p = [&](int kt, uint32_t (&sp)[CB], uint32_t (&op)[CB]) {
+        const uint32_t grp = div_by(static_cast<uint32_t>(k_beg + static_cast<int64_t>(kt) * BK), a.by_gs);
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+            const uint32_t pi = prow[cb] + grp;
+            sp[cb] = a.scale[pi];
+            op[cb] = OFF ? a.offset[pi] : 0u;
+        }
+    };
+
+    // Parameters (T bits) of the steps held in the two weight sets (per
+    // group), or of every step (per tensor, per channel: set 0 only).
+    constexpr int PS = POL == DQ_PER_GROUP ? 2 : 1;
+    uint32_t sp[PS][CB], op[PS][CB];
+    if constexpr (POL != DQ_PER_GROUP) {
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+            const uint32_t pi = POL == DQ_PER_TENSOR ? 0u : prow[cb];
+            sp[0][cb] = a.scale[pi];
+            op[0][cb] = OFF ? a.offset[pi] : 0u;
+        }
+    }
+
+    f32x16 acc[RB][CB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+            acc[rb][cb] = f32x16{};
+
+    // Eight weights (slice sl of column block cb) of a raw set as one operand.
+    auto dequant = [&](const WideRaw<WT> (&raw_set)[CB], const uint32_t (&spv)[CB], const uint32_t (&opv)[CB],
+                       int cb, int sl) -> uint4 {
+        const float s0 = t_to_f32<XT>(static_cast<uint16_t>(spv[cb]));
+        const float of = OFF ? t_to_f32<XT>(static_cast<uint16_t>(opv[cb])) : 0.0f;
+        const float sc = WT == WQ_I4 && !OFF ? s0 * 0.0625f : s0;
+        float v[8], w[8];
+        if constexpr (WT == WQ_I8)
+            decode8<WT>(raw_set[cb].lo, raw_set[cb].hi, sl, v);
+        else
+            decode8<WT>(raw_set[cb].lo, raw_set[cb].lo, sl, v);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if constexpr (OFF) {
+                // RN(code + o): the decoded value times 1/16 (int4) is the code exactly.
+                const float u = __builtin_fmaf(v[j], WT == WQ_I4 ? 0.0625f : 1.0f, of);
+                w[j] = u * s0;
+            } else {
+                w[j] = v[j] * sc;
+            }
+        }
+        return pack8_t<XT>(w);
+    };
+
+    // Step kt on LDS buffer B = kt % 2, as 32 row-block iterations of two
+    // matrix-core instructions each (slice s in iterations 8 s .. 8 s + 7),
+    // with the x1 operand reads three iterations ahead.  On entry bop[0..2]
+    // hold step kt's slices 0-2 as operands, wr[B] step kt's raw weights,
+    // wr[B ^ 1] step kt + 1's, ar[B] step kt + 1's x1 and ar[B ^ 1] step
+    // kt + 2's.  Spread over the iterations:
+    //   0-7    stage ar[B] in the other LDS buffer; dequantize step kt's
+    //          slice 3 into bop[3] (free since the last step's slice 3);
+    //   8      load step kt + 3's x1 into ar[B] and step kt + 2's weights
+    //          into wr[B] (consumed by now);
+    //   8-31   dequantize step kt + 1's slices 0, 1, 2 into bop[0..2], each
+    //          after this step's use of that slice.
+    // x1 is thus loaded two steps and weights one step before their use.
+    // The code is straight-line: past the last step the loads read zeros
+    // (past the buffer resources' ends) and the staged x1 and operands are
+    // never used.  Scheduling barriers keep each iteration's work in place,
+    // so the operand reads do not all move to the top.
+    uint4 ar[2][AV];
+    WideRaw<WT> wr[2][CB];
+    uint4 bop[SL][CB];
+    auto step = [&](int kt, auto bsel) {
+        constexpr int B = decltype(bsel)::value;
+        const uint4* Ab = As + B * (BM * 8);
+        auto aread = [&](int it) {
+            const int s = it / RB, rb = it % RB;
+            return Ab[(32 * rb + li) * 8 + ((4 * h + s) ^ ((li / 2) % 8))];
+        };
+        uint4 av[3] = {aread(0), aread(1), aread(2)};
+#pragma unroll
+        for (int it = 0; it < SL * RB; ++it) {
+            const int s = it / RB, rb = it % RB;
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb)
+                acc[rb][cb] = mfma32<XT>(av[it % 3], bop[s][cb], acc[rb][cb]);
+            if (it + 3 < SL * RB)
+                av[it % 3] = aread(it + 3);
+            if (it < AV)
+                store_a1(B ^ 1, it, ar[B]);
+            if (it == 1 || it == 5)  // this step's slice 3
+                bop[3][it / 4] = dequant(wr[B], sp[B % PS], op[B % PS], it / 4, 3);
+            if (it == AV) {
+                load_a(kt + 3, ar[B]);
+                load_w(kt + 2, wr[B]);
+                if constexpr (POL == DQ_PER_GROUP)
+                    load_p(kt + 2 < nk ? kt + 2 : nk - 1, sp[B % PS], op[B % PS]);
+            }
+            if (it >= RB && it % 4 == 1) {  // next step's slice it / 8 - 1, after this step used it
+                const int sn = it / RB - 1, cb = (it / 4) % 2;
+                bop[sn][cb] = dequant(wr[B ^ 1], sp[(B ^ 1) % PS], op[(B ^ 1) % PS], cb, sn);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+    };
+
+    // Steps come in pairs (the host plans k chunks of whole pairs).
+    if (nk > 0) {
+        load_a(0, ar[1]);
+        load_w(0, wr[0]);
+        load_w(1, wr[1]);
+        if constexpr (POL == DQ_PER_GROUP) {
+            load_p(0, sp[0], op[0]);
+            load_p(1, sp[PS - 1], op[PS - 1]);
+        }
+        load_a(1, ar[0]);
+#pragma unroll
+        for (int p = 0; p < AV; ++p)
+            store_a1(0, p, ar[1]);
+        load_a(2, ar[1]);
+#pragma unroll
+        for (int sl = 0; sl < SL - 1; ++sl)
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb)
+                bop[sl][cb] = dequant(wr[0], sp[0], op[0], cb, sl);
+        __syncthreads();
+        for (int kt = 0; kt < nk; kt += 2) {
+            step(kt, std::integral_constant<int, 0>{});
+            step(kt + 1, std::integral_constant<int, 1>{});
+        }
+    }
+
+    // Epilogue in 8 passes of 32 rows (one row block): each wave writes its
+    // 32 x 64 sums (+ bias) as binary32 into a padded row-major tile, then
+    // every lane takes 8 consecutive columns of a row: + x3, one rounding to
+    // T, one 16-byte store (or the binary32 partial sums of a k split).
+    float bias[CB];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+        const int64_t c = n0 + 64 * wave + 32 * cb + li;
+        bias[cb] = a.bias && !a.partial ? t_to_f32<XT>(a.bias[c < a.n ? c : a.n - 1]) : 0.0f;
+    }
+    float* const tile = reinterpret_cast<float*>(smem) + wave * (32 * ER);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        __syncthreads();  // the previous pass's (or the main loop's) LDS reads are done
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    tile[(8 * j + 4 * h + i) * ER + 32 * cb + li] = acc[rb][cb][4 * j + i] + bias[cb];
+        __syncthreads();
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int q = p * kWave + lane, rr = q / 8, cc = (q % 8) * 8;
+            const int64_t row = m0 + 32 * rb + rr;
+            const int64_t c0 = n0 + 64 * wave + cc;
+            if (row >= a.m || c0 >= a.n)
+                continue;
+            const float4 lo = *reinterpret_cast<const float4*>(&tile[rr * ER + cc]);
+            const float4 hi = *reinterpret_cast<const float4*>(&tile[rr * ER + cc + 4]);
+            float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+            const bool full = c0 + 8 <= a.n;
+            if (a.partial) {
+                float* dst = a.partial + (static_cast<int64_t>(blockIdx.z) * a.m + row) * a.n + c0;
+                for (int j = 0; j < 8; ++j)
+                    if (full || c0 + j < a.n)
+                        dst[j] = v[j];
+                continue;
+            }
+            uint16_t* dst = a.out + row * a.n + c0;
+            const bool vec = full && (reinterpret_cast<uintptr_t>(dst) & 15) == 0;
+            if (a.x3) {
+                const uint16_t* x3p = a.x3 + row * a.n + c0;
+                if (vec && (reinterpret_cast<uintptr_t>(x3p) & 15) == 0) {
+                    const uint4 x = *reinterpret_cast<const uint4*>(x3p);
+                    const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        v[j] += t_to_f32<XT>(static_cast<uint16_t>(xw[j / 2] >> (16 * (j % 2))));
+                } else {
+                    for (int j = 0; j < 8; ++j)
+                        if (c0 + j < a.n)
+                            v[j] += t_to_f32<XT>(x3p[j]);
+                }
+            }
+            if (vec) {
+                const uint4 o = make_uint4(pack2_t<XT>(v[0], v[1]), pack2_t<XT>(v[2], v[3]),
+                                           pack2_t<XT>(v[4], v[5]), pack2_t<XT>(v[6], v[7]));
+                *reinterpret_cast<uint4*>(dst) = o;
+            } else {
+                for (int j = 0; j < 8; ++j)
+                    if (c0 + j < a.n)
+                        dst[j] = f32_to_t<XT>(v[j]);
+            }
+        }
+    }
+}
+
+template <int XT, int WT, int POL, bool OFF>
+hipError_t launch_wide(const WqArgs& a, int splits, hipStream_t stream)
+{
+    const int64_t gx = (a.n + kWqWideCols - 1) / kWqWideCols;
+    const int64_t gy = (a.m + kWqWideRows - 1) / kWqWideRows;
+    if (gy > 65535)
+        return hipErrorInvalidConfiguration;
+    const dim3 grid(static_cast<uint32_t>(gx), static_cast<uint32_t>(gy), static_cast<uint32_t>(splits));
+    hipLaunchKernelGGL((wq_wide_kernel<XT, WT, POL, OFF>), grid, dim3(kWave * 4), 0, stream, a);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess || splits == 1)
+        return err;
+    const int64_t blocks = (a.m * a.n + kBlock - 1) / kBlock;
+    hipLaunchKernelGGL((wq_reduce_kernel<XT>), dim3(static_cast<uint32_t>(blocks)), dim3(kBlock), 0, stream, a, splits);
+    return hipGetLastError();
+}
+
 template <int XT, int WT, int POL, bool OFF, int RN, int U>
 hipError_t launch_decode(const WqArgs& a, int splits, hipStream_t stream)
 {
@@ -937,6 +1279,8 @@ hipError_t pick_tile(const WqPlan& p, const WqArgs& a, hipStream_t stream)
 {
     if (p.tile == WQ_TILE_DECODE)
         return launch_decode<XT, WT, POL, OFF, kWqDecodeCols, wq_batch(WQ_TILE_DECODE, WT)>(a, p.splits, stream);
+    if (p.tile == WQ_TILE_WIDE)
+        return launch_wide<XT, WT, POL, OFF>(a, p.splits, stream);
     return launch_gemm<XT, WT, POL, OFF>(a, p.splits, stream);
 }
 

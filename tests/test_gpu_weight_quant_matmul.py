@@ -268,3 +268,51 @@ def test_wq_full_size_sampled(orc, name):
     rows = np.unique(np.linspace(0, m - 1, count).astype(int))
     frac = check_weight_quant_matmul(orc, q, rows=rows)
     print(f"{name}: {frac:.4f} of sampled outputs equal the once-rounded exact result", flush=True)
+
+
+# The wide kernel (256 x 256 workgroup tiles, weights loaded straight into
+# the matrix-core operands, x1 through LDS) takes at least 256 rows when its
+# tiles alone give 128 workgroups, k is a multiple of 128 and groups a
+# multiple of 64: ragged rows and columns, every policy, offsets, bias, x3,
+# bf16 and fp16, checked on sampled rows (the first and last rows of every
+# row tile among them).
+WIDE = [(300, 256, 64 * 256 - 37, "int8", "channel", 0, False, "bfloat16", True),
+        (257, 384, 16384, "int4", "group", 64, True, "float16", False),
+        (512, 512, 16384, "int4", "group", 128, True, "bfloat16", True),
+        (260, 640, 16400, "int8", "group", 128, True, "float16", True),
+        (256, 256, 32768, "int4", "tensor", 0, False, "bfloat16", False),
+        (256, 1024, 32768 - 5, "int8", "channel", 0, True, "bfloat16", True)]
+
+
+@pytest.mark.parametrize("m,k,n,weight,kind,gs,offset,dtype,x3", WIDE,
+                         ids=[f"{w[0]}x{w[1]}x{w[2]}-{w[3]}-{w[4]}{w[5]}" for w in WIDE])
+def test_wq_wide_tiles(orc, m, k, n, weight, kind, gs, offset, dtype, x3):
+    announce("wq wide", m, k, n, weight, kind, gs, offset, dtype, x3)
+    q = synth.wq_inputs(m, k, n, 6100 + m + k, dtype=dtype, weight=weight, group_size=gs,
+                        per_tensor=kind == "tensor", offset=offset, bias=True, x3=x3)
+    edges = [min(r, m - 1) for t in range(0, m, 256) for r in (t, t + 1, t + 255)]
+    rows = np.unique(np.r_[edges, np.linspace(0, m - 1, 12).astype(int), m - 1])
+    check_weight_quant_matmul(orc, q, rows=rows)
+
+
+@pytest.mark.parametrize("weight", ["int8", "int4"])
+@pytest.mark.parametrize("kind,gs", [("tensor", 0), ("channel", 0), ("group", 64), ("group", 128)])
+@pytest.mark.parametrize("offset", [True, False])
+def test_wq_wide_identity_exposes_weight(orc, weight, kind, gs, offset):
+    """x1 = identity [256, 256] against 32768 columns (128 wide tiles): out
+    must be the oracle's dequantized W bit for bit, so a weight paired with
+    the wrong k slot of x1, or dequantized with another step's parameters,
+    would show."""
+    announce("wq wide identity", weight, kind, gs, offset)
+    k, n = 256, 32768
+    q = synth.wq_inputs(k, k, n, 6400 + gs, weight=weight, group_size=gs, per_tensor=kind == "tensor",
+                        offset=offset, bias=False)
+    q["x1"] = torch.eye(k, dtype=q["x1"].dtype)
+    d = {key: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for key, v in q.items()}
+    import int4_quantization_amd as dq
+    out = dq.weight_quant_matmul(d["x1"], d["x2"], d["scale"], d["offset"], gs, None, None, True, weight)
+    from parity import wq_oracle_args
+    x2, policy = wq_oracle_args(q)
+    W = orc.weight_dequant(x2, q["scale"], q["offset"], policy, gs, True)
+    got = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, W), f"{int((got != W).sum())} of {W.size} weights differ"
