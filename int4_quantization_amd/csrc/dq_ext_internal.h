@@ -71,6 +71,9 @@ constexpr int kWqGemmRows = 128, kWqGemmCols = 128, kWqGemmK = 128;
 // (no k split), k is a multiple of two k-steps and the group size of one.
 constexpr int kWqWideRows = 256, kWqWideCols = 256, kWqWideK = 64;
 constexpr int64_t kWqWideMinTiles = 128;
+// Wide kernel: x1 reaches LDS by direct-to-LDS buffer loads (three buffers)
+// rather than through registers and LDS stores (two buffers).
+constexpr bool kWqWideDma = true;
 // Per-group parameters of the LDS-tiled kernel come in windows of this many
 // groups when groups are one k-step long; k splits are then planned in
 // multiples of the window.

@@ -914,12 +914,17 @@ __global__ __launch_bounds__(kWave * 4, 1) void wq_wide_kernel(const WqArgs a)
     constexpr int SL = BK / 16;             // k slices per step
     constexpr int AV = BM * (BK / 8) / NT;  // 16-byte x1 vectors staged per thread and step
     constexpr int WSTEP = WT == WQ_I8 ? BK : BK / 2;  // weight bytes per column and step
-    constexpr int ER = 64 + 4;              // epilogue tile row (binary32), padded
-    constexpr int kStage = 2 * BM * (BK / 8) * 16, kEpi = 4 * 32 * ER * 4;
+    constexpr int ER = 64;                  // epilogue tile row (binary32)
+    constexpr int kBuf = BM * (BK / 8);  // 16-byte chunks per x1 buffer
     static_assert(AV * NT == BM * BK / 8 && AV == 8, "x1 tile divides over threads");
     static_assert(RB == 8 && CB == 2 && SL == 4, "32 row-block iterations per step, 2 column blocks per wave");
-    __shared__ __align__(16) unsigned char smem[kStage > kEpi ? kStage : kEpi];
-    uint4* const As = reinterpret_cast<uint4*>(smem);  // [2][BM * 8] 16-byte chunks
+    static_assert(4 * 32 * ER * 4 <= kBuf * 16, "the epilogue tiles fit one x1 buffer");
+    // Two x1 buffers as two arrays, so the compiler can tell a buffer being
+    // filled by direct-to-LDS loads from the one being read.  The epilogue
+    // reuses the first.
+    __shared__ __align__(16) uint4 As0[kBuf], As1[kBuf];
+    auto abuf = [&](int b) -> uint4* { return b ? As1 : As0; };
+    unsigned char* const smem = reinterpret_cast<unsigned char*>(As0);
 
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const int li = lane % 32, h = lane / 32;
@@ -961,7 +966,34 @@ __global__ __launch_bounds__(kWave * 4, 1) void wq_wide_kernel(const WqArgs a)
     };
     auto store_a1 = [&](int buf, int p, const uint4 (&ar)[AV]) {
         const int row = tid / 8 + 32 * p;
-        As[buf * (BM * 8) + row * 8 + ((tid % 8) ^ a_slot)] = ar[p];
+        abuf(buf)[row * 8 + ((tid % 8) ^ a_slot)] = ar[p];
+    };
+    // x1 of step kt straight into LDS buffer buf (direct-to-LDS buffer
+    // loads, no registers): wave w's load p fills rows 64 w + 8 p .. + 7 (one
+    // KB, lane l at 16 l), so lane l takes row r = 64 w + 8 p + l / 8 and
+    // slot l % 8, i.e. chunk (l % 8) ^ ((r / 2) % 8) of that row.
+    auto dma_a = [&](int kt, uint4* dst) {
+#pragma unroll
+        for (int p = 0; p < AV; ++p) {
+            const int r = 64 * wave + 8 * p + lane / 8;
+            const int c = (lane % 8) ^ ((r / 2) % 8);
+            const uint32_t off = static_cast<uint32_t>(r) * static_cast<uint32_t>(a.k * 2) + c * 16 +
+                                 static_cast<uint32_t>(kt) * (BK * 2);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, dst + (64 * wave + 8 * p) * 8, 16, off, 0, 0, 0);
+        }
+    };
+    // Wait until at most n vector-memory operations of this wave are
+    // outstanding (they retire in order), then meet the workgroup barrier.
+    // The direct-to-LDS loads of a buffer are complete once the loads issued
+    // after them number n or fewer.  The empty asm statements keep the
+    // compiler from moving LDS accesses across.
+    auto wait_barrier = [&](auto n_outstanding) {
+        constexpr int n = decltype(n_outstanding)::value;
+        static_assert(n >= 0 && n < 64, "vmcnt range");
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
     };
     auto load_w = [&](int kt, WideRaw<WT> (&wr)[CB]) {
 #pragma unroll
@@ -1029,6 +1061,81 @@ __global__ __launch_bounds__(kWave * 4, 1) void wq_wide_kernel(const WqArgs a)
         return pack8_t<XT>(w);
     };
 
+    WideRaw<WT> wr[2][CB];
+    uint4 bop[SL][CB];
+    if constexpr (kWqWideDma) {
+        // Step kt reads LDS buffer B = kt % 2, as 32 row-block iterations of
+        // two matrix-core instructions each (slice s in iterations 8 s .. 8 s
+        // + 7), with the x1 operand reads three iterations ahead.  On entry
+        // bop[0..2] hold step kt's slices 0-2 as operands, wr[B] step kt's raw
+        // weights and wr[B ^ 1] step kt + 1's.  Spread over the iterations:
+        //   0      direct-to-LDS loads of step kt + 1's x1 into the other
+        //          buffer (last read in step kt - 1);
+        //   1, 5   dequantize step kt's slice 3 into bop[3];
+        //   8      load step kt + 2's weights into wr[B] (consumed by now);
+        //   9-31   dequantize step kt + 1's slices 0, 1, 2 into bop[0..2],
+        //          each after this step's use of that slice.
+        // The step ends waiting for step kt + 1's x1 (only step kt + 2's
+        // weight loads may remain) and meeting the barrier.
+        constexpr int kWl = CB * (WT == WQ_I8 ? 2 : 1) + (POL == DQ_PER_GROUP ? CB * (OFF ? 2 : 1) : 0);
+        auto step = [&](int kt, auto bsel) {
+            constexpr int B = decltype(bsel)::value;
+            const uint4* Ab = B ? As1 : As0;
+            auto aread = [&](int it) {
+                const int s = it / RB, rb = it % RB;
+                return Ab[(32 * rb + li) * 8 + ((4 * h + s) ^ ((li / 2) % 8))];
+            };
+            uint4 av[3] = {aread(0), aread(1), aread(2)};
+#pragma unroll
+            for (int it = 0; it < SL * RB; ++it) {
+                const int s = it / RB, rb = it % RB;
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb)
+                    acc[rb][cb] = mfma32<XT>(av[it % 3], bop[s][cb], acc[rb][cb]);
+                if (it + 3 < SL * RB)
+                    av[it % 3] = aread(it + 3);
+                if (it == 0)
+                    dma_a(kt + 1, B ? As0 : As1);
+                if (it == 1 || it == 5)  // this step's slice 3
+                    bop[3][it / 4] = dequant(wr[B], sp[B % PS], op[B % PS], it / 4, 3);
+                if (it == AV) {
+                    load_w(kt + 2, wr[B]);
+                    if constexpr (POL == DQ_PER_GROUP)
+                        load_p(kt + 2 < nk ? kt + 2 : nk - 1, sp[B % PS], op[B % PS]);
+                }
+                if (it >= RB && it % 4 == 1) {  // next step's slice it / 8 - 1, after this step used it
+                    const int sn = it / RB - 1, cb = (it / 4) % 2;
+                    bop[sn][cb] = dequant(wr[B ^ 1], sp[(B ^ 1) % PS], op[(B ^ 1) % PS], cb, sn);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            wait_barrier(std::integral_constant<int, kWl>{});
+        };
+
+        // Steps come in pairs (the host plans k chunks of whole pairs).
+        if (nk > 0) {
+            dma_a(0, As0);
+            load_w(0, wr[0]);
+            load_w(1, wr[1]);
+            if constexpr (POL == DQ_PER_GROUP) {
+                load_p(0, sp[0], op[0]);
+                load_p(1, sp[PS - 1], op[PS - 1]);
+            }
+#pragma unroll
+            for (int sl = 0; sl < SL - 1; ++sl)
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb)
+                    bop[sl][cb] = dequant(wr[0], sp[0], op[0], cb, sl);
+            wait_barrier(std::integral_constant<int, 0>{});
+            for (int kt = 0; kt < nk; kt += 2) {
+                step(kt, std::integral_constant<int, 0>{});
+                step(kt + 1, std::integral_constant<int, 1>{});
+            }
+            // The loop's last loads (past the end) may still be writing LDS.
+            wait_barrier(std::integral_constant<int, 0>{});
+        }
+    } else {
     // Step kt on LDS buffer B = kt % 2, as 32 row-block iterations of two
     // matrix-core instructions each (slice s in iterations 8 s .. 8 s + 7),
     // with the x1 operand reads three iterations ahead.  On entry bop[0..2]
@@ -1047,11 +1154,9 @@ __global__ __launch_bounds__(kWave * 4, 1) void wq_wide_kernel(const WqArgs a)
     // never used.  Scheduling barriers keep each iteration's work in place,
     // so the operand reads do not all move to the top.
     uint4 ar[2][AV];
-    WideRaw<WT> wr[2][CB];
-    uint4 bop[SL][CB];
     auto step = [&](int kt, auto bsel) {
         constexpr int B = decltype(bsel)::value;
-        const uint4* Ab = As + B * (BM * 8);
+        const uint4* Ab = B ? As1 : As0;
         auto aread = [&](int it) {
             const int s = it / RB, rb = it % RB;
             return Ab[(32 * rb + li) * 8 + ((4 * h + s) ^ ((li / 2) % 8))];
@@ -1109,6 +1214,8 @@ __global__ __launch_bounds__(kWave * 4, 1) void wq_wide_kernel(const WqArgs a)
             step(kt, std::integral_constant<int, 0>{});
             step(kt + 1, std::integral_constant<int, 1>{});
         }
+    }
+
     }
 
     // Epilogue in 8 passes of 32 rows (one row block): each wave writes its
