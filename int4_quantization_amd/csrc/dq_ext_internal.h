@@ -37,6 +37,7 @@ enum WqTile : int {
     WQ_TILE_DECODE = 3,  // at most 16 rows: kWqDecodeCols blocks per wave, x1 staged in LDS
     WQ_TILE_GEMM = 4,    // more rows: 128 x 128 workgroup tiles, x1 and dequantized weights in LDS
     WQ_TILE_WIDE = 5,    // many rows: 256 x 256 workgroup tiles, x1 in LDS, weights straight to the operands
+    WQ_TILE_BALANCED = 6,  // at most 16 rows, int4 in groups of 128: one 8-wave workgroup per CU, k split over its waves
 };
 
 struct WqPlan {
@@ -71,6 +72,12 @@ constexpr int kWqGemmRows = 128, kWqGemmCols = 128, kWqGemmK = 128;
 // (no k split), k is a multiple of two k-steps and the group size of one.
 constexpr int kWqWideRows = 256, kWqWideCols = 256, kWqWideK = 64;
 constexpr int64_t kWqWideMinTiles = 128;
+// Balanced decode kernel: workgroups (one per compute unit of MI355X), the
+// most 16-column blocks each takes, and the k multiple it needs (8 waves x
+// parameter chunks of 1024).
+constexpr int64_t kWqBalWorkgroups = 256;
+constexpr int kWqBalMaxBlocks = 7;
+constexpr int64_t kWqBalKMultiple = 8192;
 // Wide kernel: x1 reaches LDS by direct-to-LDS buffer loads (three buffers)
 // rather than through registers and LDS stores (two buffers).
 constexpr bool kWqWideDma = true;

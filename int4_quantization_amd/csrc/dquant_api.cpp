@@ -859,12 +859,21 @@ dq_status plan_weight_quant_matmul(const dq_tensor* x1, const dq_tensor* x2, int
             int64_t{dq::kWqWideRows} * k * 2 < (int64_t{1} << 31) && int64_t{dq::kWqWideCols} * kw < (int64_t{1} << 31))
             p.tile = dq::WQ_TILE_WIDE;
     }
+    // Decode shapes whose n / 16 column blocks divide evenly over the 256
+    // compute units (int4 in groups of 128, k in whole 8 x 256 runs): the
+    // balanced kernel, one workgroup per compute unit, no k split.
+    if (p.variant == dq::WQ_VAR_MFMA && p.tile == dq::WQ_TILE_DECODE && x2->dtype == DQ_I4 && k > 0 &&
+        policy == DQ_PER_GROUP && group_size == dq::kWqSuperK && k % dq::kWqBalKMultiple == 0 &&
+        n % (16 * dq::kWqBalWorkgroups) == 0 && n / (16 * dq::kWqBalWorkgroups) <= dq::kWqBalMaxBlocks &&
+        n * (k / 2) < (int64_t{1} << 31) && n * (k / group_size) * 2 < (int64_t{1} << 31))
+        p.tile = dq::WQ_TILE_BALANCED;
     // Few output tiles: split k so that about the target number of
     // workgroups run; the binary32 partial sums [splits, m, n] live in the
     // workspace.
     p.splits = 1;
     p.k_chunk = k;
-    if (p.variant == dq::WQ_VAR_MFMA && m > 0 && p.tile != dq::WQ_TILE_WIDE) {  // m == 0 launches nothing
+    if (p.variant == dq::WQ_VAR_MFMA && m > 0 && p.tile != dq::WQ_TILE_WIDE &&
+        p.tile != dq::WQ_TILE_BALANCED) {  // m == 0 launches nothing
         const int64_t tiles = ((n + dq::wq_tile_cols(p.tile) - 1) / dq::wq_tile_cols(p.tile)) *
                               ((m + dq::wq_tile_rows(p.tile) - 1) / dq::wq_tile_rows(p.tile));
         const int64_t batch_k = static_cast<int64_t>(dq::wq_batch(p.tile, p.w_type)) * dq::kWqSuperK;

@@ -506,6 +506,277 @@ __global__ __launch_bounds__(kWqDecodeWaves * kWave) void wq_decode_kernel(const
 }
 
 // ---------------------------------------------------------------------------
+// Balanced decode kernel (at most 16 rows, int4 weights in groups of 128 k):
+// one workgroup of eight waves per compute unit.  The workgroup owns CB
+// column blocks of 16 (the host picks CB = n / (16 * 256), so the 256
+// workgroups fill the 256 compute units once), and wave w takes the k-range
+// [w k / 8, (w + 1) k / 8) of all CB blocks.  Every SIMD then carries two
+// waves of equal work, where the per-wave layout above leaves some SIMDs
+// with two waves and others with one (n / 16 blocks are not a multiple of
+// the SIMD count).  The eight partial sums of each output meet in LDS at the
+// end and are added in wave order.
+//
+// Per batch of two supersteps (256 k) a wave stages its own x1 slice in LDS
+// with direct-to-LDS loads, double-buffered, and keeps each block's next
+// weights in flight from the moment the block's registers are free.  The
+// per-group parameters come into LDS eight groups (four batches) at a time,
+// one 16-byte load per column and kind: loads of one dword per column and
+// batch measured 5 us slower at 16 x 8192 x 28672.  Each x1 operand read serves CB blocks.  The operand
+// and parameter reads from LDS are written in assembly with their wait: the
+// compiler, seeing LDS reads after direct-to-LDS loads, would otherwise wait
+// for every outstanding load there; an explicit wait on the vector memory
+// counter orders them instead.  Their outputs are early-clobber: a read's
+// data can land while later reads of the same block still need the address
+// register, so no output may share a register with an input.
+// ---------------------------------------------------------------------------
+constexpr int kWqBalWaves = 8;
+
+template <int XT, bool OFF, int CB>
+__global__ __launch_bounds__(kWqBalWaves * kWave, 1) void wq_bal_kernel(const WqArgs a)
+{
+    constexpr int WT = WQ_I4, U = 2;
+    constexpr int BK = U * kWqSuper;  // k per batch
+    constexpr int CH = BK / 8;        // 16-byte chunks per x1 row and batch
+    constexpr int SL = 16 * CH;       // x1 slots per wave buffer
+    constexpr int XI = SL / kWave;    // direct-to-LDS loads of x1 per wave and batch
+    constexpr int PC = 2 * kWave;     // parameter columns per kind (CB * 16, padded)
+    constexpr int PB = 4;             // batches per parameter chunk (8 groups, 16 bytes a column)
+    static_assert(CB >= 1 && CB <= kWqBalMaxBlocks && 16 * CB <= PC && XI * kWave == SL && CH == 32,
+                  "geometry of the balanced decode kernel");
+    // x1 slots [wave][buffer][slot] (128 KB); parameter chunks [wave][scale,
+    // offset][column] (32 KB): eight groups as T bits, dword j holding batch
+    // j's two (low half the first).  Each parameter load writes 64 lanes, so
+    // rows hold 128 columns.
+    __shared__ __align__(16) uint4 xs[kWqBalWaves][2][SL];
+    __shared__ __align__(16) uint4 ps[kWqBalWaves][2][PC];
+
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int li = lane % 16, g = lane / 16;
+    const int64_t n0 = static_cast<int64_t>(blockIdx.x) * (16 * CB);
+    const uint32_t kw = static_cast<uint32_t>(a.k / kWqBalWaves);  // k per wave
+    const uint32_t k0 = static_cast<uint32_t>(wave) * kw;
+    const int nb = static_cast<int>(kw / BK);
+
+    // The host keeps the weights, x1 and the parameters below 2^31 bytes.
+    // Offsets past a resource's end read zeros with no memory access: x1
+    // rows past m, parameter columns past the workgroup's, and the staging
+    // of the batch after a wave's last.
+    constexpr uint32_t kPast = 0xFFFFFFF0u;
+    const __amdgpu_buffer_rsrc_t wrs = make_rsrc(a.x2, static_cast<uint32_t>(a.n * (a.k / 2)));
+    const __amdgpu_buffer_rsrc_t xrs = make_rsrc(a.x1, static_cast<uint32_t>(a.m * a.k * 2));
+    const __amdgpu_buffer_rsrc_t srs = make_rsrc(a.scale, static_cast<uint32_t>(a.n * a.groups * 2));
+    const __amdgpu_buffer_rsrc_t ors = make_rsrc(OFF ? a.offset : a.scale, static_cast<uint32_t>(a.n * a.groups * 2));
+    uint32_t wcol[CB];  // byte offset of this lane's run in each block's column
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+        wcol[cb] = static_cast<uint32_t>((n0 + 16 * cb + li) * (a.k / 2)) + 16u * g;
+
+    // x1 of batch b into LDS buffer buf: load p, lane l fills slot 64 p + l,
+    // row r = 2 p + l / 32, with chunk (l % 32) ^ (r % 16) of the row (8 k
+    // each), so the operand reads below (16 rows, one chunk each) touch 16
+    // distinct 16-byte slots modulo 256 bytes in every group of 16 lanes
+    // (gfx950 serves 16-byte reads 16 lanes at a time over 64 banks).
+    auto stage_x = [&](int b, int buf) {
+        const bool in = b < nb;
+#pragma unroll
+        for (int p = 0; p < XI; ++p) {
+            const int r = 2 * p + lane / 32;
+            const int c = (lane % 32) ^ (r % 16);
+            const uint32_t off = (static_cast<uint32_t>(r) * static_cast<uint32_t>(a.k) + k0 +
+                                  static_cast<uint32_t>(b) * BK + 8u * static_cast<uint32_t>(c)) * 2u;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, &xs[wave][buf][64 * p], 16, in ? off : kPast, 0, 0, 0);
+        }
+    };
+    // Parameter chunk q (batches PB q .. PB q + PB - 1): lane l of load i
+    // takes column 64 i + l of the workgroup, 16 bytes of its groups.
+    auto stage_p = [&](int q) {
+        const uint32_t gb = (k0 + static_cast<uint32_t>(q) * (PB * BK)) / kWqSuper;
+#pragma unroll
+        for (int kind = 0; kind < (OFF ? 2 : 1); ++kind)
+#pragma unroll
+            for (int i = 0; i < PC / kWave; ++i) {
+                const int c = kWave * i + lane;
+                const uint32_t off = c < 16 * CB ? static_cast<uint32_t>((n0 + c) * a.groups + gb) * 2u : kPast;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(kind ? ors : srs, &ps[wave][kind][kWave * i], 16, off, 0, 0,
+                                                         0);
+            }
+    };
+    auto load_w = [&](int b, int u, int cb, uint4 (&w)[U][CB]) {
+        const uint32_t kb = k0 + static_cast<uint32_t>(b) * BK;
+        w[u][cb] = buf_load16<kBufNonTemporal>(wrs, b < nb ? wcol[cb] + kb / 2 + 64u * u : kPast);
+    };
+
+    // Vector memory operations retire in order: batch b's staging (and a
+    // parameter chunk's) is followed by its weight loads (U CB), issued while
+    // batch b - 1 is computed, so the staging (and all before it) is complete
+    // once that many or fewer are outstanding.
+    constexpr int kAfter = U * CB;
+    static_assert(kAfter < 64, "vmcnt range");
+    auto wait_vm = [&](auto n_outstanding) {
+        constexpr int n = decltype(n_outstanding)::value;
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
+        asm volatile("" ::: "memory");
+    };
+
+    f32x4 acc[CB];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+        acc[cb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    uint4 w[U][CB];
+    stage_p(0);
+    stage_x(0, 0);
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            load_w(0, u, cb, w);
+    const uint32_t xs_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&xs[wave][0][0]));
+    const uint32_t ps_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&ps[wave][0][0]));
+    for (int b = 0; b < nb; ++b) {
+        const int buf = b & 1;
+        wait_vm(std::integral_constant<int, kAfter>{});
+        stage_x(b + 1, buf ^ 1);
+        // This batch's parameters of the 7 block slots (slots past CB read
+        // padding columns, unused): dword b % PB of each column's chunk.
+        uint32_t sp[kWqBalMaxBlocks], op[kWqBalMaxBlocks];
+        const uint32_t pb = ps_base + static_cast<uint32_t>(li * 16 + (b % PB) * 4);
+        asm volatile(
+            "ds_read_b32 %0, %14 offset:0\n\t"
+            "ds_read_b32 %1, %14 offset:256\n\t"
+            "ds_read_b32 %2, %14 offset:512\n\t"
+            "ds_read_b32 %3, %14 offset:768\n\t"
+            "ds_read_b32 %4, %14 offset:1024\n\t"
+            "ds_read_b32 %5, %14 offset:1280\n\t"
+            "ds_read_b32 %6, %14 offset:1536\n\t"
+            "ds_read_b32 %7, %14 offset:2048\n\t"
+            "ds_read_b32 %8, %14 offset:2304\n\t"
+            "ds_read_b32 %9, %14 offset:2560\n\t"
+            "ds_read_b32 %10, %14 offset:2816\n\t"
+            "ds_read_b32 %11, %14 offset:3072\n\t"
+            "ds_read_b32 %12, %14 offset:3328\n\t"
+            "ds_read_b32 %13, %14 offset:3584\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(sp[0]), "=&v"(sp[1]), "=&v"(sp[2]), "=&v"(sp[3]), "=&v"(sp[4]), "=&v"(sp[5]), "=&v"(sp[6]),
+              "=&v"(op[0]), "=&v"(op[1]), "=&v"(op[2]), "=&v"(op[3]), "=&v"(op[4]), "=&v"(op[5]), "=&v"(op[6])
+            : "v"(pb)
+            : "memory");
+        // The chunk's last batch has read it: the next chunk comes in now, ahead
+        // of the next batch's weights (the wait above covers it then).
+        if (b % PB == PB - 1 && b + 1 < nb)
+            stage_p((b + 1) / PB);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            // x1 operands of superstep u: lane group g, sub-step s2 takes
+            // chunk 16 u + 4 g + s2 of row li (the k assignment of the decode
+            // kernel above).
+            uint4 av[4];
+            uint32_t ad[4];
+#pragma unroll
+            for (int s2 = 0; s2 < 4; ++s2) {
+                const int c = 16 * u + 4 * g + s2;
+                ad[s2] = xs_base + static_cast<uint32_t>((buf * SL + li * CH + (c ^ li)) * 16);
+            }
+            asm volatile(
+                "ds_read_b128 %0, %4\n\t"
+                "ds_read_b128 %1, %5\n\t"
+                "ds_read_b128 %2, %6\n\t"
+                "ds_read_b128 %3, %7\n\t"
+                "s_waitcnt lgkmcnt(0)"
+                : "=&v"(av[0]), "=&v"(av[1]), "=&v"(av[2]), "=&v"(av[3])
+                : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3])
+                : "memory");
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) {
+                const float sc = t_to_f32<XT>(static_cast<uint16_t>(sp[cb] >> (16 * u)));
+                const float of = OFF ? t_to_f32<XT>(static_cast<uint16_t>(op[cb] >> (16 * u))) : 0.0f;
+                uint4 bv[4];
+                bool use_fma = false;
+                float os = 0.0f;
+                if constexpr (OFF) {
+                    os = of * sc;
+                    use_fma = __all(fma_exact<WT, XT>(of, sc, os));
+                }
+                if (!OFF || use_fma) {
+                    // int4 decodes to 16 code and s / 16 is exact; with an
+                    // offset, RN(16 code * (s / 16) + RN(o s)) is the formula
+                    // where fma_exact holds (wq_fma.h).
+                    const float s_eff = sc * 0.0625f;
+#pragma unroll
+                    for (int s2 = 0; s2 < 4; ++s2) {
+                        float v[8], wv[8];
+                        decode8<WT>(w[u][cb], w[u][cb], s2, v);
+#pragma unroll
+                        for (int j = 0; j < 8; ++j)
+                            wv[j] = OFF ? __builtin_fmaf(v[j], s_eff, os) : v[j] * s_eff;
+                        bv[s2] = pack8_t<XT>(wv);
+                    }
+                } else {
+                    // As in the decode kernel: RN(RN(16 code + 16 o) * (s / 16))
+                    // unless 16 o overflows, then the formula step by step.
+                    const float o16 = of * 16.0f, s16 = sc * 0.0625f;
+                    const bool huge = __any(__builtin_isinf(o16));
+#pragma unroll
+                    for (int s2 = 0; s2 < 4; ++s2) {
+                        float v[8], wv[8];
+                        decode8<WT>(w[u][cb], w[u][cb], s2, v);
+                        if (__builtin_expect(huge, 0)) {
+#pragma unroll 1
+                            for (int j = 0; j < 8; ++j)
+                                wv[j] = dequant1<WT, true>(v[j], sc, of);
+                        } else {
+#pragma unroll
+                            for (int j = 0; j < 8; ++j)
+                                wv[j] = (v[j] + o16) * s16;
+                        }
+                        bv[s2] = pack8_t<XT>(wv);
+                    }
+                }
+                // The block's registers for superstep u are free: the next
+                // batch's run goes out.
+                load_w(b + 1, u, cb, w);
+#pragma unroll
+                for (int s2 = 0; s2 < 4; ++s2)
+                    acc[cb] = mfma16<XT>(av[s2], bv[s2], acc[cb]);
+            }
+        }
+    }
+
+    // Partial sums of the eight waves meet in LDS over the x1 buffers, once
+    // every direct-to-LDS load (the empty staging after the last batch
+    // included) has landed and every wave has finished reading.
+    wait_vm(std::integral_constant<int, 0>{});
+    __syncthreads();
+    static_assert(sizeof(f32x4) * kWqBalWaves * kWqBalMaxBlocks * kWave <= sizeof(xs), "partial sums fit");
+    f32x4* const red = reinterpret_cast<f32x4*>(&xs[0][0][0]);
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+        red[(wave * CB + cb) * kWave + lane] = acc[cb];
+    __syncthreads();
+    if (tid < CB * kWave) {
+        const int cb = tid / kWave, l = tid % kWave;
+        f32x4 s = red[cb * kWave + l];
+#pragma unroll
+        for (int w8 = 1; w8 < kWqBalWaves; ++w8)
+            s += red[(w8 * CB + cb) * kWave + l];
+        // Lane l holds rows 4 (l / 16) .. + 3 of column l % 16 of the block.
+        const int64_t c = n0 + 16 * cb + l % 16;
+        const float bias = a.bias ? t_to_f32<XT>(a.bias[c]) : 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t row = 4 * (l / 16) + i;
+            if (row >= a.m)
+                continue;
+            float v = s[i] + bias;
+            if (a.x3)
+                v += t_to_f32<XT>(a.x3[row * a.n + c]);
+            a.out[row * a.n + c] = f32_to_t<XT>(v);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Prefill-shaped kernel: a 128 x 128 output tile per workgroup, four waves
 // in a 2 x 2 grid, each 64 x 64 (4 x 4 blocks of 16 x 16).  Per k-step of
 // 128 the x1 tile and the dequantized weight tile are staged in LDS, so every
@@ -1381,9 +1652,36 @@ hipError_t launch_gemm(const WqArgs& a, int splits, hipStream_t stream)
     return hipSuccess;
 }
 
+template <int XT, bool OFF>
+hipError_t launch_balanced(const WqArgs& a, hipStream_t stream)
+{
+    const int64_t cb = a.n / (16 * kWqBalWorkgroups);
+    const dim3 grid(static_cast<uint32_t>(kWqBalWorkgroups)), block(kWqBalWaves * kWave);
+    switch (cb) {
+    case 1: hipLaunchKernelGGL((wq_bal_kernel<XT, OFF, 1>), grid, block, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((wq_bal_kernel<XT, OFF, 2>), grid, block, 0, stream, a); break;
+    case 3: hipLaunchKernelGGL((wq_bal_kernel<XT, OFF, 3>), grid, block, 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((wq_bal_kernel<XT, OFF, 4>), grid, block, 0, stream, a); break;
+    case 5: hipLaunchKernelGGL((wq_bal_kernel<XT, OFF, 5>), grid, block, 0, stream, a); break;
+    case 6: hipLaunchKernelGGL((wq_bal_kernel<XT, OFF, 6>), grid, block, 0, stream, a); break;
+    case 7: hipLaunchKernelGGL((wq_bal_kernel<XT, OFF, 7>), grid, block, 0, stream, a); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 template <int XT, int WT, int POL, bool OFF>
 hipError_t pick_tile(const WqPlan& p, const WqArgs& a, hipStream_t stream)
 {
+    if constexpr (WT == WQ_I4 && POL == DQ_PER_GROUP) {
+        if (p.tile == WQ_TILE_BALANCED)
+            return p.splits == 1 && a.group_size == kWqSuper && a.k % kWqBalKMultiple == 0 && a.m <= 16 &&
+                           a.n % (16 * kWqBalWorkgroups) == 0
+                       ? launch_balanced<XT, OFF>(a, stream)
+                       : hipErrorInvalidValue;
+    }
+    if (p.tile == WQ_TILE_BALANCED)
+        return hipErrorInvalidValue;
     if (p.tile == WQ_TILE_DECODE)
         return launch_decode<XT, WT, POL, OFF, kWqDecodeCols, wq_batch(WQ_TILE_DECODE, WT)>(a, p.splits, stream);
     if (p.tile == WQ_TILE_WIDE)

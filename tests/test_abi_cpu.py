@@ -430,6 +430,29 @@ def test_wq_split_k_workspace(lib):
     lib.dq_executor_destroy(ex)
 
 
+def test_wq_balanced_plan(lib):
+    """int4 in groups of 128 with at most 16 rows, k a multiple of 8192 and n
+    a multiple of 4096 (up to 7 * 4096) plan the balanced decode kernel: one
+    workgroup per compute unit and no k split, so no workspace, where the
+    per-wave decode kernel would split k over its few output tiles."""
+    def plan_ws(m, k, n, wdt=D.I4, gs=128):
+        sshape = [n, -(-k // gs)] if gs else [n]
+        # addresses 256 MB apart: the weights reach 117 MB
+        st, ws, ex = wq_ws(lib, desc(D.BF16, [m, k], 0x1000000), desc(wdt, [n, k], 0x10000000), 1,
+                           desc(D.BF16, sshape, 0x20000000), desc(D.BF16, sshape, 0x30000000), gs, None, None,
+                           desc(D.BF16, [m, n], 0x40000000), keep=True)
+        assert st == D.SUCCESS
+        lib.dq_executor_destroy(ex)
+        return ws
+    assert plan_ws(16, 8192, 4096) == 0
+    assert plan_ws(1, 16384, 8192) == 0
+    assert plan_ws(16, 8192, 7 * 4096) == 0
+    assert plan_ws(16, 4096, 4096) > 0         # k not whole runs of 8192: the decode kernel, split
+    assert plan_ws(16, 8192, 4096 + 64) > 0    # n not a multiple of 4096
+    assert plan_ws(16, 8192, 4096, gs=64) > 0  # groups of 64
+    assert plan_ws(16, 8192, 4096, wdt=D.I8) > 0
+
+
 # ---- execute-phase errors that never reach the device -------------------------
 
 def test_execute_null_executor(lib):
