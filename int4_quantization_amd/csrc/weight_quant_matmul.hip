@@ -518,7 +518,8 @@ __global__ __launch_bounds__(kWqDecodeWaves * kWave) void wq_decode_kernel(const
 //
 // Per batch of two supersteps (256 k) a wave stages its own x1 slice in LDS
 // with direct-to-LDS loads, double-buffered, and keeps each block's next
-// weights in flight from the moment the block's registers are free.  The
+// weights in flight from the moment the block's registers are free (both
+// supersteps of a block at once: they share each column's 128-byte line).  The
 // per-group parameters come into LDS eight groups (four batches) at a time,
 // one 16-byte load per column and kind: loads of one dword per column and
 // batch measured 5 us slower at 16 x 8192 x 28672.  Each x1 operand read serves CB blocks.  The operand
@@ -733,9 +734,15 @@ __global__ __launch_bounds__(kWqBalWaves * kWave, 1) void wq_bal_kernel(const Wq
                         bv[s2] = pack8_t<XT>(wv);
                     }
                 }
-                // The block's registers for superstep u are free: the next
-                // batch's run goes out.
-                load_w(b + 1, u, cb, w);
+                // The block's registers are free: the next batch's runs go
+                // out, both supersteps together, since they are the two
+                // halves of one 128-byte line per column (issued apart, the
+                // line was often fetched twice: 1.64 times the algorithmic
+                // bytes at 16 x 8192 x 28672).
+                if (u == U - 1)
+#pragma unroll
+                    for (int uu = 0; uu < U; ++uu)
+                        load_w(b + 1, uu, cb, w);
 #pragma unroll
                 for (int s2 = 0; s2 < 4; ++s2)
                     acc[cb] = mfma16<XT>(av[s2], bv[s2], acc[cb]);
