@@ -667,27 +667,36 @@ __global__ __launch_bounds__(kWqBalWaves * kWave, 1) void wq_bal_kernel(const Wq
         // of the next batch's weights (the wait above covers it then).
         if (b % PB == PB - 1 && b + 1 < nb)
             stage_p((b + 1) / PB);
+        // x1 operands of the batch: superstep u, lane group g and sub-step s2
+        // take chunk 16 u + 4 g + s2 of row li (the k assignment of the
+        // decode kernel above); both supersteps in one round trip.
+        static_assert(U == 2, "operand reads written for two supersteps");
+        uint4 av[U][4];
+        uint32_t ad[U][4];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            // x1 operands of superstep u: lane group g, sub-step s2 takes
-            // chunk 16 u + 4 g + s2 of row li (the k assignment of the decode
-            // kernel above).
-            uint4 av[4];
-            uint32_t ad[4];
+        for (int u = 0; u < U; ++u)
 #pragma unroll
             for (int s2 = 0; s2 < 4; ++s2) {
                 const int c = 16 * u + 4 * g + s2;
-                ad[s2] = xs_base + static_cast<uint32_t>((buf * SL + li * CH + (c ^ li)) * 16);
+                ad[u][s2] = xs_base + static_cast<uint32_t>((buf * SL + li * CH + (c ^ li)) * 16);
             }
-            asm volatile(
-                "ds_read_b128 %0, %4\n\t"
-                "ds_read_b128 %1, %5\n\t"
-                "ds_read_b128 %2, %6\n\t"
-                "ds_read_b128 %3, %7\n\t"
-                "s_waitcnt lgkmcnt(0)"
-                : "=&v"(av[0]), "=&v"(av[1]), "=&v"(av[2]), "=&v"(av[3])
-                : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3])
-                : "memory");
+        asm volatile(
+            "ds_read_b128 %0, %8\n\t"
+            "ds_read_b128 %1, %9\n\t"
+            "ds_read_b128 %2, %10\n\t"
+            "ds_read_b128 %3, %11\n\t"
+            "ds_read_b128 %4, %12\n\t"
+            "ds_read_b128 %5, %13\n\t"
+            "ds_read_b128 %6, %14\n\t"
+            "ds_read_b128 %7, %15\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(av[0][0]), "=&v"(av[0][1]), "=&v"(av[0][2]), "=&v"(av[0][3]), "=&v"(av[1][0]), "=&v"(av[1][1]),
+              "=&v"(av[1][2]), "=&v"(av[1][3])
+            : "v"(ad[0][0]), "v"(ad[0][1]), "v"(ad[0][2]), "v"(ad[0][3]), "v"(ad[1][0]), "v"(ad[1][1]),
+              "v"(ad[1][2]), "v"(ad[1][3])
+            : "memory");
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
 #pragma unroll
             for (int cb = 0; cb < CB; ++cb) {
                 const float sc = t_to_f32<XT>(static_cast<uint16_t>(sp[cb] >> (16 * u)));
@@ -745,7 +754,7 @@ __global__ __launch_bounds__(kWqBalWaves * kWave, 1) void wq_bal_kernel(const Wq
                         load_w(b + 1, uu, cb, w);
 #pragma unroll
                 for (int s2 = 0; s2 < 4; ++s2)
-                    acc[cb] = mfma16<XT>(av[s2], bv[s2], acc[cb]);
+                    acc[cb] = mfma16<XT>(av[u][s2], bv[s2], acc[cb]);
             }
         }
     }
