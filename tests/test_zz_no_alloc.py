@@ -22,12 +22,13 @@ pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not torch.cuda.is_available(),
 DEV = torch.device("cuda:0")
 
 # (m, k, n, weight, group size, seed): decode and prefill tiles that split k,
-# largest first; the last one does not split.
+# largest first; the last two do not split.
 CASES = [
     (200, 2048, 1024, "int4", 128, 71),  # LDS-tiled kernel, k split, parameter windows
     (8, 4096, 1024, "int4", 128, 72),    # decode kernel, k split
     (3, 2048, 512, "int8", 0, 73),       # smaller decode, k split
     (2, 1024, 4096, "int8", 64, 74),     # enough output tiles: no split
+    (4, 8192, 4096, "int4", 128, 75),    # balanced decode kernel: one workgroup per compute unit, no split
 ]
 
 
