@@ -8,8 +8,9 @@
   synchronization), so prepared calls can be captured in a HIP graph: each
   replay, with new inputs copied in eagerly and the program's own eager
   work and synchronizations between replays, equals an eager call on the
-  same inputs, bit for bit.  The split-k matmul is included: its partial
-  sums live in the prepared call's workspace.
+  same inputs, bit for bit.  The split-k matmul is included (its partial
+  sums live in the prepared call's workspace), and so is the balanced
+  decode matmul (direct-to-LDS staging, no workspace).
 """
 import pytest
 import torch
@@ -57,15 +58,17 @@ def _op(name):
     if name == "mx_quantize":
         inp = _to_dev(synth.mx_inputs(256, 2048, 904))
         return inp, lambda i, s: dq.mx_quantize(i["x"], torch.float8_e4m3fn, 1, stream=s)
-    if name == "weight_quant_matmul_split_k":
-        inp = _to_dev(synth.wq_inputs(16, 8192, 512, 905, weight="int4", group_size=128))
+    if name in ("weight_quant_matmul_split_k", "weight_quant_matmul_balanced"):
+        n = 512 if name.endswith("split_k") else 4096  # 4096: the balanced decode kernel
+        inp = _to_dev(synth.wq_inputs(16, 8192, n, 905, weight="int4", group_size=128))
         return inp, lambda i, s: (dq.weight_quant_matmul(i["x1"], i["x2"], i["scale"], i["offset"],
                                                          i["group_size"], i["bias"], i["x3"],
                                                          i["transpose_x2"], i["weight"], stream=s),)
     raise KeyError(name)
 
 
-OPS = ["dynamic_quant", "ada_layernorm_quant", "antiquantize", "mx_quantize", "weight_quant_matmul_split_k"]
+OPS = ["dynamic_quant", "ada_layernorm_quant", "antiquantize", "mx_quantize", "weight_quant_matmul_split_k",
+       "weight_quant_matmul_balanced"]
 
 
 @pytest.mark.parametrize("name", OPS)
@@ -99,7 +102,7 @@ def _prepared(name):
         def refresh(seed):
             inp["x"].copy_(synth.dq_inputs(rows, n, seed, smooth="vector")["x"])
         return inp, refresh, call, (y, scale)
-    m, k, n = 16, 8192, 512
+    m, k, n = 16, 8192, 512 if name.endswith("split_k") else 4096
     inp = _to_dev(synth.wq_inputs(m, k, n, 912, weight="int4", group_size=128))
     out = torch.empty(m, n, dtype=inp["x1"].dtype, device=DEV)
     call = D.prepare_weight_quant_matmul(inp["x1"], inp["x2"], inp["transpose_x2"], inp["scale"], inp["offset"],
@@ -110,7 +113,7 @@ def _prepared(name):
     return inp, refresh, call, (out,)
 
 
-@pytest.mark.parametrize("name", ["dynamic_quant", "weight_quant_matmul_split_k"])
+@pytest.mark.parametrize("name", ["dynamic_quant", "weight_quant_matmul_split_k", "weight_quant_matmul_balanced"])
 def test_graph_replay_matches_eager(name):
     announce("graph replay", name)
     inp, refresh, call, outs = _prepared(name)
