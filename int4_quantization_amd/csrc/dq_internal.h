@@ -39,7 +39,7 @@ struct DqPlan {
     int variant;
     int vpl;   // 16-byte vectors per lane (vector and team variants)
     int team;  // waves per row: 1, 2 or 4 (vector variant), 2 .. kDqMaxTeam (team variant)
-    bool long_rows;  // team variant: kDqTeamRowsLong rows per team, kDqTeamPrefetchLong in flight
+    bool long_rows;  // team variant: the long schedule (strided teams, then short workgroups)
 };
 
 // Largest grid (workgroups along x) a launch may use, and the largest row
@@ -99,14 +99,20 @@ hipError_t launch_copy_probe(void* dst, const void* src, size_t bytes, hipStream
 constexpr int kDqWaves = 4;
 // Team variant: the most waves a team (one workgroup) has, and the rows each
 // team converts before the workgroup exits.  Inputs without a group index
-// and with at least kDqTeamLongMinRows rows take kDqTeamRowsLong rows per
-// team with kDqTeamPrefetchLong rows in flight ahead of the one converted
-// (about two workgroups per compute unit at that size).
+// and with at least kDqTeamLongMinRows rows take the long schedule:
+// ceil(rows / kDqTeamRowsLong) teams (about two workgroups per compute unit
+// at that size) with kDqTeamPrefetchLong rows in flight ahead of the one
+// converted.
 constexpr int kDqMaxTeam = 16;
 constexpr int kDqTeamRows = 4;
 constexpr int kDqTeamRowsLong = 16;
 constexpr int kDqTeamPrefetchLong = 2;
 constexpr int64_t kDqTeamLongMinRows = 8192;
+// The long schedule's split: ceil(rows / kDqTeamRowsLong) teams convert
+// kDqTeamStridedRows strided rows each, and the rows after theirs go to
+// short workgroups of kDqTeamShortRows consecutive rows.
+constexpr int kDqTeamStridedRows = 14;
+constexpr int kDqTeamShortRows = 2;
 constexpr int kDqTeamVpl = 4;
 constexpr int kDqPrefetch = 1;
 constexpr int64_t kDqVecMaxPerWave = 16 * 8 * 64;

@@ -46,6 +46,7 @@ struct DqArgs {
     void* y;
     float* scale;
     float* offset;
+    int64_t long_teams;  // > 0: team kernel's long schedule (the count of strided teams)
 };
 
 // (D or scale_opt, offset_opt, code range) per output type, from the
@@ -414,12 +415,16 @@ __global__ __launch_bounds__(kDqWaves * kWave) void dq_vec_kernel(DqArgs a)
 // holding duplicate vectors: bf16 [*, 7168] is 896 vectors, 7 waves of 2
 // per lane instead of 4 waves of 4 with 128 duplicates).  Each team converts
 // T rows with the next PD rows' loads in flight, then the workgroup exits;
-// rows are assigned as in the vector variant.  T = 4, PD = 1 in general;
-// long inputs without a group index take T = 16, PD = 2: about two
-// workgroups per compute unit, each with up to three rows of loads
-// outstanding (bf16 [8192, 7168]: 30.8-30.9 against 31.3-31.4 us in
-// interleaved runs; deeper prefetch measured slower: 31.5 us with PD = 3,
-// 32.2 with 4).
+// rows are assigned as in the vector variant.  T = 4, PD = 1 in general.
+// Long inputs without a group index (a.long_teams > 0) take the long
+// schedule: L = a.long_teams teams of T = 14 rows strided by L, PD = 2,
+// about two workgroups per compute unit with up to three rows of loads
+// outstanding each; the rows from 14 L on go to short workgroups of two
+// consecutive rows (blockIdx.x >= L), which fill the third workgroup slot
+// of the compute units as they free.  bf16 [8192, 7168], interleaved runs:
+// 16 strided rows per team 30.8-30.9 against 31.3-31.4 us for 4 (deeper
+// prefetch measured slower: 31.5 us with PD = 3, 32.2 with 4); 14 strided
+// rows plus the short workgroups a further 1-1.7% in three sessions.
 template <int XT, bool SYM, int OUT, int VPL, int T, int PD>
 __global__ __launch_bounds__(kDqMaxTeam * kWave) void dq_team_kernel(DqArgs a)
 {
@@ -429,11 +434,34 @@ __global__ __launch_bounds__(kDqMaxTeam * kWave) void dq_team_kernel(DqArgs a)
     const int team = blockDim.x / kWave;
     const int64_t nvec = a.n >> 3;
     const int64_t r0 = static_cast<int64_t>(blockIdx.x) * T;
+    __shared__ float2 red[2][kDqMaxTeam];
+    if (a.long_teams > 0 && static_cast<int64_t>(blockIdx.x) >= a.long_teams) {
+        // Short workgroup: kDqTeamShortRows consecutive rows after the
+        // strided teams' rows, all loaded at once with the smooth scales.
+        constexpr int TS = kDqTeamShortRows;
+        const int64_t base = a.long_teams * T + (static_cast<int64_t>(blockIdx.x) - a.long_teams) * TS;
+        auto row_s = [&](int t) -> int64_t {
+            const int64_t r = base + t;
+            return r < a.rows ? r : a.rows - 1;
+        };
+        uint4 sb[TS][VPL];
+        float ss[VPL][8];
+#pragma unroll
+        for (int t = 0; t < TS; ++t) {
+            load_x<VPL>(sb[t], a.x, row_s(t), a.n, nvec, team, wit, lane);
+            if (t == 0)
+                load_smooth<VPL>(ss, a, 0, nvec, team, wit, lane);
+        }
+#pragma unroll
+        for (int t = 0; t < TS; ++t)
+            convert_row<XT, SYM, OUT, VPL, kDqMaxTeam>(a, sb[t], ss, row_s(t), t, nvec, 0, team, wit, lane, red);
+        return;
+    }
+    const int64_t stride = a.long_teams > 0 ? a.long_teams : static_cast<int64_t>(gridDim.x);
     auto row_of = [&](int t) -> int64_t {
-        const int64_t r = a.gi ? r0 + t : static_cast<int64_t>(blockIdx.x) + static_cast<int64_t>(t) * gridDim.x;
+        const int64_t r = a.gi ? r0 + t : static_cast<int64_t>(blockIdx.x) + static_cast<int64_t>(t) * stride;
         return r < a.rows ? r : a.rows - 1;
     };
-    __shared__ float2 red[2][kDqMaxTeam];
 
     const bool moe = a.gi != nullptr;
     int32_t gi_lane = 0;
@@ -572,7 +600,7 @@ template <int XT, bool SYM, int OUT>
 KernelFn pick(const DqPlan& p)
 {
     if (p.variant == DQ_VAR_TEAM) {
-        constexpr int TL = kDqTeamRowsLong, PL = kDqTeamPrefetchLong;
+        constexpr int TL = kDqTeamStridedRows, PL = kDqTeamPrefetchLong;
         switch (p.vpl) {
         case 1: return p.long_rows ? dq_team_kernel<XT, SYM, OUT, 1, TL, PL> : dq_team_kernel<XT, SYM, OUT, 1, kDqTeamRows, 1>;
         case 2: return p.long_rows ? dq_team_kernel<XT, SYM, OUT, 2, TL, PL> : dq_team_kernel<XT, SYM, OUT, 2, kDqTeamRows, 1>;
@@ -608,9 +636,9 @@ hipError_t launch_dynamic_quant(const DqPlan& p, hipStream_t stream)
     KernelFn fn = p.x_type == X_F16 ? pick_x<X_F16>(p) : pick_x<X_BF16>(p);
     if (!fn)
         return hipErrorInvalidValue;
-    DqArgs a{p.x, p.smooth, p.group_index, p.n_experts, p.rows, p.n, p.y, p.scale, p.offset};
+    DqArgs a{p.x, p.smooth, p.group_index, p.n_experts, p.rows, p.n, p.y, p.scale, p.offset, 0};
     // Vector variant: one workgroup per T * 4/TEAM rows; team variant: one
-    // per kDqTeamRows (or kDqTeamRowsLong) rows; generic: one per row.
+    // per kDqTeamRows rows (long schedule: below); generic: one per row.
     int64_t rpb = 1;
     int threads = kBlock;
     if (p.variant == DQ_VAR_VECTOR) {
@@ -624,7 +652,17 @@ hipError_t launch_dynamic_quant(const DqPlan& p, hipStream_t stream)
         rpb = p.long_rows ? kDqTeamRowsLong : kDqTeamRows;
         threads = p.team * kWave;
     }
-    const int64_t blocks = (p.rows + rpb - 1) / rpb;
+    int64_t blocks = (p.rows + rpb - 1) / rpb;
+    if (p.variant == DQ_VAR_TEAM && p.long_rows) {
+        // Long schedule: `blocks` strided teams of kDqTeamStridedRows rows,
+        // then short workgroups for the rest (the teams cover fewer than all
+        // rows: 14 ceil(rows / 16) < rows for rows >= 8192).
+        a.long_teams = blocks;
+        const int64_t rest = p.rows - blocks * kDqTeamStridedRows;
+        if (rest <= 0)
+            return hipErrorInvalidValue;
+        blocks += (rest + kDqTeamShortRows - 1) / kDqTeamShortRows;
+    }
     if (blocks > kMaxGridBlocks)
         return hipErrorInvalidValue;
     void* args[] = {&a};
