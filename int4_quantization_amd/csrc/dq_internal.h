@@ -111,7 +111,7 @@ constexpr int64_t kDqTeamLongMinRows = 8192;
 // The long schedule's split: ceil(rows / kDqTeamRowsLong) teams convert
 // kDqTeamStridedRows strided rows each, and the rows after theirs go to
 // short workgroups of kDqTeamShortRows consecutive rows.
-constexpr int kDqTeamStridedRows = 14;
+constexpr int kDqTeamStridedRows = 13;
 constexpr int kDqTeamShortRows = 2;
 constexpr int kDqTeamVpl = 4;
 constexpr int kDqPrefetch = 1;

@@ -417,14 +417,15 @@ __global__ __launch_bounds__(kDqWaves * kWave) void dq_vec_kernel(DqArgs a)
 // T rows with the next PD rows' loads in flight, then the workgroup exits;
 // rows are assigned as in the vector variant.  T = 4, PD = 1 in general.
 // Long inputs without a group index (a.long_teams > 0) take the long
-// schedule: L = a.long_teams teams of T = 14 rows strided by L, PD = 2,
+// schedule: L = a.long_teams teams of T = 13 rows strided by L, PD = 2,
 // about two workgroups per compute unit with up to three rows of loads
-// outstanding each; the rows from 14 L on go to short workgroups of two
+// outstanding each; the rows from 13 L on go to short workgroups of two
 // consecutive rows (blockIdx.x >= L), which fill the third workgroup slot
 // of the compute units as they free.  bf16 [8192, 7168], interleaved runs:
 // 16 strided rows per team 30.8-30.9 against 31.3-31.4 us for 4 (deeper
 // prefetch measured slower: 31.5 us with PD = 3, 32.2 with 4); 14 strided
-// rows plus the short workgroups a further 1-1.7% in three sessions.
+// rows plus the short workgroups a further 1-1.7% in three sessions, and
+// 13 another 0.7% (12 and three-row short workgroups measured slower).
 template <int XT, bool SYM, int OUT, int VPL, int T, int PD>
 __global__ __launch_bounds__(kDqMaxTeam * kWave) void dq_team_kernel(DqArgs a)
 {
@@ -656,7 +657,7 @@ hipError_t launch_dynamic_quant(const DqPlan& p, hipStream_t stream)
     if (p.variant == DQ_VAR_TEAM && p.long_rows) {
         // Long schedule: `blocks` strided teams of kDqTeamStridedRows rows,
         // then short workgroups for the rest (the teams cover fewer than all
-        // rows: 14 ceil(rows / 16) < rows for rows >= 8192).
+        // rows: 13 ceil(rows / 16) < rows for rows >= 8192).
         a.long_teams = blocks;
         const int64_t rest = p.rows - blocks * kDqTeamStridedRows;
         if (rest <= 0)
