@@ -695,10 +695,13 @@ __global__ __launch_bounds__(kWqBalWaves * kWave, 1) void wq_bal_kernel(const Wq
             : "v"(ad[0][0]), "v"(ad[0][1]), "v"(ad[0][2]), "v"(ad[0][3]), "v"(ad[1][0]), "v"(ad[1][1]),
               "v"(ad[1][2]), "v"(ad[1][3])
             : "memory");
+        // Block by block, both supersteps of a block before the next block, so
+        // a block's registers free (and its next runs go out) at (cb + 1) / CB
+        // of the batch, almost a whole batch before they are used.
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
+        for (int cb = 0; cb < CB; ++cb) {
 #pragma unroll
-            for (int cb = 0; cb < CB; ++cb) {
+            for (int u = 0; u < U; ++u) {
                 const float sc = t_to_f32<XT>(static_cast<uint16_t>(sp[cb] >> (16 * u)));
                 const float of = OFF ? t_to_f32<XT>(static_cast<uint16_t>(op[cb] >> (16 * u))) : 0.0f;
                 uint4 bv[4];
