@@ -635,14 +635,10 @@ __global__ __launch_bounds__(kWqBalWaves * kWave, 1) void wq_bal_kernel(const Wq
             load_w(0, u, cb, w);
     const uint32_t xs_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&xs[wave][0][0]));
     const uint32_t ps_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&ps[wave][0][0]));
-    for (int b = 0; b < nb; ++b) {
-        const int buf = b & 1;
-        wait_vm(std::integral_constant<int, kAfter>{});
-        stage_x(b + 1, buf ^ 1);
-        // This batch's parameters of the 7 block slots (slots past CB read
-        // padding columns, unused): dword b % PB of each column's chunk.
-        uint32_t sp[kWqBalMaxBlocks], op[kWqBalMaxBlocks];
-        const uint32_t pb = ps_base + static_cast<uint32_t>(li * 16 + (b % PB) * 4);
+    // Scale and offset dwords (T bits) of the 7 block slots at LDS address
+    // pa: block cb at pa + 256 cb, offsets at pa + 2048 (slots past CB read
+    // padding columns, unused).
+    auto read_params = [&](uint32_t pa, uint32_t (&sp)[kWqBalMaxBlocks], uint32_t (&op)[kWqBalMaxBlocks]) {
         asm volatile(
             "ds_read_b32 %0, %14 offset:0\n\t"
             "ds_read_b32 %1, %14 offset:256\n\t"
@@ -661,8 +657,36 @@ __global__ __launch_bounds__(kWqBalWaves * kWave, 1) void wq_bal_kernel(const Wq
             "s_waitcnt lgkmcnt(0)"
             : "=&v"(sp[0]), "=&v"(sp[1]), "=&v"(sp[2]), "=&v"(sp[3]), "=&v"(sp[4]), "=&v"(sp[5]), "=&v"(sp[6]),
               "=&v"(op[0]), "=&v"(op[1]), "=&v"(op[2]), "=&v"(op[3]), "=&v"(op[4]), "=&v"(op[5]), "=&v"(op[6])
-            : "v"(pb)
+            : "v"(pa)
             : "memory");
+    };
+    uint64_t okm[kWqBalMaxBlocks][U] = {};
+    for (int b = 0; b < nb; ++b) {
+        const int buf = b & 1;
+        wait_vm(std::integral_constant<int, kAfter>{});
+        stage_x(b + 1, buf ^ 1);
+        // Once per parameter chunk, with an offset: whether the one-FMA form
+        // holds (wq_fma.h) for every block, superstep and batch of the chunk,
+        // lane group g checking batch PB q + g of column li, so bit 16 g + li
+        // of okm[cb][u] covers that column's group (a quarter of the checks a
+        // per-batch test of every lane makes).
+        if constexpr (OFF) {
+            if (b % PB == 0) {
+                uint32_t cs[kWqBalMaxBlocks], co[kWqBalMaxBlocks];
+                read_params(ps_base + static_cast<uint32_t>(li * 16 + g * 4), cs, co);
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        const float sc = t_to_f32<XT>(static_cast<uint16_t>(cs[cb] >> (16 * u)));
+                        const float of = t_to_f32<XT>(static_cast<uint16_t>(co[cb] >> (16 * u)));
+                        okm[cb][u] = __ballot(fma_exact<WT, XT>(of, sc, of * sc));
+                    }
+            }
+        }
+        // This batch's parameters: dword b % PB of each column's chunk.
+        uint32_t sp[kWqBalMaxBlocks], op[kWqBalMaxBlocks];
+        read_params(ps_base + static_cast<uint32_t>(li * 16 + (b % PB) * 4), sp, op);
         // The chunk's last batch has read it: the next chunk comes in now, ahead
         // of the next batch's weights (the wait above covers it then).
         if (b % PB == PB - 1 && b + 1 < nb)
@@ -709,7 +733,7 @@ __global__ __launch_bounds__(kWqBalWaves * kWave, 1) void wq_bal_kernel(const Wq
                 float os = 0.0f;
                 if constexpr (OFF) {
                     os = of * sc;
-                    use_fma = __all(fma_exact<WT, XT>(of, sc, os));
+                    use_fma = ((okm[cb][u] >> (16 * (b % PB))) & 0xFFFFull) == 0xFFFFull;
                 }
                 if (!OFF || use_fma) {
                     // int4 decodes to 16 code and s / 16 is exact; with an
