@@ -620,6 +620,12 @@ __global__ __launch_bounds__(kWqBalWaves * kWave, 1) void wq_bal_kernel(const Wq
         asm volatile("" ::: "memory");
     };
 
+    // Waves w and w + 4 share a SIMD and run the same instruction stream;
+    // giving the first the higher issue priority lets it run ahead while the
+    // second fills the SIMD's idle cycles, instead of both waiting for
+    // memory at the same points.
+    if (wave < 4)
+        __builtin_amdgcn_s_setprio(2);
     f32x4 acc[CB];
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
